@@ -1,0 +1,200 @@
+/*
+ * entmaxkv.h -- C ABI of libentmaxkv.so, the EntmaxKV decode hot path for one
+ * AMD Instinct MI355X (gfx950), written as HIP kernels.
+ *
+ * What it computes follows "Resumen Tecnico: EntmaxKV - Decodificacion
+ * Consciente del Soporte para Atencion Entmax" (gist.science/es/paper/
+ * 2605.21649; cited below as [EntmaxKV s.X] for its section X):
+ *   1. per-page key metadata: per-coordinate bounding box and Gaussian
+ *      statistics ............................................ [EntmaxKV s.2.A]
+ *   2. query-aware page scores from that metadata ............. [EntmaxKV s.2.A]
+ *   3. candidate-page selection, Top-k or Gaussian-aware ...... [EntmaxKV s.2.B]
+ *   4. alpha-entmax attention over the selected pages only .... [EntmaxKV s.2.C]
+ *   plus full-cache entmax and softmax decodes, the baselines of [EntmaxKV s.4].
+ * alpha-entmax is p_t = [(alpha-1) s_t - tau]_+^(1/(alpha-1)) with tau fixed by
+ * sum_t p_t = 1 (Peters, Niculae & Martins 2019); scores s_t = scale * q.k_t.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  * Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *    buffer, including the workspace `ws`; the library allocates nothing, keeps
+ *    no pointer after returning and holds no state between calls (apart from
+ *    lazily computed constants), so calls on different streams may overlap as
+ *    long as their buffers (including `ws`) do not.
+ *  * All work is enqueued asynchronously on `stream`; nothing synchronizes.
+ *    Launch failures are reported by the return code; device faults surface at
+ *    the caller's next synchronization.
+ *  * Arguments are validated on the host before anything is launched.  Device
+ *    data (page ids, lengths, selections) is checked inside the kernels, which
+ *    never read outside the buffers implied by the shape; bad entries produce
+ *    NaN results as documented per call.
+ *  * KV dtype (`entmaxkv_shape.dtype`) applies to q, the K/V pools and the page
+ *    metadata; outputs are float32 (scores, weights, attention outputs) or
+ *    float64 (thresholds).
+ *
+ * Layouts (row-major):
+ *   q           [B][Hq][d]                       KV dtype
+ *   k_pool,v_pool [num_phys_pages][Hkv][P][d]    KV dtype (slot j of a page = token p*P+j)
+ *   meta        [num_phys_pages][Hkv][4][d]      KV dtype: k_min, k_max, mean, var
+ *   page_table  int32 [B][max_pages]             logical page -> physical page
+ *   seq_lens    int32 [B]                        L_b, clamped to [0, max_pages*P]
+ *   box, mu, var  float32 [B][Hq][max_pages]     per-page scores
+ *   sel_idx     int32 [B][Hq][max_pages]         selected logical pages, strictly ascending
+ *   sel_cnt     int32 [B][Hq]
+ *   out         float32 [B][Hq][d]
+ * Query head h reads KV head h / (Hq/Hkv).  Logical page p of sequence b holds
+ * n_{b,p} = min(P, L_b - p*P) tokens; N_b = ceil(L_b/P) pages.
+ */
+#ifndef ENTMAXKV_H
+#define ENTMAXKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum entmaxkv_status {
+  ENTMAXKV_OK = 0,
+  ENTMAXKV_ERR_INVALID_ARGUMENT = 1, /* null required pointer, bad dims, Hq % Hkv, k <= 0, alpha <= 1, ... */
+  ENTMAXKV_ERR_UNSUPPORTED = 2,      /* (d, P, dtype, group size) without a kernel */
+  ENTMAXKV_ERR_WORKSPACE = 3,        /* ws_bytes below entmaxkv_workspace_bytes(...) */
+  ENTMAXKV_ERR_HIP = 4               /* a launch failed; see entmaxkv_status_string */
+};
+
+enum entmaxkv_dtype { ENTMAXKV_F32 = 0, ENTMAXKV_BF16 = 1 };
+
+/* Supported: d in {64, 128}; P in {16, 32, 64}; Hq/Hkv in {1, 2, 4, 8}. */
+typedef struct entmaxkv_shape {
+  int32_t batch;          /* B >= 1 */
+  int32_t n_q_heads;      /* Hq >= 1 */
+  int32_t n_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* d */
+  int32_t page_size;      /* P */
+  int32_t max_pages;      /* >= 1; row stride of page_table and of per-page arrays */
+  int32_t num_phys_pages; /* >= 1; size of the K/V/metadata pools */
+  int32_t dtype;          /* entmaxkv_dtype */
+  double scale;           /* score scale; 0 selects 1/sqrt(d) */
+} entmaxkv_shape;
+
+/* which_call values for entmaxkv_workspace_bytes */
+enum entmaxkv_call {
+  ENTMAXKV_CALL_SCORE = 1,
+  ENTMAXKV_CALL_TOPK = 2,
+  ENTMAXKV_CALL_GAUSS = 3,
+  ENTMAXKV_CALL_DECODE_SPARSE = 4,
+  ENTMAXKV_CALL_DECODE_FULL = 5,
+  ENTMAXKV_CALL_SOFTMAX = 6
+};
+
+/* Bytes of workspace a call needs for this shape (0 if none).  Returns 0 for
+ * an invalid shape.  The workspace content need not be initialized and is
+ * scratch: its contents after a call are unspecified. */
+size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape /*(host)*/, int32_t which_call);
+
+/* Text for a status code; for ENTMAXKV_ERR_HIP it includes the HIP error of
+ * the most recent failure on the calling thread. */
+const char *entmaxkv_status_string(int32_t status);
+
+/*
+ * build_page_meta -- [EntmaxKV s.2.A]: per page and KV head, the per-coordinate
+ * key bounding box (k_min, k_max) and Gaussian statistics (mean, population
+ * variance) over the page's filled tokens.  mean = S1/n, var = max(0, S2/n -
+ * mean^2) with S1, S2 fp64 sums; each value is rounded once (round-to-nearest-
+ * even) to the KV dtype.  from_token (nullable): when given, only logical pages
+ * p < N_b whose range [pP, pP+P) holds a position >= from_token[b] are rebuilt
+ * (the append path as pages fill); NULL rebuilds every page.  Records of pages
+ * whose page-table entry is out of range are left untouched.
+ */
+int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const int32_t *page_table,
+                        const int32_t *seq_lens, const int32_t *from_token, void *meta,
+                        hipStream_t stream);
+
+/*
+ * score_pages -- [EntmaxKV s.2.A], per (b, h, p < N_b) with c = scale:
+ *   box = c * sum_i max(q_i kmin_i, q_i kmax_i)   (upper bound on every score in
+ *         the page; fp64 sum of exact products, stored rounded toward +inf)
+ *   mu  = c * sum_i q_i mean_i,   var = c^2 * sum_i q_i^2 var_i
+ *         (Gaussian model of the page's scores; stored round-to-nearest-even)
+ * Entries p >= N_b are not written.  An out-of-range page-table entry gives NaN
+ * in all three outputs.  ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_SCORE).
+ */
+int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta,
+                    const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                    float *var, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * select_pages_topk -- [EntmaxKV s.2.B, policy 1]: per (b, h), the k pages with
+ * the largest box; ties go to the lower page index, NaN ranks below every
+ * number, -0 equals +0, and N_b <= k keeps every page.  sel_idx lists the
+ * chosen pages in ascending order, sel_cnt = min(k, N_b).  seq_mask (nullable,
+ * uint8 [B]): rows of sequences with mask 0 are not written.
+ */
+int32_t select_pages_topk(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,
+                          int32_t k, const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * select_pages_gauss -- [EntmaxKV s.2.B, policy 2]: estimate the global entmax
+ * threshold from the page Gaussians, then keep pages whose estimated maximum
+ * score reaches it minus a margin Delta.  This library's reading:
+ *   F(t) = sum_p n_p sum_j w_j [(alpha-1)(mu_p + sqrt(2) sigma_p x_j) - t]_+^(1/(alpha-1))
+ * with (x_j, w_j sqrt(pi)) the 16-point Gauss-Hermite rule; tau_hat is the root
+ * of F = 1; keep p iff min(mu_p + n_sigma*sigma_p, box_p) >= tau_hat/(alpha-1)
+ * - delta; if none passes, keep the page of largest estimate (lowest index on
+ * ties).  Pages with non-finite box/mu/var are never kept.  tau_hat (nullable,
+ * float64 [B][Hq]) receives tau_hat/(alpha-1) (score units); NaN if N_b = 0.
+ * Requires alpha > 1, delta >= 0, n_sigma >= 0.  alpha in {1.5, 2} runs the
+ * fast histogram solver; other alpha use a slower per-row bisection.
+ */
+int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const float *mu,
+                           const float *var, const int32_t *seq_lens, double alpha, double delta,
+                           double n_sigma, const uint8_t *seq_mask, int32_t *sel_idx,
+                           int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/*
+ * entmax_decode_sparse -- [EntmaxKV s.2.C]: alpha-entmax attention of each
+ * query head over the tokens t < L_b of ITS selected pages only:
+ *   p_t = [(alpha-1) s_t - tau]_+^(1/(alpha-1)) / Z,  out = sum_t p_t v_t,
+ * tau the root of sum_t [(alpha-1)s_t - tau]_+^(1/(alpha-1)) = 1 over the kept
+ * tokens, Z the sum of the unnormalized weights.  tau_method: 0 = root finder
+ * (any alpha), 1 = sort closed form (alpha == 2 only).  tau (nullable, float64
+ * [B][Hq]) receives tau/(alpha-1).  weights_out (nullable, float32
+ * [B][Hq][max_pages*P], for tests) receives p at logical token positions and
+ * zero elsewhere.  A row with sel_cnt = 0 gets out = 0, tau = NaN; a row whose
+ * selection is out of range or not strictly ascending gets NaN out and tau.
+ */
+int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *page_table,
+                             const int32_t *seq_lens, const int32_t *sel_idx,
+                             const int32_t *sel_cnt, double alpha, int32_t tau_method, float *out,
+                             double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* entmax_decode_full -- the same attention over every cached token (the
+ * full-cache entmax baseline of [EntmaxKV s.4]). */
+int32_t entmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                           const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                           double alpha, int32_t tau_method, float *out, double *tau,
+                           float *weights_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* softmax_decode_full -- exact softmax attention over every cached token, the
+ * full-cache softmax baseline of [EntmaxKV s.4].  lse (nullable, float32
+ * [B][Hq]) receives log sum_t exp(s_t).  L_b = 0 gives out = 0, lse = -inf. */
+int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                            const void *v_pool, const int32_t *page_table,
+                            const int32_t *seq_lens, float *out, float *lse, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* The 16-point Gauss-Hermite rule the Gaussian selector uses (host copy, for
+ * inspection): nodes ascending, weights for the weight function exp(-x^2). */
+void entmaxkv_gauss_hermite16(double *nodes /*(host)[16]*/, double *weights /*(host)[16]*/);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

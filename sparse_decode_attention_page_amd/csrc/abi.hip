@@ -1,0 +1,260 @@
+// abi.hip -- the C ABI of libentmaxkv.so (declared in include/entmaxkv.h):
+// argument validation, workspace sizing and kernel launches.  Nothing here
+// allocates device memory or synchronizes.
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace ekv {
+
+// --------------------------------------------------------- Gauss-Hermite rule
+// Nodes: sign changes of the orthonormal Hermite polynomial p_16 on a fine grid,
+// refined by bisection; weights: Christoffel numbers 1 / sum_{k<16} p_k(x)^2.
+// (p_0 = pi^(-1/4), p_1 = sqrt(2) x p_0,
+//  p_{k+1} = sqrt(2/(k+1)) x p_k - sqrt(k/(k+1)) p_{k-1}.)
+static void ortho_hermite(double x, double *pk /*[17]*/) {
+  pk[0] = std::pow(M_PI, -0.25);
+  pk[1] = std::sqrt(2.0) * x * pk[0];
+  for (int k = 1; k < 16; ++k)
+    pk[k + 1] = std::sqrt(2.0 / (k + 1)) * x * pk[k] - std::sqrt((double)k / (k + 1)) * pk[k - 1];
+}
+
+static GaussConsts compute_gh16() {
+  GaussConsts gc;
+  double pk[17];
+  int found = 0;
+  const double step = 1e-3;
+  double xa = -7.0;
+  ortho_hermite(xa, pk);
+  double fa = pk[16];
+  for (int i = 1; i <= 14000 && found < 16; ++i) {
+    const double xb = -7.0 + i * step;
+    ortho_hermite(xb, pk);
+    const double fb = pk[16];
+    if ((fa < 0) != (fb < 0)) {
+      double lo = xa, hi = xb, flo = fa;
+      for (int it = 0; it < 200; ++it) {
+        const double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        ortho_hermite(mid, pk);
+        if ((pk[16] < 0) == (flo < 0)) { lo = mid; flo = pk[16]; } else hi = mid;
+      }
+      // pick the end with the smaller |p_16|
+      double plo, phi;
+      ortho_hermite(lo, pk); plo = std::fabs(pk[16]);
+      ortho_hermite(hi, pk); phi = std::fabs(pk[16]);
+      gc.x[found++] = plo <= phi ? lo : hi;
+    }
+    xa = xb;
+    fa = fb;
+  }
+  for (int j = 0; j < 16; ++j) {
+    ortho_hermite(gc.x[j], pk);
+    double s = 0.0;
+    for (int k = 0; k < 16; ++k) s += pk[k] * pk[k];
+    gc.w[j] = (1.0 / s) / std::sqrt(M_PI);  // normalized: sum_j w_j = 1
+  }
+  return gc;
+}
+
+const GaussConsts &gauss_consts() {
+  static const GaussConsts gc = compute_gh16();
+  return gc;
+}
+
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> ctr{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull};
+  const unsigned long long mask = (1ull << 40) - 1;
+  unsigned long long e;
+  do { e = ctr.fetch_add(1) & mask; } while (e == 0);
+  return e;
+}
+
+static thread_local char g_err[256] = "";
+
+static int32_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return ENTMAXKV_OK;
+  std::snprintf(g_err, sizeof g_err, "HIP error: %s", hipGetErrorString(e));
+  return ENTMAXKV_ERR_HIP;
+}
+
+static int32_t check_shape(const entmaxkv_shape *s, Dims *D) {
+  if (!s) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->max_pages < 1 ||
+      s->num_phys_pages < 1 || s->head_dim < 1 || s->page_size < 1)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (s->n_q_heads % s->n_kv_heads != 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(s->scale >= 0.0) || !std::isfinite(s->scale)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (s->dtype != ENTMAXKV_F32 && s->dtype != ENTMAXKV_BF16) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (s->page_size != 16 && s->page_size != 32 && s->page_size != 64) return ENTMAXKV_ERR_UNSUPPORTED;
+  if ((long long)s->batch * s->n_q_heads > 8192) return ENTMAXKV_ERR_UNSUPPORTED;
+  if ((long long)s->max_pages * s->page_size >= (1ll << 31) || s->max_pages >= (1 << 24))
+    return ENTMAXKV_ERR_UNSUPPORTED;
+  if (D) {
+    D->B = s->batch;
+    D->Hq = s->n_q_heads;
+    D->Hkv = s->n_kv_heads;
+    D->G = G;
+    D->d = s->head_dim;
+    D->P = s->page_size;
+    D->max_pages = s->max_pages;
+    D->num_phys = s->num_phys_pages;
+    D->scale = s->scale != 0.0 ? s->scale : 1.0 / std::sqrt((double)s->head_dim);
+  }
+  return ENTMAXKV_OK;
+}
+
+static int32_t check_ws(size_t need, const void *ws, size_t ws_bytes) {
+  if (need == 0) return ENTMAXKV_OK;
+  if (!ws || ws_bytes < need) return ENTMAXKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  return ENTMAXKV_OK;
+}
+
+}  // namespace ekv
+
+using namespace ekv;
+
+extern "C" {
+
+size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call) {
+  Dims D;
+  if (check_shape(shape, &D) != ENTMAXKV_OK) return 0;
+  switch (which_call) {
+    case ENTMAXKV_CALL_SCORE: return score_ws_bytes(D);
+    case ENTMAXKV_CALL_TOPK: return topk_ws_bytes(D);
+    case ENTMAXKV_CALL_GAUSS: return gauss_ws_bytes(D);
+    case ENTMAXKV_CALL_DECODE_SPARSE: return decode_ws_bytes(D, false);
+    case ENTMAXKV_CALL_DECODE_FULL: return decode_ws_bytes(D, true);
+    case ENTMAXKV_CALL_SOFTMAX: return softmax_ws_bytes(D);
+  }
+  return 0;
+}
+
+const char *entmaxkv_status_string(int32_t status) {
+  switch (status) {
+    case ENTMAXKV_OK: return "ok";
+    case ENTMAXKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ENTMAXKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case ENTMAXKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case ENTMAXKV_ERR_HIP: return g_err[0] ? g_err : "HIP error";
+  }
+  return "unknown status";
+}
+
+void entmaxkv_gauss_hermite16(double *nodes, double *weights) {
+  const GaussConsts &gc = gauss_consts();
+  for (int j = 0; j < 16; ++j) {
+    if (nodes) nodes[j] = gc.x[j];
+    if (weights) weights[j] = gc.w[j] * std::sqrt(M_PI);
+  }
+}
+
+int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const int32_t *page_table,
+                        const int32_t *seq_lens, const int32_t *from_token, void *meta,
+                        hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!k_pool || !page_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_build_meta(D, shape->dtype, k_pool, page_table, seq_lens, from_token, meta, stream));
+}
+
+int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta,
+                    const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                    float *var, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(score_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_score(D, shape->dtype, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
+}
+
+int32_t select_pages_topk(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,
+                          int32_t k, const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!box || !seq_lens || !sel_idx || !sel_cnt || k <= 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(topk_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_topk(D, box, seq_lens, k, seq_mask, sel_idx, sel_cnt, ws, stream));
+}
+
+int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const float *mu,
+                           const float *var, const int32_t *seq_lens, double alpha, double delta,
+                           double n_sigma, const uint8_t *seq_mask, int32_t *sel_idx,
+                           int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!box || !mu || !var || !seq_lens || !sel_idx || !sel_cnt) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(alpha > 1.0) || !std::isfinite(alpha) || !(delta >= 0.0) || !std::isfinite(delta) ||
+      !(n_sigma >= 0.0) || !std::isfinite(n_sigma))
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(gauss_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_gauss(D, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, sel_idx,
+                                 sel_cnt, tau_hat, ws, stream));
+}
+
+static int32_t decode_common(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                             const int32_t *sel_idx, const int32_t *sel_cnt, double alpha,
+                             int32_t tau_method, float *out, double *tau, float *weights_out, void *ws,
+                             size_t ws_bytes, hipStream_t stream, bool full) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!full && (!sel_idx || !sel_cnt)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(decode_ws_bytes(D, full), ws, ws_bytes))) return st;
+  return hip_status(launch_entmax_decode(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens,
+                                         full ? nullptr : sel_idx, full ? nullptr : sel_cnt, alpha,
+                                         tau_method, out, tau, weights_out, ws, stream));
+}
+
+int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *page_table,
+                             const int32_t *seq_lens, const int32_t *sel_idx,
+                             const int32_t *sel_cnt, double alpha, int32_t tau_method, float *out,
+                             double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return decode_common(shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, alpha,
+                       tau_method, out, tau, weights_out, ws, ws_bytes, stream, false);
+}
+
+int32_t entmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                           const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                           double alpha, int32_t tau_method, float *out, double *tau,
+                           float *weights_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_common(shape, q, k_pool, v_pool, page_table, seq_lens, nullptr, nullptr, alpha,
+                       tau_method, out, tau, weights_out, ws, ws_bytes, stream, true);
+}
+
+int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                            const void *v_pool, const int32_t *page_table,
+                            const int32_t *seq_lens, float *out, float *lse, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(softmax_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_softmax(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+// common.hpp -- device helpers shared by the EntmaxKV HIP kernels (gfx950).
+//
+// Arithmetic contract used across the kernels (so that page sets and entmax
+// supports agree bit for bit with an fp64 reference):
+//  * bf16 x bf16 and bf16^2 x bf16 products carry <= 24 significant bits, so
+//    they are exact in fp32 and in fp64; every dot product over a page record or
+//    a key is summed in fp64 and rounded once when stored.
+//  * The library is compiled with -ffp-contract=off; fused multiply-adds appear
+//    only where written (__builtin_fma), i.e. where the product is exact.
+//  * Every comparison that decides membership (page kept, token in support) is
+//    made in fp64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "entmaxkv.h"
+
+namespace ekv {
+
+constexpr int kWave = 64;
+
+// --------------------------------------------------------------------------- loads
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <typename T>
+__device__ __forceinline__ float load_f(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+template <>
+__device__ __forceinline__ float load_f<float>(const float *p, size_t i) { return p[i]; }
+
+// ----------------------------------------------------------------------- roundings
+// fp64 -> bf16 round-to-nearest-even in one step: round to float with
+// round-toward-zero plus a sticky bit (round-to-odd, exact enough because float
+// carries 16 more bits than bf16), then round-to-nearest-even to bf16.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  if (x != x) return 0x7FC0;
+  float t = __double2float_rz(x);
+  uint32_t u = __float_as_uint(t);
+  if ((double)t != x) u |= 1u;
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_rne(T *p, size_t i, double x);
+template <>
+__device__ __forceinline__ void store_rne<uint16_t>(uint16_t *p, size_t i, double x) { p[i] = f64_to_bf16_rne(x); }
+template <>
+__device__ __forceinline__ void store_rne<float>(float *p, size_t i, double x) { p[i] = (float)x; }
+
+// float -> uint32 whose unsigned order is the float order (NaN mapped to the
+// lowest key, -0 mapped onto +0).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f != f) return 0u;
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------- reductions
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    T w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Block-wide sum with a deterministic order (waves combined in index order).
+// `scratch` must hold blockDim.x / 64 values; result valid in every thread.
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T *scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  T s = scratch[0];
+  for (int i = 1; i < nw; ++i) s += scratch[i];
+  return s;
+}
+template <typename T>
+__device__ __forceinline__ T block_max(T v, T *scratch) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  T s = scratch[0];
+  for (int i = 1; i < nw; ++i) s = scratch[i] > s ? scratch[i] : s;
+  return s;
+}
+
+// Exclusive prefix sum over a block (int32), returns the total in *total.
+__device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) scratch[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) base += scratch[i];
+    tot += scratch[i];
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+// --------------------------------------------------------------------- sequences
+struct Dims {
+  int B, Hq, Hkv, G, d, P, max_pages, num_phys;
+  double scale;
+};
+
+__device__ __forceinline__ int seq_len_clamped(const int32_t *seq_lens, int b, const Dims &D) {
+  long long L = seq_lens[b];
+  long long cap = (long long)D.max_pages * D.P;
+  if (L < 0) L = 0;
+  if (L > cap) L = cap;
+  return (int)L;
+}
+__device__ __forceinline__ int n_pages_of(int L, int P) { return (L + P - 1) / P; }
+
+// "last block done" handshake: every block of a group calls this once after
+// writing its results; exactly one block (the last) sees true.  The counter is
+// reset by that block so the workspace can be reused without a memset.
+__device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, int *flag_smem) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned int prev = atomicAdd(counter, 1u);
+    bool last = (prev + 1 == expected);
+    if (last) atomicExch(counter, 0u);
+    *flag_smem = last ? 1 : 0;
+  }
+  __syncthreads();
+  bool last = *flag_smem != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// Same handshake for a counter that may hold garbage (a fresh workspace): the
+// counter packs (epoch << 24 | arrivals); an arrival that finds another epoch
+// restarts the count.  `epoch` (1 .. 2^40-1) comes from the host per launch;
+// the last block resets the counter to 0, which no epoch matches.
+__device__ __forceinline__ bool arrive_last_ep(unsigned long long *ctr, unsigned long long epoch,
+                                               unsigned int expected, int *flag_smem) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long old = atomicAdd(ctr, 0ull);
+    unsigned long long nv;
+    for (;;) {
+      nv = ((old >> 24) == epoch) ? old + 1ull : ((epoch << 24) | 1ull);
+      const unsigned long long prev = atomicCAS(ctr, old, nv);
+      if (prev == old) break;
+      old = prev;
+    }
+    const bool last = (nv & 0xFFFFFFull) == (unsigned long long)expected;
+    if (last) atomicExch(ctr, 0ull);
+    *flag_smem = last ? 1 : 0;
+  }
+  __syncthreads();
+  const bool last = *flag_smem != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace ekv

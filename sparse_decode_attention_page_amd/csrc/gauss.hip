@@ -1,0 +1,568 @@
+// gauss.hip -- Gaussian-aware entmax page selection ([EntmaxKV s.2.B], policy 2).
+//
+// EntmaxKV s.2.B = section 2.B ("candidate selection policies") of "Resumen
+// Tecnico: EntmaxKV - Decodificacion Consciente del Soporte para Atencion
+// Entmax", gist.science/es/paper/2605.21649: estimate the global alpha-entmax
+// threshold from the page-level Gaussian statistics by solving an approximate
+// normalization equation, then keep the pages whose estimated maximum score
+// exceeds that threshold adjusted by a safety margin Delta.
+//
+// Reading implemented here (the page gives no formulas):
+//   F(t) = sum_p n_p sum_j w_j [a (mu_p + sqrt2 sigma_p x_j) - t]_+^beta,
+//   a = alpha - 1, beta = 1/a, (x_j, w_j) 16-point Gauss-Hermite (w / sqrt(pi)),
+//   tau_hat = root of F(tau_hat) = 1,
+//   keep p  iff  min(mu_p + n_sigma sigma_p, box_p) >= tau_hat/a - Delta,
+//   none kept -> keep the page of largest estimate (lowest index on ties).
+//
+// Root finding for beta in {1, 2} (alpha = 2, 1.5) without a sequential bisection
+// over every point (16 per page):
+//   K1  per (row, chunk): lower bracket  lo = max_p [a mu_p - (2.5/n_p)^a]
+//       (the page alone already gives F >= 1 there, since half of the rule's
+//       weight sits on nodes x_j >= 0) and upper bracket hi = max_p of the top
+//       node (F = 0 there).
+//   K2  per (row, chunk): histogram of the points v > lo over NB equal bins of
+//       [lo, hi] holding the moments M_r = sum c (v - e_b)^r, r <= beta, taken
+//       about each bin's lower edge e_b.  The last block of a row merges the
+//       chunks in order and runs a suffix scan of the moments (shifting them
+//       edge to edge keeps every term non-negative, so there is no
+//       cancellation): F at every edge follows exactly, which fixes the bin
+//       [e_k, e_k+1) that holds the root.
+//   K3  per (row, chunk): collect the points inside that bin, and classify each
+//       page as kept / dropped / undecided for every threshold the bin allows.
+//       The last block solves F = 1 inside the bin (suffix polynomial + the
+//       collected points) by Newton steps from the left (F is convex and
+//       decreasing), settles the undecided pages and writes the ascending list.
+// Other alpha fall back to one block per row running a plain bisection.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ekv {
+
+constexpr int kGThreads = 256;
+constexpr int kNB = 256;  // histogram bins
+
+struct GaussParams {
+  double a, beta, delta, nsig;
+  int chunk;   // pages per chunk
+  int nchunk;  // chunks per row (max over rows)
+  int cap;     // in-bin capacity per row (points)
+  int ibeta;   // 1, 2 or 0 (generic)
+};
+
+struct GaussWs {
+  double *part;        // [rows][nchunk][2]   lo candidate, top node
+  double *hist;        // [rows][nchunk][kNB][3]
+  double *rowinfo;     // [rows][8]           k, lo, w, T0, T1, T2
+  double *inbin;       // [rows][cap][2]      (v, c)
+  int *inbin_cnt;      // [rows]
+  int *list;           // [rows][max_pages]   page | undecided<<31, per chunk segments
+  int *list_cnt;       // [rows][nchunk]
+  double *amax;        // [rows][nchunk][2]   best estimate, its page
+  unsigned int *ctr;   // [rows][2]
+};
+
+__device__ __forceinline__ bool page_valid(float bx, float m, float v) {
+  return isfinite(bx) && isfinite(m) && isfinite(v);
+}
+__device__ __forceinline__ double powb(double x, int ibeta, double beta) {
+  return ibeta == 2 ? x * x : (ibeta == 1 ? x : pow(x, beta));
+}
+// keep predicate at threshold thr (score units); sqrt-free form of mu + n sigma >= thr
+__device__ __forceinline__ bool keep_at(double thr, double bx, double m, double s2, double nsig) {
+  const double dd = thr - m;
+  const bool g_ok = (dd <= 0.0) || (nsig * nsig * s2 >= dd * dd);
+  return g_ok && bx >= thr;
+}
+__device__ __forceinline__ double bin_edge(double lo, double w, int b) { return lo + (double)b * w; }
+__device__ __forceinline__ int bin_of(double v, double lo, double w) {
+  int b = (int)((v - lo) / w);
+  return b < 0 ? 0 : (b >= kNB ? kNB - 1 : b);
+}
+
+struct RowCtx {
+  int row, b, L, np, nch;
+  bool active;
+};
+__device__ __forceinline__ RowCtx row_ctx(const Dims &D, const GaussParams &gp, const int32_t *seq_lens,
+                                          const uint8_t *seq_mask, int row) {
+  RowCtx r;
+  r.row = row;
+  r.b = row / D.Hq;
+  r.active = !(seq_mask && !seq_mask[r.b]);
+  r.L = seq_len_clamped(seq_lens, r.b, D);
+  r.np = n_pages_of(r.L, D.P);
+  r.nch = (r.np + gp.chunk - 1) / gp.chunk;
+  return r;
+}
+
+// ---------------------------------------------------------------- K1: brackets
+__global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussParams gp, GaussConsts gc,
+                                                                  const float *__restrict__ box,
+                                                                  const float *__restrict__ mu,
+                                                                  const float *__restrict__ var,
+                                                                  const int32_t *__restrict__ seq_lens,
+                                                                  const uint8_t *__restrict__ seq_mask,
+                                                                  GaussWs ws) {
+  __shared__ double red[kGThreads / kWave];
+  const int chunk = blockIdx.x;
+  const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
+  if (!rc.active) return;
+  if (chunk == 0 && threadIdx.x == 0) {
+    ws.inbin_cnt[rc.row] = 0;
+    ws.ctr[rc.row * 2 + 0] = 0;
+    ws.ctr[rc.row * 2 + 1] = 0;
+  }
+  if (chunk >= rc.nch && chunk > 0) return;
+  const size_t base = (size_t)rc.row * D.max_pages;
+  const double sqrt2 = 1.4142135623730951;
+  double lo_c = -INFINITY, top = -INFINITY;
+  const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  for (int p = chunk * gp.chunk + threadIdx.x; p < p_end; p += kGThreads) {
+    const float bx = box[base + p], m = mu[base + p], v = var[base + p];
+    if (!page_valid(bx, m, v)) continue;
+    const int n = min(D.P, rc.L - p * D.P);
+    const double sig = sqrt(v > 0.0f ? (double)v : 0.0);
+    lo_c = fmax(lo_c, gp.a * (double)m - pow(2.5 / (double)n, gp.a));
+    top = fmax(top, gp.a * ((double)m + sqrt2 * sig * gc.x[15]));
+  }
+  lo_c = block_max(lo_c, red);
+  top = block_max(top, red);
+  if (threadIdx.x == 0) {
+    ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = lo_c;
+    ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1] = top;
+  }
+}
+
+__device__ __forceinline__ void row_bracket(const GaussParams &gp, const GaussWs &ws, const RowCtx &rc,
+                                            double &lo, double &hi) {
+  lo = -INFINITY;
+  hi = -INFINITY;
+  const int n = rc.nch > 0 ? rc.nch : 1;
+  for (int c = 0; c < n; ++c) {
+    lo = fmax(lo, ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 0]);
+    hi = fmax(hi, ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 1]);
+  }
+  if (hi > -INFINITY && !(hi > lo)) hi = lo + fmax(1e-300, fabs(lo) * 1e-15);
+}
+
+// ------------------------------------------------------------- K2: histograms
+__global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussParams gp, GaussConsts gc,
+                                                               const float *__restrict__ mu,
+                                                               const float *__restrict__ var,
+                                                               const float *__restrict__ box,
+                                                               const int32_t *__restrict__ seq_lens,
+                                                               const uint8_t *__restrict__ seq_mask,
+                                                               GaussWs ws) {
+  __shared__ double h0[kNB], h1[kNB], h2[kNB];
+  __shared__ double s0[kNB], s1[kNB], s2[kNB];
+  __shared__ int s_last, s_best;
+  const int chunk = blockIdx.x;
+  const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
+  if (!rc.active || chunk >= rc.nch) return;
+  double lo, hi;
+  row_bracket(gp, ws, rc, lo, hi);
+  if (!(hi > -INFINITY)) return;  // no valid page in the row
+  const double w = (hi - lo) / kNB;
+  const double sqrt2 = 1.4142135623730951;
+  for (int i = threadIdx.x; i < kNB; i += kGThreads) h0[i] = h1[i] = h2[i] = 0.0;
+  __syncthreads();
+  const size_t base = (size_t)rc.row * D.max_pages;
+  const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  for (int p = chunk * gp.chunk + threadIdx.x; p < p_end; p += kGThreads) {
+    const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
+    if (!page_valid(bx, m, v2)) continue;
+    const double n = (double)min(D.P, rc.L - p * D.P);
+    const double sig = sqrt(v2 > 0.0f ? (double)v2 : 0.0);
+    for (int j = 15; j >= 0; --j) {
+      const double v = gp.a * ((double)m + sqrt2 * sig * gc.x[j]);
+      if (!(v > lo)) break;  // nodes ascend in j
+      const int bn = bin_of(v, lo, w);
+      const double e = v - bin_edge(lo, w, bn);
+      const double c = n * gc.w[j];
+      atomicAdd(&h0[bn], c);
+      atomicAdd(&h1[bn], c * e);
+      if (gp.ibeta == 2) atomicAdd(&h2[bn], c * e * e);
+    }
+  }
+  __syncthreads();
+  double *hc = ws.hist + ((size_t)rc.row * gp.nchunk + chunk) * kNB * 3;
+  for (int i = threadIdx.x; i < kNB; i += kGThreads) {
+    hc[i * 3 + 0] = h0[i];
+    hc[i * 3 + 1] = h1[i];
+    hc[i * 3 + 2] = h2[i];
+  }
+  if (!arrive_last(&ws.ctr[rc.row * 2 + 0], (unsigned)rc.nch, &s_last)) return;
+
+  // ---- last block of the row: merge chunks in order, suffix-scan the moments
+  for (int i = threadIdx.x; i < kNB; i += kGThreads) {
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0;
+    for (int c = 0; c < rc.nch; ++c) {
+      const double *hh = ws.hist + ((size_t)rc.row * gp.nchunk + c) * kNB * 3 + i * 3;
+      a0 += hh[0];
+      a1 += hh[1];
+      a2 += hh[2];
+    }
+    s0[i] = a0;
+    s1[i] = a1;
+    s2[i] = a2;
+  }
+  __syncthreads();
+  // inclusive suffix scan: S_b = m_b (+) shift(S_{b+d}, e_{b+d} -> e_b)
+  for (int dist = 1; dist < kNB; dist <<= 1) {
+    double n0 = 0, n1 = 0, n2 = 0;
+    const int i = threadIdx.x;
+    const bool has = i < kNB && i + dist < kNB;
+    if (i < kNB) {
+      n0 = s0[i]; n1 = s1[i]; n2 = s2[i];
+      if (has) {
+        const double Dd = bin_edge(lo, w, i + dist) - bin_edge(lo, w, i);
+        const double t0 = s0[i + dist], t1 = s1[i + dist], t2 = s2[i + dist];
+        n0 += t0;
+        n1 += t1 + Dd * t0;
+        n2 += t2 + 2.0 * Dd * t1 + Dd * Dd * t0;
+      }
+    }
+    __syncthreads();
+    if (i < kNB) { s0[i] = n0; s1[i] = n1; s2[i] = n2; }
+    __syncthreads();
+  }
+  // F(e_b) = s2[b] (beta 2) or s1[b] (beta 1); root bin = largest b with F >= 1
+  if (threadIdx.x == 0) s_best = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kNB; i += kGThreads) {
+    const double F = gp.ibeta == 2 ? s2[i] : s1[i];
+    if (F >= 1.0) atomicMax(&s_best, i);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int k = s_best;
+    double *ri = ws.rowinfo + (size_t)rc.row * 8;
+    ri[0] = (double)k;
+    ri[1] = lo;
+    ri[2] = w;
+    // moments of the bins above k, about e_{k+1}
+    ri[3] = k + 1 < kNB ? s0[k + 1] : 0.0;
+    ri[4] = k + 1 < kNB ? s1[k + 1] : 0.0;
+    ri[5] = k + 1 < kNB ? s2[k + 1] : 0.0;
+  }
+}
+
+// --------------------------------------- K3: collect, classify, solve, compact
+__global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
+    Dims D, GaussParams gp, GaussConsts gc, const float *__restrict__ box, const float *__restrict__ mu,
+    const float *__restrict__ var, const int32_t *__restrict__ seq_lens,
+    const uint8_t *__restrict__ seq_mask, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_cnt,
+    double *__restrict__ tau_hat, GaussWs ws) {
+  __shared__ int scan_scratch[kGThreads / kWave];
+  __shared__ double dred[kGThreads / kWave];
+  __shared__ double s_best_est;
+  __shared__ int s_best_p, s_last;
+  const int chunk = blockIdx.x;
+  const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
+  if (!rc.active) return;
+  double lo, hi;
+  row_bracket(gp, ws, rc, lo, hi);
+  const size_t base = (size_t)rc.row * D.max_pages;
+  if (!(hi > -INFINITY)) {  // no pages (or none valid): empty selection
+    if (chunk == 0 && threadIdx.x == 0) {
+      sel_cnt[rc.row] = 0;
+      if (tau_hat) tau_hat[rc.row] = NAN;
+    }
+    return;
+  }
+  if (chunk >= rc.nch) return;
+  const double *ri = ws.rowinfo + (size_t)rc.row * 8;
+  const int k = (int)ri[0];
+  const double w = ri[2];
+  const double ek = bin_edge(lo, w, k), ek1 = bin_edge(lo, w, k + 1);
+  const double thr_lo = ek / gp.a - gp.delta, thr_hi = ek1 / gp.a - gp.delta;
+  const double sqrt2 = 1.4142135623730951;
+
+  // ---- collect in-bin points and classify this chunk's pages (ascending order)
+  const int p_begin = chunk * gp.chunk, p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  int listed = 0;
+  double best = -INFINITY;
+  int bestp = 0x7FFFFFFF;
+  for (int pb = p_begin; pb < p_end; pb += kGThreads) {
+    const int p = pb + threadIdx.x;
+    int code = -1;
+    if (p < p_end) {
+      const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
+      if (page_valid(bx, m, v2)) {
+        const double n = (double)min(D.P, rc.L - p * D.P);
+        const double s2d = v2 > 0.0f ? (double)v2 : 0.0;
+        const double sig = sqrt(s2d);
+        for (int j = 15; j >= 0; --j) {
+          const double v = gp.a * ((double)m + sqrt2 * sig * gc.x[j]);
+          if (!(v > lo)) break;
+          if (bin_of(v, lo, w) == k) {
+            const int slot = atomicAdd(&ws.inbin_cnt[rc.row], 1);
+            if (slot < gp.cap) {
+              ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0] = v;
+              ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1] = n * gc.w[j];
+            }
+          }
+        }
+        if (keep_at(thr_hi, bx, m, s2d, gp.nsig)) code = p;
+        else if (keep_at(thr_lo, bx, m, s2d, gp.nsig)) code = p | (int)0x80000000;
+        const double e1 = (double)m + gp.nsig * sig;
+        const double est = e1 < (double)bx ? e1 : (double)bx;
+        if (est > best || (est == best && p < bestp)) { best = est; bestp = p; }
+      }
+    }
+    int tot;
+    const int pos = block_excl_scan(code != -1 ? 1 : 0, scan_scratch, &tot);
+    if (code != -1) ws.list[base + p_begin + listed + pos] = code;
+    listed += tot;
+  }
+  // chunk argmax of the estimate (lowest page on ties)
+  {
+    double bm = block_max(best, dred);
+    int cand = (best == bm) ? bestp : 0x7FFFFFFF;
+    __syncthreads();
+    if (threadIdx.x == 0) s_best_p = 0x7FFFFFFF;
+    __syncthreads();
+    if (cand != 0x7FFFFFFF) atomicMin(&s_best_p, cand);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = bm;
+      ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1] = (double)s_best_p;
+      ws.list_cnt[(size_t)rc.row * gp.nchunk + chunk] = listed;
+    }
+  }
+  if (!arrive_last(&ws.ctr[rc.row * 2 + 1], (unsigned)rc.nch, &s_last)) return;
+
+  // ---- last block of the row: solve F(t) = 1 inside [ek, ek1]
+  const int nin = min(ws.inbin_cnt[rc.row], gp.cap);
+  const double T0 = ri[3], T1 = ri[4], T2 = ri[5];
+  double t = ek;
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0;
+    for (int i = threadIdx.x; i < nin; i += kGThreads) {
+      const double v = ws.inbin[((size_t)rc.row * gp.cap + i) * 2 + 0];
+      const double c = ws.inbin[((size_t)rc.row * gp.cap + i) * 2 + 1];
+      const double x = v - t;
+      if (x > 0.0) {
+        if (gp.ibeta == 2) { f += c * x * x; fp += 2.0 * c * x; }
+        else { f += c * x; fp += c; }
+      }
+    }
+    f = block_sum(f, dred);
+    fp = block_sum(fp, dred);
+    const double Dd = ek1 - t;  // >= 0
+    if (gp.ibeta == 2) { f += T2 + 2.0 * Dd * T1 + Dd * Dd * T0; fp += 2.0 * T1 + 2.0 * Dd * T0; }
+    else { f += T1 + Dd * T0; fp += T0; }
+    if (!(fp > 0.0)) break;
+    double tn = t + (f - 1.0) / fp;
+    if (tn > ek1) tn = ek1;
+    if (!(tn > t)) break;  // converged from the left (or rounding stalls)
+    t = tn;
+  }
+  const double tau = t;
+  if (threadIdx.x == 0) {
+    if (tau_hat) tau_hat[rc.row] = tau / gp.a;
+    ws.inbin_cnt[rc.row] = 0;
+  }
+  const double thr = tau / gp.a - gp.delta;
+
+  // ---- settle undecided pages and write the ascending list
+  int total = 0;
+  for (int c = 0; c < rc.nch; ++c) {
+    const int cnt = ws.list_cnt[(size_t)rc.row * gp.nchunk + c];
+    const int seg = c * gp.chunk;
+    for (int i0 = 0; i0 < cnt; i0 += kGThreads) {
+      const int i = i0 + threadIdx.x;
+      int take = 0, p = 0;
+      if (i < cnt) {
+        const int code = ws.list[base + seg + i];
+        p = code & 0x7FFFFFFF;
+        if (code >= 0) take = 1;
+        else {
+          const float m = mu[base + p], v2 = var[base + p];
+          take = keep_at(thr, (double)box[base + p], (double)m, v2 > 0.0f ? (double)v2 : 0.0, gp.nsig) ? 1 : 0;
+        }
+      }
+      int tot;
+      const int pos = block_excl_scan(take, scan_scratch, &tot);
+      if (take) sel_idx[base + total + pos] = p;
+      total += tot;
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (total == 0) {
+      double be = -INFINITY;
+      int bp = 0x7FFFFFFF;
+      for (int c = 0; c < rc.nch; ++c) {
+        const double e = ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 0];
+        const int p = (int)ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 1];
+        if (p == 0x7FFFFFFF) continue;
+        if (bp == 0x7FFFFFFF || e > be) { be = e; bp = p; }
+      }
+      sel_idx[base] = bp;
+      total = 1;
+    }
+    sel_cnt[rc.row] = total;
+  }
+}
+
+// ---------------------------------------------- generic alpha: one block / row
+constexpr int kGenThreads = 1024;
+__global__ __launch_bounds__(kGenThreads) void gauss_generic_kernel(
+    Dims D, GaussParams gp, GaussConsts gc, const float *__restrict__ box, const float *__restrict__ mu,
+    const float *__restrict__ var, const int32_t *__restrict__ seq_lens,
+    const uint8_t *__restrict__ seq_mask, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_cnt,
+    double *__restrict__ tau_hat) {
+  __shared__ double dred[kGenThreads / kWave];
+  __shared__ int scan_scratch[kGenThreads / kWave];
+  __shared__ int s_best_p;
+  const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.x);
+  if (!rc.active) return;
+  const size_t base = (size_t)rc.row * D.max_pages;
+  const double sqrt2 = 1.4142135623730951;
+  double mumax = -INFINITY, top = -INFINITY;
+  for (int p = threadIdx.x; p < rc.np; p += kGenThreads) {
+    const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
+    if (!page_valid(bx, m, v2)) continue;
+    mumax = fmax(mumax, (double)m);
+    top = fmax(top, gp.a * ((double)m + sqrt2 * sqrt(v2 > 0.0f ? (double)v2 : 0.0) * gc.x[15]));
+  }
+  mumax = block_max(mumax, dred);
+  top = block_max(top, dred);
+  if (!(top > -INFINITY)) {
+    if (threadIdx.x == 0) {
+      sel_cnt[rc.row] = 0;
+      if (tau_hat) tau_hat[rc.row] = NAN;
+    }
+    return;
+  }
+  auto F = [&](double t) {
+    double f = 0.0;
+    for (int p = threadIdx.x; p < rc.np; p += kGenThreads) {
+      const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
+      if (!page_valid(bx, m, v2)) continue;
+      const double n = (double)min(D.P, rc.L - p * D.P);
+      const double sig = sqrt(v2 > 0.0f ? (double)v2 : 0.0);
+      double inner = 0.0;
+      for (int j = 0; j < 16; ++j) {
+        const double x = gp.a * ((double)m + sqrt2 * sig * gc.x[j]) - t;
+        if (x > 0.0) inner += gc.w[j] * powb(x, gp.ibeta, gp.beta);
+      }
+      f += n * inner;
+    }
+    return block_sum(f, dred);
+  };
+  double gap = 1.0, lo = gp.a * mumax - gap;
+  while (F(lo) < 1.0) { gap *= 2.0; lo = gp.a * mumax - gap; }
+  double hi = top;
+  for (int it = 0; it < 2100; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (F(mid) >= 1.0) lo = mid; else hi = mid;
+  }
+  if (threadIdx.x == 0 && tau_hat) tau_hat[rc.row] = lo / gp.a;
+  const double thr = lo / gp.a - gp.delta;
+  int total = 0;
+  double best = -INFINITY;
+  int bestp = 0x7FFFFFFF;
+  for (int p0 = 0; p0 < rc.np; p0 += kGenThreads) {
+    const int p = p0 + threadIdx.x;
+    int take = 0;
+    if (p < rc.np) {
+      const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
+      if (page_valid(bx, m, v2)) {
+        const double s2d = v2 > 0.0f ? (double)v2 : 0.0;
+        take = keep_at(thr, bx, m, s2d, gp.nsig) ? 1 : 0;
+        const double e1 = (double)m + gp.nsig * sqrt(s2d);
+        const double est = e1 < (double)bx ? e1 : (double)bx;
+        if (est > best) { best = est; bestp = p; }
+      }
+    }
+    int tot;
+    const int pos = block_excl_scan(take, scan_scratch, &tot);
+    if (take) sel_idx[base + total + pos] = p;
+    total += tot;
+  }
+  const double bm = block_max(best, dred);
+  if (threadIdx.x == 0) s_best_p = 0x7FFFFFFF;
+  __syncthreads();
+  if (best == bm && bestp != 0x7FFFFFFF) atomicMin(&s_best_p, bestp);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (total == 0) {
+      sel_idx[base] = s_best_p;
+      total = 1;
+    }
+    sel_cnt[rc.row] = total;
+  }
+}
+
+// ----------------------------------------------------------------------- host
+static GaussParams make_params(const Dims &D, double alpha, double delta, double n_sigma) {
+  GaussParams gp;
+  gp.a = alpha - 1.0;
+  gp.beta = 1.0 / gp.a;
+  gp.delta = delta;
+  gp.nsig = n_sigma;
+  gp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
+  const int rows = D.B * D.Hq;
+  // enough chunks to give the GPU ~512 blocks, at least 256 pages per chunk
+  int want = (512 + rows - 1) / rows;
+  int chunk = (D.max_pages + want - 1) / want;
+  chunk = ((chunk + 255) / 256) * 256;
+  if (chunk < 256) chunk = 256;
+  gp.chunk = chunk;
+  gp.nchunk = (D.max_pages + chunk - 1) / chunk;
+  gp.cap = 16 * D.max_pages;
+  return gp;
+}
+
+static GaussWs carve_gauss(const Dims &D, const GaussParams &gp, void *base, size_t *bytes) {
+  Carve cv(base);
+  const size_t rows = (size_t)D.B * D.Hq;
+  GaussWs w;
+  w.part = cv.take<double>(rows * gp.nchunk * 2);
+  w.hist = cv.take<double>(rows * gp.nchunk * kNB * 3);
+  w.rowinfo = cv.take<double>(rows * 8);
+  w.inbin = cv.take<double>(rows * (size_t)gp.cap * 2);
+  w.inbin_cnt = cv.take<int>(rows);
+  w.list = cv.take<int>(rows * (size_t)D.max_pages);
+  w.list_cnt = cv.take<int>(rows * gp.nchunk);
+  w.amax = cv.take<double>(rows * gp.nchunk * 2);
+  w.ctr = cv.take<unsigned int>(rows * 2);
+  if (bytes) *bytes = cv.bytes();
+  return w;
+}
+
+size_t gauss_ws_bytes(const Dims &D) {
+  GaussParams gp = make_params(D, 1.5, 0.0, 3.0);
+  size_t bytes = 0;
+  carve_gauss(D, gp, nullptr, &bytes);
+  return bytes;
+}
+
+hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const float *var,
+                        const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                        double *tau_hat, void *ws, hipStream_t s) {
+  const GaussParams gp = make_params(D, alpha, delta, n_sigma);
+  const GaussConsts &gc = gauss_consts();
+  const int rows = D.B * D.Hq;
+  if (gp.ibeta == 0) {
+    hipLaunchKernelGGL(gauss_generic_kernel, dim3(rows), dim3(kGenThreads), 0, s, D, gp, gc, box, mu,
+                       var, seq_lens, seq_mask, sel_idx, sel_cnt, tau_hat);
+    return hipGetLastError();
+  }
+  GaussWs w = carve_gauss(D, gp, ws, nullptr);
+  dim3 grid(gp.nchunk, rows);
+  hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var,
+                     seq_lens, seq_mask, w);
+  hipLaunchKernelGGL(gauss_hist_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, mu, var, box, seq_lens,
+                     seq_mask, w);
+  hipLaunchKernelGGL(gauss_select_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var,
+                     seq_lens, seq_mask, sel_idx, sel_cnt, tau_hat, w);
+  return hipGetLastError();
+}
+
+}  // namespace ekv

@@ -1,0 +1,297 @@
+// softmax.hip -- full-cache softmax decode, the baseline the EntmaxKV summary
+// measures its speedups against ("Resumen Tecnico: EntmaxKV ...", gist.science/
+// es/paper/2605.21649, section 4, efficiency): exact softmax attention over every
+// cached token with the same score scale.
+//
+// The whole K and V cache is streamed once, so the kernel is bound by HBM.
+// Design (split-K, one pass):
+//  * a block owns a KV head g of sequence b and a contiguous range of pages; all
+//    G query heads of the group are served from the same K/V bytes;
+//  * thread (token slot j, coordinate slice) loads its slice of K and V for slot j
+//    of every page straight into registers (coalesced 16-byte loads, prefetched
+//    one page ahead), so the main loop touches no LDS and has no barriers;
+//  * each thread keeps a running softmax (max, sum, weighted V slice) per head
+//    over "its" tokens and rescales only when its max grows;
+//  * the running states are merged across slots (shuffles, then LDS), written per
+//    range, and the last block of (b, g) merges the ranges in order.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ekv {
+
+constexpr int kSThreads = 256;
+
+struct SoftmaxWs {
+  float *part;              // [B][Hq][S][DIM + 2]  (m, l, acc[DIM])
+  unsigned long long *ctr;  // [B][Hkv]
+  unsigned long long epoch;
+  int S;                    // ranges per (b, g)
+  int pps;                  // pages per range
+};
+
+template <typename T, int DIM, int P, int G>
+__global__ __launch_bounds__(kSThreads) void softmax_decode_kernel(
+    Dims D, const T *__restrict__ q, const T *__restrict__ k_pool, const T *__restrict__ v_pool,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, float *__restrict__ out,
+    float *__restrict__ lse, SoftmaxWs ws) {
+  constexpr int kParts = kSThreads / P;        // threads per token slot
+  constexpr int kPer = DIM / kParts;           // coordinates per thread
+  static_assert(kPer >= 2 && kPer % 2 == 0, "slice must hold bf16 pairs");
+  constexpr int kWords = kPer * (int)sizeof(T) / 4;  // 32-bit words per slice
+  __shared__ float xch[kSThreads / kWave][kParts][G][DIM / kParts + 2];
+  __shared__ int s_last;
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int slot = tid / kParts, part = tid % kParts;
+  const int L = seq_len_clamped(seq_lens, b, D);
+  const int np = n_pages_of(L, P);
+  const int p_begin = s * ws.pps, p_end = min(np, (s + 1) * ws.pps);
+
+  float qv[G][kPer];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      qv[h][e] = load_f<T>(q, ((size_t)b * D.Hq + g * G + h) * DIM + part * kPer + e) * (float)D.scale;
+
+  float m[G], l[G], acc[G][kPer];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc[h][e] = 0.0f;
+  }
+
+  auto slice_ptr = [&](const T *pool, int p) -> const uint32_t * {
+    const int phys = page_table[(size_t)b * D.max_pages + p];
+    return reinterpret_cast<const uint32_t *>(pool + (((size_t)phys * D.Hkv + g) * P + slot) * DIM + part * kPer);
+  };
+  auto page_ok = [&](int p) {
+    const int phys = page_table[(size_t)b * D.max_pages + p];
+    return phys >= 0 && phys < D.num_phys;
+  };
+
+  bool bad = false;
+  uint32_t kw[kWords], vw[kWords];
+  int p = p_begin;
+  bool have = p < p_end && page_ok(p) && slot < min(P, L - p * P);
+  if (p < p_end && !page_ok(p)) bad = true;
+  if (have) {
+    const uint32_t *kp = slice_ptr(k_pool, p), *vp = slice_ptr(v_pool, p);
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) { kw[w] = kp[w]; vw[w] = vp[w]; }
+  }
+  for (; p < p_end; ++p) {
+    // prefetch the next page's slices
+    uint32_t nk[kWords], nv[kWords];
+    const int pn = p + 1;
+    bool have_n = false;
+    if (pn < p_end) {
+      if (!page_ok(pn)) bad = true;
+      else if (slot < min(P, L - pn * P)) {
+        have_n = true;
+        const uint32_t *kp = slice_ptr(k_pool, pn), *vp = slice_ptr(v_pool, pn);
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) { nk[w] = kp[w]; nv[w] = vp[w]; }
+      }
+    }
+    if (have) {
+      float kf[kPer], vf[kPer];
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        if constexpr (sizeof(T) == 2) {
+          kf[2 * w] = bf16lo(kw[w]); kf[2 * w + 1] = bf16hi(kw[w]);
+          vf[2 * w] = bf16lo(vw[w]); vf[2 * w + 1] = bf16hi(vw[w]);
+        } else {
+          kf[w] = __uint_as_float(kw[w]);
+          vf[w] = __uint_as_float(vw[w]);
+        }
+      }
+      float sc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a = __builtin_fmaf(qv[h][e], kf[e], a);
+        sc[h] = a;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {  // full score of the token: sum over the slot's parts
+#pragma unroll
+        for (int o = kParts / 2; o > 0; o >>= 1) sc[h] += __shfl_xor(sc[h], o, kWave);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (sc[h] > m[h]) {
+          const float r = __expf(m[h] - sc[h]);
+          l[h] *= r;
+#pragma unroll
+          for (int e = 0; e < kPer; ++e) acc[h][e] *= r;
+          m[h] = sc[h];
+        }
+        const float pw = __expf(sc[h] - m[h]);
+        l[h] += pw;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[h][e] = __builtin_fmaf(pw, vf[e], acc[h][e]);
+      }
+    }
+    have = have_n;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) { kw[w] = nk[w]; vw[w] = nv[w]; }
+  }
+
+  // ---- merge the running states of the slots: within the wave (same part) ...
+  constexpr int kSlotsPerWave = kWave / kParts;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int o = kParts; o < kWave; o <<= 1) {
+      const float mo = __shfl_xor(m[h], o, kWave), lo = __shfl_xor(l[h], o, kWave);
+      const float mn = fmaxf(m[h], mo);
+      const float ra = mn == -INFINITY ? 0.0f : __expf(m[h] - mn);
+      const float rb = mn == -INFINITY ? 0.0f : __expf(mo - mn);
+      l[h] = l[h] * ra + lo * rb;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const float ao = __shfl_xor(acc[h][e], o, kWave);
+        acc[h][e] = acc[h][e] * ra + ao * rb;
+      }
+      m[h] = mn;
+    }
+  }
+  (void)kSlotsPerWave;
+  // ... then across the waves through LDS
+  const int wave = tid / kWave, lane = tid % kWave;
+  if (lane < kParts) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      xch[wave][part][h][0] = m[h];
+      xch[wave][part][h][1] = l[h];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) xch[wave][part][h][2 + e] = acc[h][e];
+    }
+  }
+  __syncthreads();
+  constexpr int kNW = kSThreads / kWave;
+  float *dst = ws.part;
+  for (int idx = tid; idx < G * DIM; idx += kSThreads) {
+    const int h = idx / DIM, i = idx % DIM;
+    const int pr = i / kPer, e = i % kPer;
+    float mm = -INFINITY;
+    for (int w = 0; w < kNW; ++w) mm = fmaxf(mm, xch[w][pr][h][0]);
+    float ll = 0.0f, aa = 0.0f;
+    for (int w = 0; w < kNW; ++w) {
+      const float r = mm == -INFINITY ? 0.0f : __expf(xch[w][pr][h][0] - mm);
+      ll += xch[w][pr][h][1] * r;
+      aa += xch[w][pr][h][2 + e] * r;
+    }
+    float *rec = dst + (((size_t)b * D.Hq + g * G + h) * ws.S + s) * (DIM + 2);
+    rec[2 + i] = aa;
+    if (i == 0) { rec[0] = mm; rec[1] = ll; }
+  }
+  if (bad) {
+    if (tid == 0) {  // poison this range: the merged row becomes NaN
+      for (int h = 0; h < G; ++h) dst[(((size_t)b * D.Hq + g * G + h) * ws.S + s) * (DIM + 2) + 1] = NAN;
+    }
+  }
+  if (!arrive_last_ep(&ws.ctr[(size_t)b * D.Hkv + g], ws.epoch, (unsigned)ws.S, &s_last)) return;
+
+  // ---- last block of (b, g): merge the ranges in order
+  for (int idx = tid; idx < G * DIM; idx += kSThreads) {
+    const int h = idx / DIM, i = idx % DIM;
+    const float *rec0 = dst + (((size_t)b * D.Hq + g * G + h) * ws.S) * (DIM + 2);
+    float mm = -INFINITY;
+    for (int r = 0; r < ws.S; ++r) mm = fmaxf(mm, rec0[(size_t)r * (DIM + 2)]);
+    float ll = 0.0f, aa = 0.0f;
+    for (int r = 0; r < ws.S; ++r) {
+      const float *rec = rec0 + (size_t)r * (DIM + 2);
+      const float lr = rec[1];
+      if (lr != lr) { ll = NAN; break; }
+      if (rec[0] == -INFINITY) continue;
+      const float f = __expf(rec[0] - mm);
+      ll += lr * f;
+      aa += rec[2 + i] * f;
+    }
+    const size_t o = ((size_t)b * D.Hq + g * G + h) * DIM + i;
+    if (ll != ll) out[o] = NAN;
+    else out[o] = ll > 0.0f ? aa / ll : 0.0f;
+    if (i == 0 && lse) {
+      const size_t ro = (size_t)b * D.Hq + g * G + h;
+      lse[ro] = (ll != ll) ? NAN : (ll > 0.0f ? mm + logf(ll) : -INFINITY);
+    }
+  }
+}
+
+static SoftmaxWs carve_softmax(const Dims &D, void *base, size_t *bytes) {
+  SoftmaxWs w;
+  const int bg = D.B * D.Hkv;
+  int S = (1024 + bg - 1) / bg;
+  const int maxS = (D.max_pages + 7) / 8;  // at least 8 pages per range
+  if (S > maxS) S = maxS;
+  if (S < 1) S = 1;
+  w.S = S;
+  w.pps = (D.max_pages + S - 1) / S;
+  Carve cv(base);
+  w.part = cv.take<float>((size_t)D.B * D.Hq * S * (D.d + 2));
+  w.ctr = cv.take<unsigned long long>((size_t)bg);
+  w.epoch = 0;
+  if (bytes) *bytes = cv.bytes();
+  return w;
+}
+
+size_t softmax_ws_bytes(const Dims &D) {
+  size_t b = 0;
+  carve_softmax(D, nullptr, &b);
+  return b;
+}
+
+template <typename T, int DIM, int P, int G>
+static hipError_t launch_sm(const Dims &D, const void *q, const void *k, const void *v, const int32_t *pt,
+                            const int32_t *sl, float *out, float *lse, SoftmaxWs w, hipStream_t s) {
+  dim3 grid(w.S, D.Hkv, D.B);
+  hipLaunchKernelGGL((softmax_decode_kernel<T, DIM, P, G>), grid, dim3(kSThreads), 0, s, D, (const T *)q,
+                     (const T *)k, (const T *)v, pt, sl, out, lse, w);
+  return hipGetLastError();
+}
+
+template <typename T, int DIM, int P>
+static hipError_t launch_sm_g(const Dims &D, const void *q, const void *k, const void *v, const int32_t *pt,
+                              const int32_t *sl, float *out, float *lse, SoftmaxWs w, hipStream_t s) {
+  switch (D.G) {
+    case 1: return launch_sm<T, DIM, P, 1>(D, q, k, v, pt, sl, out, lse, w, s);
+    case 2: return launch_sm<T, DIM, P, 2>(D, q, k, v, pt, sl, out, lse, w, s);
+    case 4: return launch_sm<T, DIM, P, 4>(D, q, k, v, pt, sl, out, lse, w, s);
+    case 8: return launch_sm<T, DIM, P, 8>(D, q, k, v, pt, sl, out, lse, w, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DIM>
+static hipError_t launch_sm_p(const Dims &D, const void *q, const void *k, const void *v, const int32_t *pt,
+                              const int32_t *sl, float *out, float *lse, SoftmaxWs w, hipStream_t s) {
+  switch (D.P) {
+    case 16: return launch_sm_g<T, DIM, 16>(D, q, k, v, pt, sl, out, lse, w, s);
+    case 32: return launch_sm_g<T, DIM, 32>(D, q, k, v, pt, sl, out, lse, w, s);
+    case 64: return launch_sm_g<T, DIM, 64>(D, q, k, v, pt, sl, out, lse, w, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_softmax(const Dims &D, int dtype, const void *q, const void *k_pool,
+                          const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                          float *out, float *lse, void *ws, hipStream_t s) {
+  SoftmaxWs w = carve_softmax(D, ws, nullptr);
+  w.epoch = next_epoch();
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64) return launch_sm_p<uint16_t, 64>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
+    return launch_sm_p<uint16_t, 128>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
+  }
+  if (D.d == 64) return launch_sm_p<float, 64>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
+  return launch_sm_p<float, 128>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
+}
+
+}  // namespace ekv

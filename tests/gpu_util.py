@@ -1,0 +1,99 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+HIP library through its binding, and compare with the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import sparse_decode_attention_page_amd as E
+from sparse_decode_attention_page_amd import synth
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev(a, kind):
+    """numpy -> device tensor; kind in {"kv_bf16", "kv_f32", "i32", "u8", "f32", "f64"}."""
+    t = torch()
+    a = np.ascontiguousarray(a)
+    if kind == "kv_bf16":
+        return t.from_numpy(a.view(np.int16)).view(t.bfloat16).cuda()
+    if kind == "kv_f32":
+        return t.from_numpy(a.astype(np.float32)).cuda()
+    if kind == "i32":
+        return t.from_numpy(a.astype(np.int32)).cuda()
+    if kind == "u8":
+        return t.from_numpy(a.astype(np.uint8)).cuda()
+    if kind == "f32":
+        return t.from_numpy(a.astype(np.float32)).cuda()
+    return t.from_numpy(a.astype(np.float64)).cuda()
+
+
+def host_raw(x, dtype):
+    """device KV-dtype tensor -> numpy raw storage (uint16 bits for bf16)."""
+    t = torch()
+    if dtype == "bf16":
+        return x.view(t.int16).cpu().numpy().view(np.uint16)
+    return x.cpu().numpy()
+
+
+class Dev:
+    """Device copy of a synth.Inputs instance."""
+
+    def __init__(self, inp: synth.Inputs, scale=0.0):
+        t = torch()
+        self.inp = inp
+        kind = "kv_bf16" if inp.dtype == "bf16" else "kv_f32"
+        self.kind = kind
+        self.q = dev(inp.q, kind)
+        self.k = dev(inp.k_pool, kind)
+        self.v = dev(inp.v_pool, kind)
+        self.pt = dev(inp.page_table, "i32")
+        self.sl = dev(inp.seq_lens, "i32")
+        self.shape = E.make_shape(self.q, self.k, self.pt, scale)
+        self.oshape = oracle.Shape(inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys,
+                                   inp.dtype, scale)
+        self.kv_dtype = t.bfloat16 if inp.dtype == "bf16" else t.float32
+
+    def zeros_meta(self):
+        t = torch()
+        i = self.inp
+        return t.zeros((i.num_phys, i.Hkv, 4, i.d), dtype=self.kv_dtype, device="cuda")
+
+    def per_page(self, fill=np.nan, dtype=None):
+        t = torch()
+        i = self.inp
+        return t.full((i.B, i.Hq, i.max_pages), fill, dtype=dtype or t.float32, device="cuda")
+
+    def sel_buffers(self):
+        t = torch()
+        i = self.inp
+        return (t.full((i.B, i.Hq, i.max_pages), -1, dtype=t.int32, device="cuda"),
+                t.full((i.B, i.Hq), -1, dtype=t.int32, device="cuda"))
+
+
+def rel_l2_rows(a, b):
+    """max over rows of ||a - b|| / ||b|| (rows = all but the last axis)."""
+    a = np.asarray(a, np.float64).reshape(-1, np.shape(a)[-1])
+    b = np.asarray(b, np.float64).reshape(-1, np.shape(b)[-1])
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return float(np.max(num / den))
+
+
+def sets_equal(sel_a, cnt_a, sel_b, cnt_b, rows=None):
+    """Compare two (sel_idx, sel_cnt) pairs row by row; returns list of mismatching rows."""
+    bad = []
+    B, Hq = cnt_b.shape
+    for b in range(B):
+        for h in range(Hq):
+            r = b * Hq + h
+            if rows is not None and r not in rows:
+                continue
+            ca, cb = int(cnt_a[b, h]), int(cnt_b[b, h])
+            if ca != cb or not np.array_equal(sel_a[b, h, :ca], sel_b[b, h, :cb]):
+                bad.append((b, h, ca, cb))
+    return bad

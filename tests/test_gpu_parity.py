@@ -1,0 +1,165 @@
+"""GPU parity: each C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bars: page metadata, page scores (stored float32 bits), page sets and entmax
+supports are bit-exact; outputs are within 2e-3 relative L2 per row for bf16 KV
+and 1e-5 for fp32 KV (fp32 accumulation of exact fp64-decided weights);
+thresholds agree to 1e-12 relative.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import Dev, host_raw, rel_l2_rows, sets_equal, torch
+from sparse_decode_attention_page_amd import synth
+import sparse_decode_attention_page_amd as E
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+SMALL = [
+    # (seed, B, Hq, Hkv, d, P, dtype, ctx)
+    (0, 2, 4, 2, 64, 16, "bf16", (700, 333)),
+    (1, 1, 8, 2, 128, 32, "bf16", (1500,)),
+    (2, 3, 2, 1, 64, 64, "f32", (4096, 65, 1)),
+    (3, 2, 8, 1, 64, 32, "bf16", (3000, 2017)),
+    (4, 1, 1, 1, 64, 16, "f32", (4096,)),
+]
+
+
+def small(seed, B, Hq, Hkv, d, P, dtype, ctx):
+    return synth.random_small(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, P=P, dtype=dtype, ctx=ctx, planted_per_kv=5)
+
+
+@pytest.fixture(scope="module", params=SMALL, ids=lambda c: f"s{c[0]}_B{c[1]}_H{c[2]}x{c[3]}_d{c[4]}_P{c[5]}_{c[6]}")
+def case(request):
+    inp = small(*request.param)
+    D = Dev(inp)
+    meta_o = oracle.build_page_meta(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens)
+    box_o, mu_o, var_o = oracle.score_pages(D.oshape, inp.q, meta_o, inp.page_table, inp.seq_lens)
+    return inp, D, meta_o, (box_o, mu_o, var_o)
+
+
+def _valid_mask(inp):
+    m = np.zeros((inp.B, inp.Hq, inp.max_pages), bool)
+    for b in range(inp.B):
+        npg = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        m[b, :, :npg] = True
+    return m
+
+
+def test_build_page_meta(case):
+    inp, D, meta_o, _ = case
+    meta = D.zeros_meta()
+    E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta)
+    got = host_raw(meta, inp.dtype)
+    assert np.array_equal(got, meta_o)
+
+
+def test_build_page_meta_append(case):
+    inp, D, meta_o, _ = case
+    t = torch()
+    meta = D.zeros_meta()
+    from_tok = np.maximum(inp.seq_lens - 1, 0).astype(np.int32)  # one new token per sequence
+    E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta, from_token=t.from_numpy(from_tok).cuda())
+    got = host_raw(meta, inp.dtype)
+    want = oracle.build_page_meta(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens, from_token=from_tok,
+                                  meta=np.zeros_like(meta_o))
+    assert np.array_equal(got, want)
+
+
+def test_score_pages(case):
+    inp, D, meta_o, (box_o, mu_o, var_o) = case
+    meta = D.zeros_meta()
+    E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta)
+    box, mu, var = D.per_page(), D.per_page(), D.per_page()
+    E.score_pages(D.shape, D.q, meta, D.pt, D.sl, box, mu, var)
+    m = _valid_mask(inp)
+    for got, want in ((box, box_o), (mu, mu_o), (var, var_o)):
+        g = got.cpu().numpy()
+        assert np.array_equal(g[m].view(np.uint32), want[m].view(np.uint32))
+        assert np.all(np.isnan(g[~m]))  # pages past N_b untouched
+
+
+@pytest.mark.parametrize("k", [1, 3, 17, 1000])
+def test_select_topk(case, k):
+    inp, D, _, (box_o, _, _) = case
+    box = torch().from_numpy(box_o).cuda()
+    sel, cnt = D.sel_buffers()
+    E.select_pages_topk(D.shape, box, D.sl, k, sel, cnt)
+    so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, k)
+    assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+
+
+@pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (2.0, 0.5), (1.5, 0.0), (2.0, 1.5), (1.25, 0.5)])
+def test_select_gauss(case, alpha, delta):
+    inp, D, _, (box_o, mu_o, var_o) = case
+    t = torch()
+    box, mu, var = (t.from_numpy(a).cuda() for a in (box_o, mu_o, var_o))
+    sel, cnt = D.sel_buffers()
+    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    E.select_pages_gauss(D.shape, box, mu, var, D.sl, alpha, delta, sel, cnt, tau_hat=tau)
+    so, co, to = oracle.select_gauss(D.oshape, box_o, mu_o, var_o, inp.seq_lens, alpha, delta)
+    assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+    tg = tau.cpu().numpy()
+    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
+
+
+def _decode_check(inp, D, alpha, sel_o, cnt_o, full=False, tau_method=0):
+    t = torch()
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
+    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    w = t.full((inp.B, inp.Hq, inp.max_pages * inp.P), np.nan, dtype=t.float32, device="cuda")
+    if full:
+        E.entmax_decode_full(D.shape, D.q, D.k, D.v, D.pt, D.sl, alpha, out, tau=tau, weights_out=w,
+                             tau_method=tau_method)
+        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
+                                          inp.seq_lens, alpha, want_weights=True)
+    else:
+        E.entmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(sel_o).cuda(),
+                               t.from_numpy(cnt_o).cuda(), alpha, out, tau=tau, weights_out=w,
+                               tau_method=tau_method)
+        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
+                                          inp.seq_lens, alpha, sel_o, cnt_o, want_weights=True)
+    og, tg, wg = out.cpu().numpy(), tau.cpu().numpy(), w.cpu().numpy()
+    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(wg > 0, wo > 0), "support differs"
+    assert np.max(np.abs(wg - wo)) < 1e-5
+    assert rel_l2_rows(og, oo) <= TOL[inp.dtype]
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_entmax_decode_sparse_topk(case, alpha):
+    inp, D, _, (box_o, _, _) = case
+    so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, 7)
+    _decode_check(inp, D, alpha, so, co)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_entmax_decode_sparse_gauss(case, alpha):
+    inp, D, _, (box_o, mu_o, var_o) = case
+    so, co, _ = oracle.select_gauss(D.oshape, box_o, mu_o, var_o, inp.seq_lens, alpha, 0.5)
+    _decode_check(inp, D, alpha, so, co)
+
+
+def test_entmax_decode_sparse_sort_alpha2(case):
+    inp, D, _, (box_o, _, _) = case
+    so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, 9)
+    _decode_check(inp, D, 2.0, so, co, tau_method=1)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_entmax_decode_full(case, alpha):
+    inp, D, _, _ = case
+    _decode_check(inp, D, alpha, None, None, full=True)
+
+
+def test_softmax_decode_full(case):
+    inp, D, _, _ = case
+    t = torch()
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
+    lse = t.full((inp.B, inp.Hq), np.nan, dtype=t.float32, device="cuda")
+    E.softmax_decode_full(D.shape, D.q, D.k, D.v, D.pt, D.sl, out, lse=lse)
+    oo, lo = oracle.softmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens)
+    assert rel_l2_rows(out.cpu().numpy(), oo) <= TOL[inp.dtype]
+    assert np.allclose(lse.cpu().numpy(), lo, rtol=1e-5, atol=1e-5)
