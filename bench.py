@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""EntmaxKV sparse decode benchmark on one MI355X.
+
+One step = one decode step of one layer for the whole batch, inputs resident in
+HBM: score_pages -> select_pages_gauss (or top-k) -> entmax_decode_sparse, all
+through the HIP library (libentmaxkv.so).  Default workload: 1,048,576-token
+context, B=1, 32 query heads over 8 KV heads, d=64, bf16 K/V, pages of 64,
+alpha=1.5, Gaussian selection with Delta=0.5.
+
+The timed loop rotates over R input replicas (metadata, q and K/V pools) so
+that each step reads its bytes from HBM rather than from the 256 MB last-level
+cache.  Steps are replayed from HIP graphs (one per replica) unless --no-graph.
+
+Prints one JSON line (the last line of stdout).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse entmax decode us/step @1M ctx; HBM GB/s (% peak); speedup vs full-cache"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_1m")
+    ap.add_argument("--policy", default="gauss", choices=["gauss", "topk"])
+    ap.add_argument("--replicas", type=int, default=6)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--only", default="", help="profiling aid: 'score', 'step', 'softmax' or 'entmax_full'")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_page_amd as E
+    from sparse_decode_attention_page_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    E.load()
+    wl = synth.WORKLOADS[args.workload]
+    alpha = wl.alphas[0]
+    t0 = time.time()
+    inp = synth.make_device(wl, args.seed)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {wl.name} on device in {time.time() - t0:.1f}s: B={inp.B} Hq={inp.Hq} "
+        f"Hkv={inp.Hkv} d={inp.d} P={inp.P} pages/seq={inp.max_pages}")
+    shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+    B, Hq, Hkv, d, P, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages
+    dev = "cuda"
+
+    # ---- replicas: metadata, q and K/V pools (distinct HBM copies)
+    R = max(1, args.replicas)
+    reps = []
+    meta0 = torch.zeros((inp.num_phys, Hkv, 4, d), dtype=inp.k_pool.dtype, device=dev)
+    E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta0)
+    torch.cuda.synchronize()
+    for r in range(R):
+        if r == 0:
+            reps.append((inp.q, inp.k_pool, inp.v_pool, meta0))
+        else:
+            reps.append((inp.q.clone(), inp.k_pool.clone(), inp.v_pool.clone(), meta0.clone()))
+    torch.cuda.synchronize()
+    log(f"[bench] {R} replicas ready ({R * (2 * inp.k_pool.nbytes + meta0.nbytes) / 2**30:.1f} GiB)")
+
+    box = torch.empty((B, Hq, MP), device=dev)
+    mu = torch.empty_like(box)
+    var = torch.empty_like(box)
+    sel = torch.empty((B, Hq, MP), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), device=dev)
+    ws_s = E.workspace(shape, E.CALL_SCORE)
+    ws_g = E.workspace(shape, E.CALL_GAUSS)
+    ws_t = E.workspace(shape, E.CALL_TOPK)
+    ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE)
+    sl, pt = inp.seq_lens, inp.page_table
+
+    def score(r):
+        q, k, v, meta = reps[r]
+        E.score_pages(shape, q, meta, pt, sl, box, mu, var, ws=ws_s)
+
+    def select():
+        if args.policy == "gauss":
+            E.select_pages_gauss(shape, box, mu, var, sl, alpha, wl.delta, sel, cnt, ws=ws_g)
+        else:
+            E.select_pages_topk(shape, box, sl, wl.topk or 64, sel, cnt, ws=ws_t)
+
+    def decode(r):
+        q, k, v, meta = reps[r]
+        E.entmax_decode_sparse(shape, q, k, v, pt, sl, sel, cnt, alpha, out, ws=ws_d)
+
+    def step(r):
+        score(r)
+        select()
+        decode(r)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def time_calls(fn, n, per_call=True):
+        """Average duration of fn(i) with HIP events on the current stream."""
+        ts = []
+        for i in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn(i)
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3  # us
+
+    # ---- warm up every call once (also builds lazily computed constants)
+    for r in range(R):
+        step(r)
+    torch.cuda.synchronize()
+
+    if args.only == "score":
+        for i in range(args.steps):
+            score(i % R)
+        torch.cuda.synchronize()
+        return
+    if args.only == "step":
+        for i in range(args.steps):
+            step(i % R)
+        torch.cuda.synchronize()
+        return
+
+    # ---- the timed step loop
+    graphs = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for r in range(R):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        step(r)
+                    graphs.append(g)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eager launches
+            log(f"[bench] graph capture failed ({e}); timing eager launches")
+            graphs = None
+
+    def run_step(i):
+        if graphs:
+            graphs[i % R].replay()
+        else:
+            step(i % R)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    for i in range(args.steps):
+        run_step(i)
+    b.record()
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) * 1e3 / args.steps
+    log(f"[bench] step: {step_us:.2f} us ({'graph' if graphs else 'eager'})")
+
+    # ---- per-call breakdown (eager, events around each call, rotating replicas)
+    n = max(3 * R, 12)
+    score_us = time_calls(lambda i: score(i % R), n)
+    sel_us = time_calls(lambda i: select(), n)
+    dec_us = time_calls(lambda i: decode(i % R), n)
+    log(f"[bench] eager per call: score {score_us:.2f} us, select {sel_us:.2f} us, decode {dec_us:.2f} us")
+
+    # ---- algorithmic bytes of the dominant kernel (score_pages)
+    seq = sl.cpu().numpy().astype(np.int64)
+    npg = (seq + P - 1) // P
+    esz = inp.k_pool.element_size()
+    rec = 4 * d * esz
+    # metadata records + q + box/mu/var outputs + page-table entries
+    score_bytes = int(npg.sum() * Hkv * rec + B * Hq * d * esz + Hq * npg.sum() * 12 + npg.sum() * 4)
+    score_gbs = score_bytes / (score_us * 1e-6) / 1e9
+
+    # ---- selection statistics and decode bytes
+    torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy()
+    sel_h = sel.cpu().numpy()
+    union = 0
+    G = Hq // Hkv
+    for bb in range(B):
+        for g in range(Hkv):
+            s_ = set()
+            for h in range(g * G, (g + 1) * G):
+                s_.update(sel_h[bb, h, :cnt_h[bb, h]].tolist())
+            union += len(s_)
+    per_head_pages = int(cnt_h.sum())
+    dec_bytes = per_head_pages * 2 * P * d * esz  # K and V of every kept page (per head)
+    step_bytes = score_bytes + Hq * npg.sum() * 12 + dec_bytes  # + selector reads of box/mu/var
+
+    result = {
+        "metric": METRIC,
+        "value": round(step_us, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{wl.name}: B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, {wl.dtype} K/V, "
+                         f"{int(seq.max())} tokens in pages of {P}; alpha={alpha}, "
+                         + (f"Gaussian selection Delta={wl.delta}" if args.policy == "gauss"
+                            else f"top-k {wl.topk or 64}")),
+            "step": "score_pages + select_pages_" + args.policy + " + entmax_decode_sparse",
+            "replicas": R,
+            "launch": "hip graph replay" if graphs else "eager",
+            "kv_dtype": wl.dtype,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_pages",
+            "achieved": round(score_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes": score_bytes,
+            "launch_us": round(score_us, 3),
+        },
+        "breakdown_us": {"score_pages": round(score_us, 3), "select": round(sel_us, 3),
+                         "entmax_decode_sparse": round(dec_us, 3)},
+        "selection": {"pages_per_head_mean": round(per_head_pages / (B * Hq), 2),
+                      "kv_group_union_pages": union, "pages_per_seq": int(npg.max())},
+        "step_algorithmic_bytes": int(step_bytes),
+        "step_GBps": round(step_bytes / (step_us * 1e-6) / 1e9, 1),
+    }
+
+    # ---- comparators: this build's full-cache softmax and entmax decodes
+    if not args.no_comparators:
+        ws_sm = E.workspace(shape, E.CALL_SOFTMAX)
+        ws_f = E.workspace(shape, E.CALL_DECODE_FULL)
+        out2 = torch.empty_like(out)
+
+        def sm(i):
+            q, k, v, meta = reps[i % R]
+            E.softmax_decode_full(shape, q, k, v, pt, sl, out2, ws=ws_sm)
+
+        def ef(i):
+            q, k, v, meta = reps[i % R]
+            E.entmax_decode_full(shape, q, k, v, pt, sl, alpha, out2, ws=ws_f)
+
+        sm(0)
+        torch.cuda.synchronize()
+        sm_us = time_calls(sm, max(R, 6))
+        t1 = time.time()
+        ef(0)
+        torch.cuda.synchronize()
+        n_ef = 3 if time.time() - t1 < 2.0 else 1
+        ef_us = time_calls(ef, n_ef)
+        kv_bytes = int(npg.sum() * P * Hkv * 2 * d * esz)
+        result["comparators_us"] = {"softmax_decode_full": round(sm_us, 2),
+                                    "entmax_decode_full": round(ef_us, 2),
+                                    "softmax_full_GBps": round(kv_bytes / (sm_us * 1e-6) / 1e9, 1)}
+        result["speedup"] = {"vs_full_softmax": round(sm_us / step_us, 2),
+                             "vs_full_entmax": round(ef_us / step_us, 2)}
+        log(f"[bench] full softmax {sm_us:.1f} us, full entmax {ef_us:.1f} us")
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, shape, wl, alpha, args.policy)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, shape, wl, alpha, policy):
+    """The oracle (plain fp64 C, OpenMP over rows) on the query heads of 2 KV
+    groups of the same workload, scaled to the full step."""
+    import numpy as np
+    import oracle
+
+    G = inp.Hq // inp.Hkv
+    groups = min(2, inp.Hkv)
+    rows = [b * inp.Hq + h for b in range(1) for h in range(groups * G)]
+    osh = oracle.Shape(inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys, inp.dtype)
+    t0 = time.time()
+    k = inp.host("k_pool")
+    v = inp.host("v_pool")
+    q = inp.host("q")
+    pt = inp.page_table.cpu().numpy()
+    sl = inp.seq_lens.cpu().numpy()
+    meta = oracle.build_page_meta(osh, k, pt, sl)
+    log(f"[bench] oracle inputs ready in {time.time() - t0:.1f}s")
+    t1 = time.perf_counter()
+    box, mu, var = oracle.score_pages(osh, q, meta, pt, sl, rows=rows)
+    if policy == "gauss":
+        sel, cnt, _ = oracle.select_gauss(osh, box, mu, var, sl, alpha, wl.delta, rows=rows)
+    else:
+        sel, cnt = oracle.select_topk(osh, box, sl, wl.topk or 64, rows=rows)
+    oracle.entmax_decode(osh, q, k, v, pt, sl, alpha, sel, cnt, rows=rows)
+    dt = time.perf_counter() - t1
+    scale = (inp.B * inp.Hq) / len(rows)
+    threads = min(len(rows), os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    return {"value": round(dt * scale * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {inp.B * inp.Hq} query heads (batch 0, KV heads 0-{groups - 1}), "
+                      f"score+select+sparse decode in {dt:.2f}s, scaled x{scale:g}"}
+
+
+if __name__ == "__main__":
+    main()

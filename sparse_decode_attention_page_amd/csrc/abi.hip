@@ -134,7 +134,7 @@ size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call)
     case ENTMAXKV_CALL_TOPK: return topk_ws_bytes(D);
     case ENTMAXKV_CALL_GAUSS: return gauss_ws_bytes(D);
     case ENTMAXKV_CALL_DECODE_SPARSE: return decode_ws_bytes(D, false);
-    case ENTMAXKV_CALL_DECODE_FULL: return decode_ws_bytes(D, true);
+    case ENTMAXKV_CALL_DECODE_FULL: return full_ws_bytes(D);
     case ENTMAXKV_CALL_SOFTMAX: return softmax_ws_bytes(D);
   }
   return 0;
@@ -221,10 +221,12 @@ static int32_t decode_common(const entmaxkv_shape *shape, const void *q, const v
   if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
-  if ((st = check_ws(decode_ws_bytes(D, full), ws, ws_bytes))) return st;
-  return hip_status(launch_entmax_decode(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens,
-                                         full ? nullptr : sel_idx, full ? nullptr : sel_cnt, alpha,
-                                         tau_method, out, tau, weights_out, ws, stream));
+  if ((st = check_ws(full ? full_ws_bytes(D) : decode_ws_bytes(D, false), ws, ws_bytes))) return st;
+  if (full)  // the sparsemax sort form is a sparse-path option; the full path's root finder is exact
+    return hip_status(launch_entmax_full(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, alpha, out,
+                                         tau, weights_out, ws, stream));
+  return hip_status(launch_entmax_decode(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
+                                         sel_cnt, alpha, tau_method, out, tau, weights_out, ws, stream));
 }
 
 int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,

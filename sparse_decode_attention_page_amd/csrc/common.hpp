@@ -140,11 +140,40 @@ __device__ __forceinline__ int seq_len_clamped(const int32_t *seq_lens, int b, c
 }
 __device__ __forceinline__ int n_pages_of(int L, int P) { return (L + P - 1) / P; }
 
+// Barrier that orders LDS accesses only.  __syncthreads() also waits for every
+// outstanding global load and store (vmcnt(0)), which would drain prefetches
+// that are meant to stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ----------------------------------------------------- cross-block handoff
+// Data one block writes and another block of the SAME launch reads (partials
+// handed to the "last block" of a group) goes through agent-scope relaxed
+// atomic stores/loads.  On gfx950 these are plain sc1 global stores/loads that
+// are coherent across the XCDs' L2 caches, so the handoff needs no
+// __threadfence() -- which here compiles to an L2 write-back plus invalidate
+// per block and costs microseconds.
+template <typename T>
+struct ident { using type = T; };
+template <typename T>
+__device__ __forceinline__ void st_agent(T *p, typename ident<T>::type v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // "last block done" handshake: every block of a group calls this once after
-// writing its results; exactly one block (the last) sees true.  The counter is
-// reset by that block so the workspace can be reused without a memset.
+// handing off its results with st_agent; exactly one block (the last) sees
+// true and may then read them with ld_agent.  Each thread first waits for its
+// own stores to complete; thread 0 then bumps the group counter.  The last
+// block resets the counter so the workspace can be reused without a memset.
 __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int expected, int *flag_smem) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned int prev = atomicAdd(counter, 1u);
@@ -153,9 +182,7 @@ __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int 
     *flag_smem = last ? 1 : 0;
   }
   __syncthreads();
-  bool last = *flag_smem != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag_smem != 0;
 }
 
 // Same handshake for a counter that may hold garbage (a fresh workspace): the
@@ -164,7 +191,7 @@ __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int 
 // the last block resets the counter to 0, which no epoch matches.
 __device__ __forceinline__ bool arrive_last_ep(unsigned long long *ctr, unsigned long long epoch,
                                                unsigned int expected, int *flag_smem) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned long long old = atomicAdd(ctr, 0ull);
@@ -180,9 +207,7 @@ __device__ __forceinline__ bool arrive_last_ep(unsigned long long *ctr, unsigned
     *flag_smem = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *flag_smem != 0;
-  if (last) __threadfence();
-  return last;
+  return *flag_smem != 0;
 }
 
 }  // namespace ekv

@@ -189,20 +189,29 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   __syncthreads();
   double *hc = ws.hist + ((size_t)rc.row * gp.nchunk + chunk) * kNB * 3;
   for (int i = threadIdx.x; i < kNB; i += kGThreads) {
-    hc[i * 3 + 0] = h0[i];
-    hc[i * 3 + 1] = h1[i];
-    hc[i * 3 + 2] = h2[i];
+    st_agent(&hc[i * 3 + 0], h0[i]);
+    st_agent(&hc[i * 3 + 1], h1[i]);
+    st_agent(&hc[i * 3 + 2], h2[i]);
   }
   if (!arrive_last(&ws.ctr[rc.row * 2 + 0], (unsigned)rc.nch, &s_last)) return;
 
   // ---- last block of the row: merge chunks in order, suffix-scan the moments
   for (int i = threadIdx.x; i < kNB; i += kGThreads) {
     double a0 = 0.0, a1 = 0.0, a2 = 0.0;
-    for (int c = 0; c < rc.nch; ++c) {
-      const double *hh = ws.hist + ((size_t)rc.row * gp.nchunk + c) * kNB * 3 + i * 3;
-      a0 += hh[0];
-      a1 += hh[1];
-      a2 += hh[2];
+    for (int c0 = 0; c0 < rc.nch; c0 += 8) {  // batches of 8 chunks: one round trip each
+      double v[8][3];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(c0 + u, rc.nch - 1);
+        const double *hh = ws.hist + ((size_t)rc.row * gp.nchunk + c) * kNB * 3 + i * 3;
+        v[u][0] = ld_agent(&hh[0]);
+        v[u][1] = ld_agent(&hh[1]);
+        v[u][2] = ld_agent(&hh[2]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < rc.nch) { a0 += v[u][0]; a1 += v[u][1]; a2 += v[u][2]; }
+      }
     }
     s0[i] = a0;
     s1[i] = a1;
@@ -300,8 +309,8 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
           if (bin_of(v, lo, w) == k) {
             const int slot = atomicAdd(&ws.inbin_cnt[rc.row], 1);
             if (slot < gp.cap) {
-              ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0] = v;
-              ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1] = n * gc.w[j];
+              st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0], v);
+              st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1], n * gc.w[j]);
             }
           }
         }
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     }
     int tot;
     const int pos = block_excl_scan(code != -1 ? 1 : 0, scan_scratch, &tot);
-    if (code != -1) ws.list[base + p_begin + listed + pos] = code;
+    if (code != -1) st_agent(&ws.list[base + p_begin + listed + pos], code);
     listed += tot;
   }
   // chunk argmax of the estimate (lowest page on ties)
@@ -327,28 +336,43 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     if (cand != 0x7FFFFFFF) atomicMin(&s_best_p, cand);
     __syncthreads();
     if (threadIdx.x == 0) {
-      ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = bm;
-      ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1] = (double)s_best_p;
-      ws.list_cnt[(size_t)rc.row * gp.nchunk + chunk] = listed;
+      st_agent(&ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0], bm);
+      st_agent(&ws.amax[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1], (double)s_best_p);
+      st_agent(&ws.list_cnt[(size_t)rc.row * gp.nchunk + chunk], listed);
     }
   }
   if (!arrive_last(&ws.ctr[rc.row * 2 + 1], (unsigned)rc.nch, &s_last)) return;
 
-  // ---- last block of the row: solve F(t) = 1 inside [ek, ek1]
-  const int nin = min(ws.inbin_cnt[rc.row], gp.cap);
+  // ---- last block of the row: solve F(t) = 1 inside [ek, ek1].  The in-bin
+  // points are staged in registers once (kInReg per thread), any excess is
+  // re-read in batches.
+  const int nin = min(ld_agent(&ws.inbin_cnt[rc.row]), gp.cap);
   const double T0 = ri[3], T1 = ri[4], T2 = ri[5];
+  const double *inb = ws.inbin + (size_t)rc.row * gp.cap * 2;
+  constexpr int kInReg = 8;
+  double rv[kInReg], rcw[kInReg];
+#pragma unroll
+  for (int u = 0; u < kInReg; ++u) {
+    const int i = u * kGThreads + threadIdx.x;
+    const int ic = min(i, max(nin - 1, 0));
+    const double v = ld_agent(&inb[ic * 2 + 0]), c = ld_agent(&inb[ic * 2 + 1]);
+    rv[u] = i < nin ? v : -INFINITY;
+    rcw[u] = i < nin ? c : 0.0;
+  }
   double t = ek;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
-    for (int i = threadIdx.x; i < nin; i += kGThreads) {
-      const double v = ws.inbin[((size_t)rc.row * gp.cap + i) * 2 + 0];
-      const double c = ws.inbin[((size_t)rc.row * gp.cap + i) * 2 + 1];
+    auto acc_pt = [&](double v, double c) {
       const double x = v - t;
       if (x > 0.0) {
         if (gp.ibeta == 2) { f += c * x * x; fp += 2.0 * c * x; }
         else { f += c * x; fp += c; }
       }
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < kInReg; ++u) acc_pt(rv[u], rcw[u]);
+    for (int i = kInReg * kGThreads + threadIdx.x; i < nin; i += kGThreads)
+      acc_pt(ld_agent(&inb[i * 2 + 0]), ld_agent(&inb[i * 2 + 1]));
     f = block_sum(f, dred);
     fp = block_sum(fp, dred);
     const double Dd = ek1 - t;  // >= 0
@@ -367,38 +391,54 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   }
   const double thr = tau / gp.a - gp.delta;
 
-  // ---- settle undecided pages and write the ascending list
+  // ---- settle undecided pages and write the ascending list.  Chunk counts
+  // and argmax partials are fetched in one batch; list entries are then read
+  // in parallel across chunks (prefix offsets in LDS).
+  __shared__ int s_off[1024 + 1];
+  __shared__ double s_ae[1024];
+  __shared__ int s_ap[1024];
+  for (int c = threadIdx.x; c < rc.nch; c += kGThreads) {
+    s_off[c + 1] = ld_agent(&ws.list_cnt[(size_t)rc.row * gp.nchunk + c]);
+    s_ae[c] = ld_agent(&ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 0]);
+    s_ap[c] = (int)ld_agent(&ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 1]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s_off[0] = 0;
+    for (int c = 0; c < rc.nch; ++c) s_off[c + 1] += s_off[c];
+  }
+  __syncthreads();
+  const int n_listed = s_off[rc.nch];
   int total = 0;
-  for (int c = 0; c < rc.nch; ++c) {
-    const int cnt = ws.list_cnt[(size_t)rc.row * gp.nchunk + c];
-    const int seg = c * gp.chunk;
-    for (int i0 = 0; i0 < cnt; i0 += kGThreads) {
-      const int i = i0 + threadIdx.x;
-      int take = 0, p = 0;
-      if (i < cnt) {
-        const int code = ws.list[base + seg + i];
-        p = code & 0x7FFFFFFF;
-        if (code >= 0) take = 1;
-        else {
-          const float m = mu[base + p], v2 = var[base + p];
-          take = keep_at(thr, (double)box[base + p], (double)m, v2 > 0.0f ? (double)v2 : 0.0, gp.nsig) ? 1 : 0;
-        }
+  for (int e0 = 0; e0 < n_listed; e0 += kGThreads) {
+    const int e = e0 + threadIdx.x;
+    int take = 0, p = 0;
+    if (e < n_listed) {
+      int lo_c = 0, hi_c = rc.nch - 1;  // chunk holding entry e
+      while (lo_c < hi_c) {
+        const int mid = (lo_c + hi_c + 1) >> 1;
+        if (s_off[mid] <= e) lo_c = mid; else hi_c = mid - 1;
       }
-      int tot;
-      const int pos = block_excl_scan(take, scan_scratch, &tot);
-      if (take) sel_idx[base + total + pos] = p;
-      total += tot;
+      const int code = ld_agent(&ws.list[base + (size_t)lo_c * gp.chunk + (e - s_off[lo_c])]);
+      p = code & 0x7FFFFFFF;
+      if (code >= 0) take = 1;
+      else {
+        const float m = mu[base + p], v2 = var[base + p];
+        take = keep_at(thr, (double)box[base + p], (double)m, v2 > 0.0f ? (double)v2 : 0.0, gp.nsig) ? 1 : 0;
+      }
     }
+    int tot;
+    const int pos = block_excl_scan(take, scan_scratch, &tot);
+    if (take) sel_idx[base + total + pos] = p;
+    total += tot;
   }
   if (threadIdx.x == 0) {
     if (total == 0) {
       double be = -INFINITY;
       int bp = 0x7FFFFFFF;
       for (int c = 0; c < rc.nch; ++c) {
-        const double e = ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 0];
-        const int p = (int)ws.amax[((size_t)rc.row * gp.nchunk + c) * 2 + 1];
-        if (p == 0x7FFFFFFF) continue;
-        if (bp == 0x7FFFFFFF || e > be) { be = e; bp = p; }
+        if (s_ap[c] == 0x7FFFFFFF) continue;
+        if (bp == 0x7FFFFFFF || s_ae[c] > be) { be = s_ae[c]; bp = s_ap[c]; }
       }
       sel_idx[base] = bp;
       total = 1;
@@ -514,6 +554,10 @@ static GaussParams make_params(const Dims &D, double alpha, double delta, double
   if (chunk < 256) chunk = 256;
   gp.chunk = chunk;
   gp.nchunk = (D.max_pages + chunk - 1) / chunk;
+  if (gp.nchunk > 1024) {  // the selection kernel stages per-chunk data for up to 1024 chunks
+    gp.chunk = ((D.max_pages + 1023) / 1024 + 255) / 256 * 256;
+    gp.nchunk = (D.max_pages + gp.chunk - 1) / gp.chunk;
+  }
   gp.cap = 16 * D.max_pages;
   return gp;
 }

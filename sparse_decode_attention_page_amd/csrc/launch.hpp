@@ -61,6 +61,11 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
                                 const int32_t *sel_cnt, double alpha, int tau_method, float *out,
                                 double *tau, float *weights_out, void *ws, hipStream_t s);
 
+size_t full_ws_bytes(const Dims &D);
+hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *page_table, const int32_t *seq_lens, double alpha, float *out,
+                              double *tau, float *weights_out, void *ws, hipStream_t s);
+
 size_t softmax_ws_bytes(const Dims &D);
 hipError_t launch_softmax(const Dims &D, int dtype, const void *q, const void *k_pool,
                           const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,

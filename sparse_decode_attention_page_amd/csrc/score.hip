@@ -11,14 +11,18 @@
 //
 // The kernel is bound by the metadata stream (one record per page and KV head,
 // 4*d elements).  Design:
-//  * one block = one (b, KV head g) and a tile of 64 logical pages; the G query
+//  * work unit = one (b, KV head g) and a tile of 64 logical pages; the G query
 //    heads of the group share every record read (GQA reuse);
-//  * the tile's records are fetched with coalesced 16-byte loads into LDS,
-//    padded by 16 bytes per record so that lane-per-page reads are conflict free;
-//  * each wave then owns a quarter of the coordinates and each lane one page;
-//    the query-derived coefficients (q+, q-, q, q^2 in fp64) are wave-uniform
-//    and come from a small table through scalar loads, so the inner loop is
-//    four fp64 FMAs per (coordinate, head) on exact products;
+//  * persistent blocks walk a contiguous run of tiles with NBUF tile buffers in
+//    LDS: tiles t+1 .. t+NBUF-1 stream in with global_load_lds (16 bytes per
+//    lane, straight to LDS, no staging registers) while tile t is computed;
+//  * inside a record the 16-byte chunks are XOR-swizzled by the record index,
+//    so the lane-per-page reads of one chunk hit distinct LDS banks; the global
+//    side stays fully coalesced (a wave fetches whole records, permuted);
+//  * each wave owns a quarter of the coordinates, each lane one page; the
+//    query-derived coefficients (q+, q-, q, q^2 in fp64) are wave-uniform, written
+//    once per (b, g) to a workspace table and read back through scalar loads, so
+//    the inner loop is four fp64 FMAs per (coordinate, head) on exact products;
 //  * the four coordinate quarters are combined in a fixed order.
 #include "common.hpp"
 #include "launch.hpp"
@@ -27,22 +31,8 @@ namespace ekv {
 
 constexpr int kTilePages = 64;
 constexpr int kScoreThreads = 256;
-
-// coef[((b*Hkv + g)*d + i)*G + hh][4] = {max(q,0), min(q,0), q, q*q}, q = q[b][g*G+hh][i]
-template <typename T>
-__global__ void score_coef_kernel(Dims D, const T *__restrict__ q, double *__restrict__ coef) {
-  const int bg = blockIdx.x;  // b*Hkv + g
-  const int b = bg / D.Hkv, g = bg % D.Hkv;
-  for (int t = threadIdx.x; t < D.d * D.G; t += blockDim.x) {
-    const int i = t / D.G, hh = t % D.G;
-    const double qv = (double)load_f<T>(q, ((size_t)b * D.Hq + g * D.G + hh) * D.d + i);
-    double *c = coef + (((size_t)bg * D.d + i) * D.G + hh) * 4;
-    c[0] = qv >= 0.0 ? qv : 0.0;
-    c[1] = qv < 0.0 ? qv : 0.0;
-    c[2] = qv;
-    c[3] = qv * qv;
-  }
-}
+constexpr int kMaxTilesPerBlock = 16;
+constexpr size_t kScoreLds = 160 * 1024;
 
 template <typename T>
 struct Chunk;  // 16 bytes of one metadata row
@@ -64,109 +54,195 @@ struct Chunk<float> {
 };
 
 template <typename T, int DIM, int G>
+struct ScoreCfg {
+  static constexpr int kRecBytes = 4 * DIM * (int)sizeof(T);
+  static constexpr int kRecChunks = kRecBytes / 16;
+  static constexpr int kTileBytes = kTilePages * kRecBytes;
+  static constexpr int kRedBytes = 4 * 3 * G * kWave * 8;
+  static constexpr bool kRedInTile = kRedBytes <= kTileBytes;
+  static constexpr int kNBuf0 = (int)((kScoreLds - (kRedInTile ? 0 : kRedBytes)) / kTileBytes);
+  static constexpr int kNBuf = kNBuf0 > 4 ? 4 : kNBuf0;
+  static constexpr size_t kLds = (size_t)kNBuf * kTileBytes + (kRedInTile ? 0 : kRedBytes);
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 1 KB per wave instruction
+  static_assert(kNBuf >= 1, "tile does not fit in LDS");
+  static_assert(kTileBytes % 4096 == 0, "tile split across 4 waves");
+};
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+  // vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] << 14)
+  switch (n) {
+#define EKV_W(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
+    EKV_W(0) EKV_W(1) EKV_W(2) EKV_W(3) EKV_W(4) EKV_W(5) EKV_W(6) EKV_W(7) EKV_W(8) EKV_W(9) EKV_W(10)
+    EKV_W(11) EKV_W(12) EKV_W(13) EKV_W(14) EKV_W(15) EKV_W(16) EKV_W(17) EKV_W(18) EKV_W(19) EKV_W(20)
+    EKV_W(21) EKV_W(22) EKV_W(23) EKV_W(24) EKV_W(25) EKV_W(26) EKV_W(27) EKV_W(28) EKV_W(29) EKV_W(30)
+    EKV_W(31) EKV_W(32) EKV_W(33) EKV_W(34) EKV_W(35) EKV_W(36) EKV_W(37) EKV_W(38) EKV_W(39) EKV_W(40)
+    EKV_W(41) EKV_W(42) EKV_W(43) EKV_W(44) EKV_W(45) EKV_W(46) EKV_W(47) EKV_W(48) EKV_W(49) EKV_W(50)
+    EKV_W(51) EKV_W(52) EKV_W(53) EKV_W(54) EKV_W(55) EKV_W(56) EKV_W(57) EKV_W(58) EKV_W(59) EKV_W(60)
+    EKV_W(61) EKV_W(62) EKV_W(63)
+#undef EKV_W
+    default: __builtin_amdgcn_s_waitcnt(0); break;
+  }
+}
+
+template <typename T, int DIM, int G>
 __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
-    Dims D, const T *__restrict__ meta, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const double *__restrict__ coef, float *__restrict__ box,
-    float *__restrict__ mu, float *__restrict__ var) {
-  constexpr int kRecBytes = 4 * DIM * (int)sizeof(T);
-  constexpr int kStride = kRecBytes + 16;
-  constexpr int kRecChunks = kRecBytes / 16;
-  constexpr int kE = Chunk<T>::kElems;       // elements per 16-byte chunk
-  constexpr int kRowChunks = DIM / kE;        // chunks per metadata row
-  constexpr int kQuarter = DIM / 4;           // coordinates per wave
-  constexpr int kQChunks = kQuarter / kE;
+    Dims D, int tiles_per_row, int tiles_per_block, const T *__restrict__ q, const T *__restrict__ meta,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, double *__restrict__ coef_w,
+    const double *__restrict__ coef_r, float *__restrict__ box, float *__restrict__ mu,
+    float *__restrict__ var) {
+  using C = ScoreCfg<T, DIM, G>;
+  constexpr int kE = Chunk<T>::kElems;  // elements per 16-byte chunk
+  constexpr int kRowChunks = DIM / kE;   // chunks per metadata row
+  constexpr int kQChunks = DIM / 4 / kE; // chunks per coordinate quarter
+  constexpr int kQPer = (DIM * G + kScoreThreads - 1) / kScoreThreads;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_phys[kTilePages];
+  __shared__ int s_phys[kMaxTilesPerBlock][kTilePages];
+  __shared__ int s_np[kMaxTilesPerBlock];
 
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int p0 = blockIdx.x * kTilePages;
-  const int L = seq_len_clamped(seq_lens, b, D);
-  const int np = n_pages_of(L, D.P);
-  if (p0 >= np) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int n_tiles = D.B * D.Hkv * tiles_per_row;
+  const int t_begin = blockIdx.x * tiles_per_block;
+  const int t_end = min(n_tiles, t_begin + tiles_per_block);
+  if (t_begin >= t_end) return;
+  const int nt = t_end - t_begin;
+  const char *mbase = reinterpret_cast<const char *>(meta);
 
-  if (tid < kTilePages) {
-    const int p = p0 + tid;
+  // ---- page ids of every tile of this block (missing pages / bad ids -> -1)
+  for (int k = tid; k < nt * kTilePages; k += kScoreThreads) {
+    const int lt = k / kTilePages, r = k % kTilePages;
+    const int t = t_begin + lt;
+    const int row = t / tiles_per_row, pt = t % tiles_per_row;
+    const int b = row / D.Hkv;
+    const int np = n_pages_of(seq_len_clamped(seq_lens, b, D), D.P);
+    const int p = pt * kTilePages + r;
     int ph = -1;
     if (p < np) {
       ph = page_table[(size_t)b * D.max_pages + p];
       if (ph < 0 || ph >= D.num_phys) ph = -1;
     }
-    s_phys[tid] = ph;
+    s_phys[lt][r] = ph;
+    if (r == 0) s_np[lt] = np;
   }
   __syncthreads();
 
-  // ---- stage the tile's records in LDS (coalesced 16-byte loads)
-  const char *mbase = reinterpret_cast<const char *>(meta);
-  for (int c = tid; c < kTilePages * kRecChunks; c += kScoreThreads) {
-    const int r = c / kRecChunks, off = c % kRecChunks;
-    const int ph = s_phys[r];
-    if (ph >= 0) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(
-          mbase + ((size_t)ph * D.Hkv + g) * kRecBytes + (size_t)off * 16);
-      *reinterpret_cast<uint4 *>(smem + r * kStride + off * 16) = v;
+  // ---- tile loads: wave w fetches LDS bytes [w*T/4, (w+1)*T/4) of the tile
+  // buffer; lane l of instruction u lands at +16 l, which holds chunk
+  // (pos ^ (rec & 7)) of record rec.
+  auto issue_tile = [&](int lt) {
+    const int t = t_begin + lt;
+    const int g = (t / tiles_per_row) % D.Hkv;
+    unsigned char *buf = smem + (size_t)(lt % C::kNBuf) * C::kTileBytes;
+#pragma unroll
+    for (int u = 0; u < C::kLoadsPerWave; ++u) {
+      const int off = (wave * C::kLoadsPerWave + u) * 1024 + lane * 16;
+      const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
+      const int chunk = pos ^ (rec & 7);
+      const int ph = max(s_phys[lt][rec], 0);  // missing pages read record 0 and are masked later
+      const char *src = mbase + ((size_t)ph * D.Hkv + g) * C::kRecBytes + (size_t)chunk * 16;
+      __builtin_amdgcn_global_load_lds((const void *)src,
+                                       (__attribute__((address_space(3))) void *)(buf + (wave * C::kLoadsPerWave + u) * 1024),
+                                       16, 0, 0);
     }
-  }
-  __syncthreads();
+  };
+  for (int lt = 0; lt < C::kNBuf - 1 && lt < nt; ++lt) issue_tile(lt);  // tiles 0 .. NBUF-2
 
-  // ---- each wave: one coordinate quarter, lane = page
-  double acc_b[G], acc_m[G], acc_v[G];
+  int cur_bg = -1;
+  double *red = reinterpret_cast<double *>(C::kRedInTile ? smem : smem + (size_t)C::kNBuf * C::kTileBytes);
+  for (int lt = 0; lt < nt; ++lt) {
+    const int t = t_begin + lt;
+    const int row = t / tiles_per_row, pt = t % tiles_per_row;
+    const int b = row / D.Hkv, g = row % D.Hkv;
+    const int p0 = pt * kTilePages;
+    const int np = s_np[lt];
+    unsigned char *buf = smem + (size_t)(lt % C::kNBuf) * C::kTileBytes;
+    // ---- prefetch: tile lt+NBUF-1 goes into the buffer freed by tile lt-1
+    // (with a single buffer this is tile lt itself)
+    if (lt + C::kNBuf - 1 < nt) issue_tile(lt + C::kNBuf - 1);
+
+    // ---- coefficient table of (b, g), once per run of tiles of that row.
+    // Every block that scores (b, g) stores the same bytes into the same slot.
+    if (row != cur_bg) {
+      cur_bg = row;
+      double *cw = coef_w + (size_t)row * DIM * G * 4;
 #pragma unroll
-  for (int h = 0; h < G; ++h) acc_b[h] = acc_m[h] = acc_v[h] = 0.0;
-  const double *cf = coef + ((size_t)(b * D.Hkv + g) * DIM) * G * 4;
-  const unsigned char *rec = smem + lane * kStride;
+      for (int u = 0; u < kQPer; ++u) {  // surplus threads repeat the last entry (same bytes)
+        const int tt = min(u * kScoreThreads + tid, DIM * G - 1);
+        const double qv = (double)load_f<T>(q, ((size_t)b * D.Hq + g * G + tt % G) * DIM + tt / G);
+        double *c4 = cw + (size_t)tt * 4;
+        c4[0] = qv >= 0.0 ? qv : 0.0;
+        c4[1] = qv < 0.0 ? qv : 0.0;
+        c4[2] = qv;
+        c4[3] = qv * qv;
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // table stores (and any tile loads) complete
+    }
+    // ---- tile lt is resident once this wave's loads for it completed
+    const int ahead = min(C::kNBuf - 1, nt - 1 - lt);  // tiles issued after lt
+    wait_vmcnt(ahead * C::kLoadsPerWave);  // loads return in order: this covers all of tile lt
+    lds_barrier();
+
+    // ---- compute: wave = coordinate quarter, lane = page
+    double acc_b[G], acc_m[G], acc_v[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc_b[h] = acc_m[h] = acc_v[h] = 0.0;
+    const double *cf = coef_r + (size_t)row * DIM * G * 4;
+    const unsigned char *rec = buf + lane * C::kRecBytes;
+    const int sw = lane & 7;
 #pragma unroll 1
-  for (int qc = 0; qc < kQChunks; ++qc) {
-    const int chunk = wave * kQChunks + qc;  // chunk index within a row
-    double kmin[kE], kmax[kE], kmean[kE], kvar[kE];
-    Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (0 * kRowChunks + chunk) * 16), kmin);
-    Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (1 * kRowChunks + chunk) * 16), kmax);
-    Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (2 * kRowChunks + chunk) * 16), kmean);
-    Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (3 * kRowChunks + chunk) * 16), kvar);
+    for (int qc = 0; qc < kQChunks; ++qc) {
+      const int chunk = wave * kQChunks + qc;  // chunk index within a row
+      double kmin[kE], kmax[kE], kmean[kE], kvar[kE];
+      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((0 * kRowChunks + chunk) ^ sw) * 16), kmin);
+      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((1 * kRowChunks + chunk) ^ sw) * 16), kmax);
+      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((2 * kRowChunks + chunk) ^ sw) * 16), kmean);
+      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((3 * kRowChunks + chunk) ^ sw) * 16), kvar);
 #pragma unroll
-    for (int e = 0; e < kE; ++e) {
-      const int i = chunk * kE + e;
-      const double *ci = cf + (size_t)i * G * 4;
+      for (int e = 0; e < kE; ++e) {
+        const int i = chunk * kE + e;
+        const double *ci = cf + (size_t)i * G * 4;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const double cpos = ci[h * 4 + 0], cneg = ci[h * 4 + 1], cq = ci[h * 4 + 2], cqq = ci[h * 4 + 3];
-        acc_b[h] = __builtin_fma(cpos, kmax[e], acc_b[h]);
-        acc_b[h] = __builtin_fma(cneg, kmin[e], acc_b[h]);
-        acc_m[h] = __builtin_fma(cq, kmean[e], acc_m[h]);
-        if constexpr (sizeof(T) == 2)
-          acc_v[h] = __builtin_fma(cqq, kvar[e], acc_v[h]);  // exact product: fused == separate
-        else
-          acc_v[h] = acc_v[h] + cqq * kvar[e];               // fp32 keys: round the product first
+        for (int h = 0; h < G; ++h) {
+          const double cpos = ci[h * 4 + 0], cneg = ci[h * 4 + 1], cq = ci[h * 4 + 2], cqq = ci[h * 4 + 3];
+          acc_b[h] = __builtin_fma(cpos, kmax[e], acc_b[h]);
+          acc_b[h] = __builtin_fma(cneg, kmin[e], acc_b[h]);
+          acc_m[h] = __builtin_fma(cq, kmean[e], acc_m[h]);
+          if constexpr (sizeof(T) == 2)
+            acc_v[h] = __builtin_fma(cqq, kvar[e], acc_v[h]);  // exact product: fused == separate
+          else
+            acc_v[h] = acc_v[h] + cqq * kvar[e];               // fp32 keys: round the product first
+        }
       }
     }
-  }
-  __syncthreads();  // the tile is no longer needed; reuse LDS for the reduction
-
-  // red[w][k][lane], k = kind*G + h
-  double *red = reinterpret_cast<double *>(smem);
+    // ---- combine the four coordinate quarters in a fixed order
+    double *rd = C::kRedInTile ? reinterpret_cast<double *>(buf) : red;
+    if (C::kRedInTile) lds_barrier();  // every wave is done reading the tile
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    red[(wave * 3 * G + 0 * G + h) * kWave + lane] = acc_b[h];
-    red[(wave * 3 * G + 1 * G + h) * kWave + lane] = acc_m[h];
-    red[(wave * 3 * G + 2 * G + h) * kWave + lane] = acc_v[h];
-  }
-  __syncthreads();
-  const double c = D.scale, c2 = D.scale * D.scale;
-  for (int idx = tid; idx < 3 * G * kWave; idx += kScoreThreads) {
-    const int k = idx / kWave, r = idx % kWave;
-    const int p = p0 + r;
-    if (p >= np) continue;
-    double s = red[(0 * 3 * G + k) * kWave + r];
-    s += red[(1 * 3 * G + k) * kWave + r];
-    s += red[(2 * 3 * G + k) * kWave + r];
-    s += red[(3 * 3 * G + k) * kWave + r];
-    const int kind = k / G, h = g * G + (k % G);
-    const size_t o = ((size_t)b * D.Hq + h) * D.max_pages + p;
-    const bool ok = s_phys[r] >= 0;
-    if (kind == 0) box[o] = ok ? __double2float_ru(c * s) : NAN;
-    else if (kind == 1) mu[o] = ok ? (float)(c * s) : NAN;
-    else var[o] = ok ? (float)(c2 * s) : NAN;
+    for (int h = 0; h < G; ++h) {
+      rd[(wave * 3 * G + 0 * G + h) * kWave + lane] = acc_b[h];
+      rd[(wave * 3 * G + 1 * G + h) * kWave + lane] = acc_m[h];
+      rd[(wave * 3 * G + 2 * G + h) * kWave + lane] = acc_v[h];
+    }
+    lds_barrier();
+    const double c = D.scale, c2 = D.scale * D.scale;
+    for (int idx = tid; idx < 3 * G * kWave; idx += kScoreThreads) {
+      const int k = idx / kWave, r = idx % kWave;
+      const int p = p0 + r;
+      if (p >= np) continue;
+      double sacc = rd[(0 * 3 * G + k) * kWave + r];
+      sacc += rd[(1 * 3 * G + k) * kWave + r];
+      sacc += rd[(2 * 3 * G + k) * kWave + r];
+      sacc += rd[(3 * 3 * G + k) * kWave + r];
+      const int kind = k / G, h = g * G + (k % G);
+      const size_t o = ((size_t)b * D.Hq + h) * D.max_pages + p;
+      const bool ok = s_phys[lt][r] >= 0;
+      if (kind == 0) box[o] = ok ? __double2float_ru(c * sacc) : NAN;
+      else if (kind == 1) mu[o] = ok ? (float)(c * sacc) : NAN;
+      else var[o] = ok ? (float)(c2 * sacc) : NAN;
+    }
+    lds_barrier();  // buffer lt % NBUF (and red) may be refilled from here on
   }
 }
 
@@ -180,17 +256,24 @@ template <typename T, int DIM, int G>
 static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
                                  const int32_t *page_table, const int32_t *seq_lens, float *box,
                                  float *mu, float *var, void *ws, hipStream_t s) {
+  using C = ScoreCfg<T, DIM, G>;
   Carve cv(ws);
   double *coef = cv.take<double>((size_t)D.B * D.Hkv * D.d * D.G * 4);
-  hipLaunchKernelGGL(score_coef_kernel<T>, dim3(D.B * D.Hkv), dim3(256), 0, s, D,
-                     (const T *)q, coef);
-  constexpr int kRecBytes = 4 * DIM * (int)sizeof(T);
-  const size_t tile = (size_t)kTilePages * (kRecBytes + 16);
-  const size_t red = (size_t)4 * 3 * G * kWave * sizeof(double);
-  const size_t smem = tile > red ? tile : red;
-  dim3 grid((D.max_pages + kTilePages - 1) / kTilePages, D.Hkv, D.B);
-  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G>), grid, dim3(kScoreThreads), smem, s, D,
-                     (const T *)meta, page_table, seq_lens, coef, box, mu, var);
+  // persistent blocks (one per CU), each walking a contiguous run of tiles
+  const int tiles_per_row = (D.max_pages + kTilePages - 1) / kTilePages;
+  const int n_tiles = D.B * D.Hkv * tiles_per_row;
+  int tiles_per_block = (n_tiles + 255) / 256;
+  if (tiles_per_block > kMaxTilesPerBlock) tiles_per_block = kMaxTilesPerBlock;
+  const int grid = (n_tiles + tiles_per_block - 1) / tiles_per_block;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void *)score_pages_kernel<T, DIM, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)C::kLds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G>), dim3(grid), dim3(kScoreThreads), C::kLds, s, D,
+                     tiles_per_row, tiles_per_block, (const T *)q, (const T *)meta, page_table, seq_lens, coef,
+                     (const double *)coef, box, mu, var);
   return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@
 //    one page ahead), so the main loop touches no LDS and has no barriers;
 //  * each thread keeps a running softmax (max, sum, weighted V slice) per head
 //    over "its" tokens and rescales only when its max grows;
-//  * the running states are merged across slots (shuffles, then LDS), written per
-//    range, and the last block of (b, g) merges the ranges in order.
+//  * the running states are merged across slots (shuffles, then LDS) and written
+//    per range; a small second launch merges the ranges of each query row in
+//    range order.
 #include <math.h>
 
 #include "common.hpp"
@@ -24,10 +25,8 @@ namespace ekv {
 constexpr int kSThreads = 256;
 
 struct SoftmaxWs {
-  float *part;              // [B][Hq][S][DIM + 2]  (m, l, acc[DIM])
-  unsigned long long *ctr;  // [B][Hkv]
-  unsigned long long epoch;
-  int S;                    // ranges per (b, g)
+  float *part;              // [B][Hq][S][DIM + 2]  (m, l, acc[DIM]); l = NaN marks a bad page id
+  int S;                    // ranges per (b, g), at most 1024
   int pps;                  // pages per range
 };
 
@@ -41,7 +40,6 @@ __global__ __launch_bounds__(kSThreads) void softmax_decode_kernel(
   static_assert(kPer >= 2 && kPer % 2 == 0, "slice must hold bf16 pairs");
   constexpr int kWords = kPer * (int)sizeof(T) / 4;  // 32-bit words per slice
   __shared__ float xch[kSThreads / kWave][kParts][G][DIM / kParts + 2];
-  __shared__ int s_last;
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -191,39 +189,39 @@ __global__ __launch_bounds__(kSThreads) void softmax_decode_kernel(
     }
     float *rec = dst + (((size_t)b * D.Hq + g * G + h) * ws.S + s) * (DIM + 2);
     rec[2 + i] = aa;
-    if (i == 0) { rec[0] = mm; rec[1] = ll; }
+    if (i == 0) { rec[0] = mm; rec[1] = bad ? NAN : ll; }
   }
-  if (bad) {
-    if (tid == 0) {  // poison this range: the merged row becomes NaN
-      for (int h = 0; h < G; ++h) dst[(((size_t)b * D.Hq + g * G + h) * ws.S + s) * (DIM + 2) + 1] = NAN;
-    }
-  }
-  if (!arrive_last_ep(&ws.ctr[(size_t)b * D.Hkv + g], ws.epoch, (unsigned)ws.S, &s_last)) return;
+}
 
-  // ---- last block of (b, g): merge the ranges in order
-  for (int idx = tid; idx < G * DIM; idx += kSThreads) {
-    const int h = idx / DIM, i = idx % DIM;
-    const float *rec0 = dst + (((size_t)b * D.Hq + g * G + h) * ws.S) * (DIM + 2);
-    float mm = -INFINITY;
-    for (int r = 0; r < ws.S; ++r) mm = fmaxf(mm, rec0[(size_t)r * (DIM + 2)]);
-    float ll = 0.0f, aa = 0.0f;
-    for (int r = 0; r < ws.S; ++r) {
-      const float *rec = rec0 + (size_t)r * (DIM + 2);
-      const float lr = rec[1];
-      if (lr != lr) { ll = NAN; break; }
-      if (rec[0] == -INFINITY) continue;
-      const float f = __expf(rec[0] - mm);
-      ll += lr * f;
-      aa += rec[2 + i] * f;
-    }
-    const size_t o = ((size_t)b * D.Hq + g * G + h) * DIM + i;
-    if (ll != ll) out[o] = NAN;
-    else out[o] = ll > 0.0f ? aa / ll : 0.0f;
-    if (i == 0 && lse) {
-      const size_t ro = (size_t)b * D.Hq + g * G + h;
-      lse[ro] = (ll != ll) ? NAN : (ll > 0.0f ? mm + logf(ll) : -INFINITY);
-    }
+// Merge the ranges of one query row in range order (a separate launch: plain
+// cached loads of all ranges at once beat a last-block handoff here).
+template <int DIM>
+__global__ __launch_bounds__(DIM) void softmax_merge_kernel(Dims D, SoftmaxWs ws, float *__restrict__ out,
+                                                            float *__restrict__ lse) {
+  __shared__ float sm[1024], sl[1024];
+  const int row = blockIdx.x, i = threadIdx.x;
+  const float *rec0 = ws.part + (size_t)row * ws.S * (DIM + 2);
+  float mm = -INFINITY;
+  bool nan = false;
+  for (int r = i; r < ws.S; r += DIM) {
+    sm[r] = rec0[(size_t)r * (DIM + 2)];
+    sl[r] = rec0[(size_t)r * (DIM + 2) + 1];
   }
+  __syncthreads();
+  for (int r = 0; r < ws.S; ++r) {
+    mm = fmaxf(mm, sm[r]);
+    nan |= sl[r] != sl[r];
+  }
+  float ll = 0.0f, aa = 0.0f;
+  for (int r = 0; r < ws.S; ++r) {
+    const float f = sm[r] == -INFINITY ? 0.0f : __expf(sm[r] - mm);
+    ll += sl[r] * f;
+    aa += rec0[(size_t)r * (DIM + 2) + 2 + i] * f;
+  }
+  const size_t o = (size_t)row * DIM + i;
+  if (nan) out[o] = NAN;
+  else out[o] = ll > 0.0f ? aa / ll : 0.0f;
+  if (i == 0 && lse) lse[row] = nan ? NAN : (ll > 0.0f ? mm + logf(ll) : -INFINITY);
 }
 
 static SoftmaxWs carve_softmax(const Dims &D, void *base, size_t *bytes) {
@@ -237,8 +235,6 @@ static SoftmaxWs carve_softmax(const Dims &D, void *base, size_t *bytes) {
   w.pps = (D.max_pages + S - 1) / S;
   Carve cv(base);
   w.part = cv.take<float>((size_t)D.B * D.Hq * S * (D.d + 2));
-  w.ctr = cv.take<unsigned long long>((size_t)bg);
-  w.epoch = 0;
   if (bytes) *bytes = cv.bytes();
   return w;
 }
@@ -255,6 +251,7 @@ static hipError_t launch_sm(const Dims &D, const void *q, const void *k, const v
   dim3 grid(w.S, D.Hkv, D.B);
   hipLaunchKernelGGL((softmax_decode_kernel<T, DIM, P, G>), grid, dim3(kSThreads), 0, s, D, (const T *)q,
                      (const T *)k, (const T *)v, pt, sl, out, lse, w);
+  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(DIM), 0, s, D, w, out, lse);
   return hipGetLastError();
 }
 
@@ -285,7 +282,6 @@ hipError_t launch_softmax(const Dims &D, int dtype, const void *q, const void *k
                           const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
                           float *out, float *lse, void *ws, hipStream_t s) {
   SoftmaxWs w = carve_softmax(D, ws, nullptr);
-  w.epoch = next_epoch();
   if (dtype == ENTMAXKV_BF16) {
     if (D.d == 64) return launch_sm_p<uint16_t, 64>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
     return launch_sm_p<uint16_t, 128>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);

@@ -204,3 +204,116 @@ def random_small(seed: int, B=2, Hq=4, Hkv=2, d=64, P=16, dtype="bf16", ctx=(200
         kf = storage_to_f64(inp.k_pool, dtype) * scale_keys
         inp.k_pool = _store(kf.astype(np.float32), dtype)
     return inp
+
+
+@dataclass
+class DeviceInputs:
+    """A workload drawn directly on the GPU (torch Philox, seeded).  Same recipe
+    as make(); different random stream.  Tensors: q [B][Hq][d], k_pool/v_pool
+    [num_phys][Hkv][P][d] (bf16 or fp32), page_table/seq_lens int32."""
+    wl: Workload
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    P: int
+    dtype: str
+    max_pages: int
+    num_phys: int
+    q: object
+    k_pool: object
+    v_pool: object
+    page_table: object
+    seq_lens: object
+    planted: list
+    seq_mask_topk: object
+    seq_mask_gauss: object
+
+    def host(self, name):
+        """Raw host storage of a tensor (uint16 bit patterns for bf16), for the oracle."""
+        import torch
+        t = getattr(self, name)
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+
+def make_device(wl: Workload | str, seed: int = 0, ctx_override=None, device="cuda") -> DeviceInputs:
+    import torch
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    hgen = torch.Generator()
+    hgen.manual_seed(int(seed))
+    B, Hq, Hkv, d, P = wl.B, wl.Hq, wl.Hkv, wl.d, wl.P
+    G = Hq // Hkv
+    if ctx_override is not None:
+        ctx = list(ctx_override) if np.ndim(ctx_override) else [int(ctx_override)] * B
+        ctx = (ctx * B)[:B] if len(ctx) < B else ctx
+    elif wl.ragged:
+        ctx = [int(x) for x in torch.randint(wl.ctx[0], wl.ctx[1] + 1, (B,), generator=hgen)]
+    else:
+        ctx = [int(wl.ctx[0])] * B
+    npages = [(L + P - 1) // P for L in ctx]
+    max_pages = max(max(npages), 1)
+    num_phys = sum(npages)
+    perm = torch.randperm(num_phys, generator=hgen) if wl.shuffle_pages else torch.arange(num_phys)
+    pt = torch.full((B, max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b in range(B):
+        pt[b, : npages[b]] = perm[off: off + npages[b]].to(torch.int32)
+        off += npages[b]
+    kdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    q = torch.randn((B, Hq, d), generator=gen, device=device, dtype=torch.float32).to(kdt)
+    qs = q.to(torch.float64)
+    k_pool = torch.zeros((num_phys, Hkv, P, d), dtype=kdt, device=device)
+    v_pool = torch.zeros_like(k_pool)
+    planted = []
+    for b in range(B):
+        L, nb = ctx[b], npages[b]
+        diffuse = wl.diffuse_first_half and b < B // 2
+        phys = pt[b, :nb].to(device=device, dtype=torch.int64)
+        plist = []
+        for g in range(Hkv):
+            kf = torch.randn((nb * P, d), generator=gen, device=device, dtype=torch.float32)
+            vf = torch.randn((nb * P, d), generator=gen, device=device, dtype=torch.float32)
+            if diffuse:
+                kf *= 8.0 / float(np.sqrt(L))
+            if wl.drift_per_1k:
+                r = torch.randint(0, 2, (d,), generator=gen, device=device).to(torch.float32) * 2 - 1
+                t = torch.arange(nb * P, device=device, dtype=torch.float32)[:, None]
+                kf += float(wl.drift_per_1k) * r[None, :] * t / 1000.0
+            if wl.planted_per_kv and not diffuse:
+                n = min(wl.planted_per_kv, L)
+                if wl.planted_layout == "even":
+                    pos = ((torch.arange(n, dtype=torch.float64) + 0.5) * L / n).to(torch.int64)
+                else:
+                    pos = torch.sort(torch.randperm(L, generator=hgen)[:n]).values
+                hs = torch.tensor([g * G + (j % G) for j in range(n)], device=device)
+                qv = qs[b, hs]                                           # [n, d]
+                dirs = (4.0 * qv / torch.linalg.norm(qv, dim=1, keepdim=True)).to(torch.float32)
+                noise = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32) * 0.1
+                kf[pos.to(device)] = dirs + noise
+                plist += [(g, int(hs[j]), int(pos[j])) for j in range(n)]
+            if L < nb * P:
+                kf[L:] = 0.0
+                vf[L:] = 0.0
+            k_pool[phys, g] = kf.view(nb, P, d).to(kdt)
+            v_pool[phys, g] = vf.view(nb, P, d).to(kdt)
+            del kf, vf
+        planted.append(plist)
+    if wl.policy == "mixed":
+        mt = np.array([1 if b % 2 == 0 else 0 for b in range(B)], dtype=np.uint8)
+        mg = 1 - mt
+    elif wl.policy == "topk":
+        mt, mg = np.ones(B, np.uint8), np.zeros(B, np.uint8)
+    elif wl.policy == "gauss":
+        mt, mg = np.zeros(B, np.uint8), np.ones(B, np.uint8)
+    else:
+        mt, mg = np.ones(B, np.uint8), np.ones(B, np.uint8)
+    return DeviceInputs(wl, seed, B, Hq, Hkv, d, P, wl.dtype, max_pages, num_phys, q, k_pool, v_pool,
+                        pt.to(device), torch.tensor(ctx, dtype=torch.int32, device=device), planted,
+                        torch.from_numpy(mt.astype(np.uint8)).to(device),
+                        torch.from_numpy(mg.astype(np.uint8)).to(device))
