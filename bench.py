@@ -216,6 +216,8 @@ def main():
                 s_.update(sel_h[bb, h, :cnt_h[bb, h]].tolist())
             union += len(s_)
     per_head_pages = int(cnt_h.sum())
+    log(f"[bench] kept pages per row: min {cnt_h.min()} median {int(np.median(cnt_h))} max {cnt_h.max()} "
+        f"(of {MP})")
     dec_bytes = per_head_pages * 2 * P * d * esz  # K and V of every kept page (per head)
     step_bytes = score_bytes + Hq * npg.sum() * 12 + dec_bytes  # + selector reads of box/mu/var
 

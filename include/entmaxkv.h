@@ -28,6 +28,8 @@
  *    data (page ids, lengths, selections) is checked inside the kernels, which
  *    never read outside the buffers implied by the shape; bad entries produce
  *    NaN results as documented per call.
+ *  * q, k_pool, v_pool and meta must be 16-byte aligned (vector loads);
+ *    a misaligned pointer is rejected with ENTMAXKV_ERR_INVALID_ARGUMENT.
  *  * KV dtype (`entmaxkv_shape.dtype`) applies to q, the K/V pools and the page
  *    metadata; outputs are float32 (scores, weights, attention outputs) or
  *    float64 (thresholds).
@@ -67,7 +69,9 @@ enum entmaxkv_status {
 
 enum entmaxkv_dtype { ENTMAXKV_F32 = 0, ENTMAXKV_BF16 = 1 };
 
-/* Supported: d in {64, 128}; P in {16, 32, 64}; Hq/Hkv in {1, 2, 4, 8}. */
+/* Supported: d in {64, 128}; P in {16, 32, 64}; Hq/Hkv in {1, 2, 4, 8};
+ * B*Hq <= 8192; max_pages*P < 2^31; num_phys_pages*Hkv*P < 2^32 (pool rows are
+ * indexed in 32 bits).  Other shapes return ENTMAXKV_ERR_UNSUPPORTED. */
 typedef struct entmaxkv_shape {
   int32_t batch;          /* B >= 1 */
   int32_t n_q_heads;      /* Hq >= 1 */

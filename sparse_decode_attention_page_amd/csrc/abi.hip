@@ -99,6 +99,7 @@ static int32_t check_shape(const entmaxkv_shape *s, Dims *D) {
   if ((long long)s->batch * s->n_q_heads > 8192) return ENTMAXKV_ERR_UNSUPPORTED;
   if ((long long)s->max_pages * s->page_size >= (1ll << 31) || s->max_pages >= (1 << 24))
     return ENTMAXKV_ERR_UNSUPPORTED;
+  if ((long long)s->num_phys_pages * s->n_kv_heads * s->page_size >= (1ll << 32)) return ENTMAXKV_ERR_UNSUPPORTED;
   if (D) {
     D->B = s->batch;
     D->Hq = s->n_q_heads;
@@ -118,6 +119,10 @@ static int32_t check_ws(size_t need, const void *ws, size_t ws_bytes) {
   if (!ws || ws_bytes < need) return ENTMAXKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   return ENTMAXKV_OK;
+}
+
+static bool misaligned16(const void *a, const void *b = nullptr, const void *c = nullptr) {
+  return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(c)) & 15) != 0;
 }
 
 }  // namespace ekv
@@ -166,6 +171,7 @@ int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const i
   int32_t st = check_shape(shape, &D);
   if (st) return st;
   if (!k_pool || !page_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(k_pool, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   return hip_status(launch_build_meta(D, shape->dtype, k_pool, page_table, seq_lens, from_token, meta, stream));
 }
 
@@ -176,6 +182,7 @@ int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta
   int32_t st = check_shape(shape, &D);
   if (st) return st;
   if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(score_ws_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_score(D, shape->dtype, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
 }
@@ -217,6 +224,7 @@ static int32_t decode_common(const entmaxkv_shape *shape, const void *q, const v
   int32_t st = check_shape(shape, &D);
   if (st) return st;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, k_pool, v_pool)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (!full && (!sel_idx || !sel_cnt)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
@@ -255,6 +263,7 @@ int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const vo
   int32_t st = check_shape(shape, &D);
   if (st) return st;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, k_pool, v_pool)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(softmax_ws_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_softmax(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, stream));
 }

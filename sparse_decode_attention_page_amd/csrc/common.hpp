@@ -32,6 +32,39 @@ __device__ __forceinline__ float load_f<uint16_t>(const uint16_t *p, size_t i) {
 template <>
 __device__ __forceinline__ float load_f<float>(const float *p, size_t i) { return p[i]; }
 
+// N consecutive elements as floats with the widest loads that alignment allows:
+// p must be aligned to min(16, N * sizeof(T)) bytes.
+template <int N>
+__device__ __forceinline__ void load_vec(const uint16_t *p, float (&v)[N]) {
+  static_assert(N % 4 == 0, "bf16 vector loads take multiples of 4 elements");
+  if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int c = 0; c < N / 8; ++c) {
+      const uint4 u = reinterpret_cast<const uint4 *>(p)[c];
+      v[8 * c + 0] = bf16lo(u.x); v[8 * c + 1] = bf16hi(u.x);
+      v[8 * c + 2] = bf16lo(u.y); v[8 * c + 3] = bf16hi(u.y);
+      v[8 * c + 4] = bf16lo(u.z); v[8 * c + 5] = bf16hi(u.z);
+      v[8 * c + 6] = bf16lo(u.w); v[8 * c + 7] = bf16hi(u.w);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < N / 4; ++c) {
+      const uint2 u = reinterpret_cast<const uint2 *>(p)[c];
+      v[4 * c + 0] = bf16lo(u.x); v[4 * c + 1] = bf16hi(u.x);
+      v[4 * c + 2] = bf16lo(u.y); v[4 * c + 3] = bf16hi(u.y);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void load_vec(const float *p, float (&v)[N]) {
+  static_assert(N % 4 == 0, "f32 vector loads take multiples of 4 elements");
+#pragma unroll
+  for (int c = 0; c < N / 4; ++c) {
+    const float4 u = reinterpret_cast<const float4 *>(p)[c];
+    v[4 * c + 0] = u.x; v[4 * c + 1] = u.y; v[4 * c + 2] = u.z; v[4 * c + 3] = u.w;
+  }
+}
+
 // ----------------------------------------------------------------------- roundings
 // fp64 -> bf16 round-to-nearest-even in one step: round to float with
 // round-toward-zero plus a sticky bit (round-to-odd, exact enough because float

@@ -9,17 +9,23 @@
 // alpha-entmax (Peters, Niculae & Martins 2019): with X_t = (alpha-1) s_t,
 // p_t = [X_t - tau]_+^(1/(alpha-1)), tau the root of sum_t p_t = 1.
 //
-// One launch.  Work is a flat list of items (row, i): the i-th selected page of
-// query row (b, h); every block maps items through a prefix sum of the
-// selection counts it computes itself.
-//  * item: exact fp64 scores of the page's tokens (bf16 products are exact;
-//    fp64 sums), handed to the row's last block through the workspace;
-//  * last item of a row (atomic handshake): stages the row's scores in LDS
-//    with batched loads, solves tau by safeguarded Newton from
-//    the left (F is convex and decreasing for alpha <= 2; bisection steps keep
-//    it safe otherwise) or by the sparsemax sort closed form, then gathers the
-//    V rows of the support tokens only and writes the output.  Kept tokens
-//    outside the support cost no V traffic at all.
+// Two launches.
+//  1. Scores.  Work is a flat list of items (row, i): the i-th selected page of
+//     query row (b, h); every block maps items through a prefix sum of the
+//     selection counts it computes itself.  An item writes the exact fp64
+//     scores X of the page's tokens (bf16 products are exact; fp64 sums), the
+//     page's maximum (NaN for a malformed item) and its physical page.
+//  2. Threshold and output.  Since F(max X - 1) >= 1, tau is at least
+//     max X - 1 and only tokens with X > max X - 1 can carry weight.  Each row
+//     is cut into up to kSplitMax chunks of kChunkTok tokens; the block of a
+//     chunk reads the row's page maxima, compacts its chunk's candidates in
+//     place, and the row's last block (atomic handshake; kernel 1 zeroed the
+//     counters) gathers them into LDS.  tau comes from safeguarded Newton from
+//     the left on the candidates (one wave and shuffles when they are few) or
+//     from the sparsemax sort form; the V rows of the support are then
+//     gathered with 16-byte loads.  Kept tokens outside the support cost no V
+//     traffic.  Rows with more candidates than LDS holds are solved by passes
+//     over the compacted candidates in the workspace.
 #include <math.h>
 
 #include "common.hpp"
@@ -28,59 +34,94 @@
 namespace ekv {
 
 constexpr int kDThreads = 256;
-constexpr int kDGrid = 1024;    // persistent-style grid; items are strided over it
-constexpr int kStage = 4096;    // scores of a row staged in LDS by the last block
-constexpr int kSortMax = 8192;  // largest kept-token count sorted in LDS (alpha = 2)
-constexpr int kSupChunk = 1024; // support entries gathered per LDS pass
+constexpr int kDGrid = 1024;      // kernel 1: items are strided over this many blocks
+constexpr int kChunkTok = 4096;   // kernel 2: tokens per chunk block
+constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
+constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
+constexpr int kSupChunk = 512;    // support entries gathered per LDS pass
 
 struct DecodeWs {
-  double *xs;                // [rows][max_pages*P]  X_t of kept tokens (item-major), -inf in empty slots
-  unsigned long long *badf;  // [rows]  == epoch when an item of the row is malformed
-  unsigned long long *ctr;   // [rows]  epoch-tagged arrival counters
-  unsigned long long epoch;
+  double *xs;        // [rows][max_pages*P]  X of kept tokens (item-major); kernel 2 compacts
+                     //                      each chunk's candidates to the chunk's start
+  uint32_t *xi;      // [rows][max_pages*P]  token index (item*P + slot) of a compacted candidate
+  double *pmax;      // [rows][max_pages]    max X over item i's tokens, NaN if the item is malformed
+  uint32_t *iphys;   // [rows][max_pages]    physical page of item i
+  int *segcnt;       // [rows][kSplitMax]    candidates of each chunk
+  unsigned int *ctr; // [rows]               arrival counters (zeroed by kernel 1)
 };
 
 struct DecodeParams {
   double a, beta, c;
-  int ibeta, tau_method, full;
+  int ibeta, tau_method;
 };
 
+// pow for the generic exponent, kept out of line: the solver loops are
+// unrolled and would otherwise carry one copy per call site.
+__device__ __noinline__ double pow_generic(double x, double y) { return pow(x, y); }
+
 __device__ __forceinline__ double entw(double x, const DecodeParams &dp) {
-  return dp.ibeta == 2 ? x * x : (dp.ibeta == 1 ? x : pow(x, dp.beta));
+  return dp.ibeta == 2 ? x * x : (dp.ibeta == 1 ? x : pow_generic(x, dp.beta));
 }
 __device__ __forceinline__ double entw_d(double x, const DecodeParams &dp) {  // d/dx of entw
-  return dp.ibeta == 2 ? 2.0 * x : (dp.ibeta == 1 ? 1.0 : dp.beta * pow(x, dp.beta - 1.0));
+  return dp.ibeta == 2 ? 2.0 * x : (dp.ibeta == 1 ? 1.0 : dp.beta * pow_generic(x, dp.beta - 1.0));
 }
 
-// Item count of a row: selected pages (sparse) or all pages (full), clamped to
-// [0, max_pages]; *bad is set for a malformed count.
-__device__ __forceinline__ int row_items(const Dims &D, const DecodeParams &dp, const int32_t *seq_lens,
-                                         const int32_t *sel_cnt, int row, bool *bad) {
-  const int b = row / D.Hq;
-  const int np = n_pages_of(seq_len_clamped(seq_lens, b, D), D.P);
-  *bad = false;
-  if (dp.full) return np;
+// The same powers with the exponent fixed at compile time (kB = 2: alpha = 1.5,
+// kB = 1: alpha = 2, kB = 0: any alpha through pow).
+template <int kB>
+__device__ __forceinline__ double pw(double y, const DecodeParams &dp) {
+  if constexpr (kB == 2) return y * y;
+  else if constexpr (kB == 1) return y;
+  else return pow_generic(y, dp.beta);
+}
+template <int kB>
+__device__ __forceinline__ double pw_d(double y, const DecodeParams &dp) {
+  if constexpr (kB == 2) return 2.0 * y;
+  else if constexpr (kB == 1) return 1.0;
+  else return dp.beta * pow_generic(y, dp.beta - 1.0);
+}
+
+// Selected-page count of a row clamped to [0, max_pages]; *bad is set for a
+// count outside [0, number of pages of the sequence].
+__device__ __forceinline__ int row_items(const Dims &D, const int32_t *seq_lens, const int32_t *sel_cnt,
+                                         int row, bool *bad) {
+  const int np = n_pages_of(seq_len_clamped(seq_lens, row / D.Hq, D), D.P);
   int c = sel_cnt[row];
-  if (c < 0 || c > np) { *bad = true; c = c < 0 ? 0 : (c > D.max_pages ? D.max_pages : c); }
-  return c;
+  *bad = c < 0 || c > np;
+  return c < 0 ? 0 : (c > D.max_pages ? D.max_pages : c);
 }
 
 // Block-shared item map: prefix[r] = first item of row r, prefix[rows] = total.
-__device__ int build_item_map(const Dims &D, const DecodeParams &dp, const int32_t *seq_lens,
-                              const int32_t *sel_cnt, int *prefix, int rows, int *scan_scratch) {
-  int run = 0;
-  for (int r0 = 0; r0 < rows; r0 += kDThreads) {
-    const int r = r0 + threadIdx.x;
-    bool bad;
-    const int c = r < rows ? row_items(D, dp, seq_lens, sel_cnt, r, &bad) : 0;
-    int tot;
-    const int ex = block_excl_scan(c, scan_scratch, &tot);
-    if (r < rows) prefix[r] = run + ex;
-    run += tot;
+// Each thread owns a contiguous run of rows; its counts are loaded 8 at a time.
+__device__ int build_item_map(const Dims &D, const int32_t *seq_lens, const int32_t *sel_cnt,
+                              int *prefix, int rows, int *scan_scratch) {
+  const int per = (rows + kDThreads - 1) / kDThreads;
+  const int r0 = threadIdx.x * per;
+  int sum = 0;
+#pragma unroll 1
+  for (int c0 = 0; c0 < per; c0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      bool bad;
+      c[u] = row_items(D, seq_lens, sel_cnt, min(r0 + c0 + u, rows - 1), &bad);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = r0 + c0 + u;
+      if (c0 + u < per && r < rows) { prefix[r] = c[u]; sum += c[u]; }
+    }
   }
-  if (threadIdx.x == 0) prefix[rows] = run;
+  int tot;
+  int run = block_excl_scan(sum, scan_scratch, &tot);
+#pragma unroll 1
+  for (int u = 0; u < per; ++u) {
+    const int r = r0 + u;
+    if (r < rows) { const int c = prefix[r]; prefix[r] = run; run += c; }
+  }
+  if (threadIdx.x == 0) prefix[rows] = tot;
   __syncthreads();
-  return run;
+  return tot;
 }
 __device__ __forceinline__ int find_row(const int *prefix, int rows, int item) {
   int lo = 0, hi = rows - 1;  // largest r with prefix[r] <= item
@@ -91,60 +132,98 @@ __device__ __forceinline__ int find_row(const int *prefix, int rows, int item) {
   return lo;
 }
 
-// The scores of one row, as seen by the last block: the first kStage in LDS
-// (staged once with batched loads), any remainder re-read from the workspace in
-// batches.  Loops stay rolled: this code runs once per row and must stay small.
-struct RowScores {
-  double *xl;        // LDS copy of X[0 .. min(n, kStage))
-  const double *X;   // the row in the workspace
-  int n, ns;
-
-  __device__ void load(const double *xrow, int nX, double *lds) {
-    X = xrow;
-    xl = lds;
-    n = nX;
-    ns = min(nX, kStage);
-#pragma unroll 1
-    for (int base = 0; base < ns; base += 8 * kDThreads) {
-      double v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ld_agent(&xrow[min(base + u * kDThreads + (int)threadIdx.x, ns - 1)]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kDThreads + threadIdx.x;
-        if (i < ns) xl[i] = v[u];
-      }
-    }
-    __syncthreads();
+// ------------------------------------------------------------- threshold solve
+// Values seen by the solver: LDS candidates (strided over the participating
+// threads) or, for a row whose candidates overflow LDS, every score of the row
+// in the workspace above the bound `thr` (batched agent-scope loads).
+struct LdsVals {
+  const double *v;
+  int n, t0, stride;
+  template <typename Fn>
+  __device__ __forceinline__ void each(Fn &&fn) const {
+#pragma unroll 2
+    for (int i = t0; i < n; i += stride) fn(v[i]);
+  }
+};
+// Compacted candidates in the workspace: segment s (chunk s of the row) holds
+// soff[s+1]-soff[s] entries from token offset sbase[s]; entry k of the
+// concatenation is found by a scan over the (at most kSplitMax) segments.
+template <int kBatch>
+struct GlobSeg {
+  const double *x;
+  const int *soff;   // LDS, [nseg + 1] first entry of each segment
+  const int *sbase;  // LDS, [nseg]     token offset where each segment starts
+  int nseg, n;
+  __device__ __forceinline__ int addr(int k) const {
+    int s = 0;
+    while (s + 1 < nseg && soff[s + 1] <= k) ++s;
+    return sbase[s] + (k - soff[s]);
   }
   template <typename Fn>
-  __device__ void for_each(Fn &&fn) const {
+  __device__ __forceinline__ void each(Fn &&fn) const {
 #pragma unroll 1
-    for (int i = threadIdx.x; i < ns; i += kDThreads) fn(i, xl[i]);
-#pragma unroll 1
-    for (int base = ns; base < n; base += 8 * kDThreads) {
-      double v[8];
+    for (int base = 0; base < n; base += kBatch * kDThreads) {
+      double v[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ld_agent(&X[min(base + u * kDThreads + (int)threadIdx.x, n - 1)]);
-#pragma unroll 1
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kDThreads + threadIdx.x;
-        if (i < n) fn(i, v[u]);
-      }
+      for (int u = 0; u < kBatch; ++u) v[u] = ld_agent(&x[addr(min(base + u * kDThreads + (int)threadIdx.x, n - 1))]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (base + u * kDThreads + (int)threadIdx.x < n) fn(v[u]);
     }
   }
-  __device__ double at(int i) const { return i < ns ? xl[i] : ld_agent(&X[i]); }
 };
 
-// Root of F(t) = sum [X - t]_+^beta = 1: safeguarded Newton from the left.
-__device__ __noinline__ double solve_tau(const RowScores &rs, const DecodeParams &dp, double *dred) {
-  double mx = -INFINITY, cnt = 0.0;
-  rs.for_each([&](int, double x) { if (x > -INFINITY) { mx = fmax(mx, x); cnt += 1.0; } });
-  mx = block_max(mx, dred);
-  cnt = block_sum(cnt, dred);
-  double lo = mx - 1.0;               // F(lo) >= 1
-  double hi = mx - pow(cnt, -dp.a);   // F(hi) <= 1
+// Candidates held in registers: thread t owns entries t, t + 256, ...
+constexpr int kRegPer = 32;
+struct RegVals {
+  const double (&v)[kRegPer];
+  int n;
+  template <typename Fn>
+  __device__ __forceinline__ void each(Fn &&fn) const {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j)
+      if ((int)threadIdx.x + j * kDThreads < n) fn(v[j]);
+  }
+};
+struct WaveRed {
+  __device__ __forceinline__ double operator()(double v, double *) const { return wave_sum(v); }
+};
+struct BlockRed {
+  __device__ __forceinline__ double operator()(double v, double *s) const { return block_sum(v, s); }
+};
+
+// Root of F(t) = sum [X - t]_+^beta = 1 by Newton from the left: lo = mx - 1
+// has F >= 1, hi = mx - n^-(alpha-1) has F <= 1 (n >= the number of scores
+// above hi).  For alpha <= 2 (beta >= 1) F is convex and decreasing, so every
+// Newton iterate from the left stays left of the root: one pass per step.
+// Otherwise each Newton candidate is checked with a second pass; one that
+// leaves (lo, hi) becomes a bisection step, and after a step lands right of
+// the root the next step bisects.
+template <int kB, typename Src, typename Red>
+__device__ __forceinline__ double newton_tau(const Src &src, double n, double mx, const DecodeParams &dp,
+                                             double *dred) {
+  const Red red;
+  double lo = mx - 1.0;
+  double hi = mx - pow(n, -dp.a);
   if (!(hi > lo)) return lo;
+  if (kB != 0 || dp.beta >= 1.0) {
+#pragma unroll 1
+    for (int it = 0; it < 200; ++it) {
+      double f = 0.0, fp = 0.0;
+      src.each([&](double x) {
+        const double y = x - lo;
+        if (y > 0.0) { f += pw<kB>(y, dp); fp += pw_d<kB>(y, dp); }
+      });
+      f = red(f, dred);
+      fp = red(fp, dred);
+      if (!(f > 1.0) || !(fp > 0.0)) break;  // at the root (to rounding)
+      const double cand = lo + (f - 1.0) / fp;
+      if (!(cand > lo)) break;                 // no progress: converged
+      if (!(cand < hi)) break;                 // only through rounding, next to the root
+      lo = cand;
+    }
+    return lo;
+  }
   bool bisect_next = false;
 #pragma unroll 1
   for (int it = 0; it < 400; ++it) {
@@ -153,12 +232,12 @@ __device__ __noinline__ double solve_tau(const RowScores &rs, const DecodeParams
       cand = 0.5 * (lo + hi);
     } else {
       double f = 0.0, fp = 0.0;
-      rs.for_each([&](int, double x) {
+      src.each([&](double x) {
         const double y = x - lo;
-        if (y > 0.0) { f += entw(y, dp); fp += entw_d(y, dp); }
+        if (y > 0.0) { f += pw<kB>(y, dp); fp += pw_d<kB>(y, dp); }
       });
-      f = block_sum(f, dred);
-      fp = block_sum(fp, dred);
+      f = red(f, dred);
+      fp = red(fp, dred);
       cand = fp > 0.0 ? lo + (f - 1.0) / fp : 0.5 * (lo + hi);
       if (!(cand > lo) || !(cand < hi)) {
         if (!(cand > lo) && f >= 1.0) break;  // Newton makes no progress: converged
@@ -167,11 +246,11 @@ __device__ __noinline__ double solve_tau(const RowScores &rs, const DecodeParams
     }
     if (cand == lo || cand == hi) break;
     double f = 0.0;
-    rs.for_each([&](int, double x) {
+    src.each([&](double x) {
       const double y = x - cand;
-      if (y > 0.0) f += entw(y, dp);
+      if (y > 0.0) f += pw<kB>(y, dp);
     });
-    f = block_sum(f, dred);
+    f = red(f, dred);
     if (f >= 1.0) { lo = cand; bisect_next = false; }
     else { hi = cand; bisect_next = true; }
   }
@@ -181,13 +260,16 @@ __device__ __noinline__ double solve_tau(const RowScores &rs, const DecodeParams
 // sparsemax closed form (Martins & Astudillo 2016) by a bitonic sort in LDS:
 // sort z descending; k* = max{k : 1 + k z_(k) > sum_{j<=k} z_(j)};
 // tau = (sum_{j<=k*} z_(j) - 1) / k*.  The condition holds exactly for k <= k*.
-__device__ double sparsemax_tau_sort(const RowScores &rs, double *buf, double *dred) {
-  const int n = rs.n;
+// Only the candidates are sorted: every score outside them is below tau.
+__device__ double sparsemax_tau_sort(const double *cx, int n, double *buf, double *dred, int *s_kstar) {
   int m = 1;
   while (m < n) m <<= 1;
-  for (int i = threadIdx.x; i < m; i += kDThreads) buf[i] = i < n ? rs.at(i) : -INFINITY;
+  for (int i = threadIdx.x; i < m; i += kDThreads) buf[i] = i < n ? cx[i] : -INFINITY;
+  if (threadIdx.x == 0) *s_kstar = 0;
   __syncthreads();
+#pragma unroll 1
   for (int kk = 2; kk <= m; kk <<= 1) {
+#pragma unroll 1
     for (int j = kk >> 1; j > 0; j >>= 1) {
       for (int i = threadIdx.x; i < m; i += kDThreads) {
         const int ixj = i ^ j;
@@ -200,199 +282,399 @@ __device__ double sparsemax_tau_sort(const RowScores &rs, double *buf, double *d
       __syncthreads();
     }
   }
-  __shared__ double wsum[kDThreads / kWave];
-  __shared__ int s_kstar;
-  if (threadIdx.x == 0) s_kstar = 0;
-  __syncthreads();
   double carry = 0.0;
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+#pragma unroll 1
   for (int c0 = 0; c0 < n; c0 += kDThreads) {
     const int k = c0 + threadIdx.x;
     const double z = k < n ? buf[k] : 0.0;
-    const bool finite = z > -INFINITY;
-    double x = finite ? z : 0.0;
+    double x = z;
+#pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const double y = __shfl_up(x, o, kWave);
       if (lane >= o) x += y;
     }
-    if (lane == kWave - 1) wsum[wv] = x;
+    __syncthreads();
+    if (lane == kWave - 1) dred[wv] = x;
     __syncthreads();
     double off = carry, tot = 0.0;
     for (int i = 0; i < kDThreads / kWave; ++i) {
-      if (i < wv) off += wsum[i];
-      tot += wsum[i];
+      if (i < wv) off += dred[i];
+      tot += dred[i];
     }
-    if (k < n && finite && 1.0 + (double)(k + 1) * z > off + x) atomicMax(&s_kstar, k + 1);
-    __syncthreads();
+    if (k < n && 1.0 + (double)(k + 1) * z > off + x) atomicMax(s_kstar, k + 1);
     carry += tot;
   }
-  const int ks = s_kstar > 0 ? s_kstar : 1;
+  __syncthreads();
+  const int ks = *s_kstar > 0 ? *s_kstar : 1;
   double part = 0.0;
   for (int k = threadIdx.x; k < ks; k += kDThreads) part += buf[k];
   part = block_sum(part, dred);
   return (part - 1.0) / (double)ks;
 }
 
-template <typename T, int DIM>
-__global__ __launch_bounds__(kDThreads) void entmax_decode_kernel(
+// Threshold tau and normalizer z = sum p of a row from its candidates, which
+// sit in LDS (tier 0), in registers (tier 1, not for generic alpha) or in the
+// workspace (tier 2).
+template <int kB>
+__device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, double mx, int total, const double *cx,
+                                          double *sortbuf, const double (&rx)[kRegPer], const GlobSeg<1> &gs,
+                                          double *dred, int *s_kstar, double *s_tau, double &tau, double &z) {
+  const int tid = threadIdx.x;
+  const GlobSeg<8> gs8{gs.x, gs.soff, gs.sbase, gs.nseg, gs.n};
+  if (tier == 0 && kB == 1 && dp.tau_method == 1) {
+    tau = sparsemax_tau_sort(cx, total, sortbuf, dred, s_kstar);
+  } else if (tier == 0) {
+    if (tid < kWave) {
+      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, dp, dred);
+      if (tid == 0) *s_tau = t;
+    }
+    __syncthreads();
+    tau = *s_tau;
+  } else if (kB != 0 && tier == 1) {
+    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, dp, dred);
+  } else if (kB != 0) {
+    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, dp, dred);
+  } else {
+    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, dp, dred);
+  }
+  double zz = 0.0;
+  auto zsum = [&](double x) { const double y = x - tau; if (y > 0.0) zz += pw<kB>(y, dp); };
+  if (tier == 0) LdsVals{cx, total, tid, kDThreads}.each(zsum);
+  else if (kB != 0 && tier == 1) RegVals{rx, total}.each(zsum);
+  else if (kB != 0) gs8.each(zsum);
+  else gs.each(zsum);
+  z = block_sum(zz, dred);
+}
+
+// ---------------------------------------------------------------- kernel 1: scores
+template <typename T, int DIM, int P>
+__global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
     Dims D, DecodeParams dp, const T *__restrict__ q, const T *__restrict__ k_pool,
-    const T *__restrict__ v_pool, const int32_t *__restrict__ page_table,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ sel_idx,
-    const int32_t *__restrict__ sel_cnt, float *__restrict__ out, double *__restrict__ tau_out,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt,
     float *__restrict__ weights_out, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kGroups = kDThreads / DIM;  // support entries processed in parallel
+  constexpr int kParts = kDThreads / P;  // threads per token
+  constexpr int kPer = DIM / kParts;     // coordinates per thread
   __shared__ double dred[kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
-  __shared__ double qs[DIM];
-  __shared__ int s_last;
-  __shared__ size_t sup_off[kSupChunk];
-  __shared__ float sup_w[kSupChunk];
-  __shared__ float accs[kGroups][DIM];
   const int rows = D.B * D.Hq;
   int *prefix = reinterpret_cast<int *>(smem);
-  double *xstage = reinterpret_cast<double *>(smem + (((rows + 1) * 4 + 15) & ~15));
-  double *sortbuf = xstage + kStage;
-  const int total = build_item_map(D, dp, seq_lens, sel_cnt, prefix, rows, scan_scratch);
-  const int P = D.P;
-  const size_t wrow = (size_t)D.max_pages * P;
-
-  // rows without items: their results are defined here (no last block will come)
-  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
-    bool bad;
-    const int c = row_items(D, dp, seq_lens, sel_cnt, r, &bad);
-    if (c != 0) continue;
-    if (threadIdx.x == 0 && tau_out) tau_out[r] = NAN;
-    for (int i = threadIdx.x; i < DIM; i += kDThreads) out[(size_t)r * DIM + i] = bad ? NAN : 0.0f;
-    if (weights_out)
-      for (size_t i = threadIdx.x; i < wrow; i += kDThreads) st_agent(&weights_out[(size_t)r * wrow + i], 0.0f);
-  }
-
-  const int parts = kDThreads / P;  // threads per token
-  const int per = DIM / parts;      // coordinates per thread
-  const int tok = threadIdx.x / parts, part = threadIdx.x % parts;
+  const int tid = threadIdx.x;
+  // kernel 2's arrival counters start at zero
+  for (int r = blockIdx.x * kDThreads + tid; r < rows; r += gridDim.x * kDThreads) ws.ctr[r] = 0u;
+  const int total = build_item_map(D, seq_lens, sel_cnt, prefix, rows, scan_scratch);
+  const int MP = D.max_pages;
+  const size_t wrow = (size_t)MP * P;
+  const int tok = tid / kParts, part = tid % kParts;
+#pragma unroll 1
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int r = find_row(prefix, rows, item);
     const int i = item - prefix[r];
-    const int b = r / D.Hq, h = r % D.Hq, g = h / D.G;
+    const int cnt = prefix[r + 1] - prefix[r];
+    const int b = r / D.Hq, g = (r % D.Hq) / D.G;
+    // independent loads first: sequence length, page ids, the query slice
     const int L = seq_len_clamped(seq_lens, b, D);
+    const int p = sel_idx[(size_t)r * MP + i];
+    const int prev = i > 0 ? sel_idx[(size_t)r * MP + i - 1] : -1;
+    float qv[kPer];
+    load_vec<kPer>(q + (size_t)r * DIM + part * kPer, qv);
     const int np = n_pages_of(L, P);
-    bool row_bad;
-    const int cnt = row_items(D, dp, seq_lens, sel_cnt, r, &row_bad);
-    bool bad_item = false;
-    int p = i, prev = i - 1;
-    if (!dp.full) {
-      p = sel_idx[(size_t)r * D.max_pages + i];
-      prev = i > 0 ? sel_idx[(size_t)r * D.max_pages + i - 1] : -1;
-      if (p < 0 || p >= np || prev >= p) bad_item = true;
+    const int pc = min(max(p, 0), MP - 1);
+    const int phys = page_table[(size_t)b * MP + pc];
+    const bool bad_item = p < 0 || p >= np || prev >= p || phys < 0 || phys >= D.num_phys;
+    const int physc = min(max(phys, 0), D.num_phys - 1);
+    const int n = min(P, L - pc * P);
+    float kv[kPer];
+    load_vec<kPer>(k_pool + (((size_t)physc * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
+    double acc = 0.0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[e], acc);
+#pragma unroll
+    for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    const double x = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
+    if (part == 0) ws.xs[(size_t)r * wrow + (size_t)i * P + tok] = x;
+    const double pm = block_max(x, dred);
+    if (tid == 0) {
+      ws.pmax[(size_t)r * MP + i] = bad_item ? NAN : pm;
+      ws.iphys[(size_t)r * MP + i] = (uint32_t)physc;
     }
-    int phys = -1;
-    if (!bad_item) {
-      phys = page_table[(size_t)b * D.max_pages + p];
-      if (phys < 0 || phys >= D.num_phys) bad_item = true;
+    // weights_out: zero every slot of the pages this item covers, (prev, p]
+    // (the last item also covers the pages after p); kernel 2 writes the
+    // support weights.
+    if (weights_out && !bad_item) {
+      const size_t lo_s = (size_t)(prev + 1) * P;
+      const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
+      for (size_t s = lo_s + tid; s < hi_s; s += kDThreads) weights_out[(size_t)r * wrow + s] = 0.0f;
     }
-    double *xrow = ws.xs + (size_t)r * wrow;
-    __syncthreads();
-    for (int t = threadIdx.x; t < DIM; t += kDThreads) qs[t] = (double)load_f<T>(q, (size_t)r * DIM + t);
-    __syncthreads();
-    if (bad_item) {
-      if (threadIdx.x == 0) st_agent(&ws.badf[r], ws.epoch);  // benign race: every writer stores the epoch
-      for (int j = threadIdx.x; j < P; j += kDThreads) st_agent(&xrow[(size_t)i * P + j], -INFINITY);
-    } else {
-      const int n = min(P, L - p * P);
-      const T *kp = k_pool + (((size_t)phys * D.Hkv + g) * P + tok) * DIM + part * per;
-      double acc = 0.0;
-      if (tok < n) {
-#pragma unroll 8
-        for (int e = 0; e < per; ++e) acc = __builtin_fma((double)load_f<T>(kp, e), qs[part * per + e], acc);
-      }
-      for (int o = parts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-      if (part == 0) st_agent(&xrow[(size_t)i * P + tok], tok < n ? dp.a * (dp.c * acc) : -INFINITY);
-      // weights_out: zero every slot of the pages this item covers, (prev, p]
-      // (the last item also covers the pages after p); the support weights are
-      // written later by the row's last block.
-      if (weights_out) {
-        const size_t lo_s = (size_t)(prev + 1) * P;
-        const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
-        for (size_t s = lo_s + threadIdx.x; s < hi_s; s += kDThreads)
-          st_agent(&weights_out[(size_t)r * wrow + s], 0.0f);
-      }
-    }
-    if (!arrive_last_ep(&ws.ctr[r], ws.epoch, (unsigned)cnt, &s_last)) continue;
+  }
+}
 
-    // ================= last item of row r: threshold, normalizer, output
-    const bool badrow = row_bad || ld_agent(&ws.badf[r]) == ws.epoch;
-    if (badrow) {
-      if (threadIdx.x == 0 && tau_out) tau_out[r] = NAN;
-      for (int c2 = threadIdx.x; c2 < DIM; c2 += kDThreads) out[(size_t)r * DIM + c2] = NAN;
-      continue;
+// ------------------------------------------------ kernel 2: threshold and output
+template <typename T, int DIM, int P>
+__global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
+    Dims D, DecodeParams dp, const T *__restrict__ v_pool, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt, float *__restrict__ out,
+    double *__restrict__ tau_out, float *__restrict__ weights_out, DecodeWs ws) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kTpe = DIM / 8;           // threads per support entry in the V gather
+  constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
+  __shared__ double dred[kDThreads / kWave];
+  __shared__ int scan_scratch[kDThreads / kWave];
+  __shared__ int s_last, s_kstar;
+  __shared__ double s_tau;
+  __shared__ int soff[kSplitMax + 1], sbase[kSplitMax];
+  __shared__ uint32_t sup_v[kSupChunk];
+  __shared__ int sup_i[kSupChunk];
+  __shared__ float sup_w[kSupChunk];
+  __shared__ float accs[kEpp][DIM + 1];
+  double *cx = reinterpret_cast<double *>(smem);              // [kCand] candidate X
+  int *ci = reinterpret_cast<int *>(cx + kCand);              // [kCand] token index
+  uint32_t *cv = reinterpret_cast<uint32_t *>(ci + kCand);    // [kCand] V row index
+  double *sortbuf = reinterpret_cast<double *>(cv + kCand);   // [kCand] (sort form only)
+  const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int MP = D.max_pages;
+  const size_t wrow = (size_t)MP * P;
+  const int g = (r % D.Hq) / D.G;
+  bool bad;
+  const int cnt = row_items(D, seq_lens, sel_cnt, r, &bad);
+  if (cnt == 0) {
+    if (c == 0) {
+      if (tid == 0 && tau_out) tau_out[r] = NAN;
+      for (int i = tid; i < DIM; i += kDThreads) out[(size_t)r * DIM + i] = bad ? NAN : 0.0f;
+      if (weights_out)
+        for (size_t i = tid; i < wrow; i += kDThreads) weights_out[(size_t)r * wrow + i] = 0.0f;
     }
-    const int nX = cnt * P;
-    RowScores rs;
-    rs.load(xrow, nX, xstage);
-    double tau;
-    if (dp.tau_method == 1 && dp.ibeta == 1 && nX <= kSortMax) tau = sparsemax_tau_sort(rs, sortbuf, dred);
-    else tau = solve_tau(rs, dp, dred);
-    double z = 0.0;
-    rs.for_each([&](int, double x) {
-      const double y = x - tau;
-      if (y > 0.0) z += entw(y, dp);
-    });
-    z = block_sum(z, dred);
-    if (threadIdx.x == 0 && tau_out) tau_out[r] = tau / dp.a;
+    return;
+  }
+  const int nX = cnt * P;
+  const int nsplit = min((int)gridDim.y, (nX + kChunkTok - 1) / kChunkTok);
+  if (c >= nsplit) return;
+  const double *pmr = ws.pmax + (size_t)r * MP;
+  const uint32_t *ipr = ws.iphys + (size_t)r * MP;
+  double *xrow = ws.xs + (size_t)r * wrow;
+  uint32_t *xir = ws.xi + (size_t)r * wrow;
 
-    // support gather: compact (V row offset, weight, weight slot) in index
-    // order, chunk by chunk.  The thread that takes an entry resolves its page
-    // (one round of dependent loads, in parallel across entries); the groups of
-    // DIM threads then add p_t * v_t with independent loads, in a fixed order.
-    const int grp = threadIdx.x / DIM, c2 = threadIdx.x % DIM;
-    float acc = 0.0f;
-    int base_cnt = 0;
-    auto flush = [&](int nsup) {
-      __syncthreads();
-      int e = grp;
-      for (; e + 3 * kGroups < nsup; e += 4 * kGroups) {
-        const float v0 = load_f<T>(v_pool, sup_off[e] + c2);
-        const float v1 = load_f<T>(v_pool, sup_off[e + kGroups] + c2);
-        const float v2 = load_f<T>(v_pool, sup_off[e + 2 * kGroups] + c2);
-        const float v3 = load_f<T>(v_pool, sup_off[e + 3 * kGroups] + c2);
-        acc += sup_w[e] * v0;
-        acc += sup_w[e + kGroups] * v1;
-        acc += sup_w[e + 2 * kGroups] * v2;
-        acc += sup_w[e + 3 * kGroups] * v3;
-      }
-      for (; e < nsup; e += kGroups) acc += sup_w[e] * load_f<T>(v_pool, sup_off[e] + c2);
-      __syncthreads();
-    };
-    auto take_entry = [&](int slot, int idx, float w) {
-      const int it = idx / P, j = idx % P;
-      const int pg = dp.full ? it : sel_idx[(size_t)r * D.max_pages + it];
-      const int ph = page_table[(size_t)b * D.max_pages + pg];
-      sup_off[slot] = (((size_t)ph * D.Hkv + g) * P + j) * DIM;
-      sup_w[slot] = w;
-      if (weights_out) st_agent(&weights_out[(size_t)r * wrow + (size_t)pg * P + j], w);
-    };
-    // in index order, one block-wide compaction step per 256 scores
+  // 1. row maximum from the page maxima; a NaN maximum marks a malformed item
+  double mx = -INFINITY;
+  int nan = 0;
 #pragma unroll 1
-    for (int i0 = 0; i0 < nX; i0 += kDThreads) {
-      const int ii = i0 + threadIdx.x;
-      const double y = (ii < nX ? rs.at(ii) : -INFINITY) - tau;
-      const int take = y > 0.0 ? 1 : 0;
+  for (int base = 0; base < cnt; base += 8 * kDThreads) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pmr[min(base + u * kDThreads + tid, cnt - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { mx = fmax(mx, v[u]); nan |= v[u] != v[u]; }
+  }
+  mx = block_max(mx, dred);
+  nan = __syncthreads_or(nan);
+  if (bad || nan) {
+    if (c == 0) {
+      if (tid == 0 && tau_out) tau_out[r] = NAN;
+      for (int i = tid; i < DIM; i += kDThreads) out[(size_t)r * DIM + i] = NAN;
+    }
+    return;
+  }
+  const double thr = mx - 1.0;  // tau >= thr
+
+  // 2. this chunk's candidates X > thr, compacted in index order to the
+  //    chunk's start in the workspace (and into LDS when this block is alone)
+  const int tlo = (int)((long long)c * cnt / nsplit) * P, thi = (int)((long long)(c + 1) * cnt / nsplit) * P;
+  const bool alone = nsplit == 1;
+  int ncand = 0;
+#pragma unroll 1
+  for (int base = tlo; base < thi; base += 8 * kDThreads) {
+    double v[8];
+    uint32_t ph[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = min(base + u * kDThreads + tid, thi - 1);
+      v[u] = xrow[t];
+      ph[u] = ipr[t / P];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (base + u * kDThreads >= thi) break;
+      const int t = base + u * kDThreads + tid;
+      const int take = (t < thi && v[u] > thr) ? 1 : 0;
       int tot;
-      const int pos = block_excl_scan(take, scan_scratch, &tot);
-      if (base_cnt + tot > kSupChunk) { flush(base_cnt); base_cnt = 0; }
-      if (take) take_entry(base_cnt + pos, ii, (float)(entw(y, dp) / z));
-      base_cnt += tot;
+      const int at = ncand + block_excl_scan(take, scan_scratch, &tot);
+      if (take) {
+        st_agent(&xrow[tlo + at], v[u]);
+        st_agent(&xir[tlo + at], (uint32_t)t);
+        if (alone && at < kCand) {
+          cx[at] = v[u];
+          ci[at] = t;
+          cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+        }
+      }
+      ncand += tot;
     }
-    flush(base_cnt);
-    accs[grp][c2] = acc;
-    __syncthreads();
-    for (int cc = threadIdx.x; cc < DIM; cc += kDThreads) {
-      float sacc = accs[0][cc];
-      for (int gi = 1; gi < kGroups; ++gi) sacc += accs[gi][cc];
-      out[(size_t)r * DIM + cc] = sacc;
+  }
+  int total = ncand;
+  if (!alone) {
+    if (tid == 0) st_agent(&ws.segcnt[(size_t)r * kSplitMax + c], ncand);
+    if (!arrive_last(&ws.ctr[r], (unsigned)nsplit, &s_last)) return;
+    // the row's last block: segment offsets, then the candidates into LDS
+    if (tid == 0) {
+      int run = 0;
+      for (int s2 = 0; s2 < nsplit; ++s2) {
+        soff[s2] = run;
+        sbase[s2] = (int)((long long)s2 * cnt / nsplit) * P;
+        run += ld_agent(&ws.segcnt[(size_t)r * kSplitMax + s2]);
+      }
+      soff[nsplit] = run;
     }
     __syncthreads();
+    total = soff[nsplit];
+    if (total <= kCand) {
+      const GlobSeg<1> gs{xrow, soff, sbase, nsplit, total};
+#pragma unroll 1
+      for (int base = 0; base < total; base += 4 * kDThreads) {
+        double v[4];
+        uint32_t t[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int a = gs.addr(min(base + u * kDThreads + tid, total - 1));
+          v[u] = ld_agent(&xrow[a]);
+          t[u] = ld_agent(&xir[a]);
+        }
+        uint32_t ph[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ph[u] = ipr[t[u] / P];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int k = base + u * kDThreads + tid;
+          if (k < total) {
+            cx[k] = v[u];
+            ci[k] = (int)t[u];
+            cv[k] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
+          }
+        }
+      }
+    }
+  } else if (tid == 0) {
+    soff[0] = 0;
+    soff[1] = total;
+    sbase[0] = 0;
+  }
+  __syncthreads();
+  // candidate tiers: LDS (one wave solves), registers (block), workspace passes
+  const int tier = total <= kCand ? 0 : ((total <= kRegPer * kDThreads && dp.ibeta != 0) ? 1 : 2);
+  const int nseg = alone ? 1 : nsplit;
+  const GlobSeg<1> gs{xrow, soff, sbase, nseg, total};
+  double rx[kRegPer];
+  uint32_t ri[kRegPer];
+  if (tier == 1) {
+#pragma unroll
+    for (int j = 0; j < kRegPer; ++j) {
+      const int a = gs.addr(min(tid + j * kDThreads, total - 1));
+      rx[j] = ld_agent(&xrow[a]);
+      ri[j] = ld_agent(&xir[a]);
+    }
+  }
+
+  // 3. threshold and normalizer
+  double tau, z;
+  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  else solve_row<0>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  if (tid == 0 && tau_out) tau_out[r] = tau / dp.a;
+
+  // 4. support gather, chunk by chunk in index order: compact (token, weight;
+  //    V row when known), then kEpp entries at a time, kTpe threads per
+  //    entry, each thread 8 coordinates with one 16-byte load; fixed-order
+  //    final sum.
+  const int ge = tid / kTpe, gc = tid % kTpe;
+  float acc8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc8[u] = 0.0f;
+  int nsup = 0;
+  const bool resolve = tier != 0;  // V rows looked up per flush from the item's physical page
+  auto flush = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+    if (resolve) {
+      for (int k = tid; k < nsup; k += kDThreads) {
+        const uint32_t t = (uint32_t)sup_i[k];
+        sup_v[k] = (ipr[t / P] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t % P;
+      }
+      __syncthreads();
+    }
+    int e = ge;
+#pragma unroll 1
+    for (; e + kEpp < nsup; e += 2 * kEpp) {
+      float v0[8], v1[8];
+      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sup_v[e + kEpp] * DIM + gc * 8, v1);
+      const float w0 = sup_w[e], w1 = sup_w[e + kEpp];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w1 * v1[u];
+    }
+    if (e < nsup) {
+      float v0[8];
+      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
+      const float w0 = sup_w[e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
+    }
+    if (weights_out) {
+      for (int k = tid; k < nsup; k += kDThreads) {
+        const int pg = sel_idx[(size_t)r * MP + sup_i[k] / P];
+        weights_out[(size_t)r * wrow + (size_t)pg * P + sup_i[k] % P] = sup_w[k];
+      }
+    }
+    __syncthreads();
+    nsup = 0;
+  };
+  // one compaction step over 256 entries (x, token, V row) in index order
+  auto step = [&](double xk, int ik, uint32_t vk) __attribute__((always_inline)) {
+    const double y = xk - tau;
+    const int take = y > 0.0 ? 1 : 0;
+    int tot;
+    const int pos = block_excl_scan(take, scan_scratch, &tot);
+    if (nsup + tot > kSupChunk) flush();
+    if (take) {
+      sup_v[nsup + pos] = vk;
+      sup_i[nsup + pos] = ik;
+      sup_w[nsup + pos] = (float)(entw(y, dp) / z);
+    }
+    nsup += tot;
+  };
+  if (tier == 0) {
+#pragma unroll 1
+    for (int k0 = 0; k0 < total; k0 += kDThreads) {
+      const int k = k0 + tid;
+      step(k < total ? cx[k] : -INFINITY, k < total ? ci[k] : 0, k < total ? cv[k] : 0u);
+    }
+  } else if (tier == 1) {
+    // registers rotate down one slot per step, so every access has a fixed index
+#pragma unroll 1
+    for (int k0 = 0; k0 < total; k0 += kDThreads) {
+      step(k0 + tid < total ? rx[0] : -INFINITY, (int)ri[0], 0u);
+#pragma unroll
+      for (int j = 0; j + 1 < kRegPer; ++j) { rx[j] = rx[j + 1]; ri[j] = ri[j + 1]; }
+    }
+  } else {
+#pragma unroll 1
+    for (int k0 = 0; k0 < total; k0 += kDThreads) {
+      const int k = k0 + tid;
+      const int a = gs.addr(min(k, total - 1));
+      const double xv = ld_agent(&xrow[a]);
+      const uint32_t t = ld_agent(&xir[a]);
+      step(k < total ? xv : -INFINITY, (int)t, 0u);
+    }
+  }
+  flush();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) accs[ge][gc * 8 + u] = acc8[u];
+  __syncthreads();
+  for (int cc = tid; cc < DIM; cc += kDThreads) {
+    float s = accs[0][cc];
+    for (int e = 1; e < kEpp; ++e) s += accs[e][cc];
+    out[(size_t)r * DIM + cc] = s;
   }
 }
 
@@ -401,9 +683,11 @@ static DecodeWs carve_decode(const Dims &D, void *base, size_t *bytes) {
   const size_t rows = (size_t)D.B * D.Hq;
   DecodeWs w;
   w.xs = cv.take<double>(rows * D.max_pages * D.P);
-  w.badf = cv.take<unsigned long long>(rows);
-  w.ctr = cv.take<unsigned long long>(rows);
-  w.epoch = 0;
+  w.xi = cv.take<uint32_t>(rows * D.max_pages * D.P);
+  w.pmax = cv.take<double>(rows * D.max_pages);
+  w.iphys = cv.take<uint32_t>(rows * D.max_pages);
+  w.segcnt = cv.take<int>(rows * kSplitMax);
+  w.ctr = cv.take<unsigned int>(rows);
   if (bytes) *bytes = cv.bytes();
   return w;
 }
@@ -414,29 +698,40 @@ size_t decode_ws_bytes(const Dims &D, bool) {
   return b;
 }
 
-template <typename T, int DIM>
+template <typename T, int DIM, int P>
 static hipError_t launch_decode_t(const Dims &D, const DecodeParams &dp, const void *q,
                                   const void *k_pool, const void *v_pool, const int32_t *page_table,
                                   const int32_t *seq_lens, const int32_t *sel_idx,
                                   const int32_t *sel_cnt, float *out, double *tau,
                                   float *weights_out, void *ws, hipStream_t s) {
-  DecodeWs w = carve_decode(D, ws, nullptr);
-  w.epoch = next_epoch();
+  const DecodeWs w = carve_decode(D, ws, nullptr);
   const int rows = D.B * D.Hq;
-  const size_t map_bytes = (((size_t)(rows + 1) * 4 + 15) & ~(size_t)15);
-  const size_t smem = map_bytes + (size_t)kStage * sizeof(double) +
-                      (dp.tau_method == 1 ? (size_t)kSortMax * sizeof(double) : 0);
+  const size_t map_bytes = (size_t)(rows + 1) * 4;
+  hipLaunchKernelGGL((decode_scores_kernel<T, DIM, P>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
+                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t cand_bytes = (size_t)kCand * (8 + 4 + 4) + (dp.tau_method == 1 ? (size_t)kCand * 8 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    // largest dynamic LDS any shape can ask for: item map of 8192 rows + stage + sort buffer
-    hipFuncSetAttribute((const void *)entmax_decode_kernel<T, DIM>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)(((8193 * 4 + 15) & ~15) + (size_t)(kStage + kSortMax) * sizeof(double)));
+    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)((size_t)kCand * (8 + 4 + 4 + 8)));
     attr_set = true;
   }
-  hipLaunchKernelGGL((entmax_decode_kernel<T, DIM>), dim3(kDGrid), dim3(kDThreads), smem, s, D, dp,
-                     (const T *)q, (const T *)k_pool, (const T *)v_pool, page_table, seq_lens, sel_idx,
-                     sel_cnt, out, tau, weights_out, w);
+  const long long chunks = ((long long)D.max_pages * D.P + kChunkTok - 1) / kChunkTok;
+  const int split = (int)(chunks < kSplitMax ? chunks : kSplitMax);
+  hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P>), dim3(rows, split), dim3(kDThreads), cand_bytes, s, D, dp,
+                     (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
   return hipGetLastError();
+}
+
+template <typename T, int DIM>
+static hipError_t launch_decode_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
+                                  const void *v_pool, const int32_t *pt, const int32_t *sl, const int32_t *si,
+                                  const int32_t *sc, float *out, double *tau, float *wo, void *ws, hipStream_t s) {
+  if (D.P == 16) return launch_decode_t<T, DIM, 16>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
+  if (D.P == 32) return launch_decode_t<T, DIM, 32>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
+  return launch_decode_t<T, DIM, 64>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
 }
 
 hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const void *k_pool,
@@ -450,13 +745,12 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
   dp.c = D.scale;
   dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
   dp.tau_method = tau_method;
-  dp.full = sel_idx == nullptr ? 1 : 0;
   if (dtype == ENTMAXKV_BF16) {
-    if (D.d == 64) return launch_decode_t<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-    return launch_decode_t<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+    if (D.d == 64) return launch_decode_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+    return launch_decode_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
   }
-  if (D.d == 64) return launch_decode_t<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-  return launch_decode_t<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+  if (D.d == 64) return launch_decode_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+  return launch_decode_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
 }
 
 }  // namespace ekv

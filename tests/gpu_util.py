@@ -74,6 +74,33 @@ class Dev:
                 t.full((i.B, i.Hq), -1, dtype=t.int32, device="cuda"))
 
 
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def decode_check(inp, D, alpha, sel_o, cnt_o, full=False, tau_method=0):
+    """Run one entmax decode call and compare out, tau, support and weights with the oracle."""
+    t = torch()
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
+    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    w = t.full((inp.B, inp.Hq, inp.max_pages * inp.P), np.nan, dtype=t.float32, device="cuda")
+    if full:
+        E.entmax_decode_full(D.shape, D.q, D.k, D.v, D.pt, D.sl, alpha, out, tau=tau, weights_out=w,
+                             tau_method=tau_method)
+        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
+                                          inp.seq_lens, alpha, want_weights=True)
+    else:
+        E.entmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(sel_o).cuda(),
+                               t.from_numpy(cnt_o).cuda(), alpha, out, tau=tau, weights_out=w,
+                               tau_method=tau_method)
+        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
+                                          inp.seq_lens, alpha, sel_o, cnt_o, want_weights=True)
+    og, tg, wg = out.cpu().numpy(), tau.cpu().numpy(), w.cpu().numpy()
+    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(wg > 0, wo > 0), "support differs"
+    assert np.max(np.abs(wg - wo)) < 1e-5
+    assert rel_l2_rows(og, oo) <= TOL[inp.dtype]
+
+
 def rel_l2_rows(a, b):
     """max over rows of ||a - b|| / ||b|| (rows = all but the last axis)."""
     a = np.asarray(a, np.float64).reshape(-1, np.shape(a)[-1])

@@ -1,0 +1,62 @@
+"""GPU parity of the entmax decodes on long selections.
+
+Rows here keep more than one chunk of tokens (the sparse decode then splits a
+row over several blocks and merges their candidates), and with a small score
+scale more candidates than fit in LDS (the threshold is then solved over the
+candidates in the workspace).  Same bars as the small cases: thresholds to
+1e-12, bit-exact supports, weights to 1e-5, outputs to the KV-dtype tolerance.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import Dev, decode_check
+from sparse_decode_attention_page_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+# score scales: default 1/sqrt(d) (few candidates), 0.08 (a few thousand
+# candidates, small support), 0.002 (every token a candidate and in the support)
+SCALES = [0.0, 0.08, 0.002]
+
+
+@pytest.fixture(scope="module", params=SCALES, ids=lambda s: f"scale{s}")
+def large(request):
+    inp = synth.random_small(11, B=2, Hq=4, Hkv=2, d=64, P=16, dtype="bf16", ctx=(20000, 9001),
+                             planted_per_kv=5)
+    return inp, Dev(inp, scale=request.param)
+
+
+def _selections(inp, seed=5):
+    """Per row: all pages, a random half, a contiguous run, a single page."""
+    rng = np.random.default_rng(seed)
+    sel = np.full((inp.B, inp.Hq, inp.max_pages), -1, np.int32)
+    cnt = np.zeros((inp.B, inp.Hq), np.int32)
+    for b in range(inp.B):
+        npg = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        for h in range(inp.Hq):
+            kind = (b * inp.Hq + h) % 4
+            if kind == 0:
+                s = np.arange(npg)
+            elif kind == 1:
+                s = np.sort(rng.choice(npg, size=max(1, npg // 2), replace=False))
+            elif kind == 2:
+                lo = int(rng.integers(0, max(1, npg - 300)))
+                s = np.arange(lo, min(npg, lo + 300))
+            else:
+                s = np.array([npg - 1])
+            sel[b, h, :len(s)] = s
+            cnt[b, h] = len(s)
+    return sel, cnt
+
+
+@pytest.mark.parametrize("alpha,method", [(1.5, 0), (2.0, 0), (2.0, 1)])
+def test_entmax_decode_sparse_long_rows(large, alpha, method):
+    inp, D = large
+    sel, cnt = _selections(inp)
+    decode_check(inp, D, alpha, sel, cnt, tau_method=method)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_entmax_decode_full_long_rows(large, alpha):
+    inp, D = large
+    decode_check(inp, D, alpha, None, None, full=True)

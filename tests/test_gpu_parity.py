@@ -8,14 +8,12 @@ thresholds agree to 1e-12 relative.
 import numpy as np
 import pytest
 
-from gpu_util import Dev, host_raw, rel_l2_rows, sets_equal, torch
+from gpu_util import TOL, Dev, decode_check, host_raw, rel_l2_rows, sets_equal, torch
 from sparse_decode_attention_page_amd import synth
 import sparse_decode_attention_page_amd as E
 import oracle
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 SMALL = [
     # (seed, B, Hq, Hkv, d, P, dtype, ctx)
@@ -105,53 +103,30 @@ def test_select_gauss(case, alpha, delta):
     assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
 
 
-def _decode_check(inp, D, alpha, sel_o, cnt_o, full=False, tau_method=0):
-    t = torch()
-    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
-    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
-    w = t.full((inp.B, inp.Hq, inp.max_pages * inp.P), np.nan, dtype=t.float32, device="cuda")
-    if full:
-        E.entmax_decode_full(D.shape, D.q, D.k, D.v, D.pt, D.sl, alpha, out, tau=tau, weights_out=w,
-                             tau_method=tau_method)
-        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
-                                          inp.seq_lens, alpha, want_weights=True)
-    else:
-        E.entmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(sel_o).cuda(),
-                               t.from_numpy(cnt_o).cuda(), alpha, out, tau=tau, weights_out=w,
-                               tau_method=tau_method)
-        oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table,
-                                          inp.seq_lens, alpha, sel_o, cnt_o, want_weights=True)
-    og, tg, wg = out.cpu().numpy(), tau.cpu().numpy(), w.cpu().numpy()
-    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
-    assert np.array_equal(wg > 0, wo > 0), "support differs"
-    assert np.max(np.abs(wg - wo)) < 1e-5
-    assert rel_l2_rows(og, oo) <= TOL[inp.dtype]
-
-
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
 def test_entmax_decode_sparse_topk(case, alpha):
     inp, D, _, (box_o, _, _) = case
     so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, 7)
-    _decode_check(inp, D, alpha, so, co)
+    decode_check(inp, D, alpha, so, co)
 
 
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_entmax_decode_sparse_gauss(case, alpha):
     inp, D, _, (box_o, mu_o, var_o) = case
     so, co, _ = oracle.select_gauss(D.oshape, box_o, mu_o, var_o, inp.seq_lens, alpha, 0.5)
-    _decode_check(inp, D, alpha, so, co)
+    decode_check(inp, D, alpha, so, co)
 
 
 def test_entmax_decode_sparse_sort_alpha2(case):
     inp, D, _, (box_o, _, _) = case
     so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, 9)
-    _decode_check(inp, D, 2.0, so, co, tau_method=1)
+    decode_check(inp, D, 2.0, so, co, tau_method=1)
 
 
 @pytest.mark.parametrize("alpha", [1.5, 2.0])
 def test_entmax_decode_full(case, alpha):
     inp, D, _, _ = case
-    _decode_check(inp, D, alpha, None, None, full=True)
+    decode_check(inp, D, alpha, None, None, full=True)
 
 
 def test_softmax_decode_full(case):
