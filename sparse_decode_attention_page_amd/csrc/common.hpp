@@ -112,6 +112,53 @@ __device__ __forceinline__ T wave_max(T v) {
   return v;
 }
 
+// fp64 wave reductions on DPP: quad permutes and row rotates combine each row
+// of 16 lanes inside the VALU, then the four row results are read out with
+// readlane.  The order is fixed and the result is wave-uniform.  All 64 lanes
+// must be active.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+template <>
+__device__ __forceinline__ double wave_sum<double>(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppRor4>(v);
+  v += dpp_f64<kDppRor8>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+template <>
+__device__ __forceinline__ int wave_sum<int>(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRor4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRor8, 0xF, 0xF, false);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+template <>
+__device__ __forceinline__ double wave_max<double>(double v) {
+  v = fmax(v, dpp_f64<kDppXor1>(v));
+  v = fmax(v, dpp_f64<kDppXor2>(v));
+  v = fmax(v, dpp_f64<kDppRor4>(v));
+  v = fmax(v, dpp_f64<kDppRor8>(v));
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 // Block-wide sum with a deterministic order (waves combined in index order).
 // `scratch` must hold blockDim.x / 64 values; result valid in every thread.
 template <typename T>
@@ -124,6 +171,20 @@ __device__ __forceinline__ T block_sum(T v, T *scratch) {
   T s = scratch[0];
   for (int i = 1; i < nw; ++i) s += scratch[i];
   return s;
+}
+// Two block sums for the price of one barrier pair; `scratch` holds
+// 2 * blockDim.x / 64 values.
+__device__ __forceinline__ void block_sum2(double &a, double &b, double *scratch) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) { scratch[w] = a; scratch[nw + w] = b; }
+  __syncthreads();
+  double sa = scratch[0], sb = scratch[nw];
+  for (int i = 1; i < nw; ++i) { sa += scratch[i]; sb += scratch[nw + i]; }
+  a = sa;
+  b = sb;
 }
 template <typename T>
 __device__ __forceinline__ T block_max(T v, T *scratch) {
@@ -158,6 +219,35 @@ __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) 
   return base + x - v;
 }
 
+// ------------------------------------------------------------------ phase marks
+// EKV_MARK(kernel, phase) records the 100 MHz real-time clock per block and
+// phase in builds compiled with -DEKV_TRACE (timeline analysis of a kernel's
+// phases; each source file gets its own buffer and a dump function declared
+// with EKV_TRACE_DUMP).  Without EKV_TRACE both compile to nothing.
+#ifdef EKV_TRACE
+static __device__ unsigned long long ekv_trace_buf[8][1 << 15][8];
+#define EKV_MARK(K, PH)                                                                    \
+  do {                                                                                     \
+    if (threadIdx.x == 0)                                                                  \
+      ekv_trace_buf[(K)][(blockIdx.x + gridDim.x * blockIdx.y) & ((1 << 15) - 1)][(PH)] =  \
+          __builtin_amdgcn_s_memrealtime();                                                \
+  } while (0)
+#define EKV_TRACE_DUMP(NAME)                                                               \
+  extern "C" int NAME(void *host) {                                                        \
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(ekv_trace_buf), sizeof(ekv_trace_buf)); \
+  }                                                                                        \
+  extern "C" int NAME##_clear() {                                                          \
+    void *p = nullptr;                                                                     \
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(ekv_trace_buf)) != hipSuccess) return -1;        \
+    return (int)hipMemset(p, 0, sizeof(ekv_trace_buf));                                    \
+  }
+#else
+#define EKV_MARK(K, PH) \
+  do {                  \
+  } while (0)
+#define EKV_TRACE_DUMP(NAME)
+#endif
+
 // --------------------------------------------------------------------- sequences
 struct Dims {
   int B, Hq, Hkv, G, d, P, max_pages, num_phys;
@@ -173,13 +263,15 @@ __device__ __forceinline__ int seq_len_clamped(const int32_t *seq_lens, int b, c
 }
 __device__ __forceinline__ int n_pages_of(int L, int P) { return (L + P - 1) / P; }
 
-// Barrier that orders LDS accesses only.  __syncthreads() also waits for every
-// outstanding global load and store (vmcnt(0)), which would drain prefetches
-// that are meant to stay in flight across the barrier.
+// Barrier that orders LDS accesses only.  __syncthreads() waits for every
+// outstanding global load (vmcnt(0)), and so does a workgroup fence on LDS,
+// since LDS-DMA loads (global_load_lds) count as LDS writes tracked by vmcnt;
+// either would drain prefetches that are meant to stay in flight across the
+// barrier.  This one waits for the wave's LDS operations only; the memory
+// clobber keeps the compiler from moving memory accesses across it.  Data
+// arriving by LDS-DMA must be waited for explicitly (vmcnt) before it.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // ----------------------------------------------------- cross-block handoff

@@ -39,6 +39,7 @@ constexpr int kChunkTok = 4096;   // kernel 2: tokens per chunk block
 constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
 constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
 constexpr int kSupChunk = 512;    // support entries gathered per LDS pass
+constexpr int kNThr = 8;          // count thresholds mx - 2^-i behind the certified bound on tau
 
 struct DecodeWs {
   double *xs;        // [rows][max_pages*P]  X of kept tokens (item-major); kernel 2 compacts
@@ -47,6 +48,7 @@ struct DecodeWs {
   double *pmax;      // [rows][max_pages]    max X over item i's tokens, NaN if the item is malformed
   uint32_t *iphys;   // [rows][max_pages]    physical page of item i
   int *segcnt;       // [rows][kSplitMax]    candidates of each chunk
+  double *segL;      // [rows][kSplitMax]    each chunk's lower bound on tau
   unsigned int *ctr; // [rows]               arrival counters (zeroed by kernel 1)
 };
 
@@ -59,11 +61,13 @@ struct DecodeParams {
 // unrolled and would otherwise carry one copy per call site.
 __device__ __noinline__ double pow_generic(double x, double y) { return pow(x, y); }
 
-__device__ __forceinline__ double entw(double x, const DecodeParams &dp) {
+__device__ __forceinline__ double pw_rt(double x, const DecodeParams &dp) {
   return dp.ibeta == 2 ? x * x : (dp.ibeta == 1 ? x : pow_generic(x, dp.beta));
 }
-__device__ __forceinline__ double entw_d(double x, const DecodeParams &dp) {  // d/dx of entw
-  return dp.ibeta == 2 ? 2.0 * x : (dp.ibeta == 1 ? 1.0 : dp.beta * pow_generic(x, dp.beta - 1.0));
+
+// c^-(alpha-1)
+__device__ __forceinline__ double pow_neg_a(double c, const DecodeParams &dp) {
+  return dp.ibeta == 2 ? 1.0 / sqrt(c) : (dp.ibeta == 1 ? 1.0 / c : pow_generic(c, -dp.a));
 }
 
 // The same powers with the exponent fixed at compile time (kB = 2: alpha = 1.5,
@@ -155,9 +159,12 @@ struct GlobSeg {
   const int *sbase;  // LDS, [nseg]     token offset where each segment starts
   int nseg, n;
   __device__ __forceinline__ int addr(int k) const {
-    int s = 0;
-    while (s + 1 < nseg && soff[s + 1] <= k) ++s;
-    return sbase[s] + (k - soff[s]);
+    int lo = 0, hi = nseg - 1;  // last segment starting at or before k
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (soff[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    return sbase[lo] + (k - soff[lo]);
   }
   template <typename Fn>
   __device__ __forceinline__ void each(Fn &&fn) const {
@@ -173,7 +180,7 @@ struct GlobSeg {
   }
 };
 
-// Candidates held in registers: thread t owns entries t, t + 256, ...
+// Candidates held in registers: thread t owns entries 32t .. 32t + 31.
 constexpr int kRegPer = 32;
 struct RegVals {
   const double (&v)[kRegPer];
@@ -182,28 +189,30 @@ struct RegVals {
   __device__ __forceinline__ void each(Fn &&fn) const {
 #pragma unroll
     for (int j = 0; j < kRegPer; ++j)
-      if ((int)threadIdx.x + j * kDThreads < n) fn(v[j]);
+      if ((int)threadIdx.x * kRegPer + j < n) fn(v[j]);
   }
 };
 struct WaveRed {
   __device__ __forceinline__ double operator()(double v, double *) const { return wave_sum(v); }
+  __device__ __forceinline__ void pair(double &a, double &b, double *) const { a = wave_sum(a); b = wave_sum(b); }
 };
 struct BlockRed {
   __device__ __forceinline__ double operator()(double v, double *s) const { return block_sum(v, s); }
+  __device__ __forceinline__ void pair(double &a, double &b, double *s) const { block_sum2(a, b, s); }
 };
 
-// Root of F(t) = sum [X - t]_+^beta = 1 by Newton from the left: lo = mx - 1
-// has F >= 1, hi = mx - n^-(alpha-1) has F <= 1 (n >= the number of scores
-// above hi).  For alpha <= 2 (beta >= 1) F is convex and decreasing, so every
+// Root of F(t) = sum [X - t]_+^beta = 1 by Newton from the left: lo0 has
+// F >= 1 (mx - 1 or a tighter certified bound), hi = mx - n^-(alpha-1) has
+// F <= 1 (n >= the number of scores above hi).  For alpha <= 2 (beta >= 1) F is convex and decreasing, so every
 // Newton iterate from the left stays left of the root: one pass per step.
 // Otherwise each Newton candidate is checked with a second pass; one that
 // leaves (lo, hi) becomes a bisection step, and after a step lands right of
 // the root the next step bisects.
 template <int kB, typename Src, typename Red>
-__device__ __forceinline__ double newton_tau(const Src &src, double n, double mx, const DecodeParams &dp,
-                                             double *dred) {
+__device__ __forceinline__ double newton_tau(const Src &src, double n, double mx, double lo0,
+                                             const DecodeParams &dp, double *dred) {
   const Red red;
-  double lo = mx - 1.0;
+  double lo = lo0;
   double hi = mx - pow(n, -dp.a);
   if (!(hi > lo)) return lo;
   if (kB != 0 || dp.beta >= 1.0) {
@@ -214,8 +223,7 @@ __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx
         const double y = x - lo;
         if (y > 0.0) { f += pw<kB>(y, dp); fp += pw_d<kB>(y, dp); }
       });
-      f = red(f, dred);
-      fp = red(fp, dred);
+      red.pair(f, fp, dred);
       if (!(f > 1.0) || !(fp > 0.0)) break;  // at the root (to rounding)
       const double cand = lo + (f - 1.0) / fp;
       if (!(cand > lo)) break;                 // no progress: converged
@@ -236,8 +244,7 @@ __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx
         const double y = x - lo;
         if (y > 0.0) { f += pw<kB>(y, dp); fp += pw_d<kB>(y, dp); }
       });
-      f = red(f, dred);
-      fp = red(fp, dred);
+      red.pair(f, fp, dred);
       cand = fp > 0.0 ? lo + (f - 1.0) / fp : 0.5 * (lo + hi);
       if (!(cand > lo) || !(cand < hi)) {
         if (!(cand > lo) && f >= 1.0) break;  // Newton makes no progress: converged
@@ -317,7 +324,7 @@ __device__ double sparsemax_tau_sort(const double *cx, int n, double *buf, doubl
 // sit in LDS (tier 0), in registers (tier 1, not for generic alpha) or in the
 // workspace (tier 2).
 template <int kB>
-__device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, double mx, int total, const double *cx,
+__device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, double mx, double lo0, int total, const double *cx,
                                           double *sortbuf, const double (&rx)[kRegPer], const GlobSeg<1> &gs,
                                           double *dred, int *s_kstar, double *s_tau, double &tau, double &z) {
   const int tid = threadIdx.x;
@@ -326,17 +333,17 @@ __device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, doub
     tau = sparsemax_tau_sort(cx, total, sortbuf, dred, s_kstar);
   } else if (tier == 0) {
     if (tid < kWave) {
-      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, dp, dred);
+      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, lo0, dp, dred);
       if (tid == 0) *s_tau = t;
     }
     __syncthreads();
     tau = *s_tau;
   } else if (kB != 0 && tier == 1) {
-    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, dp, dred);
+    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, lo0, dp, dred);
   } else if (kB != 0) {
-    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, dp, dred);
+    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred);
   } else {
-    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, dp, dred);
+    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, lo0, dp, dred);
   }
   double zz = 0.0;
   auto zsum = [&](double x) { const double y = x - tau; if (y > 0.0) zz += pw<kB>(y, dp); };
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kParts = kDThreads / P;  // threads per token
   constexpr int kPer = DIM / kParts;     // coordinates per thread
-  __shared__ double dred[kDThreads / kWave];
+  __shared__ double dred[2 * kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
   const int rows = D.B * D.Hq;
   int *prefix = reinterpret_cast<int *>(smem);
@@ -420,11 +427,13 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kTpe = DIM / 8;           // threads per support entry in the V gather
   constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
-  __shared__ double dred[kDThreads / kWave];
+  __shared__ double dred[2 * kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
   __shared__ int s_last, s_kstar;
   __shared__ double s_tau;
   __shared__ int soff[kSplitMax + 1], sbase[kSplitMax];
+  __shared__ double sL[kSplitMax];
+  __shared__ int s_cnt[kDThreads / kWave][kNThr];
   __shared__ uint32_t sup_v[kSupChunk];
   __shared__ int sup_i[kSupChunk];
   __shared__ float sup_w[kSupChunk];
@@ -434,6 +443,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   uint32_t *cv = reinterpret_cast<uint32_t *>(ci + kCand);    // [kCand] V row index
   double *sortbuf = reinterpret_cast<double *>(cv + kCand);   // [kCand] (sort form only)
   const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  EKV_MARK(1, 0);
   const int MP = D.max_pages;
   const size_t wrow = (size_t)MP * P;
   const int g = (r % D.Hq) / D.G;
@@ -476,82 +486,169 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     }
     return;
   }
-  const double thr = mx - 1.0;  // tau >= thr
+  const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
 
-  // 2. this chunk's candidates X > thr, compacted in index order to the
-  //    chunk's start in the workspace (and into LDS when this block is alone)
+  EKV_MARK(1, 1);
+  // 2. this chunk's candidates.  Pass 1 counts the chunk's scores above
+  //    mx - 2^-i (i < 8); C tokens above mx - d give F(mx - d - C^-(alpha-1))
+  //    >= C * (C^-(alpha-1))^(1/(alpha-1)) = 1, so each count certifies a
+  //    lower bound on tau, valid for the whole row.  A lone block also keeps
+  //    its candidates X > mx - 1 in LDS.  Each thread takes 8 consecutive
+  //    tokens of one page (P is a multiple of 8), so one block scan per 2048
+  //    tokens keeps the index order.
   const int tlo = (int)((long long)c * cnt / nsplit) * P, thi = (int)((long long)(c + 1) * cnt / nsplit) * P;
   const bool alone = nsplit == 1;
-  int ncand = 0;
+  double th[kNThr];
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) th[i] = mx - ldexp(1.0, -i);
+  int cnt8[kNThr];
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) cnt8[i] = 0;
+  int nlds = 0;
 #pragma unroll 1
   for (int base = tlo; base < thi; base += 8 * kDThreads) {
+    const int t0 = base + 8 * tid;
+    const bool valid = t0 < thi;  // all 8 tokens or none (thi - t0 is a multiple of 8)
+    const int tc = min(t0, thi - 8);
+    const double2 *src = reinterpret_cast<const double2 *>(xrow + tc);
     double v[8];
-    uint32_t ph[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) { const double2 d2 = src[h]; v[2 * h] = d2.x; v[2 * h + 1] = d2.y; }
+    const uint32_t ph = ipr[tc / P];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int t = min(base + u * kDThreads + tid, thi - 1);
-      v[u] = xrow[t];
-      ph[u] = ipr[t / P];
+#pragma unroll
+      for (int i = 0; i < kNThr; ++i) cnt8[i] += (valid && v[u] > th[i]) ? 1 : 0;
     }
+    if (alone) {
+      int take = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (base + u * kDThreads >= thi) break;
-      const int t = base + u * kDThreads + tid;
-      const int take = (t < thi && v[u] > thr) ? 1 : 0;
+      for (int u = 0; u < 8; ++u) take += (valid && v[u] > thr) ? 1 : 0;
       int tot;
-      const int at = ncand + block_excl_scan(take, scan_scratch, &tot);
-      if (take) {
-        st_agent(&xrow[tlo + at], v[u]);
-        st_agent(&xir[tlo + at], (uint32_t)t);
-        if (alone && at < kCand) {
-          cx[at] = v[u];
-          ci[at] = t;
-          cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+      int at = nlds + block_excl_scan(take, scan_scratch, &tot);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (valid && v[u] > thr) {
+          if (at < kCand) {
+            const int t = t0 + u;
+            cx[at] = v[u];
+            ci[at] = t;
+            cv[at] = (ph * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+          }
+          ++at;
+        }
+      }
+      nlds += tot;
+    }
+  }
+  // block totals of the counts, then the tightest certified bound
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) cnt8[i] = wave_sum(cnt8[i]);
+  __syncthreads();
+  if ((tid & (kWave - 1)) == 0)
+    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = cnt8[i];
+  __syncthreads();
+  double Lc = thr;
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) {
+    int ci_ = 0;
+    for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
+    if (ci_ > 0) Lc = fmax(Lc, th[i] - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)));
+  }
+  const bool lds_all = alone && nlds <= kCand;  // every candidate X > mx - 1 is in LDS
+  int total = nlds;                              // entries in the workspace segments (tiers 1, 2)
+  double L = Lc;
+  if (!lds_all) {
+    // pass 2: compact X > Lc in place to the chunk's start (and into LDS when
+    // alone); writes trail the reads, so no unread score is overwritten
+    nlds = 0;
+    int ncand = 0;
+#pragma unroll 1
+    for (int base = tlo; base < thi; base += 8 * kDThreads) {
+      const int t0 = base + 8 * tid;
+      const bool valid = t0 < thi;
+      const int tc = min(t0, thi - 8);
+      const double2 *src = reinterpret_cast<const double2 *>(xrow + tc);
+      double v[8];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) { const double2 d2 = src[h]; v[2 * h] = d2.x; v[2 * h + 1] = d2.y; }
+      const uint32_t ph = ipr[tc / P];
+      int take = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) take += (valid && v[u] > Lc) ? 1 : 0;
+      int tot;
+      int at = ncand + block_excl_scan(take, scan_scratch, &tot);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (valid && v[u] > Lc) {
+          const int t = t0 + u;
+          st_agent(&xrow[tlo + at], v[u]);
+          st_agent(&xir[tlo + at], (uint32_t)t);
+          if (alone && at < kCand) {
+            cx[at] = v[u];
+            ci[at] = t;
+            cv[at] = (ph * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
+          }
+          ++at;
         }
       }
       ncand += tot;
     }
+    total = ncand;
+    nlds = alone ? ncand : 0;
   }
-  int total = ncand;
+  EKV_MARK(1, 2);
   if (!alone) {
-    if (tid == 0) st_agent(&ws.segcnt[(size_t)r * kSplitMax + c], ncand);
-    if (!arrive_last(&ws.ctr[r], (unsigned)nsplit, &s_last)) return;
-    // the row's last block: segment offsets, then the candidates into LDS
     if (tid == 0) {
-      int run = 0;
-      for (int s2 = 0; s2 < nsplit; ++s2) {
-        soff[s2] = run;
-        sbase[s2] = (int)((long long)s2 * cnt / nsplit) * P;
-        run += ld_agent(&ws.segcnt[(size_t)r * kSplitMax + s2]);
-      }
-      soff[nsplit] = run;
+      st_agent(&ws.segcnt[(size_t)r * kSplitMax + c], total);
+      st_agent(&ws.segL[(size_t)r * kSplitMax + c], Lc);
+    }
+    if (!arrive_last(&ws.ctr[r], (unsigned)nsplit, &s_last)) return;
+    EKV_MARK(1, 3);
+    // the row's last block: segment offsets, the row's bound, then the
+    // candidates above it into LDS
+    if (tid < nsplit) {
+      soff[tid + 1] = ld_agent(&ws.segcnt[(size_t)r * kSplitMax + tid]);
+      sL[tid] = ld_agent(&ws.segL[(size_t)r * kSplitMax + tid]);
+      sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      soff[0] = 0;
+      double lm = thr;
+      for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
+      s_tau = lm;
     }
     __syncthreads();
     total = soff[nsplit];
-    if (total <= kCand) {
-      const GlobSeg<1> gs{xrow, soff, sbase, nsplit, total};
+    L = s_tau;
+    const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
+    nlds = 0;
 #pragma unroll 1
-      for (int base = 0; base < total; base += 4 * kDThreads) {
-        double v[4];
-        uint32_t t[4];
+    for (int base = 0; base < total; base += 4 * kDThreads) {
+      double v[4];
+      uint32_t t[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int a = gs.addr(min(base + u * kDThreads + tid, total - 1));
-          v[u] = ld_agent(&xrow[a]);
-          t[u] = ld_agent(&xir[a]);
+      for (int u = 0; u < 4; ++u) {
+        const int a = gs0.addr(min(base + u * kDThreads + tid, total - 1));
+        v[u] = ld_agent(&xrow[a]);
+        t[u] = ld_agent(&xir[a]);
+      }
+      uint32_t ph[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ph[u] = ipr[t[u] / P];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = base + u * kDThreads + tid;
+        const int take = (k < total && v[u] > L) ? 1 : 0;
+        int tot;
+        const int at = nlds + block_excl_scan(take, scan_scratch, &tot);
+        if (take && at < kCand) {
+          cx[at] = v[u];
+          ci[at] = (int)t[u];
+          cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
         }
-        uint32_t ph[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ph[u] = ipr[t[u] / P];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int k = base + u * kDThreads + tid;
-          if (k < total) {
-            cx[k] = v[u];
-            ci[k] = (int)t[u];
-            cv[k] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
-          }
-        }
+        nlds += tot;
       }
     }
   } else if (tid == 0) {
@@ -560,8 +657,10 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     sbase[0] = 0;
   }
   __syncthreads();
+  EKV_MARK(1, 4);
   // candidate tiers: LDS (one wave solves), registers (block), workspace passes
-  const int tier = total <= kCand ? 0 : ((total <= kRegPer * kDThreads && dp.ibeta != 0) ? 1 : 2);
+  const int tier = nlds <= kCand ? 0 : ((total <= kRegPer * kDThreads && dp.ibeta != 0) ? 1 : 2);
+  const int nsol = tier == 0 ? nlds : total;  // values the solver sees
   const int nseg = alone ? 1 : nsplit;
   const GlobSeg<1> gs{xrow, soff, sbase, nseg, total};
   double rx[kRegPer];
@@ -569,17 +668,19 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   if (tier == 1) {
 #pragma unroll
     for (int j = 0; j < kRegPer; ++j) {
-      const int a = gs.addr(min(tid + j * kDThreads, total - 1));
+      const int a = gs.addr(min(tid * kRegPer + j, total - 1));
       rx[j] = ld_agent(&xrow[a]);
       ri[j] = ld_agent(&xir[a]);
     }
   }
 
+  EKV_MARK(1, 5);
   // 3. threshold and normalizer
   double tau, z;
-  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
-  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
-  else solve_row<0>(tier, dp, mx, total, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  else solve_row<0>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  EKV_MARK(1, 6);
   if (tid == 0 && tau_out) tau_out[r] = tau / dp.a;
 
   // 4. support gather, chunk by chunk in index order: compact (token, weight;
@@ -639,23 +740,43 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     if (take) {
       sup_v[nsup + pos] = vk;
       sup_i[nsup + pos] = ik;
-      sup_w[nsup + pos] = (float)(entw(y, dp) / z);
+      sup_w[nsup + pos] = (float)(pw_rt(y, dp) / z);
     }
     nsup += tot;
   };
   if (tier == 0) {
 #pragma unroll 1
-    for (int k0 = 0; k0 < total; k0 += kDThreads) {
+    for (int k0 = 0; k0 < nsol; k0 += kDThreads) {
       const int k = k0 + tid;
-      step(k < total ? cx[k] : -INFINITY, k < total ? ci[k] : 0, k < total ? cv[k] : 0u);
+      step(k < nsol ? cx[k] : -INFINITY, k < nsol ? ci[k] : 0, k < nsol ? cv[k] : 0u);
     }
   } else if (tier == 1) {
-    // registers rotate down one slot per step, so every access has a fixed index
-#pragma unroll 1
-    for (int k0 = 0; k0 < total; k0 += kDThreads) {
-      step(k0 + tid < total ? rx[0] : -INFINITY, (int)ri[0], 0u);
+    // each thread's support entries are consecutive in index order: one scan
+    // places them all when they fit one gather pass
+    int mine = 0;
 #pragma unroll
-      for (int j = 0; j + 1 < kRegPer; ++j) { rx[j] = rx[j + 1]; ri[j] = ri[j + 1]; }
+    for (int j = 0; j < kRegPer; ++j) mine += (tid * kRegPer + j < total && rx[j] - tau > 0.0) ? 1 : 0;
+    int stot;
+    int at = block_excl_scan(mine, scan_scratch, &stot);
+    if (stot <= kSupChunk) {
+#pragma unroll
+      for (int j = 0; j < kRegPer; ++j) {
+        const double y = rx[j] - tau;
+        if (tid * kRegPer + j < total && y > 0.0) {
+          sup_i[at] = (int)ri[j];
+          sup_w[at] = (float)(pw_rt(y, dp) / z);
+          ++at;
+        }
+      }
+      nsup = stot;
+    } else {
+      // registers rotate down one slot per step, so every access has a fixed index
+#pragma unroll 1
+      for (int j = 0; j < kRegPer; ++j) {
+        step(tid * kRegPer + j < total ? rx[0] : -INFINITY, (int)ri[0], 0u);
+#pragma unroll
+        for (int u = 0; u + 1 < kRegPer; ++u) { rx[u] = rx[u + 1]; ri[u] = ri[u + 1]; }
+      }
     }
   } else {
 #pragma unroll 1
@@ -668,6 +789,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     }
   }
   flush();
+  EKV_MARK(1, 7);
 #pragma unroll
   for (int u = 0; u < 8; ++u) accs[ge][gc * 8 + u] = acc8[u];
   __syncthreads();
@@ -687,6 +809,7 @@ static DecodeWs carve_decode(const Dims &D, void *base, size_t *bytes) {
   w.pmax = cv.take<double>(rows * D.max_pages);
   w.iphys = cv.take<uint32_t>(rows * D.max_pages);
   w.segcnt = cv.take<int>(rows * kSplitMax);
+  w.segL = cv.take<double>(rows * kSplitMax);
   w.ctr = cv.take<unsigned int>(rows);
   if (bytes) *bytes = cv.bytes();
   return w;
@@ -753,4 +876,5 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
   return launch_decode_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
 }
 
+EKV_TRACE_DUMP(ekv_trace_dump_decode)
 }  // namespace ekv

@@ -16,10 +16,12 @@
 //
 // Root finding for beta in {1, 2} (alpha = 2, 1.5) without a sequential bisection
 // over every point (16 per page):
-//   K1  per (row, chunk): lower bracket  lo = max_p [a mu_p - (2.5/n_p)^a]
-//       (the page alone already gives F >= 1 there, since half of the rule's
-//       weight sits on nodes x_j >= 0) and upper bracket hi = max_p of the top
-//       node (F = 0 there).
+//   K1  per (row, chunk): lower bracket lo with F(lo) >= 1, the larger of
+//       max_p [a mu_p - (2.5/n_p)^a] (the page alone already gives F >= 1
+//       there, since half of the rule's weight sits on nodes x_j >= 0) and
+//       theta - W^-a for rule weight W of the chunk's points above theta
+//       (eight thresholds theta below the top node); upper bracket hi =
+//       max_p of the top node (F = 0 there).
 //   K2  per (row, chunk): histogram of the points v > lo over NB equal bins of
 //       [lo, hi] holding the moments M_r = sum c (v - e_b)^r, r <= beta, taken
 //       about each bin's lower edge e_b.  The last block of a row merges the
@@ -42,6 +44,7 @@ namespace ekv {
 
 constexpr int kGThreads = 256;
 constexpr int kNB = 256;  // histogram bins
+constexpr int kNThr = 8;  // thresholds of the certified lower bracket
 
 struct GaussParams {
   double a, beta, delta, nsig;
@@ -76,10 +79,41 @@ __device__ __forceinline__ bool keep_at(double thr, double bx, double m, double 
   return g_ok && bx >= thr;
 }
 __device__ __forceinline__ double bin_edge(double lo, double w, int b) { return lo + (double)b * w; }
-__device__ __forceinline__ int bin_of(double v, double lo, double w) {
-  int b = (int)((v - lo) / w);
+// LDS slot of histogram bin b: neighbouring Gauss-Hermite nodes of one page
+// land ~16-40 bins apart, so a plain layout sends the lanes of one atomic to
+// the same LDS banks; XOR-ing the low bits with the high ones spreads them
+// (a permutation of 0 .. kNB-1).
+__device__ __forceinline__ int hslot(int b) { return b ^ ((b >> 4) & 15); }
+// Bin of a point from the reciprocal width (the histogram and the in-bin
+// collection compute iw = 1/w from the same w, so they agree on every point;
+// a point may sit a rounding error below its bin's edge, which the moment
+// algebra about the edge absorbs).
+__device__ __forceinline__ int bin_of(double v, double lo, double iw) {
+  int b = (int)((v - lo) * iw);
   return b < 0 ? 0 : (b >= kNB ? kNB - 1 : b);
 }
+
+// Quadrature point j of a page in (alpha-1)-scaled score units; every kernel
+// evaluates it with this one expression, so they agree on each point's bits.
+__device__ __forceinline__ double gh_point(double a, double m, double sig, double x) {
+  return a * (m + 1.4142135623730951 * sig * x);
+}
+
+// The page statistics of pages pb .. pb+3 (clamped to p_end - 1; the caller
+// masks pages past the end).
+struct Pages4 {
+  float bx[4], m[4], v2[4];
+  __device__ __forceinline__ void load(const float *box, const float *mu, const float *var, size_t base, int pb,
+                                       int p_end) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(pb + u, p_end - 1);
+      bx[u] = box[base + p];
+      m[u] = mu[base + p];
+      v2[u] = var[base + p];
+    }
+  }
+};
 
 struct RowCtx {
   int row, b, L, np, nch;
@@ -107,6 +141,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussP
                                                                   GaussWs ws) {
   __shared__ double red[kGThreads / kWave];
   const int chunk = blockIdx.x;
+  EKV_MARK(0, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
   if (!rc.active) return;
   if (chunk == 0 && threadIdx.x == 0) {
@@ -117,20 +152,78 @@ __global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussP
   if (chunk >= rc.nch && chunk > 0) return;
   const size_t base = (size_t)rc.row * D.max_pages;
   const double sqrt2 = 1.4142135623730951;
+  const double pw_full = pow(2.5 / (double)D.P, gp.a);  // the lone-page bracket term of a full page
   double lo_c = -INFINITY, top = -INFINITY;
   const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
-  for (int p = chunk * gp.chunk + threadIdx.x; p < p_end; p += kGThreads) {
-    const float bx = box[base + p], m = mu[base + p], v = var[base + p];
-    if (!page_valid(bx, m, v)) continue;
-    const int n = min(D.P, rc.L - p * D.P);
-    const double sig = sqrt(v > 0.0f ? (double)v : 0.0);
-    lo_c = fmax(lo_c, gp.a * (double)m - pow(2.5 / (double)n, gp.a));
-    top = fmax(top, gp.a * ((double)m + sqrt2 * sig * gc.x[15]));
+#pragma unroll 1
+  for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
+    float bx[4], m[4], v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = min(p0 + u * kGThreads + (int)threadIdx.x, p_end - 1);
+      bx[u] = box[base + p];
+      m[u] = mu[base + p];
+      v[u] = var[base + p];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * kGThreads + threadIdx.x;
+      if (p >= p_end || !page_valid(bx[u], m[u], v[u])) continue;
+      const int n = min(D.P, rc.L - p * D.P);
+      const double sig = sqrt(v[u] > 0.0f ? (double)v[u] : 0.0);
+      lo_c = fmax(lo_c, gp.a * (double)m[u] - (n == D.P ? pw_full : pow(2.5 / (double)n, gp.a)));
+      top = fmax(top, gh_point(gp.a, (double)m[u], sig, gc.x[15]));
+    }
   }
+  EKV_MARK(0, 1);
   lo_c = block_max(lo_c, red);
   top = block_max(top, red);
+  // Tighter certified bound: with W_i the rule weight (n_p w_j) of the
+  // chunk's points above theta_i = top - (top - lo_c) 2^-i,
+  // F(theta_i - W_i^-(alpha-1)) >= W_i (W_i^-(alpha-1))^(1/(alpha-1)) = 1, and
+  // F of the row is at least F of the chunk.
+  double lo_b = lo_c;
+  if (top > lo_c) {
+    const double span = top - lo_c;
+    double th[kNThr], W[kNThr];
+#pragma unroll
+    for (int i = 0; i < kNThr; ++i) { th[i] = top - span * ldexp(1.0, -i); W[i] = 0.0; }
+#pragma unroll 1
+    for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
+      float bx[4], m[4], v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int p = min(p0 + u * kGThreads + (int)threadIdx.x, p_end - 1);
+        bx[u] = box[base + p];
+        m[u] = mu[base + p];
+        v[u] = var[base + p];
+      }
+#pragma unroll 1
+      for (int u = 0; u < 4; ++u) {
+        const int p = p0 + u * kGThreads + threadIdx.x;
+        if (p >= p_end || !page_valid(bx[u], m[u], v[u])) continue;
+        const double n = (double)min(D.P, rc.L - p * D.P);
+        const double sig = sqrt(v[u] > 0.0f ? (double)v[u] : 0.0);
+        for (int j = 15; j >= 0; --j) {
+          const double vj = gh_point(gp.a, (double)m[u], sig, gc.x[j]);
+          if (!(vj > th[0])) break;  // nodes ascend in j
+          const double c = n * gc.w[j];
+#pragma unroll
+          for (int i = 0; i < kNThr; ++i) W[i] += vj > th[i] ? c : 0.0;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kNThr; ++i) {
+      const double wi = block_sum(W[i], red);
+      if (wi > 0.0) {
+        const double d = gp.ibeta == 2 ? 1.0 / sqrt(wi) : 1.0 / wi;  // wi^-(alpha-1), alpha in {1.5, 2}
+        lo_b = fmax(lo_b, th[i] - d - 1e-12 * fmax(1.0, fabs(top)));
+      }
+    }
+  }
   if (threadIdx.x == 0) {
-    ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = lo_c;
+    ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = lo_b;
     ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1] = top;
   }
 }
@@ -159,41 +252,68 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   __shared__ double s0[kNB], s1[kNB], s2[kNB];
   __shared__ int s_last, s_best;
   const int chunk = blockIdx.x;
+  EKV_MARK(1, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
   if (!rc.active || chunk >= rc.nch) return;
   double lo, hi;
   row_bracket(gp, ws, rc, lo, hi);
   if (!(hi > -INFINITY)) return;  // no valid page in the row
-  const double w = (hi - lo) / kNB;
+  EKV_MARK(1, 1);
+  const double w = (hi - lo) / kNB, iw = 1.0 / w;
   const double sqrt2 = 1.4142135623730951;
   for (int i = threadIdx.x; i < kNB; i += kGThreads) h0[i] = h1[i] = h2[i] = 0.0;
   __syncthreads();
   const size_t base = (size_t)rc.row * D.max_pages;
   const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
-  for (int p = chunk * gp.chunk + threadIdx.x; p < p_end; p += kGThreads) {
-    const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
-    if (!page_valid(bx, m, v2)) continue;
-    const double n = (double)min(D.P, rc.L - p * D.P);
-    const double sig = sqrt(v2 > 0.0f ? (double)v2 : 0.0);
+  // Each thread takes 4 consecutive pages and walks the nodes from the top
+  // (a wave-uniform index, so the node constants sit in scalar registers);
+  // the 4 pages advance together for instruction-level parallelism, and a
+  // page drops out at its first node below lo (the nodes ascend in j).
+#pragma unroll 1
+  for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
+    const int pb = p0 + 4 * threadIdx.x;
+    Pages4 pg;
+    pg.load(box, mu, var, base, pb, p_end);
+    double mm[4], sg[4], nn[4];
+    bool act[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      act[u] = pb + u < p_end && page_valid(pg.bx[u], pg.m[u], pg.v2[u]);
+      mm[u] = (double)pg.m[u];
+      sg[u] = sqrt(pg.v2[u] > 0.0f ? (double)pg.v2[u] : 0.0);
+      nn[u] = (double)min(D.P, rc.L - (pb + u) * D.P);
+    }
+#pragma unroll 1
     for (int j = 15; j >= 0; --j) {
-      const double v = gp.a * ((double)m + sqrt2 * sig * gc.x[j]);
-      if (!(v > lo)) break;  // nodes ascend in j
-      const int bn = bin_of(v, lo, w);
-      const double e = v - bin_edge(lo, w, bn);
-      const double c = n * gc.w[j];
-      atomicAdd(&h0[bn], c);
-      atomicAdd(&h1[bn], c * e);
-      if (gp.ibeta == 2) atomicAdd(&h2[bn], c * e * e);
+      const double xj = gc.x[j], wj = gc.w[j];
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!act[u]) continue;
+        const double v = gh_point(gp.a, mm[u], sg[u], xj);
+        if (!(v > lo)) { act[u] = false; continue; }
+        any = true;
+        const int bn = bin_of(v, lo, iw);
+        const double e = v - bin_edge(lo, w, bn);
+        const double c = nn[u] * wj;
+        const int hs = hslot(bn);
+        atomicAdd(&h0[hs], c);
+        atomicAdd(&h1[hs], c * e);
+        if (gp.ibeta == 2) atomicAdd(&h2[hs], c * e * e);
+      }
+      if (!__any(any)) break;
     }
   }
   __syncthreads();
+  EKV_MARK(1, 2);
   double *hc = ws.hist + ((size_t)rc.row * gp.nchunk + chunk) * kNB * 3;
   for (int i = threadIdx.x; i < kNB; i += kGThreads) {
-    st_agent(&hc[i * 3 + 0], h0[i]);
-    st_agent(&hc[i * 3 + 1], h1[i]);
-    st_agent(&hc[i * 3 + 2], h2[i]);
+    st_agent(&hc[i * 3 + 0], h0[hslot(i)]);
+    st_agent(&hc[i * 3 + 1], h1[hslot(i)]);
+    st_agent(&hc[i * 3 + 2], h2[hslot(i)]);
   }
   if (!arrive_last(&ws.ctr[rc.row * 2 + 0], (unsigned)rc.nch, &s_last)) return;
+  EKV_MARK(1, 3);
 
   // ---- last block of the row: merge chunks in order, suffix-scan the moments
   for (int i = threadIdx.x; i < kNB; i += kGThreads) {
@@ -218,6 +338,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
     s2[i] = a2;
   }
   __syncthreads();
+  EKV_MARK(1, 4);
   // inclusive suffix scan: S_b = m_b (+) shift(S_{b+d}, e_{b+d} -> e_b)
   for (int dist = 1; dist < kNB; dist <<= 1) {
     double n0 = 0, n1 = 0, n2 = 0;
@@ -256,6 +377,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
     ri[4] = k + 1 < kNB ? s1[k + 1] : 0.0;
     ri[5] = k + 1 < kNB ? s2[k + 1] : 0.0;
   }
+  EKV_MARK(1, 5);
 }
 
 // --------------------------------------- K3: collect, classify, solve, compact
@@ -265,10 +387,11 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     const uint8_t *__restrict__ seq_mask, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_cnt,
     double *__restrict__ tau_hat, GaussWs ws) {
   __shared__ int scan_scratch[kGThreads / kWave];
-  __shared__ double dred[kGThreads / kWave];
+  __shared__ double dred[2 * kGThreads / kWave];
   __shared__ double s_best_est;
   __shared__ int s_best_p, s_last;
   const int chunk = blockIdx.x;
+  EKV_MARK(2, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
   if (!rc.active) return;
   double lo, hi;
@@ -282,9 +405,10 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     return;
   }
   if (chunk >= rc.nch) return;
+  EKV_MARK(2, 1);
   const double *ri = ws.rowinfo + (size_t)rc.row * 8;
   const int k = (int)ri[0];
-  const double w = ri[2];
+  const double w = ri[2], iw = 1.0 / w;
   const double ek = bin_edge(lo, w, k), ek1 = bin_edge(lo, w, k + 1);
   const double thr_lo = ek / gp.a - gp.delta, thr_hi = ek1 / gp.a - gp.delta;
   const double sqrt2 = 1.4142135623730951;
@@ -294,38 +418,67 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   int listed = 0;
   double best = -INFINITY;
   int bestp = 0x7FFFFFFF;
-  for (int pb = p_begin; pb < p_end; pb += kGThreads) {
-    const int p = pb + threadIdx.x;
-    int code = -1;
-    if (p < p_end) {
-      const float bx = box[base + p], m = mu[base + p], v2 = var[base + p];
-      if (page_valid(bx, m, v2)) {
-        const double n = (double)min(D.P, rc.L - p * D.P);
-        const double s2d = v2 > 0.0f ? (double)v2 : 0.0;
-        const double sig = sqrt(s2d);
-        for (int j = 15; j >= 0; --j) {
-          const double v = gp.a * ((double)m + sqrt2 * sig * gc.x[j]);
-          if (!(v > lo)) break;
-          if (bin_of(v, lo, w) == k) {
-            const int slot = atomicAdd(&ws.inbin_cnt[rc.row], 1);
-            if (slot < gp.cap) {
-              st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0], v);
-              st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1], n * gc.w[j]);
-            }
-          }
-        }
-        if (keep_at(thr_hi, bx, m, s2d, gp.nsig)) code = p;
-        else if (keep_at(thr_lo, bx, m, s2d, gp.nsig)) code = p | (int)0x80000000;
-        const double e1 = (double)m + gp.nsig * sig;
-        const double est = e1 < (double)bx ? e1 : (double)bx;
+  // Each thread takes 4 consecutive pages (one block scan per 1024 pages
+  // keeps the list ascending); the nodes are walked from the top with a
+  // wave-uniform index and a page drops out below bin k.
+#pragma unroll 1
+  for (int p0 = p_begin; p0 < p_end; p0 += 4 * kGThreads) {
+    const int pb = p0 + 4 * threadIdx.x;
+    Pages4 pg;
+    pg.load(box, mu, var, base, pb, p_end);
+    double mm[4], sg[4], s2d[4], nn[4];
+    bool valid[4], act[4];
+    int code[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = pb + u;
+      valid[u] = p < p_end && page_valid(pg.bx[u], pg.m[u], pg.v2[u]);
+      act[u] = valid[u];
+      mm[u] = (double)pg.m[u];
+      s2d[u] = pg.v2[u] > 0.0f ? (double)pg.v2[u] : 0.0;
+      sg[u] = sqrt(s2d[u]);
+      nn[u] = (double)min(D.P, rc.L - p * D.P);
+      code[u] = -1;
+      if (valid[u]) {
+        if (keep_at(thr_hi, pg.bx[u], pg.m[u], s2d[u], gp.nsig)) code[u] = p;
+        else if (keep_at(thr_lo, pg.bx[u], pg.m[u], s2d[u], gp.nsig)) code[u] = p | (int)0x80000000;
+        const double e1 = mm[u] + gp.nsig * sg[u];
+        const double est = e1 < (double)pg.bx[u] ? e1 : (double)pg.bx[u];
         if (est > best || (est == best && p < bestp)) { best = est; bestp = p; }
       }
     }
+#pragma unroll 1
+    for (int j = 15; j >= 0; --j) {
+      const double xj = gc.x[j], wj = gc.w[j];
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!act[u]) continue;
+        const double v = gh_point(gp.a, mm[u], sg[u], xj);
+        const int bn = v > lo ? bin_of(v, lo, iw) : -1;
+        if (bn < k) { act[u] = false; continue; }
+        any = true;
+        if (bn == k) {
+          const int slot = atomicAdd(&ws.inbin_cnt[rc.row], 1);
+          if (slot < gp.cap) {
+            st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0], v);
+            st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1], nn[u] * wj);
+          }
+        }
+      }
+      if (!__any(any)) break;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mine += code[u] != -1 ? 1 : 0;
     int tot;
-    const int pos = block_excl_scan(code != -1 ? 1 : 0, scan_scratch, &tot);
-    if (code != -1) st_agent(&ws.list[base + p_begin + listed + pos], code);
+    int at = listed + block_excl_scan(mine, scan_scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (code[u] != -1) st_agent(&ws.list[base + p_begin + at++], code[u]);
     listed += tot;
   }
+  EKV_MARK(2, 2);
   // chunk argmax of the estimate (lowest page on ties)
   {
     double bm = block_max(best, dred);
@@ -342,6 +495,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     }
   }
   if (!arrive_last(&ws.ctr[rc.row * 2 + 1], (unsigned)rc.nch, &s_last)) return;
+  EKV_MARK(2, 3);
 
   // ---- last block of the row: solve F(t) = 1 inside [ek, ek1].  The in-bin
   // points are staged in registers once (kInReg per thread), any excess is
@@ -359,6 +513,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     rv[u] = i < nin ? v : -INFINITY;
     rcw[u] = i < nin ? c : 0.0;
   }
+  EKV_MARK(2, 4);
   double t = ek;
   for (int it = 0; it < 200; ++it) {
     double f = 0.0, fp = 0.0;
@@ -373,8 +528,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     for (int u = 0; u < kInReg; ++u) acc_pt(rv[u], rcw[u]);
     for (int i = kInReg * kGThreads + threadIdx.x; i < nin; i += kGThreads)
       acc_pt(ld_agent(&inb[i * 2 + 0]), ld_agent(&inb[i * 2 + 1]));
-    f = block_sum(f, dred);
-    fp = block_sum(fp, dred);
+    block_sum2(f, fp, dred);
     const double Dd = ek1 - t;  // >= 0
     if (gp.ibeta == 2) { f += T2 + 2.0 * Dd * T1 + Dd * Dd * T0; fp += 2.0 * T1 + 2.0 * Dd * T0; }
     else { f += T1 + Dd * T0; fp += T0; }
@@ -391,7 +545,8 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   }
   const double thr = tau / gp.a - gp.delta;
 
-  // ---- settle undecided pages and write the ascending list.  Chunk counts
+
+  EKV_MARK(2, 5);  // ---- settle undecided pages and write the ascending list.  Chunk counts
   // and argmax partials are fetched in one batch; list entries are then read
   // in parallel across chunks (prefix offsets in LDS).
   __shared__ int s_off[1024 + 1];
@@ -409,6 +564,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   }
   __syncthreads();
   const int n_listed = s_off[rc.nch];
+  EKV_MARK(2, 6);
   int total = 0;
   for (int e0 = 0; e0 < n_listed; e0 += kGThreads) {
     const int e = e0 + threadIdx.x;
@@ -609,4 +765,5 @@ hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const 
   return hipGetLastError();
 }
 
+EKV_TRACE_DUMP(ekv_trace_dump_gauss)
 }  // namespace ekv

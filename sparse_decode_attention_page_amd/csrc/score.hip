@@ -60,11 +60,15 @@ struct ScoreCfg {
   static constexpr int kTileBytes = kTilePages * kRecBytes;
   static constexpr int kRedBytes = 4 * 3 * G * kWave * 8;
   static constexpr bool kRedInTile = kRedBytes <= kTileBytes;
-  static constexpr int kNBuf0 = (int)((kScoreLds - (kRedInTile ? 0 : kRedBytes)) / kTileBytes);
-  static constexpr int kNBuf = kNBuf0 > 4 ? 4 : kNBuf0;
+  // One tile buffer per block: LDS-DMA throughput grows with the number of
+  // waves issuing it, so LDS goes to more resident blocks per CU rather than
+  // to deeper per-block prefetch; the blocks of a CU overlap each other's
+  // loads and compute.
+  static constexpr int kNBuf = 1;
   static constexpr size_t kLds = (size_t)kNBuf * kTileBytes + (kRedInTile ? 0 : kRedBytes);
+  static constexpr int kBlocksPerCu = (int)(kScoreLds / (kLds + 8 * 1024)) < 1 ? 1 : (int)(kScoreLds / (kLds + 8 * 1024));
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 1 KB per wave instruction
-  static_assert(kNBuf >= 1, "tile does not fit in LDS");
+  static_assert(kLds <= kScoreLds, "tile does not fit in LDS");
   static_assert(kTileBytes % 4096 == 0, "tile split across 4 waves");
 };
 
@@ -95,7 +99,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   constexpr int kE = Chunk<T>::kElems;  // elements per 16-byte chunk
   constexpr int kRowChunks = DIM / kE;   // chunks per metadata row
   constexpr int kQChunks = DIM / 4 / kE; // chunks per coordinate quarter
-  constexpr int kQPer = (DIM * G + kScoreThreads - 1) / kScoreThreads;
 
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_phys[kMaxTilesPerBlock][kTilePages];
@@ -109,24 +112,69 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
   if (t_begin >= t_end) return;
   const int nt = t_end - t_begin;
   const char *mbase = reinterpret_cast<const char *>(meta);
+  EKV_MARK(0, 0);
 
-  // ---- page ids of every tile of this block (missing pages / bad ids -> -1)
-  for (int k = tid; k < nt * kTilePages; k += kScoreThreads) {
-    const int lt = k / kTilePages, r = k % kTilePages;
-    const int t = t_begin + lt;
-    const int row = t / tiles_per_row, pt = t % tiles_per_row;
-    const int b = row / D.Hkv;
-    const int np = n_pages_of(seq_len_clamped(seq_lens, b, D), D.P);
-    const int p = pt * kTilePages + r;
-    int ph = -1;
-    if (p < np) {
-      ph = page_table[(size_t)b * D.max_pages + p];
-      if (ph < 0 || ph >= D.num_phys) ph = -1;
-    }
-    s_phys[lt][r] = ph;
-    if (r == 0) s_np[lt] = np;
+  // ---- prologue, one round trip: the page ids of every tile of the block
+  // (missing pages / bad ids -> -1) and the coefficient table (q+, q-, q, q^2
+  // in fp64) of every (b, g) row the block touches.  Every block that scores
+  // (b, g) stores the same bytes into the same slot; the tile loop reads the
+  // table back through scalar loads once the stores have completed.
+  constexpr int kPtPer = kMaxTilesPerBlock * kTilePages / kScoreThreads;
+  int pt_ph[kPtPer], pt_len[kPtPer];
+#pragma unroll
+  for (int u = 0; u < kPtPer; ++u) {
+    const int k = min(u * kScoreThreads + tid, nt * kTilePages - 1);
+    const int t = t_begin + k / kTilePages;
+    const int b = t / tiles_per_row / D.Hkv;
+    const int p = min((t % tiles_per_row) * kTilePages + k % kTilePages, D.max_pages - 1);
+    pt_len[u] = seq_lens[b];
+    pt_ph[u] = page_table[(size_t)b * D.max_pages + p];
   }
-  __syncthreads();
+  {
+    const int row0 = t_begin / tiles_per_row, nrows = (t_end - 1) / tiles_per_row - row0 + 1;
+    const int n_coef = nrows * DIM * G;
+#pragma unroll 1
+    for (int k0 = 0; k0 < n_coef; k0 += 4 * kScoreThreads) {
+      double qv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = min(k0 + u * kScoreThreads + tid, n_coef - 1);
+        const int row = row0 + k / (DIM * G), tt = k % (DIM * G);
+        const int b = row / D.Hkv, g = row % D.Hkv;
+        qv[u] = (double)load_f<T>(q, ((size_t)b * D.Hq + g * G + tt % G) * DIM + tt / G);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + u * kScoreThreads + tid;
+        if (k < n_coef) {
+          double *c4 = coef_w + ((size_t)(row0 + k / (DIM * G)) * DIM * G + k % (DIM * G)) * 4;
+          c4[0] = qv[u] >= 0.0 ? qv[u] : 0.0;
+          c4[1] = qv[u] < 0.0 ? qv[u] : 0.0;
+          c4[2] = qv[u];
+          c4[3] = qv[u] * qv[u];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPtPer; ++u) {
+    const int k = u * kScoreThreads + tid;
+    if (k < nt * kTilePages) {
+      const int lt = k / kTilePages, r = k % kTilePages;
+      const int t = t_begin + lt;
+      const int np = n_pages_of(pt_len[u] < 0 ? 0 : min(pt_len[u], D.max_pages * D.P), D.P);
+      const int p = (t % tiles_per_row) * kTilePages + r;
+      int ph = p < np ? pt_ph[u] : -1;
+      if (ph < 0 || ph >= D.num_phys) ph = -1;
+      s_phys[lt][r] = ph;
+      if (r == 0) s_np[lt] = np;
+    }
+  }
+  // page ids visible to the block; the coefficient stores are older than
+  // every tile load, so the per-tile vmcnt wait plus the barrier that follows
+  // it also cover them before the first scalar load of the table
+  lds_barrier();
+  EKV_MARK(0, 1);
 
   // ---- tile loads: wave w fetches LDS bytes [w*T/4, (w+1)*T/4) of the tile
   // buffer; lane l of instruction u lands at +16 l, which holds chunk
@@ -148,8 +196,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
     }
   };
   for (int lt = 0; lt < C::kNBuf - 1 && lt < nt; ++lt) issue_tile(lt);  // tiles 0 .. NBUF-2
+  EKV_MARK(0, 2);
 
-  int cur_bg = -1;
   double *red = reinterpret_cast<double *>(C::kRedInTile ? smem : smem + (size_t)C::kNBuf * C::kTileBytes);
   for (int lt = 0; lt < nt; ++lt) {
     const int t = t_begin + lt;
@@ -162,29 +210,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
     // (with a single buffer this is tile lt itself)
     if (lt + C::kNBuf - 1 < nt) issue_tile(lt + C::kNBuf - 1);
 
-    // ---- coefficient table of (b, g), once per run of tiles of that row.
-    // Every block that scores (b, g) stores the same bytes into the same slot.
-    if (row != cur_bg) {
-      cur_bg = row;
-      double *cw = coef_w + (size_t)row * DIM * G * 4;
-#pragma unroll
-      for (int u = 0; u < kQPer; ++u) {  // surplus threads repeat the last entry (same bytes)
-        const int tt = min(u * kScoreThreads + tid, DIM * G - 1);
-        const double qv = (double)load_f<T>(q, ((size_t)b * D.Hq + g * G + tt % G) * DIM + tt / G);
-        double *c4 = cw + (size_t)tt * 4;
-        c4[0] = qv >= 0.0 ? qv : 0.0;
-        c4[1] = qv < 0.0 ? qv : 0.0;
-        c4[2] = qv;
-        c4[3] = qv * qv;
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // table stores (and any tile loads) complete
-    }
     // ---- tile lt is resident once this wave's loads for it completed
     const int ahead = min(C::kNBuf - 1, nt - 1 - lt);  // tiles issued after lt
     wait_vmcnt(ahead * C::kLoadsPerWave);  // loads return in order: this covers all of tile lt
     lds_barrier();
 
     // ---- compute: wave = coordinate quarter, lane = page
+    if (lt == 0) EKV_MARK(0, 3);
     double acc_b[G], acc_m[G], acc_v[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) acc_b[h] = acc_m[h] = acc_v[h] = 0.0;
@@ -244,6 +276,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
     }
     lds_barrier();  // buffer lt % NBUF (and red) may be refilled from here on
   }
+  EKV_MARK(0, 4);
 }
 
 size_t score_ws_bytes(const Dims &D) {
@@ -259,10 +292,11 @@ static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
   using C = ScoreCfg<T, DIM, G>;
   Carve cv(ws);
   double *coef = cv.take<double>((size_t)D.B * D.Hkv * D.d * D.G * 4);
-  // persistent blocks (one per CU), each walking a contiguous run of tiles
+  // persistent blocks (kBlocksPerCu per CU), each walking a contiguous run of tiles
   const int tiles_per_row = (D.max_pages + kTilePages - 1) / kTilePages;
   const int n_tiles = D.B * D.Hkv * tiles_per_row;
-  int tiles_per_block = (n_tiles + 255) / 256;
+  const int slots = 256 * C::kBlocksPerCu;
+  int tiles_per_block = (n_tiles + slots - 1) / slots;
   if (tiles_per_block > kMaxTilesPerBlock) tiles_per_block = kMaxTilesPerBlock;
   const int grid = (n_tiles + tiles_per_block - 1) / tiles_per_block;
   static bool attr_set = false;
@@ -301,4 +335,5 @@ hipError_t launch_score(const Dims &D, int dtype, const void *q, const void *met
   return launch_score_d<float, 128>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
 }
 
+EKV_TRACE_DUMP(ekv_trace_dump_score)
 }  // namespace ekv
