@@ -44,7 +44,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
-    ap.add_argument("--only", default="", help="profiling aid: 'score', 'step', 'softmax' or 'entmax_full'")
+    ap.add_argument("--only", default="", choices=["", "score", "step", "copy"],
+                    help="profiling aid: run only score_pages, only the step, or a plain 1 GiB device copy "
+                         "(the calibration of the HBM byte counters), then exit")
     return ap.parse_args()
 
 
@@ -62,6 +64,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     E.load()
+    if args.only == "copy":
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {src.nbytes} bytes x4")
+        return
     wl = synth.WORKLOADS[args.workload]
     alpha = wl.alphas[0]
     t0 = time.time()
@@ -185,12 +195,39 @@ def main():
     step_us = a.elapsed_time(b) * 1e3 / args.steps
     log(f"[bench] step: {step_us:.2f} us ({'graph' if graphs else 'eager'})")
 
+    # ---- score_pages launch duration: HIP events around a graph of back-to-back
+    # launches (rotating replicas) on the stream they run on
+    n_sc = 4 * R
+    score_us = None
+    try:
+        gsc = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            with torch.cuda.graph(gsc, stream=s2):
+                for i in range(n_sc):
+                    score(i % R)
+        torch.cuda.current_stream().wait_stream(s2)
+        gsc.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(5):
+            gsc.replay()
+        b.record()
+        torch.cuda.synchronize()
+        score_us = a.elapsed_time(b) * 1e3 / (5 * n_sc)
+    except Exception as e:  # capture unsupported: events around eager launches
+        log(f"[bench] score graph failed ({e})")
     # ---- per-call breakdown (eager, events around each call, rotating replicas)
     n = max(3 * R, 12)
-    score_us = time_calls(lambda i: score(i % R), n)
+    score_eager_us = time_calls(lambda i: score(i % R), n)
+    if score_us is None:
+        score_us = score_eager_us
     sel_us = time_calls(lambda i: select(), n)
     dec_us = time_calls(lambda i: decode(i % R), n)
-    log(f"[bench] eager per call: score {score_us:.2f} us, select {sel_us:.2f} us, decode {dec_us:.2f} us")
+    log(f"[bench] score_pages per launch (graph of {n_sc}): {score_us:.2f} us; eager per call: score "
+        f"{score_eager_us:.2f} us, select {sel_us:.2f} us, decode {dec_us:.2f} us")
 
     # ---- algorithmic bytes of the dominant kernel (score_pages)
     seq = sl.cpu().numpy().astype(np.int64)
@@ -251,12 +288,12 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(score_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": score_traffic(args.workload),
             "algorithmic_bytes": score_bytes,
             "launch_us": round(score_us, 3),
         },
         "breakdown_us": {"score_pages": round(score_us, 3), "select": round(sel_us, 3),
-                         "entmax_decode_sparse": round(dec_us, 3)},
+                         "entmax_decode_sparse": round(dec_us, 3), "note": "select/decode: eager, per call"},
         "selection": {"pages_per_head_mean": round(per_head_pages / (B * Hq), 2),
                       "kv_group_union_pages": union, "pages_per_seq": int(npg.max())},
         "step_algorithmic_bytes": int(step_bytes),
@@ -300,16 +337,51 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+SCORE_SOURCES = ("sparse_decode_attention_page_amd/csrc/score.hip", "sparse_decode_attention_page_amd/csrc/common.hpp")
+
+
+def score_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def score_traffic(workload):
+    """HBM bytes per score_pages launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when the
+    scorer's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"score_pages_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != score_sources_sha():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, shape, wl, alpha, policy):
-    """The oracle (plain fp64 C, OpenMP over rows) on the query heads of 2 KV
-    groups of the same workload, scaled to the full step."""
+    """The oracle (plain fp64 C, OpenMP over query rows) on the same workload:
+    score_pages + selection + sparse decode for every query row, repeated until
+    about 10 s of work have run (the metadata build is not part of a step).  A
+    workload whose step would take the oracle more than ~30 s is cut to whole
+    KV-head groups of batch 0 and scaled to the full step."""
     import numpy as np
     import oracle
 
-    G = inp.Hq // inp.Hkv
-    groups = min(2, inp.Hkv)
-    rows = [b * inp.Hq + h for b in range(1) for h in range(groups * G)]
-    osh = oracle.Shape(inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys, inp.dtype)
+    B, Hq, Hkv = inp.B, inp.Hq, inp.Hkv
+    G = Hq // Hkv
+    osh = oracle.Shape(B, Hq, Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys, inp.dtype)
     t0 = time.time()
     k = inp.host("k_pool")
     v = inp.host("v_pool")
@@ -318,19 +390,42 @@ def cpu_baseline(inp, shape, wl, alpha, policy):
     sl = inp.seq_lens.cpu().numpy()
     meta = oracle.build_page_meta(osh, k, pt, sl)
     log(f"[bench] oracle inputs ready in {time.time() - t0:.1f}s")
-    t1 = time.perf_counter()
-    box, mu, var = oracle.score_pages(osh, q, meta, pt, sl, rows=rows)
-    if policy == "gauss":
-        sel, cnt, _ = oracle.select_gauss(osh, box, mu, var, sl, alpha, wl.delta, rows=rows)
+
+    def step(rows):
+        t1 = time.perf_counter()
+        box, mu, var = oracle.score_pages(osh, q, meta, pt, sl, rows=rows)
+        if policy == "gauss":
+            sel, cnt, _ = oracle.select_gauss(osh, box, mu, var, sl, alpha, wl.delta, rows=rows)
+        else:
+            sel, cnt = oracle.select_topk(osh, box, sl, wl.topk or 64, rows=rows)
+        oracle.entmax_decode(osh, q, k, v, pt, sl, alpha, sel, cnt, rows=rows)
+        return time.perf_counter() - t1
+
+    all_rows = list(range(B * Hq))
+    probe = all_rows[:G]
+    dt_probe = step(probe)
+    omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    # rows run in parallel over min(rows, threads) threads
+    est_full = dt_probe * len(all_rows) / len(probe) * min(len(probe), omp) / min(len(all_rows), omp)
+    if est_full <= 30.0:
+        rows = all_rows
+        reps = max(1, int(10.0 / max(est_full, 1e-3)))
     else:
-        sel, cnt = oracle.select_topk(osh, box, sl, wl.topk or 64, rows=rows)
-    oracle.entmax_decode(osh, q, k, v, pt, sl, alpha, sel, cnt, rows=rows)
-    dt = time.perf_counter() - t1
-    scale = (inp.B * inp.Hq) / len(rows)
-    threads = min(len(rows), os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+        groups = max(1, min(Hkv, int(30.0 / est_full * Hkv)))
+        rows = list(range(groups * G))
+        reps = 1
+    total = 0.0
+    for _ in range(reps):
+        total += step(rows)
+    dt = total / reps
+    scale = len(all_rows) / len(rows)
+    threads = min(len(rows), omp, os.cpu_count() or 1)
+    sample = (f"score+select+sparse decode of {len(rows)} of {len(all_rows)} query rows, "
+              f"{reps} run(s) averaged ({total:.1f}s of work)"
+              + (f", scaled x{scale:g}" if scale != 1 else ""))
+    log(f"[bench] cpu baseline: {dt * scale * 1e3:.1f} ms/step ({sample}, {threads} threads)")
     return {"value": round(dt * scale * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {inp.B * inp.Hq} query heads (batch 0, KV heads 0-{groups - 1}), "
-                      f"score+select+sparse decode in {dt:.2f}s, scaled x{scale:g}"}
+            "sample": sample}
 
 
 if __name__ == "__main__":

@@ -186,6 +186,23 @@ __device__ __forceinline__ void block_sum2(double &a, double &b, double *scratch
   a = sa;
   b = sb;
 }
+// N block sums with one barrier pair; `scratch` holds N * blockDim.x / 64 values.
+template <int N>
+__device__ __forceinline__ void block_sum_n(double (&v)[N], double *scratch) {
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    for (int i = 0; i < N; ++i) scratch[i * nw + w] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double s = scratch[i * nw];
+    for (int k = 1; k < nw; ++k) s += scratch[i * nw + k];
+    v[i] = s;
+  }
+}
 template <typename T>
 __device__ __forceinline__ T block_max(T v, T *scratch) {
   v = wave_max(v);

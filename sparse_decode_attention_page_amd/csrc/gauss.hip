@@ -44,7 +44,25 @@ namespace ekv {
 
 constexpr int kGThreads = 256;
 constexpr int kNB = 256;  // histogram bins
-constexpr int kNThr = 8;  // thresholds of the certified lower bracket
+constexpr int kNThr = 3;  // thresholds of the certified lower bracket
+constexpr int kZB = 128;  // buckets of the node lookup over z in [-5, 5)
+constexpr double kZLo = -5.0, kZScale = kZB / 10.0;
+
+// Suffix tables of the rule about each node and the node lookup (host-built):
+// T_r[k] = sum_{j >= k} w_j (x_j - x_k)^r, so the rule weight of a page's
+// points above theta is n T0[k] with k the first node above
+// z = (theta - a mu) / (a sqrt2 sigma).
+struct GaussTables {
+  double t[17][4];        // T0[k], T1[k], T2[k], x_k (row 16: no node above, x = +inf)
+  unsigned char kb[kZB];  // first node above the bucket's lower edge
+};
+
+// First node above z: bucket table plus one compare (a bucket holds at most one node).
+__device__ __forceinline__ int node_above(double z, const double (*tab)[4], const unsigned char *kb) {
+  const double zc = fmin(fmax((z - kZLo) * kZScale, 0.0), (double)(kZB - 1));
+  const int k = kb[(int)zc];
+  return k + ((z >= tab[k][3]) ? 1 : 0);
+}
 
 struct GaussParams {
   double a, beta, delta, nsig;
@@ -133,13 +151,16 @@ __device__ __forceinline__ RowCtx row_ctx(const Dims &D, const GaussParams &gp, 
 
 // ---------------------------------------------------------------- K1: brackets
 __global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussParams gp, GaussConsts gc,
+                                                                  GaussTables gt,
                                                                   const float *__restrict__ box,
                                                                   const float *__restrict__ mu,
                                                                   const float *__restrict__ var,
                                                                   const int32_t *__restrict__ seq_lens,
                                                                   const uint8_t *__restrict__ seq_mask,
                                                                   GaussWs ws) {
-  __shared__ double red[kGThreads / kWave];
+  __shared__ double red[kNThr * kGThreads / kWave];
+  __shared__ double tab[17][4];
+  __shared__ unsigned char kb[kZB];
   const int chunk = blockIdx.x;
   EKV_MARK(0, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
@@ -150,78 +171,72 @@ __global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussP
     ws.ctr[rc.row * 2 + 1] = 0;
   }
   if (chunk >= rc.nch && chunk > 0) return;
+  for (int i = threadIdx.x; i < 17 * 4; i += kGThreads) tab[i / 4][i % 4] = gt.t[i / 4][i % 4];
+  for (int i = threadIdx.x; i < kZB; i += kGThreads) kb[i] = gt.kb[i];
   const size_t base = (size_t)rc.row * D.max_pages;
-  const double sqrt2 = 1.4142135623730951;
   const double pw_full = pow(2.5 / (double)D.P, gp.a);  // the lone-page bracket term of a full page
+  const int p_begin = chunk * gp.chunk, p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  // pass 1 (each thread 4 consecutive pages): the single-page bound and the top node
   double lo_c = -INFINITY, top = -INFINITY;
-  const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  Pages4 pg;
 #pragma unroll 1
-  for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
-    float bx[4], m[4], v[4];
+  for (int p0 = p_begin; p0 < p_end; p0 += 4 * kGThreads) {
+    const int pb = p0 + 4 * threadIdx.x;
+    pg.load(box, mu, var, base, pb, p_end);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = min(p0 + u * kGThreads + (int)threadIdx.x, p_end - 1);
-      bx[u] = box[base + p];
-      m[u] = mu[base + p];
-      v[u] = var[base + p];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = p0 + u * kGThreads + threadIdx.x;
-      if (p >= p_end || !page_valid(bx[u], m[u], v[u])) continue;
-      const int n = min(D.P, rc.L - p * D.P);
-      const double sig = sqrt(v[u] > 0.0f ? (double)v[u] : 0.0);
-      lo_c = fmax(lo_c, gp.a * (double)m[u] - (n == D.P ? pw_full : pow(2.5 / (double)n, gp.a)));
-      top = fmax(top, gh_point(gp.a, (double)m[u], sig, gc.x[15]));
+      if (pb + u >= p_end || !page_valid(pg.bx[u], pg.m[u], pg.v2[u])) continue;
+      const int n = min(D.P, rc.L - (pb + u) * D.P);
+      const double sig = sqrt(pg.v2[u] > 0.0f ? (double)pg.v2[u] : 0.0);
+      lo_c = fmax(lo_c, gp.a * (double)pg.m[u] - (n == D.P ? pw_full : pow(2.5 / (double)n, gp.a)));
+      top = fmax(top, gh_point(gp.a, (double)pg.m[u], sig, gc.x[15]));
     }
   }
   EKV_MARK(0, 1);
   lo_c = block_max(lo_c, red);
   top = block_max(top, red);
-  // Tighter certified bound: with W_i the rule weight (n_p w_j) of the
-  // chunk's points above theta_i = top - (top - lo_c) 2^-i,
-  // F(theta_i - W_i^-(alpha-1)) >= W_i (W_i^-(alpha-1))^(1/(alpha-1)) = 1, and
-  // F of the row is at least F of the chunk.
+  // pass 2, a tighter certified bound: with W the rule weight (n_p w_j) of the
+  // chunk's points above theta = top - f (top - lo_c),
+  // F(theta - W^-(alpha-1)) >= W (W^-(alpha-1))^(1/(alpha-1)) = 1, and F of the
+  // row is at least F of the chunk.  Per page W is n T0[k] (one table lookup).
   double lo_b = lo_c;
   if (top > lo_c) {
     const double span = top - lo_c;
-    double th[kNThr], W[kNThr];
+    constexpr double kFrac[kNThr] = {0.35, 0.42, 0.5};
+    double W[kNThr];
 #pragma unroll
-    for (int i = 0; i < kNThr; ++i) { th[i] = top - span * ldexp(1.0, -i); W[i] = 0.0; }
+    for (int j = 0; j < kNThr; ++j) W[j] = 0.0;
 #pragma unroll 1
-    for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
-      float bx[4], m[4], v[4];
+    for (int p0 = p_begin; p0 < p_end; p0 += 4 * kGThreads) {
+      const int pb = p0 + 4 * threadIdx.x;
+      if (p_end - p_begin > 4 * kGThreads) pg.load(box, mu, var, base, pb, p_end);  // else still loaded
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int p = min(p0 + u * kGThreads + (int)threadIdx.x, p_end - 1);
-        bx[u] = box[base + p];
-        m[u] = mu[base + p];
-        v[u] = var[base + p];
-      }
-#pragma unroll 1
-      for (int u = 0; u < 4; ++u) {
-        const int p = p0 + u * kGThreads + threadIdx.x;
-        if (p >= p_end || !page_valid(bx[u], m[u], v[u])) continue;
-        const double n = (double)min(D.P, rc.L - p * D.P);
-        const double sig = sqrt(v[u] > 0.0f ? (double)v[u] : 0.0);
-        for (int j = 15; j >= 0; --j) {
-          const double vj = gh_point(gp.a, (double)m[u], sig, gc.x[j]);
-          if (!(vj > th[0])) break;  // nodes ascend in j
-          const double c = n * gc.w[j];
+        if (pb + u >= p_end || !page_valid(pg.bx[u], pg.m[u], pg.v2[u])) continue;
+        const double n = (double)min(D.P, rc.L - (pb + u) * D.P);
+        const double am = gp.a * (double)pg.m[u];
+        const double B = gp.a * 1.4142135623730951 * sqrt(pg.v2[u] > 0.0f ? (double)pg.v2[u] : 0.0);
+        const double ib = B > 0.0 ? 1.0 / B : 0.0;
 #pragma unroll
-          for (int i = 0; i < kNThr; ++i) W[i] += vj > th[i] ? c : 0.0;
+        for (int j = 0; j < kNThr; ++j) {
+          const double th = top - span * kFrac[j];
+          if (!(B > 0.0)) { W[j] += am > th ? n : 0.0; continue; }  // point mass at a mu
+          const int k = node_above((th - am) * ib, tab, kb);
+          W[j] += k < 16 ? n * tab[k][0] : 0.0;
         }
       }
     }
+    block_sum_n<kNThr>(W, red);
 #pragma unroll
-    for (int i = 0; i < kNThr; ++i) {
-      const double wi = block_sum(W[i], red);
-      if (wi > 0.0) {
-        const double d = gp.ibeta == 2 ? 1.0 / sqrt(wi) : 1.0 / wi;  // wi^-(alpha-1), alpha in {1.5, 2}
-        lo_b = fmax(lo_b, th[i] - d - 1e-12 * fmax(1.0, fabs(top)));
+    for (int j = 0; j < kNThr; ++j) {
+      if (W[j] > 0.0) {
+        const double th = top - span * kFrac[j];
+        const double d = gp.ibeta == 2 ? 1.0 / sqrt(W[j]) : 1.0 / W[j];  // W^-(alpha-1), alpha in {1.5, 2}
+        lo_b = fmax(lo_b, th - d - 1e-12 * fmax(1.0, fabs(top)));
       }
     }
   }
+  EKV_MARK(0, 2);
   if (threadIdx.x == 0) {
     ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 0] = lo_b;
     ws.part[((size_t)rc.row * gp.nchunk + chunk) * 2 + 1] = top;
@@ -233,9 +248,13 @@ __device__ __forceinline__ void row_bracket(const GaussParams &gp, const GaussWs
   lo = -INFINITY;
   hi = -INFINITY;
   const int n = rc.nch > 0 ? rc.nch : 1;
-  for (int c = 0; c < n; ++c) {
-    lo = fmax(lo, ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 0]);
-    hi = fmax(hi, ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 1]);
+  // every slot is loaded (independent of the row's length, so the loads issue
+  // at once); slots past the row's chunks are ignored
+#pragma unroll 8
+  for (int c = 0; c < gp.nchunk; ++c) {
+    const double l = ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 0];
+    const double h = ws.part[((size_t)rc.row * gp.nchunk + c) * 2 + 1];
+    if (c < n) { lo = fmax(lo, l); hi = fmax(hi, h); }
   }
   if (hi > -INFINITY && !(hi > lo)) hi = lo + fmax(1e-300, fabs(lo) * 1e-15);
 }
@@ -735,6 +754,30 @@ static GaussWs carve_gauss(const Dims &D, const GaussParams &gp, void *base, siz
   return w;
 }
 
+static GaussTables build_tables(const GaussConsts &gc) {
+  GaussTables gt;
+  for (int k = 0; k <= 16; ++k) {
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+    for (int j = k; j < 16; ++j) {
+      const double dx = gc.x[j] - gc.x[k];
+      t0 += gc.w[j];
+      t1 += gc.w[j] * dx;
+      t2 += gc.w[j] * dx * dx;
+    }
+    gt.t[k][0] = t0;
+    gt.t[k][1] = t1;
+    gt.t[k][2] = t2;
+    gt.t[k][3] = k < 16 ? gc.x[k] : INFINITY;
+  }
+  for (int b = 0; b < kZB; ++b) {
+    const double edge = kZLo + b / kZScale;
+    int k = 0;
+    while (k < 16 && gc.x[k] <= edge) ++k;
+    gt.kb[b] = (unsigned char)k;
+  }
+  return gt;
+}
+
 size_t gauss_ws_bytes(const Dims &D) {
   GaussParams gp = make_params(D, 1.5, 0.0, 3.0);
   size_t bytes = 0;
@@ -756,7 +799,8 @@ hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const 
   }
   GaussWs w = carve_gauss(D, gp, ws, nullptr);
   dim3 grid(gp.nchunk, rows);
-  hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var,
+  static const GaussTables gt = build_tables(gc);
+  hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, gt, box, mu, var,
                      seq_lens, seq_mask, w);
   hipLaunchKernelGGL(gauss_hist_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, mu, var, box, seq_lens,
                      seq_mask, w);

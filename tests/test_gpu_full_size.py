@@ -1,0 +1,156 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (same generator, same calls, same workspaces).
+
+The oracle recomputes sampled query rows one by one: page metadata of the
+sampled sequences (bit-exact), page scores of the sampled rows (stored float32
+values; the fp64 sums may round once more or less than the oracle's
+sequential sums, so a value may sit one float32 ulp away), the page sets of
+both selectors computed from the GPU's own scores (bit-exact), the sparse and
+full-cache entmax outputs, thresholds and supports, and the full-cache softmax
+output (tolerances as in the small cases).
+"""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, rel_l2_rows, sets_equal, torch
+import sparse_decode_attention_page_amd as E
+from sparse_decode_attention_page_amd import synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+N_SAMPLE = 3
+
+
+def _rows_sample(B, Hq, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, B * Hq - 1}
+    rows.update(int(r) for r in rng.choice(B * Hq, size=min(N_SAMPLE, B * Hq), replace=False))
+    return sorted(rows)
+
+
+@pytest.fixture(scope="module", params=list(synth.WORKLOADS))
+def full(request):
+    t = torch()
+    wl = synth.WORKLOADS[request.param]
+    print(f"\n[full-size] generating {wl.name}", flush=True)
+    inp = synth.make_device(wl, 0)
+    shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+    osh = oracle.Shape(inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys, inp.dtype, 0.0)
+    B, Hq, MP = inp.B, inp.Hq, inp.max_pages
+    meta = t.zeros((inp.num_phys, inp.Hkv, 4, inp.d), dtype=inp.k_pool.dtype, device="cuda")
+    E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta)
+    box = t.full((B, Hq, MP), np.nan, device="cuda")
+    mu, var = t.full_like(box, np.nan), t.full_like(box, np.nan)
+    E.score_pages(shape, inp.q, meta, inp.page_table, inp.seq_lens, box, mu, var)
+    rows = _rows_sample(B, Hq, 7)
+    host = {k: inp.host(k) for k in ("q", "k_pool", "v_pool", "page_table", "seq_lens")}
+    t.cuda.synchronize()
+    return dict(wl=wl, inp=inp, shape=shape, osh=osh, meta=meta, box=box, mu=mu, var=var, rows=rows, host=host)
+
+
+def _take_rows(a, rows):
+    a = np.asarray(a)
+    return a.reshape(-1, *a.shape[2:])[rows]
+
+
+def test_full_meta_sampled_sequences(full):
+    inp, h = full["inp"], full["host"]
+    bs = sorted({r // inp.Hq for r in full["rows"]})
+    sl = np.zeros_like(h["seq_lens"])
+    sl[bs] = h["seq_lens"][bs]  # the oracle rebuilds the sampled sequences' pages only
+    want = oracle.build_page_meta(full["osh"], h["k_pool"], h["page_table"], sl)
+    t = torch()
+    got = full["meta"].view(t.int16).cpu().numpy().view(np.uint16) if inp.dtype == "bf16" else full["meta"].cpu().numpy()
+    for b in bs:
+        npg = (int(h["seq_lens"][b]) + inp.P - 1) // inp.P
+        phys = h["page_table"][b, :npg]
+        assert np.array_equal(got[phys], want[phys]), f"metadata of sequence {b} differs"
+
+
+def test_full_score_sampled_rows(full):
+    inp, h, rows = full["inp"], full["host"], full["rows"]
+    t = torch()
+    meta_h = full["meta"].view(t.int16).cpu().numpy().view(np.uint16) if inp.dtype == "bf16" else full["meta"].cpu().numpy()
+    bo, mo, vo = oracle.score_pages(full["osh"], h["q"], meta_h, h["page_table"], h["seq_lens"], rows=rows)
+    for got, want in ((full["box"], bo), (full["mu"], mo), (full["var"], vo)):
+        g = _take_rows(got.cpu().numpy(), rows)
+        w = _take_rows(want, rows)
+        for i, r in enumerate(rows):
+            npg = (int(h["seq_lens"][r // inp.Hq]) + inp.P - 1) // inp.P
+            gi, wi = g[i, :npg], w[i, :npg]
+            ulp = np.abs(gi.view(np.int32).astype(np.int64) - wi.view(np.int32).astype(np.int64))
+            assert ulp.max() <= 1, f"row {r}: score differs by {ulp.max()} ulp"
+            assert (ulp == 0).mean() > 0.999, f"row {r}: too many 1-ulp differences"
+
+
+def _select(full, policy):
+    t = torch()
+    inp, wl = full["inp"], full["wl"]
+    B, Hq, MP = inp.B, inp.Hq, inp.max_pages
+    sel = t.full((B, Hq, MP), -1, dtype=t.int32, device="cuda")
+    cnt = t.full((B, Hq), -1, dtype=t.int32, device="cuda")
+    tau = t.full((B, Hq), np.nan, dtype=t.float64, device="cuda")
+    if policy == "topk":
+        E.select_pages_topk(full["shape"], full["box"], inp.seq_lens, wl.topk, sel, cnt)
+    else:
+        E.select_pages_gauss(full["shape"], full["box"], full["mu"], full["var"], inp.seq_lens, wl.alphas[0],
+                             wl.delta, sel, cnt, tau_hat=tau)
+    return sel, cnt, tau
+
+
+@pytest.mark.parametrize("policy", ["topk", "gauss"])
+def test_full_selection_sampled_rows(full, policy):
+    inp, h, rows, wl = full["inp"], full["host"], full["rows"], full["wl"]
+    sel, cnt, tau = _select(full, policy)
+    box, mu, var = (full[k].cpu().numpy() for k in ("box", "mu", "var"))
+    if policy == "topk":
+        so, co = oracle.select_topk(full["osh"], box, h["seq_lens"], wl.topk, rows=rows)
+    else:
+        so, co, to = oracle.select_gauss(full["osh"], box, mu, var, h["seq_lens"], wl.alphas[0], wl.delta, rows=rows)
+        tg = tau.cpu().numpy().reshape(-1)[rows]
+        assert np.allclose(tg, to.reshape(-1)[rows], rtol=1e-12, atol=1e-12)
+    assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co, rows=set(rows)) == []
+
+
+@pytest.mark.parametrize("kind", ["sparse_gauss", "sparse_topk", "full"])
+def test_full_entmax_sampled_rows(full, kind):
+    t = torch()
+    inp, h, rows, wl = full["inp"], full["host"], full["rows"], full["wl"]
+    B, Hq, MP, P, d = inp.B, inp.Hq, inp.max_pages, inp.P, inp.d
+    alpha = wl.alphas[0]
+    out = t.full((B, Hq, d), np.nan, device="cuda")
+    tau = t.full((B, Hq), np.nan, dtype=t.float64, device="cuda")
+    w = t.full((B, Hq, MP * P), np.nan, device="cuda")
+    if kind == "full":
+        E.entmax_decode_full(full["shape"], inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, alpha,
+                             out, tau=tau, weights_out=w)
+        oo, to, wo = oracle.entmax_decode(full["osh"], h["q"], h["k_pool"], h["v_pool"], h["page_table"],
+                                          h["seq_lens"], alpha, rows=rows, want_weights=True)
+    else:
+        sel, cnt, _ = _select(full, "gauss" if kind == "sparse_gauss" else "topk")
+        E.entmax_decode_sparse(full["shape"], inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, sel, cnt,
+                               alpha, out, tau=tau, weights_out=w)
+        oo, to, wo = oracle.entmax_decode(full["osh"], h["q"], h["k_pool"], h["v_pool"], h["page_table"],
+                                          h["seq_lens"], alpha, sel.cpu().numpy(), cnt.cpu().numpy(), rows=rows,
+                                          want_weights=True)
+    og = _take_rows(out.cpu().numpy(), rows)
+    tg = tau.cpu().numpy().reshape(-1)[rows]
+    wg = w.view(B * Hq, -1)[rows].cpu().numpy()
+    oo, to, wo = _take_rows(oo, rows), to.reshape(-1)[rows], _take_rows(wo, rows)
+    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(wg > 0, wo > 0), "support differs"
+    assert np.max(np.abs(wg - wo)) < 1e-5
+    assert rel_l2_rows(og, oo) <= TOL[inp.dtype]
+
+
+def test_full_softmax_sampled_rows(full):
+    t = torch()
+    inp, h, rows = full["inp"], full["host"], full["rows"]
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, device="cuda")
+    lse = t.full((inp.B, inp.Hq), np.nan, device="cuda")
+    E.softmax_decode_full(full["shape"], inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, out, lse=lse)
+    oo, lo = oracle.softmax_decode(full["osh"], h["q"], h["k_pool"], h["v_pool"], h["page_table"], h["seq_lens"],
+                                   rows=rows)
+    assert rel_l2_rows(_take_rows(out.cpu().numpy(), rows), _take_rows(oo, rows)) <= TOL[inp.dtype]
+    assert np.allclose(lse.cpu().numpy().reshape(-1)[rows], lo.reshape(-1)[rows], rtol=1e-5, atol=1e-5)
