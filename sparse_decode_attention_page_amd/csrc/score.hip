@@ -10,29 +10,39 @@
 //                 mu  = c sum_i q_i mean_i,   var = c^2 sum_i q_i^2 var_i.
 //
 // The kernel is bound by the metadata stream (one record per page and KV head,
-// 4*d elements).  Design:
-//  * work unit = one (b, KV head g) and a tile of 64 logical pages; the G query
-//    heads of the group share every record read (GQA reuse);
-//  * persistent blocks walk a contiguous run of tiles with NBUF tile buffers in
-//    LDS: tiles t+1 .. t+NBUF-1 stream in with global_load_lds (16 bytes per
-//    lane, straight to LDS, no staging registers) while tile t is computed;
-//  * inside a record the 16-byte chunks are XOR-swizzled by the record index,
-//    so the lane-per-page reads of one chunk hit distinct LDS banks; the global
-//    side stays fully coalesced (a wave fetches whole records, permuted);
-//  * each wave owns a quarter of the coordinates, each lane one page; the
-//    query-derived coefficients (q+, q-, q, q^2 in fp64) are wave-uniform, written
-//    once per (b, g) to a workspace table and read back through scalar loads, so
-//    the inner loop is four fp64 FMAs per (coordinate, head) on exact products;
-//  * the four coordinate quarters are combined in a fixed order.
+// rows kmin | kmax | mean | var of d elements each).  Design:
+//  * a block scores two tiles of 64 logical pages of one (b, KV head g); the G
+//    query heads of the group share every record read (GQA reuse);
+//  * wave k of the block handles metadata row k for all 64 pages (lane = page), so
+//    mu and var are finished inside one wave and the box needs only the kmin and
+//    kmax halves swapped between waves 0 and 1 (a 64 x G x 8-byte exchange);
+//  * tiles are fetched with coalesced 16-byte vector loads into registers (the
+//    second tile while the first is scored), then written to LDS with
+//    the 16-byte chunks of each record XOR-swizzled by the record index, so that
+//    the lane-per-record reads of the compute hit distinct banks;
+//  * the query-derived coefficients (q-, q+, q, q^2 in fp64, one table per
+//    (b, g) row and kind) are written once to a workspace table at the start and
+//    read back through scalar loads, so the inner loop is one fp64 FMA per
+//    (element, head) on exact products with a wave-uniform operand.  The table's
+//    lines are pulled into the scalar cache with one batch of loads that overlaps
+//    the tile fetch: otherwise the first tile's compute issues its coefficient
+//    loads a few lines at a time, each a full L2 round trip behind the stream;
+//  * the blocks that share a CU (on MI355X block i runs beside i + n_cu,
+//    i + 2 n_cu, ...) are given consecutive tiles of the same row, so one
+//    coefficient table serves the CU's scalar cache;
+//  * outputs stay in registers until both tiles are scored, so that the vector
+//    memory queue holds only loads while tiles are in flight (a store among them
+//    would make every later wait drain the whole queue).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ekv {
 
-constexpr int kTilePages = 64;
-constexpr int kScoreThreads = 256;
-constexpr int kMaxTilesPerBlock = 16;
-constexpr size_t kScoreLds = 160 * 1024;
+constexpr int kTilePages = 64;      // one page per lane
+constexpr int kScoreThreads = 256;  // four waves: one per metadata row kind
+constexpr int kScoreTiles = 2;      // tiles per block
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Chunk;  // 16 bytes of one metadata row
@@ -55,258 +65,281 @@ struct Chunk<float> {
 
 template <typename T, int DIM, int G>
 struct ScoreCfg {
+  static constexpr int kE = Chunk<T>::kElems;          // elements per 16-byte chunk
+  static constexpr int kRowChunks = DIM / kE;          // chunks per metadata row
   static constexpr int kRecBytes = 4 * DIM * (int)sizeof(T);
-  static constexpr int kRecChunks = kRecBytes / 16;
   static constexpr int kTileBytes = kTilePages * kRecBytes;
-  static constexpr int kRedBytes = 4 * 3 * G * kWave * 8;
-  static constexpr bool kRedInTile = kRedBytes <= kTileBytes;
-  // One tile buffer per block: LDS-DMA throughput grows with the number of
-  // waves issuing it, so LDS goes to more resident blocks per CU rather than
-  // to deeper per-block prefetch; the blocks of a CU overlap each other's
-  // loads and compute.
-  static constexpr int kNBuf = 1;
-  static constexpr size_t kLds = (size_t)kNBuf * kTileBytes + (kRedInTile ? 0 : kRedBytes);
-  static constexpr int kBlocksPerCu = (int)(kScoreLds / (kLds + 8 * 1024)) < 1 ? 1 : (int)(kScoreLds / (kLds + 8 * 1024));
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;  // 1 KB per wave instruction
-  static_assert(kLds <= kScoreLds, "tile does not fit in LDS");
-  static_assert(kTileBytes % 4096 == 0, "tile split across 4 waves");
+  static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
+  // the second tile is requested once the first is in LDS: with both in flight from
+  // the start the per-tile latency grows with the deeper memory queue and the first
+  // tile arrives later (measured on cold HBM)
+  static constexpr bool kBothTiles = false;
+  static constexpr int kLds = kTileBytes + G * kTilePages * 8 + kScoreTiles * (kTilePages + 1) * 4;
+  static constexpr int kBlocksPerCu = (160 * 1024) / (kLds + 1024) >= 4 ? 4 : (160 * 1024) / (kLds + 1024);
+  static constexpr int kCoefRow = 4 * DIM * G;         // doubles per (b, g) row: [kind][i][h]
+  static constexpr int kWarmLines = DIM * G * 8 / 64;  // 64-byte lines of one kind's coefficients
 };
 
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-  // vmcnt[3:0] | expcnt[6:4]=7 | lgkmcnt[11:8]=15 | vmcnt[5:4] << 14)
-  switch (n) {
-#define EKV_W(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (7 << 4) | (15 << 8) | (((k) >> 4) << 14)); break;
-    EKV_W(0) EKV_W(1) EKV_W(2) EKV_W(3) EKV_W(4) EKV_W(5) EKV_W(6) EKV_W(7) EKV_W(8) EKV_W(9) EKV_W(10)
-    EKV_W(11) EKV_W(12) EKV_W(13) EKV_W(14) EKV_W(15) EKV_W(16) EKV_W(17) EKV_W(18) EKV_W(19) EKV_W(20)
-    EKV_W(21) EKV_W(22) EKV_W(23) EKV_W(24) EKV_W(25) EKV_W(26) EKV_W(27) EKV_W(28) EKV_W(29) EKV_W(30)
-    EKV_W(31) EKV_W(32) EKV_W(33) EKV_W(34) EKV_W(35) EKV_W(36) EKV_W(37) EKV_W(38) EKV_W(39) EKV_W(40)
-    EKV_W(41) EKV_W(42) EKV_W(43) EKV_W(44) EKV_W(45) EKV_W(46) EKV_W(47) EKV_W(48) EKV_W(49) EKV_W(50)
-    EKV_W(51) EKV_W(52) EKV_W(53) EKV_W(54) EKV_W(55) EKV_W(56) EKV_W(57) EKV_W(58) EKV_W(59) EKV_W(60)
-    EKV_W(61) EKV_W(62) EKV_W(63)
-#undef EKV_W
-    default: __builtin_amdgcn_s_waitcnt(0); break;
+// Tile loads: thread t fetches 16-byte chunks u*256 + t of the tile (a wave
+// instruction covers 1 KB of consecutive records); missing pages read record 0
+// and are masked later.
+template <typename T, int DIM, int G, int L>
+__device__ __forceinline__ void score_load_tile(u32x4 (&r)[L], const char *mbase, const int *phys, int g, int hkv,
+                                                int tid) {
+  using C = ScoreCfg<T, DIM, G>;
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int off = (u * kScoreThreads + tid) * 16;
+    const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
+    const int ph = max(phys[rec], 0);
+    r[u] = *reinterpret_cast<const u32x4 *>(mbase + ((size_t)ph * hkv + g) * C::kRecBytes + pos * 16);
+  }
+}
+// ... and into LDS, chunk pos of record rec at slot pos ^ (rec & 7)
+template <typename T, int DIM, int G, int L>
+__device__ __forceinline__ void score_stash_tile(const u32x4 (&r)[L], unsigned char *buf, int tid) {
+  using C = ScoreCfg<T, DIM, G>;
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int off = (u * kScoreThreads + tid) * 16;
+    const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
+    *reinterpret_cast<u32x4 *>(buf + rec * C::kRecBytes + ((pos ^ (rec & 7)) * 16)) = r[u];
   }
 }
 
 template <typename T, int DIM, int G>
-__global__ __launch_bounds__(kScoreThreads) void score_pages_kernel(
-    Dims D, int tiles_per_row, int tiles_per_block, const T *__restrict__ q, const T *__restrict__ meta,
+__global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G>::kBlocksPerCu)) void score_pages_kernel(
+    Dims D, int tiles_per_row, int n_cu, const T *__restrict__ q, const T *__restrict__ meta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, double *__restrict__ coef_w,
     const double *__restrict__ coef_r, float *__restrict__ box, float *__restrict__ mu,
     float *__restrict__ var) {
   using C = ScoreCfg<T, DIM, G>;
-  constexpr int kE = Chunk<T>::kElems;  // elements per 16-byte chunk
-  constexpr int kRowChunks = DIM / kE;   // chunks per metadata row
-  constexpr int kQChunks = DIM / 4 / kE; // chunks per coordinate quarter
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_phys[kMaxTilesPerBlock][kTilePages];
-  __shared__ int s_np[kMaxTilesPerBlock];
+  constexpr int kE = C::kE;
+  constexpr int kGH = G > 1 ? G / 2 : 1;  // box heads finished by each of waves 0 and 1
+  __shared__ __align__(16) unsigned char tile[C::kTileBytes];
+  __shared__ double xb[G][kTilePages];  // box halves swapped between waves 0 and 1
+  __shared__ int s_phys[kScoreTiles][kTilePages];
+  __shared__ int s_np[kScoreTiles];
+  __shared__ int s_zero;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // metadata row kind
   const int n_tiles = D.B * D.Hkv * tiles_per_row;
-  const int t_begin = blockIdx.x * tiles_per_block;
-  const int t_end = min(n_tiles, t_begin + tiles_per_block);
+  // blocks resident on one CU (i, i + n_cu, ...) take consecutive tile pairs
+  const int nb = gridDim.x, bi = blockIdx.x;
+  const int lb = (n_cu > 0 && nb % n_cu == 0) ? (bi % n_cu) * (nb / n_cu) + bi / n_cu : bi;
+  const int t_begin = lb * kScoreTiles;
+  const int t_end = min(n_tiles, t_begin + kScoreTiles);
   if (t_begin >= t_end) return;
   const int nt = t_end - t_begin;
   const char *mbase = reinterpret_cast<const char *>(meta);
+  const int row0 = t_begin / tiles_per_row, nrows = (t_end - 1) / tiles_per_row - row0 + 1;
   EKV_MARK(0, 0);
 
-  // ---- prologue, one round trip: the page ids of every tile of the block
-  // (missing pages / bad ids -> -1) and the coefficient table (q+, q-, q, q^2
-  // in fp64) of every (b, g) row the block touches.  Every block that scores
-  // (b, g) stores the same bytes into the same slot; the tile loop reads the
-  // table back through scalar loads once the stores have completed.
-  constexpr int kPtPer = kMaxTilesPerBlock * kTilePages / kScoreThreads;
-  int pt_ph[kPtPer], pt_len[kPtPer];
-#pragma unroll
-  for (int u = 0; u < kPtPer; ++u) {
-    const int k = min(u * kScoreThreads + tid, nt * kTilePages - 1);
+  // ---- prologue, one round trip: page ids (missing pages / bad ids -> -1) and q;
+  // then the coefficient table of the block's rows, completed before any tile load
+  // is issued (every block that scores row (b, g) stores the same bytes).
+  {
+    const int k = min(tid, nt * kTilePages - 1);
     const int t = t_begin + k / kTilePages;
     const int b = t / tiles_per_row / D.Hkv;
     const int p = min((t % tiles_per_row) * kTilePages + k % kTilePages, D.max_pages - 1);
-    pt_len[u] = seq_lens[b];
-    pt_ph[u] = page_table[(size_t)b * D.max_pages + p];
-  }
-  {
-    const int row0 = t_begin / tiles_per_row, nrows = (t_end - 1) / tiles_per_row - row0 + 1;
+    const int len = seq_lens[b];
+    const int ph0 = page_table[(size_t)b * D.max_pages + p];
     const int n_coef = nrows * DIM * G;
 #pragma unroll 1
     for (int k0 = 0; k0 < n_coef; k0 += 4 * kScoreThreads) {
       double qv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int k = min(k0 + u * kScoreThreads + tid, n_coef - 1);
-        const int row = row0 + k / (DIM * G), tt = k % (DIM * G);
-        const int b = row / D.Hkv, g = row % D.Hkv;
-        qv[u] = (double)load_f<T>(q, ((size_t)b * D.Hq + g * G + tt % G) * DIM + tt / G);
+        const int kk = min(k0 + u * kScoreThreads + tid, n_coef - 1);
+        const int row = row0 + kk / (DIM * G), tt = kk % (DIM * G);
+        const int bb = row / D.Hkv, g = row % D.Hkv;
+        qv[u] = (double)load_f<T>(q, ((size_t)bb * D.Hq + g * G + tt % G) * DIM + tt / G);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int k = k0 + u * kScoreThreads + tid;
-        if (k < n_coef) {
-          double *c4 = coef_w + ((size_t)(row0 + k / (DIM * G)) * DIM * G + k % (DIM * G)) * 4;
-          c4[0] = qv[u] >= 0.0 ? qv[u] : 0.0;
-          c4[1] = qv[u] < 0.0 ? qv[u] : 0.0;
-          c4[2] = qv[u];
-          c4[3] = qv[u] * qv[u];
+        const int kk = k0 + u * kScoreThreads + tid;
+        if (kk < n_coef) {
+          // [row][kind][i][h]: kind 0 q- (kmin), 1 q+ (kmax), 2 q (mean), 3 q^2 (var)
+          double *cw = coef_w + (size_t)(row0 + kk / (DIM * G)) * C::kCoefRow + kk % (DIM * G);
+          const double qq = qv[u];
+          cw[0 * DIM * G] = qq < 0.0 ? qq : 0.0;
+          cw[1 * DIM * G] = qq >= 0.0 ? qq : 0.0;
+          cw[2 * DIM * G] = qq;
+          cw[3 * DIM * G] = qq * qq;
         }
       }
     }
-  }
-#pragma unroll
-  for (int u = 0; u < kPtPer; ++u) {
-    const int k = u * kScoreThreads + tid;
-    if (k < nt * kTilePages) {
-      const int lt = k / kTilePages, r = k % kTilePages;
-      const int t = t_begin + lt;
-      const int np = n_pages_of(pt_len[u] < 0 ? 0 : min(pt_len[u], D.max_pages * D.P), D.P);
-      const int p = (t % tiles_per_row) * kTilePages + r;
-      int ph = p < np ? pt_ph[u] : -1;
+    if (tid < nt * kTilePages) {
+      const int lt = tid / kTilePages, r = tid % kTilePages;
+      const int np = n_pages_of(len < 0 ? 0 : min(len, D.max_pages * D.P), D.P);
+      const int pp = ((t_begin + lt) % tiles_per_row) * kTilePages + r;
+      int ph = pp < np ? ph0 : -1;
       if (ph < 0 || ph >= D.num_phys) ph = -1;
       s_phys[lt][r] = ph;
       if (r == 0) s_np[lt] = np;
     }
+    if (tid == 0) s_zero = 0;
   }
-  // page ids visible to the block; the coefficient stores are older than
-  // every tile load, so the per-tile vmcnt wait plus the barrier that follows
-  // it also cover them before the first scalar load of the table
+  // vmcnt(0): the table's stores have completed before its lines are loaded back
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
   lds_barrier();
   EKV_MARK(0, 1);
 
-  // ---- tile loads: wave w fetches LDS bytes [w*T/4, (w+1)*T/4) of the tile
-  // buffer; lane l of instruction u lands at +16 l, which holds chunk
-  // (pos ^ (rec & 7)) of record rec.
-  auto issue_tile = [&](int lt) {
-    const int t = t_begin + lt;
-    const int g = (t / tiles_per_row) % D.Hkv;
-    unsigned char *buf = smem + (size_t)(lt % C::kNBuf) * C::kTileBytes;
+  // The table is read only after the barrier: the offset below is a zero the block
+  // wrote to LDS before it, so no load of the table can be scheduled earlier.
+  // (coef_r stays restrict-qualified, which lets the reads be scalar loads.)
+  const int zoff = __builtin_amdgcn_readfirstlane(s_zero);
+  const double *cf0 = coef_r + zoff + (size_t)row0 * C::kCoefRow + (size_t)wave * DIM * G;
+  // scalar-cache warm-up: one load per 64-byte line of this wave's coefficients,
+  // all in flight together; consumed before the first tile is scored
+  unsigned warm = 0;
+  {
+    const unsigned *cl = reinterpret_cast<const unsigned *>(cf0);
 #pragma unroll
-    for (int u = 0; u < C::kLoadsPerWave; ++u) {
-      const int off = (wave * C::kLoadsPerWave + u) * 1024 + lane * 16;
-      const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
-      const int chunk = pos ^ (rec & 7);
-      const int ph = max(s_phys[lt][rec], 0);  // missing pages read record 0 and are masked later
-      const char *src = mbase + ((size_t)ph * D.Hkv + g) * C::kRecBytes + (size_t)chunk * 16;
-      __builtin_amdgcn_global_load_lds((const void *)src,
-                                       (__attribute__((address_space(3))) void *)(buf + (wave * C::kLoadsPerWave + u) * 1024),
-                                       16, 0, 0);
-    }
-  };
-  for (int lt = 0; lt < C::kNBuf - 1 && lt < nt; ++lt) issue_tile(lt);  // tiles 0 .. NBUF-2
-  EKV_MARK(0, 2);
+    for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[i * 16];
+  }
+  u32x4 ring0[C::kLoads], ring1[C::kLoads];
+  score_load_tile<T, DIM, G>(ring0, mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
+  if (C::kBothTiles) {
+    const int l1 = min(1, nt - 1);
+    score_load_tile<T, DIM, G>(ring1, mbase, s_phys[l1], ((t_begin + l1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+  }
 
-  double *red = reinterpret_cast<double *>(C::kRedInTile ? smem : smem + (size_t)C::kNBuf * C::kTileBytes);
-  for (int lt = 0; lt < nt; ++lt) {
-    const int t = t_begin + lt;
-    const int row = t / tiles_per_row, pt = t % tiles_per_row;
-    const int b = row / D.Hkv, g = row % D.Hkv;
-    const int p0 = pt * kTilePages;
-    const int np = s_np[lt];
-    unsigned char *buf = smem + (size_t)(lt % C::kNBuf) * C::kTileBytes;
-    // ---- prefetch: tile lt+NBUF-1 goes into the buffer freed by tile lt-1
-    // (with a single buffer this is tile lt itself)
-    if (lt + C::kNBuf - 1 < nt) issue_tile(lt + C::kNBuf - 1);
-
-    // ---- tile lt is resident once this wave's loads for it completed
-    const int ahead = min(C::kNBuf - 1, nt - 1 - lt);  // tiles issued after lt
-    wait_vmcnt(ahead * C::kLoadsPerWave);  // loads return in order: this covers all of tile lt
-    lds_barrier();
-
-    // ---- compute: wave = coordinate quarter, lane = page
-    if (lt == 0) EKV_MARK(0, 3);
-    double acc_b[G], acc_m[G], acc_v[G];
+  const double c = D.scale, c2 = D.scale * D.scale;
+  const unsigned char *rec = tile + lane * C::kRecBytes;
+  const int sw = lane & 7;
+  float outv[kScoreTiles][G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc_b[h] = acc_m[h] = acc_v[h] = 0.0;
-    const double *cf = coef_r + (size_t)row * DIM * G * 4;
-    const unsigned char *rec = buf + lane * C::kRecBytes;
-    const int sw = lane & 7;
-#pragma unroll 1
-    for (int qc = 0; qc < kQChunks; ++qc) {
-      const int chunk = wave * kQChunks + qc;  // chunk index within a row
-      double kmin[kE], kmax[kE], kmean[kE], kvar[kE];
-      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((0 * kRowChunks + chunk) ^ sw) * 16), kmin);
-      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((1 * kRowChunks + chunk) ^ sw) * 16), kmax);
-      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((2 * kRowChunks + chunk) ^ sw) * 16), kmean);
-      Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((3 * kRowChunks + chunk) ^ sw) * 16), kvar);
+  for (int lt = 0; lt < kScoreTiles; ++lt)
 #pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const int i = chunk * kE + e;
-        const double *ci = cf + (size_t)i * G * 4;
+    for (int h = 0; h < G; ++h) outv[lt][h] = 0.f;
+
+#pragma unroll
+  for (int lt = 0; lt < kScoreTiles; ++lt) {
+    if (lt < nt) {
+      if (lt > 0) lds_barrier();  // the previous tile and exchange are fully read
+      if (lt == 0) score_stash_tile<T, DIM, G>(ring0, tile, tid);
+      else score_stash_tile<T, DIM, G>(ring1, tile, tid);
+      asm volatile("" ::: "memory");
+      if (!C::kBothTiles && lt == 0 && nt > 1)
+        score_load_tile<T, DIM, G>(ring1, mbase, s_phys[1], ((t_begin + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+      lds_barrier();
+      if (lt == 0) asm volatile("" ::"s"(warm));
+      if (lt == 0) EKV_MARK(0, 2);
+
+      // ---- wave = row kind, lane = page: acc[h] = sum_i coef[kind][i][h] * row_i
+      const int row = (t_begin + lt) / tiles_per_row;
+      const double *cf = cf0 + (size_t)(row - row0) * C::kCoefRow;
+      double acc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll 2
+      for (int ch = 0; ch < C::kRowChunks; ++ch) {
+        double x[kE];
+        Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          const double *ci = cf + (size_t)(ch * kE + e) * G;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            if constexpr (sizeof(T) == 2)
+              acc[h] = __builtin_fma(ci[h], x[e], acc[h]);  // exact product: fused == separate
+            else
+              acc[h] = acc[h] + ci[h] * x[e];               // fp32 keys: round the product first
+          }
+        }
+      }
+
+      // ---- box = (kmin part) + (kmax part); waves 0 / 1 finish heads [0, G/2) / [G/2, G)
+      const bool ok = s_phys[lt][lane] >= 0;
+      if (wave < 2) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const double cpos = ci[h * 4 + 0], cneg = ci[h * 4 + 1], cq = ci[h * 4 + 2], cqq = ci[h * 4 + 3];
-          acc_b[h] = __builtin_fma(cpos, kmax[e], acc_b[h]);
-          acc_b[h] = __builtin_fma(cneg, kmin[e], acc_b[h]);
-          acc_m[h] = __builtin_fma(cq, kmean[e], acc_m[h]);
-          if constexpr (sizeof(T) == 2)
-            acc_v[h] = __builtin_fma(cqq, kvar[e], acc_v[h]);  // exact product: fused == separate
-          else
-            acc_v[h] = acc_v[h] + cqq * kvar[e];               // fp32 keys: round the product first
+          const bool mine = G == 1 ? wave == 0 : (h / kGH) == wave;
+          if (!mine) xb[h][lane] = acc[h];
+        }
+      }
+      lds_barrier();
+      if (wave < 2) {
+#pragma unroll
+        for (int j = 0; j < kGH; ++j) {
+          const int h = G == 1 ? 0 : wave * kGH + j;
+          const double own = (G == 1 || wave == 0) ? acc[j] : acc[(G == 1 ? 0 : kGH) + j];
+          const double other = xb[h][lane];
+          const double s_min = wave == 0 ? own : other;
+          const double s_max = wave == 0 ? other : own;
+          outv[lt][j] = ok ? __double2float_ru(c * (s_min + s_max)) : NAN;
+        }
+      } else {
+        const double sc = wave == 2 ? c : c2;
+#pragma unroll
+        for (int h = 0; h < G; ++h) outv[lt][h] = ok ? (float)(sc * acc[h]) : NAN;
+      }
+    }
+  }
+  EKV_MARK(0, 3);
+
+  // ---- outputs: lane = page, 64 consecutive floats per (kind, head) and tile
+#pragma unroll
+  for (int lt = 0; lt < kScoreTiles; ++lt) {
+    if (lt < nt) {
+      const int t = t_begin + lt;
+      const int row = t / tiles_per_row;
+      const int b = row / D.Hkv, g = row - b * D.Hkv;
+      const int p = (t - row * tiles_per_row) * kTilePages + lane;
+      if (p < s_np[lt]) {
+        if (wave < 2) {
+          if (G > 1 || wave == 0) {
+#pragma unroll
+            for (int j = 0; j < kGH; ++j) {
+              const int h = G == 1 ? 0 : wave * kGH + j;
+              box[((size_t)b * D.Hq + g * G + h) * D.max_pages + p] = outv[lt][j];
+            }
+          }
+        } else {
+          float *dst = wave == 2 ? mu : var;
+#pragma unroll
+          for (int h = 0; h < G; ++h) dst[((size_t)b * D.Hq + g * G + h) * D.max_pages + p] = outv[lt][h];
         }
       }
     }
-    // ---- combine the four coordinate quarters in a fixed order
-    double *rd = C::kRedInTile ? reinterpret_cast<double *>(buf) : red;
-    if (C::kRedInTile) lds_barrier();  // every wave is done reading the tile
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      rd[(wave * 3 * G + 0 * G + h) * kWave + lane] = acc_b[h];
-      rd[(wave * 3 * G + 1 * G + h) * kWave + lane] = acc_m[h];
-      rd[(wave * 3 * G + 2 * G + h) * kWave + lane] = acc_v[h];
-    }
-    lds_barrier();
-    const double c = D.scale, c2 = D.scale * D.scale;
-    for (int idx = tid; idx < 3 * G * kWave; idx += kScoreThreads) {
-      const int k = idx / kWave, r = idx % kWave;
-      const int p = p0 + r;
-      if (p >= np) continue;
-      double sacc = rd[(0 * 3 * G + k) * kWave + r];
-      sacc += rd[(1 * 3 * G + k) * kWave + r];
-      sacc += rd[(2 * 3 * G + k) * kWave + r];
-      sacc += rd[(3 * 3 * G + k) * kWave + r];
-      const int kind = k / G, h = g * G + (k % G);
-      const size_t o = ((size_t)b * D.Hq + h) * D.max_pages + p;
-      const bool ok = s_phys[lt][r] >= 0;
-      if (kind == 0) box[o] = ok ? __double2float_ru(c * sacc) : NAN;
-      else if (kind == 1) mu[o] = ok ? (float)(c * sacc) : NAN;
-      else var[o] = ok ? (float)(c2 * sacc) : NAN;
-    }
-    lds_barrier();  // buffer lt % NBUF (and red) may be refilled from here on
   }
   EKV_MARK(0, 4);
 }
 
 size_t score_ws_bytes(const Dims &D) {
   Carve cv(nullptr);
-  cv.take<double>((size_t)D.B * D.Hkv * D.d * D.G * 4);
+  cv.take<double>((size_t)D.B * D.Hkv * 4 * D.d * D.G);
   return cv.bytes();
+}
+
+static int device_cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = -1;
+    cached[dev] = n;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
 }
 
 template <typename T, int DIM, int G>
 static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
                                  const int32_t *page_table, const int32_t *seq_lens, float *box,
                                  float *mu, float *var, void *ws, hipStream_t s) {
-  using C = ScoreCfg<T, DIM, G>;
   Carve cv(ws);
-  double *coef = cv.take<double>((size_t)D.B * D.Hkv * D.d * D.G * 4);
-  // persistent blocks (kBlocksPerCu per CU), each walking a contiguous run of tiles
+  double *coef = cv.take<double>((size_t)D.B * D.Hkv * 4 * D.d * D.G);
   const int tiles_per_row = (D.max_pages + kTilePages - 1) / kTilePages;
-  const int n_tiles = D.B * D.Hkv * tiles_per_row;
-  const int slots = 256 * C::kBlocksPerCu;
-  int tiles_per_block = (n_tiles + slots - 1) / slots;
-  if (tiles_per_block > kMaxTilesPerBlock) tiles_per_block = kMaxTilesPerBlock;
-  const int grid = (n_tiles + tiles_per_block - 1) / tiles_per_block;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void *)score_pages_kernel<T, DIM, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)C::kLds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G>), dim3(grid), dim3(kScoreThreads), C::kLds, s, D,
-                     tiles_per_row, tiles_per_block, (const T *)q, (const T *)meta, page_table, seq_lens, coef,
+  const long long n_tiles = (long long)D.B * D.Hkv * tiles_per_row;
+  const long long grid = (n_tiles + kScoreTiles - 1) / kScoreTiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s, D,
+                     tiles_per_row, device_cu_count(), (const T *)q, (const T *)meta, page_table, seq_lens, coef,
                      (const double *)coef, box, mu, var);
   return hipGetLastError();
 }
