@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--selector-sweep", action="store_true",
+                    help="time select_pages_topk (k=64) and select_pages_gauss over contexts 32k..1M "
+                         "(one JSON line with the table), then exit")
     ap.add_argument("--only", default="", choices=["", "score", "step", "copy"],
                     help="profiling aid: run only score_pages, only the step, or a plain 1 GiB device copy "
                          "(the calibration of the HBM byte counters), then exit")
@@ -71,6 +74,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {src.nbytes} bytes x4")
+        return
+    if args.selector_sweep:
+        selector_sweep(args)
         return
     wl = synth.WORKLOADS[args.workload]
     alpha = wl.alphas[0]
@@ -229,6 +235,39 @@ def main():
     log(f"[bench] score_pages per launch (graph of {n_sc}): {score_us:.2f} us; eager per call: score "
         f"{score_eager_us:.2f} us, select {sel_us:.2f} us, decode {dec_us:.2f} us")
 
+    # ---- top-k selection (k=64 unless the workload names one) on the same scores
+    k_top = wl.topk or 64
+    sel2 = torch.empty_like(sel)
+    cnt2 = torch.empty_like(cnt)
+    E.select_pages_topk(shape, box, sl, k_top, sel2, cnt2, ws=ws_t)
+    torch.cuda.synchronize()
+    topk_us = time_calls(lambda i: E.select_pages_topk(shape, box, sl, k_top, sel2, cnt2, ws=ws_t), n)
+
+    # ---- metadata append for the new token: rebuild the page holding each
+    # sequence's last token (build_page_meta with from_token = L_b - 1)
+    from_tok = (sl - 1).clamp(min=0).to(torch.int32)
+    meta_scratch = reps[0][3].clone()
+
+    def append(i):
+        E.build_page_meta(shape, reps[0][1], pt, sl, meta_scratch, from_token=from_tok)
+
+    append(0)
+    torch.cuda.synchronize()
+    append_us = time_calls(append, n)
+    del meta_scratch
+
+    # ---- a measured stream read on this GPU (the library's read probe over a
+    # 2 GiB K/V replica, rotating replicas so each pass reads HBM): the practical
+    # ceiling next to the 8 TB/s peak
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for r in range(R):
+        E.stream_read(reps[r][1], sink)
+    torch.cuda.synchronize()
+    sr_us = time_calls(lambda i: E.stream_read(reps[i % R][1 + (i // R) % 2], sink), 2 * R)
+    stream_gbs = reps[0][1].nbytes / (sr_us * 1e-6) / 1e9
+    log(f"[bench] top-k select {topk_us:.2f} us, metadata append {append_us:.2f} us, "
+        f"stream read {stream_gbs:.0f} GB/s")
+
     # ---- algorithmic bytes of the dominant kernel (score_pages)
     seq = sl.cpu().numpy().astype(np.int64)
     npg = (seq + P - 1) // P
@@ -291,9 +330,14 @@ def main():
             "traffic": score_traffic(args.workload),
             "algorithmic_bytes": score_bytes,
             "launch_us": round(score_us, 3),
+            "stream_read_GBps": round(stream_gbs, 1),
+            "frac_of_stream_read": round(score_gbs / stream_gbs, 4),
         },
         "breakdown_us": {"score_pages": round(score_us, 3), "select": round(sel_us, 3),
-                         "entmax_decode_sparse": round(dec_us, 3), "note": "select/decode: eager, per call"},
+                         "entmax_decode_sparse": round(dec_us, 3), "select_topk": round(topk_us, 3),
+                         "metadata_append": round(append_us, 3),
+                         "note": "select/decode/top-k/append: eager, per call; append = rebuild of "
+                                 "the page holding each sequence's newest token"},
         "selection": {"pages_per_head_mean": round(per_head_pages / (B * Hq), 2),
                       "kv_group_union_pages": union, "pages_per_seq": int(npg.max())},
         "step_algorithmic_bytes": int(step_bytes),
@@ -335,6 +379,57 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, shape, wl, alpha, args.policy)
 
     print(json.dumps(result), flush=True)
+
+
+def selector_sweep(args):
+    """Top-k (k=64) vs Gaussian selection time as the context grows, on the
+    long-context workload's shapes (B=1, 32 query / 8 KV heads, d=64, pages of
+    64); scores come from score_pages on freshly built metadata."""
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_page_amd as E
+    from sparse_decode_attention_page_amd import synth
+
+    wl = synth.WORKLOADS["long_1m"]
+    alpha = wl.alphas[0]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rows = []
+    for ctx in (32768, 131072, 524288, 1048576):
+        inp = synth.make_device(wl, args.seed, ctx_override=ctx)
+        shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+        B, Hq, Hkv, d, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.max_pages
+        meta = torch.zeros((inp.num_phys, Hkv, 4, d), dtype=inp.k_pool.dtype, device="cuda")
+        E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta)
+        box = torch.empty((B, Hq, MP), device="cuda"); mu = torch.empty_like(box); var = torch.empty_like(box)
+        sel = torch.empty((B, Hq, MP), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+        E.score_pages(shape, inp.q, meta, inp.page_table, inp.seq_lens, box, mu, var,
+                      ws=E.workspace(shape, E.CALL_SCORE))
+        ws_t, ws_g = E.workspace(shape, E.CALL_TOPK), E.workspace(shape, E.CALL_GAUSS)
+        calls = {"topk64": lambda: E.select_pages_topk(shape, box, inp.seq_lens, 64, sel, cnt, ws=ws_t),
+                 "gauss": lambda: E.select_pages_gauss(shape, box, mu, var, inp.seq_lens, alpha, wl.delta,
+                                                       sel, cnt, ws=ws_g)}
+        row = {"context": ctx, "pages": MP}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(20):
+                a, b = ev(), ev()
+                a.record(); fn(); b.record()
+                ts.append((a, b))
+            torch.cuda.synchronize()
+            row[name + "_us"] = round(float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3, 2)
+            if name == "gauss":
+                row["gauss_kept_pages_mean"] = round(float(cnt.float().mean().item()), 2)
+        log(f"[sweep] {row}")
+        rows.append(row)
+        del inp, meta, box, mu, var, sel, cnt
+        torch.cuda.empty_cache()
+    print(json.dumps({"selector_sweep": rows, "unit": "us per call (median of 20, eager)",
+                      "workload": "long_1m shapes at the listed contexts"}), flush=True)
 
 
 SCORE_SOURCES = ("sparse_decode_attention_page_amd/csrc/score.hip", "sparse_decode_attention_page_amd/csrc/common.hpp")

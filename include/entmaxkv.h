@@ -196,6 +196,12 @@ int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const vo
 
 /* The 16-point Gauss-Hermite rule the Gaussian selector uses (host copy, for
  * inspection): nodes ascending, weights for the weight function exp(-x^2). */
+/* Measurement probe, not part of the decode path: reads `bytes` of device memory
+ * at src (16-byte aligned, bytes a multiple of 16) with coalesced 16-byte loads
+ * and no other traffic (one 4-byte store to sink only if a checksum matches a
+ * fixed value), so that its duration gives the HBM read rate this GPU sustains.
+ * Returns ENTMAXKV_OK or ENTMAXKV_ERR_INVALID_ARGUMENT / ENTMAXKV_ERR_HIP. */
+int32_t entmaxkv_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
 void entmaxkv_gauss_hermite16(double *nodes /*(host)[16]*/, double *weights /*(host)[16]*/);
 
 #ifdef __cplusplus

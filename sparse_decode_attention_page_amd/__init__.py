@@ -25,7 +25,8 @@ CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SO
 
 EXPORTS = ("build_page_meta", "score_pages", "select_pages_topk", "select_pages_gauss",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full",
-           "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16")
+           "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
+           "entmaxkv_stream_read")
 
 
 class EntmaxKVError(RuntimeError):
@@ -59,6 +60,8 @@ def load(path: str | None = None):
     lib.entmaxkv_status_string.argtypes = [i32]
     lib.entmaxkv_gauss_hermite16.restype = None
     lib.entmaxkv_gauss_hermite16.argtypes = [vp, vp]
+    lib.entmaxkv_stream_read.restype = i32
+    lib.entmaxkv_stream_read.argtypes = [vp, sz, vp, vp]
     lib.build_page_meta.restype = i32
     lib.build_page_meta.argtypes = [sh, vp, vp, vp, vp, vp, vp]
     lib.score_pages.restype = i32
@@ -79,6 +82,14 @@ def load(path: str | None = None):
 
 def status_string(status: int) -> str:
     return load().entmaxkv_status_string(int(status)).decode()
+
+
+def stream_read(src, sink, stream=None):
+    """Measurement probe: read every byte of the device tensor src once with
+    coalesced 16-byte loads (sink: a device int32/uint32 tensor of >= 1 element)."""
+    st = load().entmaxkv_stream_read(_ptr(src, name="src"), src.numel() * src.element_size(),
+                                     _ptr(sink, name="sink"), _stream(stream))
+    _check("entmaxkv_stream_read", st)
 
 
 def gauss_hermite16():

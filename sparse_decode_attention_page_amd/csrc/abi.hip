@@ -129,6 +129,31 @@ static bool misaligned16(const void *a, const void *b = nullptr, const void *c =
 
 using namespace ekv;
 
+// ---------------------------------------------------------------- measurement probe
+// Reads a buffer with coalesced 16-byte loads (eight in flight per thread) and
+// keeps the loads alive through a checksum that is stored only if it equals a
+// fixed value: the HBM read rate of a plain stream on this GPU.
+namespace {
+typedef unsigned int probe_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kProbeUnroll = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const probe_u32x4 *__restrict__ src, size_t n16,
+                                                          uint32_t *__restrict__ sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256 * kProbeUnroll;
+  for (size_t base = (size_t)blockIdx.x * 256 * kProbeUnroll + threadIdx.x; base < n16; base += stride) {
+    probe_u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const size_t i = base + (size_t)u * 256;
+      v[u] = src[i < n16 ? i : n16 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+}  // namespace
+
 extern "C" {
 
 size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call) {
@@ -268,4 +293,13 @@ int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const vo
   return hip_status(launch_softmax(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, stream));
 }
 
+int32_t entmaxkv_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(1024), dim3(256), 0, stream,
+                     reinterpret_cast<const probe_u32x4 *>(src), bytes / 16, sink);
+  return hip_status(hipGetLastError());
+}
+
 }  // extern "C"
+

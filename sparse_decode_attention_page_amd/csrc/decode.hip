@@ -26,7 +26,16 @@
 //     gathered with 16-byte loads.  Kept tokens outside the support cost no V
 //     traffic.  Rows with more candidates than LDS holds are solved by passes
 //     over the compacted candidates in the workspace.
+//
+// Full cache (the decode that reads every cached token, one of the baselines of
+// the summary's efficiency results, section 4): the same kernel 2 runs on a
+// selection of every page.  Its first launch streams K once per (b, KV head)
+// and range of pages, scoring all G query heads of the group from the same
+// bytes, and writes the identity selection next to the scores; V is then read
+// for the support only.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -822,18 +831,10 @@ size_t decode_ws_bytes(const Dims &D, bool) {
 }
 
 template <typename T, int DIM, int P>
-static hipError_t launch_decode_t(const Dims &D, const DecodeParams &dp, const void *q,
-                                  const void *k_pool, const void *v_pool, const int32_t *page_table,
-                                  const int32_t *seq_lens, const int32_t *sel_idx,
-                                  const int32_t *sel_cnt, float *out, double *tau,
-                                  float *weights_out, void *ws, hipStream_t s) {
-  const DecodeWs w = carve_decode(D, ws, nullptr);
+static hipError_t launch_finish_t(const Dims &D, const DecodeParams &dp, const void *v_pool, const int32_t *seq_lens,
+                                  const int32_t *sel_idx, const int32_t *sel_cnt, float *out, double *tau,
+                                  float *weights_out, const DecodeWs &w, hipStream_t s) {
   const int rows = D.B * D.Hq;
-  const size_t map_bytes = (size_t)(rows + 1) * 4;
-  hipLaunchKernelGGL((decode_scores_kernel<T, DIM, P>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
-                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const size_t cand_bytes = (size_t)kCand * (8 + 4 + 4) + (dp.tau_method == 1 ? (size_t)kCand * 8 : 0);
   static bool attr_set = false;
   if (!attr_set) {
@@ -846,6 +847,22 @@ static hipError_t launch_decode_t(const Dims &D, const DecodeParams &dp, const v
   hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P>), dim3(rows, split), dim3(kDThreads), cand_bytes, s, D, dp,
                      (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
   return hipGetLastError();
+}
+
+template <typename T, int DIM, int P>
+static hipError_t launch_decode_t(const Dims &D, const DecodeParams &dp, const void *q,
+                                  const void *k_pool, const void *v_pool, const int32_t *page_table,
+                                  const int32_t *seq_lens, const int32_t *sel_idx,
+                                  const int32_t *sel_cnt, float *out, double *tau,
+                                  float *weights_out, void *ws, hipStream_t s) {
+  const DecodeWs w = carve_decode(D, ws, nullptr);
+  const int rows = D.B * D.Hq;
+  const size_t map_bytes = (size_t)(rows + 1) * 4;
+  hipLaunchKernelGGL((decode_scores_kernel<T, DIM, P>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
+                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w, s);
 }
 
 template <typename T, int DIM>
@@ -874,6 +891,167 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
   }
   if (D.d == 64) return launch_decode_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
   return launch_decode_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+}
+
+// ------------------------------------------- full cache: every page selected
+// One block per (range of pps pages, KV head g, sequence b); 256 threads, one
+// page per iteration (kDThreads / P threads per token), the next page's K slice
+// loaded while the current one is scored.  For each of the G query heads of the
+// group: exact X of every token (-inf past the sequence end) in kernel 2's
+// item-major layout, the page maximum (NaN for a bad page id), the physical
+// page, the identity selection sel_idx[i] = i and its count N_b.
+template <typename T, int DIM, int P, int G>
+__global__ __launch_bounds__(kDThreads) void full_scores_kernel(Dims D, DecodeParams dp, int pps,
+                                                                const T *__restrict__ q,
+                                                                const T *__restrict__ k_pool,
+                                                                const int32_t *__restrict__ page_table,
+                                                                const int32_t *__restrict__ seq_lens,
+                                                                int32_t *__restrict__ sel_idx,
+                                                                int32_t *__restrict__ sel_cnt,
+                                                                float *__restrict__ weights_out, DecodeWs ws) {
+  constexpr int kParts = kDThreads / P;  // threads per token
+  constexpr int kPer = DIM / kParts;     // coordinates per thread
+  __shared__ double smax[kDThreads / kWave][G];
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, tok = tid / kParts, part = tid % kParts;
+  const int MP = D.max_pages;
+  const size_t wrow = (size_t)MP * P;
+  const int L = seq_len_clamped(seq_lens, b, D);
+  const int np = n_pages_of(L, P);
+  const int p0 = s * pps, p1 = min(np, p0 + pps);
+  const int r0 = b * D.Hq + g * G;
+  if (s == 0 && tid < G) {
+    ws.ctr[r0 + tid] = 0u;  // kernel 2's arrival counters start at zero
+    sel_cnt[r0 + tid] = np;
+  }
+  // weights_out: kernel 2 writes the support; every other slot is zeroed here
+  // (the range holding the last page also zeroes the tail of the row)
+  const int last_s = np > 0 ? (np - 1) / pps : 0;
+  if (weights_out && s <= last_s) {
+    const size_t lo = (size_t)p0 * P, hi = s == last_s ? wrow : (size_t)p1 * P;
+    for (int h = 0; h < G; ++h)
+      for (size_t i = lo + tid; i < hi; i += kDThreads) weights_out[(size_t)(r0 + h) * wrow + i] = 0.0f;
+  }
+  if (p0 >= p1) return;
+
+  float qv[G][kPer];
+#pragma unroll
+  for (int h = 0; h < G; ++h) load_vec<kPer>(q + (size_t)(r0 + h) * DIM + part * kPer, qv[h]);
+  auto phys_of = [&](int p) { return page_table[(size_t)b * MP + p]; };
+  int ph = phys_of(p0);
+  float kv[kPer];
+  load_vec<kPer>(k_pool + (((size_t)min(max(ph, 0), D.num_phys - 1) * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
+#pragma unroll 1
+  for (int p = p0; p < p1; ++p) {
+    // next page's K slice first
+    const int pn = min(p + 1, p1 - 1);
+    const int phn = phys_of(pn);
+    float kn[kPer];
+    load_vec<kPer>(k_pool + (((size_t)min(max(phn, 0), D.num_phys - 1) * D.Hkv + g) * P + tok) * DIM + part * kPer, kn);
+    const bool bad = ph < 0 || ph >= D.num_phys;
+    const int n = min(P, L - p * P);
+    double x[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[h][e], acc);  // exact products
+#pragma unroll
+      for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+      x[h] = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
+      if (part == 0) ws.xs[(size_t)(r0 + h) * wrow + (size_t)p * P + tok] = x[h];
+    }
+    // page maxima of the G heads
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] = wave_max(x[h]);
+    if ((tid & (kWave - 1)) == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h) smax[tid / kWave][h] = x[h];
+    __syncthreads();
+    if (tid < G) {
+      double m = smax[0][tid];
+      for (int w = 1; w < kDThreads / kWave; ++w) m = fmax(m, smax[w][tid]);
+      const size_t o = (size_t)(r0 + tid) * MP + p;
+      ws.pmax[o] = bad ? NAN : m;
+      ws.iphys[o] = (uint32_t)min(max(ph, 0), D.num_phys - 1);
+      sel_idx[o] = p;
+    }
+    __syncthreads();
+    ph = phn;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) kv[e] = kn[e];
+  }
+}
+
+size_t full_ws_bytes(const Dims &D) {
+  Carve cv(nullptr);
+  size_t b = 0;
+  carve_decode(D, nullptr, &b);
+  cv.take<char>(b);
+  cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
+  cv.take<int32_t>((size_t)D.B * D.Hq);
+  return cv.bytes();
+}
+
+template <typename T, int DIM, int P, int G>
+static hipError_t launch_full_t(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
+                                const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
+  size_t dec_bytes = 0;
+  carve_decode(D, nullptr, &dec_bytes);
+  Carve cv(ws);
+  char *dec = cv.take<char>(dec_bytes);
+  int32_t *sel_idx = cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
+  int32_t *sel_cnt = cv.take<int32_t>((size_t)D.B * D.Hq);
+  const DecodeWs w = carve_decode(D, dec, nullptr);
+  // about 2048 blocks over the (b, g, page) space
+  const long long items = (long long)D.B * D.Hkv * D.max_pages;
+  const int pps = (int)std::max<long long>(1, (items + 2047) / 2048);
+  const int S = (D.max_pages + pps - 1) / pps;
+  hipLaunchKernelGGL((full_scores_kernel<T, DIM, P, G>), dim3(S, D.Hkv, D.B), dim3(kDThreads), 0, s, D, dp, pps,
+                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w, s);
+}
+
+template <typename T, int DIM, int P>
+static hipError_t launch_full_g(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
+                                const int32_t *pt, const int32_t *sl, float *out, double *tau, float *wo, void *ws,
+                                hipStream_t s) {
+  switch (D.G) {
+    case 1: return launch_full_t<T, DIM, P, 1>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+    case 2: return launch_full_t<T, DIM, P, 2>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+    case 4: return launch_full_t<T, DIM, P, 4>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+    case 8: return launch_full_t<T, DIM, P, 8>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DIM>
+static hipError_t launch_full_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
+                                const int32_t *pt, const int32_t *sl, float *out, double *tau, float *wo, void *ws,
+                                hipStream_t s) {
+  if (D.P == 16) return launch_full_g<T, DIM, 16>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+  if (D.P == 32) return launch_full_g<T, DIM, 32>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+  return launch_full_g<T, DIM, 64>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+}
+
+hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *page_table, const int32_t *seq_lens, double alpha, float *out,
+                              double *tau, float *weights_out, void *ws, hipStream_t s) {
+  DecodeParams dp;
+  dp.a = alpha - 1.0;
+  dp.beta = 1.0 / dp.a;
+  dp.c = D.scale;
+  dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
+  dp.tau_method = 0;  // safeguarded Newton (the sort form is a sparse-path option)
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64) return launch_full_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
+    return launch_full_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
+  }
+  if (D.d == 64) return launch_full_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
+  return launch_full_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
 }
 
 EKV_TRACE_DUMP(ekv_trace_dump_decode)
