@@ -44,9 +44,14 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming multi-step decode timing")
     ap.add_argument("--selector-sweep", action="store_true",
                     help="time select_pages_topk (k=64) and select_pages_gauss over contexts 32k..1M "
                          "(one JSON line with the table), then exit")
+    ap.add_argument("--quality", action="store_true",
+                    help="approximation quality vs KV budget on every synthetic workload (recall of the "
+                         "full-cache entmax support, discarded mass and relative output error of entmax and "
+                         "softmax under the same kept pages); one JSON line, then exit")
     ap.add_argument("--only", default="", choices=["", "score", "step", "copy"],
                     help="profiling aid: run only score_pages, only the step, or a plain 1 GiB device copy "
                          "(the calibration of the HBM byte counters), then exit")
@@ -56,7 +61,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus N > 1 is not supported",
+        print(json.dumps({"error": "this library runs on one GPU; --gpus N > 1 is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np
@@ -77,6 +82,9 @@ def main():
         return
     if args.selector_sweep:
         selector_sweep(args)
+        return
+    if args.quality:
+        quality_sweep(args)
         return
     wl = synth.WORKLOADS[args.workload]
     alpha = wl.alphas[0]
@@ -268,6 +276,66 @@ def main():
     log(f"[bench] top-k select {topk_us:.2f} us, metadata append {append_us:.2f} us, "
         f"stream read {stream_gbs:.0f} GB/s")
 
+    # ---- streaming decode: one graph per step appends the new token's K and V
+    # to its page, rebuilds that page's metadata, then scores, selects and
+    # decodes with the context one token longer (the context grows from
+    # L - n_total to L over the replays); on copies of replica 0
+    stream_res = None
+    if not args.no_stream:
+        try:
+            n_st, n_wu = 50, 5
+            k2, v2, meta2 = reps[0][1].clone(), reps[0][2].clone(), reps[0][3].clone()
+            seq2 = (sl - (n_st + n_wu + 1)).clamp(min=1).to(torch.int32)
+            knew = torch.randn((B, Hkv, d), device=dev).to(k2.dtype)
+            vnew = torch.randn((B, Hkv, d), device=dev).to(v2.dtype)
+            ptl = pt.long()
+            sel3, cnt3 = torch.empty_like(sel), torch.empty_like(cnt)
+            out3 = torch.empty_like(out)
+
+            def stream_step():
+                seq2.add_(1)
+                pos = (seq2 - 1).long()
+                ph = torch.gather(ptl, 1, (pos // P).unsqueeze(1)).squeeze(1)
+                slot = pos % P
+                k2[ph, :, slot, :] = knew
+                v2[ph, :, slot, :] = vnew
+                E.build_page_meta(shape, k2, pt, seq2, meta2, from_token=(seq2 - 1))
+                E.score_pages(shape, reps[0][0], meta2, pt, seq2, box, mu, var, ws=ws_s)
+                if args.policy == "gauss":
+                    E.select_pages_gauss(shape, box, mu, var, seq2, alpha, wl.delta, sel3, cnt3, ws=ws_g)
+                else:
+                    E.select_pages_topk(shape, box, seq2, wl.topk or 64, sel3, cnt3, ws=ws_t)
+                E.entmax_decode_sparse(shape, reps[0][0], k2, v2, pt, seq2, sel3, cnt3, alpha, out3, ws=ws_d)
+
+            stream_step()  # warm (also the first token)
+            torch.cuda.synchronize()
+            gst = torch.cuda.CUDAGraph()
+            s3 = torch.cuda.Stream()
+            s3.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s3):
+                with torch.cuda.graph(gst, stream=s3):
+                    stream_step()
+            torch.cuda.current_stream().wait_stream(s3)
+            for _ in range(n_wu - 1):
+                gst.replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(n_st):
+                gst.replay()
+            b.record()
+            torch.cuda.synchronize()
+            st_us = a.elapsed_time(b) * 1e3 / n_st
+            L_end = int(seq2.max().item())
+            stream_res = {"us_per_step": round(st_us, 3), "steps": n_st,
+                          "context_end": L_end, "context_start": L_end - n_st,
+                          "step": "K/V append (torch index_put) + build_page_meta append + score_pages + "
+                                  "select_pages_" + args.policy + " + entmax_decode_sparse, one HIP graph per step"}
+            log(f"[bench] streaming step (append + metadata + step): {st_us:.2f} us")
+            del k2, v2, meta2
+        except Exception as e:  # capture unsupported
+            log(f"[bench] streaming step failed ({e})")
+
     # ---- algorithmic bytes of the dominant kernel (score_pages)
     seq = sl.cpu().numpy().astype(np.int64)
     npg = (seq + P - 1) // P
@@ -340,11 +408,12 @@ def main():
                                  "the page holding each sequence's newest token"},
         "selection": {"pages_per_head_mean": round(per_head_pages / (B * Hq), 2),
                       "kv_group_union_pages": union, "pages_per_seq": int(npg.max())},
+        "streaming": stream_res,
         "step_algorithmic_bytes": int(step_bytes),
         "step_GBps": round(step_bytes / (step_us * 1e-6) / 1e9, 1),
     }
 
-    # ---- comparators: this build's full-cache softmax and entmax decodes
+    # ---- comparators: the library's own full-cache softmax and entmax decodes
     if not args.no_comparators:
         ws_sm = E.workspace(shape, E.CALL_SOFTMAX)
         ws_f = E.workspace(shape, E.CALL_DECODE_FULL)
@@ -373,6 +442,55 @@ def main():
         result["speedup"] = {"vs_full_softmax": round(sm_us / step_us, 2),
                              "vs_full_entmax": round(ef_us / step_us, 2)}
         log(f"[bench] full softmax {sm_us:.1f} us, full entmax {ef_us:.1f} us")
+
+        # ---- entmax vs softmax under the same kept set (the step's selection):
+        # discarded probability mass delta and relative output error against each
+        # one's full-cache result (untimed), and the softmax-over-kept-pages time
+        ws_ss = E.workspace(shape, E.CALL_SOFTMAX_SPARSE)
+        q0, k0, v0, _ = reps[0]
+        step(0)
+        torch.cuda.synchronize()
+        out_es = out.clone()
+        wfull = torch.empty((B, Hq, MP * P), device=dev)
+        out_ef = torch.empty_like(out)
+        E.entmax_decode_full(shape, q0, k0, v0, pt, sl, alpha, out_ef, weights_out=wfull, ws=ws_f)
+        out_sf = torch.empty_like(out)
+        lse_f = torch.empty((B, Hq), device=dev)
+        E.softmax_decode_full(shape, q0, k0, v0, pt, sl, out_sf, lse=lse_f, ws=ws_sm)
+        out_ss = torch.empty_like(out)
+        lse_s = torch.empty((B, Hq), device=dev)
+        E.softmax_decode_sparse(shape, q0, k0, v0, pt, sl, sel, cnt, out_ss, lse=lse_s, ws=ws_ss)
+        torch.cuda.synchronize()
+        # unused slots go to a spare column MP (a shared target of True and
+        # False writes would leave the kept flag to the write order)
+        keep = torch.zeros((B, Hq, MP + 1), dtype=torch.bool, device=dev)
+        ar = torch.arange(MP, device=dev)
+        valid = ar[None, None, :] < cnt[:, :, None]
+        keep.scatter_(2, torch.where(valid, sel, torch.full_like(sel, MP)).long(), valid)
+        keep = keep[:, :, :MP]
+        kept_mass = (wfull.view(B, Hq, MP, P).double().sum(-1) * keep).sum(-1)
+        d_ent = (1.0 - kept_mass).clamp(min=0.0)
+        d_sm = (1.0 - torch.exp((lse_s - lse_f).double())).clamp(min=0.0)
+
+        def rel(a, b):
+            return (torch.linalg.vector_norm((a - b).double(), dim=-1)
+                    / torch.linalg.vector_norm(b.double(), dim=-1).clamp(min=1e-30))
+
+        e_ent, e_sm = rel(out_es, out_ef), rel(out_ss, out_sf)
+        ss_us = time_calls(lambda i: E.softmax_decode_sparse(shape, reps[i % R][0], reps[i % R][1], reps[i % R][2],
+                                                             pt, sl, sel, cnt, out_ss, ws=ws_ss), max(R, 6))
+        result["same_kept_set"] = {
+            "selection": "step's " + args.policy + " selection",
+            "delta_entmax_mean": float(d_ent.mean()), "delta_entmax_max": float(d_ent.max()),
+            "delta_softmax_mean": float(d_sm.mean()), "delta_softmax_max": float(d_sm.max()),
+            "rel_err_entmax_mean": float(e_ent.mean()), "rel_err_entmax_max": float(e_ent.max()),
+            "rel_err_softmax_mean": float(e_sm.mean()), "rel_err_softmax_max": float(e_sm.max()),
+            "softmax_decode_sparse_us": round(ss_us, 2),
+        }
+        log(f"[bench] same kept set: delta entmax {float(d_ent.mean()):.3e} vs softmax {float(d_sm.mean()):.3e}; "
+            f"rel err entmax {float(e_ent.mean()):.3e} vs softmax {float(e_sm.mean()):.3e}; "
+            f"softmax over kept pages {ss_us:.1f} us")
+        del wfull
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
@@ -430,6 +548,114 @@ def selector_sweep(args):
         torch.cuda.empty_cache()
     print(json.dumps({"selector_sweep": rows, "unit": "us per call (median of 20, eager)",
                       "workload": "long_1m shapes at the listed contexts"}), flush=True)
+
+
+def quality_sweep(args):
+    """Approximation quality against the KV budget (the comparison of the
+    EntmaxKV summary, sections 3 and 4, on synthetic inputs).  For every
+    workload, alpha and selector setting: kept pages per head, recall of the
+    full-cache entmax support S (|S n T| / |S|, T the tokens of the kept
+    pages), the discarded probability mass delta of entmax (full-cache weights
+    outside T) and of softmax (1 - exp(lse_T - lse_full)), the relative output
+    error ||o - o~|| / ||o|| of each decoded over T, and the largest ratio of
+    that error to its bound 2 B delta (B = largest value norm of the row's
+    sequence and KV head).  Every number comes from this library's kernels."""
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_page_amd as E
+    from sparse_decode_attention_page_amd import synth
+
+    dev = "cuda"
+    rows = []
+    for name in ("tiny_4k", "gqa_32k", "gqa_128k", "long_1m", "batch16_ragged", "gqa_128k_passage",
+                 "long_1m_passage"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_device(wl, args.seed)
+        shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+        B, Hq, Hkv, d, P, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages
+        G = Hq // Hkv
+        sl, pt, q, kp, vp = inp.seq_lens, inp.page_table, inp.q, inp.k_pool, inp.v_pool
+        meta = torch.zeros((inp.num_phys, Hkv, 4, d), dtype=kp.dtype, device=dev)
+        E.build_page_meta(shape, kp, pt, sl, meta)
+        box = torch.empty((B, Hq, MP), device=dev)
+        mu, var = torch.empty_like(box), torch.empty_like(box)
+        E.score_pages(shape, q, meta, pt, sl, box, mu, var)
+        ntok = MP * P
+        valid = torch.arange(ntok, device=dev)[None, :] < sl[:, None]            # [B][ntok]
+        # B of the bound: the largest value norm over the row's sequence and KV head
+        vn = torch.linalg.vector_norm(vp.float(), dim=-1)                         # [phys][Hkv][P]
+        vnb = vn[pt.clamp(min=0).long()].permute(0, 2, 1, 3).reshape(B, Hkv, ntok)
+        vnb = torch.where(valid[:, None, :], vnb, torch.zeros_like(vnb))
+        bnd = vnb.amax(-1).repeat_interleave(G, dim=1).double()                  # [B][Hq]
+        out_sf = torch.empty((B, Hq, d), device=dev)
+        lse_f = torch.empty((B, Hq), device=dev)
+        E.softmax_decode_full(shape, q, kp, vp, pt, sl, out_sf, lse=lse_f)
+        sel = torch.empty((B, Hq, MP), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+        out_es, out_ss = torch.empty_like(out_sf), torch.empty_like(out_sf)
+        lse_s = torch.empty_like(lse_f)
+        ar = torch.arange(MP, device=dev)
+        settings = [("topk", {"k": k}) for k in (4, 16, 64, 256) if k < MP]
+        settings += [("gauss", {"delta": dl, "n_sigma": ns})
+                     for dl, ns in ((0.5, 2.0), (0.5, 3.0), (0.5, 4.0), (0.5, 6.0), (0.0, 3.0), (1.0, 3.0),
+                                    (2.0, 3.0))]
+
+        def rel(a, b):
+            return (torch.linalg.vector_norm((a - b).double(), dim=-1),
+                    torch.linalg.vector_norm(b.double(), dim=-1))
+
+        for alpha in wl.alphas:
+            wfull = torch.empty((B, Hq, ntok), device=dev)
+            out_ef = torch.empty_like(out_sf)
+            E.entmax_decode_full(shape, q, kp, vp, pt, sl, alpha, out_ef, weights_out=wfull)
+            supp = wfull > 0
+            n_supp = supp.sum(-1).double()
+            for kind, par in settings:
+                if kind == "topk":
+                    E.select_pages_topk(shape, box, sl, par["k"], sel, cnt)
+                else:
+                    E.select_pages_gauss(shape, box, mu, var, sl, alpha, par["delta"], sel, cnt,
+                                         n_sigma=par["n_sigma"])
+                E.entmax_decode_sparse(shape, q, kp, vp, pt, sl, sel, cnt, alpha, out_es)
+                E.softmax_decode_sparse(shape, q, kp, vp, pt, sl, sel, cnt, out_ss, lse=lse_s)
+                torch.cuda.synchronize()
+                inside = ar[None, None, :] < cnt[:, :, None]
+                keep = torch.zeros((B, Hq, MP + 1), dtype=torch.bool, device=dev)   # column MP: unused slots
+                keep.scatter_(2, torch.where(inside, sel, torch.full_like(sel, MP)).long(), inside)
+                T = keep[:, :, :MP].repeat_interleave(P, dim=2) & valid[:, None, :]
+                recall = (supp & T).sum(-1).double() / n_supp.clamp(min=1)
+                d_ent = (wfull.double() * (~T)).sum(-1)
+                d_sm = (-torch.expm1((lse_s - lse_f).double())).clamp(min=0.0)
+                ee, ne = rel(out_es, out_ef)
+                es, ns_ = rel(out_ss, out_sf)
+                r_ent, r_sm = ee / ne.clamp(min=1e-30), es / ns_.clamp(min=1e-30)
+                big_e, big_s = d_ent > 1e-6, d_sm > 1e-6
+                ratio_e = float((ee / (2 * bnd * d_ent))[big_e].max()) if bool(big_e.any()) else None
+                ratio_s = float((es / (2 * bnd * d_sm))[big_s].max()) if bool(big_s.any()) else None
+                exact = ~big_e
+                row = {"workload": name, "alpha": alpha, "selector": kind, **par,
+                       "kept_pages_mean": round(float(cnt.double().mean()), 2),
+                       "kept_token_frac": float(T.sum(-1).double().mean() / sl.double().mean()),
+                       "support_mean": round(float(n_supp.mean()), 1),
+                       "recall_mean": float(recall.mean()), "recall_min": float(recall.min()),
+                       "rows_support_kept": float((recall == 1.0).double().mean()),
+                       "delta_entmax_mean": float(d_ent.mean()), "delta_softmax_mean": float(d_sm.mean()),
+                       "rel_err_entmax_mean": float(r_ent.mean()), "rel_err_softmax_mean": float(r_sm.mean()),
+                       "rows_entmax_less_mass": float((d_ent <= d_sm).double().mean()),
+                       "err_over_bound_max_entmax": ratio_e, "err_over_bound_max_softmax": ratio_s,
+                       "err_where_delta0_max": float(ee[exact].max()) if bool(exact.any()) else None}
+                log(f"[quality] {name} a={alpha} {kind} {par}: pages {row['kept_pages_mean']} "
+                    f"recall {row['recall_mean']:.3f} delta ent {row['delta_entmax_mean']:.3e} "
+                    f"sm {row['delta_softmax_mean']:.3e} relerr ent {row['rel_err_entmax_mean']:.3e} "
+                    f"sm {row['rel_err_softmax_mean']:.3e}")
+                rows.append(row)
+            del wfull, supp
+        del inp, meta, box, mu, var, vn, vnb
+        torch.cuda.empty_cache()
+    print(json.dumps({"quality_sweep": rows, "seed": args.seed,
+                      "note": "selection on box/mu/var from score_pages; T = tokens of the kept pages"}),
+          flush=True)
 
 
 SCORE_SOURCES = ("sparse_decode_attention_page_amd/csrc/score.hip", "sparse_decode_attention_page_amd/csrc/common.hpp")

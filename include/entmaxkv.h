@@ -91,7 +91,8 @@ enum entmaxkv_call {
   ENTMAXKV_CALL_GAUSS = 3,
   ENTMAXKV_CALL_DECODE_SPARSE = 4,
   ENTMAXKV_CALL_DECODE_FULL = 5,
-  ENTMAXKV_CALL_SOFTMAX = 6
+  ENTMAXKV_CALL_SOFTMAX = 6,
+  ENTMAXKV_CALL_SOFTMAX_SPARSE = 7
 };
 
 /* Bytes of workspace a call needs for this shape (0 if none).  Returns 0 for
@@ -193,6 +194,26 @@ int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const vo
                             const void *v_pool, const int32_t *page_table,
                             const int32_t *seq_lens, float *out, float *lse, void *ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * softmax_decode_sparse -- softmax attention over the kept pages only: the
+ * comparison of [EntmaxKV s.3] (under one kept set, softmax gives weight to
+ * every discarded token, so its discarded mass is positive, while entmax loses
+ * nothing once the kept set contains its support) and [EntmaxKV s.4]
+ * (discarded mass and relative output error, entmax vs softmax sparse decoding
+ * at equal KV budgets).  Selection contract as entmax_decode_sparse: per query
+ * row, sel_cnt in [0, N_b] and sel_idx[0 .. sel_cnt) ascending logical pages
+ * < N_b; a violation or an out-of-range page-table entry gives NaN in out and
+ * lse.  out: float32 [B][Hq][d] = sum_{t in T} softmax_T(s)_t v_t over the kept
+ * tokens T (t < L_b); lse (nullable, float32 [B][Hq]): log sum_{t in T} exp(s_t),
+ * -inf with out = 0 when T is empty.  fp32 arithmetic (as softmax_decode_full).
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_SOFTMAX_SPARSE).
+ */
+int32_t softmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *page_table,
+                              const int32_t *seq_lens, const int32_t *sel_idx,
+                              const int32_t *sel_cnt, float *out, float *lse, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* The 16-point Gauss-Hermite rule the Gaussian selector uses (host copy, for
  * inspection): nodes ascending, weights for the weight function exp(-x^2). */

@@ -59,7 +59,7 @@ def _load():
                                      ctypes.c_double, vp, vp, ctypes.c_int32, vp, vp, vp]
     lib.orc_entmax_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_double, vp,
                                       ctypes.c_int32, vp, vp, vp]
-    lib.orc_softmax_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp]
+    lib.orc_softmax_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp]
     lib.orc_gauss_mass.restype = ctypes.c_double
     lib.orc_gauss_mass.argtypes = [vp, vp, vp, ctypes.c_int32, ctypes.c_double, ctypes.c_double]
     lib.orc_entmax_tau.restype = ctypes.c_double
@@ -206,15 +206,21 @@ def entmax_decode(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, alpha, 
     return out, tau, w
 
 
-def softmax_decode(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, rows=None):
+def softmax_decode(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, rows=None, sel_idx=None,
+                   sel_cnt=None):
+    """Softmax attention over every cached token, or over the kept pages when a
+    selection (sel_idx [B][Hq][max_pages], sel_cnt [B][Hq]) is given."""
     lib = _load()
     out = np.full((shape.B, shape.Hq, shape.d), np.nan)
     lse = np.full((shape.B, shape.Hq), np.nan)
     r, nr = _rows(rows)
+    si = None if sel_idx is None else np.ascontiguousarray(sel_idx, dtype=np.int32)
+    sc = None if sel_cnt is None else np.ascontiguousarray(sel_cnt, dtype=np.int32)
     sh = shape.c()
     lib.orc_softmax_decode(ctypes.byref(sh), _p(_raw(q, shape)), _p(_raw(k_pool, shape)),
                            _p(_raw(v_pool, shape)), _p(np.ascontiguousarray(page_table, dtype=np.int32)),
-                           _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), _p(r), nr, _p(out), _p(lse))
+                           _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), _p(si), _p(sc), _p(r), nr,
+                           _p(out), _p(lse))
     return out, lse
 
 

@@ -549,10 +549,16 @@ void orc_entmax_decode(const orc_shape *s, const void *q, const void *k_pool, co
 /* ------------------------------------------------------------------------ */
 /* softmax_decode_full -- the full-cache softmax baseline the EntmaxKV summary  */
 /* compares against (section 4, efficiency): exact softmax attention over every  */
-/* cached token, same score scale.                                              */
+/* cached token, same score scale.  With a selection (sel_idx, sel_cnt not NULL) */
+/* the same softmax runs over the kept pages only: the comparison of section 3   */
+/* (under one kept set softmax keeps weight on every discarded token) and of the */
+/* approximation-quality results of section 4.  Selection contract as           */
+/* orc_entmax_decode, plus: a count outside [0, N_b] makes the row NaN; an empty */
+/* kept set gives out = 0 and lse = -inf.                                       */
 /* ------------------------------------------------------------------------ */
 void orc_softmax_decode(const orc_shape *s, const void *q, const void *k_pool, const void *v_pool,
                         const int32_t *page_table, const int32_t *seq_lens,
+                        const int32_t *sel_idx, const int32_t *sel_cnt,
                         const int32_t *rows, int32_t n_rows, double *out, double *lse) {
   const int d = s->d, G = s->Hq / s->Hkv, P = s->P;
   const double c = cscale(s);
@@ -562,32 +568,47 @@ void orc_softmax_decode(const orc_shape *s, const void *q, const void *k_pool, c
     int row = row_at(rows, r), b = row / s->Hq, h = row % s->Hq, g = h / G;
     int32_t L = seq_len(s, seq_lens, b);
     int32_t np = n_pages(s, L);
+    int32_t cnt = sel_idx ? sel_cnt[row] : np;
     double *o = out + (size_t)row * d;
     for (int i = 0; i < d; ++i) o[i] = 0.0;
-    double *S = (double *)malloc(sizeof(double) * (L > 0 ? L : 1));
-    int bad = 0;
-    for (int32_t p = 0; p < np && !bad; ++p) {
+    int bad = cnt < 0 || cnt > np;
+    if (bad) cnt = 0;
+    /* the kept tokens: scores, physical pages and slots, page order */
+    int64_t cap = (int64_t)(cnt > 0 ? cnt : 1) * P;
+    double *S = (double *)malloc(sizeof(double) * cap);
+    int32_t *phs = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int32_t *slot = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int64_t n = 0;
+    int32_t prev = -1;
+    for (int32_t i = 0; i < cnt && !bad; ++i) {
+      int32_t p = sel_idx ? sel_idx[(size_t)row * s->max_pages + i] : i;
+      if (p < 0 || p >= np || p <= prev) { bad = 1; break; }
+      prev = p;
       int32_t phys = page_table[(size_t)b * s->max_pages + p];
       if (phys < 0 || phys >= s->num_phys) { bad = 1; break; }
-      for (int j = 0; j < page_fill(s, L, p); ++j) S[(size_t)p * P + j] = score_of(s, q, k_pool, row, g, phys, j, c);
+      for (int j = 0; j < page_fill(s, L, p); ++j) {
+        S[n] = score_of(s, q, k_pool, row, g, phys, j, c);
+        phs[n] = phys;
+        slot[n] = j;
+        ++n;
+      }
     }
-    if (bad || L == 0) {
+    if (bad || n == 0) {
       if (bad) for (int i = 0; i < d; ++i) o[i] = NAN;
       if (lse) lse[row] = bad ? NAN : -INFINITY;
-      free(S);
+      free(S); free(phs); free(slot);
       continue;
     }
     double m = -INFINITY;
-    for (int32_t t = 0; t < L; ++t) if (S[t] > m) m = S[t];
+    for (int64_t t = 0; t < n; ++t) if (S[t] > m) m = S[t];
     double l = 0.0;
-    for (int32_t t = 0; t < L; ++t) { S[t] = exp(S[t] - m); l += S[t]; }
-    for (int32_t t = 0; t < L; ++t) {
+    for (int64_t t = 0; t < n; ++t) { S[t] = exp(S[t] - m); l += S[t]; }
+    for (int64_t t = 0; t < n; ++t) {
       double p = S[t] / l;
-      int32_t phys = page_table[(size_t)b * s->max_pages + t / P];
-      size_t vbase = ((((size_t)phys * s->Hkv + g) * P) + t % P) * d;
+      size_t vbase = ((((size_t)phs[t] * s->Hkv + g) * P) + slot[t]) * d;
       for (int i = 0; i < d; ++i) o[i] += p * ld(v_pool, s->dtype, vbase + i);
     }
     if (lse) lse[row] = m + log(l);
-    free(S);
+    free(S); free(phs); free(slot);
   }
 }

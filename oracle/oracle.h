@@ -71,6 +71,7 @@ void orc_entmax_decode(const orc_shape *s, const void *q, const void *k_pool, co
 
 void orc_softmax_decode(const orc_shape *s, const void *q, const void *k_pool, const void *v_pool,
                         const int32_t *page_table, const int32_t *seq_lens,
+                        const int32_t *sel_idx, const int32_t *sel_cnt,
                         const int32_t *rows, int32_t n_rows, double *out, double *lse);
 
 /* alpha-entmax threshold of one score vector by bisection (exposed for pins). */

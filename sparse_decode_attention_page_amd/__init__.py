@@ -21,10 +21,11 @@ _lib = None
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX = range(1, 7)
+CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE = \
+    range(1, 8)
 
 EXPORTS = ("build_page_meta", "score_pages", "select_pages_topk", "select_pages_gauss",
-           "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full",
+           "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
            "entmaxkv_stream_read")
 
@@ -72,6 +73,8 @@ def load(path: str | None = None):
     lib.select_pages_gauss.argtypes = [sh, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp, vp, vp, sz, vp]
     lib.entmax_decode_sparse.restype = i32
     lib.entmax_decode_sparse.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
+    lib.softmax_decode_sparse.restype = i32
+    lib.softmax_decode_sparse.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.entmax_decode_full.restype = i32
     lib.entmax_decode_full.argtypes = [sh, vp, vp, vp, vp, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
     lib.softmax_decode_full.restype = i32
@@ -252,6 +255,21 @@ def entmax_decode_full(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, al
                                    _ptr(weights_out, torch.float32, "weights_out"), wp, wn,
                                    _stream(stream))
     _check("entmax_decode_full", st)
+    return out
+
+
+def softmax_decode_sparse(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out,
+                          lse=None, ws=None, stream=None):
+    """Softmax attention over the kept pages (the selection entmax_decode_sparse takes)."""
+    torch = _torch()
+    kd = _kv_dtype(shape)
+    wp, wn, keep = _ws(shape, CALL_SOFTMAX_SPARSE, ws)
+    st = load().softmax_decode_sparse(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
+                                      _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
+                                      _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(sel_idx, torch.int32, "sel_idx"),
+                                      _ptr(sel_cnt, torch.int32, "sel_cnt"), _ptr(out, torch.float32, "out"),
+                                      _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream))
+    _check("softmax_decode_sparse", st)
     return out
 
 

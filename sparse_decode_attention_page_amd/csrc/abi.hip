@@ -166,6 +166,7 @@ size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call)
     case ENTMAXKV_CALL_DECODE_SPARSE: return decode_ws_bytes(D, false);
     case ENTMAXKV_CALL_DECODE_FULL: return full_ws_bytes(D);
     case ENTMAXKV_CALL_SOFTMAX: return softmax_ws_bytes(D);
+    case ENTMAXKV_CALL_SOFTMAX_SPARSE: return softmax_sparse_ws_bytes(D);
   }
   return 0;
 }
@@ -291,6 +292,22 @@ int32_t softmax_decode_full(const entmaxkv_shape *shape, const void *q, const vo
   if (misaligned16(q, k_pool, v_pool)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(softmax_ws_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_softmax(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, out, lse, ws, stream));
+}
+
+int32_t softmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *page_table,
+                              const int32_t *seq_lens, const int32_t *sel_idx,
+                              const int32_t *sel_cnt, float *out, float *lse, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !sel_idx || !sel_cnt || !out)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, k_pool, v_pool)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(softmax_sparse_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_softmax_sparse(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
+                                          sel_cnt, out, lse, ws, stream));
 }
 
 int32_t entmaxkv_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {

@@ -67,6 +67,10 @@ hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const voi
                               double *tau, float *weights_out, void *ws, hipStream_t s);
 
 size_t softmax_ws_bytes(const Dims &D);
+size_t softmax_sparse_ws_bytes(const Dims &D);
+hipError_t launch_softmax_sparse(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *page_table, const int32_t *seq_lens, const int32_t *sel_idx,
+                                 const int32_t *sel_cnt, float *out, float *lse, void *ws, hipStream_t s);
 hipError_t launch_softmax(const Dims &D, int dtype, const void *q, const void *k_pool,
                           const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
                           float *out, float *lse, void *ws, hipStream_t s);

@@ -15,6 +15,14 @@
 //  * the running states are merged across slots (shuffles, then LDS) and written
 //    per range; a small second launch merges the ranges of each query row in
 //    range order.
+//
+// softmax_decode_sparse runs the same softmax over the kept pages of each query
+// row only (the selection entmax_decode_sparse receives), so that entmax and
+// softmax can be compared under one kept set (the summary's discarded-mass
+// argument, section 3).  Selections differ between the query heads of a group,
+// so a block serves one query row; the row's kept pages are dealt round-robin
+// to a fixed number of ranges, so long and short selections both spread over
+// blocks, and the merge launch combines the ranges in range order.
 #include <math.h>
 
 #include "common.hpp"
@@ -288,6 +296,206 @@ hipError_t launch_softmax(const Dims &D, int dtype, const void *q, const void *k
   }
   if (D.d == 64) return launch_sm_p<float, 64>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
   return launch_sm_p<float, 128>(D, q, k_pool, v_pool, page_table, seq_lens, out, lse, w, s);
+}
+
+
+// ------------------------------------------------ softmax over the kept pages
+template <typename T, int DIM, int P>
+__global__ __launch_bounds__(kSThreads) void softmax_sparse_kernel(
+    Dims D, const T *__restrict__ q, const T *__restrict__ k_pool, const T *__restrict__ v_pool,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt, SoftmaxWs ws) {
+  constexpr int kParts = kSThreads / P;
+  constexpr int kPer = DIM / kParts;
+  static_assert(kPer >= 2 && kPer % 2 == 0, "slice must hold bf16 pairs");
+  constexpr int kWords = kPer * (int)sizeof(T) / 4;
+  __shared__ float xch[kSThreads / kWave][kParts][DIM / kParts + 2];
+  const int s = blockIdx.x, row = blockIdx.y;
+  const int b = row / D.Hq, h = row % D.Hq, g = h / D.G;
+  const int tid = threadIdx.x, slot = tid / kParts, part = tid % kParts;
+  const int MP = D.max_pages;
+  const int L = seq_len_clamped(seq_lens, b, D);
+  const int np = n_pages_of(L, P);
+  const int c_raw = sel_cnt[row];
+  bool bad = c_raw < 0 || c_raw > np;  // a count outside [0, N_b] poisons the row
+  const int cnt = bad ? 0 : c_raw;
+  const int32_t *srow = sel_idx + (size_t)row * MP;
+
+  float qv[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) qv[e] = load_f<T>(q, (size_t)row * DIM + part * kPer + e) * (float)D.scale;
+  float m = -INFINITY, l = 0.0f, acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.0f;
+
+  // item i of the row: its page must lie in [0, N_b), above the previous kept
+  // page, with a valid physical page; returns the physical page or -1 (bad)
+  auto item_phys = [&](int i, int &fill) -> int {
+    const int p = srow[i];
+    const int prev = i > 0 ? srow[i - 1] : -1;
+    if (p < 0 || p >= np || p <= prev) return -1;
+    const int ph = page_table[(size_t)b * MP + p];
+    if (ph < 0 || ph >= D.num_phys) return -1;
+    fill = min(P, L - p * P);
+    return ph;
+  };
+  auto slice_ptr = [&](const T *pool, int ph) -> const uint32_t * {
+    return reinterpret_cast<const uint32_t *>(pool + (((size_t)ph * D.Hkv + g) * P + slot) * DIM + part * kPer);
+  };
+
+  uint32_t kw[kWords], vw[kWords];
+  int i = s;
+  int fill = 0;
+  int ph = i < cnt ? item_phys(i, fill) : -1;
+  if (i < cnt && ph < 0) bad = true;
+  bool have = ph >= 0 && slot < fill;
+  if (have) {
+    const uint32_t *kp = slice_ptr(k_pool, ph), *vp = slice_ptr(v_pool, ph);
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) { kw[w] = kp[w]; vw[w] = vp[w]; }
+  }
+  for (; i < cnt; i += gridDim.x) {
+    uint32_t nk[kWords], nv[kWords];
+    const int in = i + gridDim.x;
+    bool have_n = false;
+    if (in < cnt) {
+      int fn = 0;
+      const int phn = item_phys(in, fn);
+      if (phn < 0) bad = true;
+      else if (slot < fn) {
+        have_n = true;
+        const uint32_t *kp = slice_ptr(k_pool, phn), *vp = slice_ptr(v_pool, phn);
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) { nk[w] = kp[w]; nv[w] = vp[w]; }
+      }
+    }
+    if (have) {
+      float kf[kPer], vf[kPer];
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        if constexpr (sizeof(T) == 2) {
+          kf[2 * w] = bf16lo(kw[w]); kf[2 * w + 1] = bf16hi(kw[w]);
+          vf[2 * w] = bf16lo(vw[w]); vf[2 * w + 1] = bf16hi(vw[w]);
+        } else {
+          kf[w] = __uint_as_float(kw[w]);
+          vf[w] = __uint_as_float(vw[w]);
+        }
+      }
+      float sc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) sc = __builtin_fmaf(qv[e], kf[e], sc);
+#pragma unroll
+      for (int o = kParts / 2; o > 0; o >>= 1) sc += __shfl_xor(sc, o, kWave);
+      if (sc > m) {
+        const float r = __expf(m - sc);
+        l *= r;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[e] *= r;
+        m = sc;
+      }
+      const float pw = __expf(sc - m);
+      l += pw;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] = __builtin_fmaf(pw, vf[e], acc[e]);
+    }
+    have = have_n;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) { kw[w] = nk[w]; vw[w] = nv[w]; }
+  }
+
+  // merge the slots: within the wave (same part), then across waves through LDS
+#pragma unroll
+  for (int o = kParts; o < kWave; o <<= 1) {
+    const float mo = __shfl_xor(m, o, kWave), lo = __shfl_xor(l, o, kWave);
+    const float mn = fmaxf(m, mo);
+    const float ra = mn == -INFINITY ? 0.0f : __expf(m - mn);
+    const float rb = mn == -INFINITY ? 0.0f : __expf(mo - mn);
+    l = l * ra + lo * rb;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const float ao = __shfl_xor(acc[e], o, kWave);
+      acc[e] = acc[e] * ra + ao * rb;
+    }
+    m = mn;
+  }
+  const int wave = tid / kWave, lane = tid % kWave;
+  if (lane < kParts) {
+    xch[wave][part][0] = m;
+    xch[wave][part][1] = l;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) xch[wave][part][2 + e] = acc[e];
+  }
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  constexpr int kNW = kSThreads / kWave;
+  float *rec = ws.part + ((size_t)row * ws.S + s) * (DIM + 2);
+  for (int idx = tid; idx < DIM; idx += kSThreads) {
+    const int pr = idx / kPer, e = idx % kPer;
+    float mm = -INFINITY;
+    for (int w = 0; w < kNW; ++w) mm = fmaxf(mm, xch[w][pr][0]);
+    float ll = 0.0f, aa = 0.0f;
+    for (int w = 0; w < kNW; ++w) {
+      const float r = mm == -INFINITY ? 0.0f : __expf(xch[w][pr][0] - mm);
+      ll += xch[w][pr][1] * r;
+      aa += xch[w][pr][2 + e] * r;
+    }
+    rec[2 + idx] = aa;
+    if (idx == 0) { rec[0] = mm; rec[1] = any_bad ? NAN : ll; }
+  }
+}
+
+static SoftmaxWs carve_softmax_sparse(const Dims &D, void *base, size_t *bytes) {
+  SoftmaxWs w;
+  const int rows = D.B * D.Hq;
+  int S = (2048 + rows - 1) / rows;  // about 2048 blocks
+  if (S > 64) S = 64;
+  if (S > D.max_pages) S = D.max_pages;
+  if (S < 1) S = 1;
+  w.S = S;
+  w.pps = 0;  // ranges take every S-th kept page
+  Carve cv(base);
+  w.part = cv.take<float>((size_t)rows * S * (D.d + 2));
+  if (bytes) *bytes = cv.bytes();
+  return w;
+}
+
+size_t softmax_sparse_ws_bytes(const Dims &D) {
+  size_t b = 0;
+  carve_softmax_sparse(D, nullptr, &b);
+  return b;
+}
+
+template <typename T, int DIM, int P>
+static hipError_t launch_sms(const Dims &D, const void *q, const void *k, const void *v, const int32_t *pt,
+                             const int32_t *sl, const int32_t *si, const int32_t *sc, float *out, float *lse,
+                             SoftmaxWs w, hipStream_t s) {
+  hipLaunchKernelGGL((softmax_sparse_kernel<T, DIM, P>), dim3(w.S, D.B * D.Hq), dim3(kSThreads), 0, s, D,
+                     (const T *)q, (const T *)k, (const T *)v, pt, sl, si, sc, w);
+  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(DIM), 0, s, D, w, out, lse);
+  return hipGetLastError();
+}
+
+template <typename T, int DIM>
+static hipError_t launch_sms_p(const Dims &D, const void *q, const void *k, const void *v, const int32_t *pt,
+                               const int32_t *sl, const int32_t *si, const int32_t *sc, float *out, float *lse,
+                               SoftmaxWs w, hipStream_t s) {
+  switch (D.P) {
+    case 16: return launch_sms<T, DIM, 16>(D, q, k, v, pt, sl, si, sc, out, lse, w, s);
+    case 32: return launch_sms<T, DIM, 32>(D, q, k, v, pt, sl, si, sc, out, lse, w, s);
+    case 64: return launch_sms<T, DIM, 64>(D, q, k, v, pt, sl, si, sc, out, lse, w, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_softmax_sparse(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *page_table, const int32_t *seq_lens, const int32_t *sel_idx,
+                                 const int32_t *sel_cnt, float *out, float *lse, void *ws, hipStream_t s) {
+  SoftmaxWs w = carve_softmax_sparse(D, ws, nullptr);
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64) return launch_sms_p<uint16_t, 64>(D, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, lse, w, s);
+    return launch_sms_p<uint16_t, 128>(D, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, lse, w, s);
+  }
+  if (D.d == 64) return launch_sms_p<float, 64>(D, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, lse, w, s);
+  return launch_sms_p<float, 128>(D, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, lse, w, s);
 }
 
 }  // namespace ekv

@@ -9,8 +9,9 @@ The EntmaxKV summary ("Resumen Tecnico: EntmaxKV ...", gist.science/es/paper/
 2605.21649, section 4) evaluates on long-context retrieval/LM suites and on
 efficiency runs up to 1M tokens; none of those inputs exist here.  These
 workloads stand in for them: Gaussian keys with planted "needle" tokens whose
-key points along the query (k = 4 q/|q| + N(0, 0.1^2) per coordinate), at the
-context lengths the summary reports.
+key points along the query (k = g q/|q| + N(0, 0.1^2) per coordinate, g = 4), at
+the context lengths the summary reports.  The "_passage" variants plant runs of
+16 such tokens with g = 8 instead: short passages that stand out of the bulk.
 """
 from __future__ import annotations
 
@@ -39,6 +40,8 @@ class Workload:
     topk: int = 0
     delta: float = 0.5
     policy: str = "gauss"      # "gauss" | "topk" | "mixed" (even b top-k, odd b Gaussian)
+    needle_gain: float = 4.0   # planted key = needle_gain * q/|q| + noise (score ~ needle_gain)
+    needle_run: int = 1        # consecutive planted tokens per item (a short passage when > 1)
     extra: dict = field(default_factory=dict)
 
 
@@ -61,6 +64,15 @@ WORKLOADS = {
                                shuffle_pages=True, alphas=(1.5,), topk=128, delta=0.5,
                                policy="mixed"),
 }
+# the same shapes with planted passages: runs of 16 consecutive tokens whose
+# keys point along the query, scoring ~8 against a bulk maximum of ~5 at 1M
+# tokens (the few relevant passages a retrieval query attends to)
+WORKLOADS["gqa_128k_passage"] = Workload("gqa_128k_passage", 1, 32, 8, 64, 32, "bf16", (131072,),
+                                         planted_per_kv=64, planted_layout="even", alphas=(1.5, 2.0),
+                                         topk=64, delta=0.5, policy="both", needle_gain=8.0, needle_run=16)
+WORKLOADS["long_1m_passage"] = Workload("long_1m_passage", 1, 32, 8, 64, 64, "bf16", (1048576,),
+                                        planted_per_kv=32, alphas=(1.5,), topk=64, delta=0.5,
+                                        policy="gauss", needle_gain=8.0, needle_run=16)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -165,12 +177,13 @@ def make(wl: Workload | str, seed: int = 0, ctx_override=None, shuffle=None) -> 
                     pos = ((np.arange(n) + 0.5) * L / n).astype(np.int64)
                 else:
                     pos = np.sort(rng.choice(L, size=n, replace=False))
-                for j, t in enumerate(pos):
+                for j, t0 in enumerate(pos):
                     h = g * G + (j % G)
                     qv = qs[b, h]
-                    noise = rng.standard_normal(d, dtype=np.float32) * np.float32(0.1)
-                    kf[t] = (4.0 * qv / np.linalg.norm(qv)).astype(np.float32) + noise
-                    plist.append((g, h, int(t)))
+                    for t in range(int(t0), min(int(t0) + wl.needle_run, L)):
+                        noise = rng.standard_normal(d, dtype=np.float32) * np.float32(0.1)
+                        kf[t] = (float(wl.needle_gain) * qv / np.linalg.norm(qv)).astype(np.float32) + noise
+                        plist.append((g, h, int(t)))
             if L < nb * P:  # slots past the end of the sequence stay zero
                 kf[L:] = 0.0
                 vf[L:] = 0.0
@@ -293,10 +306,13 @@ def make_device(wl: Workload | str, seed: int = 0, ctx_override=None, device="cu
                     pos = torch.sort(torch.randperm(L, generator=hgen)[:n]).values
                 hs = torch.tensor([g * G + (j % G) for j in range(n)], device=device)
                 qv = qs[b, hs]                                           # [n, d]
-                dirs = (4.0 * qv / torch.linalg.norm(qv, dim=1, keepdim=True)).to(torch.float32)
-                noise = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32) * 0.1
-                kf[pos.to(device)] = dirs + noise
-                plist += [(g, int(hs[j]), int(pos[j])) for j in range(n)]
+                dirs = (float(wl.needle_gain) * qv / torch.linalg.norm(qv, dim=1, keepdim=True)).to(torch.float32)
+                for o in range(wl.needle_run):
+                    noise = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32) * 0.1
+                    tt = pos + o
+                    ok = tt < L
+                    kf[tt[ok].to(device)] = (dirs + noise)[ok.to(device)]
+                    plist += [(g, int(hs[j]), int(tt[j])) for j in range(n) if bool(ok[j])]
             if L < nb * P:
                 kf[L:] = 0.0
                 vf[L:] = 0.0

@@ -154,3 +154,20 @@ def test_full_softmax_sampled_rows(full):
                                    rows=rows)
     assert rel_l2_rows(_take_rows(out.cpu().numpy(), rows), _take_rows(oo, rows)) <= TOL[inp.dtype]
     assert np.allclose(lse.cpu().numpy().reshape(-1)[rows], lo.reshape(-1)[rows], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("policy", ["gauss", "topk"])
+def test_full_softmax_sparse_sampled_rows(full, policy):
+    """Softmax over the kept pages of the GPU's own selection, against the oracle
+    on the same selection (sampled rows)."""
+    t = torch()
+    inp, h, rows = full["inp"], full["host"], full["rows"]
+    sel, cnt, _ = _select(full, policy)
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, device="cuda")
+    lse = t.full((inp.B, inp.Hq), np.nan, device="cuda")
+    E.softmax_decode_sparse(full["shape"], inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, sel, cnt,
+                            out, lse=lse)
+    oo, lo = oracle.softmax_decode(full["osh"], h["q"], h["k_pool"], h["v_pool"], h["page_table"], h["seq_lens"],
+                                   rows=rows, sel_idx=sel.cpu().numpy(), sel_cnt=cnt.cpu().numpy())
+    assert rel_l2_rows(_take_rows(out.cpu().numpy(), rows), _take_rows(oo, rows)) <= TOL[inp.dtype]
+    assert np.allclose(lse.cpu().numpy().reshape(-1)[rows], lo.reshape(-1)[rows], rtol=1e-5, atol=1e-5)

@@ -1,0 +1,178 @@
+"""HIP-graph capture of the decode step: every replay against the same calls made
+eagerly.
+
+Two graphs on a 8,192-token, 32/8-head, bf16 slice with pages of 16:
+
+* the decode step (score_pages -> select_pages_gauss / select_pages_topk ->
+  entmax_decode_sparse) captured once; before each of four replays the query
+  is overwritten eagerly, and the replay's page sets, counts and outputs are
+  compared with an eager run on the same query;
+* the streaming step of the EntmaxKV summary (section 2, pages' metadata kept
+  up to date as they fill): append one token's K and V to its page, rebuild
+  that page's metadata from the new token on, then score, select and decode
+  with the context one token longer.  Four replays grow the context by four
+  tokens; a copy driven eagerly takes the same steps, and metadata, sets and
+  outputs must agree after every replay.
+
+Page sets and counts must match bit for bit, metadata too; outputs within
+1e-6 relative L2 (the selection's histogram sums use atomics, so the order of
+floating-point additions may differ between runs, never the decisions).
+"""
+import numpy as np
+import pytest
+
+import sparse_decode_attention_page_amd as E
+from sparse_decode_attention_page_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+CTX = 8192
+
+
+def _inputs(seed):
+    import torch
+    wl = synth.WORKLOADS["gqa_32k"]
+    inp = synth.make_device(wl, seed, ctx_override=CTX)
+    shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+    meta = torch.zeros((inp.num_phys, inp.Hkv, 4, inp.d), dtype=inp.k_pool.dtype, device="cuda")
+    E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta)
+    torch.cuda.synchronize()
+    return wl, inp, shape, meta
+
+
+class _Step:
+    """Static buffers and one decode step over them."""
+
+    def __init__(self, shape, inp, policy, alpha, delta, k):
+        import torch
+        B, Hq, MP, d = inp.B, inp.Hq, inp.max_pages, inp.d
+        self.shape, self.policy, self.alpha, self.delta, self.k = shape, policy, alpha, delta, k
+        self.box = torch.empty((B, Hq, MP), device="cuda")
+        self.mu, self.var = torch.empty_like(self.box), torch.empty_like(self.box)
+        self.sel = torch.full((B, Hq, MP), -7, dtype=torch.int32, device="cuda")
+        self.cnt = torch.full((B, Hq), -7, dtype=torch.int32, device="cuda")
+        self.out = torch.full((B, Hq, d), float("nan"), device="cuda")
+        self.ws_s = E.workspace(shape, E.CALL_SCORE)
+        self.ws_g = E.workspace(shape, E.CALL_GAUSS)
+        self.ws_t = E.workspace(shape, E.CALL_TOPK)
+        self.ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE)
+
+    def __call__(self, q, k_pool, v_pool, meta, pt, sl):
+        E.score_pages(self.shape, q, meta, pt, sl, self.box, self.mu, self.var, ws=self.ws_s)
+        if self.policy == "gauss":
+            E.select_pages_gauss(self.shape, self.box, self.mu, self.var, sl, self.alpha, self.delta,
+                                 self.sel, self.cnt, ws=self.ws_g)
+        else:
+            E.select_pages_topk(self.shape, self.box, sl, self.k, self.sel, self.cnt, ws=self.ws_t)
+        E.entmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
+                               self.out, ws=self.ws_d)
+
+
+def _capture(fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def _same_sets(a, b, tag):
+    import torch
+    assert torch.equal(a.cnt, b.cnt), f"{tag}: sel_cnt differs"
+    MP = a.sel.shape[-1]
+    inside = torch.arange(MP, device="cuda")[None, None, :] < a.cnt[:, :, None]
+    assert torch.equal(torch.where(inside, a.sel, -1), torch.where(inside, b.sel, -1)), f"{tag}: sel_idx differs"
+
+
+def _close(x, y, tag, tol=1e-6):
+    import torch
+    assert bool(torch.isfinite(x).all()), f"{tag}: non-finite output"
+    num = torch.linalg.vector_norm((x - y).double())
+    den = torch.linalg.vector_norm(y.double()).clamp(min=1e-30)
+    assert float(num / den) <= tol, f"{tag}: relative L2 {float(num / den):.3e}"
+
+
+@pytest.mark.parametrize("policy", ["gauss", "topk"])
+def test_graph_replays_match_eager_step(policy):
+    import torch
+    wl, inp, shape, meta = _inputs(11)
+    alpha = wl.alphas[0]
+    q_static = inp.q.clone()
+    gstep = _Step(shape, inp, policy, alpha, wl.delta, 16)
+    estep = _Step(shape, inp, policy, alpha, wl.delta, 16)
+    gstep(q_static, inp.k_pool, inp.v_pool, meta, inp.page_table, inp.seq_lens)  # warm
+    torch.cuda.synchronize()
+    g = _capture(lambda: gstep(q_static, inp.k_pool, inp.v_pool, meta, inp.page_table, inp.seq_lens))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    for r in range(4):
+        qn = torch.randn(inp.q.shape, generator=gen, device="cuda").to(inp.q.dtype)
+        q_static.copy_(qn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        estep(qn, inp.k_pool, inp.v_pool, meta, inp.page_table, inp.seq_lens)
+        torch.cuda.synchronize()
+        tag = f"{policy} replay {r}"
+        _same_sets(gstep, estep, tag)
+        _close(gstep.out, estep.out, tag)
+
+
+def test_graph_streaming_step_matches_eager():
+    import torch
+    wl, inp, shape, meta = _inputs(12)
+    alpha, P = wl.alphas[0], inp.P
+    n_steps = 4
+    ptl = inp.page_table.long()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    knew = torch.randn((inp.B, inp.Hkv, inp.d), generator=gen, device="cuda").to(inp.k_pool.dtype)
+    vnew = torch.randn((inp.B, inp.Hkv, inp.d), generator=gen, device="cuda").to(inp.v_pool.dtype)
+
+    class Stream:
+        def __init__(self):
+            self.k = inp.k_pool.clone()
+            self.v = inp.v_pool.clone()
+            self.meta = meta.clone()
+            self.seq = (inp.seq_lens - (n_steps + 1)).to(torch.int32)
+            self.step = _Step(shape, inp, "gauss", alpha, wl.delta, 16)
+
+        def __call__(self):
+            self.seq.add_(1)
+            pos = (self.seq - 1).long()
+            ph = torch.gather(ptl, 1, (pos // P).unsqueeze(1)).squeeze(1)
+            slot = pos % P
+            self.k[ph, :, slot, :] = knew
+            self.v[ph, :, slot, :] = vnew
+            E.build_page_meta(shape, self.k, inp.page_table, self.seq, self.meta, from_token=self.seq - 1)
+            self.step(inp.q, self.k, self.v, self.meta, inp.page_table, self.seq)
+
+    gs, es = Stream(), Stream()
+    gs()  # warm: first token
+    es()
+    torch.cuda.synchronize()
+    g = _capture(gs)
+    for r in range(n_steps - 1):
+        g.replay()
+        torch.cuda.synchronize()
+        es()
+        torch.cuda.synchronize()
+        tag = f"streaming replay {r}"
+        assert torch.equal(gs.seq, es.seq), f"{tag}: context length differs"
+        assert torch.equal(gs.k, es.k) and torch.equal(gs.v, es.v), f"{tag}: K/V pools differ"
+        assert torch.equal(gs.meta.view(torch.int16), es.meta.view(torch.int16)), f"{tag}: metadata differs"
+        _same_sets(gs.step, es.step, tag)
+        _close(gs.step.out, es.step.out, tag)
+    # after the last replay the context is back at its full length: the
+    # appended metadata equals a full rebuild over the final pools
+    assert int(gs.seq[0]) == int(inp.seq_lens[0]) - 1
+    full = torch.zeros_like(gs.meta)
+    E.build_page_meta(shape, gs.k, inp.page_table, gs.seq, full)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), gs.meta.view(torch.int16)), "appended metadata != full rebuild"
+    np.testing.assert_array_equal(gs.seq.cpu().numpy(), es.seq.cpu().numpy())

@@ -138,3 +138,60 @@ def test_softmax_decode_full(case):
     oo, lo = oracle.softmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens)
     assert rel_l2_rows(out.cpu().numpy(), oo) <= TOL[inp.dtype]
     assert np.allclose(lse.cpu().numpy(), lo, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("policy", ["topk", "gauss"])
+def test_softmax_decode_sparse(case, policy):
+    """Softmax over the oracle's own selection of each case."""
+    inp, D, _, (box_o, mu_o, var_o) = case
+    t = torch()
+    if policy == "topk":
+        so, co = oracle.select_topk(D.oshape, box_o, inp.seq_lens, 7)
+    else:
+        so, co, _ = oracle.select_gauss(D.oshape, box_o, mu_o, var_o, inp.seq_lens, 1.5, 0.5)
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
+    lse = t.full((inp.B, inp.Hq), np.nan, dtype=t.float32, device="cuda")
+    E.softmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(so).cuda(), t.from_numpy(co).cuda(),
+                            out, lse=lse)
+    oo, lo = oracle.softmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                   sel_idx=so, sel_cnt=co)
+    assert rel_l2_rows(out.cpu().numpy(), oo) <= TOL[inp.dtype]
+    assert np.allclose(lse.cpu().numpy(), lo, rtol=1e-5, atol=1e-5)
+
+
+def test_softmax_decode_sparse_edge_cases(case):
+    """Bad selections give NaN rows, an empty one zeros and lse = -inf, as in the oracle."""
+    inp, D, _, _ = case
+    t = torch()
+    MP = inp.max_pages
+    so = np.zeros((inp.B, inp.Hq, MP), np.int32)
+    co = np.zeros((inp.B, inp.Hq), np.int32)
+    rows = inp.B * inp.Hq
+    flat_s, flat_c = so.reshape(rows, MP), co.reshape(rows)
+    for r in range(rows):
+        b = r // inp.Hq
+        np_b = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        kind = r % 4
+        if kind == 0:      # empty
+            flat_c[r] = 0
+        elif kind == 1:    # count above N_b
+            flat_c[r] = np_b + 1
+            flat_s[r, :np_b + 1 if np_b + 1 <= MP else MP] = np.arange(min(np_b + 1, MP))
+        elif kind == 2 and np_b >= 2:  # not ascending
+            flat_c[r] = 2
+            flat_s[r, :2] = [1, 0]
+        else:              # every page
+            flat_c[r] = np_b
+            flat_s[r, :np_b] = np.arange(np_b)
+    out = t.full((inp.B, inp.Hq, inp.d), 7.0, dtype=t.float32, device="cuda")
+    lse = t.full((inp.B, inp.Hq), 7.0, dtype=t.float32, device="cuda")
+    E.softmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(so).cuda(), t.from_numpy(co).cuda(),
+                            out, lse=lse)
+    oo, lo = oracle.softmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                   sel_idx=so, sel_cnt=co)
+    og, lg = out.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(np.isnan(og), np.isnan(oo)) and np.array_equal(np.isnan(lg), np.isnan(lo))
+    fin = ~np.isnan(lo)
+    assert np.array_equal(np.isinf(lg[fin]), np.isinf(lo[fin]))
+    ok = ~np.isnan(oo).any(axis=-1)
+    assert rel_l2_rows(og[ok][None], oo[ok][None]) <= TOL[inp.dtype] if ok.any() else True

@@ -494,6 +494,77 @@ def test_softmax_vs_scipy(orc):
             assert abs(lse[b, h] - scipy.special.logsumexp(s)) < 1e-12
 
 
+def _some_selection(inp, seed, keep_frac=0.3):
+    """A seeded selection: ascending kept pages per row, at least one page."""
+    rng = np.random.default_rng(seed)
+    sel = np.zeros((inp.B, inp.Hq, inp.max_pages), np.int32)
+    cnt = np.zeros((inp.B, inp.Hq), np.int32)
+    for b in range(inp.B):
+        np_b = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        for h in range(inp.Hq):
+            k = max(1, int(keep_frac * np_b))
+            pages = np.sort(rng.choice(np_b, size=k, replace=False))
+            sel[b, h, :k] = pages
+            cnt[b, h] = k
+    return sel, cnt
+
+
+def test_softmax_over_selection_vs_scipy(orc):
+    """Softmax over the kept pages only: scipy's softmax / logsumexp of the kept
+    tokens' scores, the identity 1 - exp(lse_T - lse_full) = softmax mass of the
+    discarded tokens (the discarded-mass notion of section 3), and a full
+    selection reproducing the full-cache result."""
+    inp, sh = _decode_inputs(orc, seed=16, dtype="f32")
+    sel, cnt = _some_selection(inp, 16)
+    out, lse = orc.softmax_decode(sh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                  sel_idx=sel, sel_cnt=cnt)
+    out_f, lse_f = orc.softmax_decode(sh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens)
+    G = inp.Hq // inp.Hkv
+    for b in range(inp.B):
+        L = int(inp.seq_lens[b])
+        for h in range(inp.Hq):
+            kept = sel[b, h, :cnt[b, h]]
+            s = np.concatenate([_token_scores(inp, b, h, p) for p in kept])
+            V = np.concatenate([f64(inp.v_pool[inp.page_table[b, p], h // G, :min(16, L - p * 16)], "f32")
+                                for p in kept])
+            assert np.allclose(out[b, h], scipy.special.softmax(s) @ V, atol=1e-12)
+            assert abs(lse[b, h] - scipy.special.logsumexp(s)) < 1e-12
+            s_all = np.concatenate([_token_scores(inp, b, h, p) for p in range((L + 15) // 16)])
+            p_all = scipy.special.softmax(s_all)
+            dropped = np.ones(len(s_all), bool)
+            for p in kept:
+                dropped[p * 16:min(L, (p + 1) * 16)] = False
+            assert abs((1.0 - math.exp(lse[b, h] - lse_f[b, h])) - p_all[dropped].sum()) < 1e-12
+    # every page kept: the full-cache softmax
+    full_sel = np.zeros_like(sel)
+    full_cnt = np.zeros_like(cnt)
+    for b in range(inp.B):
+        np_b = (int(inp.seq_lens[b]) + 15) // 16
+        full_sel[b, :, :np_b] = np.arange(np_b)
+        full_cnt[b, :] = np_b
+    out_a, lse_a = orc.softmax_decode(sh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                      sel_idx=full_sel, sel_cnt=full_cnt)
+    assert np.array_equal(out_a, out_f) and np.array_equal(lse_a, lse_f)
+
+
+def test_softmax_selection_edge_cases(orc):
+    inp, sh = _decode_inputs(orc, seed=17)
+    sel = np.zeros((inp.B, inp.Hq, inp.max_pages), np.int32)
+    cnt = np.zeros((inp.B, inp.Hq), np.int32)
+    cnt[0, 0] = 2
+    sel[0, 0, :2] = [3, 1]           # not ascending -> NaN
+    cnt[0, 1] = -1                   # negative count -> NaN
+    cnt[1, 0] = 0                    # empty -> zeros, lse = -inf
+    cnt[1, 1] = 1
+    sel[1, 1, 0] = 10 ** 6           # page beyond N_b -> NaN
+    out, lse = orc.softmax_decode(sh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                  rows=[0, 1, 4, 5], sel_idx=sel, sel_cnt=cnt)
+    assert np.all(np.isnan(out[0, 0])) and np.isnan(lse[0, 0])
+    assert np.all(np.isnan(out[0, 1])) and np.isnan(lse[0, 1])
+    assert np.all(out[1, 0] == 0.0) and lse[1, 0] == -np.inf
+    assert np.all(np.isnan(out[1, 1])) and np.isnan(lse[1, 1])
+
+
 def test_tiny_workload_end_to_end(orc):
     """The 4k-token fp32 workload: both selectors run and the sparse result obeys section 3."""
     inp = synth.make("tiny_4k", 0)
