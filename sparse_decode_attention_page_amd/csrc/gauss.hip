@@ -466,21 +466,45 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
         if (est > best || (est == best && p < bestp)) { best = est; bestp = p; }
       }
     }
+    // In-bin points take slots from one counter per row.  When many pages
+    // share their statistics (a flat score distribution) thousands of points
+    // fall into the root bin, so the slots are claimed per wave: one atomic
+    // for the wave's points at a node, lane offsets from the ballot masks.
 #pragma unroll 1
     for (int j = 15; j >= 0; --j) {
       const double xj = gc.x[j], wj = gc.w[j];
       bool any = false;
+      bool in[4];
+      double vin[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        in[u] = false;
+        vin[u] = 0.0;
         if (!act[u]) continue;
         const double v = gh_point(gp.a, mm[u], sg[u], xj);
         const int bn = v > lo ? bin_of(v, lo, iw) : -1;
         if (bn < k) { act[u] = false; continue; }
         any = true;
-        if (bn == k) {
-          const int slot = atomicAdd(&ws.inbin_cnt[rc.row], 1);
-          if (slot < gp.cap) {
-            st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0], v);
+        in[u] = bn == k;
+        vin[u] = v;
+      }
+      int off[4], wave_tot = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const unsigned long long m = __ballot(in[u]);
+        off[u] = wave_tot + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        wave_tot += __popcll(m);
+      }
+      if (wave_tot > 0) {  // wave-uniform
+        int slot0 = 0;
+        if ((threadIdx.x & (kWave - 1)) == 0) slot0 = atomicAdd(&ws.inbin_cnt[rc.row], wave_tot);
+        slot0 = __shfl(slot0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int slot = slot0 + off[u];
+          if (in[u] && slot < gp.cap) {
+            st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 0], vin[u]);
             st_agent(&ws.inbin[((size_t)rc.row * gp.cap + slot) * 2 + 1], nn[u] * wj);
           }
         }
