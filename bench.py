@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -52,6 +53,9 @@ def parse():
                     help="approximation quality vs KV budget on every synthetic workload (recall of the "
                          "full-cache entmax support, discarded mass and relative output error of entmax and "
                          "softmax under the same kept pages); one JSON line, then exit")
+    ap.add_argument("--oracle-1t", action="store_true",
+                    help="time the oracle's step on the tiny and 32k workloads (CPU only; run with "
+                         "OMP_NUM_THREADS=1 by the CPU-baseline leg), print one JSON line, then exit")
     ap.add_argument("--only", default="", choices=["", "score", "step", "copy"],
                     help="profiling aid: run only score_pages, only the step, or a plain 1 GiB device copy "
                          "(the calibration of the HBM byte counters), then exit")
@@ -60,6 +64,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.oracle_1t:
+        print(json.dumps(oracle_small_steps()), flush=True)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus N > 1 is not supported",
                           "n_gpus": args.gpus}))
@@ -745,8 +752,56 @@ def cpu_baseline(inp, shape, wl, alpha, policy):
               f"{reps} run(s) averaged ({total:.1f}s of work)"
               + (f", scaled x{scale:g}" if scale != 1 else ""))
     log(f"[bench] cpu baseline: {dt * scale * 1e3:.1f} ms/step ({sample}, {threads} threads)")
-    return {"value": round(dt * scale * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
-            "sample": sample}
+    res = {"value": round(dt * scale * 1e6, 1), "unit": "us/step", "cores": threads, "kind": "oracle",
+           "sample": sample, "cpu_model": cpu_model()}
+    # one thread on the two small workloads, in a child process that never touches the GPU
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-1t"],
+                           env=dict(os.environ, OMP_NUM_THREADS="1"), capture_output=True, text=True,
+                           timeout=300)
+        res["single_thread_us_per_step"] = json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:  # reported, never fatal
+        res["single_thread_us_per_step"] = {"error": str(e)[:200]}
+    log(f"[bench] oracle, one thread: {res['single_thread_us_per_step']}")
+    return res
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_small_steps():
+    """The oracle's step (score + Gaussian selection + sparse decode, every query
+    row) on the 4k-token and 32k-token workloads, repeated to about a second of
+    work each; us per step."""
+    import oracle
+    from sparse_decode_attention_page_amd import synth
+
+    out = {}
+    for name in ("tiny_4k", "gqa_32k"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make(wl, 0)
+        osh = oracle.Shape(inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages, inp.num_phys, inp.dtype)
+        meta = oracle.build_page_meta(osh, inp.k_pool, inp.page_table, inp.seq_lens)
+        alpha = wl.alphas[0]
+        n, total = 0, 0.0
+        while total < 1.0 and n < 1000:
+            t1 = time.perf_counter()
+            box, mu, var = oracle.score_pages(osh, inp.q, meta, inp.page_table, inp.seq_lens)
+            sel, cnt, _ = oracle.select_gauss(osh, box, mu, var, inp.seq_lens, alpha, wl.delta)
+            oracle.entmax_decode(osh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, alpha,
+                                 sel, cnt)
+            total += time.perf_counter() - t1
+            n += 1
+        out[name] = round(total / n * 1e6, 1)
+    return out
 
 
 if __name__ == "__main__":
