@@ -132,6 +132,29 @@ int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta
                     float *var, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Compact metadata -- the records above with the Gaussian moments stored in
+ * 8 bits, a variant the summary leaves open ([EntmaxKV s.2.A] only asks for
+ * "lightweight" per-page statistics).  bf16 keys only (ENTMAXKV_ERR_UNSUPPORTED
+ * otherwise).  Record [num_phys][Hkv] of 6d bytes:
+ *   k_min bf16[d] | k_max bf16[d] | mean e4m3[d] | var e4m3[d]
+ * e4m3 = OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities; 0x7F / 0xFF are NaN; largest finite value 448).
+ * build_page_meta_f8: k_min / k_max exactly as build_page_meta; mean and var
+ * (fp64, as there) rounded to the nearest E4M3 value, ties to even, magnitudes
+ * >= 448 saturating to +-448.  from_token as in build_page_meta.
+ * score_pages_f8: score_pages over compact records, with the same outputs,
+ * fp64 sums of exact products and roundings (a NaN code gives NaN mu / var);
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_SCORE).
+ * meta must be 16-byte aligned; 6d is a multiple of 16 for d in {64, 128}.
+ */
+int32_t build_page_meta_f8(const entmaxkv_shape *shape, const void *k_pool,
+                           const int32_t *page_table, const int32_t *seq_lens,
+                           const int32_t *from_token, void *meta, hipStream_t stream);
+int32_t score_pages_f8(const entmaxkv_shape *shape, const void *q, const void *meta,
+                       const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                       float *var, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * select_pages_topk -- [EntmaxKV s.2.B, policy 1]: per (b, h), the k pages with
  * the largest box; ties go to the lower page index, NaN ranks below every
  * number, -0 equals +0, and N_b <= k keeps every page.  sel_idx lists the

@@ -53,7 +53,13 @@ def _load():
     lib.orc_round_f32_up.argtypes = [ctypes.c_double]
     lib.orc_gauss_hermite16.argtypes = [vp, vp]
     lib.orc_build_page_meta.argtypes = [vp] * 6
+    lib.orc_build_page_meta_f8.argtypes = [vp] * 6
     lib.orc_score_pages.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp]
+    lib.orc_score_pages_f8.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp]
+    lib.orc_e4m3_decode.restype = ctypes.c_double
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
     lib.orc_select_topk.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp]
     lib.orc_select_gauss.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, vp, vp, ctypes.c_int32, vp, vp, vp]
@@ -122,6 +128,16 @@ def round_f32_up(x: float) -> float:
     return _load().orc_round_f32_up(float(x))
 
 
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code (0..255)."""
+    return _load().orc_e4m3_decode(int(code) & 0xFF)
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest E4M3 code (ties to even, saturating at +-448, NaN -> 0x7F)."""
+    return int(_load().orc_e4m3_encode(float(x)))
+
+
 def gauss_hermite16():
     x = np.zeros(16)
     w = np.zeros(16)
@@ -141,6 +157,43 @@ def build_page_meta(shape: Shape, k_pool, page_table, seq_lens, from_token=None,
     sh = shape.c()
     lib.orc_build_page_meta(ctypes.byref(sh), _p(k_pool), _p(pt), _p(sl), _p(ft), _p(meta))
     return meta
+
+
+def build_page_meta_f8(shape: Shape, k_pool, page_table, seq_lens, from_token=None, meta=None):
+    """Compact records (bf16 keys): uint8 [num_phys][Hkv][6d] holding k_min and
+    k_max as bf16 and the mean and variance as E4M3."""
+    assert shape.dtype == "bf16", "compact metadata is defined for bf16 keys"
+    lib = _load()
+    k_pool = _raw(k_pool, shape)
+    if meta is None:
+        meta = np.zeros((shape.num_phys, shape.Hkv, 6 * shape.d), dtype=np.uint8)
+    meta = np.ascontiguousarray(meta)
+    assert meta.dtype == np.uint8 and meta.nbytes == shape.num_phys * shape.Hkv * 6 * shape.d
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    ft = None if from_token is None else np.ascontiguousarray(from_token, dtype=np.int32)
+    sh = shape.c()
+    lib.orc_build_page_meta_f8(ctypes.byref(sh), _p(k_pool), _p(pt), _p(sl), _p(ft), _p(meta))
+    return meta
+
+
+def score_pages_f8(shape: Shape, q, meta, page_table, seq_lens, rows=None):
+    """score_pages over compact records."""
+    lib = _load()
+    n = shape.B * shape.Hq * shape.max_pages
+    box = np.full(n, np.nan, np.float32)
+    mu = np.full(n, np.nan, np.float32)
+    var = np.full(n, np.nan, np.float32)
+    r, nr = _rows(rows)
+    m = np.ascontiguousarray(meta)
+    assert m.dtype == np.uint8
+    sh = shape.c()
+    lib.orc_score_pages_f8(ctypes.byref(sh), _p(_raw(q, shape)), _p(m),
+                           _p(np.ascontiguousarray(page_table, dtype=np.int32)),
+                           _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), _p(r), nr,
+                           _p(box), _p(mu), _p(var))
+    s3 = (shape.B, shape.Hq, shape.max_pages)
+    return box.reshape(s3), mu.reshape(s3), var.reshape(s3)
 
 
 def score_pages(shape: Shape, q, meta, page_table, seq_lens, rows=None):

@@ -47,6 +47,38 @@ double orc_round_bf16(double x) {
   return y;
 }
 
+/* OCP 8-bit floating point, E4M3 ("FN": no infinities).  Code = s eeee mmm,
+ * exponent bias 7: e = 0 gives the subnormals m/8 * 2^-6, otherwise
+ * (1 + m/8) * 2^(e-7); e = 15, m = 7 is NaN, so the largest finite value is
+ * 448.  This is the format of the compact metadata's mean and variance. */
+double orc_e4m3_decode(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* Nearest E4M3 code to x, ties to the even code (mantissa bit 0 clear),
+ * magnitudes beyond the largest finite value saturate to +-448, NaN gives the
+ * NaN code.  Done by binary search over the 127 non-negative finite codes,
+ * whose values increase with the code. */
+uint8_t orc_e4m3_encode(double x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t sgn = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(sgn | 0x7E);
+  int lo = 0, hi = 0x7E; /* decode(lo) <= a < decode(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (orc_e4m3_decode((uint8_t)mid) <= a) lo = mid; else hi = mid;
+  }
+  double dl = a - orc_e4m3_decode((uint8_t)lo), dh = orc_e4m3_decode((uint8_t)hi) - a;
+  int c = (dl < dh) ? lo : (dh < dl) ? hi : ((lo & 1) == 0 ? lo : hi);
+  return (uint8_t)(sgn | c);
+}
+
 static void store_val(void *p, int dtype, size_t i, double x) {
   if (dtype == 0) {
     ((float *)p)[i] = (float)x; /* RNE */
@@ -172,8 +204,11 @@ void orc_gauss_hermite16(double *nodes, double *weights) {
 /* the filled slots, var = max(0, S2/n - mean^2) from fp64 sums, each stored    */
 /* value rounded once to the metadata dtype.                                    */
 /* ------------------------------------------------------------------------ */
-void orc_build_page_meta(const orc_shape *s, const void *k_pool, const int32_t *page_table,
-                         const int32_t *seq_lens, const int32_t *from_token, void *meta) {
+/* Compact records (fmt 1, bf16 keys only): k_min and k_max as above, mean and */
+/* var each rounded once to E4M3 (nearest, ties to even, saturating), record   */
+/* = k_min bf16[d] | k_max bf16[d] | mean e4m3[d] | var e4m3[d] (6d bytes).    */
+static void build_meta(const orc_shape *s, const void *k_pool, const int32_t *page_table,
+                       const int32_t *seq_lens, const int32_t *from_token, void *meta, int fmt) {
   const int d = s->d, P = s->P, Hkv = s->Hkv;
   for (int b = 0; b < s->B; ++b) {
     int32_t L = seq_len(s, seq_lens, b);
@@ -203,14 +238,32 @@ void orc_build_page_meta(const orc_shape *s, const void *k_pool, const int32_t *
           double mean = s1 / n;
           double var = s2 / n - mean * mean;
           if (!(var > 0.0)) var = 0.0;
-          store_val(meta, s->dtype, mbase + 0 * d + i, kmin);
-          store_val(meta, s->dtype, mbase + 1 * d + i, kmax);
-          store_val(meta, s->dtype, mbase + 2 * d + i, mean);
-          store_val(meta, s->dtype, mbase + 3 * d + i, var);
+          if (fmt == 0) {
+            store_val(meta, s->dtype, mbase + 0 * d + i, kmin);
+            store_val(meta, s->dtype, mbase + 1 * d + i, kmax);
+            store_val(meta, s->dtype, mbase + 2 * d + i, mean);
+            store_val(meta, s->dtype, mbase + 3 * d + i, var);
+          } else {
+            uint8_t *rec = (uint8_t *)meta + ((size_t)phys * Hkv + g) * (size_t)(6 * d);
+            store_val(rec, 1, (size_t)i, kmin);
+            store_val(rec, 1, (size_t)d + i, kmax);
+            rec[4 * d + i] = orc_e4m3_encode(mean);
+            rec[5 * d + i] = orc_e4m3_encode(var);
+          }
         }
       }
     }
   }
+}
+
+void orc_build_page_meta(const orc_shape *s, const void *k_pool, const int32_t *page_table,
+                         const int32_t *seq_lens, const int32_t *from_token, void *meta) {
+  build_meta(s, k_pool, page_table, seq_lens, from_token, meta, 0);
+}
+
+void orc_build_page_meta_f8(const orc_shape *s, const void *k_pool, const int32_t *page_table,
+                            const int32_t *seq_lens, const int32_t *from_token, void *meta) {
+  build_meta(s, k_pool, page_table, seq_lens, from_token, meta, 1);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -225,9 +278,21 @@ static int row_count(const orc_shape *s, const int32_t *rows, int32_t n_rows) {
 }
 static int row_at(const int32_t *rows, int i) { return rows ? rows[i] : i; }
 
-void orc_score_pages(const orc_shape *s, const void *q, const void *meta,
-                     const int32_t *page_table, const int32_t *seq_lens,
-                     const int32_t *rows, int32_t n_rows, float *box, float *mu, float *var) {
+/* Compact records: the stored mean and variance are E4M3 values, decoded      */
+/* exactly; the products with q (bf16) remain exact in fp64.                    */
+static double meta_at(const orc_shape *s, const void *meta, int32_t phys, int g, int kind, int i,
+                      int fmt) {
+  const int d = s->d;
+  if (fmt == 0) return ld(meta, s->dtype, (((size_t)phys * s->Hkv + g) * 4 + kind) * d + i);
+  const uint8_t *rec = (const uint8_t *)meta + ((size_t)phys * s->Hkv + g) * (size_t)(6 * d);
+  if (kind < 2) return ld(rec, 1, (size_t)kind * d + i);
+  return orc_e4m3_decode(rec[(size_t)(4 + (kind - 2)) * d + i]);
+}
+
+static void score_pages(const orc_shape *s, const void *q, const void *meta,
+                        const int32_t *page_table, const int32_t *seq_lens,
+                        const int32_t *rows, int32_t n_rows, float *box, float *mu, float *var,
+                        int fmt) {
   const int d = s->d, G = s->Hq / s->Hkv;
   const double c = cscale(s);
   const double c2 = c * c;
@@ -244,21 +309,32 @@ void orc_score_pages(const orc_shape *s, const void *q, const void *meta,
         box[o] = NAN; mu[o] = NAN; var[o] = NAN;
         continue;
       }
-      size_t mbase = (((size_t)phys * s->Hkv + g) * 4) * d;
       double sb = 0.0, sm = 0.0, sv = 0.0;
       for (int i = 0; i < d; ++i) {
         double qi = ld(q, s->dtype, (size_t)row * d + i);
-        double a = qi * ld(meta, s->dtype, mbase + 0 * d + i);
-        double bb = qi * ld(meta, s->dtype, mbase + 1 * d + i);
+        double a = qi * meta_at(s, meta, phys, g, 0, i, fmt);
+        double bb = qi * meta_at(s, meta, phys, g, 1, i, fmt);
         sb += (a > bb ? a : bb);
-        sm += qi * ld(meta, s->dtype, mbase + 2 * d + i);
-        sv += (qi * qi) * ld(meta, s->dtype, mbase + 3 * d + i);
+        sm += qi * meta_at(s, meta, phys, g, 2, i, fmt);
+        sv += (qi * qi) * meta_at(s, meta, phys, g, 3, i, fmt);
       }
       box[o] = (float)orc_round_f32_up(c * sb);
       mu[o] = (float)(c * sm);
       var[o] = (float)(c2 * sv);
     }
   }
+}
+
+void orc_score_pages(const orc_shape *s, const void *q, const void *meta,
+                     const int32_t *page_table, const int32_t *seq_lens,
+                     const int32_t *rows, int32_t n_rows, float *box, float *mu, float *var) {
+  score_pages(s, q, meta, page_table, seq_lens, rows, n_rows, box, mu, var, 0);
+}
+
+void orc_score_pages_f8(const orc_shape *s, const void *q, const void *meta,
+                        const int32_t *page_table, const int32_t *seq_lens,
+                        const int32_t *rows, int32_t n_rows, float *box, float *mu, float *var) {
+  score_pages(s, q, meta, page_table, seq_lens, rows, n_rows, box, mu, var, 1);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -35,12 +35,20 @@ typedef struct {
 double orc_round_bf16(double x);   /* round-to-nearest-even to bfloat16 */
 double orc_round_f32(double x);    /* round-to-nearest-even to float32 */
 double orc_round_f32_up(double x); /* round toward +infinity to float32 */
+/* OCP FP8 E4M3 (no infinities, NaN = 0x7F/0xFF, largest finite 448): exact
+ * decode; encode = nearest, ties to even, saturating at +-448. */
+double orc_e4m3_decode(uint8_t c);
+uint8_t orc_e4m3_encode(double x);
 
 /* 16-point Gauss-Hermite rule (weight exp(-x^2)) by Golub-Welsch. */
 void orc_gauss_hermite16(double *nodes, double *weights);
 
 void orc_build_page_meta(const orc_shape *s, const void *k_pool, const int32_t *page_table,
                          const int32_t *seq_lens, const int32_t *from_token, void *meta);
+/* compact records for bf16 keys: [num_phys][Hkv] of
+ * k_min bf16[d] | k_max bf16[d] | mean e4m3[d] | var e4m3[d]  (6d bytes) */
+void orc_build_page_meta_f8(const orc_shape *s, const void *k_pool, const int32_t *page_table,
+                            const int32_t *seq_lens, const int32_t *from_token, void *meta);
 
 /* rows: optional list of (b*Hq+h) rows to compute (NULL = all).  Outputs are
  * float32 arrays; entries of rows not listed and pages >= N_b are untouched. */
@@ -48,6 +56,11 @@ void orc_score_pages(const orc_shape *s, const void *q, const void *meta,
                      const int32_t *page_table, const int32_t *seq_lens,
                      const int32_t *rows, int32_t n_rows,
                      float *box, float *mu, float *var);
+/* the same scores from compact records */
+void orc_score_pages_f8(const orc_shape *s, const void *q, const void *meta,
+                        const int32_t *page_table, const int32_t *seq_lens,
+                        const int32_t *rows, int32_t n_rows,
+                        float *box, float *mu, float *var);
 
 void orc_select_topk(const orc_shape *s, const float *box, const int32_t *seq_lens, int32_t k,
                      const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,

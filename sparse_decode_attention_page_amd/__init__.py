@@ -24,7 +24,8 @@ F32, BF16 = 0, 1
 CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE = \
     range(1, 8)
 
-EXPORTS = ("build_page_meta", "score_pages", "select_pages_topk", "select_pages_gauss",
+EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_f8",
+           "select_pages_topk", "select_pages_gauss",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
            "entmaxkv_stream_read")
@@ -67,6 +68,10 @@ def load(path: str | None = None):
     lib.build_page_meta.argtypes = [sh, vp, vp, vp, vp, vp, vp]
     lib.score_pages.restype = i32
     lib.score_pages.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.build_page_meta_f8.restype = i32
+    lib.build_page_meta_f8.argtypes = [sh, vp, vp, vp, vp, vp, vp]
+    lib.score_pages_f8.restype = i32
+    lib.score_pages_f8.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.select_pages_topk.restype = i32
     lib.select_pages_topk.argtypes = [sh, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.select_pages_gauss.restype = i32
@@ -183,6 +188,45 @@ def build_page_meta(shape: Shape, k_pool, page_table, seq_lens, meta, from_token
                                 _stream(stream))
     _check("build_page_meta", st)
     return meta
+
+
+def meta_f8_empty(shape: Shape):
+    """A zeroed compact-metadata tensor: uint8 [num_phys, Hkv, 6d]."""
+    torch = _torch()
+    return torch.zeros((shape.num_phys_pages, shape.n_kv_heads, 6 * shape.head_dim), dtype=torch.uint8,
+                       device="cuda")
+
+
+def _meta_f8(shape: Shape, meta):
+    torch = _torch()
+    need = shape.num_phys_pages * shape.n_kv_heads * 6 * shape.head_dim
+    if meta.numel() * meta.element_size() < need:
+        raise ValueError(f"compact metadata needs {need} bytes")
+    return _ptr(meta, torch.uint8, "meta")
+
+
+def build_page_meta_f8(shape: Shape, k_pool, page_table, seq_lens, meta, from_token=None, stream=None):
+    """Compact records: k_min / k_max bf16, mean / var OCP FP8 E4M3 (uint8 meta)."""
+    torch = _torch()
+    st = load().build_page_meta_f8(ctypes.byref(shape), _ptr(k_pool, _kv_dtype(shape), "k_pool"),
+                                   _ptr(page_table, torch.int32, "page_table"),
+                                   _ptr(seq_lens, torch.int32, "seq_lens"),
+                                   _ptr(from_token, torch.int32, "from_token"), _meta_f8(shape, meta),
+                                   _stream(stream))
+    _check("build_page_meta_f8", st)
+    return meta
+
+
+def score_pages_f8(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=None, stream=None):
+    torch = _torch()
+    wp, wn, keep = _ws(shape, CALL_SCORE, ws)
+    st = load().score_pages_f8(ctypes.byref(shape), _ptr(q, _kv_dtype(shape), "q"), _meta_f8(shape, meta),
+                               _ptr(page_table, torch.int32, "page_table"),
+                               _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(box, torch.float32, "box"),
+                               _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"), wp, wn,
+                               _stream(stream))
+    _check("score_pages_f8", st)
+    return box, mu, var
 
 
 def score_pages(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=None, stream=None):

@@ -198,7 +198,19 @@ int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const i
   if (st) return st;
   if (!k_pool || !page_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (misaligned16(k_pool, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_build_meta(D, shape->dtype, k_pool, page_table, seq_lens, from_token, meta, stream));
+  return hip_status(launch_build_meta(D, shape->dtype, false, k_pool, page_table, seq_lens, from_token, meta, stream));
+}
+
+int32_t build_page_meta_f8(const entmaxkv_shape *shape, const void *k_pool, const int32_t *page_table,
+                           const int32_t *seq_lens, const int32_t *from_token, void *meta,
+                           hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (shape->dtype != ENTMAXKV_BF16) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (!k_pool || !page_table || !seq_lens || !meta) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(k_pool, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_build_meta(D, shape->dtype, true, k_pool, page_table, seq_lens, from_token, meta, stream));
 }
 
 int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta,
@@ -210,7 +222,20 @@ int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta
   if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (misaligned16(q, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(score_ws_bytes(D), ws, ws_bytes))) return st;
-  return hip_status(launch_score(D, shape->dtype, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
+  return hip_status(launch_score(D, shape->dtype, false, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
+}
+
+int32_t score_pages_f8(const entmaxkv_shape *shape, const void *q, const void *meta,
+                       const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                       float *var, void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (shape->dtype != ENTMAXKV_BF16) return ENTMAXKV_ERR_UNSUPPORTED;
+  if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(score_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_score(D, shape->dtype, true, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
 }
 
 int32_t select_pages_topk(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,

@@ -34,12 +34,12 @@ const GaussConsts &gauss_consts();
 // per-launch epoch for arrival counters that may hold garbage (1 .. 2^40-1)
 unsigned long long next_epoch();
 
-hipError_t launch_build_meta(const Dims &D, int dtype, const void *k_pool, const int32_t *page_table,
+hipError_t launch_build_meta(const Dims &D, int dtype, bool f8, const void *k_pool, const int32_t *page_table,
                              const int32_t *seq_lens, const int32_t *from_token, void *meta,
                              hipStream_t s);
 
 size_t score_ws_bytes(const Dims &D);
-hipError_t launch_score(const Dims &D, int dtype, const void *q, const void *meta,
+hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const void *meta,
                         const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                         float *var, void *ws, hipStream_t s);
 

@@ -9,17 +9,39 @@
 // record: threads own a pair of coordinates and a stride of token slots, fold
 // min/max in fp32 (exact) and S1 = sum k, S2 = sum k^2 in fp64 (exact for bf16
 // keys), then a fixed-order tree over the token groups finishes the record.
+//
+// Compact records (bf16 keys): k_min bf16[d] | k_max bf16[d] | mean e4m3[d] |
+// var e4m3[d], 6d bytes -- the same statistics with the Gaussian moments in
+// OCP FP8 E4M3 (a quarter fewer bytes for the scorer to stream).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ekv {
 
-template <typename T>
+// fp64 -> OCP FP8 E4M3 (bias 7, no infinities, largest finite 448): nearest,
+// ties to even, magnitudes >= 448 saturate, NaN -> 0x7F.  The quantum is
+// 2^(E-3) in the binade [2^E, 2^(E+1)) and 2^-9 below 2^-6; codes increase with
+// the value, so code = 8(E + 7) + (r - 8) for the rounded significand r in
+// [8, 16] (r = 16 moves to the next binade) and code = r in the subnormals.
+__device__ inline uint8_t f64_to_e4m3(double x) {
+  if (x != x) return 0x7F;
+  const unsigned sg = __signbit(x) ? 0x80u : 0u;
+  const double a = fabs(x);
+  if (a >= 448.0) return (uint8_t)(sg | 0x7Eu);
+  if (a == 0.0) return (uint8_t)sg;
+  const int E = ilogb(a);
+  const int qe = E < -6 ? -9 : E - 3;
+  const int r = (int)rint(ldexp(a, -qe));
+  const int code = qe == -9 ? r : 8 * (E + 7) + (r - 8);
+  return (uint8_t)(sg | (unsigned)min(code, 0x7E));
+}
+
+template <typename T, bool F8>
 __global__ __launch_bounds__(256) void build_meta_kernel(Dims D, const T *__restrict__ k_pool,
                                                          const int32_t *__restrict__ page_table,
                                                          const int32_t *__restrict__ seq_lens,
                                                          const int32_t *__restrict__ from_token,
-                                                         T *__restrict__ meta) {
+                                                         void *__restrict__ meta) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int b = blockIdx.y, g = blockIdx.z;
   const int d = D.d, P = D.P;
@@ -80,17 +102,25 @@ __global__ __launch_bounds__(256) void build_meta_kernel(Dims D, const T *__rest
       const double mean = s1 / (double)n;
       double var = s2 / (double)n - mean * mean;
       if (!(var > 0.0)) var = 0.0;
-      T *rec = meta + ((size_t)phys * D.Hkv + g) * 4 * (size_t)d;
-      store_rne<T>(rec, 0 * d + i, (double)mn);
-      store_rne<T>(rec, 1 * d + i, (double)mx);
-      store_rne<T>(rec, 2 * d + i, mean);
-      store_rne<T>(rec, 3 * d + i, var);
+      if constexpr (F8) {
+        unsigned char *rec = reinterpret_cast<unsigned char *>(meta) + ((size_t)phys * D.Hkv + g) * 6 * (size_t)d;
+        store_rne<T>(reinterpret_cast<T *>(rec), 0 * d + i, (double)mn);
+        store_rne<T>(reinterpret_cast<T *>(rec), 1 * d + i, (double)mx);
+        rec[4 * d + i] = f64_to_e4m3(mean);
+        rec[5 * d + i] = f64_to_e4m3(var);
+      } else {
+        T *rec = reinterpret_cast<T *>(meta) + ((size_t)phys * D.Hkv + g) * 4 * (size_t)d;
+        store_rne<T>(rec, 0 * d + i, (double)mn);
+        store_rne<T>(rec, 1 * d + i, (double)mx);
+        store_rne<T>(rec, 2 * d + i, mean);
+        store_rne<T>(rec, 3 * d + i, var);
+      }
     }
     __syncthreads();
   }
 }
 
-hipError_t launch_build_meta(const Dims &D, int dtype, const void *k_pool, const int32_t *page_table,
+hipError_t launch_build_meta(const Dims &D, int dtype, bool f8, const void *k_pool, const int32_t *page_table,
                              const int32_t *seq_lens, const int32_t *from_token, void *meta,
                              hipStream_t s) {
   const int threads = 256;
@@ -99,12 +129,17 @@ hipError_t launch_build_meta(const Dims &D, int dtype, const void *k_pool, const
   // bulk: one block per page; append: a few blocks walk the rebuilt pages
   const int gx = from_token ? 4 : (D.max_pages < 65535 ? D.max_pages : 65535);
   dim3 grid(gx, D.B, D.Hkv);
-  if (dtype == ENTMAXKV_BF16)
-    hipLaunchKernelGGL(build_meta_kernel<uint16_t>, grid, dim3(threads), smem, s, D,
-                       (const uint16_t *)k_pool, page_table, seq_lens, from_token, (uint16_t *)meta);
+  if (dtype == ENTMAXKV_BF16 && f8)
+    hipLaunchKernelGGL((build_meta_kernel<uint16_t, true>), grid, dim3(threads), smem, s, D,
+                       (const uint16_t *)k_pool, page_table, seq_lens, from_token, meta);
+  else if (dtype == ENTMAXKV_BF16)
+    hipLaunchKernelGGL((build_meta_kernel<uint16_t, false>), grid, dim3(threads), smem, s, D,
+                       (const uint16_t *)k_pool, page_table, seq_lens, from_token, meta);
+  else if (!f8)
+    hipLaunchKernelGGL((build_meta_kernel<float, false>), grid, dim3(threads), smem, s, D,
+                       (const float *)k_pool, page_table, seq_lens, from_token, meta);
   else
-    hipLaunchKernelGGL(build_meta_kernel<float>, grid, dim3(threads), smem, s, D,
-                       (const float *)k_pool, page_table, seq_lens, from_token, (float *)meta);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -63,11 +63,24 @@ struct Chunk<float> {
   }
 };
 
-template <typename T, int DIM, int G>
+// OCP FP8 E4M3 code -> fp64, exact: the code's exponent and mantissa bits set
+// at the top of an fp64 give 2^(e - 1023) (1 + m/8) (a subnormal when e = 0,
+// m/8 2^-1022); scaling by 2^1016 turns the bias into the format's 7.  The
+// codes 0x7F / 0xFF are NaN.
+__device__ __forceinline__ double e4m3_to_f64(unsigned c) {
+  const unsigned hi = ((c & 0x7Fu) << 17) | ((c & 0x80u) << 24);
+  const double v = __hiloint2double((int)hi, 0) * 0x1p1016;
+  return (c & 0x7Fu) == 0x7Fu ? __builtin_nan("") : v;
+}
+
+// F8: compact records (bf16 k_min | k_max, then E4M3 mean | var: 6 DIM bytes)
+template <typename T, int DIM, int G, bool F8>
 struct ScoreCfg {
+  static_assert(!F8 || sizeof(T) == 2, "compact records hold bf16 bounds");
   static constexpr int kE = Chunk<T>::kElems;          // elements per 16-byte chunk
-  static constexpr int kRowChunks = DIM / kE;          // chunks per metadata row
-  static constexpr int kRecBytes = 4 * DIM * (int)sizeof(T);
+  static constexpr int kRowChunks = DIM / kE;          // chunks per (box) metadata row
+  static constexpr int kF8Chunks = DIM / 16;           // chunks per E4M3 row
+  static constexpr int kRecBytes = F8 ? 6 * DIM : 4 * DIM * (int)sizeof(T);
   static constexpr int kTileBytes = kTilePages * kRecBytes;
   static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
   // the second tile is requested once the first is in LDS: with both in flight from
@@ -83,10 +96,10 @@ struct ScoreCfg {
 // Tile loads: thread t fetches 16-byte chunks u*256 + t of the tile (a wave
 // instruction covers 1 KB of consecutive records); missing pages read record 0
 // and are masked later.
-template <typename T, int DIM, int G, int L>
+template <typename T, int DIM, int G, bool F8, int L>
 __device__ __forceinline__ void score_load_tile(u32x4 (&r)[L], const char *mbase, const int *phys, int g, int hkv,
                                                 int tid) {
-  using C = ScoreCfg<T, DIM, G>;
+  using C = ScoreCfg<T, DIM, G, F8>;
 #pragma unroll
   for (int u = 0; u < L; ++u) {
     const int off = (u * kScoreThreads + tid) * 16;
@@ -96,9 +109,9 @@ __device__ __forceinline__ void score_load_tile(u32x4 (&r)[L], const char *mbase
   }
 }
 // ... and into LDS, chunk pos of record rec at slot pos ^ (rec & 7)
-template <typename T, int DIM, int G, int L>
+template <typename T, int DIM, int G, bool F8, int L>
 __device__ __forceinline__ void score_stash_tile(const u32x4 (&r)[L], unsigned char *buf, int tid) {
-  using C = ScoreCfg<T, DIM, G>;
+  using C = ScoreCfg<T, DIM, G, F8>;
 #pragma unroll
   for (int u = 0; u < L; ++u) {
     const int off = (u * kScoreThreads + tid) * 16;
@@ -107,13 +120,13 @@ __device__ __forceinline__ void score_stash_tile(const u32x4 (&r)[L], unsigned c
   }
 }
 
-template <typename T, int DIM, int G>
-__global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G>::kBlocksPerCu)) void score_pages_kernel(
+template <typename T, int DIM, int G, bool F8>
+__global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPerCu)) void score_pages_kernel(
     Dims D, int tiles_per_row, int n_cu, const T *__restrict__ q, const T *__restrict__ meta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, double *__restrict__ coef_w,
     const double *__restrict__ coef_r, float *__restrict__ box, float *__restrict__ mu,
     float *__restrict__ var) {
-  using C = ScoreCfg<T, DIM, G>;
+  using C = ScoreCfg<T, DIM, G, F8>;
   constexpr int kE = C::kE;
   constexpr int kGH = G > 1 ? G / 2 : 1;  // box heads finished by each of waves 0 and 1
   __shared__ __align__(16) unsigned char tile[C::kTileBytes];
@@ -201,10 +214,10 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G>::kBlocksPerCu))
     for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[i * 16];
   }
   u32x4 ring0[C::kLoads], ring1[C::kLoads];
-  score_load_tile<T, DIM, G>(ring0, mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
+  score_load_tile<T, DIM, G, F8>(ring0, mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
   if (C::kBothTiles) {
     const int l1 = min(1, nt - 1);
-    score_load_tile<T, DIM, G>(ring1, mbase, s_phys[l1], ((t_begin + l1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+    score_load_tile<T, DIM, G, F8>(ring1, mbase, s_phys[l1], ((t_begin + l1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
   }
 
   const double c = D.scale, c2 = D.scale * D.scale;
@@ -220,11 +233,11 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G>::kBlocksPerCu))
   for (int lt = 0; lt < kScoreTiles; ++lt) {
     if (lt < nt) {
       if (lt > 0) lds_barrier();  // the previous tile and exchange are fully read
-      if (lt == 0) score_stash_tile<T, DIM, G>(ring0, tile, tid);
-      else score_stash_tile<T, DIM, G>(ring1, tile, tid);
+      if (lt == 0) score_stash_tile<T, DIM, G, F8>(ring0, tile, tid);
+      else score_stash_tile<T, DIM, G, F8>(ring1, tile, tid);
       asm volatile("" ::: "memory");
       if (!C::kBothTiles && lt == 0 && nt > 1)
-        score_load_tile<T, DIM, G>(ring1, mbase, s_phys[1], ((t_begin + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+        score_load_tile<T, DIM, G, F8>(ring1, mbase, s_phys[1], ((t_begin + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
       lds_barrier();
       if (lt == 0) asm volatile("" ::"s"(warm));
       if (lt == 0) EKV_MARK(0, 2);
@@ -235,19 +248,37 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G>::kBlocksPerCu))
       double acc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) acc[h] = 0.0;
+      if (!F8 || wave < 2) {
 #pragma unroll 2
-      for (int ch = 0; ch < C::kRowChunks; ++ch) {
-        double x[kE];
-        Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
+        for (int ch = 0; ch < C::kRowChunks; ++ch) {
+          double x[kE];
+          Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
 #pragma unroll
-        for (int e = 0; e < kE; ++e) {
-          const double *ci = cf + (size_t)(ch * kE + e) * G;
+          for (int e = 0; e < kE; ++e) {
+            const double *ci = cf + (size_t)(ch * kE + e) * G;
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            if constexpr (sizeof(T) == 2)
-              acc[h] = __builtin_fma(ci[h], x[e], acc[h]);  // exact product: fused == separate
-            else
-              acc[h] = acc[h] + ci[h] * x[e];               // fp32 keys: round the product first
+            for (int h = 0; h < G; ++h) {
+              if constexpr (sizeof(T) == 2)
+                acc[h] = __builtin_fma(ci[h], x[e], acc[h]);  // exact product: fused == separate
+              else
+                acc[h] = acc[h] + ci[h] * x[e];               // fp32 keys: round the product first
+            }
+          }
+        }
+      } else {
+        // E4M3 mean / variance rows: 16 elements per chunk; q (bf16) times an
+        // E4M3 value has 12 significant bits, q^2 times one 20: exact in fp64
+        const int base = 2 * C::kRowChunks + (wave - 2) * C::kF8Chunks;
+#pragma unroll 2
+        for (int ch = 0; ch < C::kF8Chunks; ++ch) {
+          const uint4 v = *reinterpret_cast<const uint4 *>(rec + ((base + ch) ^ sw) * 16);
+          const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const double xe = e4m3_to_f64((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+            const double *ci = cf + (size_t)(ch * 16 + e) * G;
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = __builtin_fma(ci[h], xe, acc[h]);
           }
         }
       }
@@ -327,7 +358,7 @@ static int device_cu_count() {
   return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-template <typename T, int DIM, int G>
+template <typename T, int DIM, int G, bool F8>
 static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
                                  const int32_t *page_table, const int32_t *seq_lens, float *box,
                                  float *mu, float *var, void *ws, hipStream_t s) {
@@ -338,34 +369,39 @@ static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
   const long long grid = (n_tiles + kScoreTiles - 1) / kScoreTiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s, D,
+  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G, F8>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s, D,
                      tiles_per_row, device_cu_count(), (const T *)q, (const T *)meta, page_table, seq_lens, coef,
                      (const double *)coef, box, mu, var);
   return hipGetLastError();
 }
 
-template <typename T, int DIM>
+template <typename T, int DIM, bool F8>
 static hipError_t launch_score_d(const Dims &D, const void *q, const void *meta,
                                  const int32_t *pt, const int32_t *sl, float *box, float *mu,
                                  float *var, void *ws, hipStream_t s) {
   switch (D.G) {
-    case 1: return launch_score_t<T, DIM, 1>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 2: return launch_score_t<T, DIM, 2>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 4: return launch_score_t<T, DIM, 4>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 8: return launch_score_t<T, DIM, 8>(D, q, meta, pt, sl, box, mu, var, ws, s);
+    case 1: return launch_score_t<T, DIM, 1, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
+    case 2: return launch_score_t<T, DIM, 2, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
+    case 4: return launch_score_t<T, DIM, 4, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
+    case 8: return launch_score_t<T, DIM, 8, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_score(const Dims &D, int dtype, const void *q, const void *meta,
+hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const void *meta,
                         const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                         float *var, void *ws, hipStream_t s) {
-  if (dtype == ENTMAXKV_BF16) {
-    if (D.d == 64) return launch_score_d<uint16_t, 64>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
-    return launch_score_d<uint16_t, 128>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+  if (dtype == ENTMAXKV_BF16 && f8) {
+    if (D.d == 64) return launch_score_d<uint16_t, 64, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+    return launch_score_d<uint16_t, 128, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
   }
-  if (D.d == 64) return launch_score_d<float, 64>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
-  return launch_score_d<float, 128>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+  if (f8) return hipErrorInvalidValue;
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64) return launch_score_d<uint16_t, 64, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+    return launch_score_d<uint16_t, 128, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+  }
+  if (D.d == 64) return launch_score_d<float, 64, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+  return launch_score_d<float, 128, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
 }
 
 EKV_TRACE_DUMP(ekv_trace_dump_score)

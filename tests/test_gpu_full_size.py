@@ -84,6 +84,39 @@ def test_full_score_sampled_rows(full):
             assert (ulp == 0).mean() > 0.999, f"row {r}: too many 1-ulp differences"
 
 
+def test_full_meta_and_score_f8_sampled(full):
+    """Compact records (E4M3 mean / variance) at full size: metadata of the
+    sampled sequences bit-exact, scores of the sampled rows within one ulp."""
+    inp, h, rows = full["inp"], full["host"], full["rows"]
+    if inp.dtype != "bf16":
+        pytest.skip("compact metadata holds bf16 bounds")
+    t = torch()
+    m8 = E.meta_f8_empty(full["shape"])
+    E.build_page_meta_f8(full["shape"], inp.k_pool, inp.page_table, inp.seq_lens, m8)
+    B, Hq, MP = inp.B, inp.Hq, inp.max_pages
+    box = t.full((B, Hq, MP), np.nan, device="cuda")
+    mu, var = t.full_like(box, np.nan), t.full_like(box, np.nan)
+    E.score_pages_f8(full["shape"], inp.q, m8, inp.page_table, inp.seq_lens, box, mu, var)
+    got_meta = m8.cpu().numpy()
+    bs = sorted({r // inp.Hq for r in rows})
+    sl = np.zeros_like(h["seq_lens"])
+    sl[bs] = h["seq_lens"][bs]
+    want = oracle.build_page_meta_f8(full["osh"], h["k_pool"], h["page_table"], sl)
+    for b in bs:
+        npg = (int(h["seq_lens"][b]) + inp.P - 1) // inp.P
+        phys = h["page_table"][b, :npg]
+        assert np.array_equal(got_meta[phys], want[phys]), f"compact metadata of sequence {b} differs"
+    bo, mo, vo = oracle.score_pages_f8(full["osh"], h["q"], got_meta, h["page_table"], h["seq_lens"], rows=rows)
+    for got, wnt in ((box, bo), (mu, mo), (var, vo)):
+        g = _take_rows(got.cpu().numpy(), rows)
+        w = _take_rows(wnt, rows)
+        for i, r in enumerate(rows):
+            npg = (int(h["seq_lens"][r // inp.Hq]) + inp.P - 1) // inp.P
+            ulp = np.abs(g[i, :npg].view(np.int32).astype(np.int64) - w[i, :npg].view(np.int32).astype(np.int64))
+            assert ulp.max() <= 1, f"row {r}: compact score differs by {ulp.max()} ulp"
+            assert (ulp == 0).mean() > 0.999
+
+
 def _select(full, policy):
     t = torch()
     inp, wl = full["inp"], full["wl"]

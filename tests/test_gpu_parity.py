@@ -79,6 +79,51 @@ def test_score_pages(case):
         assert np.all(np.isnan(g[~m]))  # pages past N_b untouched
 
 
+def test_build_page_meta_f8(case):
+    inp, D, _, _ = case
+    t = torch()
+    if inp.dtype != "bf16":
+        with pytest.raises(E.EntmaxKVError, match="status 2"):
+            E.build_page_meta_f8(D.shape, D.k, D.pt, D.sl, E.meta_f8_empty(D.shape))
+        return
+    meta = E.meta_f8_empty(D.shape)
+    E.build_page_meta_f8(D.shape, D.k, D.pt, D.sl, meta)
+    want = oracle.build_page_meta_f8(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens)
+    assert np.array_equal(meta.cpu().numpy(), want)
+    # append path: only the pages holding each sequence's newest token
+    from_tok = np.maximum(inp.seq_lens - 1, 0).astype(np.int32)
+    meta2 = E.meta_f8_empty(D.shape)
+    E.build_page_meta_f8(D.shape, D.k, D.pt, D.sl, meta2, from_token=t.from_numpy(from_tok).cuda())
+    want2 = oracle.build_page_meta_f8(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens, from_token=from_tok,
+                                      meta=np.zeros_like(want))
+    assert np.array_equal(meta2.cpu().numpy(), want2)
+
+
+def test_score_pages_f8_and_gauss(case):
+    inp, D, _, _ = case
+    if inp.dtype != "bf16":
+        with pytest.raises(E.EntmaxKVError, match="status 2"):
+            E.score_pages_f8(D.shape, D.q, E.meta_f8_empty(D.shape), D.pt, D.sl, D.per_page(), D.per_page(),
+                             D.per_page())
+        return
+    meta = E.meta_f8_empty(D.shape)
+    E.build_page_meta_f8(D.shape, D.k, D.pt, D.sl, meta)
+    box, mu, var = D.per_page(), D.per_page(), D.per_page()
+    E.score_pages_f8(D.shape, D.q, meta, D.pt, D.sl, box, mu, var)
+    meta_o = oracle.build_page_meta_f8(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens)
+    bo, mo, vo = oracle.score_pages_f8(D.oshape, inp.q, meta_o, inp.page_table, inp.seq_lens)
+    m = _valid_mask(inp)
+    for got, want in ((box, bo), (mu, mo), (var, vo)):
+        g = got.cpu().numpy()
+        assert np.array_equal(g[m].view(np.uint32), want[m].view(np.uint32))
+        assert np.all(np.isnan(g[~m]))
+    # the Gaussian selector on the compact scores (same kernels, other inputs)
+    sel, cnt = D.sel_buffers()
+    E.select_pages_gauss(D.shape, box, mu, var, D.sl, 1.5, 0.5, sel, cnt)
+    so, co, _ = oracle.select_gauss(D.oshape, bo, mo, vo, inp.seq_lens, 1.5, 0.5)
+    assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+
+
 @pytest.mark.parametrize("k", [1, 3, 17, 1000])
 def test_select_topk(case, k):
     inp, D, _, (box_o, _, _) = case

@@ -7,6 +7,8 @@ rounding) fails at least one of them:
 * Gauss-Hermite rule  -> numpy.polynomial.hermite.hermgauss and the Gaussian moments
 * storage roundings    -> brute force over the neighbouring representable values
 * page metadata        -> numpy min/max and exact rational mean/variance
+* FP8 E4M3 codec       -> torch.float8_e4m3fn for every code, brute-force nearest
+                          with ties to even for the encoder
 * page scores          -> brute-force token scores (upper bound, equality cases,
                           mean identity, one-coordinate variance identity)
 * top-k                -> numpy lexsort
@@ -129,6 +131,109 @@ def test_build_page_meta_definitions(orc, dtype):
                 npv = toks.var(axis=0)
                 tol = (1e-6 if dtype == "f32" else 8e-3) * np.maximum(npv, 1e-30) + 1e-12
                 assert np.all(np.abs(mf[phys, g, 3] - npv) <= tol)
+
+
+# ------------------------------------------------------------ compact metadata
+def _e4m3_table():
+    import torch
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_vs_torch(orc):
+    tab = _e4m3_table()
+    got = np.array([orc.e4m3_decode(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(tab))
+    ok = ~np.isnan(tab)
+    assert np.array_equal(got[ok], tab[ok])
+    assert orc.e4m3_decode(0x7E) == 448.0 and orc.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def _e4m3_nearest(x, tab):
+    """Brute force: nearest finite code, ties to the even code, +-448 saturation."""
+    if math.isnan(x):
+        return 0x7F
+    sgn = 0x80 if math.copysign(1.0, x) < 0 else 0
+    a = abs(x)
+    pos = [(c, tab[c]) for c in range(0x7F)]  # 0x00 .. 0x7E, finite, non-negative
+    best = min(pos, key=lambda cv: (abs(cv[1] - a), cv[0] & 1))
+    return sgn | best[0]
+
+
+def test_e4m3_encode_brute_force(orc):
+    tab = _e4m3_table()
+    rng = np.random.default_rng(3)
+    xs = list(np.exp(rng.uniform(np.log(2.0 ** -13), np.log(600.0), 400)) * rng.choice([-1.0, 1.0], 400))
+    fin = [tab[c] for c in range(0x7F)]
+    xs += fin + [-v for v in fin]
+    xs += [(a + b) / 2 for a, b in zip(fin[:-1], fin[1:])]          # every tie
+    xs += [np.nextafter((a + b) / 2, 0) for a, b in zip(fin[:-1], fin[1:])]
+    xs += [0.0, -0.0, 447.9, 448.0, 463.9, 464.0, 1e9, -1e9, 2.0 ** -10, 3 * 2.0 ** -10, float("nan")]
+    for x in xs:
+        assert orc.e4m3_encode(float(x)) == _e4m3_nearest(float(x), tab), x
+
+
+def test_e4m3_encode_vs_torch_cast(orc):
+    import torch
+    rng = np.random.default_rng(4)
+    x = (np.exp(rng.uniform(np.log(2.0 ** -12), np.log(440.0), 3000)) * rng.choice([-1.0, 1.0], 3000)).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.e4m3_encode(float(v)) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_build_page_meta_f8_definitions(orc):
+    inp = synth.random_small(5, B=2, Hq=2, Hkv=2, d=64, P=16, dtype="bf16", ctx=(53, 16))
+    sh = shape_of(inp, orc)
+    meta4 = orc.build_page_meta(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    m8 = orc.build_page_meta_f8(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    assert m8.shape == (inp.num_phys, inp.Hkv, 6 * inp.d) and m8.dtype == np.uint8
+    tab = _e4m3_table()
+    kf = f64(inp.k_pool, "bf16")
+    d = inp.d
+    for b in range(inp.B):
+        L = int(inp.seq_lens[b])
+        for p in range((L + inp.P - 1) // inp.P):
+            phys = inp.page_table[b, p]
+            n = min(inp.P, L - p * inp.P)
+            for g in range(inp.Hkv):
+                rec = m8[phys, g]
+                # bounds: the same bf16 bits as the four-row record
+                assert np.array_equal(rec[:4 * d].view(np.uint16), meta4[phys, g, :2].reshape(-1))
+                toks = kf[phys, g, :n, :]
+                for i in range(d):
+                    col = [Fraction(float(t)) for t in toks[:, i]]
+                    mean = sum(col) / n
+                    var = max(sum(c * c for c in col) / n - mean * mean, Fraction(0))
+                    assert rec[4 * d + i] == _e4m3_nearest(float(mean), tab)
+                    assert rec[5 * d + i] == _e4m3_nearest(float(var), tab)
+
+
+def test_score_pages_f8_definitions(orc):
+    inp = synth.random_small(6, B=2, Hq=4, Hkv=2, d=64, P=16, dtype="bf16", ctx=(300, 77))
+    sh = shape_of(inp, orc)
+    meta4 = orc.build_page_meta(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    m8 = orc.build_page_meta_f8(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    box4, _, _ = orc.score_pages(sh, inp.q, meta4, inp.page_table, inp.seq_lens)
+    box, mu, var = orc.score_pages_f8(sh, inp.q, m8, inp.page_table, inp.seq_lens)
+    tab = _e4m3_table()
+    qf = f64(inp.q, "bf16")
+    c = 1.0 / math.sqrt(inp.d)
+    G, d = inp.Hq // inp.Hkv, inp.d
+    for b in range(inp.B):
+        npg = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        # the box reads the same bounds as the four-row record
+        assert np.array_equal(box[b, :, :npg], box4[b, :, :npg])
+        for h in range(inp.Hq):
+            q = qf[b, h]
+            for p in range(npg):
+                rec = m8[inp.page_table[b, p], h // G]
+                mean, vv = tab[rec[4 * d:5 * d]], tab[rec[5 * d:6 * d]]
+                # exact sums of exact products, rounded once
+                m_exact = math.fsum(float(x) for x in q * mean)
+                v_exact = math.fsum(float(x) for x in (q * q) * vv)
+                for got, want in ((mu[b, h, p], np.float32(c * m_exact)), (var[b, h, p], np.float32(c * c * v_exact))):
+                    ulp = abs(int(np.array(got).view(np.int32)) - int(np.array(want).view(np.int32)))
+                    assert ulp <= 1, (b, h, p, got, want)
 
 
 def test_build_page_meta_from_token(orc):
