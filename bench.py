@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming multi-step decode timing")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the compact-metadata and group-shared-selection variants of the step")
     ap.add_argument("--selector-sweep", action="store_true",
                     help="time select_pages_topk (k=64) and select_pages_gauss over contexts 32k..1M "
                          "(one JSON line with the table), then exit")
@@ -343,6 +345,90 @@ def main():
         except Exception as e:  # capture unsupported
             log(f"[bench] streaming step failed ({e})")
 
+    # ---- variants of the step: compact metadata (score_pages_f8 on E4M3 mean /
+    # variance records) and group-shared selection (one kept set per KV head,
+    # each kept page read once for the G query heads); one graph per replica
+    variants, var_sets = None, {}
+    rec8_bytes = 6 * d
+    if not args.no_variants:
+        try:
+            meta8 = []
+            for r in range(R):
+                m8 = E.meta_f8_empty(shape)
+                E.build_page_meta_f8(shape, reps[r][1], pt, sl, m8)
+                meta8.append(m8)
+            selg = torch.empty((B, Hkv, MP), dtype=torch.int32, device=dev)
+            cntg = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+            ws_gg = E.workspace(shape, E.CALL_GAUSS_GROUP)
+            ws_tg = E.workspace(shape, E.CALL_TOPK_GROUP)
+            ws_dg = E.workspace(shape, E.CALL_DECODE_GROUP)
+
+            def v_step(r, f8, grp):
+                q, k, v, meta = reps[r]
+                if f8:
+                    E.score_pages_f8(shape, q, meta8[r], pt, sl, box, mu, var, ws=ws_s)
+                else:
+                    E.score_pages(shape, q, meta, pt, sl, box, mu, var, ws=ws_s)
+                if not grp:
+                    select()
+                    decode(r)
+                    return
+                if args.policy == "gauss":
+                    E.select_pages_gauss_group(shape, box, mu, var, sl, alpha, wl.delta, selg, cntg, ws=ws_gg)
+                else:
+                    E.select_pages_topk_group(shape, box, sl, wl.topk or 64, selg, cntg, ws=ws_tg)
+                E.entmax_decode_sparse_group(shape, q, k, v, pt, sl, selg, cntg, alpha, out, ws=ws_dg)
+
+            def graph_us(fn, n_rep):
+                gs = []
+                sv = torch.cuda.Stream()
+                sv.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(sv):
+                    for r in range(R):
+                        g = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(g, stream=sv):
+                            fn(r)
+                        gs.append(g)
+                torch.cuda.current_stream().wait_stream(sv)
+                for i in range(max(args.warmup, R)):
+                    gs[i % R].replay()
+                torch.cuda.synchronize()
+                a, b = ev(), ev()
+                a.record()
+                for i in range(n_rep):
+                    gs[i % R].replay()
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) * 1e3 / n_rep
+
+            variants = {}
+            for name, f8, grp in (("compact_meta", True, False), ("group_sets", False, True),
+                                  ("compact_meta_group_sets", True, True)):
+                us = graph_us(lambda r, f8=f8, grp=grp: v_step(r, f8, grp), args.steps)
+                v_step(0, f8, grp)  # replica 0's selection, for the quality figures below
+                torch.cuda.synchronize()
+                if grp:
+                    var_sets[name] = (selg.repeat_interleave(Hq // Hkv, dim=1).clone(),
+                                      cntg.repeat_interleave(Hq // Hkv, dim=1).clone(),
+                                      float(cntg.double().mean()))
+                else:
+                    var_sets[name] = (sel.clone(), cnt.clone(), None)
+                variants[name] = {"step_us": round(us, 2), "speedup_vs_step": round(step_us / us, 3)}
+                if grp:
+                    variants[name]["kept_pages_per_kv_head_mean"] = round(var_sets[name][2], 2)
+                log(f"[bench] variant {name}: step {us:.2f} us")
+            # score_pages_f8 per launch, as for score_pages
+            sc8_us = graph_us(lambda r: [E.score_pages_f8(shape, reps[(r + j) % R][0], meta8[(r + j) % R], pt, sl,
+                                                          box, mu, var, ws=ws_s) for j in range(4)], 5 * R) / 4
+            variants["compact_meta"]["score_pages_f8_us"] = round(sc8_us, 2)
+            log(f"[bench] score_pages_f8 per launch: {sc8_us:.2f} us")
+            step(0)  # the main step's state again (replica 0)
+            torch.cuda.synchronize()
+            del meta8
+        except Exception as e:
+            log(f"[bench] variants failed ({e})")
+            variants = None
+
     # ---- algorithmic bytes of the dominant kernel (score_pages)
     seq = sl.cpu().numpy().astype(np.int64)
     npg = (seq + P - 1) // P
@@ -351,6 +437,12 @@ def main():
     # metadata records + q + box/mu/var outputs + page-table entries
     score_bytes = int(npg.sum() * Hkv * rec + B * Hq * d * esz + Hq * npg.sum() * 12 + npg.sum() * 4)
     score_gbs = score_bytes / (score_us * 1e-6) / 1e9
+    if variants and "score_pages_f8_us" in variants.get("compact_meta", {}):
+        b8 = int(npg.sum() * Hkv * rec8_bytes + B * Hq * d * esz + Hq * npg.sum() * 12 + npg.sum() * 4)
+        t8 = variants["compact_meta"]["score_pages_f8_us"]
+        variants["compact_meta"]["score_pages_f8_roofline"] = {
+            "bound": "hbm", "algorithmic_bytes": b8, "achieved": round(b8 / (t8 * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(b8 / (t8 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     # ---- selection statistics and decode bytes
     torch.cuda.synchronize()
@@ -416,6 +508,7 @@ def main():
         "selection": {"pages_per_head_mean": round(per_head_pages / (B * Hq), 2),
                       "kv_group_union_pages": union, "pages_per_seq": int(npg.max())},
         "streaming": stream_res,
+        "variants": variants,
         "step_algorithmic_bytes": int(step_bytes),
         "step_GBps": round(step_bytes / (step_us * 1e-6) / 1e9, 1),
     }
@@ -486,6 +579,22 @@ def main():
         e_ent, e_sm = rel(out_es, out_ef), rel(out_ss, out_sf)
         ss_us = time_calls(lambda i: E.softmax_decode_sparse(shape, reps[i % R][0], reps[i % R][1], reps[i % R][2],
                                                              pt, sl, sel, cnt, out_ss, ws=ws_ss), max(R, 6))
+        # the variants' selections on replica 0: discarded entmax mass and the
+        # relative error of their outputs against the full-cache entmax
+        if variants:
+            for name, (vs, vc, _) in var_sets.items():
+                vk = torch.zeros((B, Hq, MP + 1), dtype=torch.bool, device=dev)
+                vin = ar[None, None, :] < vc[:, :, None]
+                vk.scatter_(2, torch.where(vin, vs, torch.full_like(vs, MP)).long(), vin)
+                vkeep = vk[:, :, :MP]
+                d_v = (1.0 - (wfull.view(B, Hq, MP, P).double().sum(-1) * vkeep).sum(-1)).clamp(min=0.0)
+                out_v = torch.empty_like(out)
+                E.entmax_decode_sparse(shape, q0, k0, v0, pt, sl, vs.contiguous(), vc.contiguous(), alpha, out_v,
+                                       ws=ws_d)
+                torch.cuda.synchronize()
+                variants[name]["delta_entmax_mean"] = float(d_v.mean())
+                variants[name]["rel_err_entmax_mean"] = float(rel(out_v, out_ef).mean())
+                variants[name]["kept_pages_per_head_mean"] = round(float(vc.double().mean()), 2)
         result["same_kept_set"] = {
             "selection": "step's " + args.policy + " selection",
             "delta_entmax_mean": float(d_ent.mean()), "delta_entmax_max": float(d_ent.max()),

@@ -92,7 +92,10 @@ enum entmaxkv_call {
   ENTMAXKV_CALL_DECODE_SPARSE = 4,
   ENTMAXKV_CALL_DECODE_FULL = 5,
   ENTMAXKV_CALL_SOFTMAX = 6,
-  ENTMAXKV_CALL_SOFTMAX_SPARSE = 7
+  ENTMAXKV_CALL_SOFTMAX_SPARSE = 7,
+  ENTMAXKV_CALL_TOPK_GROUP = 8,
+  ENTMAXKV_CALL_GAUSS_GROUP = 9,
+  ENTMAXKV_CALL_DECODE_GROUP = 10
 };
 
 /* Bytes of workspace a call needs for this shape (0 if none).  Returns 0 for
@@ -202,6 +205,42 @@ int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const v
                              const int32_t *sel_cnt, double alpha, int32_t tau_method, float *out,
                              double *tau, float *weights_out, void *ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * Group-shared selection -- one kept set per KV head, for the G = Hq/Hkv query
+ * heads that read it, so the decode fetches each kept page once.  The policies
+ * of [EntmaxKV s.2.B] are stated per query; this grouping is a variant the
+ * summary leaves open.  Group sets: sel_idx int32 [B][Hkv][max_pages]
+ * (ascending), sel_cnt int32 [B][Hkv].
+ * select_pages_topk_group: per (b, g), the k pages with the largest
+ *   max_h box[b][g G + h][p] over the group's heads (a NaN box ranks below
+ *   every number; ties to the lower page; N_b <= k keeps every page).
+ *   ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_TOPK_GROUP).
+ * select_pages_gauss_group: per (b, g), the union of the G heads' sets as
+ *   select_pages_gauss computes them (page p kept iff some head h keeps it:
+ *   the largest margin est_{h,p} - (tau_hat_h/(alpha-1) - Delta) is >= 0, or p
+ *   is a head's fallback page).  tau_hat (nullable) [B][Hq] as there.
+ *   ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_GAUSS_GROUP).
+ * entmax_decode_sparse_group: entmax_decode_sparse with every head h of KV
+ *   head g attending over the group's set sel_idx[b][g]; outputs, tau,
+ *   weights_out, malformed-selection rules and tau_method as there (a
+ *   malformed group set makes all G rows NaN).  Each kept K page is read once
+ *   per group.  ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_DECODE_GROUP).
+ * seq_mask (nullable, uint8 [B]): as in the per-head calls.
+ */
+int32_t select_pages_topk_group(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,
+                                int32_t k, const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+int32_t select_pages_gauss_group(const entmaxkv_shape *shape, const float *box, const float *mu,
+                                 const float *var, const int32_t *seq_lens, double alpha, double delta,
+                                 double n_sigma, const uint8_t *seq_mask, int32_t *sel_idx,
+                                 int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+int32_t entmax_decode_sparse_group(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                   const int32_t *sel_idx, const int32_t *sel_cnt, double alpha,
+                                   int32_t tau_method, float *out, double *tau, float *weights_out, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* entmax_decode_full -- the same attention over every cached token (the
  * full-cache entmax baseline of [EntmaxKV s.4]). */

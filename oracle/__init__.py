@@ -63,6 +63,9 @@ def _load():
     lib.orc_select_topk.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp]
     lib.orc_select_gauss.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_double, vp, vp, ctypes.c_int32, vp, vp, vp]
+    lib.orc_select_topk_group.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp, ctypes.c_int32, vp, vp]
+    lib.orc_select_gauss_group.argtypes = [vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, vp, vp, ctypes.c_int32, vp, vp, vp]
     lib.orc_entmax_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_double, vp,
                                       ctypes.c_int32, vp, vp, vp]
     lib.orc_softmax_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp]
@@ -239,6 +242,46 @@ def select_gauss(shape: Shape, box, mu, var, seq_lens, alpha, delta, n_sigma=3.0
                          _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), float(alpha),
                          float(delta), float(n_sigma), _p(m), _p(r), nr, _p(sel), _p(cnt), _p(tau))
     return sel, cnt, tau
+
+
+def select_topk_group(shape: Shape, box, seq_lens, k, seq_mask=None, rows=None):
+    """One set per KV head: top-k of the largest box over the group's heads.
+    rows: group rows b*Hkv+g.  Returns sel [B][Hkv][max_pages], cnt [B][Hkv]."""
+    lib = _load()
+    sel = np.full((shape.B, shape.Hkv, shape.max_pages), -1, np.int32)
+    cnt = np.full((shape.B, shape.Hkv), -1, np.int32)
+    r, nr = _rows(rows)
+    m = None if seq_mask is None else np.ascontiguousarray(seq_mask, dtype=np.uint8)
+    sh = shape.c()
+    lib.orc_select_topk_group(ctypes.byref(sh), _p(np.ascontiguousarray(box, dtype=np.float32)),
+                              _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), int(k), _p(m), _p(r), nr,
+                              _p(sel), _p(cnt))
+    return sel, cnt
+
+
+def select_gauss_group(shape: Shape, box, mu, var, seq_lens, alpha, delta, n_sigma=3.0, seq_mask=None,
+                       rows=None):
+    """One set per KV head: the union of the group's per-head Gaussian sets.
+    Returns sel [B][Hkv][max_pages], cnt [B][Hkv], tau_hat [B][Hq]."""
+    lib = _load()
+    sel = np.full((shape.B, shape.Hkv, shape.max_pages), -1, np.int32)
+    cnt = np.full((shape.B, shape.Hkv), -1, np.int32)
+    tau = np.full((shape.B, shape.Hq), np.nan)
+    r, nr = _rows(rows)
+    m = None if seq_mask is None else np.ascontiguousarray(seq_mask, dtype=np.uint8)
+    sh = shape.c()
+    box_c, mu_c, var_c = (np.ascontiguousarray(a, dtype=np.float32) for a in (box, mu, var))
+    lib.orc_select_gauss_group(ctypes.byref(sh), _p(box_c), _p(mu_c), _p(var_c),
+                               _p(np.ascontiguousarray(seq_lens, dtype=np.int32)), float(alpha),
+                               float(delta), float(n_sigma), _p(m), _p(r), nr, _p(sel), _p(cnt), _p(tau))
+    return sel, cnt, tau
+
+
+def expand_group_selection(shape: Shape, sel_g, cnt_g):
+    """Per-query-head copies of a group selection (head h reads group h // G)."""
+    G = shape.Hq // shape.Hkv
+    return (np.ascontiguousarray(np.repeat(np.asarray(sel_g), G, axis=1)),
+            np.ascontiguousarray(np.repeat(np.asarray(cnt_g), G, axis=1)))
 
 
 def entmax_decode(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, alpha, sel_idx=None,

@@ -513,6 +513,87 @@ void orc_select_gauss(const orc_shape *s, const float *box, const float *mu, con
 }
 
 /* ------------------------------------------------------------------------ */
+/* Group-shared selection: one kept set per KV head, for the G query heads    */
+/* that read it.  A variant the EntmaxKV summary leaves open (its policies,    */
+/* section 2.B, are stated per query).  Readings:                              */
+/*  * Top-k: a page's group score is the largest box over the G heads (a NaN  */
+/*    box ranks below every number, as in select_pages_topk); the k pages     */
+/*    with the largest group scores, ties to the lower page, ascending list;  */
+/*  * Gaussian: a page is kept for the group iff at least one of the G heads  */
+/*    keeps it (each head with its own tau_hat, margin and fallback page),    */
+/*    i.e. the largest per-head margin est_p - threshold is >= 0.             */
+/* rows: optional list of group rows b*Hkv + g (NULL = all).  Outputs are     */
+/* [B][Hkv][max_pages] and [B][Hkv]; tau_hat (nullable) [B][Hq] receives the  */
+/* heads of the listed groups.                                                 */
+/* ------------------------------------------------------------------------ */
+void orc_select_topk_group(const orc_shape *s, const float *box, const int32_t *seq_lens, int32_t k,
+                           const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,
+                           int32_t *sel_idx, int32_t *sel_cnt) {
+  const int G = s->Hq / s->Hkv;
+  int nr = rows ? n_rows : s->B * s->Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < nr; ++r) {
+    int grow = rows ? rows[r] : r, b = grow / s->Hkv, g = grow % s->Hkv;
+    if (seq_mask && !seq_mask[b]) continue;
+    int32_t np = n_pages(s, seq_len(s, seq_lens, b));
+    kv_pair *v = (kv_pair *)malloc(sizeof(kv_pair) * (np > 0 ? np : 1));
+    for (int32_t p = 0; p < np; ++p) {
+      double key = -INFINITY;
+      for (int h = 0; h < G; ++h) {
+        double x = box[((size_t)b * s->Hq + (size_t)g * G + h) * s->max_pages + p];
+        if (!isnan(x) && x > key) key = x;
+      }
+      v[p].key = key;
+      v[p].idx = p;
+    }
+    qsort(v, np, sizeof(kv_pair), cmp_desc);
+    int32_t m = np < k ? np : k;
+    int32_t *out = sel_idx + (size_t)grow * s->max_pages;
+    for (int32_t i = 0; i < m; ++i) out[i] = v[i].idx;
+    qsort(out, m, sizeof(int32_t), cmp_int);
+    sel_cnt[grow] = m;
+    free(v);
+  }
+}
+
+void orc_select_gauss_group(const orc_shape *s, const float *box, const float *mu, const float *var,
+                            const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                            const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,
+                            int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat) {
+  const int G = s->Hq / s->Hkv;
+  const int MP = s->max_pages;
+  int nr = rows ? n_rows : s->B * s->Hkv;
+  int32_t *hrows = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nr > 0 ? nr : 1) * G);
+  for (int r = 0; r < nr; ++r) {
+    int grow = rows ? rows[r] : r, b = grow / s->Hkv, g = grow % s->Hkv;
+    for (int h = 0; h < G; ++h) hrows[(size_t)r * G + h] = b * s->Hq + g * G + h;
+  }
+  int32_t *hs = (int32_t *)malloc(sizeof(int32_t) * (size_t)s->B * s->Hq * MP);
+  int32_t *hc = (int32_t *)malloc(sizeof(int32_t) * (size_t)s->B * s->Hq);
+  orc_select_gauss(s, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, hrows, nr * G, hs, hc,
+                   tau_hat);
+  for (int r = 0; r < nr; ++r) {
+    int grow = rows ? rows[r] : r, b = grow / s->Hkv;
+    if (seq_mask && !seq_mask[b]) continue;
+    int32_t np = n_pages(s, seq_len(s, seq_lens, b));
+    uint8_t *kept = (uint8_t *)calloc((size_t)(np > 0 ? np : 1), 1);
+    for (int h = 0; h < G; ++h) {
+      int32_t row = hrows[(size_t)r * G + h];
+      for (int32_t i = 0; i < hc[row]; ++i) kept[hs[(size_t)row * MP + i]] = 1;
+    }
+    int32_t cnt = 0;
+    int32_t *out = sel_idx + (size_t)grow * MP;
+    for (int32_t p = 0; p < np; ++p)
+      if (kept[p]) out[cnt++] = p;
+    sel_cnt[grow] = cnt;
+    free(kept);
+  }
+  free(hs);
+  free(hc);
+  free(hrows);
+}
+
+/* ------------------------------------------------------------------------ */
 /* alpha-entmax over a reduced set -- EntmaxKV summary 2.C and 3.               */
 /* p_t = [(alpha-1)s_t - tau]_+^(1/(alpha-1)) with tau the root of sum p = 1,   */
 /* found by bisection on [max X - 1, max X - n^(1-alpha)], X = (alpha-1)s.       */

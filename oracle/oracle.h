@@ -71,6 +71,17 @@ void orc_select_gauss(const orc_shape *s, const float *box, const float *mu, con
                       const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,
                       int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat);
 
+/* Group-shared selection (one set per KV head; rows = group rows b*Hkv+g):
+ * Top-k on the largest box over the G heads; Gaussian = union of the G heads'
+ * sets.  sel_idx [B][Hkv][max_pages], sel_cnt [B][Hkv], tau_hat [B][Hq]. */
+void orc_select_topk_group(const orc_shape *s, const float *box, const int32_t *seq_lens, int32_t k,
+                           const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,
+                           int32_t *sel_idx, int32_t *sel_cnt);
+void orc_select_gauss_group(const orc_shape *s, const float *box, const float *mu, const float *var,
+                            const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                            const uint8_t *seq_mask, const int32_t *rows, int32_t n_rows,
+                            int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat);
+
 /* F(tau) of the Gaussian selector over an explicit page list (for pins). */
 double orc_gauss_mass(const float *mu, const float *var, const int32_t *n, int32_t np, double alpha,
                       double tau);

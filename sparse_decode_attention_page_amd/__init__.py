@@ -21,11 +21,12 @@ _lib = None
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
-CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE = \
-    range(1, 8)
+(CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE,
+ CALL_TOPK_GROUP, CALL_GAUSS_GROUP, CALL_DECODE_GROUP) = range(1, 11)
 
 EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_f8",
-           "select_pages_topk", "select_pages_gauss",
+           "select_pages_topk", "select_pages_gauss", "select_pages_topk_group", "select_pages_gauss_group",
+           "entmax_decode_sparse_group",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
            "entmaxkv_stream_read")
@@ -76,6 +77,12 @@ def load(path: str | None = None):
     lib.select_pages_topk.argtypes = [sh, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.select_pages_gauss.restype = i32
     lib.select_pages_gauss.argtypes = [sh, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp, vp, vp, sz, vp]
+    lib.select_pages_topk_group.restype = i32
+    lib.select_pages_topk_group.argtypes = [sh, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.select_pages_gauss_group.restype = i32
+    lib.select_pages_gauss_group.argtypes = [sh, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp, vp, vp, sz, vp]
+    lib.entmax_decode_sparse_group.restype = i32
+    lib.entmax_decode_sparse_group.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
     lib.entmax_decode_sparse.restype = i32
     lib.entmax_decode_sparse.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
     lib.softmax_decode_sparse.restype = i32
@@ -268,6 +275,54 @@ def select_pages_gauss(shape: Shape, box, mu, var, seq_lens, alpha, delta, sel_i
                                    _ptr(tau_hat, torch.float64, "tau_hat"), wp, wn, _stream(stream))
     _check("select_pages_gauss", st)
     return sel_idx, sel_cnt
+
+
+def select_pages_topk_group(shape: Shape, box, seq_lens, k, sel_idx, sel_cnt, seq_mask=None, ws=None,
+                            stream=None):
+    """One set per KV head: sel_idx int32 [B, Hkv, max_pages], sel_cnt int32 [B, Hkv]."""
+    torch = _torch()
+    wp, wn, keep = _ws(shape, CALL_TOPK_GROUP, ws)
+    st = load().select_pages_topk_group(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
+                                        _ptr(seq_lens, torch.int32, "seq_lens"), int(k),
+                                        _ptr(seq_mask, torch.uint8, "seq_mask"),
+                                        _ptr(sel_idx, torch.int32, "sel_idx"),
+                                        _ptr(sel_cnt, torch.int32, "sel_cnt"), wp, wn, _stream(stream))
+    _check("select_pages_topk_group", st)
+    return sel_idx, sel_cnt
+
+
+def select_pages_gauss_group(shape: Shape, box, mu, var, seq_lens, alpha, delta, sel_idx, sel_cnt,
+                             n_sigma=3.0, seq_mask=None, tau_hat=None, ws=None, stream=None):
+    """One set per KV head: the union of the group's per-head Gaussian sets."""
+    torch = _torch()
+    wp, wn, keep = _ws(shape, CALL_GAUSS_GROUP, ws)
+    st = load().select_pages_gauss_group(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
+                                         _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"),
+                                         _ptr(seq_lens, torch.int32, "seq_lens"), float(alpha), float(delta),
+                                         float(n_sigma), _ptr(seq_mask, torch.uint8, "seq_mask"),
+                                         _ptr(sel_idx, torch.int32, "sel_idx"),
+                                         _ptr(sel_cnt, torch.int32, "sel_cnt"),
+                                         _ptr(tau_hat, torch.float64, "tau_hat"), wp, wn, _stream(stream))
+    _check("select_pages_gauss_group", st)
+    return sel_idx, sel_cnt
+
+
+def entmax_decode_sparse_group(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt,
+                               alpha, out, tau=None, weights_out=None, tau_method=0, ws=None, stream=None):
+    """entmax_decode_sparse with one kept set per KV head (sel_idx [B, Hkv, max_pages])."""
+    torch = _torch()
+    kd = _kv_dtype(shape)
+    wp, wn, keep = _ws(shape, CALL_DECODE_GROUP, ws)
+    st = load().entmax_decode_sparse_group(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
+                                           _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
+                                           _ptr(seq_lens, torch.int32, "seq_lens"),
+                                           _ptr(sel_idx, torch.int32, "sel_idx"),
+                                           _ptr(sel_cnt, torch.int32, "sel_cnt"), float(alpha), int(tau_method),
+                                           _ptr(out, torch.float32, "out"), _ptr(tau, torch.float64, "tau"),
+                                           _ptr(weights_out, torch.float32, "weights_out"), wp, wn,
+                                           _stream(stream))
+    _check("entmax_decode_sparse_group", st)
+    return out
 
 
 def entmax_decode_sparse(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt,

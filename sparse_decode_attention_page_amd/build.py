@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libentmaxkv.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.hip", "meta.hip", "score.hip", "topk.hip", "gauss.hip", "decode.hip", "softmax.hip"]
+SOURCES = ["abi.hip", "meta.hip", "score.hip", "topk.hip", "gauss.hip", "group.hip", "decode.hip", "softmax.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

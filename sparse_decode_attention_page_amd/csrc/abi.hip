@@ -167,6 +167,9 @@ size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call)
     case ENTMAXKV_CALL_DECODE_FULL: return full_ws_bytes(D);
     case ENTMAXKV_CALL_SOFTMAX: return softmax_ws_bytes(D);
     case ENTMAXKV_CALL_SOFTMAX_SPARSE: return softmax_sparse_ws_bytes(D);
+    case ENTMAXKV_CALL_TOPK_GROUP: return topk_group_ws_bytes(D);
+    case ENTMAXKV_CALL_GAUSS_GROUP: return gauss_group_ws_bytes(D);
+    case ENTMAXKV_CALL_DECODE_GROUP: return decode_group_ws_bytes(D);
   }
   return 0;
 }
@@ -296,6 +299,53 @@ int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const v
                              hipStream_t stream) {
   return decode_common(shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, alpha,
                        tau_method, out, tau, weights_out, ws, ws_bytes, stream, false);
+}
+
+int32_t select_pages_topk_group(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,
+                                int32_t k, const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                                void *ws, size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!box || !seq_lens || !sel_idx || !sel_cnt || k <= 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(topk_group_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_topk_group(D, box, seq_lens, k, seq_mask, sel_idx, sel_cnt, ws, stream));
+}
+
+int32_t select_pages_gauss_group(const entmaxkv_shape *shape, const float *box, const float *mu,
+                                 const float *var, const int32_t *seq_lens, double alpha, double delta,
+                                 double n_sigma, const uint8_t *seq_mask, int32_t *sel_idx,
+                                 int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!box || !mu || !var || !seq_lens || !sel_idx || !sel_cnt) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(alpha > 1.0) || !std::isfinite(alpha) || !(delta >= 0.0) || !std::isfinite(delta) ||
+      !(n_sigma >= 0.0) || !std::isfinite(n_sigma))
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(gauss_group_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_gauss_group(D, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, sel_idx,
+                                       sel_cnt, tau_hat, ws, stream));
+}
+
+int32_t entmax_decode_sparse_group(const entmaxkv_shape *shape, const void *q, const void *k_pool,
+                                   const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                   const int32_t *sel_idx, const int32_t *sel_cnt, double alpha,
+                                   int32_t tau_method, float *out, double *tau, float *weights_out, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !out || !sel_idx || !sel_cnt)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, k_pool, v_pool)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(decode_group_ws_bytes(D), ws, ws_bytes))) return st;
+  return hip_status(launch_entmax_decode_group(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
+                                               sel_cnt, alpha, tau_method, out, tau, weights_out, ws, stream));
 }
 
 int32_t entmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,

@@ -189,8 +189,8 @@ struct GlobSeg {
   }
 };
 
-// Candidates held in registers: thread t owns entries 32t .. 32t + 31.
-constexpr int kRegPer = 32;
+// Candidates held in registers: thread t owns entries 16t .. 16t + 15.
+constexpr int kRegPer = 16;
 struct RegVals {
   const double (&v)[kRegPer];
   int n;
@@ -204,10 +204,16 @@ struct RegVals {
 struct WaveRed {
   __device__ __forceinline__ double operator()(double v, double *) const { return wave_sum(v); }
   __device__ __forceinline__ void pair(double &a, double &b, double *) const { a = wave_sum(a); b = wave_sum(b); }
+  __device__ __forceinline__ void sums3(double (&v)[3], double *) const {
+    v[0] = wave_sum(v[0]); v[1] = wave_sum(v[1]); v[2] = wave_sum(v[2]);
+  }
+  __device__ __forceinline__ double max(double v, double *) const { return wave_max(v); }
 };
 struct BlockRed {
   __device__ __forceinline__ double operator()(double v, double *s) const { return block_sum(v, s); }
   __device__ __forceinline__ void pair(double &a, double &b, double *s) const { block_sum2(a, b, s); }
+  __device__ __forceinline__ void sums3(double (&v)[3], double *s) const { block_sum_n<3>(v, s); }
+  __device__ __forceinline__ double max(double v, double *s) const { return block_max(v, s); }
 };
 
 // Root of F(t) = sum [X - t]_+^beta = 1 by Newton from the left: lo0 has
@@ -217,13 +223,49 @@ struct BlockRed {
 // Otherwise each Newton candidate is checked with a second pass; one that
 // leaves (lo, hi) becomes a bisection step, and after a step lands right of
 // the root the next step bisects.
+//
+// alpha = 2 and 1.5 (beta = 1, 2): between consecutive scores F is linear or
+// quadratic, F(lo + u) = sum_A (y - u)^beta over the active set A = {y = X - lo
+// > 0}.  Each pass also solves that piece exactly (u = (S1 - 1)/|A|, or the
+// smaller root (S2 - 1)/(S1 + sqrt(S1^2 - |A|(S2 - 1))) of |A| u^2 - 2 S1 u + S2
+// = 1); when u <= min_A y every active score stays active at lo + u, so lo + u
+// is F's root and the pass ends the search (*z_out = F there, from the same
+// sums).  Otherwise the Newton step is taken as above.  Rows end in 1-4 passes
+// instead of 5-8.  *z_out = 0 when the search ends another way.
 template <int kB, typename Src, typename Red>
 __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx, double lo0,
-                                             const DecodeParams &dp, double *dred) {
+                                             const DecodeParams &dp, double *dred, double *z_out) {
   const Red red;
   double lo = lo0;
   double hi = mx - pow(n, -dp.a);
+  *z_out = 0.0;
   if (!(hi > lo)) return lo;
+  if (kB == 1 || kB == 2) {
+#pragma unroll 1
+    for (int it = 0; it < 200; ++it) {
+      double sm[3] = {0.0, 0.0, 0.0};  // S1, S2, |A| over y = X - lo > 0
+      double nmn = -INFINITY;          // -min_A y
+      src.each([&](double x) {
+        const double y = x - lo;
+        if (y > 0.0) { sm[0] += y; sm[1] += y * y; sm[2] += 1.0; nmn = fmax(nmn, -y); }
+      });
+      red.sums3(sm, dred);
+      nmn = red.max(nmn, dred);
+      const double s1 = sm[0], s2 = sm[1], c = sm[2];
+      const double f = kB == 2 ? s2 : s1;
+      if (!(f > 1.0) || !(c > 0.0)) break;  // at the root (to rounding)
+      const double u = kB == 2 ? (s2 - 1.0) / (s1 + sqrt(fmax(s1 * s1 - c * (s2 - 1.0), 0.0))) : (s1 - 1.0) / c;
+      if (u <= -nmn) {
+        *z_out = kB == 2 ? (s2 - 2.0 * u * s1) + c * u * u : s1 - c * u;
+        return lo + u;
+      }
+      const double cand = lo + (f - 1.0) / (kB == 2 ? 2.0 * s1 : c);
+      if (!(cand > lo)) break;  // no progress: converged
+      if (!(cand < hi)) break;  // only through rounding, next to the root
+      lo = cand;
+    }
+    return lo;
+  }
   if (kB != 0 || dp.beta >= 1.0) {
 #pragma unroll 1
     for (int it = 0; it < 200; ++it) {
@@ -338,21 +380,28 @@ __device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, doub
                                           double *dred, int *s_kstar, double *s_tau, double &tau, double &z) {
   const int tid = threadIdx.x;
   const GlobSeg<8> gs8{gs.x, gs.soff, gs.sbase, gs.nseg, gs.n};
+  double zk = 0.0;  // F at tau when the solver found it from its sums (else 0)
   if (tier == 0 && kB == 1 && dp.tau_method == 1) {
     tau = sparsemax_tau_sort(cx, total, sortbuf, dred, s_kstar);
   } else if (tier == 0) {
     if (tid < kWave) {
-      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, lo0, dp, dred);
-      if (tid == 0) *s_tau = t;
+      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, lo0, dp,
+                                                         dred, &zk);
+      if (tid == 0) { s_tau[0] = t; s_tau[1] = zk; }
     }
     __syncthreads();
-    tau = *s_tau;
+    tau = s_tau[0];
+    zk = s_tau[1];
   } else if (kB != 0 && tier == 1) {
-    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, lo0, dp, dred);
+    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, lo0, dp, dred, &zk);
   } else if (kB != 0) {
-    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred);
+    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred, &zk);
   } else {
-    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, lo0, dp, dred);
+    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, lo0, dp, dred, &zk);
+  }
+  if (zk > 0.0) {
+    z = zk;
+    return;
   }
   double zz = 0.0;
   auto zsum = [&](double x) { const double y = x - tau; if (y > 0.0) zz += pw<kB>(y, dp); };
@@ -436,10 +485,10 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int kTpe = DIM / 8;           // threads per support entry in the V gather
   constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
-  __shared__ double dred[2 * kDThreads / kWave];
+  __shared__ double dred[3 * kDThreads / kWave];  // up to three block sums at once
   __shared__ int scan_scratch[kDThreads / kWave];
   __shared__ int s_last, s_kstar;
-  __shared__ double s_tau;
+  __shared__ double s_tau[2];
   __shared__ int soff[kSplitMax + 1], sbase[kSplitMax];
   __shared__ double sL[kSplitMax];
   __shared__ int s_cnt[kDThreads / kWave][kNThr];
@@ -626,11 +675,11 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       soff[0] = 0;
       double lm = thr;
       for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
-      s_tau = lm;
+      s_tau[0] = lm;
     }
     __syncthreads();
     total = soff[nsplit];
-    L = s_tau;
+    L = s_tau[0];
     const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
     nlds = 0;
 #pragma unroll 1
@@ -686,9 +735,9 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   EKV_MARK(1, 5);
   // 3. threshold and normalizer
   double tau, z;
-  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
-  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
-  else solve_row<0>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, &s_tau, tau, z);
+  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
+  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
+  else solve_row<0>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
   EKV_MARK(1, 6);
   if (tid == 0 && tau_out) tau_out[r] = tau / dp.a;
 
@@ -891,6 +940,169 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
   }
   if (D.d == 64) return launch_decode_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
   return launch_decode_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+}
+
+// ------------------------------------- group-shared selection: one set per KV head
+// Items (group row (b, g), i): the i-th page of the KV head's set.  The page's
+// K slice is read once and scored for the G query heads of the group; each
+// head's row receives the item in kernel 2's layout (exact X per token, page
+// maximum -- NaN for a malformed item --, physical page) and the expanded
+// selection (every head of the group lists the group's pages), so kernel 2 runs
+// unchanged.  Group counts are copied to the heads as given, so a count outside
+// [0, N_b] marks all G rows as malformed in kernel 2.
+template <typename T, int DIM, int P, int G>
+__global__ __launch_bounds__(kDThreads) void group_scores_kernel(
+    Dims D, DecodeParams dp, const T *__restrict__ q, const T *__restrict__ k_pool,
+    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ gsel_idx, const int32_t *__restrict__ gsel_cnt, int32_t *__restrict__ hsel_idx,
+    int32_t *__restrict__ hsel_cnt, float *__restrict__ weights_out, DecodeWs ws) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kParts = kDThreads / P;  // threads per token
+  constexpr int kPer = DIM / kParts;     // coordinates per thread
+  __shared__ double smax[kDThreads / kWave][G];
+  __shared__ int scan_scratch[kDThreads / kWave];
+  Dims Dg = D;  // rows = KV heads
+  Dg.Hq = D.Hkv;
+  Dg.G = 1;
+  const int grows = D.B * D.Hkv, rows = D.B * D.Hq;
+  int *prefix = reinterpret_cast<int *>(smem);
+  const int tid = threadIdx.x;
+  for (int r = blockIdx.x * kDThreads + tid; r < rows; r += gridDim.x * kDThreads) {
+    ws.ctr[r] = 0u;  // kernel 2's arrival counters start at zero
+    hsel_cnt[r] = gsel_cnt[(size_t)(r / D.Hq) * D.Hkv + (r % D.Hq) / G];
+  }
+  const int total = build_item_map(Dg, seq_lens, gsel_cnt, prefix, grows, scan_scratch);
+  const int MP = D.max_pages;
+  const size_t wrow = (size_t)MP * P;
+  const int tok = tid / kParts, part = tid % kParts;
+#pragma unroll 1
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const int gr = find_row(prefix, grows, item);
+    const int i = item - prefix[gr];
+    const int cnt = prefix[gr + 1] - prefix[gr];
+    const int b = gr / D.Hkv, g = gr % D.Hkv;
+    const int r0 = b * D.Hq + g * G;
+    const int L = seq_len_clamped(seq_lens, b, D);
+    const int p = gsel_idx[(size_t)gr * MP + i];
+    const int prev = i > 0 ? gsel_idx[(size_t)gr * MP + i - 1] : -1;
+    float qv[G][kPer];
+#pragma unroll
+    for (int h = 0; h < G; ++h) load_vec<kPer>(q + (size_t)(r0 + h) * DIM + part * kPer, qv[h]);
+    const int np = n_pages_of(L, P);
+    const int pc = min(max(p, 0), MP - 1);
+    const int phys = page_table[(size_t)b * MP + pc];
+    const bool bad_item = p < 0 || p >= np || prev >= p || phys < 0 || phys >= D.num_phys;
+    const int physc = min(max(phys, 0), D.num_phys - 1);
+    const int n = min(P, L - pc * P);
+    float kv[kPer];
+    load_vec<kPer>(k_pool + (((size_t)physc * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
+    double x[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[h][e], acc);  // exact products
+#pragma unroll
+      for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+      x[h] = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
+      if (part == 0) ws.xs[(size_t)(r0 + h) * wrow + (size_t)i * P + tok] = x[h];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) x[h] = wave_max(x[h]);
+    if ((tid & (kWave - 1)) == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h) smax[tid / kWave][h] = x[h];
+    __syncthreads();
+    if (tid < G) {
+      double m = smax[0][tid];
+      for (int w = 1; w < kDThreads / kWave; ++w) m = fmax(m, smax[w][tid]);
+      const size_t o = (size_t)(r0 + tid) * MP + i;
+      ws.pmax[o] = bad_item ? NAN : m;
+      ws.iphys[o] = (uint32_t)physc;
+      hsel_idx[o] = p;
+    }
+    __syncthreads();
+    // weights_out: zero every slot of the pages this item covers, (prev, p]
+    // (the last item also covers the pages after p); kernel 2 writes the
+    // support weights
+    if (weights_out && !bad_item) {
+      const size_t lo_s = (size_t)(prev + 1) * P;
+      const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
+      for (int h = 0; h < G; ++h)
+        for (size_t s = lo_s + tid; s < hi_s; s += kDThreads) weights_out[(size_t)(r0 + h) * wrow + s] = 0.0f;
+    }
+  }
+}
+
+size_t decode_group_ws_bytes(const Dims &D) {
+  Carve cv(nullptr);
+  size_t b = 0;
+  carve_decode(D, nullptr, &b);
+  cv.take<char>(b);
+  cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
+  cv.take<int32_t>((size_t)D.B * D.Hq);
+  return cv.bytes();
+}
+
+template <typename T, int DIM, int P, int G>
+static hipError_t launch_group_t(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
+                                 const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                 const int32_t *gsel_idx, const int32_t *gsel_cnt, float *out, double *tau,
+                                 float *weights_out, void *ws, hipStream_t s) {
+  size_t dec_bytes = 0;
+  carve_decode(D, nullptr, &dec_bytes);
+  Carve cv(ws);
+  char *dec = cv.take<char>(dec_bytes);
+  int32_t *hsel_idx = cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
+  int32_t *hsel_cnt = cv.take<int32_t>((size_t)D.B * D.Hq);
+  const DecodeWs w = carve_decode(D, dec, nullptr);
+  const size_t map_bytes = (size_t)(D.B * D.Hkv + 1) * 4;
+  hipLaunchKernelGGL((group_scores_kernel<T, DIM, P, G>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
+                     (const T *)q, (const T *)k_pool, page_table, seq_lens, gsel_idx, gsel_cnt, hsel_idx, hsel_cnt,
+                     weights_out, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, hsel_idx, hsel_cnt, out, tau, weights_out, w, s);
+}
+
+template <typename T, int DIM, int P>
+static hipError_t launch_group_g(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
+                                 const int32_t *pt, const int32_t *sl, const int32_t *si, const int32_t *sc,
+                                 float *out, double *tau, float *wo, void *ws, hipStream_t s) {
+  switch (D.G) {
+    case 1: return launch_group_t<T, DIM, P, 1>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+    case 2: return launch_group_t<T, DIM, P, 2>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+    case 4: return launch_group_t<T, DIM, P, 4>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+    case 8: return launch_group_t<T, DIM, P, 8>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DIM>
+static hipError_t launch_group_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
+                                 const int32_t *pt, const int32_t *sl, const int32_t *si, const int32_t *sc,
+                                 float *out, double *tau, float *wo, void *ws, hipStream_t s) {
+  if (D.P == 16) return launch_group_g<T, DIM, 16>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+  if (D.P == 32) return launch_group_g<T, DIM, 32>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+  return launch_group_g<T, DIM, 64>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+}
+
+hipError_t launch_entmax_decode_group(const Dims &D, int dtype, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                      const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
+                                      float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
+  DecodeParams dp;
+  dp.a = alpha - 1.0;
+  dp.beta = 1.0 / dp.a;
+  dp.c = D.scale;
+  dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
+  dp.tau_method = tau_method;
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64) return launch_group_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+    return launch_group_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+  }
+  if (D.d == 64) return launch_group_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+  return launch_group_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
 }
 
 // ------------------------------------------- full cache: every page selected

@@ -61,6 +61,22 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
                                 const int32_t *sel_cnt, double alpha, int tau_method, float *out,
                                 double *tau, float *weights_out, void *ws, hipStream_t s);
 
+size_t decode_group_ws_bytes(const Dims &D);
+hipError_t launch_entmax_decode_group(const Dims &D, int dtype, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                      const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
+                                      float *out, double *tau, float *weights_out, void *ws, hipStream_t s);
+
+size_t topk_group_ws_bytes(const Dims &D);
+hipError_t launch_topk_group(const Dims &D, const float *box, const int32_t *seq_lens, int k,
+                             const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt, void *ws,
+                             hipStream_t s);
+size_t gauss_group_ws_bytes(const Dims &D);
+hipError_t launch_gauss_group(const Dims &D, const float *box, const float *mu, const float *var,
+                              const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                              const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat,
+                              void *ws, hipStream_t s);
+
 size_t full_ws_bytes(const Dims &D);
 hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *page_table, const int32_t *seq_lens, double alpha, float *out,

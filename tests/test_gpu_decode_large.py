@@ -14,9 +14,11 @@ from sparse_decode_attention_page_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-# score scales: default 1/sqrt(d) (few candidates), 0.08 (a few thousand
-# candidates, small support), 0.002 (every token a candidate and in the support)
-SCALES = [0.0, 0.08, 0.002]
+# score scales: default 1/sqrt(d) (few candidates), 0.08 (candidates that
+# still fit LDS), 0.02 and 0.01 (alpha = 1.5: 1k-4k candidates per row, solved
+# from registers, and some rows beyond), 0.002 (every token a candidate and in
+# the support: solved over the workspace)
+SCALES = [0.0, 0.08, 0.02, 0.01, 0.002]
 
 
 @pytest.fixture(scope="module", params=SCALES, ids=lambda s: f"scale{s}")

@@ -204,3 +204,43 @@ def test_full_softmax_sparse_sampled_rows(full, policy):
                                    rows=rows, sel_idx=sel.cpu().numpy(), sel_cnt=cnt.cpu().numpy())
     assert rel_l2_rows(_take_rows(out.cpu().numpy(), rows), _take_rows(oo, rows)) <= TOL[inp.dtype]
     assert np.allclose(lse.cpu().numpy().reshape(-1)[rows], lo.reshape(-1)[rows], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("policy", ["gauss", "topk"])
+def test_full_group_selection_and_decode_sampled(full, policy):
+    """Group-shared selection (one set per KV head) and the group decode at full
+    size: the sampled rows' groups against the oracle on the GPU's own scores."""
+    t = torch()
+    inp, h, rows, wl = full["inp"], full["host"], full["rows"], full["wl"]
+    B, Hq, Hkv, MP, P, d = inp.B, inp.Hq, inp.Hkv, inp.max_pages, inp.P, inp.d
+    G = Hq // Hkv
+    alpha = wl.alphas[0]
+    sel = t.full((B, Hkv, MP), -1, dtype=t.int32, device="cuda")
+    cnt = t.full((B, Hkv), -1, dtype=t.int32, device="cuda")
+    box, mu, var = (full[k].cpu().numpy() for k in ("box", "mu", "var"))
+    grows = sorted({(r // Hq) * Hkv + (r % Hq) // G for r in rows})
+    if policy == "topk":
+        E.select_pages_topk_group(full["shape"], full["box"], inp.seq_lens, wl.topk, sel, cnt)
+        so, co = oracle.select_topk_group(full["osh"], box, h["seq_lens"], wl.topk, rows=grows)
+    else:
+        E.select_pages_gauss_group(full["shape"], full["box"], full["mu"], full["var"], inp.seq_lens, alpha,
+                                   wl.delta, sel, cnt)
+        so, co, _ = oracle.select_gauss_group(full["osh"], box, mu, var, h["seq_lens"], alpha, wl.delta, rows=grows)
+    sg, cg = sel.cpu().numpy(), cnt.cpu().numpy()
+    assert sets_equal(sg, cg, so, co, rows=set(grows)) == []
+    out = t.full((B, Hq, d), np.nan, device="cuda")
+    tau = t.full((B, Hq), np.nan, dtype=t.float64, device="cuda")
+    w = t.full((B, Hq, MP * P), np.nan, device="cuda")
+    E.entmax_decode_sparse_group(full["shape"], inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, sel, cnt,
+                                 alpha, out, tau=tau, weights_out=w)
+    se, ce = oracle.expand_group_selection(full["osh"], sg, cg)
+    oo, to, wo = oracle.entmax_decode(full["osh"], h["q"], h["k_pool"], h["v_pool"], h["page_table"], h["seq_lens"],
+                                      alpha, se, ce, rows=rows, want_weights=True)
+    og = _take_rows(out.cpu().numpy(), rows)
+    tg = tau.cpu().numpy().reshape(-1)[rows]
+    wg = w.view(B * Hq, -1)[rows].cpu().numpy()
+    oo, to, wo = _take_rows(oo, rows), to.reshape(-1)[rows], _take_rows(wo, rows)
+    assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(wg > 0, wo > 0), "support differs"
+    assert np.max(np.abs(wg - wo)) < 1e-5
+    assert rel_l2_rows(og, oo) <= TOL[inp.dtype]

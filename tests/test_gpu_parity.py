@@ -240,3 +240,76 @@ def test_softmax_decode_sparse_edge_cases(case):
     assert np.array_equal(np.isinf(lg[fin]), np.isinf(lo[fin]))
     ok = ~np.isnan(oo).any(axis=-1)
     assert rel_l2_rows(og[ok][None], oo[ok][None]) <= TOL[inp.dtype] if ok.any() else True
+
+
+# ------------------------------------------------------- group-shared selection
+def _group_decode_check(inp, D, alpha, sg, cg, tau_method=0):
+    """entmax_decode_sparse_group against the oracle decoding every head over
+    its group's set (the expanded selection)."""
+    t = torch()
+    out = t.full((inp.B, inp.Hq, inp.d), np.nan, dtype=t.float32, device="cuda")
+    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    w = t.full((inp.B, inp.Hq, inp.max_pages * inp.P), np.nan, dtype=t.float32, device="cuda")
+    E.entmax_decode_sparse_group(D.shape, D.q, D.k, D.v, D.pt, D.sl, t.from_numpy(sg).cuda(), t.from_numpy(cg).cuda(),
+                                 alpha, out, tau=tau, weights_out=w, tau_method=tau_method)
+    se, ce = oracle.expand_group_selection(D.oshape, sg, cg)
+    oo, to, wo = oracle.entmax_decode(D.oshape, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens,
+                                      alpha, se, ce, want_weights=True)
+    og, tg, wg = out.cpu().numpy(), tau.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(np.isnan(og).any(-1), np.isnan(oo).any(-1)), "malformed rows differ"
+    ok = ~np.isnan(oo).any(-1)
+    assert np.array_equal(np.isnan(tg), np.isnan(to))
+    fin = ~np.isnan(to)
+    assert np.allclose(tg[fin], to[fin], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(wg[ok] > 0, wo[ok] > 0), "support differs"
+    assert np.max(np.abs(wg[ok] - wo[ok]), initial=0.0) < 1e-5
+    if ok.any():
+        assert rel_l2_rows(og[ok][None], oo[ok][None]) <= TOL[inp.dtype]
+
+
+@pytest.mark.parametrize("policy", ["topk", "gauss"])
+def test_group_selection_and_decode(case, policy):
+    inp, D, meta_o, (box_o, mu_o, var_o) = case
+    t = torch()
+    B, Hkv, MP = inp.B, inp.Hkv, inp.max_pages
+    box, mu, var = (t.from_numpy(a).cuda() for a in (box_o, mu_o, var_o))
+    sel = t.full((B, Hkv, MP), -1, dtype=t.int32, device="cuda")
+    cnt = t.full((B, Hkv), -1, dtype=t.int32, device="cuda")
+    if policy == "topk":
+        for k in (1, 5, 1000):
+            E.select_pages_topk_group(D.shape, box, D.sl, k, sel, cnt)
+            so, co = oracle.select_topk_group(D.oshape, box_o, inp.seq_lens, k)
+            assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+    else:
+        tau = t.full((B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+        E.select_pages_gauss_group(D.shape, box, mu, var, D.sl, 1.5, 0.5, sel, cnt, tau_hat=tau)
+        so, co, to = oracle.select_gauss_group(D.oshape, box_o, mu_o, var_o, inp.seq_lens, 1.5, 0.5)
+        assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+        assert np.allclose(tau.cpu().numpy(), to, rtol=1e-12, atol=1e-12)
+    for alpha in (1.5, 2.0):
+        _group_decode_check(inp, D, alpha, so, co)
+    _group_decode_check(inp, D, 2.0, so, co, tau_method=1)
+
+
+def test_group_decode_edge_cases(case):
+    """Empty, over-long, non-ascending and full group sets, as the oracle rules them."""
+    inp, D, _, _ = case
+    MP = inp.max_pages
+    sg = np.zeros((inp.B, inp.Hkv, MP), np.int32)
+    cg = np.zeros((inp.B, inp.Hkv), np.int32)
+    for b in range(inp.B):
+        np_b = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        for g in range(inp.Hkv):
+            kind = (b * inp.Hkv + g) % 4
+            if kind == 0:
+                cg[b, g] = 0
+            elif kind == 1:
+                cg[b, g] = np_b + 1
+                sg[b, g, :min(np_b + 1, MP)] = np.arange(min(np_b + 1, MP))
+            elif kind == 2 and np_b >= 2:
+                cg[b, g] = 2
+                sg[b, g, :2] = [1, 0]
+            else:
+                cg[b, g] = np_b
+                sg[b, g, :np_b] = np.arange(np_b)
+    _group_decode_check(inp, D, 1.5, sg, cg)

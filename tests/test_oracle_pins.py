@@ -341,6 +341,74 @@ def test_topk_vs_lexsort(orc):
                 assert np.array_equal(sel[b, h, :cnt[b, h]], want)
 
 
+def test_topk_group_vs_lexsort_of_head_max(orc):
+    rng = np.random.default_rng(17)
+    B, Hkv, G, mp = 2, 2, 3, 40
+    sh = orc.Shape(B, Hkv * G, Hkv, 64, 16, mp, 100, "bf16")
+    box = rng.standard_normal((B, Hkv * G, mp)).astype(np.float32)
+    box[0, 0:3, 10:20] = 0.5                    # ties across pages
+    box[0, 1, 5] = np.nan                       # one head's NaN: the others decide
+    box[1, 3:6, 7] = np.nan                     # every head NaN: ranks last
+    seq = np.array([16 * 40, 16 * 31 - 5], np.int32)
+    for k in (1, 6, 31, 64):
+        sel, cnt = orc.select_topk_group(sh, box, seq, k)
+        assert sel.shape == (B, Hkv, mp)
+        for b in range(B):
+            npg = (int(seq[b]) + 15) // 16
+            for g in range(Hkv):
+                blk = box[b, g * G:(g + 1) * G, :npg].astype(np.float64)
+                key = np.where(np.isnan(blk), -np.inf, blk).max(axis=0)
+                order = np.lexsort((np.arange(npg), -key))
+                want = np.sort(order[:min(k, npg)])
+                assert cnt[b, g] == len(want)
+                assert np.array_equal(sel[b, g, :cnt[b, g]], want)
+
+
+def test_group_selection_reduces_to_per_head_for_one_head_groups(orc):
+    inp = synth.random_small(8, B=2, Hq=3, Hkv=3, d=64, P=16, dtype="bf16", ctx=(900, 333), planted_per_kv=3)
+    sh = shape_of(inp, orc)
+    meta = orc.build_page_meta(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    box, mu, var = orc.score_pages(sh, inp.q, meta, inp.page_table, inp.seq_lens)
+    s1, c1 = orc.select_topk(sh, box, inp.seq_lens, 9)
+    s2, c2 = orc.select_topk_group(sh, box, inp.seq_lens, 9)
+    assert np.array_equal(c1, c2) and all(np.array_equal(s1[b, h, :c1[b, h]], s2[b, h, :c2[b, h]])
+                                          for b in range(2) for h in range(3))
+    s1, c1, t1 = orc.select_gauss(sh, box, mu, var, inp.seq_lens, 1.5, 0.5)
+    s2, c2, t2 = orc.select_gauss_group(sh, box, mu, var, inp.seq_lens, 1.5, 0.5)
+    assert np.array_equal(c1, c2) and np.array_equal(t1, t2)
+    assert all(np.array_equal(s1[b, h, :c1[b, h]], s2[b, h, :c2[b, h]]) for b in range(2) for h in range(3))
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_gauss_group_is_union_and_discards_less(orc, alpha):
+    inp = synth.random_small(9, B=2, Hq=8, Hkv=2, d=64, P=16, dtype="bf16", ctx=(2000, 700), planted_per_kv=8)
+    sh = shape_of(inp, orc)
+    G = inp.Hq // inp.Hkv
+    meta = orc.build_page_meta(sh, inp.k_pool, inp.page_table, inp.seq_lens)
+    box, mu, var = orc.score_pages(sh, inp.q, meta, inp.page_table, inp.seq_lens)
+    sh_, ch_, th_ = orc.select_gauss(sh, box, mu, var, inp.seq_lens, alpha, 0.0)
+    sg, cg, tg = orc.select_gauss_group(sh, box, mu, var, inp.seq_lens, alpha, 0.0)
+    assert np.array_equal(th_, tg)
+    _, _, wfull = orc.entmax_decode(sh, inp.q, inp.k_pool, inp.v_pool, inp.page_table, inp.seq_lens, alpha,
+                                    want_weights=True)
+    P = inp.P
+    for b in range(inp.B):
+        for g in range(inp.Hkv):
+            gset = set(sg[b, g, :cg[b, g]].tolist())
+            heads = [set(sh_[b, g * G + j, :ch_[b, g * G + j]].tolist()) for j in range(G)]
+            assert gset == set().union(*heads)
+            assert sg[b, g, :cg[b, g]].tolist() == sorted(gset)
+            for j in range(G):
+                h = g * G + j
+                w = wfull[b, h]
+                out_own = sum(w[p * P:(p + 1) * P].sum() for p in range(len(w) // P) if p not in heads[j])
+                out_grp = sum(w[p * P:(p + 1) * P].sum() for p in range(len(w) // P) if p not in gset)
+                assert out_grp <= out_own + 1e-15   # a superset of the kept pages discards less mass
+    # decoding over the group set is decoding each head over the expanded selection
+    se, ce = orc.expand_group_selection(sh, sg, cg)
+    assert se.shape == (inp.B, inp.Hq, inp.max_pages) and np.array_equal(ce[:, :G], np.repeat(cg[:, :1], G, 1))
+
+
 # ------------------------------------------------------------ Gaussian selector
 def test_gauss_polynomial_regime_closed_form(orc):
     # every quadrature node above tau: the rule is exact for the polynomial integrand
