@@ -94,6 +94,51 @@ __global__ __launch_bounds__(256) void group_union_kernel(Dims D, const int32_t 
   if (tid == 0) sel_cnt[gr] = listed;
 }
 
+// The same union with the page flags as a bitmap in LDS (one bit per page,
+// set with LDS atomic OR), compacted in one pass: thread t owns a run of
+// bitmap words, counts their bits, takes its first output slot from a block
+// scan and writes its pages in ascending order.  For rows whose bitmap fits
+// the LDS budget; group_union_kernel takes the others.
+__global__ __launch_bounds__(256) void group_union_lds_kernel(Dims D, int words, const int32_t *__restrict__ seq_lens,
+                                                              const uint8_t *__restrict__ seq_mask,
+                                                              const int32_t *__restrict__ hsel,
+                                                              const int32_t *__restrict__ hcnt,
+                                                              int32_t *__restrict__ sel_idx,
+                                                              int32_t *__restrict__ sel_cnt) {
+  extern __shared__ unsigned int bm[];  // [words]
+  __shared__ int scan_scratch[256 / kWave];
+  const int gr = blockIdx.x, b = gr / D.Hkv, g = gr % D.Hkv;
+  if (seq_mask && !seq_mask[b]) return;
+  const int np = n_pages_of(seq_len_clamped(seq_lens, b, D), D.P);
+  const int tid = threadIdx.x;
+  for (int w = tid; w < words; w += 256) bm[w] = 0u;
+  __syncthreads();
+  for (int h = 0; h < D.G; ++h) {
+    const size_t r = (size_t)b * D.Hq + (size_t)g * D.G + h;
+    const int c = min(max(hcnt[r], 0), np);
+    for (int i = tid; i < c; i += 256) {
+      const int p = hsel[r * D.max_pages + i];
+      if (p >= 0 && p < np) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+  const int per = (words + 255) / 256;
+  const int w0 = min(tid * per, words), w1 = min(w0 + per, words);
+  int mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(bm[w]);
+  int tot;
+  int at = block_excl_scan(mine, scan_scratch, &tot);
+  int32_t *out = sel_idx + (size_t)gr * D.max_pages;
+  for (int w = w0; w < w1; ++w) {
+    unsigned int bits = bm[w];
+    while (bits) {
+      out[at++] = w * 32 + (__ffs(bits) - 1);
+      bits &= bits - 1u;
+    }
+  }
+  if (tid == 0) sel_cnt[gr] = tot;
+}
+
 size_t topk_group_ws_bytes(const Dims &D) {
   Carve cv(nullptr);
   cv.take<float>((size_t)D.B * D.Hkv * D.max_pages);
@@ -138,8 +183,13 @@ hipError_t launch_gauss_group(const Dims &D, const float *box, const float *mu, 
                               gws, s);
   if (e != hipSuccess) return e;
   if (D.B * D.Hkv <= 0) return hipSuccess;
-  hipLaunchKernelGGL(group_union_kernel, dim3(D.B * D.Hkv), dim3(256), 0, s, D, seq_lens, seq_mask, hsel, hcnt,
-                     flags, sel_idx, sel_cnt);
+  const int words = (D.max_pages + 31) / 32;
+  if ((size_t)words * 4 <= 48 * 1024)
+    hipLaunchKernelGGL(group_union_lds_kernel, dim3(D.B * D.Hkv), dim3(256), (size_t)words * 4, s, D, words,
+                       seq_lens, seq_mask, hsel, hcnt, sel_idx, sel_cnt);
+  else
+    hipLaunchKernelGGL(group_union_kernel, dim3(D.B * D.Hkv), dim3(256), 0, s, D, seq_lens, seq_mask, hsel, hcnt,
+                       flags, sel_idx, sel_cnt);
   return hipGetLastError();
 }
 
