@@ -58,6 +58,7 @@ struct DecodeWs {
   uint32_t *iphys;   // [rows][max_pages]    physical page of item i
   int *segcnt;       // [rows][kSplitMax]    candidates of each chunk
   double *segL;      // [rows][kSplitMax]    each chunk's lower bound on tau
+  int *segn;         // [rows][kSplitMax][kNThr] each chunk's counts above mx - 2^-i
   unsigned int *ctr; // [rows]               arrival counters (zeroed by kernel 1)
 };
 
@@ -613,6 +614,11 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
     if (ci_ > 0) Lc = fmax(Lc, th[i] - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)));
   }
+  if (!alone && tid < kNThr) {  // the chunk's counts, summed over the row by the last block
+    int ct = 0;
+    for (int w = 0; w < kDThreads / kWave; ++w) ct += s_cnt[w][tid];
+    st_agent(&ws.segn[((size_t)r * kSplitMax + c) * kNThr + tid], ct);
+  }
   const bool lds_all = alone && nlds <= kCand;  // every candidate X > mx - 1 is in LDS
   int total = nlds;                              // entries in the workspace segments (tiers 1, 2)
   double L = Lc;
@@ -670,44 +676,61 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       sL[tid] = ld_agent(&ws.segL[(size_t)r * kSplitMax + tid]);
       sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
     }
+    // the row's counts above mx - 2^-i are the chunks' counts summed: a bound
+    // as certified as each chunk's and tighter (about sqrt(chunks) for alpha 1.5)
+    if (tid < kNThr) {
+      int ct = 0;
+      for (int s2 = 0; s2 < nsplit; ++s2) ct += ld_agent(&ws.segn[((size_t)r * kSplitMax + s2) * kNThr + tid]);
+      s_cnt[0][tid] = ct;
+    }
     __syncthreads();
     if (tid == 0) {
       soff[0] = 0;
       double lm = thr;
       for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
+      for (int i = 0; i < kNThr; ++i)
+        if (s_cnt[0][i] > 0)
+          lm = fmax(lm, (mx - ldexp(1.0, -i)) - pow_neg_a((double)s_cnt[0][i], dp) - 1e-12 * fmax(1.0, fabs(mx)));
       s_tau[0] = lm;
     }
     __syncthreads();
     total = soff[nsplit];
     L = s_tau[0];
     const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
+    // each thread takes 8 consecutive entries, so one block scan per 2048
+    // entries keeps the candidates in index order
     nlds = 0;
 #pragma unroll 1
-    for (int base = 0; base < total; base += 4 * kDThreads) {
-      double v[4];
-      uint32_t t[4];
+    for (int base = 0; base < total; base += 8 * kDThreads) {
+      const int k0 = base + 8 * tid;
+      double v[8];
+      uint32_t t[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int a = gs0.addr(min(base + u * kDThreads + tid, total - 1));
+      for (int u = 0; u < 8; ++u) {
+        const int a = gs0.addr(min(k0 + u, total - 1));
         v[u] = ld_agent(&xrow[a]);
         t[u] = ld_agent(&xir[a]);
       }
-      uint32_t ph[4];
+      uint32_t ph[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ph[u] = ipr[t[u] / P];
+      for (int u = 0; u < 8; ++u) ph[u] = ipr[t[u] / P];
+      int mine = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = base + u * kDThreads + tid;
-        const int take = (k < total && v[u] > L) ? 1 : 0;
-        int tot;
-        const int at = nlds + block_excl_scan(take, scan_scratch, &tot);
-        if (take && at < kCand) {
-          cx[at] = v[u];
-          ci[at] = (int)t[u];
-          cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
+      for (int u = 0; u < 8; ++u) mine += (k0 + u < total && v[u] > L) ? 1 : 0;
+      int tot;
+      int at = nlds + block_excl_scan(mine, scan_scratch, &tot);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < total && v[u] > L) {
+          if (at < kCand) {
+            cx[at] = v[u];
+            ci[at] = (int)t[u];
+            cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
+          }
+          ++at;
         }
-        nlds += tot;
       }
+      nlds += tot;
     }
   } else if (tid == 0) {
     soff[0] = 0;
@@ -868,6 +891,7 @@ static DecodeWs carve_decode(const Dims &D, void *base, size_t *bytes) {
   w.iphys = cv.take<uint32_t>(rows * D.max_pages);
   w.segcnt = cv.take<int>(rows * kSplitMax);
   w.segL = cv.take<double>(rows * kSplitMax);
+  w.segn = cv.take<int>(rows * kSplitMax * kNThr);
   w.ctr = cv.take<unsigned int>(rows);
   if (bytes) *bytes = cv.bytes();
   return w;
