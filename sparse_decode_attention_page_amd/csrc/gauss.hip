@@ -337,10 +337,10 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   // ---- last block of the row: merge chunks in order, suffix-scan the moments
   for (int i = threadIdx.x; i < kNB; i += kGThreads) {
     double a0 = 0.0, a1 = 0.0, a2 = 0.0;
-    for (int c0 = 0; c0 < rc.nch; c0 += 8) {  // batches of 8 chunks: one round trip each
-      double v[8][3];
+    for (int c0 = 0; c0 < rc.nch; c0 += 16) {  // batches of 16 chunks: one round trip each
+      double v[16][3];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int c = min(c0 + u, rc.nch - 1);
         const double *hh = ws.hist + ((size_t)rc.row * gp.nchunk + c) * kNB * 3 + i * 3;
         v[u][0] = ld_agent(&hh[0]);
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
         v[u][2] = ld_agent(&hh[2]);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         if (c0 + u < rc.nch) { a0 += v[u][0]; a1 += v[u][1]; a2 += v[u][2]; }
       }
     }
@@ -358,23 +358,51 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   }
   __syncthreads();
   EKV_MARK(1, 4);
-  // inclusive suffix scan: S_b = m_b (+) shift(S_{b+d}, e_{b+d} -> e_b)
-  for (int dist = 1; dist < kNB; dist <<= 1) {
-    double n0 = 0, n1 = 0, n2 = 0;
-    const int i = threadIdx.x;
-    const bool has = i < kNB && i + dist < kNB;
-    if (i < kNB) {
-      n0 = s0[i]; n1 = s1[i]; n2 = s2[i];
-      if (has) {
+  // inclusive suffix scan, S_b = m_b (+) shift(S_{b+1}, e_{b+1} -> e_b) with
+  // shift(M, e' -> e) = (M0, M1 + D M0, M2 + 2 D M1 + D^2 M0), D = e' - e
+  // (associative): within each wave by shuffles, then each lane adds the
+  // higher waves' suffix, combined top-down in a fixed order, shifted to its
+  // edge.  One thread per bin (kGThreads == kNB).
+  {
+    static_assert(kGThreads == kNB, "one thread per bin");
+    __shared__ double hd[kNB / kWave][3];  // each wave's own suffix at its first bin
+    const int i = threadIdx.x, lane = i & (kWave - 1), wv = i / kWave;
+    double n0 = s0[i], n1 = s1[i], n2 = s2[i];
+#pragma unroll
+    for (int dist = 1; dist < kWave; dist <<= 1) {
+      const double t0 = __shfl_down(n0, dist, kWave), t1 = __shfl_down(n1, dist, kWave),
+                   t2 = __shfl_down(n2, dist, kWave);
+      if (lane + dist < kWave) {
         const double Dd = bin_edge(lo, w, i + dist) - bin_edge(lo, w, i);
-        const double t0 = s0[i + dist], t1 = s1[i + dist], t2 = s2[i + dist];
         n0 += t0;
         n1 += t1 + Dd * t0;
         n2 += t2 + 2.0 * Dd * t1 + Dd * Dd * t0;
       }
     }
+    if (lane == 0) { hd[wv][0] = n0; hd[wv][1] = n1; hd[wv][2] = n2; }
     __syncthreads();
-    if (i < kNB) { s0[i] = n0; s1[i] = n1; s2[i] = n2; }
+    // suffix of the waves above this one, about the edge of the next wave's first bin
+    double h0 = 0.0, h1 = 0.0, h2 = 0.0;
+    for (int v = kNB / kWave - 1; v > wv; --v) {
+      if (v < kNB / kWave - 1) {  // shift the running suffix from e_{64(v+1)} to e_{64 v}
+        const double Dd = bin_edge(lo, w, (v + 1) * kWave) - bin_edge(lo, w, v * kWave);
+        h2 = h2 + 2.0 * Dd * h1 + Dd * Dd * h0;
+        h1 = h1 + Dd * h0;
+      }
+      h0 += hd[v][0];
+      h1 += hd[v][1];
+      h2 += hd[v][2];
+    }
+    if (wv < kNB / kWave - 1) {
+      const double Dd = bin_edge(lo, w, (wv + 1) * kWave) - bin_edge(lo, w, i);
+      n0 += h0;
+      n1 += h1 + Dd * h0;
+      n2 += h2 + 2.0 * Dd * h1 + Dd * Dd * h0;
+    }
+    __syncthreads();
+    s0[i] = n0;
+    s1[i] = n1;
+    s2[i] = n2;
     __syncthreads();
   }
   // F(e_b) = s2[b] (beta 2) or s1[b] (beta 1); root bin = largest b with F >= 1
