@@ -607,12 +607,18 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   if ((tid & (kWave - 1)) == 0)
     for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = cnt8[i];
   __syncthreads();
-  double Lc = thr;
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) {
+  // lane i (mod kNThr) evaluates threshold i's bound and a wave max combines
+  // them: one reciprocal power per lane instead of kNThr in sequence (a chain
+  // of dependent fp64 operations that dominates this phase otherwise)
+  double Lc;
+  {
+    static_assert((kNThr & (kNThr - 1)) == 0, "kNThr is a power of two");
+    const int i = tid & (kNThr - 1);
     int ci_ = 0;
     for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
-    if (ci_ > 0) Lc = fmax(Lc, th[i] - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)));
+    const double cand =
+        ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+    Lc = fmax(thr, wave_max(cand));
   }
   if (!alone && tid < kNThr) {  // the chunk's counts, summed over the row by the last block
     int ct = 0;
@@ -684,14 +690,18 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       s_cnt[0][tid] = ct;
     }
     __syncthreads();
-    if (tid == 0) {
-      soff[0] = 0;
-      double lm = thr;
-      for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
-      for (int i = 0; i < kNThr; ++i)
-        if (s_cnt[0][i] > 0)
-          lm = fmax(lm, (mx - ldexp(1.0, -i)) - pow_neg_a((double)s_cnt[0][i], dp) - 1e-12 * fmax(1.0, fabs(mx)));
-      s_tau[0] = lm;
+    if (tid < kWave) {  // lane i (mod kNThr): threshold i's bound from the summed count
+      const int i = tid & (kNThr - 1);
+      const int ct = s_cnt[0][i];
+      const double cand =
+          ct > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ct, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+      const double cmax = wave_max(cand);
+      if (tid == 0) {
+        soff[0] = 0;
+        double lm = fmax(thr, cmax);
+        for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
+        s_tau[0] = lm;
+      }
     }
     __syncthreads();
     total = soff[nsplit];
