@@ -427,6 +427,52 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   EKV_MARK(1, 5);
 }
 
+// F = 1 inside the root bin [ek, ek1] for rows with at most kWave * kBinReg
+// in-bin points, on one wave (no block barriers): Newton from the left, and
+// each pass also solves its piece exactly.  With A the in-bin points above t
+// and every point of the bins above active (moments T about ek1),
+// F(t + u) = f - fp u + q u^2 (beta 2, q = sum_A c + T0) or f - fp u (beta 1)
+// until u reaches the nearest active in-bin point; the smaller root of
+// F(t + u) = 1, when it stays below that point and inside the bin, is F's root.
+constexpr int kBinReg = 8;
+__device__ double bin_root_wave(const double (&v)[kBinReg], const double (&c)[kBinReg], double ek, double ek1,
+                                double T0, double T1, double T2, int ibeta) {
+  double t = ek;
+#pragma unroll 1
+  for (int it = 0; it < 200; ++it) {
+    double f = 0.0, fp = 0.0, qa = 0.0, nmn = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBinReg; ++u) {
+      const double x = v[u] - t;
+      if (x > 0.0) {
+        if (ibeta == 2) { f += c[u] * x * x; fp += 2.0 * c[u] * x; }
+        else { f += c[u] * x; fp += c[u]; }
+        qa += c[u];
+        nmn = fmax(nmn, -x);
+      }
+    }
+    f = wave_sum(f);
+    fp = wave_sum(fp);
+    qa = wave_sum(qa);
+    nmn = wave_max(nmn);
+    const double Dd = ek1 - t;  // >= 0
+    if (ibeta == 2) { f += T2 + 2.0 * Dd * T1 + Dd * Dd * T0; fp += 2.0 * T1 + 2.0 * Dd * T0; }
+    else { f += T1 + Dd * T0; fp += T0; }
+    if (!(fp > 0.0)) break;
+    if (f > 1.0) {
+      const double q = qa + T0;
+      const double u = ibeta == 2 ? (f - 1.0) / (0.5 * fp + sqrt(fmax(0.25 * fp * fp - q * (f - 1.0), 0.0)))
+                                  : (f - 1.0) / fp;
+      if (u <= -nmn && t + u <= ek1) return t + u;
+    }
+    double tn = t + (f - 1.0) / fp;
+    if (tn > ek1) tn = ek1;
+    if (!(tn > t)) break;  // converged from the left (or rounding stalls)
+    t = tn;
+  }
+  return t;
+}
+
 // --------------------------------------- K3: collect, classify, solve, compact
 __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     Dims D, GaussParams gp, GaussConsts gc, const float *__restrict__ box, const float *__restrict__ mu,
@@ -434,7 +480,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     const uint8_t *__restrict__ seq_mask, int32_t *__restrict__ sel_idx, int32_t *__restrict__ sel_cnt,
     double *__restrict__ tau_hat, GaussWs ws) {
   __shared__ int scan_scratch[kGThreads / kWave];
-  __shared__ double dred[2 * kGThreads / kWave];
+  __shared__ double dred[3 * kGThreads / kWave];  // up to three block sums at once
   __shared__ double s_best_est;
   __shared__ int s_best_p, s_last;
   const int chunk = blockIdx.x;
@@ -568,12 +614,33 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   if (!arrive_last(&ws.ctr[rc.row * 2 + 1], (unsigned)rc.nch, &s_last)) return;
   EKV_MARK(2, 3);
 
-  // ---- last block of the row: solve F(t) = 1 inside [ek, ek1].  The in-bin
-  // points are staged in registers once (kInReg per thread), any excess is
-  // re-read in batches.
+  // ---- last block of the row: solve F(t) = 1 inside [ek, ek1].  Up to
+  // kWave * kBinReg in-bin points: one wave holds them in registers and solves
+  // alone; more: the block holds kInReg per thread, any excess re-read per pass.
   const int nin = min(ld_agent(&ws.inbin_cnt[rc.row]), gp.cap);
   const double T0 = ri[3], T1 = ri[4], T2 = ri[5];
   const double *inb = ws.inbin + (size_t)rc.row * gp.cap * 2;
+  EKV_MARK(2, 4);
+  __shared__ double s_tbin;
+  double t = ek;
+  if (nin <= kWave * kBinReg) {
+    if (threadIdx.x < kWave) {
+      double wv[kBinReg], wc[kBinReg];
+#pragma unroll
+      for (int u = 0; u < kBinReg; ++u) {  // lane-strided copies of the points staged above
+        const int i = u * kWave + (int)threadIdx.x;
+        const int ic = min(i, max(nin - 1, 0));
+        const double v = ld_agent(&inb[ic * 2 + 0]), c = ld_agent(&inb[ic * 2 + 1]);
+        wv[u] = i < nin ? v : -INFINITY;
+        wc[u] = i < nin ? c : 0.0;
+      }
+      const double tw = bin_root_wave(wv, wc, ek, ek1, T0, T1, T2, gp.ibeta);
+      if (threadIdx.x == 0) s_tbin = tw;
+    }
+    __syncthreads();
+    t = s_tbin;
+  } else {
+  // more points: the block holds kInReg per thread, any excess is re-read per pass
   constexpr int kInReg = 8;
   double rv[kInReg], rcw[kInReg];
 #pragma unroll
@@ -584,30 +651,49 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
     rv[u] = i < nin ? v : -INFINITY;
     rcw[u] = i < nin ? c : 0.0;
   }
-  EKV_MARK(2, 4);
-  double t = ek;
+  // Newton from the left, and each pass also solves its piece exactly: with
+  // A the in-bin points above t and every point of the bins above active,
+  // F(t + u) = f - fp u + q u^2 (beta 2, q = sum_A c + T0) or f - fp u
+  // (beta 1) until u reaches the nearest active in-bin point, so the smaller
+  // root u of F(t + u) = 1, when it stays below that point and inside the
+  // bin, is F's root and ends the search.
   for (int it = 0; it < 200; ++it) {
-    double f = 0.0, fp = 0.0;
+    double sm[3] = {0.0, 0.0, 0.0};  // f, fp, sum_A c over the in-bin points
+    double nmn = -INFINITY;          // -(distance to the nearest active in-bin point)
     auto acc_pt = [&](double v, double c) {
       const double x = v - t;
       if (x > 0.0) {
-        if (gp.ibeta == 2) { f += c * x * x; fp += 2.0 * c * x; }
-        else { f += c * x; fp += c; }
+        if (gp.ibeta == 2) { sm[0] += c * x * x; sm[1] += 2.0 * c * x; }
+        else { sm[0] += c * x; sm[1] += c; }
+        sm[2] += c;
+        nmn = fmax(nmn, -x);
       }
     };
 #pragma unroll
     for (int u = 0; u < kInReg; ++u) acc_pt(rv[u], rcw[u]);
     for (int i = kInReg * kGThreads + threadIdx.x; i < nin; i += kGThreads)
       acc_pt(ld_agent(&inb[i * 2 + 0]), ld_agent(&inb[i * 2 + 1]));
-    block_sum2(f, fp, dred);
+    block_sum_n<3>(sm, dred);
+    nmn = block_max(nmn, dred);
+    double f = sm[0], fp = sm[1];
     const double Dd = ek1 - t;  // >= 0
     if (gp.ibeta == 2) { f += T2 + 2.0 * Dd * T1 + Dd * Dd * T0; fp += 2.0 * T1 + 2.0 * Dd * T0; }
     else { f += T1 + Dd * T0; fp += T0; }
     if (!(fp > 0.0)) break;
+    if (f > 1.0) {
+      const double q = sm[2] + T0;
+      const double u = gp.ibeta == 2 ? (f - 1.0) / (0.5 * fp + sqrt(fmax(0.25 * fp * fp - q * (f - 1.0), 0.0)))
+                                     : (f - 1.0) / fp;
+      if (u <= -nmn && t + u <= ek1) {
+        t = t + u;
+        break;
+      }
+    }
     double tn = t + (f - 1.0) / fp;
     if (tn > ek1) tn = ek1;
     if (!(tn > t)) break;  // converged from the left (or rounding stalls)
     t = tn;
+  }
   }
   const double tau = t;
   if (threadIdx.x == 0) {
