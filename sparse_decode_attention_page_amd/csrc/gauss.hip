@@ -274,6 +274,12 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   EKV_MARK(1, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
   if (!rc.active || chunk >= rc.nch) return;
+  const size_t base = (size_t)rc.row * D.max_pages;
+  const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  // the first pages' statistics are requested before the bracket, so the two
+  // round trips overlap
+  Pages4 pg0;
+  pg0.load(box, mu, var, base, chunk * gp.chunk + 4 * threadIdx.x, p_end);
   double lo, hi;
   row_bracket(gp, ws, rc, lo, hi);
   if (!(hi > -INFINITY)) return;  // no valid page in the row
@@ -282,8 +288,6 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
   const double sqrt2 = 1.4142135623730951;
   for (int i = threadIdx.x; i < kNB; i += kGThreads) h0[i] = h1[i] = h2[i] = 0.0;
   __syncthreads();
-  const size_t base = (size_t)rc.row * D.max_pages;
-  const int p_end = min(rc.np, (chunk + 1) * gp.chunk);
   // Each thread takes 4 consecutive pages and walks the nodes from the top
   // (a wave-uniform index, so the node constants sit in scalar registers);
   // the 4 pages advance together for instruction-level parallelism, and a
@@ -291,8 +295,8 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
 #pragma unroll 1
   for (int p0 = chunk * gp.chunk; p0 < p_end; p0 += 4 * kGThreads) {
     const int pb = p0 + 4 * threadIdx.x;
-    Pages4 pg;
-    pg.load(box, mu, var, base, pb, p_end);
+    Pages4 pg = pg0;
+    if (p0 != chunk * gp.chunk) pg.load(box, mu, var, base, pb, p_end);
     double mm[4], sg[4], nn[4];
     bool act[4];
 #pragma unroll
@@ -302,25 +306,36 @@ __global__ __launch_bounds__(kGThreads) void gauss_hist_kernel(Dims D, GaussPara
       sg[u] = sqrt(pg.v2[u] > 0.0f ? (double)pg.v2[u] : 0.0);
       nn[u] = (double)min(D.P, rc.L - (pb + u) * D.P);
     }
-#pragma unroll 1
+    // The four pages' chains are computed side by side without branches (a
+    // page past its last node yields a value that is simply not added), and
+    // the node loop is unrolled so its constants are loaded up front: a
+    // scalar load inside the loop would make every pass wait for the LDS
+    // atomics before it (both count in the same wait counter).
+#pragma unroll
     for (int j = 15; j >= 0; --j) {
       const double xj = gc.x[j], wj = gc.w[j];
-      bool any = false;
+      double v[4], e[4], c[4];
+      int hs[4];
+      bool in[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (!act[u]) continue;
-        const double v = gh_point(gp.a, mm[u], sg[u], xj);
-        if (!(v > lo)) { act[u] = false; continue; }
-        any = true;
-        const int bn = bin_of(v, lo, iw);
-        const double e = v - bin_edge(lo, w, bn);
-        const double c = nn[u] * wj;
-        const int hs = hslot(bn);
-        atomicAdd(&h0[hs], c);
-        atomicAdd(&h1[hs], c * e);
-        if (gp.ibeta == 2) atomicAdd(&h2[hs], c * e * e);
+        v[u] = gh_point(gp.a, mm[u], sg[u], xj);
+        in[u] = act[u] && v[u] > lo;
+        act[u] = in[u];
+        const int bn = bin_of(in[u] ? v[u] : lo, lo, iw);
+        e[u] = v[u] - bin_edge(lo, w, bn);
+        c[u] = nn[u] * wj;
+        hs[u] = hslot(bn);
       }
-      if (!__any(any)) break;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (in[u]) {
+          atomicAdd(&h0[hs[u]], c[u]);
+          atomicAdd(&h1[hs[u]], c[u] * e[u]);
+          if (gp.ibeta == 2) atomicAdd(&h2[hs[u]], c[u] * e[u] * e[u]);
+        }
+      }
+      if (!__any(in[0] || in[1] || in[2] || in[3])) break;
     }
   }
   __syncthreads();
@@ -487,9 +502,16 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   EKV_MARK(2, 0);
   const RowCtx rc = row_ctx(D, gp, seq_lens, seq_mask, blockIdx.y);
   if (!rc.active) return;
+  const size_t base = (size_t)rc.row * D.max_pages;
+  const int p_begin = chunk * gp.chunk, p_end = min(rc.np, (chunk + 1) * gp.chunk);
+  // independent reads first, so their round trips overlap: this chunk's first
+  // page statistics, the root bin and width, the bracket
+  Pages4 pg0;
+  if (chunk < rc.nch) pg0.load(box, mu, var, base, p_begin + 4 * threadIdx.x, p_end);
+  const double *ri = ws.rowinfo + (size_t)rc.row * 8;
+  const double ri_k = ri[0], ri_w = ri[2];
   double lo, hi;
   row_bracket(gp, ws, rc, lo, hi);
-  const size_t base = (size_t)rc.row * D.max_pages;
   if (!(hi > -INFINITY)) {  // no pages (or none valid): empty selection
     if (chunk == 0 && threadIdx.x == 0) {
       sel_cnt[rc.row] = 0;
@@ -499,15 +521,13 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
   }
   if (chunk >= rc.nch) return;
   EKV_MARK(2, 1);
-  const double *ri = ws.rowinfo + (size_t)rc.row * 8;
-  const int k = (int)ri[0];
-  const double w = ri[2], iw = 1.0 / w;
+  const int k = (int)ri_k;
+  const double w = ri_w, iw = 1.0 / w;
   const double ek = bin_edge(lo, w, k), ek1 = bin_edge(lo, w, k + 1);
   const double thr_lo = ek / gp.a - gp.delta, thr_hi = ek1 / gp.a - gp.delta;
   const double sqrt2 = 1.4142135623730951;
 
   // ---- collect in-bin points and classify this chunk's pages (ascending order)
-  const int p_begin = chunk * gp.chunk, p_end = min(rc.np, (chunk + 1) * gp.chunk);
   int listed = 0;
   double best = -INFINITY;
   int bestp = 0x7FFFFFFF;
@@ -517,8 +537,8 @@ __global__ __launch_bounds__(kGThreads) void gauss_select_kernel(
 #pragma unroll 1
   for (int p0 = p_begin; p0 < p_end; p0 += 4 * kGThreads) {
     const int pb = p0 + 4 * threadIdx.x;
-    Pages4 pg;
-    pg.load(box, mu, var, base, pb, p_end);
+    Pages4 pg = pg0;
+    if (p0 != p_begin) pg.load(box, mu, var, base, pb, p_end);
     double mm[4], sg[4], s2d[4], nn[4];
     bool valid[4], act[4];
     int code[4];
