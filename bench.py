@@ -286,9 +286,10 @@ def main():
         f"stream read {stream_gbs:.0f} GB/s")
 
     # ---- streaming decode: one graph per step appends the new token's K and V
-    # to its page, rebuilds that page's metadata, then scores, selects and
-    # decodes with the context one token longer (the context grows from
-    # L - n_total to L over the replays); on copies of replica 0
+    # to its page and rebuilds that page's metadata (append_token, one launch),
+    # then scores, selects and decodes with the context one token longer (the
+    # context grows from L - n_total to L over the replays); on copies of
+    # replica 0
     stream_res = None
     if not args.no_stream:
         try:
@@ -297,18 +298,12 @@ def main():
             seq2 = (sl - (n_st + n_wu + 1)).clamp(min=1).to(torch.int32)
             knew = torch.randn((B, Hkv, d), device=dev).to(k2.dtype)
             vnew = torch.randn((B, Hkv, d), device=dev).to(v2.dtype)
-            ptl = pt.long()
             sel3, cnt3 = torch.empty_like(sel), torch.empty_like(cnt)
             out3 = torch.empty_like(out)
 
             def stream_step():
                 seq2.add_(1)
-                pos = (seq2 - 1).long()
-                ph = torch.gather(ptl, 1, (pos // P).unsqueeze(1)).squeeze(1)
-                slot = pos % P
-                k2[ph, :, slot, :] = knew
-                v2[ph, :, slot, :] = vnew
-                E.build_page_meta(shape, k2, pt, seq2, meta2, from_token=(seq2 - 1))
+                E.append_token(shape, knew, vnew, k2, v2, pt, seq2, meta2)
                 E.score_pages(shape, reps[0][0], meta2, pt, seq2, box, mu, var, ws=ws_s)
                 if args.policy == "gauss":
                     E.select_pages_gauss(shape, box, mu, var, seq2, alpha, wl.delta, sel3, cnt3, ws=ws_g)
@@ -338,9 +333,29 @@ def main():
             L_end = int(seq2.max().item())
             stream_res = {"us_per_step": round(st_us, 3), "steps": n_st,
                           "context_end": L_end, "context_start": L_end - n_st,
-                          "step": "K/V append (torch index_put) + build_page_meta append + score_pages + "
+                          "step": "append_token (K/V row + page metadata) + score_pages + "
                                   "select_pages_" + args.policy + " + entmax_decode_sparse, one HIP graph per step"}
-            log(f"[bench] streaming step (append + metadata + step): {st_us:.2f} us")
+            # append_token's own launch duration: a graph of 20 launches (the
+            # same token rewritten, so every launch does the same work)
+            gap = torch.cuda.CUDAGraph()
+            s3.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s3):
+                with torch.cuda.graph(gap, stream=s3):
+                    for _ in range(20):
+                        E.append_token(shape, knew, vnew, k2, v2, pt, seq2, meta2)
+            torch.cuda.current_stream().wait_stream(s3)
+            gap.replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(5):
+                gap.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ap_us = a.elapsed_time(b) * 1e3 / 100
+            stream_res["append_token_us"] = round(ap_us, 2)
+            log(f"[bench] streaming step (append + metadata + step): {st_us:.2f} us; append_token per launch "
+                f"(graph of 20): {ap_us:.2f} us")
             del k2, v2, meta2
         except Exception as e:  # capture unsupported
             log(f"[bench] streaming step failed ({e})")

@@ -24,7 +24,7 @@ F32, BF16 = 0, 1
 (CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE,
  CALL_TOPK_GROUP, CALL_GAUSS_GROUP, CALL_DECODE_GROUP) = range(1, 11)
 
-EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_f8",
+EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_f8", "append_token",
            "select_pages_topk", "select_pages_gauss", "select_pages_topk_group", "select_pages_gauss_group",
            "entmax_decode_sparse_group",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
@@ -69,6 +69,8 @@ def load(path: str | None = None):
     lib.build_page_meta.argtypes = [sh, vp, vp, vp, vp, vp, vp]
     lib.score_pages.restype = i32
     lib.score_pages.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.append_token.restype = i32
+    lib.append_token.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.build_page_meta_f8.restype = i32
     lib.build_page_meta_f8.argtypes = [sh, vp, vp, vp, vp, vp, vp]
     lib.score_pages_f8.restype = i32
@@ -221,6 +223,21 @@ def build_page_meta_f8(shape: Shape, k_pool, page_table, seq_lens, meta, from_to
                                    _ptr(from_token, torch.int32, "from_token"), _meta_f8(shape, meta),
                                    _stream(stream))
     _check("build_page_meta_f8", st)
+    return meta
+
+
+def append_token(shape: Shape, k_new, v_new, k_pool, v_pool, page_table, seq_lens, meta, compact=False,
+                 stream=None):
+    """Write token seq_lens[b] - 1's K and V rows (k_new / v_new [B, Hkv, d]) into the pools and
+    rebuild that page's metadata (compact records when compact=True)."""
+    torch = _torch()
+    kd = _kv_dtype(shape)
+    st = load().append_token(ctypes.byref(shape), _ptr(k_new, kd, "k_new"), _ptr(v_new, kd, "v_new"),
+                             _ptr(k_pool, kd, "k_pool"), _ptr(v_pool, kd, "v_pool"),
+                             _ptr(page_table, torch.int32, "page_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+                             _meta_f8(shape, meta) if compact else _ptr(meta, kd, "meta"), 1 if compact else 0,
+                             _stream(stream))
+    _check("append_token", st)
     return meta
 
 

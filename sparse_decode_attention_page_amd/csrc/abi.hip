@@ -216,6 +216,20 @@ int32_t build_page_meta_f8(const entmaxkv_shape *shape, const void *k_pool, cons
   return hip_status(launch_build_meta(D, shape->dtype, true, k_pool, page_table, seq_lens, from_token, meta, stream));
 }
 
+int32_t append_token(const entmaxkv_shape *shape, const void *k_new, const void *v_new, void *k_pool,
+                     void *v_pool, const int32_t *page_table, const int32_t *seq_lens, void *meta,
+                     int32_t meta_format, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!k_new || !v_new || !k_pool || !v_pool || !page_table || !seq_lens || !meta)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (meta_format != 0 && meta_format != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (meta_format == 1 && shape->dtype != ENTMAXKV_BF16) return ENTMAXKV_ERR_UNSUPPORTED;
+  return hip_status(launch_append_token(D, shape->dtype, meta_format == 1, k_new, v_new, k_pool, v_pool, page_table,
+                                        seq_lens, meta, stream));
+}
+
 int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta,
                     const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                     float *var, void *ws, size_t ws_bytes, hipStream_t stream) {

@@ -38,6 +38,10 @@ hipError_t launch_build_meta(const Dims &D, int dtype, bool f8, const void *k_po
                              const int32_t *seq_lens, const int32_t *from_token, void *meta,
                              hipStream_t s);
 
+hipError_t launch_append_token(const Dims &D, int dtype, bool f8, const void *k_new, const void *v_new, void *k_pool,
+                               void *v_pool, const int32_t *page_table, const int32_t *seq_lens, void *meta,
+                               hipStream_t s);
+
 size_t score_ws_bytes(const Dims &D);
 hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const void *meta,
                         const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,

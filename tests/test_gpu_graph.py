@@ -8,9 +8,10 @@ Two graphs on a 8,192-token, 32/8-head, bf16 slice with pages of 16:
   is overwritten eagerly, and the replay's page sets, counts and outputs are
   compared with an eager run on the same query;
 * the streaming step of the EntmaxKV summary (section 2, pages' metadata kept
-  up to date as they fill): append one token's K and V to its page, rebuild
-  that page's metadata from the new token on, then score, select and decode
-  with the context one token longer.  Four replays grow the context by four
+  up to date as they fill): append one token's K and V to its page and rebuild
+  that page's metadata (append_token, or torch writes + build_page_meta from
+  the new token), then score, select and decode with the context one token
+  longer.  Four replays grow the context by four
   tokens; a copy driven eagerly takes the same steps, and metadata, sets and
   outputs must agree after every replay.
 
@@ -123,7 +124,8 @@ def test_graph_replays_match_eager_step(policy):
         _close(gstep.out, estep.out, tag)
 
 
-def test_graph_streaming_step_matches_eager():
+@pytest.mark.parametrize("append", ["append_token", "torch_index_put"])
+def test_graph_streaming_step_matches_eager(append):
     import torch
     wl, inp, shape, meta = _inputs(12)
     alpha, P = wl.alphas[0], inp.P
@@ -144,12 +146,15 @@ def test_graph_streaming_step_matches_eager():
 
         def __call__(self):
             self.seq.add_(1)
-            pos = (self.seq - 1).long()
-            ph = torch.gather(ptl, 1, (pos // P).unsqueeze(1)).squeeze(1)
-            slot = pos % P
-            self.k[ph, :, slot, :] = knew
-            self.v[ph, :, slot, :] = vnew
-            E.build_page_meta(shape, self.k, inp.page_table, self.seq, self.meta, from_token=self.seq - 1)
+            if append == "append_token":
+                E.append_token(shape, knew, vnew, self.k, self.v, inp.page_table, self.seq, self.meta)
+            else:
+                pos = (self.seq - 1).long()
+                ph = torch.gather(ptl, 1, (pos // P).unsqueeze(1)).squeeze(1)
+                slot = pos % P
+                self.k[ph, :, slot, :] = knew
+                self.v[ph, :, slot, :] = vnew
+                E.build_page_meta(shape, self.k, inp.page_table, self.seq, self.meta, from_token=self.seq - 1)
             self.step(inp.q, self.k, self.v, self.meta, inp.page_table, self.seq)
 
     gs, es = Stream(), Stream()

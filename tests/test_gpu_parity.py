@@ -8,7 +8,7 @@ thresholds agree to 1e-12 relative.
 import numpy as np
 import pytest
 
-from gpu_util import TOL, Dev, decode_check, host_raw, rel_l2_rows, sets_equal, torch
+from gpu_util import TOL, Dev, decode_check, dev, host_raw, rel_l2_rows, sets_equal, torch
 from sparse_decode_attention_page_amd import synth
 import sparse_decode_attention_page_amd as E
 import oracle
@@ -313,3 +313,49 @@ def test_group_decode_edge_cases(case):
                 cg[b, g] = np_b
                 sg[b, g, :np_b] = np.arange(np_b)
     _group_decode_check(inp, D, 1.5, sg, cg)
+
+
+# ------------------------------------------------------------ streaming append
+@pytest.mark.parametrize("compact", [False, True])
+def test_append_token(case, compact):
+    """append_token writes token L_b - 1 into its slot and rebuilds that page's
+    record: pools and metadata bit-exact against the pools updated on the host
+    and the oracle's rebuild from that token; a sequence whose page entry is
+    out of range stays untouched."""
+    inp, D, _, _ = case
+    t = torch()
+    if compact and inp.dtype != "bf16":
+        with pytest.raises(E.EntmaxKVError, match="status 2"):
+            rows = D.q[:, :inp.Hkv].contiguous()
+            E.append_token(D.shape, rows, rows, D.k.clone(), D.v.clone(), D.pt, D.sl, E.meta_f8_empty(D.shape),
+                           compact=True)
+        return
+    rng = np.random.default_rng(31)
+    B, Hkv, d, P = inp.B, inp.Hkv, inp.d, inp.P
+    kn = synth._store(rng.standard_normal((B, Hkv, d), dtype=np.float32), inp.dtype)
+    vn = synth._store(rng.standard_normal((B, Hkv, d), dtype=np.float32), inp.dtype)
+    pt = inp.page_table.copy()
+    if B > 1:  # the last sequence's newest page: an out-of-range entry
+        pt[B - 1, (int(inp.seq_lens[B - 1]) - 1) // P] = inp.num_phys
+    k_exp, v_exp = inp.k_pool.copy(), inp.v_pool.copy()
+    for b in range(B):
+        L = int(inp.seq_lens[b])
+        ph = pt[b, (L - 1) // P]
+        if L >= 1 and 0 <= ph < inp.num_phys:
+            k_exp[ph, :, (L - 1) % P, :] = kn[b]
+            v_exp[ph, :, (L - 1) % P, :] = vn[b]
+    build = oracle.build_page_meta_f8 if compact else oracle.build_page_meta
+    meta0 = build(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens)
+    from_tok = np.maximum(inp.seq_lens - 1, 0).astype(np.int32)
+    meta_exp = build(D.oshape, k_exp, pt, inp.seq_lens, from_token=from_tok, meta=meta0.copy())
+    kind = D.kind
+    k, v = D.k.clone(), D.v.clone()
+    if compact:
+        meta = t.from_numpy(meta0.copy()).cuda()
+    else:
+        meta = D.zeros_meta()
+        E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta)
+    E.append_token(D.shape, dev(kn, kind), dev(vn, kind), k, v, dev(pt, "i32"), D.sl, meta, compact=compact)
+    assert np.array_equal(host_raw(k, inp.dtype), k_exp) and np.array_equal(host_raw(v, inp.dtype), v_exp)
+    got = meta.cpu().numpy() if compact else host_raw(meta, inp.dtype)
+    assert np.array_equal(got, meta_exp)
