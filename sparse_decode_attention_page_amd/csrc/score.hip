@@ -41,6 +41,7 @@ namespace ekv {
 constexpr int kTilePages = 64;      // one page per lane
 constexpr int kScoreThreads = 256;  // four waves: one per metadata row kind
 constexpr int kScoreTiles = 2;      // tiles per block
+static_assert(kScoreTiles * kTilePages <= kScoreThreads, "one page id per thread in the prologue");
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -83,10 +84,6 @@ struct ScoreCfg {
   static constexpr int kRecBytes = F8 ? 6 * DIM : 4 * DIM * (int)sizeof(T);
   static constexpr int kTileBytes = kTilePages * kRecBytes;
   static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
-  // the second tile is requested once the first is in LDS: with both in flight from
-  // the start the per-tile latency grows with the deeper memory queue and the first
-  // tile arrives later (measured on cold HBM)
-  static constexpr bool kBothTiles = false;
   static constexpr int kLds = kTileBytes + G * kTilePages * 8 + kScoreTiles * (kTilePages + 1) * 4;
   static constexpr int kBlocksPerCu = (160 * 1024) / (kLds + 1024) >= 4 ? 4 : (160 * 1024) / (kLds + 1024);
   static constexpr int kCoefRow = 4 * DIM * G;         // doubles per (b, g) row: [kind][i][h]
@@ -159,29 +156,25 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
     const int p = min((t % tiles_per_row) * kTilePages + k % kTilePages, D.max_pages - 1);
     const int len = seq_lens[b];
     const int ph0 = page_table[(size_t)b * D.max_pages + p];
-    const int n_coef = nrows * DIM * G;
+    // coefficient rows, one (b, g) at a time: entry tt = i G + h of row (b, g)
+    // is built from q[b, g G + h, i]; the row's (b, g) is uniform
+    {
+      const int b0 = row0 / D.Hkv;
+      int bb = b0, gg = row0 - b0 * D.Hkv;
 #pragma unroll 1
-    for (int k0 = 0; k0 < n_coef; k0 += 4 * kScoreThreads) {
-      double qv[4];
+      for (int rr = 0; rr < nrows; ++rr) {
+        const T *qrow = q + ((size_t)bb * D.Hq + (size_t)gg * G) * DIM;
+        double *cw = coef_w + (size_t)(row0 + rr) * C::kCoefRow;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = min(k0 + u * kScoreThreads + tid, n_coef - 1);
-        const int row = row0 + kk / (DIM * G), tt = kk % (DIM * G);
-        const int bb = row / D.Hkv, g = row % D.Hkv;
-        qv[u] = (double)load_f<T>(q, ((size_t)bb * D.Hq + g * G + tt % G) * DIM + tt / G);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kk = k0 + u * kScoreThreads + tid;
-        if (kk < n_coef) {
-          // [row][kind][i][h]: kind 0 q- (kmin), 1 q+ (kmax), 2 q (mean), 3 q^2 (var)
-          double *cw = coef_w + (size_t)(row0 + kk / (DIM * G)) * C::kCoefRow + kk % (DIM * G);
-          const double qq = qv[u];
-          cw[0 * DIM * G] = qq < 0.0 ? qq : 0.0;
-          cw[1 * DIM * G] = qq >= 0.0 ? qq : 0.0;
-          cw[2 * DIM * G] = qq;
-          cw[3 * DIM * G] = qq * qq;
+        for (int tt = tid; tt < DIM * G; tt += kScoreThreads) {
+          // [kind][i][h]: kind 0 q- (kmin), 1 q+ (kmax), 2 q (mean), 3 q^2 (var)
+          const double qq = (double)load_f<T>(qrow, (tt % G) * DIM + tt / G);
+          cw[0 * DIM * G + tt] = qq < 0.0 ? qq : 0.0;
+          cw[1 * DIM * G + tt] = qq >= 0.0 ? qq : 0.0;
+          cw[2 * DIM * G + tt] = qq;
+          cw[3 * DIM * G + tt] = qq * qq;
         }
+        if (++gg == D.Hkv) { gg = 0; ++bb; }
       }
     }
     if (tid < nt * kTilePages) {
@@ -213,12 +206,11 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
 #pragma unroll
     for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[i * 16];
   }
-  u32x4 ring0[C::kLoads], ring1[C::kLoads];
-  score_load_tile<T, DIM, G, F8>(ring0, mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
-  if (C::kBothTiles) {
-    const int l1 = min(1, nt - 1);
-    score_load_tile<T, DIM, G, F8>(ring1, mbase, s_phys[l1], ((t_begin + l1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
-  }
+  // two register buffers: tile lt + 1 is requested once tile lt is in LDS (with
+  // more in flight from the start the per-tile latency grows with the deeper
+  // memory queue and the first tile arrives later, measured on cold HBM)
+  u32x4 ring[2][C::kLoads];
+  score_load_tile<T, DIM, G, F8>(ring[0], mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
 
   const double c = D.scale, c2 = D.scale * D.scale;
   const unsigned char *rec = tile + lane * C::kRecBytes;
@@ -233,11 +225,11 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   for (int lt = 0; lt < kScoreTiles; ++lt) {
     if (lt < nt) {
       if (lt > 0) lds_barrier();  // the previous tile and exchange are fully read
-      if (lt == 0) score_stash_tile<T, DIM, G, F8>(ring0, tile, tid);
-      else score_stash_tile<T, DIM, G, F8>(ring1, tile, tid);
+      score_stash_tile<T, DIM, G, F8>(ring[lt & 1], tile, tid);
       asm volatile("" ::: "memory");
-      if (!C::kBothTiles && lt == 0 && nt > 1)
-        score_load_tile<T, DIM, G, F8>(ring1, mbase, s_phys[1], ((t_begin + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+      if (lt + 1 < nt)
+        score_load_tile<T, DIM, G, F8>(ring[(lt + 1) & 1], mbase, s_phys[lt + 1],
+                                       ((t_begin + lt + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
       lds_barrier();
       if (lt == 0) asm volatile("" ::"s"(warm));
       if (lt == 0) EKV_MARK(0, 2);
