@@ -137,13 +137,15 @@ int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta
 /*
  * append_token -- the streaming side of [EntmaxKV s.2.A]: the page metadata
  * is kept current as pages fill.  For every sequence b with L_b = seq_lens[b]
- * >= 1 (seq_lens already count the new token): the new token's key and value
- * rows k_new / v_new [B][Hkv][d] (KV dtype) are written to slot (L_b - 1) % P
- * of logical page (L_b - 1) / P in k_pool / v_pool, and that page's metadata
- * record is rebuilt over its filled slots exactly as build_page_meta (or
- * build_page_meta_f8 when meta_format = 1; bf16 keys only) computes it, the
- * sums taken in slot order.  A sequence whose page-table entry is out of range
- * is left untouched.  One launch; no workspace.
+ * >= 1 (seq_lens already count the new token; L_b is clamped to
+ * max_pages * P as in every call): the new token's key and value rows
+ * k_new / v_new [B][Hkv][d] (KV dtype) are written to slot (L_b - 1) % P of
+ * logical page (L_b - 1) / P in k_pool / v_pool, and that page's metadata
+ * record is rebuilt over its filled slots by the code build_page_meta (or
+ * build_page_meta_f8 when meta_format = 1; bf16 keys only) runs, in the same
+ * order of additions, so it equals a rebuild of the page bit for bit.  A
+ * sequence whose page-table entry is out of range is left untouched.  One
+ * launch; no workspace.
  */
 int32_t append_token(const entmaxkv_shape *shape, const void *k_new, const void *v_new, void *k_pool,
                      void *v_pool, const int32_t *page_table, const int32_t *seq_lens, void *meta,

@@ -359,3 +359,41 @@ def test_append_token(case, compact):
     assert np.array_equal(host_raw(k, inp.dtype), k_exp) and np.array_equal(host_raw(v, inp.dtype), v_exp)
     got = meta.cpu().numpy() if compact else host_raw(meta, inp.dtype)
     assert np.array_equal(got, meta_exp)
+
+
+@pytest.mark.parametrize("dtype,compact", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_append_token_edges(dtype, compact):
+    """append_token at the page boundaries and the degenerate lengths: eight
+    sequences of 700 tokens in pages of 16 (cap 704) append with L = 1 (first
+    token), 16 (last slot of page 0), 17 and 33 (first slot of a new page), 700,
+    704 (the cap), 0 (nothing written) and 720 (clamped to the cap, as in every
+    call).  Pools and records bit-exact against the host update and the
+    oracle's rebuild of the touched pages."""
+    inp = small(7, 8, 4, 2, 64, 16, dtype, (700,) * 8)
+    D = Dev(inp)
+    B, P, MP = inp.B, inp.P, inp.max_pages
+    new_sl = np.array([1, 16, 17, 33, 700, 704, 0, 720], dtype=np.int32)
+    cap = MP * P
+    rng = np.random.default_rng(41)
+    kn = synth._store(rng.standard_normal((B, inp.Hkv, inp.d), dtype=np.float32), dtype)
+    vn = synth._store(rng.standard_normal((B, inp.Hkv, inp.d), dtype=np.float32), dtype)
+    k_exp, v_exp = inp.k_pool.copy(), inp.v_pool.copy()
+    for b in range(B):
+        L = min(max(int(new_sl[b]), 0), cap)
+        if L >= 1:
+            ph = inp.page_table[b, (L - 1) // P]
+            assert 0 <= ph < inp.num_phys
+            k_exp[ph, :, (L - 1) % P, :] = kn[b]
+            v_exp[ph, :, (L - 1) % P, :] = vn[b]
+    build = oracle.build_page_meta_f8 if compact else oracle.build_page_meta
+    meta0 = build(D.oshape, inp.k_pool, inp.page_table, inp.seq_lens)
+    from_tok = np.maximum(np.minimum(new_sl, cap) - 1, 0).astype(np.int32)
+    meta_exp = build(D.oshape, k_exp, inp.page_table, new_sl, from_token=from_tok, meta=meta0.copy())
+    t = torch()
+    k, v = D.k.clone(), D.v.clone()
+    meta = t.from_numpy(meta0.copy()).cuda() if compact else dev(meta0, D.kind)
+    E.append_token(D.shape, dev(kn, D.kind), dev(vn, D.kind), k, v, D.pt, dev(new_sl, "i32"), meta,
+                   compact=compact)
+    assert np.array_equal(host_raw(k, dtype), k_exp) and np.array_equal(host_raw(v, dtype), v_exp)
+    got = meta.cpu().numpy() if compact else host_raw(meta, dtype)
+    assert np.array_equal(got, meta_exp)
