@@ -49,6 +49,8 @@ constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
 constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
 constexpr int kSupChunk = 512;    // support entries gathered per LDS pass
 constexpr int kNThr = 8;          // count thresholds mx - 2^-i behind the certified bound on tau
+constexpr int kKeepIt = 3;        // kernel 2: 2048-token steps of a chunk kept in registers between passes
+constexpr int kIprLds = 2048;     // kernel 2: a split row's item -> physical page table staged in LDS up to this size
 
 struct DecodeWs {
   double *xs;        // [rows][max_pages*P]  X of kept tokens (item-major); kernel 2 compacts
@@ -497,6 +499,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   __shared__ int sup_i[kSupChunk];
   __shared__ float sup_w[kSupChunk];
   __shared__ float accs[kEpp][DIM + 1];
+  __shared__ uint32_t s_ipr[kIprLds];
   double *cx = reinterpret_cast<double *>(smem);              // [kCand] candidate X
   int *ci = reinterpret_cast<int *>(cx + kCand);              // [kCand] token index
   uint32_t *cv = reinterpret_cast<uint32_t *>(ci + kCand);    // [kCand] V row index
@@ -564,16 +567,21 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
 #pragma unroll
   for (int i = 0; i < kNThr; ++i) cnt8[i] = 0;
   int nlds = 0;
-#pragma unroll 1
-  for (int base = tlo; base < thi; base += 8 * kDThreads) {
-    const int t0 = base + 8 * tid;
-    const bool valid = t0 < thi;  // all 8 tokens or none (thi - t0 is a multiple of 8)
-    const int tc = min(t0, thi - 8);
+  // thread tid takes tokens base + 8 tid .. + 7 of each 2048-token step; the
+  // first kKeepIt steps stay in registers for pass 2 (a chunk of up to
+  // kChunkTok + P tokens is read once)
+  double keep[kKeepIt][8];
+  uint32_t keep_ph[kKeepIt];
+  auto load8 = [&](int base, double (&v)[8], uint32_t &ph) __attribute__((always_inline)) {
+    const int tc = min(base + 8 * tid, thi - 8);
     const double2 *src = reinterpret_cast<const double2 *>(xrow + tc);
-    double v[8];
 #pragma unroll
     for (int h = 0; h < 4; ++h) { const double2 d2 = src[h]; v[2 * h] = d2.x; v[2 * h + 1] = d2.y; }
-    const uint32_t ph = ipr[tc / P];
+    ph = ipr[tc / P];
+  };
+  auto count8 = [&](int base, const double (&v)[8], uint32_t ph) __attribute__((always_inline)) {
+    const int t0 = base + 8 * tid;
+    const bool valid = t0 < thi;  // all 8 tokens or none (thi - t0 is a multiple of 8)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
 #pragma unroll
@@ -599,6 +607,21 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       }
       nlds += tot;
     }
+  };
+#pragma unroll
+  for (int it = 0; it < kKeepIt; ++it) {
+    const int base = tlo + it * 8 * kDThreads;
+    if (base < thi) {  // uniform
+      load8(base, keep[it], keep_ph[it]);
+      count8(base, keep[it], keep_ph[it]);
+    }
+  }
+#pragma unroll 1
+  for (int base = tlo + kKeepIt * 8 * kDThreads; base < thi; base += 8 * kDThreads) {
+    double v[8];
+    uint32_t ph;
+    load8(base, v, ph);
+    count8(base, v, ph);
   }
   // block totals of the counts, then the tightest certified bound
 #pragma unroll
@@ -633,16 +656,9 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     // alone); writes trail the reads, so no unread score is overwritten
     nlds = 0;
     int ncand = 0;
-#pragma unroll 1
-    for (int base = tlo; base < thi; base += 8 * kDThreads) {
+    auto compact8 = [&](int base, const double (&v)[8], uint32_t ph) __attribute__((always_inline)) {
       const int t0 = base + 8 * tid;
       const bool valid = t0 < thi;
-      const int tc = min(t0, thi - 8);
-      const double2 *src = reinterpret_cast<const double2 *>(xrow + tc);
-      double v[8];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) { const double2 d2 = src[h]; v[2 * h] = d2.x; v[2 * h + 1] = d2.y; }
-      const uint32_t ph = ipr[tc / P];
       int take = 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) take += (valid && v[u] > Lc) ? 1 : 0;
@@ -663,6 +679,18 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
         }
       }
       ncand += tot;
+    };
+#pragma unroll
+    for (int it = 0; it < kKeepIt; ++it) {
+      const int base = tlo + it * 8 * kDThreads;
+      if (base < thi) compact8(base, keep[it], keep_ph[it]);
+    }
+#pragma unroll 1
+    for (int base = tlo + kKeepIt * 8 * kDThreads; base < thi; base += 8 * kDThreads) {
+      double v[8];
+      uint32_t ph;
+      load8(base, v, ph);
+      compact8(base, v, ph);
     }
     total = ncand;
     nlds = alone ? ncand : 0;
@@ -689,6 +717,9 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       for (int s2 = 0; s2 < nsplit; ++s2) ct += ld_agent(&ws.segn[((size_t)r * kSplitMax + s2) * kNThr + tid]);
       s_cnt[0][tid] = ct;
     }
+    const bool ipr_lds = cnt <= kIprLds;  // the merge below looks pages up in LDS
+    if (ipr_lds)
+      for (int k = tid; k < cnt; k += kDThreads) s_ipr[k] = ipr[k];
     __syncthreads();
     if (tid < kWave) {  // lane i (mod kNThr): threshold i's bound from the summed count
       const int i = tid & (kNThr - 1);
@@ -710,20 +741,36 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     // each thread takes 8 consecutive entries, so one block scan per 2048
     // entries keeps the candidates in index order
     nlds = 0;
-#pragma unroll 1
-    for (int base = 0; base < total; base += 8 * kDThreads) {
+    // each step's scores and token ids are requested one step ahead, so their
+    // round trip overlaps the previous step's scan
+    auto ld8 = [&](int base, double (&v)[8], uint32_t (&t)[8]) __attribute__((always_inline)) {
       const int k0 = base + 8 * tid;
-      double v[8];
-      uint32_t t[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int a = gs0.addr(min(k0 + u, total - 1));
         v[u] = ld_agent(&xrow[a]);
         t[u] = ld_agent(&xir[a]);
       }
-      uint32_t ph[8];
+    };
+    double vn[8];
+    uint32_t tn[8];
+    if (total > 0) ld8(0, vn, tn);
+#pragma unroll 1
+    for (int base = 0; base < total; base += 8 * kDThreads) {
+      const int k0 = base + 8 * tid;
+      double v[8];
+      uint32_t t[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) ph[u] = ipr[t[u] / P];
+      for (int u = 0; u < 8; ++u) { v[u] = vn[u]; t[u] = tn[u]; }
+      if (base + 8 * kDThreads < total) ld8(base + 8 * kDThreads, vn, tn);
+      uint32_t ph[8];
+      if (ipr_lds) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ph[u] = s_ipr[min(t[u] / P, (uint32_t)(cnt - 1))];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ph[u] = ipr[t[u] / P];
+      }
       int mine = 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) mine += (k0 + u < total && v[u] > L) ? 1 : 0;
