@@ -215,7 +215,18 @@ __device__ __forceinline__ T block_max(T v, T *scratch) {
   return s;
 }
 
+// Block barrier: __syncthreads(), or (kLdsOnly) one that orders LDS accesses
+// only and leaves the thread's global loads in flight (lds_barrier below).
+template <bool kLdsOnly>
+__device__ __forceinline__ void block_sync() {
+  if constexpr (kLdsOnly) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else __syncthreads();
+}
+
 // Exclusive prefix sum over a block (int32), returns the total in *total.
+// kLdsOnly: its barriers order LDS only (global loads issued before it stay
+// in flight; the caller must not rely on it to order global memory).
+template <bool kLdsOnly = false>
 __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
   int x = v;
@@ -224,9 +235,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int *scratch, int *total) 
     int y = __shfl_up(x, o, kWave);
     if (lane >= o) x += y;
   }
-  __syncthreads();
+  block_sync<kLdsOnly>();
   if (lane == kWave - 1) scratch[w] = x;
-  __syncthreads();
+  block_sync<kLdsOnly>();
   int base = 0, tot = 0;
   for (int i = 0; i < nw; ++i) {
     if (i < w) base += scratch[i];

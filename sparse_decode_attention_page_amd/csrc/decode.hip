@@ -170,13 +170,33 @@ struct GlobSeg {
   const int *soff;   // LDS, [nseg + 1] first entry of each segment
   const int *sbase;  // LDS, [nseg]     token offset where each segment starts
   int nseg, n;
-  __device__ __forceinline__ int addr(int k) const {
+  __device__ __forceinline__ int seg_of(int k) const {
     int lo = 0, hi = nseg - 1;  // last segment starting at or before k
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (soff[mid] <= k) lo = mid; else hi = mid - 1;
     }
+    return lo;
+  }
+  __device__ __forceinline__ int addr(int k) const {
+    const int lo = seg_of(k);
     return sbase[lo] + (k - soff[lo]);
+  }
+  // addresses of entries min(k0 + u, n - 1), u < R: one search, then the
+  // segment advances with k (empty segments are stepped over)
+  template <int R>
+  __device__ __forceinline__ void addr_run(int k0, int (&a)[R]) const {
+    int lo = seg_of(min(k0, n - 1));
+    int next = lo + 1 < nseg ? soff[lo + 1] : 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = min(k0 + u, n - 1);
+      while (k >= next) {
+        ++lo;
+        next = lo + 1 < nseg ? soff[lo + 1] : 0x7fffffff;
+      }
+      a[u] = sbase[lo] + (k - soff[lo]);
+    }
   }
   template <typename Fn>
   __device__ __forceinline__ void each(Fn &&fn) const {
@@ -721,6 +741,30 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     if (ipr_lds)
       for (int k = tid; k < cnt; k += kDThreads) s_ipr[k] = ipr[k];
     __syncthreads();
+    if (tid == 0) {  // segment offsets (the first step's entry addresses need them)
+      soff[0] = 0;
+      for (int s2 = 0; s2 < nsplit; ++s2) soff[s2 + 1] += soff[s2];
+    }
+    __syncthreads();
+    total = soff[nsplit];
+    const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
+    // each thread takes 8 consecutive entries, so one block scan per 2048
+    // entries keeps the candidates in index order; each step's scores and
+    // token ids are requested one step ahead, so their round trip overlaps the
+    // previous step's scan (the first step's, the row bound below)
+    nlds = 0;
+    auto ld8 = [&](int base, double (&v)[8], uint32_t (&t)[8]) __attribute__((always_inline)) {
+      int a[8];
+      gs0.addr_run<8>(base + 8 * tid, a);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v[u] = ld_agent(&xrow[a[u]]);
+        t[u] = ld_agent(&xir[a[u]]);
+      }
+    };
+    double vn[8];
+    uint32_t tn[8];
+    if (total > 0) ld8(0, vn, tn);
     if (tid < kWave) {  // lane i (mod kNThr): threshold i's bound from the summed count
       const int i = tid & (kNThr - 1);
       const int ct = s_cnt[0][i];
@@ -728,33 +772,13 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
           ct > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ct, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
       const double cmax = wave_max(cand);
       if (tid == 0) {
-        soff[0] = 0;
         double lm = fmax(thr, cmax);
-        for (int s2 = 0; s2 < nsplit; ++s2) { soff[s2 + 1] += soff[s2]; lm = fmax(lm, sL[s2]); }
+        for (int s2 = 0; s2 < nsplit; ++s2) lm = fmax(lm, sL[s2]);
         s_tau[0] = lm;
       }
     }
-    __syncthreads();
-    total = soff[nsplit];
+    lds_barrier();  // s_tau; the first step's loads stay in flight
     L = s_tau[0];
-    const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
-    // each thread takes 8 consecutive entries, so one block scan per 2048
-    // entries keeps the candidates in index order
-    nlds = 0;
-    // each step's scores and token ids are requested one step ahead, so their
-    // round trip overlaps the previous step's scan
-    auto ld8 = [&](int base, double (&v)[8], uint32_t (&t)[8]) __attribute__((always_inline)) {
-      const int k0 = base + 8 * tid;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int a = gs0.addr(min(k0 + u, total - 1));
-        v[u] = ld_agent(&xrow[a]);
-        t[u] = ld_agent(&xir[a]);
-      }
-    };
-    double vn[8];
-    uint32_t tn[8];
-    if (total > 0) ld8(0, vn, tn);
 #pragma unroll 1
     for (int base = 0; base < total; base += 8 * kDThreads) {
       const int k0 = base + 8 * tid;
@@ -775,7 +799,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) mine += (k0 + u < total && v[u] > L) ? 1 : 0;
       int tot;
-      int at = nlds + block_excl_scan(mine, scan_scratch, &tot);
+      int at = nlds + block_excl_scan<true>(mine, scan_scratch, &tot);  // the next step's loads stay in flight
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (k0 + u < total && v[u] > L) {
