@@ -10,6 +10,16 @@
 // 8-bit passes with an LDS histogram); a final ordered pass emits every page
 // above that key plus the lowest-index pages equal to it, in ascending order.
 // All of it is integer work, so the page set is exact.
+//
+// Rows of up to kTopkThreads * kTopkPer pages (topk_reg_kernel): thread t
+// holds pages [t kTopkPer, (t + 1) kTopkPer) in registers for every pass; in
+// the histogram the lanes of a wave that share the leading lane's digit add
+// with one atomic (the bounds of a row share their high bytes, so plain atomics
+// would pile onto one or two bins), and each wave counts into its own
+// histogram (no atomics across waves); the bin holding the k-th key is
+// found by a scan over the 256 bins (summed over the waves); the
+// emission needs two block scans, since each thread's pages are consecutive.
+// Longer rows use topk_kernel, which streams the row from memory each pass.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -87,13 +97,129 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Dims D, const float 
   if (tid == 0) sel_cnt[row] = k;
 }
 
+constexpr int kTopkPer = 16;
+
+// Adds each active lane's digit d to hist: the lanes sharing the lowest active
+// lane's digit add with one atomic, the rest one by one.  (Measured on the 1M
+// context: one aggregated group 22.9 us per top-k, two 24.7, four 28.0, none
+// 31.5 -- further rounds cost more than the conflicts they remove.)
+__device__ __forceinline__ void hist_add_wave(unsigned int *hist, unsigned int d, bool active) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const unsigned long long act = __ballot(active);
+  if (act != 0ull) {  // uniform
+    const int leader = __ffsll((long long)act) - 1;
+    const unsigned int dl = (unsigned int)__builtin_amdgcn_readlane((int)d, leader);
+    const unsigned long long m = __ballot(active && d == dl) & act;
+    if (lane == leader) atomicAdd(&hist[dl], (unsigned int)__popcll(m));
+    if ((m >> lane) & 1ull) active = false;
+  }
+  if (active) atomicAdd(&hist[d], 1u);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(Dims D, const float *__restrict__ box,
+                                                                const int32_t *__restrict__ seq_lens, int k,
+                                                                const uint8_t *__restrict__ seq_mask,
+                                                                int32_t *__restrict__ sel_idx,
+                                                                int32_t *__restrict__ sel_cnt) {
+  constexpr int kNw = kTopkThreads / kWave;
+  __shared__ unsigned int hist[kNw][256];  // one histogram per wave: no atomics across waves
+  __shared__ int scan_scratch[kTopkThreads / kWave];
+  __shared__ unsigned int bin_tot[256 / kWave];
+  __shared__ unsigned int s_prefix, s_need;
+  const int row = blockIdx.x;  // b*Hq + h
+  const int b = row / D.Hq;
+  if (seq_mask && !seq_mask[b]) return;
+  const int L = seq_len_clamped(seq_lens, b, D);
+  const int np = n_pages_of(L, D.P);
+  const float *key_row = box + (size_t)row * D.max_pages;
+  int32_t *out = sel_idx + (size_t)row * D.max_pages;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+
+  if (np <= k) {
+    for (int p = tid; p < np; p += kTopkThreads) out[p] = p;
+    if (tid == 0) sel_cnt[row] = np;
+    return;
+  }
+  const int p0 = tid * kTopkPer;
+  unsigned int key[kTopkPer];
+#pragma unroll
+  for (int u = 0; u < kTopkPer; ++u) key[u] = p0 + u < np ? order_key(key_row[p0 + u]) : 0u;
+
+  // ---- radix select of the k-th largest key
+  unsigned int prefix = 0, pmask = 0, need = (unsigned int)k;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int i = tid; i < kNw * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kTopkPer; ++u)
+      hist_add_wave(hist[tid / kWave], (key[u] >> shift) & 255u, p0 + u < np && (key[u] & pmask) == prefix);
+    __syncthreads();
+    // thread t < 256 takes bin 255 - t: an inclusive scan over t gives the count
+    // of keys in bins >= 255 - t; the bin where it reaches `need` holds the key
+    unsigned int h = 0, x = 0;
+    if (tid < 256) {  // waves 0 .. 3, whole
+#pragma unroll
+      for (int w = 0; w < kNw; ++w) h += hist[w][255 - tid];
+      x = h;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      if (lane == kWave - 1) bin_tot[tid / kWave] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      unsigned int base = 0;
+      for (int w = 0; w < tid / kWave; ++w) base += bin_tot[w];
+      const unsigned int incl = base + x, excl = incl - h;
+      if (excl < need && incl >= need) {
+        s_prefix = prefix | ((unsigned int)(255 - tid) << shift);
+        s_need = need - excl;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    pmask |= 255u << shift;
+  }
+  // prefix is the k-th largest key; take every key above it and the `need`
+  // lowest-index keys equal to it, in index order
+  const unsigned int T = prefix;
+  int n_eq = 0;
+#pragma unroll
+  for (int u = 0; u < kTopkPer; ++u) n_eq += (p0 + u < np && key[u] == T) ? 1 : 0;
+  int eq_total;
+  int eq_rank = block_excl_scan(n_eq, scan_scratch, &eq_total);
+  unsigned int takem = 0;
+#pragma unroll
+  for (int u = 0; u < kTopkPer; ++u) {
+    const bool ok = p0 + u < np;
+    const bool eq = ok && key[u] == T;
+    if (ok && (key[u] > T || (eq && eq_rank < (int)need))) takem |= 1u << u;
+    eq_rank += eq ? 1 : 0;
+  }
+  int sel_total;
+  int pos = block_excl_scan(__popc(takem), scan_scratch, &sel_total);
+#pragma unroll
+  for (int u = 0; u < kTopkPer; ++u)
+    if ((takem >> u) & 1u) out[pos++] = p0 + u;
+  if (tid == 0) sel_cnt[row] = k;
+}
+
 size_t topk_ws_bytes(const Dims &) { return 0; }
 
 hipError_t launch_topk(const Dims &D, const float *box, const int32_t *seq_lens, int k,
                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt, void *,
                        hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k,
-                     seq_mask, sel_idx, sel_cnt);
+  if (D.max_pages <= kTopkThreads * kTopkPer)
+    hipLaunchKernelGGL(topk_reg_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k,
+                       seq_mask, sel_idx, sel_cnt);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k,
+                       seq_mask, sel_idx, sel_cnt);
   return hipGetLastError();
 }
 

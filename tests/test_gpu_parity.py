@@ -134,6 +134,30 @@ def test_select_topk(case, k):
     assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
 
 
+@pytest.mark.parametrize("mp", [1000, 16384, 17500])
+@pytest.mark.parametrize("k", [1, 64, 999])
+def test_select_topk_ties_and_long_rows(mp, k):
+    """Top-k on bounds with many ties (40 distinct values), NaN and both signed
+    zeros, over rows of 1,000 and 16,384 pages (the register-resident select)
+    and 17,500 pages (the streaming select), one row ragged; bit-exact sets
+    against the oracle (ties to the lowest page index, NaN last)."""
+    t = torch()
+    B, Hq, P = 2, 4, 16  # one KV head of four query heads
+    rng = np.random.default_rng(mp * 7 + k)
+    box = (rng.integers(0, 40, size=(B, Hq, mp)).astype(np.float32) * 0.25 - 3.0).astype(np.float32)
+    box[0, 0, rng.integers(0, mp, 25)] = np.nan
+    box[1, 2, rng.integers(0, mp, 25)] = -0.0
+    box[1, 2, rng.integers(0, mp, 25)] = 0.0
+    seq_lens = np.array([mp * P, (mp - 37) * P - 5], dtype=np.int32)
+    shape = E.Shape(B, Hq, 1, 64, P, mp, mp * B, E.BF16, 0.0)
+    oshape = oracle.Shape(B, Hq, 1, 64, P, mp, mp * B, "bf16", 0.0)
+    sel = t.full((B, Hq, mp), -7, dtype=t.int32, device="cuda")
+    cnt = t.full((B, Hq), -7, dtype=t.int32, device="cuda")
+    E.select_pages_topk(shape, t.from_numpy(box).cuda(), dev(seq_lens, "i32"), k, sel, cnt)
+    so, co = oracle.select_topk(oshape, box, seq_lens, k)
+    assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co) == []
+
+
 @pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (2.0, 0.5), (1.5, 0.0), (2.0, 1.5), (1.25, 0.5)])
 def test_select_gauss(case, alpha, delta):
     inp, D, _, (box_o, mu_o, var_o) = case
