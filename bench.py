@@ -644,7 +644,7 @@ def selector_sweep(args):
     alpha = wl.alphas[0]
     ev = lambda: torch.cuda.Event(enable_timing=True)
     rows = []
-    for ctx in (32768, 131072, 524288, 1048576):
+    for ctx in (32768, 131072, 524288, 1048576, 4194304):
         inp = synth.make_device(wl, args.seed, ctx_override=ctx)
         shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
         B, Hq, Hkv, d, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.max_pages

@@ -11,93 +11,24 @@
 // above that key plus the lowest-index pages equal to it, in ascending order.
 // All of it is integer work, so the page set is exact.
 //
-// Rows of up to kTopkThreads * kTopkPer pages (topk_reg_kernel): thread t
-// holds pages [t kTopkPer, (t + 1) kTopkPer) in registers for every pass; in
-// the histogram the lanes of a wave that share the leading lane's digit add
-// with one atomic (the bounds of a row share their high bytes, so plain atomics
-// would pile onto one or two bins), and each wave counts into its own
-// histogram (no atomics across waves); the bin holding the k-th key is
-// found by a scan over the 256 bins (summed over the waves); the
-// emission needs two block scans, since each thread's pages are consecutive.
-// Longer rows use topk_kernel, which streams the row from memory each pass.
+// The row is taken in batches of kTopkThreads * kTopkPer pages, thread t
+// holding pages [t kTopkPer, (t + 1) kTopkPer) of the batch in registers; a
+// row of one batch (up to 16,384 pages) is read once and kept for every pass,
+// longer rows read each batch again per pass.  In the histogram the lanes of a
+// wave that share the leading lane's digit add with one atomic (the bounds of a
+// row share their high bytes, so plain atomics would pile onto one or two
+// bins), and each wave counts into its own histogram (no atomics across
+// waves); the bin holding the k-th key comes from a scan over the 256 bins
+// (summed over the waves); the emission takes two block scans per batch, since
+// each thread's pages are consecutive.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ekv {
 
 constexpr int kTopkThreads = 1024;
-
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(Dims D, const float *__restrict__ box,
-                                                            const int32_t *__restrict__ seq_lens,
-                                                            int k, const uint8_t *__restrict__ seq_mask,
-                                                            int32_t *__restrict__ sel_idx,
-                                                            int32_t *__restrict__ sel_cnt) {
-  __shared__ unsigned int hist[256];
-  __shared__ int scan_scratch[kTopkThreads / kWave];
-  __shared__ unsigned int s_prefix, s_need;
-  const int row = blockIdx.x;  // b*Hq + h
-  const int b = row / D.Hq;
-  if (seq_mask && !seq_mask[b]) return;
-  const int L = seq_len_clamped(seq_lens, b, D);
-  const int np = n_pages_of(L, D.P);
-  const float *key_row = box + (size_t)row * D.max_pages;
-  int32_t *out = sel_idx + (size_t)row * D.max_pages;
-  const int tid = threadIdx.x;
-
-  if (np <= k) {
-    for (int p = tid; p < np; p += kTopkThreads) out[p] = p;
-    if (tid == 0) sel_cnt[row] = np;
-    return;
-  }
-
-  // ---- radix select of the k-th largest key
-  unsigned int prefix = 0, pmask = 0, need = (unsigned int)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
-    __syncthreads();
-    for (int p = tid; p < np; p += kTopkThreads) {
-      const unsigned int key = order_key(key_row[p]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      unsigned int above = 0;
-      int dgt = 255;
-      for (; dgt > 0; --dgt) {
-        if (above + hist[dgt] >= need) break;
-        above += hist[dgt];
-      }
-      s_prefix = prefix | ((unsigned int)dgt << shift);
-      s_need = need - above;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    need = s_need;
-    pmask |= 255u << shift;
-    __syncthreads();
-  }
-  // prefix is the k-th largest key; take every key above it and the `need`
-  // lowest-index keys equal to it.
-  const unsigned int T = prefix;
-  int eq_before = 0, sel_before = 0;
-  for (int base = 0; base < np; base += kTopkThreads) {
-    const int p = base + tid;
-    unsigned int key = 0;
-    if (p < np) key = order_key(key_row[p]);
-    const int is_eq = (p < np && key == T) ? 1 : 0;
-    int eq_total;
-    const int eq_rank = eq_before + block_excl_scan(is_eq, scan_scratch, &eq_total);
-    const int take = (p < np) && (key > T || (is_eq && eq_rank < (int)need));
-    int sel_total;
-    const int pos = sel_before + block_excl_scan(take, scan_scratch, &sel_total);
-    if (take) out[pos] = p;
-    eq_before += eq_total;
-    sel_before += sel_total;
-  }
-  if (tid == 0) sel_cnt[row] = k;
-}
-
 constexpr int kTopkPer = 16;
+constexpr int kTopkBatch = kTopkThreads * kTopkPer;
 
 // Adds each active lane's digit d to hist: the lanes sharing the lowest active
 // lane's digit add with one atomic, the rest one by one.  (Measured on the 1M
@@ -116,11 +47,11 @@ __device__ __forceinline__ void hist_add_wave(unsigned int *hist, unsigned int d
   if (active) atomicAdd(&hist[d], 1u);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(Dims D, const float *__restrict__ box,
-                                                                const int32_t *__restrict__ seq_lens, int k,
-                                                                const uint8_t *__restrict__ seq_mask,
-                                                                int32_t *__restrict__ sel_idx,
-                                                                int32_t *__restrict__ sel_cnt) {
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(Dims D, const float *__restrict__ box,
+                                                            const int32_t *__restrict__ seq_lens, int k,
+                                                            const uint8_t *__restrict__ seq_mask,
+                                                            int32_t *__restrict__ sel_idx,
+                                                            int32_t *__restrict__ sel_cnt) {
   constexpr int kNw = kTopkThreads / kWave;
   __shared__ unsigned int hist[kNw][256];  // one histogram per wave: no atomics across waves
   __shared__ int scan_scratch[kTopkThreads / kWave];
@@ -140,10 +71,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(Dims D, const fl
     if (tid == 0) sel_cnt[row] = np;
     return;
   }
-  const int p0 = tid * kTopkPer;
+  const int nbat = (np + kTopkBatch - 1) / kTopkBatch;
   unsigned int key[kTopkPer];
+  auto load = [&](int bat) __attribute__((always_inline)) {
+    const int p0 = bat * kTopkBatch + tid * kTopkPer;
 #pragma unroll
-  for (int u = 0; u < kTopkPer; ++u) key[u] = p0 + u < np ? order_key(key_row[p0 + u]) : 0u;
+    for (int u = 0; u < kTopkPer; ++u) key[u] = p0 + u < np ? order_key(key_row[p0 + u]) : 0u;
+  };
+  if (nbat == 1) load(0);  // kept for every pass
 
   // ---- radix select of the k-th largest key
   unsigned int prefix = 0, pmask = 0, need = (unsigned int)k;
@@ -152,9 +87,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(Dims D, const fl
 #pragma unroll
     for (int i = tid; i < kNw * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
+#pragma unroll 1
+    for (int bat = 0; bat < nbat; ++bat) {
+      if (nbat > 1) load(bat);
+      const int p0 = bat * kTopkBatch + tid * kTopkPer;
 #pragma unroll
-    for (int u = 0; u < kTopkPer; ++u)
-      hist_add_wave(hist[tid / kWave], (key[u] >> shift) & 255u, p0 + u < np && (key[u] & pmask) == prefix);
+      for (int u = 0; u < kTopkPer; ++u)
+        hist_add_wave(hist[tid / kWave], (key[u] >> shift) & 255u, p0 + u < np && (key[u] & pmask) == prefix);
+    }
     __syncthreads();
     // thread t < 256 takes bin 255 - t: an inclusive scan over t gives the count
     // of keys in bins >= 255 - t; the bin where it reaches `need` holds the key
@@ -186,26 +126,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(Dims D, const fl
     pmask |= 255u << shift;
   }
   // prefix is the k-th largest key; take every key above it and the `need`
-  // lowest-index keys equal to it, in index order
+  // lowest-index keys equal to it, in index order, batch by batch
   const unsigned int T = prefix;
-  int n_eq = 0;
+  int eq_before = 0, sel_before = 0;
+#pragma unroll 1
+  for (int bat = 0; bat < nbat; ++bat) {
+    if (nbat > 1) load(bat);
+    const int p0 = bat * kTopkBatch + tid * kTopkPer;
+    int n_eq = 0;
 #pragma unroll
-  for (int u = 0; u < kTopkPer; ++u) n_eq += (p0 + u < np && key[u] == T) ? 1 : 0;
-  int eq_total;
-  int eq_rank = block_excl_scan(n_eq, scan_scratch, &eq_total);
-  unsigned int takem = 0;
+    for (int u = 0; u < kTopkPer; ++u) n_eq += (p0 + u < np && key[u] == T) ? 1 : 0;
+    int eq_total;
+    int eq_rank = eq_before + block_excl_scan(n_eq, scan_scratch, &eq_total);
+    unsigned int takem = 0;  // bit u: page p0 + u is taken
 #pragma unroll
-  for (int u = 0; u < kTopkPer; ++u) {
-    const bool ok = p0 + u < np;
-    const bool eq = ok && key[u] == T;
-    if (ok && (key[u] > T || (eq && eq_rank < (int)need))) takem |= 1u << u;
-    eq_rank += eq ? 1 : 0;
+    for (int u = 0; u < kTopkPer; ++u) {
+      const bool ok = p0 + u < np;
+      const bool eq = ok && key[u] == T;
+      if (ok && (key[u] > T || (eq && eq_rank < (int)need))) takem |= 1u << u;
+      eq_rank += eq ? 1 : 0;
+    }
+    int sel_total;
+    int pos = sel_before + block_excl_scan(__popc(takem), scan_scratch, &sel_total);
+#pragma unroll
+    for (int u = 0; u < kTopkPer; ++u)
+      if ((takem >> u) & 1u) out[pos++] = p0 + u;
+    eq_before += eq_total;
+    sel_before += sel_total;
   }
-  int sel_total;
-  int pos = block_excl_scan(__popc(takem), scan_scratch, &sel_total);
-#pragma unroll
-  for (int u = 0; u < kTopkPer; ++u)
-    if ((takem >> u) & 1u) out[pos++] = p0 + u;
   if (tid == 0) sel_cnt[row] = k;
 }
 
@@ -214,12 +162,8 @@ size_t topk_ws_bytes(const Dims &) { return 0; }
 hipError_t launch_topk(const Dims &D, const float *box, const int32_t *seq_lens, int k,
                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt, void *,
                        hipStream_t s) {
-  if (D.max_pages <= kTopkThreads * kTopkPer)
-    hipLaunchKernelGGL(topk_reg_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k,
-                       seq_mask, sel_idx, sel_cnt);
-  else
-    hipLaunchKernelGGL(topk_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k,
-                       seq_mask, sel_idx, sel_cnt);
+  hipLaunchKernelGGL(topk_kernel, dim3(D.B * D.Hq), dim3(kTopkThreads), 0, s, D, box, seq_lens, k, seq_mask,
+                     sel_idx, sel_cnt);
   return hipGetLastError();
 }
 

@@ -138,9 +138,10 @@ def test_select_topk(case, k):
 @pytest.mark.parametrize("k", [1, 64, 999])
 def test_select_topk_ties_and_long_rows(mp, k):
     """Top-k on bounds with many ties (40 distinct values), NaN and both signed
-    zeros, over rows of 1,000 and 16,384 pages (the register-resident select)
-    and 17,500 pages (the streaming select), one row ragged; bit-exact sets
-    against the oracle (ties to the lowest page index, NaN last)."""
+    zeros, over rows of 1,000 and 16,384 pages (one batch of keys, held in
+    registers for every pass) and 17,500 pages (two batches, read again each
+    pass), one row ragged; bit-exact sets against the oracle (ties to the
+    lowest page index, NaN last)."""
     t = torch()
     B, Hq, P = 2, 4, 16  # one KV head of four query heads
     rng = np.random.default_rng(mp * 7 + k)
