@@ -62,3 +62,24 @@ def test_entmax_decode_sparse_long_rows(large, alpha, method):
 def test_entmax_decode_full_long_rows(large, alpha):
     inp, D = large
     decode_check(inp, D, alpha, None, None, full=True)
+
+
+@pytest.mark.parametrize("scale", [0.0, 0.002], ids=["scale_default", "scale0.002"])
+def test_entmax_decode_sparse_very_long_row(scale):
+    """One context of 262,144 tokens in pages of 16 (16,384 pages): row 0 keeps
+    every page (32 chunk blocks of 8,192 tokens, so a chunk's later tokens are
+    read again between its passes, and the merge looks pages up in memory
+    rather than LDS: more than 2,048 items), row 1 a random 60% of them."""
+    inp = synth.random_small(12, B=1, Hq=2, Hkv=1, d=64, P=16, dtype="bf16", ctx=(262144,), planted_per_kv=5)
+    D = Dev(inp, scale=scale)
+    npg = inp.max_pages
+    assert npg == 16384
+    rng = np.random.default_rng(3)
+    sel = np.full((1, 2, npg), -1, np.int32)
+    cnt = np.zeros((1, 2), np.int32)
+    sel[0, 0] = np.arange(npg)
+    cnt[0, 0] = npg
+    half = np.sort(rng.choice(npg, size=int(0.6 * npg), replace=False))
+    sel[0, 1, :len(half)] = half
+    cnt[0, 1] = len(half)
+    decode_check(inp, D, 1.5, sel, cnt)
