@@ -44,7 +44,7 @@ namespace ekv {
 
 constexpr int kDThreads = 256;
 constexpr int kDGrid = 1024;      // kernel 1: items are strided over this many blocks
-constexpr int kChunkTok = 4096;   // kernel 2: tokens per chunk block
+constexpr int kChunkTok = 2048;   // kernel 2: tokens per chunk block (long_1m decode: 2048 26.6 us, 1024 30.3, 4096 27.2, 8192 30.9)
 constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
 constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
 constexpr int kSupChunk = 512;    // support entries gathered per LDS pass
@@ -588,8 +588,9 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   for (int i = 0; i < kNThr; ++i) cnt8[i] = 0;
   int nlds = 0;
   // thread tid takes tokens base + 8 tid .. + 7 of each 2048-token step; the
-  // first kKeepIt steps stay in registers for pass 2 (a chunk of up to
-  // kChunkTok + P tokens is read once)
+  // first kKeepIt steps stay in registers for pass 2 (a chunk of up to 6144
+  // tokens -- every chunk until a row keeps more than kSplitMax of them -- is
+  // read once)
   double keep[kKeepIt][8];
   uint32_t keep_ph[kKeepIt];
   auto load8 = [&](int base, double (&v)[8], uint32_t &ph) __attribute__((always_inline)) {
