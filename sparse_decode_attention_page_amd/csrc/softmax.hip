@@ -31,6 +31,7 @@
 namespace ekv {
 
 constexpr int kSThreads = 256;
+constexpr int kMergeThreads = 256;  // merge: groups of DIM threads, each over every (256/DIM)-th partial
 
 struct SoftmaxWs {
   float *part;              // [B][Hq][S][DIM + 2]  (m, l, acc[DIM]); l = NaN marks a bad page id
@@ -204,32 +205,66 @@ __global__ __launch_bounds__(kSThreads) void softmax_decode_kernel(
 // Merge the ranges of one query row in range order (a separate launch: plain
 // cached loads of all ranges at once beat a last-block handoff here).
 template <int DIM>
-__global__ __launch_bounds__(DIM) void softmax_merge_kernel(Dims D, SoftmaxWs ws, float *__restrict__ out,
-                                                            float *__restrict__ lse) {
-  __shared__ float sm[1024], sl[1024];
-  const int row = blockIdx.x, i = threadIdx.x;
-  const float *rec0 = ws.part + (size_t)row * ws.S * (DIM + 2);
-  float mm = -INFINITY;
-  bool nan = false;
-  for (int r = i; r < ws.S; r += DIM) {
+__global__ __launch_bounds__(kMergeThreads) void softmax_merge_kernel(Dims D, SoftmaxWs ws, float *__restrict__ out,
+                                                                     float *__restrict__ lse) {
+  // thread (grp, i): coordinate i of the partials r = grp, grp + kMergeGroups, ...
+  // (loads issued 16 at a time); the groups' sums are combined in a fixed order
+  constexpr int kMergeGroups = kMergeThreads / DIM;
+  __shared__ float sm[1024], sf[1024], sl[1024];
+  __shared__ float s_ll[kMergeGroups], s_aa[kMergeGroups][DIM];
+  __shared__ float s_mm;
+  __shared__ int s_nan;
+  const int row = blockIdx.x, tid = threadIdx.x, grp = tid / DIM, i = tid % DIM;
+  const int S = ws.S;
+  const float *rec0 = ws.part + (size_t)row * S * (DIM + 2);
+  for (int r = tid; r < S; r += kMergeThreads) {
     sm[r] = rec0[(size_t)r * (DIM + 2)];
     sl[r] = rec0[(size_t)r * (DIM + 2) + 1];
   }
   __syncthreads();
-  for (int r = 0; r < ws.S; ++r) {
-    mm = fmaxf(mm, sm[r]);
-    nan |= sl[r] != sl[r];
+  if (tid == 0) {
+    float mm = -INFINITY;
+    int nan = 0;
+    for (int r = 0; r < S; ++r) {
+      mm = fmaxf(mm, sm[r]);
+      nan |= sl[r] != sl[r];
+    }
+    s_mm = mm;
+    s_nan = nan;
   }
+  __syncthreads();
+  const float mm = s_mm;
+  for (int r = tid; r < S; r += kMergeThreads) sf[r] = sm[r] == -INFINITY ? 0.0f : __expf(sm[r] - mm);
+  __syncthreads();
   float ll = 0.0f, aa = 0.0f;
-  for (int r = 0; r < ws.S; ++r) {
-    const float f = sm[r] == -INFINITY ? 0.0f : __expf(sm[r] - mm);
-    ll += sl[r] * f;
-    aa += rec0[(size_t)r * (DIM + 2) + 2 + i] * f;
+#pragma unroll 1
+  for (int r0 = grp; r0 < S; r0 += 16 * kMergeGroups) {
+    float a[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = min(r0 + u * kMergeGroups, S - 1);
+      a[u] = rec0[(size_t)r * (DIM + 2) + 2 + i];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = r0 + u * kMergeGroups;
+      if (r < S) {
+        ll += sl[r] * sf[r];
+        aa += a[u] * sf[r];
+      }
+    }
   }
-  const size_t o = (size_t)row * DIM + i;
-  if (nan) out[o] = NAN;
-  else out[o] = ll > 0.0f ? aa / ll : 0.0f;
-  if (i == 0 && lse) lse[row] = nan ? NAN : (ll > 0.0f ? mm + logf(ll) : -INFINITY);
+  if (i == 0) s_ll[grp] = ll;
+  s_aa[grp][i] = aa;
+  __syncthreads();
+  if (grp == 0) {
+    float lt = s_ll[0], at = s_aa[0][i];
+    for (int g = 1; g < kMergeGroups; ++g) { lt += s_ll[g]; at += s_aa[g][i]; }
+    const size_t o = (size_t)row * DIM + i;
+    if (s_nan) out[o] = NAN;
+    else out[o] = lt > 0.0f ? at / lt : 0.0f;
+    if (i == 0 && lse) lse[row] = s_nan ? NAN : (lt > 0.0f ? mm + logf(lt) : -INFINITY);
+  }
 }
 
 static SoftmaxWs carve_softmax(const Dims &D, void *base, size_t *bytes) {
@@ -259,7 +294,7 @@ static hipError_t launch_sm(const Dims &D, const void *q, const void *k, const v
   dim3 grid(w.S, D.Hkv, D.B);
   hipLaunchKernelGGL((softmax_decode_kernel<T, DIM, P, G>), grid, dim3(kSThreads), 0, s, D, (const T *)q,
                      (const T *)k, (const T *)v, pt, sl, out, lse, w);
-  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(DIM), 0, s, D, w, out, lse);
+  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(kMergeThreads), 0, s, D, w, out, lse);
   return hipGetLastError();
 }
 
@@ -470,7 +505,7 @@ static hipError_t launch_sms(const Dims &D, const void *q, const void *k, const 
                              SoftmaxWs w, hipStream_t s) {
   hipLaunchKernelGGL((softmax_sparse_kernel<T, DIM, P>), dim3(w.S, D.B * D.Hq), dim3(kSThreads), 0, s, D,
                      (const T *)q, (const T *)k, (const T *)v, pt, sl, si, sc, w);
-  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(DIM), 0, s, D, w, out, lse);
+  hipLaunchKernelGGL((softmax_merge_kernel<DIM>), dim3(D.B * D.Hq), dim3(kMergeThreads), 0, s, D, w, out, lse);
   return hipGetLastError();
 }
 
