@@ -402,7 +402,7 @@ __device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, doub
                                           double *sortbuf, const double (&rx)[kRegPer], const GlobSeg<1> &gs,
                                           double *dred, int *s_kstar, double *s_tau, double &tau, double &z) {
   const int tid = threadIdx.x;
-  const GlobSeg<8> gs8{gs.x, gs.soff, gs.sbase, gs.nseg, gs.n};
+  const GlobSeg<16> gs8{gs.x, gs.soff, gs.sbase, gs.nseg, gs.n};  // 16 scores per thread in flight per step
   double zk = 0.0;  // F at tau when the solver found it from its sums (else 0)
   if (tier == 0 && kB == 1 && dp.tau_method == 1) {
     tau = sparsemax_tau_sort(cx, total, sortbuf, dred, s_kstar);
@@ -418,7 +418,7 @@ __device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, doub
   } else if (kB != 0 && tier == 1) {
     tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, lo0, dp, dred, &zk);
   } else if (kB != 0) {
-    tau = newton_tau<kB, GlobSeg<8>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred, &zk);
+    tau = newton_tau<kB, GlobSeg<16>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred, &zk);
   } else {
     tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, lo0, dp, dred, &zk);
   }
@@ -813,6 +813,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
         }
       }
       nlds += tot;
+      if (nlds > kCand) break;  // the LDS set is only used when it holds them all (uniform)
     }
   } else if (tid == 0) {
     soff[0] = 0;
@@ -866,8 +867,25 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       __syncthreads();
     }
     int e = ge;
+    // four entries per thread in flight, then two, then one
 #pragma unroll 1
-    for (; e + kEpp < nsup; e += 2 * kEpp) {
+    for (; e + 3 * kEpp < nsup; e += 4 * kEpp) {
+      float v0[8], v1[8], v2[8], v3[8];
+      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sup_v[e + kEpp] * DIM + gc * 8, v1);
+      load_vec<8>(v_pool + (size_t)sup_v[e + 2 * kEpp] * DIM + gc * 8, v2);
+      load_vec<8>(v_pool + (size_t)sup_v[e + 3 * kEpp] * DIM + gc * 8, v3);
+      const float w0 = sup_w[e], w1 = sup_w[e + kEpp], w2 = sup_w[e + 2 * kEpp], w3 = sup_w[e + 3 * kEpp];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w1 * v1[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w2 * v2[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc8[u] += w3 * v3[u];
+    }
+    if (e + kEpp < nsup) {
       float v0[8], v1[8];
       load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
       load_vec<8>(v_pool + (size_t)sup_v[e + kEpp] * DIM + gc * 8, v1);
@@ -876,6 +894,7 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w1 * v1[u];
+      e += 2 * kEpp;
     }
     if (e < nsup) {
       float v0[8];
