@@ -193,8 +193,18 @@ __global__ __launch_bounds__(kGThreads) void gauss_bracket_kernel(Dims D, GaussP
     }
   }
   EKV_MARK(0, 1);
-  lo_c = block_max(lo_c, red);
-  top = block_max(top, red);
+  {  // both block maxima with one pair of barriers
+    lo_c = wave_max(lo_c);
+    top = wave_max(top);
+    constexpr int nw = kGThreads / kWave;
+    const int w = threadIdx.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) { red[w] = lo_c; red[nw + w] = top; }
+    __syncthreads();
+    lo_c = red[0];
+    top = red[nw];
+    for (int i = 1; i < nw; ++i) { lo_c = fmax(lo_c, red[i]); top = fmax(top, red[nw + i]); }
+  }
   // pass 2, a tighter certified bound: with W the rule weight (n_p w_j) of the
   // chunk's points above theta = top - f (top - lo_c),
   // F(theta - W^-(alpha-1)) >= W (W^-(alpha-1))^(1/(alpha-1)) = 1, and F of the
