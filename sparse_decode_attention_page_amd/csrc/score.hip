@@ -210,7 +210,11 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   // more in flight from the start the per-tile latency grows with the deeper
   // memory queue and the first tile arrives later, measured on cold HBM)
   u32x4 ring[2][C::kLoads];
+  // tile loads are issued at raised wave priority (measured: 0.1-0.6 us per launch
+  // faster; the whole prologue at raised priority was slower)
+  __builtin_amdgcn_s_setprio(3);
   score_load_tile<T, DIM, G, F8>(ring[0], mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
+  __builtin_amdgcn_s_setprio(0);
 
   const double c = D.scale, c2 = D.scale * D.scale;
   const unsigned char *rec = tile + lane * C::kRecBytes;
@@ -227,9 +231,12 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
       if (lt > 0) lds_barrier();  // the previous tile and exchange are fully read
       score_stash_tile<T, DIM, G, F8>(ring[lt & 1], tile, tid);
       asm volatile("" ::: "memory");
-      if (lt + 1 < nt)
+      if (lt + 1 < nt) {
+        __builtin_amdgcn_s_setprio(3);  // the loads issue ahead of other waves' FMA stream
         score_load_tile<T, DIM, G, F8>(ring[(lt + 1) & 1], mbase, s_phys[lt + 1],
                                        ((t_begin + lt + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
+        __builtin_amdgcn_s_setprio(0);
+      }
       lds_barrier();
       if (lt == 0) asm volatile("" ::"s"(warm));
       if (lt == 0) EKV_MARK(0, 2);
