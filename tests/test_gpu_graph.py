@@ -4,7 +4,8 @@ eagerly.
 Two graphs on a 8,192-token, 32/8-head, bf16 slice with pages of 16:
 
 * the decode step (score_pages -> select_pages_gauss / select_pages_topk ->
-  entmax_decode_sparse) captured once; before each of four replays the query
+  entmax_decode_sparse, and the group-shared forms: one set per KV head)
+  captured once; before each of four replays the query
   is overwritten eagerly, and the replay's page sets, counts and outputs are
   compared with an eager run on the same query;
 * the streaming step of the EntmaxKV summary (section 2, pages' metadata kept
@@ -50,23 +51,36 @@ class _Step:
         self.shape, self.policy, self.alpha, self.delta, self.k = shape, policy, alpha, delta, k
         self.box = torch.empty((B, Hq, MP), device="cuda")
         self.mu, self.var = torch.empty_like(self.box), torch.empty_like(self.box)
-        self.sel = torch.full((B, Hq, MP), -7, dtype=torch.int32, device="cuda")
-        self.cnt = torch.full((B, Hq), -7, dtype=torch.int32, device="cuda")
+        nset = inp.Hkv if policy.endswith("_group") else Hq  # group policies: one set per KV head
+        self.sel = torch.full((B, nset, MP), -7, dtype=torch.int32, device="cuda")
+        self.cnt = torch.full((B, nset), -7, dtype=torch.int32, device="cuda")
         self.out = torch.full((B, Hq, d), float("nan"), device="cuda")
         self.ws_s = E.workspace(shape, E.CALL_SCORE)
         self.ws_g = E.workspace(shape, E.CALL_GAUSS)
         self.ws_t = E.workspace(shape, E.CALL_TOPK)
         self.ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE)
+        self.ws_gg = E.workspace(shape, E.CALL_GAUSS_GROUP)
+        self.ws_tg = E.workspace(shape, E.CALL_TOPK_GROUP)
+        self.ws_dg = E.workspace(shape, E.CALL_DECODE_GROUP)
 
     def __call__(self, q, k_pool, v_pool, meta, pt, sl):
         E.score_pages(self.shape, q, meta, pt, sl, self.box, self.mu, self.var, ws=self.ws_s)
         if self.policy == "gauss":
             E.select_pages_gauss(self.shape, self.box, self.mu, self.var, sl, self.alpha, self.delta,
                                  self.sel, self.cnt, ws=self.ws_g)
-        else:
+        elif self.policy == "topk":
             E.select_pages_topk(self.shape, self.box, sl, self.k, self.sel, self.cnt, ws=self.ws_t)
-        E.entmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
-                               self.out, ws=self.ws_d)
+        elif self.policy == "gauss_group":
+            E.select_pages_gauss_group(self.shape, self.box, self.mu, self.var, sl, self.alpha, self.delta,
+                                       self.sel, self.cnt, ws=self.ws_gg)
+        else:
+            E.select_pages_topk_group(self.shape, self.box, sl, self.k, self.sel, self.cnt, ws=self.ws_tg)
+        if self.policy.endswith("_group"):
+            E.entmax_decode_sparse_group(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
+                                         self.out, ws=self.ws_dg)
+        else:
+            E.entmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
+                                   self.out, ws=self.ws_d)
 
 
 def _capture(fn):
@@ -98,7 +112,7 @@ def _close(x, y, tag, tol=1e-6):
     assert float(num / den) <= tol, f"{tag}: relative L2 {float(num / den):.3e}"
 
 
-@pytest.mark.parametrize("policy", ["gauss", "topk"])
+@pytest.mark.parametrize("policy", ["gauss", "topk", "gauss_group", "topk_group"])
 def test_graph_replays_match_eager_step(policy):
     import torch
     wl, inp, shape, meta = _inputs(11)
