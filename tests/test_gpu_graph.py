@@ -4,8 +4,9 @@ eagerly.
 Two graphs on a 8,192-token, 32/8-head, bf16 slice with pages of 16:
 
 * the decode step (score_pages -> select_pages_gauss / select_pages_topk ->
-  entmax_decode_sparse, and the group-shared forms: one set per KV head)
-  captured once; before each of four replays the query
+  entmax_decode_sparse, the group-shared forms with one set per KV head, the
+  compact-record scorer, softmax over the kept pages) captured once; before each
+  of four replays the query
   is overwritten eagerly, and the replay's page sets, counts and outputs are
   compared with an eager run on the same query;
 * the streaming step of the EntmaxKV summary (section 2, pages' metadata kept
@@ -62,10 +63,18 @@ class _Step:
         self.ws_gg = E.workspace(shape, E.CALL_GAUSS_GROUP)
         self.ws_tg = E.workspace(shape, E.CALL_TOPK_GROUP)
         self.ws_dg = E.workspace(shape, E.CALL_DECODE_GROUP)
+        self.ws_sm = E.workspace(shape, E.CALL_SOFTMAX_SPARSE)
+        self.meta8 = None
 
     def __call__(self, q, k_pool, v_pool, meta, pt, sl):
-        E.score_pages(self.shape, q, meta, pt, sl, self.box, self.mu, self.var, ws=self.ws_s)
-        if self.policy == "gauss":
+        if self.policy == "gauss_f8":  # compact records, built once from the same keys
+            if self.meta8 is None:
+                self.meta8 = E.meta_f8_empty(self.shape)
+                E.build_page_meta_f8(self.shape, k_pool, pt, sl, self.meta8)
+            E.score_pages_f8(self.shape, q, self.meta8, pt, sl, self.box, self.mu, self.var, ws=self.ws_s)
+        else:
+            E.score_pages(self.shape, q, meta, pt, sl, self.box, self.mu, self.var, ws=self.ws_s)
+        if self.policy in ("gauss", "gauss_f8", "gauss_softmax"):
             E.select_pages_gauss(self.shape, self.box, self.mu, self.var, sl, self.alpha, self.delta,
                                  self.sel, self.cnt, ws=self.ws_g)
         elif self.policy == "topk":
@@ -78,6 +87,9 @@ class _Step:
         if self.policy.endswith("_group"):
             E.entmax_decode_sparse_group(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
                                          self.out, ws=self.ws_dg)
+        elif self.policy == "gauss_softmax":
+            E.softmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.out,
+                                    ws=self.ws_sm)
         else:
             E.entmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
                                    self.out, ws=self.ws_d)
@@ -112,7 +124,7 @@ def _close(x, y, tag, tol=1e-6):
     assert float(num / den) <= tol, f"{tag}: relative L2 {float(num / den):.3e}"
 
 
-@pytest.mark.parametrize("policy", ["gauss", "topk", "gauss_group", "topk_group"])
+@pytest.mark.parametrize("policy", ["gauss", "topk", "gauss_group", "topk_group", "gauss_f8", "gauss_softmax"])
 def test_graph_replays_match_eager_step(policy):
     import torch
     wl, inp, shape, meta = _inputs(11)
