@@ -124,9 +124,14 @@ int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const i
 /*
  * score_pages -- [EntmaxKV s.2.A], per (b, h, p < N_b) with c = scale:
  *   box = c * sum_i max(q_i kmin_i, q_i kmax_i)   (upper bound on every score in
- *         the page; fp64 sum of exact products, stored rounded toward +inf)
+ *         the page; stored rounded toward +inf)
  *   mu  = c * sum_i q_i mean_i,   var = c^2 * sum_i q_i^2 var_i
  *         (Gaussian model of the page's scores; stored round-to-nearest-even)
+ * Each sum is taken in fp64 over i = 0 .. d-1 in that order, adding each term
+ * once (bf16 products and f32 products with q and k are exact in fp64; an f32
+ * q_i^2 var_i is rounded to fp64 first), so the stored floats equal an fp64
+ * evaluation of these definitions in index order bit for bit.  Keys are
+ * assumed finite (an infinite k_min / k_max may give a NaN box).
  * Entries p >= N_b are not written.  An out-of-range page-table entry gives NaN
  * in all three outputs.  ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_SCORE).
  */
@@ -210,7 +215,12 @@ int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const 
  *   p_t = [(alpha-1) s_t - tau]_+^(1/(alpha-1)) / Z,  out = sum_t p_t v_t,
  * tau the root of sum_t [(alpha-1)s_t - tau]_+^(1/(alpha-1)) = 1 over the kept
  * tokens, Z the sum of the unnormalized weights.  tau_method: 0 = root finder
- * (any alpha), 1 = sort closed form (alpha == 2 only).  tau (nullable, float64
+ * (any alpha), 1 = sparsemax sort closed form (alpha == 2 only; any other
+ * alpha with tau_method 1 is ENTMAXKV_ERR_INVALID_ARGUMENT).  The sort runs
+ * over the row's candidate tokens, those above a certified lower bound on tau
+ * (every other token is outside the support), when at most 1024 of them
+ * remain; a row with more candidates is solved by the root finder, which
+ * reaches the same tau to fp64 resolution.  tau (nullable, float64
  * [B][Hq]) receives tau/(alpha-1).  weights_out (nullable, float32
  * [B][Hq][max_pages*P], for tests) receives p at logical token positions and
  * zero elsewhere.  A row with sel_cnt = 0 gets out = 0, tau = NaN; a row whose
@@ -260,7 +270,10 @@ int32_t entmax_decode_sparse_group(const entmaxkv_shape *shape, const void *q, c
                                    size_t ws_bytes, hipStream_t stream);
 
 /* entmax_decode_full -- the same attention over every cached token (the
- * full-cache entmax baseline of [EntmaxKV s.4]). */
+ * full-cache entmax baseline of [EntmaxKV s.4]).  tau_method, tau,
+ * weights_out and the alpha rules as in entmax_decode_sparse (the sort form
+ * runs over the candidates of the whole cache under the same 1024 limit).
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_DECODE_FULL). */
 int32_t entmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,
                            const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
                            double alpha, int32_t tau_method, float *out, double *tau,

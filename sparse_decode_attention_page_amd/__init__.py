@@ -139,9 +139,13 @@ def make_shape(q, k_pool, page_table, scale: float = 0.0) -> Shape:
     return Shape(B, Hq, Hkv, d, P, page_table.shape[1], phys, dt, float(scale))
 
 
-def _ptr(t, dtype=None, name="tensor"):
+def _ptr(t, dtype=None, name="tensor", numel=None):
+    """Device pointer of t after the checks the kernels rely on: at least `numel`
+    elements (the extent the shape implies), on the device, contiguous, dtype."""
     if t is None:
         return None
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements; the shape needs {numel}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
@@ -182,19 +186,48 @@ def _check(fn, st):
         raise EntmaxKVError(fn, st)
 
 
+def _call(fn, shape: Shape, which, ws, args, stream):
+    """Run a workspace-taking call: args are the already checked pointers and
+    scalars between the shape and the workspace; the workspace is allocated only
+    after every argument has passed its checks."""
+    wp, wn, keep = _ws(shape, which, ws)
+    st = getattr(load(), fn)(ctypes.byref(shape), *args, wp, wn, _stream(stream))
+    _check(fn, st)
+
+
 def _kv_dtype(shape: Shape):
     torch = _torch()
     return torch.bfloat16 if shape.dtype == BF16 else torch.float32
 
 
+class _N:
+    """Element counts of every buffer a call reads or writes, from the shape."""
+
+    def __init__(self, s: Shape):
+        B, Hq, Hkv, d, P, MP, NP = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.page_size, s.max_pages,
+                                    s.num_phys_pages)
+        self.q = self.out = B * Hq * d
+        self.pool = NP * Hkv * P * d
+        self.meta = NP * Hkv * 4 * d
+        self.meta_f8 = NP * Hkv * 6 * d
+        self.page_table = B * MP
+        self.batch = B            # seq_lens, seq_mask, from_token
+        self.rows = B * Hq        # sel_cnt, tau, tau_hat, lse
+        self.per_page = B * Hq * MP   # box, mu, var, sel_idx
+        self.grows = B * Hkv      # group sel_cnt
+        self.gper_page = B * Hkv * MP  # group sel_idx
+        self.weights = B * Hq * MP * P
+        self.token_rows = B * Hkv * d  # k_new, v_new
+
+
 def build_page_meta(shape: Shape, k_pool, page_table, seq_lens, meta, from_token=None, stream=None):
     torch = _torch()
-    kd = _kv_dtype(shape)
-    st = load().build_page_meta(ctypes.byref(shape), _ptr(k_pool, kd, "k_pool"),
-                                _ptr(page_table, torch.int32, "page_table"),
-                                _ptr(seq_lens, torch.int32, "seq_lens"),
-                                _ptr(from_token, torch.int32, "from_token"), _ptr(meta, kd, "meta"),
-                                _stream(stream))
+    kd, n = _kv_dtype(shape), _N(shape)
+    st = load().build_page_meta(ctypes.byref(shape), _ptr(k_pool, kd, "k_pool", n.pool),
+                                _ptr(page_table, torch.int32, "page_table", n.page_table),
+                                _ptr(seq_lens, torch.int32, "seq_lens", n.batch),
+                                _ptr(from_token, torch.int32, "from_token", n.batch),
+                                _ptr(meta, kd, "meta", n.meta), _stream(stream))
     _check("build_page_meta", st)
     return meta
 
@@ -206,21 +239,14 @@ def meta_f8_empty(shape: Shape):
                        device="cuda")
 
 
-def _meta_f8(shape: Shape, meta):
-    torch = _torch()
-    need = shape.num_phys_pages * shape.n_kv_heads * 6 * shape.head_dim
-    if meta.numel() * meta.element_size() < need:
-        raise ValueError(f"compact metadata needs {need} bytes")
-    return _ptr(meta, torch.uint8, "meta")
-
-
 def build_page_meta_f8(shape: Shape, k_pool, page_table, seq_lens, meta, from_token=None, stream=None):
     """Compact records: k_min / k_max bf16, mean / var OCP FP8 E4M3 (uint8 meta)."""
     torch = _torch()
-    st = load().build_page_meta_f8(ctypes.byref(shape), _ptr(k_pool, _kv_dtype(shape), "k_pool"),
-                                   _ptr(page_table, torch.int32, "page_table"),
-                                   _ptr(seq_lens, torch.int32, "seq_lens"),
-                                   _ptr(from_token, torch.int32, "from_token"), _meta_f8(shape, meta),
+    n = _N(shape)
+    st = load().build_page_meta_f8(ctypes.byref(shape), _ptr(k_pool, _kv_dtype(shape), "k_pool", n.pool),
+                                   _ptr(page_table, torch.int32, "page_table", n.page_table),
+                                   _ptr(seq_lens, torch.int32, "seq_lens", n.batch),
+                                   _ptr(from_token, torch.int32, "from_token", n.batch), _meta_f8(shape, meta),
                                    _stream(stream))
     _check("build_page_meta_f8", st)
     return meta
@@ -231,146 +257,130 @@ def append_token(shape: Shape, k_new, v_new, k_pool, v_pool, page_table, seq_len
     """Write token seq_lens[b] - 1's K and V rows (k_new / v_new [B, Hkv, d]) into the pools and
     rebuild that page's metadata (compact records when compact=True)."""
     torch = _torch()
-    kd = _kv_dtype(shape)
-    st = load().append_token(ctypes.byref(shape), _ptr(k_new, kd, "k_new"), _ptr(v_new, kd, "v_new"),
-                             _ptr(k_pool, kd, "k_pool"), _ptr(v_pool, kd, "v_pool"),
-                             _ptr(page_table, torch.int32, "page_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
-                             _meta_f8(shape, meta) if compact else _ptr(meta, kd, "meta"), 1 if compact else 0,
+    kd, n = _kv_dtype(shape), _N(shape)
+    st = load().append_token(ctypes.byref(shape), _ptr(k_new, kd, "k_new", n.token_rows),
+                             _ptr(v_new, kd, "v_new", n.token_rows), _ptr(k_pool, kd, "k_pool", n.pool),
+                             _ptr(v_pool, kd, "v_pool", n.pool), _ptr(page_table, torch.int32, "page_table", n.page_table),
+                             _ptr(seq_lens, torch.int32, "seq_lens", n.batch),
+                             _meta_f8(shape, meta) if compact else _ptr(meta, kd, "meta", n.meta), 1 if compact else 0,
                              _stream(stream))
     _check("append_token", st)
     return meta
 
 
-def score_pages_f8(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=None, stream=None):
+def _score_args(shape: Shape, q, page_table, seq_lens, box, mu, var):
     torch = _torch()
-    wp, wn, keep = _ws(shape, CALL_SCORE, ws)
-    st = load().score_pages_f8(ctypes.byref(shape), _ptr(q, _kv_dtype(shape), "q"), _meta_f8(shape, meta),
-                               _ptr(page_table, torch.int32, "page_table"),
-                               _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(box, torch.float32, "box"),
-                               _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"), wp, wn,
-                               _stream(stream))
-    _check("score_pages_f8", st)
+    n = _N(shape)
+    return (_ptr(q, _kv_dtype(shape), "q", n.q), _ptr(page_table, torch.int32, "page_table", n.page_table),
+            _ptr(seq_lens, torch.int32, "seq_lens", n.batch), _ptr(box, torch.float32, "box", n.per_page),
+            _ptr(mu, torch.float32, "mu", n.per_page), _ptr(var, torch.float32, "var", n.per_page))
+
+
+def score_pages_f8(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=None, stream=None):
+    qp, pt, sl, bp, mp, vp = _score_args(shape, q, page_table, seq_lens, box, mu, var)
+    _call("score_pages_f8", shape, CALL_SCORE, ws, (qp, _meta_f8(shape, meta), pt, sl, bp, mp, vp), stream)
     return box, mu, var
 
 
 def score_pages(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=None, stream=None):
-    torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_SCORE, ws)
-    st = load().score_pages(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(meta, kd, "meta"),
-                            _ptr(page_table, torch.int32, "page_table"),
-                            _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(box, torch.float32, "box"),
-                            _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"), wp, wn,
-                            _stream(stream))
-    _check("score_pages", st)
+    qp, pt, sl, bp, mp, vp = _score_args(shape, q, page_table, seq_lens, box, mu, var)
+    mt = _ptr(meta, _kv_dtype(shape), "meta", _N(shape).meta)
+    _call("score_pages", shape, CALL_SCORE, ws, (qp, mt, pt, sl, bp, mp, vp), stream)
     return box, mu, var
+
+
+def _sel_args(shape: Shape, sel_idx, sel_cnt, group=False):
+    torch = _torch()
+    n = _N(shape)
+    return (_ptr(sel_idx, torch.int32, "sel_idx", n.gper_page if group else n.per_page),
+            _ptr(sel_cnt, torch.int32, "sel_cnt", n.grows if group else n.rows))
+
+
+def _gauss_args(shape: Shape, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask):
+    torch = _torch()
+    n = _N(shape)
+    return (_ptr(box, torch.float32, "box", n.per_page), _ptr(mu, torch.float32, "mu", n.per_page),
+            _ptr(var, torch.float32, "var", n.per_page), _ptr(seq_lens, torch.int32, "seq_lens", n.batch),
+            float(alpha), float(delta), float(n_sigma), _ptr(seq_mask, torch.uint8, "seq_mask", n.batch))
+
+
+def _topk_args(shape: Shape, box, seq_lens, k, seq_mask):
+    torch = _torch()
+    n = _N(shape)
+    return (_ptr(box, torch.float32, "box", n.per_page), _ptr(seq_lens, torch.int32, "seq_lens", n.batch), int(k),
+            _ptr(seq_mask, torch.uint8, "seq_mask", n.batch))
 
 
 def select_pages_topk(shape: Shape, box, seq_lens, k, sel_idx, sel_cnt, seq_mask=None, ws=None,
                       stream=None):
-    torch = _torch()
-    wp, wn, keep = _ws(shape, CALL_TOPK, ws)
-    st = load().select_pages_topk(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
-                                  _ptr(seq_lens, torch.int32, "seq_lens"), int(k),
-                                  _ptr(seq_mask, torch.uint8, "seq_mask"),
-                                  _ptr(sel_idx, torch.int32, "sel_idx"),
-                                  _ptr(sel_cnt, torch.int32, "sel_cnt"), wp, wn, _stream(stream))
-    _check("select_pages_topk", st)
+    args = (*_topk_args(shape, box, seq_lens, k, seq_mask), *_sel_args(shape, sel_idx, sel_cnt))
+    _call("select_pages_topk", shape, CALL_TOPK, ws, args, stream)
     return sel_idx, sel_cnt
 
 
 def select_pages_gauss(shape: Shape, box, mu, var, seq_lens, alpha, delta, sel_idx, sel_cnt,
                        n_sigma=3.0, seq_mask=None, tau_hat=None, ws=None, stream=None):
-    torch = _torch()
-    wp, wn, keep = _ws(shape, CALL_GAUSS, ws)
-    st = load().select_pages_gauss(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
-                                   _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"),
-                                   _ptr(seq_lens, torch.int32, "seq_lens"), float(alpha), float(delta),
-                                   float(n_sigma), _ptr(seq_mask, torch.uint8, "seq_mask"),
-                                   _ptr(sel_idx, torch.int32, "sel_idx"),
-                                   _ptr(sel_cnt, torch.int32, "sel_cnt"),
-                                   _ptr(tau_hat, torch.float64, "tau_hat"), wp, wn, _stream(stream))
-    _check("select_pages_gauss", st)
+    args = (*_gauss_args(shape, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask),
+            *_sel_args(shape, sel_idx, sel_cnt), _ptr(tau_hat, _torch().float64, "tau_hat", _N(shape).rows))
+    _call("select_pages_gauss", shape, CALL_GAUSS, ws, args, stream)
     return sel_idx, sel_cnt
 
 
 def select_pages_topk_group(shape: Shape, box, seq_lens, k, sel_idx, sel_cnt, seq_mask=None, ws=None,
                             stream=None):
     """One set per KV head: sel_idx int32 [B, Hkv, max_pages], sel_cnt int32 [B, Hkv]."""
-    torch = _torch()
-    wp, wn, keep = _ws(shape, CALL_TOPK_GROUP, ws)
-    st = load().select_pages_topk_group(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
-                                        _ptr(seq_lens, torch.int32, "seq_lens"), int(k),
-                                        _ptr(seq_mask, torch.uint8, "seq_mask"),
-                                        _ptr(sel_idx, torch.int32, "sel_idx"),
-                                        _ptr(sel_cnt, torch.int32, "sel_cnt"), wp, wn, _stream(stream))
-    _check("select_pages_topk_group", st)
+    args = (*_topk_args(shape, box, seq_lens, k, seq_mask), *_sel_args(shape, sel_idx, sel_cnt, group=True))
+    _call("select_pages_topk_group", shape, CALL_TOPK_GROUP, ws, args, stream)
     return sel_idx, sel_cnt
 
 
 def select_pages_gauss_group(shape: Shape, box, mu, var, seq_lens, alpha, delta, sel_idx, sel_cnt,
                              n_sigma=3.0, seq_mask=None, tau_hat=None, ws=None, stream=None):
     """One set per KV head: the union of the group's per-head Gaussian sets."""
-    torch = _torch()
-    wp, wn, keep = _ws(shape, CALL_GAUSS_GROUP, ws)
-    st = load().select_pages_gauss_group(ctypes.byref(shape), _ptr(box, torch.float32, "box"),
-                                         _ptr(mu, torch.float32, "mu"), _ptr(var, torch.float32, "var"),
-                                         _ptr(seq_lens, torch.int32, "seq_lens"), float(alpha), float(delta),
-                                         float(n_sigma), _ptr(seq_mask, torch.uint8, "seq_mask"),
-                                         _ptr(sel_idx, torch.int32, "sel_idx"),
-                                         _ptr(sel_cnt, torch.int32, "sel_cnt"),
-                                         _ptr(tau_hat, torch.float64, "tau_hat"), wp, wn, _stream(stream))
-    _check("select_pages_gauss_group", st)
+    args = (*_gauss_args(shape, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask),
+            *_sel_args(shape, sel_idx, sel_cnt, group=True),
+            _ptr(tau_hat, _torch().float64, "tau_hat", _N(shape).rows))
+    _call("select_pages_gauss_group", shape, CALL_GAUSS_GROUP, ws, args, stream)
     return sel_idx, sel_cnt
+
+
+def _decode_args(shape: Shape, q, k_pool, v_pool, page_table, seq_lens):
+    torch = _torch()
+    kd, n = _kv_dtype(shape), _N(shape)
+    return (_ptr(q, kd, "q", n.q), _ptr(k_pool, kd, "k_pool", n.pool), _ptr(v_pool, kd, "v_pool", n.pool),
+            _ptr(page_table, torch.int32, "page_table", n.page_table), _ptr(seq_lens, torch.int32, "seq_lens", n.batch))
+
+
+def _out_args(shape: Shape, out, tau, weights_out):
+    torch = _torch()
+    n = _N(shape)
+    return (_ptr(out, torch.float32, "out", n.out), _ptr(tau, torch.float64, "tau", n.rows),
+            _ptr(weights_out, torch.float32, "weights_out", n.weights))
 
 
 def entmax_decode_sparse_group(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt,
                                alpha, out, tau=None, weights_out=None, tau_method=0, ws=None, stream=None):
     """entmax_decode_sparse with one kept set per KV head (sel_idx [B, Hkv, max_pages])."""
-    torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_DECODE_GROUP, ws)
-    st = load().entmax_decode_sparse_group(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
-                                           _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
-                                           _ptr(seq_lens, torch.int32, "seq_lens"),
-                                           _ptr(sel_idx, torch.int32, "sel_idx"),
-                                           _ptr(sel_cnt, torch.int32, "sel_cnt"), float(alpha), int(tau_method),
-                                           _ptr(out, torch.float32, "out"), _ptr(tau, torch.float64, "tau"),
-                                           _ptr(weights_out, torch.float32, "weights_out"), wp, wn,
-                                           _stream(stream))
-    _check("entmax_decode_sparse_group", st)
+    args = (*_decode_args(shape, q, k_pool, v_pool, page_table, seq_lens),
+            *_sel_args(shape, sel_idx, sel_cnt, group=True), float(alpha), int(tau_method),
+            *_out_args(shape, out, tau, weights_out))
+    _call("entmax_decode_sparse_group", shape, CALL_DECODE_GROUP, ws, args, stream)
     return out
 
 
 def entmax_decode_sparse(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt,
                          alpha, out, tau=None, weights_out=None, tau_method=0, ws=None, stream=None):
-    torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_DECODE_SPARSE, ws)
-    st = load().entmax_decode_sparse(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
-                                     _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
-                                     _ptr(seq_lens, torch.int32, "seq_lens"),
-                                     _ptr(sel_idx, torch.int32, "sel_idx"),
-                                     _ptr(sel_cnt, torch.int32, "sel_cnt"), float(alpha), int(tau_method),
-                                     _ptr(out, torch.float32, "out"), _ptr(tau, torch.float64, "tau"),
-                                     _ptr(weights_out, torch.float32, "weights_out"), wp, wn,
-                                     _stream(stream))
-    _check("entmax_decode_sparse", st)
+    args = (*_decode_args(shape, q, k_pool, v_pool, page_table, seq_lens), *_sel_args(shape, sel_idx, sel_cnt),
+            float(alpha), int(tau_method), *_out_args(shape, out, tau, weights_out))
+    _call("entmax_decode_sparse", shape, CALL_DECODE_SPARSE, ws, args, stream)
     return out
 
 
 def entmax_decode_full(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, alpha, out, tau=None,
                        weights_out=None, tau_method=0, ws=None, stream=None):
-    torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_DECODE_FULL, ws)
-    st = load().entmax_decode_full(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
-                                   _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
-                                   _ptr(seq_lens, torch.int32, "seq_lens"), float(alpha), int(tau_method),
-                                   _ptr(out, torch.float32, "out"), _ptr(tau, torch.float64, "tau"),
-                                   _ptr(weights_out, torch.float32, "weights_out"), wp, wn,
-                                   _stream(stream))
-    _check("entmax_decode_full", st)
+    args = (*_decode_args(shape, q, k_pool, v_pool, page_table, seq_lens), float(alpha), int(tau_method),
+            *_out_args(shape, out, tau, weights_out))
+    _call("entmax_decode_full", shape, CALL_DECODE_FULL, ws, args, stream)
     return out
 
 
@@ -378,25 +388,18 @@ def softmax_decode_sparse(shape: Shape, q, k_pool, v_pool, page_table, seq_lens,
                           lse=None, ws=None, stream=None):
     """Softmax attention over the kept pages (the selection entmax_decode_sparse takes)."""
     torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_SOFTMAX_SPARSE, ws)
-    st = load().softmax_decode_sparse(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
-                                      _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
-                                      _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(sel_idx, torch.int32, "sel_idx"),
-                                      _ptr(sel_cnt, torch.int32, "sel_cnt"), _ptr(out, torch.float32, "out"),
-                                      _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream))
-    _check("softmax_decode_sparse", st)
+    n = _N(shape)
+    args = (*_decode_args(shape, q, k_pool, v_pool, page_table, seq_lens), *_sel_args(shape, sel_idx, sel_cnt),
+            _ptr(out, torch.float32, "out", n.out), _ptr(lse, torch.float32, "lse", n.rows))
+    _call("softmax_decode_sparse", shape, CALL_SOFTMAX_SPARSE, ws, args, stream)
     return out
 
 
 def softmax_decode_full(shape: Shape, q, k_pool, v_pool, page_table, seq_lens, out, lse=None,
                         ws=None, stream=None):
     torch = _torch()
-    kd = _kv_dtype(shape)
-    wp, wn, keep = _ws(shape, CALL_SOFTMAX, ws)
-    st = load().softmax_decode_full(ctypes.byref(shape), _ptr(q, kd, "q"), _ptr(k_pool, kd, "k_pool"),
-                                    _ptr(v_pool, kd, "v_pool"), _ptr(page_table, torch.int32, "page_table"),
-                                    _ptr(seq_lens, torch.int32, "seq_lens"), _ptr(out, torch.float32, "out"),
-                                    _ptr(lse, torch.float32, "lse"), wp, wn, _stream(stream))
-    _check("softmax_decode_full", st)
+    n = _N(shape)
+    args = (*_decode_args(shape, q, k_pool, v_pool, page_table, seq_lens), _ptr(out, torch.float32, "out", n.out),
+            _ptr(lse, torch.float32, "lse", n.rows))
+    _call("softmax_decode_full", shape, CALL_SOFTMAX, ws, args, stream)
     return out

@@ -298,9 +298,9 @@ static int32_t decode_common(const entmaxkv_shape *shape, const void *q, const v
   if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(full ? full_ws_bytes(D) : decode_ws_bytes(D, false), ws, ws_bytes))) return st;
-  if (full)  // the sparsemax sort form is a sparse-path option; the full path's root finder is exact
-    return hip_status(launch_entmax_full(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, alpha, out,
-                                         tau, weights_out, ws, stream));
+  if (full)
+    return hip_status(launch_entmax_full(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, alpha,
+                                         tau_method, out, tau, weights_out, ws, stream));
   return hip_status(launch_entmax_decode(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
                                          sel_cnt, alpha, tau_method, out, tau, weights_out, ws, stream));
 }

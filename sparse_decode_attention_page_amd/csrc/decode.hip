@@ -1375,14 +1375,14 @@ static hipError_t launch_full_p(const Dims &D, const DecodeParams &dp, const voi
 }
 
 hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
-                              const int32_t *page_table, const int32_t *seq_lens, double alpha, float *out,
-                              double *tau, float *weights_out, void *ws, hipStream_t s) {
+                              const int32_t *page_table, const int32_t *seq_lens, double alpha, int tau_method,
+                              float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
   DecodeParams dp;
   dp.a = alpha - 1.0;
   dp.beta = 1.0 / dp.a;
   dp.c = D.scale;
   dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
-  dp.tau_method = 0;  // safeguarded Newton (the sort form is a sparse-path option)
+  dp.tau_method = tau_method;
   if (dtype == ENTMAXKV_BF16) {
     if (D.d == 64) return launch_full_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
     return launch_full_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);

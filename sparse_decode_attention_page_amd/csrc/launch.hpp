@@ -83,8 +83,8 @@ hipError_t launch_gauss_group(const Dims &D, const float *box, const float *mu, 
 
 size_t full_ws_bytes(const Dims &D);
 hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
-                              const int32_t *page_table, const int32_t *seq_lens, double alpha, float *out,
-                              double *tau, float *weights_out, void *ws, hipStream_t s);
+                              const int32_t *page_table, const int32_t *seq_lens, double alpha, int tau_method,
+                              float *out, double *tau, float *weights_out, void *ws, hipStream_t s);
 
 size_t softmax_ws_bytes(const Dims &D);
 size_t softmax_sparse_ws_bytes(const Dims &D);

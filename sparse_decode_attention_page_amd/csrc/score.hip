@@ -13,17 +13,20 @@
 // rows kmin | kmax | mean | var of d elements each).  Design:
 //  * a block scores two tiles of 64 logical pages of one (b, KV head g); the G
 //    query heads of the group share every record read (GQA reuse);
-//  * wave k of the block handles metadata row k for all 64 pages (lane = page), so
-//    mu and var are finished inside one wave and the box needs only the kmin and
-//    kmax halves swapped between waves 0 and 1 (a 64 x G x 8-byte exchange);
+//  * the four waves of the block split the record's work, lane = page: waves 0
+//    and 1 each form the box of half of the G query heads from the k_min and
+//    k_max rows (per coordinate, in index order, both exact products are added,
+//    one of them with a zero coefficient, so the fp64 sum is the definition's
+//    sum of max(q_i kmin_i, q_i kmax_i) added in the same order, bit for bit),
+//    wave 2 forms mu from the mean row and wave 3 var from the variance row;
 //  * tiles are fetched with coalesced 16-byte vector loads into registers (the
 //    second tile while the first is scored), then written to LDS with
 //    the 16-byte chunks of each record XOR-swizzled by the record index, so that
 //    the lane-per-record reads of the compute hit distinct banks;
 //  * the query-derived coefficients (q-, q+, q, q^2 in fp64, one table per
 //    (b, g) row and kind) are written once to a workspace table at the start and
-//    read back through scalar loads, so the inner loop is one fp64 FMA per
-//    (element, head) on exact products with a wave-uniform operand.  The table's
+//    read back through scalar loads, so the inner loop is fp64 FMAs on exact
+//    products with a wave-uniform operand.  The table's
 //    lines are pulled into the scalar cache with one batch of loads that overlaps
 //    the tile fetch: otherwise the first tile's compute issues its coefficient
 //    loads a few lines at a time, each a full L2 round trip behind the stream;
@@ -39,7 +42,7 @@
 namespace ekv {
 
 constexpr int kTilePages = 64;      // one page per lane
-constexpr int kScoreThreads = 256;  // four waves: one per metadata row kind
+constexpr int kScoreThreads = 256;  // four waves: box (two), mean, variance
 constexpr int kScoreTiles = 2;      // tiles per block
 static_assert(kScoreTiles * kTilePages <= kScoreThreads, "one page id per thread in the prologue");
 
@@ -84,7 +87,7 @@ struct ScoreCfg {
   static constexpr int kRecBytes = F8 ? 6 * DIM : 4 * DIM * (int)sizeof(T);
   static constexpr int kTileBytes = kTilePages * kRecBytes;
   static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
-  static constexpr int kLds = kTileBytes + G * kTilePages * 8 + kScoreTiles * (kTilePages + 1) * 4;
+  static constexpr int kLds = kTileBytes + kScoreTiles * (kTilePages + 1) * 4;
   static constexpr int kBlocksPerCu = (160 * 1024) / (kLds + 1024) >= 4 ? 4 : (160 * 1024) / (kLds + 1024);
   static constexpr int kCoefRow = 4 * DIM * G;         // doubles per (b, g) row: [kind][i][h]
   static constexpr int kWarmLines = DIM * G * 8 / 64;  // 64-byte lines of one kind's coefficients
@@ -125,15 +128,14 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
     float *__restrict__ var) {
   using C = ScoreCfg<T, DIM, G, F8>;
   constexpr int kE = C::kE;
-  constexpr int kGH = G > 1 ? G / 2 : 1;  // box heads finished by each of waves 0 and 1
+  constexpr int kGH = G > 1 ? G / 2 : 1;  // box heads of each of waves 0 and 1 (G = 1: wave 0 only)
   __shared__ __align__(16) unsigned char tile[C::kTileBytes];
-  __shared__ double xb[G][kTilePages];  // box halves swapped between waves 0 and 1
   __shared__ int s_phys[kScoreTiles][kTilePages];
   __shared__ int s_np[kScoreTiles];
   __shared__ int s_zero;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // metadata row kind
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // 0, 1 box; 2 mean; 3 variance
   const int n_tiles = D.B * D.Hkv * tiles_per_row;
   // blocks resident on one CU (i, i + n_cu, ...) take consecutive tile pairs
   const int nb = gridDim.x, bi = blockIdx.x;
@@ -197,7 +199,9 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   // wrote to LDS before it, so no load of the table can be scheduled earlier.
   // (coef_r stays restrict-qualified, which lets the reads be scalar loads.)
   const int zoff = __builtin_amdgcn_readfirstlane(s_zero);
-  const double *cf0 = coef_r + zoff + (size_t)row0 * C::kCoefRow + (size_t)wave * DIM * G;
+  // this wave's coefficient kinds: q- and q+ (box waves), q (mean), q^2 (variance)
+  const int kind0 = wave < 2 ? 0 : wave;
+  const double *cf0 = coef_r + zoff + (size_t)row0 * C::kCoefRow + (size_t)kind0 * DIM * G;
   // scalar-cache warm-up: one load per 64-byte line of this wave's coefficients,
   // all in flight together; consumed before the first tile is scored
   unsigned warm = 0;
@@ -205,6 +209,10 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
     const unsigned *cl = reinterpret_cast<const unsigned *>(cf0);
 #pragma unroll
     for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[i * 16];
+    if (wave < 2) {
+#pragma unroll
+      for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[(C::kWarmLines + i) * 16];
+    }
   }
   // two register buffers: tile lt + 1 is requested once tile lt is in LDS (with
   // more in flight from the start the per-tile latency grows with the deeper
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
 #pragma unroll
   for (int lt = 0; lt < kScoreTiles; ++lt) {
     if (lt < nt) {
-      if (lt > 0) lds_barrier();  // the previous tile and exchange are fully read
+      if (lt > 0) lds_barrier();  // the previous tile is fully read
       score_stash_tile<T, DIM, G, F8>(ring[lt & 1], tile, tid);
       asm volatile("" ::: "memory");
       if (lt + 1 < nt) {
@@ -241,68 +249,76 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
       if (lt == 0) asm volatile("" ::"s"(warm));
       if (lt == 0) EKV_MARK(0, 2);
 
-      // ---- wave = row kind, lane = page: acc[h] = sum_i coef[kind][i][h] * row_i
+      // ---- lane = page.  Box waves: acc[j] = sum_i (q-_i kmin_i + q+_i kmax_i)
+      // for head h0 + j, coordinate by coordinate; mean / variance waves:
+      // acc[h] = sum_i coef[kind][i][h] * row_i.
       const int row = (t_begin + lt) / tiles_per_row;
       const double *cf = cf0 + (size_t)(row - row0) * C::kCoefRow;
-      double acc[G];
+      const bool ok = s_phys[lt][lane] >= 0;
+      if (wave < 2) {
+        if (G > 1 || wave == 0) {  // wave-uniform
+          const int h0 = G > 1 ? wave * kGH : 0;
+          const double *cn = cf + h0, *cp = cf + DIM * G + h0;
+          double acc[kGH];
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0.0;
-      if (!F8 || wave < 2) {
+          for (int j = 0; j < kGH; ++j) acc[j] = 0.0;
 #pragma unroll 2
-        for (int ch = 0; ch < C::kRowChunks; ++ch) {
-          double x[kE];
-          Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
+          for (int ch = 0; ch < C::kRowChunks; ++ch) {
+            double xn[kE], xp[kE];
+            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (ch ^ sw) * 16), xn);
+            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((C::kRowChunks + ch) ^ sw) * 16), xp);
 #pragma unroll
-          for (int e = 0; e < kE; ++e) {
-            const double *ci = cf + (size_t)(ch * kE + e) * G;
+            for (int e = 0; e < kE; ++e) {
+              const size_t i = (size_t)(ch * kE + e) * G;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-              if constexpr (sizeof(T) == 2)
-                acc[h] = __builtin_fma(ci[h], x[e], acc[h]);  // exact product: fused == separate
-              else
-                acc[h] = acc[h] + ci[h] * x[e];               // fp32 keys: round the product first
+              for (int j = 0; j < kGH; ++j) {
+                // exact products (bf16 x bf16 in 16 bits, f32 x f32 in 48): fused == separate
+                acc[j] = __builtin_fma(cn[i + j], xn[e], acc[j]);
+                acc[j] = __builtin_fma(cp[i + j], xp[e], acc[j]);
+              }
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < kGH; ++j) outv[lt][j] = ok ? __double2float_ru(c * acc[j]) : NAN;
+        }
+      } else {
+        double acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.0;
+        if (!F8) {
+#pragma unroll 2
+          for (int ch = 0; ch < C::kRowChunks; ++ch) {
+            double x[kE];
+            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+              const double *ci = cf + (size_t)(ch * kE + e) * G;
+#pragma unroll
+              for (int h = 0; h < G; ++h) {
+                if constexpr (sizeof(T) == 2)
+                  acc[h] = __builtin_fma(ci[h], x[e], acc[h]);  // exact product: fused == separate
+                else
+                  acc[h] = acc[h] + ci[h] * x[e];               // fp32 keys: q^2 var rounds, as defined
+              }
+            }
+          }
+        } else {
+          // E4M3 mean / variance rows: 16 elements per chunk; q (bf16) times an
+          // E4M3 value has 12 significant bits, q^2 times one 20: exact in fp64
+          const int base = 2 * C::kRowChunks + (wave - 2) * C::kF8Chunks;
+#pragma unroll 2
+          for (int ch = 0; ch < C::kF8Chunks; ++ch) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(rec + ((base + ch) ^ sw) * 16);
+            const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const double xe = e4m3_to_f64((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+              const double *ci = cf + (size_t)(ch * 16 + e) * G;
+#pragma unroll
+              for (int h = 0; h < G; ++h) acc[h] = __builtin_fma(ci[h], xe, acc[h]);
             }
           }
         }
-      } else {
-        // E4M3 mean / variance rows: 16 elements per chunk; q (bf16) times an
-        // E4M3 value has 12 significant bits, q^2 times one 20: exact in fp64
-        const int base = 2 * C::kRowChunks + (wave - 2) * C::kF8Chunks;
-#pragma unroll 2
-        for (int ch = 0; ch < C::kF8Chunks; ++ch) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(rec + ((base + ch) ^ sw) * 16);
-          const unsigned w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const double xe = e4m3_to_f64((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-            const double *ci = cf + (size_t)(ch * 16 + e) * G;
-#pragma unroll
-            for (int h = 0; h < G; ++h) acc[h] = __builtin_fma(ci[h], xe, acc[h]);
-          }
-        }
-      }
-
-      // ---- box = (kmin part) + (kmax part); waves 0 / 1 finish heads [0, G/2) / [G/2, G)
-      const bool ok = s_phys[lt][lane] >= 0;
-      if (wave < 2) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const bool mine = G == 1 ? wave == 0 : (h / kGH) == wave;
-          if (!mine) xb[h][lane] = acc[h];
-        }
-      }
-      lds_barrier();
-      if (wave < 2) {
-#pragma unroll
-        for (int j = 0; j < kGH; ++j) {
-          const int h = G == 1 ? 0 : wave * kGH + j;
-          const double own = (G == 1 || wave == 0) ? acc[j] : acc[(G == 1 ? 0 : kGH) + j];
-          const double other = xb[h][lane];
-          const double s_min = wave == 0 ? own : other;
-          const double s_max = wave == 0 ? other : own;
-          outv[lt][j] = ok ? __double2float_ru(c * (s_min + s_max)) : NAN;
-        }
-      } else {
         const double sc = wave == 2 ? c : c2;
 #pragma unroll
         for (int h = 0; h < G; ++h) outv[lt][h] = ok ? (float)(sc * acc[h]) : NAN;

@@ -17,3 +17,13 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the cut margins the end-to-end GPU comparisons recorded."""
+    mod = sys.modules.get("gpu_util")
+    log = getattr(mod, "MARGIN_LOG", None) if mod else None
+    if log:
+        terminalreporter.write_sep("-", "cut margins (relative distance of the nearest decision from its cut)")
+        for line in log:
+            terminalreporter.write_line(line)

@@ -124,3 +124,53 @@ def sets_equal(sel_a, cnt_a, sel_b, cnt_b, rows=None):
             if ca != cb or not np.array_equal(sel_a[b, h, :ca], sel_b[b, h, :cb]):
                 bad.append((b, h, ca, cb))
     return bad
+
+
+# Cut margins of the end-to-end comparisons: (workload, cut, row, margin)
+# lines, printed in the terminal summary (tests/conftest.py).  A decision's
+# margin is its distance from the cut relative to max(1, |cut|); margins below
+# MARGIN_FLAG could flip under a last-bit difference of the threshold.
+MARGIN_LOG: list = []
+MARGIN_FLAG = 1e-12
+
+
+def gauss_keep_margin(box, mu, var, n_pages, tau_hat, delta, n_sigma=3.0):
+    """Smallest |min(mu + n_sigma sigma, box) - (tau_hat - delta)| over a row's valid pages."""
+    bx = np.asarray(box[:n_pages], np.float64)
+    m = np.asarray(mu[:n_pages], np.float64)
+    v = np.asarray(var[:n_pages], np.float64)
+    ok = np.isfinite(bx) & np.isfinite(m) & np.isfinite(v)
+    if not ok.any() or not np.isfinite(tau_hat):
+        return np.inf
+    est = np.minimum(m[ok] + n_sigma * np.sqrt(np.maximum(v[ok], 0.0)), bx[ok])
+    thr = tau_hat - delta
+    return float(np.min(np.abs(est - thr)) / max(1.0, abs(thr)))
+
+
+def topk_gap(box, n_pages, k):
+    """Relative gap between the k-th and (k+1)-th largest box of a row (inf when every page is kept);
+    ties are decided by page index on both sides, so a zero gap is not a risk."""
+    if n_pages <= k:
+        return np.inf
+    b = np.asarray(box[:n_pages], np.float64)
+    b = np.sort(np.where(np.isnan(b), -np.inf, b))[::-1]
+    return float((b[k - 1] - b[k]) / max(1.0, abs(b[k - 1])))
+
+
+def support_margin(q_row, k_pool, g, page_table_row, seq_len, P, sel_row, cnt, tau, scale, dtype):
+    """Smallest |s_t - tau| (score units) over the tokens of a row's kept pages (KV head g)."""
+    if cnt <= 0 or not np.isfinite(tau):
+        return np.inf
+    qf = synth.storage_to_f64(q_row, dtype)
+    worst = np.inf
+    for p in sel_row[:cnt]:
+        n = min(P, seq_len - int(p) * P)
+        kf = synth.storage_to_f64(k_pool[int(page_table_row[p]), g][:n], dtype)  # [n, d]
+        s = scale * (kf @ qf)
+        worst = min(worst, float(np.min(np.abs(s - tau))))
+    return worst / max(1.0, abs(tau))
+
+
+def log_margin(workload, cut, row, margin):
+    flag = "  << below %.0e" % MARGIN_FLAG if margin < MARGIN_FLAG else ""
+    MARGIN_LOG.append(f"{workload:18s} {cut:14s} row {row:5d}  margin {margin:.3e}{flag}")

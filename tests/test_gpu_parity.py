@@ -199,6 +199,12 @@ def test_entmax_decode_full(case, alpha):
     decode_check(inp, D, alpha, None, None, full=True)
 
 
+def test_entmax_decode_full_sort_alpha2(case):
+    """The full-cache decode with the sparsemax sort form (tau_method 1)."""
+    inp, D, _, _ = case
+    decode_check(inp, D, 2.0, None, None, full=True, tau_method=1)
+
+
 def test_softmax_decode_full(case):
     inp, D, _, _ = case
     t = torch()
