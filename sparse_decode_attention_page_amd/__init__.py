@@ -239,6 +239,10 @@ def meta_f8_empty(shape: Shape):
                        device="cuda")
 
 
+def _meta_f8(shape: Shape, meta):
+    return _ptr(meta, _torch().uint8, "meta", _N(shape).meta_f8)
+
+
 def build_page_meta_f8(shape: Shape, k_pool, page_table, seq_lens, meta, from_token=None, stream=None):
     """Compact records: k_min / k_max bf16, mean / var OCP FP8 E4M3 (uint8 meta)."""
     torch = _torch()

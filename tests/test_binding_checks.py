@@ -34,7 +34,8 @@ def full_args():
                 meta=t(NP * HKV * 4 * D, bf), page_table=t(B * MP, i32), seq_lens=t(B, i32),
                 box=t(B * HQ * MP), mu=t(B * HQ * MP), var=t(B * HQ * MP), sel_idx=t(B * HQ * MP, i32),
                 sel_cnt=t(B * HQ, i32), out=t(B * HQ * D, f32), tau=t(B * HQ, f64),
-                weights_out=t(B * HQ * MP * P, f32), lse=t(B * HQ, f32))
+                weights_out=t(B * HQ * MP * P, f32), lse=t(B * HQ, f32), meta8=t(NP * HKV * 6 * D, torch.uint8),
+                k_new=t(B * HKV * D, bf), v_new=t(B * HKV * D, bf))
 
 
 CALLS = {
@@ -57,6 +58,14 @@ CALLS = {
                                                                a["page_table"], a["seq_lens"], a["sel_idx"],
                                                                a["sel_cnt"], a["out"], lse=a["lse"]),
     "build_page_meta": lambda a: E.build_page_meta(shape(), a["k_pool"], a["page_table"], a["seq_lens"], a["meta"]),
+    "build_page_meta_f8": lambda a: E.build_page_meta_f8(shape(), a["k_pool"], a["page_table"], a["seq_lens"],
+                                                         a["meta8"]),
+    "score_pages_f8": lambda a: E.score_pages_f8(shape(), a["q"], a["meta8"], a["page_table"], a["seq_lens"],
+                                                 a["box"], a["mu"], a["var"]),
+    "append_token": lambda a: E.append_token(shape(), a["k_new"], a["v_new"], a["k_pool"], a["v_pool"],
+                                             a["page_table"], a["seq_lens"], a["meta"]),
+    "append_token_f8": lambda a: E.append_token(shape(), a["k_new"], a["v_new"], a["k_pool"], a["v_pool"],
+                                                a["page_table"], a["seq_lens"], a["meta8"], compact=True),
 }
 
 # the buffers each call reads or writes
@@ -70,6 +79,10 @@ USES = {
     "softmax_decode_full": ("q", "k_pool", "v_pool", "page_table", "seq_lens", "out", "lse"),
     "softmax_decode_sparse": ("q", "k_pool", "v_pool", "page_table", "seq_lens", "sel_idx", "sel_cnt", "out", "lse"),
     "build_page_meta": ("k_pool", "page_table", "seq_lens", "meta"),
+    "build_page_meta_f8": ("k_pool", "page_table", "seq_lens", "meta8"),
+    "score_pages_f8": ("q", "meta8", "page_table", "seq_lens", "box", "mu", "var"),
+    "append_token": ("k_new", "v_new", "k_pool", "v_pool", "page_table", "seq_lens", "meta"),
+    "append_token_f8": ("k_new", "v_new", "k_pool", "v_pool", "page_table", "seq_lens", "meta8"),
 }
 
 
@@ -93,6 +106,8 @@ def test_group_selection_sizes():
     gsel, gcnt = t(B * HKV * MP, torch.int32).as_subclass(Dev), t(B * HKV, torch.int32).as_subclass(Dev)
     with pytest.raises(ValueError, match="elements"):
         E.select_pages_topk_group(shape(), a["box"], a["seq_lens"], 4, gsel[:-1], gcnt)
+    with pytest.raises(ValueError, match="elements"):
+        E.select_pages_gauss_group(shape(), a["box"], a["mu"], a["var"], a["seq_lens"], 1.5, 0.5, gsel, gcnt[:-1])
     with pytest.raises(ValueError, match="elements"):
         E.entmax_decode_sparse_group(shape(), a["q"], a["k_pool"], a["v_pool"], a["page_table"], a["seq_lens"],
                                      gsel, gcnt[:-1], 1.5, a["out"])
