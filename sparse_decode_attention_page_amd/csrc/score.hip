@@ -24,7 +24,8 @@
 //    the 16-byte chunks of each record XOR-swizzled by the record index, so that
 //    the lane-per-record reads of the compute hit distinct banks;
 //  * the query-derived coefficients (q-, q+, q, q^2 in fp64, one table per
-//    (b, g) row and kind) are written once to a workspace table at the start and
+//    (b, g) row, laid out so that each wave reads one contiguous region in
+//    coordinate order) are written once to a workspace table at the start and
 //    read back through scalar loads, so the inner loop is fp64 FMAs on exact
 //    products with a wave-uniform operand.  The table's
 //    lines are pulled into the scalar cache with one batch of loads that overlaps
@@ -89,8 +90,12 @@ struct ScoreCfg {
   static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
   static constexpr int kLds = kTileBytes + kScoreTiles * (kTilePages + 1) * 4;
   static constexpr int kBlocksPerCu = (160 * 1024) / (kLds + 1024) >= 4 ? 4 : (160 * 1024) / (kLds + 1024);
-  static constexpr int kCoefRow = 4 * DIM * G;         // doubles per (b, g) row: [kind][i][h]
-  static constexpr int kWarmLines = DIM * G * 8 / 64;  // 64-byte lines of one kind's coefficients
+  // coefficient table, doubles per (b, g) row: [box wave][i][j][q-, q+] (head
+  // h = wave * kGH + j), then [i][h] of q (mean) and of q^2 (variance), so each
+  // wave reads one contiguous region in coordinate order
+  static constexpr int kGH = G > 1 ? G / 2 : 1;          // box heads per box wave
+  static constexpr int kCoefRow = 4 * DIM * G;
+  static constexpr int kWarmLines = DIM * G * 8 / 64;    // 64-byte lines of one wave's region (G > 1)
 };
 
 // Tile loads: thread t fetches 16-byte chunks u*256 + t of the tile (a wave
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
     float *__restrict__ var) {
   using C = ScoreCfg<T, DIM, G, F8>;
   constexpr int kE = C::kE;
-  constexpr int kGH = G > 1 ? G / 2 : 1;  // box heads of each of waves 0 and 1 (G = 1: wave 0 only)
+  constexpr int kGH = C::kGH;  // box heads of each of waves 0 and 1 (G = 1: wave 0 only)
   __shared__ __align__(16) unsigned char tile[C::kTileBytes];
   __shared__ int s_phys[kScoreTiles][kTilePages];
   __shared__ int s_np[kScoreTiles];
@@ -169,10 +174,14 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
         double *cw = coef_w + (size_t)(row0 + rr) * C::kCoefRow;
 #pragma unroll
         for (int tt = tid; tt < DIM * G; tt += kScoreThreads) {
-          // [kind][i][h]: kind 0 q- (kmin), 1 q+ (kmax), 2 q (mean), 3 q^2 (var)
-          const double qq = (double)load_f<T>(qrow, (tt % G) * DIM + tt / G);
-          cw[0 * DIM * G + tt] = qq < 0.0 ? qq : 0.0;
-          cw[1 * DIM * G + tt] = qq >= 0.0 ? qq : 0.0;
+          // entry tt = i G + h; box pair (q- for kmin, q+ for kmax) of head h
+          // at box wave h / kGH, slot j = h % kGH
+          const int i = tt / G, h = tt % G;
+          const double qq = (double)load_f<T>(qrow, h * DIM + i);
+          const int bw = G > 1 ? h / C::kGH : 0, j = G > 1 ? h % C::kGH : 0;
+          double *pb = cw + (((size_t)bw * DIM + i) * C::kGH + j) * 2;
+          pb[0] = qq < 0.0 ? qq : 0.0;
+          pb[1] = qq >= 0.0 ? qq : 0.0;
           cw[2 * DIM * G + tt] = qq;
           cw[3 * DIM * G + tt] = qq * qq;
         }
@@ -199,9 +208,10 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   // wrote to LDS before it, so no load of the table can be scheduled earlier.
   // (coef_r stays restrict-qualified, which lets the reads be scalar loads.)
   const int zoff = __builtin_amdgcn_readfirstlane(s_zero);
-  // this wave's coefficient kinds: q- and q+ (box waves), q (mean), q^2 (variance)
-  const int kind0 = wave < 2 ? 0 : wave;
-  const double *cf0 = coef_r + zoff + (size_t)row0 * C::kCoefRow + (size_t)kind0 * DIM * G;
+  // this wave's region of the coefficient table: its box heads' (q-, q+)
+  // pairs, q (mean) or q^2 (variance)
+  const size_t region = wave < 2 ? (size_t)wave * DIM * C::kGH * 2 : (size_t)wave * DIM * G;
+  const double *cf0 = coef_r + zoff + (size_t)row0 * C::kCoefRow + region;
   // scalar-cache warm-up: one load per 64-byte line of this wave's coefficients,
   // all in flight together; consumed before the first tile is scored
   unsigned warm = 0;
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
     const unsigned *cl = reinterpret_cast<const unsigned *>(cf0);
 #pragma unroll
     for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[i * 16];
-    if (wave < 2) {
+    if (G == 1 && wave == 0) {  // the lone box wave's region holds two doubles per coordinate
 #pragma unroll
       for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[(C::kWarmLines + i) * 16];
     }
@@ -251,14 +261,12 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
 
       // ---- lane = page.  Box waves: acc[j] = sum_i (q-_i kmin_i + q+_i kmax_i)
       // for head h0 + j, coordinate by coordinate; mean / variance waves:
-      // acc[h] = sum_i coef[kind][i][h] * row_i.
+      // acc[h] = sum_i coef[i][h] * row_i (q for the mean row, q^2 for the variance row).
       const int row = (t_begin + lt) / tiles_per_row;
       const double *cf = cf0 + (size_t)(row - row0) * C::kCoefRow;
       const bool ok = s_phys[lt][lane] >= 0;
       if (wave < 2) {
         if (G > 1 || wave == 0) {  // wave-uniform
-          const int h0 = G > 1 ? wave * kGH : 0;
-          const double *cn = cf + h0, *cp = cf + DIM * G + h0;
           double acc[kGH];
 #pragma unroll
           for (int j = 0; j < kGH; ++j) acc[j] = 0.0;
@@ -269,12 +277,12 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
             Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((C::kRowChunks + ch) ^ sw) * 16), xp);
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-              const size_t i = (size_t)(ch * kE + e) * G;
+              const double *ci = cf + (size_t)(ch * kE + e) * kGH * 2;
 #pragma unroll
               for (int j = 0; j < kGH; ++j) {
                 // exact products (bf16 x bf16 in 16 bits, f32 x f32 in 48): fused == separate
-                acc[j] = __builtin_fma(cn[i + j], xn[e], acc[j]);
-                acc[j] = __builtin_fma(cp[i + j], xp[e], acc[j]);
+                acc[j] = __builtin_fma(ci[2 * j], xn[e], acc[j]);
+                acc[j] = __builtin_fma(ci[2 * j + 1], xp[e], acc[j]);
               }
             }
           }
