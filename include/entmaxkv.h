@@ -201,7 +201,11 @@ int32_t select_pages_topk(const entmaxkv_shape *shape, const float *box, const i
  * ties).  Pages with non-finite box/mu/var are never kept.  tau_hat (nullable,
  * float64 [B][Hq]) receives tau_hat/(alpha-1) (score units); NaN if N_b = 0.
  * Requires alpha > 1, delta >= 0, n_sigma >= 0.  alpha in {1.5, 2} runs the
- * fast histogram solver; other alpha use a slower per-row bisection.
+ * chunked solver (integer counts to locate the root, then an exact solve on a
+ * window of them); other alpha use a slower per-row bisection.  The result is
+ * deterministic: the same inputs give the same tau_hat bits and sets on every
+ * call (every sum is an integer add or taken in a fixed order).
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_GAUSS).
  */
 int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const float *mu,
                            const float *var, const int32_t *seq_lens, double alpha, double delta,

@@ -147,6 +147,17 @@ def test_full_selection_sampled_rows(full, policy):
     assert sets_equal(sel.cpu().numpy(), cnt.cpu().numpy(), so, co, rows=set(rows)) == []
 
 
+def test_full_gauss_selection_is_deterministic(full):
+    """Two calls of the Gaussian selector on the same scores give the same
+    tau_hat bits and the same sets (integer counts, fixed-order sums)."""
+    t = torch()
+    s1, c1, t1 = _select(full, "gauss")
+    s2, c2, t2 = _select(full, "gauss")
+    assert t.equal(c1, c2)
+    assert t.equal(s1, s2)
+    assert t.equal(t1.view(t.int64), t2.view(t.int64)), "tau_hat bits differ between two runs"
+
+
 @pytest.mark.parametrize("kind", ["sparse_gauss", "sparse_topk", "full"])
 def test_full_entmax_sampled_rows(full, kind):
     t = torch()
