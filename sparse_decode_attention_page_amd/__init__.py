@@ -47,13 +47,19 @@ class Shape(ctypes.Structure):
 
 
 def load(path: str | None = None):
-    """Load libentmaxkv.so (raises if it has not been built)."""
+    """Load libentmaxkv.so (raises if it has not been built).
+
+    torch is imported first: its HIP runtime is then the one in the process and
+    the library binds to it (both carry the soname libamdhip64.so.7).  Loaded
+    the other way round, torch would bring a second HIP runtime and the
+    library's launches would fail."""
     global _lib
     if _lib is not None:
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} not found: build it with `python -m sparse_decode_attention_page_amd.build`")
+    import torch  # noqa: F401  (one HIP runtime per process: torch's)
     lib = ctypes.CDLL(p)
     vp, i32, sz, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_double
     sh = ctypes.POINTER(Shape)
