@@ -64,7 +64,8 @@ enum entmaxkv_status {
   ENTMAXKV_ERR_INVALID_ARGUMENT = 1, /* null required pointer, bad dims, Hq % Hkv, k <= 0, alpha <= 1, ... */
   ENTMAXKV_ERR_UNSUPPORTED = 2,      /* (d, P, dtype, group size) without a kernel */
   ENTMAXKV_ERR_WORKSPACE = 3,        /* ws_bytes below entmaxkv_workspace_bytes(...) */
-  ENTMAXKV_ERR_HIP = 4               /* a launch failed; see entmaxkv_status_string */
+  ENTMAXKV_ERR_HIP = 4,              /* a launch failed; see entmaxkv_status_string */
+  ENTMAXKV_ERR_TOO_LARGE = 5         /* shape beyond score_pages_noalloc's static scratch */
 };
 
 enum entmaxkv_dtype { ENTMAXKV_F32 = 0, ENTMAXKV_BF16 = 1 };
@@ -138,6 +139,24 @@ int32_t build_page_meta(const entmaxkv_shape *shape, const void *k_pool, const i
 int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta,
                     const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                     float *var, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * score_pages_noalloc -- score_pages for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): same arguments, outputs and rules as score_pages, but no
+ * workspace argument.  Its scratch (the query coefficient table, 32 B * batch *
+ * n_q_heads * head_dim) is a static device array of
+ * entmaxkv_score_scratch_bytes() = 4 MiB inside the library, one per GPU, kept
+ * until the process ends; a shape needing more returns ENTMAXKV_ERR_TOO_LARGE
+ * before anything is launched (batch * n_q_heads * head_dim <= 131072 fits).
+ * The call allocates nothing.  Every call on one GPU uses that GPU's array, so
+ * calls that overlap on one GPU (different streams, or other host threads)
+ * race; serialize them.  Nothing in the scratch has to start at zero.
+ */
+int32_t score_pages_noalloc(const entmaxkv_shape *shape, const void *q, const void *meta,
+                            const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                            float *var, hipStream_t stream);
+size_t entmaxkv_score_scratch_bytes(void);
 
 /*
  * append_token -- the streaming side of [EntmaxKV s.2.A]: the page metadata

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libentmaxkv.so")
 _lib = None
 
-OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = range(6)
 F32, BF16 = 0, 1
 (CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE,
  CALL_TOPK_GROUP, CALL_GAUSS_GROUP, CALL_DECODE_GROUP) = range(1, 11)
@@ -29,7 +29,7 @@ EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_
            "entmax_decode_sparse_group",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
-           "entmaxkv_stream_read")
+           "entmaxkv_stream_read", "score_pages_noalloc", "entmaxkv_score_scratch_bytes")
 
 
 class EntmaxKVError(RuntimeError):
@@ -75,6 +75,10 @@ def load(path: str | None = None):
     lib.build_page_meta.argtypes = [sh, vp, vp, vp, vp, vp, vp]
     lib.score_pages.restype = i32
     lib.score_pages.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.score_pages_noalloc.restype = i32
+    lib.score_pages_noalloc.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.entmaxkv_score_scratch_bytes.restype = sz
+    lib.entmaxkv_score_scratch_bytes.argtypes = []
     lib.append_token.restype = i32
     lib.append_token.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     lib.build_page_meta_f8.restype = i32
@@ -297,6 +301,20 @@ def score_pages(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, ws=No
     mt = _ptr(meta, _kv_dtype(shape), "meta", _N(shape).meta)
     _call("score_pages", shape, CALL_SCORE, ws, (qp, mt, pt, sl, bp, mp, vp), stream)
     return box, mu, var
+
+
+def score_pages_noalloc(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, stream=None):
+    """score_pages without a workspace: the library's static device scratch holds
+    the coefficient table (calls that overlap on one GPU race)."""
+    qp, pt, sl, bp, mp, vp = _score_args(shape, q, page_table, seq_lens, box, mu, var)
+    mt = _ptr(meta, _kv_dtype(shape), "meta", _N(shape).meta)
+    _check("score_pages_noalloc", load().score_pages_noalloc(ctypes.byref(shape), qp, mt, pt, sl, bp, mp, vp,
+                                                             _stream(stream)))
+    return box, mu, var
+
+
+def score_scratch_bytes() -> int:
+    return int(load().entmaxkv_score_scratch_bytes())
 
 
 def _sel_args(shape: Shape, sel_idx, sel_cnt, group=False):

@@ -181,6 +181,7 @@ const char *entmaxkv_status_string(int32_t status) {
     case ENTMAXKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case ENTMAXKV_ERR_WORKSPACE: return "workspace missing or too small";
     case ENTMAXKV_ERR_HIP: return g_err[0] ? g_err : "HIP error";
+    case ENTMAXKV_ERR_TOO_LARGE: return "shape needs more than the library's static scratch holds";
   }
   return "unknown status";
 }
@@ -241,6 +242,20 @@ int32_t score_pages(const entmaxkv_shape *shape, const void *q, const void *meta
   if ((st = check_ws(score_ws_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_score(D, shape->dtype, false, q, meta, page_table, seq_lens, box, mu, var, ws, stream));
 }
+
+int32_t score_pages_noalloc(const entmaxkv_shape *shape, const void *q, const void *meta,
+                            const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                            float *var, hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (score_ws_bytes(D) > score_scratch_bytes()) return ENTMAXKV_ERR_TOO_LARGE;
+  return hip_status(launch_score_noalloc(D, shape->dtype, q, meta, page_table, seq_lens, box, mu, var, stream));
+}
+
+size_t entmaxkv_score_scratch_bytes(void) { return score_scratch_bytes(); }
 
 int32_t score_pages_f8(const entmaxkv_shape *shape, const void *q, const void *meta,
                        const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,

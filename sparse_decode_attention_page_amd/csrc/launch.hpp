@@ -47,6 +47,12 @@ hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const 
                         const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                         float *var, void *ws, hipStream_t s);
 
+// score_pages with the coefficient table in the library's static device scratch
+size_t score_scratch_bytes();
+hipError_t launch_score_noalloc(const Dims &D, int dtype, const void *q, const void *meta,
+                                const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                float *var, hipStream_t s);
+
 size_t topk_ws_bytes(const Dims &D);
 hipError_t launch_topk(const Dims &D, const float *box, const int32_t *seq_lens, int k,
                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt, void *ws,

@@ -37,6 +37,8 @@
 //  * outputs stay in registers until both tiles are scored, so that the vector
 //    memory queue holds only loads while tiles are in flight (a store among them
 //    would make every later wait drain the whole queue).
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -425,6 +427,49 @@ hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const 
   }
   if (D.d == 64) return launch_score_d<float, 64, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
   return launch_score_d<float, 128, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+}
+
+// ---------------------------------------------------- allocation-free variant
+// score_pages_noalloc takes the coefficient table from this file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  The kernel writes every table row it reads
+// before reading it, so nothing in it has to start at zero; two calls that
+// overlap on one GPU share the array and race.
+constexpr size_t kScoreScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScoreScratchBytes];
+
+size_t score_scratch_bytes() { return kScoreScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the host-side name of the array is not a device address).
+static hipError_t scratch_address(void **out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_score_noalloc(const Dims &D, int dtype, const void *q, const void *meta,
+                                const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                float *var, hipStream_t s) {
+  if (score_ws_bytes(D) > kScoreScratchBytes) return hipErrorInvalidValue;  // checked by the caller first
+  void *ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_score(D, dtype, false, q, meta, page_table, seq_lens, box, mu, var, ws, s);
 }
 
 EKV_TRACE_DUMP(ekv_trace_dump_score)

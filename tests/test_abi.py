@@ -88,6 +88,19 @@ def test_bad_arguments():
                                     FAKE, big, None) == E.ERR_INVALID_ARGUMENT
 
 
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """score_pages_noalloc checks its static scratch before launching anything."""
+    lib = E.load()
+    cap = E.score_scratch_bytes()
+    assert cap == 4 << 20
+    big = shape(batch=64, head_dim=128)  # 32 B * 64 * 32 * 128 = 8 MiB of coefficients
+    assert lib.score_pages_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        E.ERR_TOO_LARGE
+    assert "scratch" in E.status_string(E.ERR_TOO_LARGE)
+    s = ctypes.byref(shape())
+    assert lib.score_pages_noalloc(s, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E.ERR_INVALID_ARGUMENT
+
+
 def test_workspace_too_small_or_misaligned():
     lib = E.load()
     sh = shape()
