@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming multi-step decode timing")
+    ap.add_argument("--no-passage", action="store_true",
+                    help="skip the quality-matched leg (the step on the passage variant of the workload)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the compact-metadata and group-shared-selection variants of the step")
     ap.add_argument("--selector-sweep", action="store_true",
@@ -129,7 +131,7 @@ def main():
     ws_s = E.workspace(shape, E.CALL_SCORE)
     ws_g = E.workspace(shape, E.CALL_GAUSS)
     ws_t = E.workspace(shape, E.CALL_TOPK)
-    ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE)
+    ws_d = None  # sized by the kept pages below
     sl, pt = inp.seq_lens, inp.page_table
 
     def score(r):
@@ -164,6 +166,17 @@ def main():
             ts.append((a, b))
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3  # us
+
+    # ---- the decode workspace holds the kept pages of a first selection with
+    # a margin (twice, at least every row's mean plus 64 pages per row)
+    score(0)
+    select()
+    torch.cuda.synchronize()
+    kept0 = int(cnt.sum())
+    ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE, max_kept_pages=2 * kept0 + 64 * B * Hq)
+    ws_dense = E.workspace_bytes(shape, E.CALL_DECODE_SPARSE)
+    log(f"[bench] decode workspace {ws_d.numel() / 2**20:.1f} MiB for {kept0} kept pages "
+        f"(every page: {ws_dense / 2**20:.1f} MiB)")
 
     # ---- warm up every call once (also builds lazily computed constants)
     for r in range(R):
@@ -490,7 +503,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": "bf16-kv/f64-score/f32-acc",
+        "dtype_detail": ("K/V and q bf16; scores, thresholds and weights p_t fp64 (exact bf16 products); "
+                         "the weighted V sum accumulated in fp32"),
         "data": "synthetic",
         "config": {
             "workload": (f"{wl.name}: B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, {wl.dtype} K/V, "
@@ -623,11 +638,138 @@ def main():
             f"softmax over kept pages {ss_us:.1f} us")
         del wfull
 
+    result["decode_workspace"] = {"bytes": int(ws_d.numel()), "kept_pages_bound": 2 * kept0 + 64 * B * Hq,
+                                  "every_page_bytes": int(ws_dense)}
+
+    # ---- quality-matched leg: the same step where the kept pages hold the support
+    if not args.no_passage and (wl.name + "_passage") in synth.WORKLOADS:
+        del reps
+        torch.cuda.empty_cache()
+        try:
+            result["quality_matched"] = passage_leg(args, wl.name + "_passage")
+        except Exception as e:
+            log(f"[bench] passage leg failed ({e})")
+
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, shape, wl, alpha, args.policy)
 
     print(json.dumps(result), flush=True)
+
+
+def passage_leg(args, name):
+    """The step on the passage variant of the workload (runs of 16 planted keys
+    along the query, so the selection keeps the pages holding the entmax
+    support): step time over HIP-graph replays of two replicas, the full-cache
+    softmax and entmax times, and the discarded entmax mass and relative output
+    error of the sparse decode against the full-cache entmax."""
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_page_amd as E
+    from sparse_decode_attention_page_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    alpha = wl.alphas[0]
+    inp = synth.make_device(wl, args.seed)
+    shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+    B, Hq, Hkv, d, P, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages
+    meta = torch.zeros((inp.num_phys, Hkv, 4, d), dtype=inp.k_pool.dtype, device="cuda")
+    E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta)
+    reps = [(inp.q, inp.k_pool, inp.v_pool, meta),
+            (inp.q.clone(), inp.k_pool.clone(), inp.v_pool.clone(), meta.clone())]
+    box = torch.empty((B, Hq, MP), device="cuda")
+    mu, var = torch.empty_like(box), torch.empty_like(box)
+    sel = torch.empty((B, Hq, MP), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, d), device="cuda")
+    sl, pt = inp.seq_lens, inp.page_table
+    ws_s, ws_g = E.workspace(shape, E.CALL_SCORE), E.workspace(shape, E.CALL_GAUSS)
+
+    def select(r):
+        q, k, v, m = reps[r]
+        E.score_pages(shape, q, m, pt, sl, box, mu, var, ws=ws_s)
+        E.select_pages_gauss(shape, box, mu, var, sl, alpha, wl.delta, sel, cnt, ws=ws_g)
+
+    select(0)
+    torch.cuda.synchronize()
+    kept = int(cnt.sum())
+    ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE, max_kept_pages=2 * kept + 64 * B * Hq)
+
+    def step(r):
+        q, k, v, m = reps[r]
+        select(r)
+        E.entmax_decode_sparse(shape, q, k, v, pt, sl, sel, cnt, alpha, out, ws=ws_d)
+
+    for r in range(2):
+        step(r)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(s):
+        for r in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step(r)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(max(args.warmup, 2)):
+        graphs[i % 2].replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        graphs[i % 2].replay()
+    b.record()
+    torch.cuda.synchronize()
+    step_us = a.elapsed_time(b) * 1e3 / args.steps
+    # comparators on the same inputs (eager, events around each call)
+    ws_sm, ws_f = E.workspace(shape, E.CALL_SOFTMAX), E.workspace(shape, E.CALL_DECODE_FULL)
+    out2 = torch.empty_like(out)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([x.elapsed_time(y) for x, y in ts])) * 1e3
+
+    q0, k0, v0, m0 = reps[0]
+    sm_us = timed(lambda: E.softmax_decode_full(shape, q0, k0, v0, pt, sl, out2, ws=ws_sm), 6)
+    ef_us = timed(lambda: E.entmax_decode_full(shape, q0, k0, v0, pt, sl, alpha, out2, ws=ws_f), 3)
+    # quality of replica 0's step against the full-cache entmax
+    step(0)
+    wfull = torch.empty((B, Hq, MP * P), device="cuda")
+    out_f = torch.empty_like(out)
+    E.entmax_decode_full(shape, q0, k0, v0, pt, sl, alpha, out_f, weights_out=wfull, ws=ws_f)
+    torch.cuda.synchronize()
+    keep = torch.zeros((B, Hq, MP + 1), dtype=torch.bool, device="cuda")
+    ar = torch.arange(MP, device="cuda")
+    valid = ar[None, None, :] < cnt[:, :, None]
+    keep.scatter_(2, torch.where(valid, sel, torch.full_like(sel, MP)).long(), valid)
+    kept_mass = (wfull.view(B, Hq, MP, P).double().sum(-1) * keep[:, :, :MP]).sum(-1)
+    delta = (1.0 - kept_mass).clamp(min=0.0)
+    rel = (torch.linalg.vector_norm((out - out_f).double(), dim=-1)
+           / torch.linalg.vector_norm(out_f.double(), dim=-1).clamp(min=1e-30))
+    res = {"workload": (f"{name}: B={B}, Hq={Hq}, Hkv={Hkv}, d={d}, {wl.dtype} K/V, {int(sl.max())} tokens in "
+                        f"pages of {P}; alpha={alpha}, Gaussian selection Delta={wl.delta}"),
+           "step_us": round(step_us, 2), "softmax_decode_full_us": round(sm_us, 2),
+           "entmax_decode_full_us": round(ef_us, 2),
+           "speedup_vs_full_softmax": round(sm_us / step_us, 2), "speedup_vs_full_entmax": round(ef_us / step_us, 2),
+           "kept_pages_per_head_mean": round(float(cnt.double().mean()), 2),
+           "delta_entmax_mean": float(delta.mean()), "delta_entmax_max": float(delta.max()),
+           "rel_err_entmax_mean": float(rel.mean()), "rel_err_entmax_max": float(rel.max()),
+           "launch": "hip graph replay (2 replicas)"}
+    log(f"[bench] quality-matched leg ({name}): step {step_us:.2f} us, full softmax {sm_us:.1f} us, full entmax "
+        f"{ef_us:.1f} us; delta entmax {res['delta_entmax_mean']:.3e}, rel err {res['rel_err_entmax_mean']:.3e}")
+    return res
 
 
 def selector_sweep(args):

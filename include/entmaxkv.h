@@ -104,6 +104,21 @@ enum entmaxkv_call {
  * scratch: its contents after a call are unspecified. */
 size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape /*(host)*/, int32_t which_call);
 
+/* Decode workspaces sized by a bound on the kept pages instead of the full
+ * cache.  which_call: ENTMAXKV_CALL_DECODE_SPARSE, _GROUP or _FULL (0 for any
+ * other call or a negative bound).  max_kept_pages bounds the kept pages
+ * summed over all query-head rows (b, h): sum of sel_cnt for the per-head
+ * call, G times the sum of the group counts for the group call, sum of N_b
+ * times Hq for the full call.  entmaxkv_workspace_bytes gives the size for
+ * every row's full set; any size from entmaxkv_decode_workspace_bytes(shape,
+ * call, 1) up is accepted, and the workspace then holds the kept pages the
+ * bytes allow: rows are laid out in row order, and a row whose pages end past
+ * that capacity gets NaN out and tau (its weights_out row stays zero).  The
+ * capacity for a workspace of B bytes is therefore the largest n with
+ * entmaxkv_decode_workspace_bytes(shape, call, n) <= B. */
+size_t entmaxkv_decode_workspace_bytes(const entmaxkv_shape *shape /*(host)*/, int32_t which_call,
+                                       int64_t max_kept_pages);
+
 /* Text for a status code; for ENTMAXKV_ERR_HIP it includes the HIP error of
  * the most recent failure on the calling thread. */
 const char *entmaxkv_status_string(int32_t status);
@@ -242,12 +257,17 @@ int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const 
  * alpha with tau_method 1 is ENTMAXKV_ERR_INVALID_ARGUMENT).  The sort runs
  * over the row's candidate tokens, those above a certified lower bound on tau
  * (every other token is outside the support), when at most 1024 of them
- * remain; a row with more candidates is solved by the root finder, which
- * reaches the same tau to fp64 resolution.  tau (nullable, float64
- * [B][Hq]) receives tau/(alpha-1).  weights_out (nullable, float32
- * [B][Hq][max_pages*P], for tests) receives p at logical token positions and
- * zero elsewhere.  A row with sel_cnt = 0 gets out = 0, tau = NaN; a row whose
- * selection is out of range or not strictly ascending gets NaN out and tau.
+ * remain and the row keeps at most 4096 tokens above its slices' first cut;
+ * any other row is solved by the root finder, which reaches the same tau to
+ * fp64 resolution.  tau (nullable, float64 [B][Hq]) receives tau/(alpha-1).
+ * weights_out (nullable, float32 [B][Hq][max_pages*P], for tests) receives p
+ * at logical token positions and zero elsewhere.  A row with sel_cnt = 0 gets
+ * out = 0, tau = NaN; a row whose selection is out of range or not strictly
+ * ascending gets NaN out and tau.  The heads of a KV group are scored
+ * together: each page kept by any of them is read once per KV head.  Results
+ * are identical from run to run (every sum has a fixed order).
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_DECODE_SPARSE), or a
+ * kept-page-bounded size from entmaxkv_decode_workspace_bytes.
  */
 int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
                              const void *v_pool, const int32_t *page_table,
@@ -275,7 +295,8 @@ int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const v
  *   head g attending over the group's set sel_idx[b][g]; outputs, tau,
  *   weights_out, malformed-selection rules and tau_method as there (a
  *   malformed group set makes all G rows NaN).  Each kept K page is read once
- *   per group.  ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_DECODE_GROUP).
+ *   per group.  ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_DECODE_GROUP)
+ *   or a kept-page-bounded size (entmaxkv_decode_workspace_bytes).
  * seq_mask (nullable, uint8 [B]): as in the per-head calls.
  */
 int32_t select_pages_topk_group(const entmaxkv_shape *shape, const float *box, const int32_t *seq_lens,

@@ -29,7 +29,8 @@ EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_
            "entmax_decode_sparse_group",
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
-           "entmaxkv_stream_read", "score_pages_noalloc", "entmaxkv_score_scratch_bytes")
+           "entmaxkv_stream_read", "score_pages_noalloc", "entmaxkv_score_scratch_bytes",
+           "entmaxkv_decode_workspace_bytes")
 
 
 class EntmaxKVError(RuntimeError):
@@ -65,6 +66,8 @@ def load(path: str | None = None):
     sh = ctypes.POINTER(Shape)
     lib.entmaxkv_workspace_bytes.restype = sz
     lib.entmaxkv_workspace_bytes.argtypes = [sh, i32]
+    lib.entmaxkv_decode_workspace_bytes.restype = sz
+    lib.entmaxkv_decode_workspace_bytes.argtypes = [sh, i32, ctypes.c_int64]
     lib.entmaxkv_status_string.restype = ctypes.c_char_p
     lib.entmaxkv_status_string.argtypes = [i32]
     lib.entmaxkv_gauss_hermite16.restype = None
@@ -175,9 +178,20 @@ def workspace_bytes(shape: Shape, which_call: int) -> int:
     return int(load().entmaxkv_workspace_bytes(ctypes.byref(shape), int(which_call)))
 
 
-def workspace(shape: Shape, which_call: int, device="cuda"):
-    """A uint8 device tensor big enough for `which_call` (or None if none is needed)."""
-    n = workspace_bytes(shape, which_call)
+def decode_workspace_bytes(shape: Shape, which_call: int, max_kept_pages: int) -> int:
+    """Bytes of a decode workspace holding `max_kept_pages` kept pages summed
+    over the query-head rows (which_call: CALL_DECODE_SPARSE, _GROUP, _FULL)."""
+    return int(load().entmaxkv_decode_workspace_bytes(ctypes.byref(shape), int(which_call), int(max_kept_pages)))
+
+
+def workspace(shape: Shape, which_call: int, device="cuda", max_kept_pages=None):
+    """A uint8 device tensor big enough for `which_call` (or None if none is
+    needed); for the decode calls, max_kept_pages bounds the kept pages summed
+    over the query-head rows (None: every row's full set)."""
+    if max_kept_pages is not None:
+        n = decode_workspace_bytes(shape, which_call, max_kept_pages)
+    else:
+        n = workspace_bytes(shape, which_call)
     if n == 0:
         return None
     return _torch().empty(n, dtype=_torch().uint8, device=device)

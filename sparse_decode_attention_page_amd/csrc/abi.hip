@@ -174,6 +174,16 @@ size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call)
   return 0;
 }
 
+size_t entmaxkv_decode_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call, int64_t max_kept_pages) {
+  Dims D;
+  if (check_shape(shape, &D) != ENTMAXKV_OK) return 0;
+  if (which_call != ENTMAXKV_CALL_DECODE_SPARSE && which_call != ENTMAXKV_CALL_DECODE_GROUP &&
+      which_call != ENTMAXKV_CALL_DECODE_FULL)
+    return 0;
+  if (max_kept_pages < 0) return 0;
+  return decode_ws_bytes_items(D, (long long)max_kept_pages);
+}
+
 const char *entmaxkv_status_string(int32_t status) {
   switch (status) {
     case ENTMAXKV_OK: return "ok";
@@ -312,12 +322,12 @@ static int32_t decode_common(const entmaxkv_shape *shape, const void *q, const v
   if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
-  if ((st = check_ws(full ? full_ws_bytes(D) : decode_ws_bytes(D, false), ws, ws_bytes))) return st;
+  if ((st = check_ws(decode_ws_min_bytes(D), ws, ws_bytes))) return st;
   if (full)
     return hip_status(launch_entmax_full(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, alpha,
-                                         tau_method, out, tau, weights_out, ws, stream));
+                                         tau_method, out, tau, weights_out, ws, ws_bytes, stream));
   return hip_status(launch_entmax_decode(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
-                                         sel_cnt, alpha, tau_method, out, tau, weights_out, ws, stream));
+                                         sel_cnt, alpha, tau_method, out, tau, weights_out, ws, ws_bytes, stream));
 }
 
 int32_t entmax_decode_sparse(const entmaxkv_shape *shape, const void *q, const void *k_pool,
@@ -372,9 +382,10 @@ int32_t entmax_decode_sparse_group(const entmaxkv_shape *shape, const void *q, c
   if (!(alpha > 1.0) || !std::isfinite(alpha)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method != 0 && tau_method != 1) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if (tau_method == 1 && alpha != 2.0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
-  if ((st = check_ws(decode_group_ws_bytes(D), ws, ws_bytes))) return st;
+  if ((st = check_ws(decode_ws_min_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_entmax_decode_group(D, shape->dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx,
-                                               sel_cnt, alpha, tau_method, out, tau, weights_out, ws, stream));
+                                               sel_cnt, alpha, tau_method, out, tau, weights_out, ws, ws_bytes,
+                                               stream));
 }
 
 int32_t entmax_decode_full(const entmaxkv_shape *shape, const void *q, const void *k_pool,

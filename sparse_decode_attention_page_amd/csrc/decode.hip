@@ -7,32 +7,37 @@
 // selection contains the whole support the result is exact.
 //
 // alpha-entmax (Peters, Niculae & Martins 2019): with X_t = (alpha-1) s_t,
-// p_t = [X_t - tau]_+^(1/(alpha-1)), tau the root of sum_t p_t = 1.
+// p_t = [X_t - tau]_+^(1/(alpha-1)), tau the root of F(tau) = sum_t p_t = 1.
 //
 // Two launches.
-//  1. Scores.  Work is a flat list of items (row, i): the i-th selected page of
-//     query row (b, h); every block maps items through a prefix sum of the
-//     selection counts it computes itself.  An item writes the exact fp64
-//     scores X of the page's tokens (bf16 products are exact; fp64 sums), the
-//     page's maximum (NaN for a malformed item) and its physical page.
-//  2. Threshold and output.  Since F(max X - 1) >= 1, tau is at least
-//     max X - 1 and only tokens with X > max X - 1 can carry weight.  Each row
-//     is cut into up to kSplitMax chunks of kChunkTok tokens; the block of a
-//     chunk reads the row's page maxima, compacts its chunk's candidates in
-//     place, and the row's last block (atomic handshake; kernel 1 zeroed the
-//     counters) gathers them into LDS.  tau comes from safeguarded Newton from
-//     the left on the candidates (one wave and shuffles when they are few) or
-//     from the sparsemax sort form; the V rows of the support are then
-//     gathered with 16-byte loads.  Kept tokens outside the support cost no V
-//     traffic.  Rows with more candidates than LDS holds are solved by passes
-//     over the compacted candidates in the workspace.
+//  1. scores_kernel.  A block takes one KV head (b, g) and one slice of the
+//     sequence's pages.  It finds each query head's kept pages inside the slice
+//     (a 64-way search of the ascending set), merges them into the group's
+//     union, reads each union page's K slice once and scores it for every head
+//     of the group that kept it (bf16 products are exact in fp64; fp64 sums).
+//     Per (row, slice) it stores the entries the threshold step reads: when the
+//     slice's scores fit in registers, only the candidates X > (slice max) - 1
+//     with their token ids (compact); otherwise every kept token's X in place
+//     (dense, token id implicit).  F(max X - 1) >= 1, so tau >= max X - 1 and
+//     no other token of the row can carry weight.
+//  2. rows_kernel.  A leader block per row reads the slices' summaries.  A row
+//     with at most 4096 entries is finished by its leader: a certified lower
+//     bound on tau from counts above max - 2^-i, the candidates above it into
+//     LDS, tau by Newton from the left with an exact last piece (or the
+//     sparsemax sort form), then the V rows of the support.  A larger row goes
+//     to helper blocks in three steps, each started by the previous one: an
+//     integer histogram of the entries, from which bounds of F at the bin edges
+//     certify a window [e_lo, e_hi] holding tau; the moments of the entries
+//     above e_hi and the entries inside the window (the step's last block
+//     solves for tau exactly); the weighted V gather, merged in helper order.
+//     A block waits only for blocks of lower index, which the hardware
+//     dispatches first, and every wait ends after a time limit (the row then
+//     reads NaN).  Every sum has a fixed order, so results repeat bit for bit.
 //
 // Full cache (the decode that reads every cached token, one of the baselines of
-// the summary's efficiency results, section 4): the same kernel 2 runs on a
-// selection of every page.  Its first launch streams K once per (b, KV head)
-// and range of pages, scoring all G query heads of the group from the same
-// bytes, and writes the identity selection next to the scores; V is then read
-// for the support only.
+// the summary's efficiency results, section 4): the same two launches with the
+// selection "every page", so K is read once per KV head and V for the support
+// only.
 #include <math.h>
 
 #include <algorithm>
@@ -43,25 +48,40 @@
 namespace ekv {
 
 constexpr int kDThreads = 256;
-constexpr int kDGrid = 1024;      // kernel 1: items are strided over this many blocks
-constexpr int kChunkTok = 2048;   // kernel 2: tokens per chunk block (long_1m decode: 2048 26.6 us, 1024 30.3, 4096 27.2, 8192 30.9)
-constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
-constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
-constexpr int kSupChunk = 512;    // support entries gathered per LDS pass
+constexpr int kMaxSlices = 1024;  // slices per (b, g) at most
+constexpr int kMaxR = 512;        // pages per slice at most (the page map of scores_kernel)
+constexpr int kLeadMax = 16384;   // entries a leader streams over (more: the helpers)
+constexpr int kCand = 1024;       // candidates in LDS for the one-wave solve and the sort form
 constexpr int kNThr = 8;          // count thresholds mx - 2^-i behind the certified bound on tau
-constexpr int kKeepIt = 3;        // kernel 2: 2048-token steps of a chunk kept in registers between passes
-constexpr int kIprLds = 2048;     // kernel 2: a split row's item -> physical page table staged in LDS up to this size
+constexpr int kHelpers = 32;      // helper blocks per row and step, at most
+constexpr int kBins = 4096;       // histogram bins of a large row
+constexpr int kSlot = 128;        // window entries a helper hands over
+constexpr int kWin = 4096;        // window entries the solving helper keeps in LDS
+constexpr int kWbuf = kHelpers * kSlot;  // candidates a leader keeps in its window buffer
+constexpr int kIprLds = 2048;     // a row's item -> physical page table staged in LDS up to this size
+constexpr unsigned kStHist = 2, kStMom = 3, kStGath = 4, kStDone = 0xFFu;  // row steps (0: scores written)
+constexpr unsigned long long kSpinTicks = 20000000ull;                     // 0.2 s of the 100 MHz clock
 
 struct DecodeWs {
-  double *xs;        // [rows][max_pages*P]  X of kept tokens (item-major); kernel 2 compacts
-                     //                      each chunk's candidates to the chunk's start
-  uint32_t *xi;      // [rows][max_pages*P]  token index (item*P + slot) of a compacted candidate
-  double *pmax;      // [rows][max_pages]    max X over item i's tokens, NaN if the item is malformed
-  uint32_t *iphys;   // [rows][max_pages]    physical page of item i
-  int *segcnt;       // [rows][kSplitMax]    candidates of each chunk
-  double *segL;      // [rows][kSplitMax]    each chunk's lower bound on tau
-  int *segn;         // [rows][kSplitMax][kNThr] each chunk's counts above mx - 2^-i
-  unsigned int *ctr; // [rows]               arrival counters (zeroed by kernel 1)
+  double *cx;         // [cap_tok]  entry X
+  uint32_t *ct;       // [cap_tok]  token id (item * P + slot) of a compact entry
+  uint32_t *iphys;    // [item_cap] physical page of an item
+  uint32_t *ipage;    // [item_cap] logical page of an item
+  int *s_cnt;         // [rows][ns] entries stored for the slice
+  double *s_max;      // [rows][ns] max X over the slice's kept tokens (-inf: none; NaN: malformed)
+  double *s_min;      // [rows][ns] min X over the slice's kept tokens (+inf: none)
+  uint32_t *s_start;  // [rows][ns] index in cx of the slice's first entry
+  int *s_dense;       // [rows][ns] 1: the entries are every kept token, in place
+  long long *rbase;   // [rows] first item of the row
+  int *rcnt;          // [rows] items of the row
+  unsigned *state;    // [rows] step of a large row
+  unsigned *ctr;      // [rows][3] arrival counters of the helper steps
+  double *rpar;       // [rows][8] published parameters (mx, lo, w, e_lo, e_hi, tau, z)
+  unsigned *hist;     // [rows][kBins]
+  double *hpart;      // [rows][kHelpers][8] moment partials
+  double *wbuf;       // [rows][kHelpers][kSlot] window entries (a leader's candidates: kWbuf)
+  uint32_t *wtok;     // [rows][kHelpers][kSlot] token ids of a leader's candidates
+  float *opart;       // [rows][kHelpers][d] partial outputs
 };
 
 struct DecodeParams {
@@ -97,61 +117,603 @@ __device__ __forceinline__ double pw_d(double y, const DecodeParams &dp) {
   else return dp.beta * pow_generic(y, dp.beta - 1.0);
 }
 
-// Selected-page count of a row clamped to [0, max_pages]; *bad is set for a
-// count outside [0, number of pages of the sequence].
-__device__ __forceinline__ int row_items(const Dims &D, const int32_t *seq_lens, const int32_t *sel_cnt,
-                                         int row, bool *bad) {
-  const int np = n_pages_of(seq_len_clamped(seq_lens, row / D.Hq, D), D.P);
-  int c = sel_cnt[row];
-  *bad = c < 0 || c > np;
-  return c < 0 ? 0 : (c > D.max_pages ? D.max_pages : c);
+__device__ __forceinline__ double wave_min_d(double v) { return -wave_max(-v); }
+__device__ __forceinline__ double block_min_d(double v, double *scratch) { return -block_max(-v, scratch); }
+
+// Exclusive prefix sum over a block of a 64-bit value (fixed order).
+__device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long long v, unsigned long long *scratch,
+                                                                unsigned long long *total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  unsigned long long x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned long long y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) scratch[w] = x;
+  __syncthreads();
+  unsigned long long base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) base += scratch[i];
+    tot += scratch[i];
+  }
+  *total = tot;
+  return base + x - v;
 }
 
-// Block-shared item map: prefix[r] = first item of row r, prefix[rows] = total.
-// Each thread owns a contiguous run of rows; its counts are loaded 8 at a time.
-__device__ int build_item_map(const Dims &D, const int32_t *seq_lens, const int32_t *sel_cnt,
-                              int *prefix, int rows, int *scan_scratch) {
-  const int per = (rows + kDThreads - 1) / kDThreads;
-  const int r0 = threadIdx.x * per;
-  int sum = 0;
-#pragma unroll 1
-  for (int c0 = 0; c0 < per; c0 += 8) {
-    int c[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      bool bad;
-      c[u] = row_items(D, seq_lens, sel_cnt, min(r0 + c0 + u, rows - 1), &bad);
+// Lower bounds of two keys in an ascending int list of n entries, by one wave:
+// each round probes 64 evenly spaced entries and keeps the gap between the
+// last probe below the key and the next one (one memory round trip per round;
+// n <= 64 takes one round, n <= 4096 two).  A list that is not ascending gives
+// some index in [0, n]; the caller checks the order of what it reads.
+__device__ __forceinline__ void wave_bounds(const int32_t *list, int n, int key1, int key2, int *out1, int *out2) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int lo1 = 0, hi1 = n, lo2 = 0, hi2 = n;
+  while (hi1 > lo1 || hi2 > lo2) {
+    const int st1 = (hi1 - lo1 + kWave - 1) / kWave, st2 = (hi2 - lo2 + kWave - 1) / kWave;
+    const int q1 = lo1 + lane * st1, q2 = lo2 + lane * st2;
+    const bool a1 = hi1 > lo1 && q1 < hi1, a2 = hi2 > lo2 && q2 < hi2;
+    const int v1 = a1 ? list[q1] : 0;
+    const int v2 = a2 ? list[q2] : 0;
+    const int c1 = __popcll(__ballot(a1 && v1 < key1));
+    const int c2 = __popcll(__ballot(a2 && v2 < key2));
+    if (hi1 > lo1) {
+      if (c1 == 0) {
+        hi1 = lo1;
+      } else {
+        const int nlo = lo1 + (c1 - 1) * st1 + 1;
+        hi1 = min(lo1 + c1 * st1, hi1);
+        lo1 = nlo;
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int r = r0 + c0 + u;
-      if (c0 + u < per && r < rows) { prefix[r] = c[u]; sum += c[u]; }
+    if (hi2 > lo2) {
+      if (c2 == 0) {
+        hi2 = lo2;
+      } else {
+        const int nlo = lo2 + (c2 - 1) * st2 + 1;
+        hi2 = min(lo2 + c2 * st2, hi2);
+        lo2 = nlo;
+      }
     }
   }
-  int tot;
-  int run = block_excl_scan(sum, scan_scratch, &tot);
-#pragma unroll 1
-  for (int u = 0; u < per; ++u) {
-    const int r = r0 + u;
-    if (r < rows) { const int c = prefix[r]; prefix[r] = run; run += c; }
-  }
-  if (threadIdx.x == 0) prefix[rows] = tot;
-  __syncthreads();
-  return tot;
+  *out1 = lo1;
+  *out2 = lo2;
 }
-__device__ __forceinline__ int find_row(const int *prefix, int rows, int item) {
-  int lo = 0, hi = rows - 1;  // largest r with prefix[r] <= item
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= item) lo = mid; else hi = mid - 1;
+
+// =========================================================== 1. scores kernel
+constexpr int kXl = 4096;  // X values a scores block stages in LDS (a slice whose union fits is compacted)
+
+// 16 consecutive K coordinates as loaded (two or four 16-byte loads), unpacked
+// to floats where they are used
+template <typename T>
+struct KRaw;
+template <>
+struct KRaw<uint16_t> {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const uint16_t *p) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    v[0] = q[0];
+    v[1] = q[1];
   }
-  return lo;
+  __device__ __forceinline__ void unpack(float (&f)[16]) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f[8 * c + 0] = bf16lo(v[c].x); f[8 * c + 1] = bf16hi(v[c].x);
+      f[8 * c + 2] = bf16lo(v[c].y); f[8 * c + 3] = bf16hi(v[c].y);
+      f[8 * c + 4] = bf16lo(v[c].z); f[8 * c + 5] = bf16hi(v[c].z);
+      f[8 * c + 6] = bf16lo(v[c].w); f[8 * c + 7] = bf16hi(v[c].w);
+    }
+  }
+};
+template <>
+struct KRaw<float> {
+  float4 v[4];
+  __device__ __forceinline__ void load(const float *p) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = q[c];
+  }
+  __device__ __forceinline__ void unpack(float (&f)[16]) const {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f[4 * c + 0] = v[c].x; f[4 * c + 1] = v[c].y; f[4 * c + 2] = v[c].z; f[4 * c + 3] = v[c].w;
+    }
+  }
+};
+struct KsArgs {
+  const void *q, *k_pool;
+  const int32_t *page_table, *seq_lens, *sel_idx, *sel_cnt;
+  float *weights_out;
+  int mode;            // 0: a set per query head; 1: a set per KV head; 2: every page
+  int ns;              // slices per (b, g)
+  long long item_cap;  // items the workspace holds
+};
+
+// items of row r: its count when in [0, N_b], else 0
+__device__ __forceinline__ int ks_row_items(const Dims &D, const KsArgs &a, int r) {
+  const int b = r / D.Hq;
+  const int np = n_pages_of(seq_len_clamped(a.seq_lens, b, D), D.P);
+  if (a.mode == 2) return np;
+  const int c = a.mode == 0 ? a.sel_cnt[r] : a.sel_cnt[(size_t)b * D.Hkv + (r % D.Hq) / D.G];
+  return (c < 0 || c > np) ? 0 : c;
+}
+
+template <typename T, int DIM, int P, int G>
+__global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
+  constexpr int kParts = DIM / 16;                            // threads per token, 16 coordinates each
+  constexpr int kUpp = P * kParts;                            // (token, part) units per page
+  constexpr int kTpp = kUpp < kDThreads ? kUpp : kDThreads;   // threads per page
+  constexpr int kPpi = kDThreads / kTpp;                      // pages per pass
+  constexpr int kUpt = kUpp / kTpp;                           // units per thread and page
+  constexpr int kLdsPages = kXl / (P * G);                   // union pages whose X fits the LDS stage
+  static_assert(kTpp % kWave == 0, "a page's threads form whole waves");
+  __shared__ unsigned umask[kMaxR];
+  __shared__ int upos[G][kMaxR];
+  __shared__ int ulist[kMaxR];
+  __shared__ uint32_t uphys[kMaxR];
+  __shared__ int s_lo[G], s_hi[G];
+  __shared__ long long s_base[G];
+  __shared__ int s_items[G];
+  __shared__ unsigned s_bad, s_nu;
+  __shared__ double s_red[kDThreads / kWave][2 * G];
+  __shared__ double s_mx[G], s_mn[G];
+  __shared__ long long red64[kDThreads / kWave];
+  __shared__ int scan_scratch[kDThreads / kWave];
+  __shared__ unsigned long long scan64[kDThreads / kWave];
+  __shared__ __align__(16) float qs[G][DIM];
+  __shared__ double xl[kXl];
+  __shared__ double s_thr[G];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int ns = a.ns;
+  const int gi = blockIdx.x / ns, s = blockIdx.x % ns;
+  const int b = gi / D.Hkv, g = gi % D.Hkv;
+  const int r0 = b * D.Hq + g * G;
+  const int MP = D.max_pages;
+  const int L = seq_len_clamped(a.seq_lens, b, D);
+  const int np = n_pages_of(L, P);
+  const int R = max(1, (np + ns - 1) / ns);
+  const int p0 = s * R;
+  const T *q = (const T *)a.q;
+  const T *k_pool = (const T *)a.k_pool;
+  EKV_MARK(0, 0);
+
+  // ---- the group's rows: first item (items of every earlier row), counts
+  long long part = 0;
+  for (int r = tid; r < r0; r += kDThreads) part += ks_row_items(D, a, r);
+  part = block_sum(part, red64);
+  if (tid == 0) {
+    long long base = part;
+    unsigned bad = 0;
+    for (int h = 0; h < G; ++h) {
+      const int r = r0 + h;
+      const int raw = a.mode == 2 ? np : (a.mode == 0 ? a.sel_cnt[r] : a.sel_cnt[gi]);
+      const int it = (raw < 0 || raw > np) ? 0 : raw;
+      s_base[h] = base;
+      s_items[h] = it;
+      if (raw < 0 || raw > np || base + it > a.item_cap) bad |= 1u << h;
+      base += it;
+    }
+    s_bad = (a.mode == 1 && bad) ? (1u << G) - 1u : bad;  // a group set serves all G rows
+  }
+  __syncthreads();
+
+  // ---- each list's items inside the slice [p0, p0 + R) (the last slice takes the rest)
+  const int nl = a.mode == 0 ? G : 1;
+  const unsigned all = (1u << G) - 1u;
+  if (a.mode == 2) {
+    if (tid < G) {
+      s_lo[tid] = min(p0, np);
+      s_hi[tid] = min(p0 + R, np);
+    }
+  } else {
+    for (int li = wv; li < nl; li += kDThreads / kWave) {
+      const bool lbad = a.mode == 0 ? ((s_bad >> li) & 1u) != 0u : s_bad != 0u;
+      const int n = lbad ? 0 : s_items[li];
+      const int32_t *list = a.sel_idx + (size_t)(a.mode == 0 ? r0 + li : gi) * MP;
+      int lo, hi;
+      wave_bounds(list, n, p0, p0 + R, &lo, &hi);
+      if (s == 0) lo = 0;
+      if (s == ns - 1) hi = n;
+      if (hi < lo) hi = lo;
+      if (lane == 0) {
+        s_lo[li] = lo;
+        s_hi[li] = hi;
+      }
+    }
+  }
+  for (int o = tid; o < R; o += kDThreads) umask[o] = 0u;
+  __syncthreads();
+  if (a.mode == 2) {
+    for (int o = tid; o < R; o += kDThreads)
+      if (p0 + o < np) {
+        umask[o] = all;
+        upos[0][o] = p0 + o;
+      }
+  } else {
+    for (int li = wv; li < nl; li += kDThreads / kWave) {
+      const int32_t *list = a.sel_idx + (size_t)(a.mode == 0 ? r0 + li : gi) * MP;
+      const int lo = s_lo[li], hi = s_hi[li];
+      int bad = 0;
+      for (int i = lo + lane; i < hi; i += kWave) {
+        const int p = list[i];
+        const int prev = i > 0 ? list[i - 1] : -1;
+        const int o = p - p0;
+        if (p < 0 || p >= np || p <= prev || o < 0 || o >= R) {
+          bad = 1;
+          continue;
+        }
+        atomicOr(&umask[o], a.mode == 0 ? (1u << li) : all);
+        upos[li][o] = i;
+      }
+      if (__any(bad) && lane == 0) atomicOr(&s_bad, a.mode == 0 ? (1u << li) : all);
+    }
+  }
+  __syncthreads();
+
+  // ---- the union in page order (two offsets per thread) and its physical pages
+  {
+    const int o0 = 2 * tid;
+    const int m0 = (o0 < R && umask[o0]) ? 1 : 0, m1 = (o0 + 1 < R && umask[o0 + 1]) ? 1 : 0;
+    int tot;
+    const int at = block_excl_scan(m0 + m1, scan_scratch, &tot);
+    if (m0) ulist[at] = o0;
+    if (m1) ulist[at + m0] = o0 + 1;
+    if (tid == 0) s_nu = (unsigned)tot;
+  }
+  __syncthreads();
+  const int nU = (int)s_nu;
+  for (int k = tid; k < nU; k += kDThreads) {
+    const int o = ulist[k];
+    const int ph = a.page_table[(size_t)b * MP + p0 + o];
+    const bool ok = ph >= 0 && ph < D.num_phys;
+    uphys[k] = ok ? (uint32_t)ph : 0u;
+    if (!ok) atomicOr(&s_bad, umask[o]);
+  }
+  __syncthreads();
+  const unsigned live = all & ~s_bad;
+  // per-item physical and logical pages of the rows' items in this slice
+  for (int k = tid; k < nU; k += kDThreads) {
+    const int o = ulist[k];
+    const unsigned m = umask[o] & live;
+    for (int h = 0; h < G; ++h)
+      if (m & (1u << h)) {
+        const int item = upos[a.mode == 0 ? h : 0][o];
+        const size_t idx = (size_t)(s_base[h] + item);
+        ws.iphys[idx] = uphys[k];
+        ws.ipage[idx] = (uint32_t)(p0 + o);
+      }
+  }
+  // weights_out: every slot of the slice's pages (the last slice to the end of
+  // the row) is zeroed here; rows_kernel writes the support
+  if (a.weights_out) {
+    const size_t wrow = (size_t)MP * P;
+    const size_t lo_s = (size_t)min(p0, MP) * P;
+    const size_t hi_s = s == ns - 1 ? wrow : (size_t)min(p0 + R, MP) * P;
+    for (int h = 0; h < G; ++h)
+      for (size_t i = lo_s + tid; i < hi_s; i += kDThreads) a.weights_out[(size_t)(r0 + h) * wrow + i] = 0.0f;
+  }
+  // row bookkeeping of the rows_kernel (once per row)
+  if (s == 0 && tid < G) {
+    const int r = r0 + tid;
+    ws.rbase[r] = s_base[tid];
+    ws.rcnt[r] = s_items[tid];
+    ws.state[r] = 0u;
+    ws.ctr[3 * r] = 0u;
+    ws.ctr[3 * r + 1] = 0u;
+    ws.ctr[3 * r + 2] = 0u;
+  }
+  EKV_MARK(0, 1);
+
+  // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
+  const int j = tid / kTpp, u0 = tid % kTpp, e = u0 % kParts;
+  for (int i = tid; i < G * DIM; i += kDThreads) qs[i / DIM][i % DIM] = load_f(q, (size_t)r0 * DIM + i);
+  __syncthreads();
+  const int npass = (nU + kPpi - 1) / kPpi;
+  double lmax[G], lmin[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lmax[h] = -INFINITY;
+    lmin[h] = INFINITY;
+  }
+  // compact when the union's X fits the LDS stage, else the dense layout
+  const bool dense = nU > kLdsPages;
+  auto item_of = [&](int h, int o) __attribute__((always_inline)) { return upos[a.mode == 0 ? h : 0][o]; };
+  auto lo_of = [&](int h) __attribute__((always_inline)) { return s_lo[a.mode == 0 ? h : 0]; };
+  auto load_pass = [&](int pass, KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
+    const int k = pass * kPpi + j;
+    if (k < nU) {  // uniform per wave
+      const size_t ph = uphys[k];
+#pragma unroll
+      for (int u = 0; u < kUpt; ++u) {
+        const int t = (u0 + u * kTpp) / kParts;
+        kv[u].load(k_pool + ((ph * D.Hkv + g) * P + t) * DIM + e * 16);
+      }
+    }
+  };
+  // X of one pass (-inf for heads that did not keep the page and for slots
+  // past the sequence end) into the LDS stage or the dense layout
+  auto score_pass = [&](int pass, const KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
+    const int k = pass * kPpi + j;
+    const bool act = k < nU;
+    const int o = act ? ulist[k] : 0;
+    const unsigned m = act ? (umask[o] & live) : 0u;
+    const int ntok = min(P, L - (p0 + o) * P);
+#pragma unroll
+    for (int u = 0; u < kUpt; ++u) {
+      const int t = (u0 + u * kTpp) / kParts;
+      float kf[16];
+      kv[u].unpack(kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        double x = -INFINITY;
+        if (m & (1u << h)) {  // uniform per wave
+          const float4 *qp = reinterpret_cast<const float4 *>(&qs[h][e * 16]);
+          double acc = 0.0;
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const float4 qv = qp[c4];
+            acc = __builtin_fma((double)kf[4 * c4 + 0], (double)qv.x, acc);  // exact products
+            acc = __builtin_fma((double)kf[4 * c4 + 1], (double)qv.y, acc);
+            acc = __builtin_fma((double)kf[4 * c4 + 2], (double)qv.z, acc);
+            acc = __builtin_fma((double)kf[4 * c4 + 3], (double)qv.w, acc);
+          }
+#pragma unroll
+          for (int sh = kParts / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh, kWave);
+          if (t < ntok) x = dp.a * (dp.c * acc);
+        }
+        lmax[h] = fmax(lmax[h], x);
+        if (x > -INFINITY) lmin[h] = fmin(lmin[h], x);
+        if (act && e == 0) {
+          if (!dense) xl[(k * P + t) * G + h] = x;
+          else if (m & (1u << h)) ws.cx[(size_t)(s_base[h] + item_of(h, o)) * P + t] = x;
+        }
+      }
+    }
+  };
+  KRaw<T> ka0[kUpt], ka1[kUpt], ka2[kUpt];
+  if (npass > 0) load_pass(0, ka0);
+  if (npass > 1) load_pass(1, ka1);
+#pragma unroll 1
+  for (int pass = 0; pass < npass; ++pass) {
+    if (pass + 2 < npass) load_pass(pass + 2, ka2);
+    score_pass(pass, ka0);
+#pragma unroll
+    for (int u = 0; u < kUpt; ++u) {
+      ka0[u] = ka1[u];
+      ka1[u] = ka2[u];
+    }
+  }
+  // slice max / min per head
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lmax[h] = wave_max(lmax[h]);
+    lmin[h] = wave_min_d(lmin[h]);
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s_red[wv][h] = lmax[h];
+      s_red[wv][G + h] = lmin[h];
+    }
+  __syncthreads();
+  if (tid < G) {
+    double m = s_red[0][tid], n = s_red[0][G + tid];
+    for (int w = 1; w < kDThreads / kWave; ++w) {
+      m = fmax(m, s_red[w][tid]);
+      n = fmin(n, s_red[w][G + tid]);
+    }
+    s_mx[tid] = m;
+    s_mn[tid] = n;
+    s_thr[tid] = m - 1.0;  // every candidate of the row (X > row max - 1) is above it
+  }
+  __syncthreads();
+  int ncnt[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) ncnt[h] = 0;
+  if (!dense) {
+    // compaction: the entries X > (slice max) - 1 of each head in index
+    // order, four heads per packed 64-bit scan (16-bit counts)
+#pragma unroll 1
+    for (int pass = 0; pass < npass; ++pass) {
+      const int k = pass * kPpi + j;
+      const bool act = k < nU;
+      const int o = act ? ulist[k] : 0;
+#pragma unroll
+      for (int u = 0; u < kUpt; ++u) {
+        const int t = (u0 + u * kTpp) / kParts;
+#pragma unroll
+        for (int h0 = 0; h0 < G; h0 += 4) {
+          double xo[4];
+          unsigned long long mine = 0;
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) {
+            xo[hh] = (h0 + hh < G && act && e == 0) ? xl[(k * P + t) * G + h0 + hh] : -INFINITY;
+            if (h0 + hh < G && xo[hh] > s_thr[h0 + hh]) mine |= 1ull << (16 * hh);
+          }
+          unsigned long long tot;
+          const unsigned long long pre = block_excl_scan64(mine, scan64, &tot);
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) {
+            const int h = h0 + hh;
+            if (h < G) {
+              if ((mine >> (16 * hh)) & 1ull) {
+                const size_t at = (size_t)(s_base[h] + lo_of(h)) * P + ncnt[h] + (int)((pre >> (16 * hh)) & 0xFFFFull);
+                ws.cx[at] = xo[hh];
+                ws.ct[at] = (uint32_t)(item_of(h, o) * P + t);
+              }
+              ncnt[h] += (int)((tot >> (16 * hh)) & 0xFFFFull);
+            }
+          }
+        }
+      }
+    }
+  }
+  // ---- per (row, slice) summary
+  if (tid < G) {
+    const int h = tid, r = r0 + h;
+    const bool bad = (s_bad >> h) & 1u;
+    const int lo = lo_of(h), hi = s_hi[a.mode == 0 ? h : 0];
+    const size_t o = (size_t)r * ns + s;
+    int c = 0;
+    if (!bad) c = dense ? (hi - lo) * P : ncnt[h];
+    ws.s_cnt[o] = c;
+    ws.s_max[o] = bad ? NAN : s_mx[h];
+    ws.s_min[o] = s_mn[h];
+    ws.s_start[o] = bad ? 0u : (uint32_t)((s_base[h] + lo) * P);
+    ws.s_dense[o] = dense ? 1 : 0;
+  }
+  EKV_MARK(0, 2);
+}
+
+// ================================================================ 2. rows kernel
+struct RowsArgs {
+  const void *v_pool;
+  float *out;
+  double *tau;
+  float *weights_out;
+  int ns, nh;
+};
+
+// The entries of a run of slices, concatenated in index order; the slice
+// tables sit in LDS.  Entry k of slice i is cx[start[i] + k - off[i]]; its
+// token id is ct[...] for a compact slice and the offset from the row's first
+// token for a dense one.
+struct Segs {
+  const int *off;           // [n + 1]
+  const uint32_t *start;    // [n]
+  const int *dense;         // [n]
+  int n, total;
+  unsigned long long tok0;  // rbase * P
+  __device__ __forceinline__ int seg_of(int k) const {
+    int lo = 0, hi = n - 1;  // last slice starting at or before k
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+  // addresses of entries min(k0 + u, total - 1), u < R: one search, then the
+  // slice advances with k (empty slices are stepped over)
+  template <int R>
+  __device__ __forceinline__ void addr_run(int k0, size_t (&ad)[R], bool (&dn)[R]) const {
+    int lo = seg_of(min(k0, total - 1));
+    int next = lo + 1 < n ? off[lo + 1] : 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int k = min(k0 + u, total - 1);
+      while (k >= next) {
+        ++lo;
+        next = lo + 1 < n ? off[lo + 1] : 0x7fffffff;
+      }
+      ad[u] = (size_t)start[lo] + (size_t)(k - off[lo]);
+      dn[u] = dense[lo] != 0;
+    }
+  }
+  __device__ __forceinline__ uint32_t tok_of(const DecodeWs &ws, size_t ad, bool dn) const {
+    return dn ? (uint32_t)(ad - tok0) : ws.ct[ad];
+  }
+};
+
+// Slice tables of the non-empty slices among [s0, s1) of row r into LDS (one
+// packed 64-bit scan gives both the entry offsets and the table positions);
+// returns the entry total, *nseg the number of tables.  With mxmn, also the
+// max and min of the slices' X over this thread's slices and a NaN mark.
+__device__ __forceinline__ int load_segs(const DecodeWs &ws, int r, int ns, int s0, int s1, int *off, uint32_t *start,
+                                         int *dense, unsigned long long *scan64, int *nseg, double *mxmn = nullptr,
+                                         int *nan = nullptr) {
+  const int n = s1 - s0;
+  constexpr int kMaxPer = (kMaxSlices + kDThreads - 1) / kDThreads;
+  const int per = (n + kDThreads - 1) / kDThreads;
+  const int i0 = threadIdx.x * per;
+  int c[kMaxPer];
+  uint32_t st[kMaxPer];
+  int dn[kMaxPer];
+  double mx = -INFINITY, mn = INFINITY;
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = i0 + u;
+    c[u] = 0;
+    if (u < per && i < n) {
+      const size_t o = (size_t)r * ns + s0 + i;
+      c[u] = ws.s_cnt[o];
+      st[u] = ws.s_start[o];
+      dn[u] = ws.s_dense[o];
+      if (mxmn) {
+        const double v = ws.s_max[o];
+        bad |= v != v;
+        mx = fmax(mx, v);
+        mn = fmin(mn, ws.s_min[o]);
+      }
+    }
+  }
+  if (mxmn) {
+    mxmn[0] = mx;
+    mxmn[1] = mn;
+    *nan = bad;
+  }
+  unsigned long long mine = 0;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) mine += ((unsigned long long)(c[u] > 0 ? 1 : 0) << 32) + (unsigned)c[u];
+  unsigned long long tot;
+  unsigned long long run = block_excl_scan64(mine, scan64, &tot);
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    if (c[u] > 0) {
+      const int at = (int)(run >> 32);
+      off[at] = (int)(run & 0xFFFFFFFFull);
+      start[at] = st[u];
+      dense[at] = dn[u];
+      run += (1ull << 32) + (unsigned)c[u];
+    }
+  }
+  const int ntab = (int)(tot >> 32), total = (int)(tot & 0xFFFFFFFFull);
+  if (threadIdx.x == 0) {
+    off[ntab] = total;
+    if (ntab == 0) {  // an empty run: one empty table keeps the lookups in range
+      off[0] = 0;
+      off[1] = 0;
+      start[0] = 0u;
+      dense[0] = 1;
+    }
+  }
+  __syncthreads();
+  *nseg = ntab > 0 ? ntab : 1;
+  return total;
+}
+
+// Eight consecutive entries per thread (X, and token ids when asked);
+// entries past the end read -inf.
+struct Batch8 {
+  double v[8];
+  uint32_t t[8];
+};
+__device__ __forceinline__ void load_batch8(const Segs &sg, const DecodeWs &ws, int k0, bool toks, Batch8 &bt) {
+  if (k0 < sg.total) {
+    size_t ad[8];
+    bool dn[8];
+    sg.addr_run<8>(k0, ad, dn);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bt.v[u] = ws.cx[ad[u]];
+    if (toks)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) bt.t[u] = sg.tok_of(ws, ad[u], dn[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u >= sg.total) bt.v[u] = -INFINITY;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      bt.v[u] = -INFINITY;
+      bt.t[u] = 0u;
+    }
+  }
 }
 
 // ------------------------------------------------------------- threshold solve
-// Values seen by the solver: LDS candidates (strided over the participating
-// threads) or, for a row whose candidates overflow LDS, every score of the row
-// in the workspace above the bound `thr` (batched agent-scope loads).
+// Values seen by the solver: LDS entries (strided over the participating
+// threads), registers, or every entry of a row in the workspace.
 struct LdsVals {
   const double *v;
   int n, t0, stride;
@@ -161,67 +723,24 @@ struct LdsVals {
     for (int i = t0; i < n; i += stride) fn(v[i]);
   }
 };
-// Compacted candidates in the workspace: segment s (chunk s of the row) holds
-// soff[s+1]-soff[s] entries from token offset sbase[s]; entry k of the
-// concatenation is found by a scan over the (at most kSplitMax) segments.
-template <int kBatch>
-struct GlobSeg {
-  const double *x;
-  const int *soff;   // LDS, [nseg + 1] first entry of each segment
-  const int *sbase;  // LDS, [nseg]     token offset where each segment starts
-  int nseg, n;
-  __device__ __forceinline__ int seg_of(int k) const {
-    int lo = 0, hi = nseg - 1;  // last segment starting at or before k
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (soff[mid] <= k) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  }
-  __device__ __forceinline__ int addr(int k) const {
-    const int lo = seg_of(k);
-    return sbase[lo] + (k - soff[lo]);
-  }
-  // addresses of entries min(k0 + u, n - 1), u < R: one search, then the
-  // segment advances with k (empty segments are stepped over)
-  template <int R>
-  __device__ __forceinline__ void addr_run(int k0, int (&a)[R]) const {
-    int lo = seg_of(min(k0, n - 1));
-    int next = lo + 1 < nseg ? soff[lo + 1] : 0x7fffffff;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int k = min(k0 + u, n - 1);
-      while (k >= next) {
-        ++lo;
-        next = lo + 1 < nseg ? soff[lo + 1] : 0x7fffffff;
-      }
-      a[u] = sbase[lo] + (k - soff[lo]);
-    }
-  }
+struct GlobVals {  // every entry of a run of slices, 8 per thread in flight
+  const DecodeWs *ws;
+  const Segs *sg;
   template <typename Fn>
   __device__ __forceinline__ void each(Fn &&fn) const {
 #pragma unroll 1
-    for (int base = 0; base < n; base += kBatch * kDThreads) {
-      double v[kBatch];
+    for (int base = 0; base < sg->total; base += 8 * kDThreads) {
+      const int k0 = base + 8 * (int)threadIdx.x;
+      size_t ad[8];
+      bool dn[8];
+      sg->addr_run<8>(k0, ad, dn);
+      double v[8];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = ld_agent(&x[addr(min(base + u * kDThreads + (int)threadIdx.x, n - 1))]);
+      for (int u = 0; u < 8; ++u) v[u] = ws->cx[ad[u]];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (base + u * kDThreads + (int)threadIdx.x < n) fn(v[u]);
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < sg->total) fn(v[u]);
     }
-  }
-};
-
-// Candidates held in registers: thread t owns entries 16t .. 16t + 15.
-constexpr int kRegPer = 16;
-struct RegVals {
-  const double (&v)[kRegPer];
-  int n;
-  template <typename Fn>
-  __device__ __forceinline__ void each(Fn &&fn) const {
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j)
-      if ((int)threadIdx.x * kRegPer + j < n) fn(v[j]);
   }
 };
 struct WaveRed {
@@ -239,13 +758,18 @@ struct BlockRed {
   __device__ __forceinline__ double max(double v, double *s) const { return block_max(v, s); }
 };
 
+// Entries known only through their moments: m0 entries above e with
+// m1 = sum (x - e), m2 = sum (x - e)^2 and ymin = min (x - e) (m0 = 0: none).
+struct Above {
+  double m0, m1, m2, ymin, e;
+};
+
 // Root of F(t) = sum [X - t]_+^beta = 1 by Newton from the left: lo0 has
-// F >= 1 (mx - 1 or a tighter certified bound), hi = mx - n^-(alpha-1) has
-// F <= 1 (n >= the number of scores above hi).  For alpha <= 2 (beta >= 1) F is convex and decreasing, so every
-// Newton iterate from the left stays left of the root: one pass per step.
-// Otherwise each Newton candidate is checked with a second pass; one that
-// leaves (lo, hi) becomes a bisection step, and after a step lands right of
-// the root the next step bisects.
+// F >= 1 (a certified lower bound), hi has F <= 1.  For alpha <= 2 (beta >= 1)
+// F is convex and decreasing, so every Newton iterate from the left stays left
+// of the root: one pass per step.  Otherwise each Newton candidate is checked
+// with a second pass; one that leaves (lo, hi) becomes a bisection step, and
+// after a step lands right of the root the next step bisects.
 //
 // alpha = 2 and 1.5 (beta = 1, 2): between consecutive scores F is linear or
 // quadratic, F(lo + u) = sum_A (y - u)^beta over the active set A = {y = X - lo
@@ -253,14 +777,13 @@ struct BlockRed {
 // smaller root (S2 - 1)/(S1 + sqrt(S1^2 - |A|(S2 - 1))) of |A| u^2 - 2 S1 u + S2
 // = 1); when u <= min_A y every active score stays active at lo + u, so lo + u
 // is F's root and the pass ends the search (*z_out = F there, from the same
-// sums).  Otherwise the Newton step is taken as above.  Rows end in 1-4 passes
-// instead of 5-8.  *z_out = 0 when the search ends another way.
+// sums).  The entries of `ab` (all above hi, so active throughout) enter the
+// sums through their moments.  *z_out = 0 when the search ends another way.
 template <int kB, typename Src, typename Red>
-__device__ __forceinline__ double newton_tau(const Src &src, double n, double mx, double lo0,
+__device__ __forceinline__ double newton_tau(const Src &src, const Above &ab, double lo0, double hi,
                                              const DecodeParams &dp, double *dred, double *z_out) {
   const Red red;
   double lo = lo0;
-  double hi = mx - pow(n, -dp.a);
   *z_out = 0.0;
   if (!(hi > lo)) return lo;
   if (kB == 1 || kB == 2) {
@@ -274,6 +797,13 @@ __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx
       });
       red.sums3(sm, dred);
       nmn = red.max(nmn, dred);
+      if (ab.m0 > 0.0) {
+        const double d = ab.e - lo;  // >= 0
+        sm[0] += ab.m1 + d * ab.m0;
+        sm[1] += ab.m2 + (2.0 * d) * ab.m1 + (d * d) * ab.m0;
+        sm[2] += ab.m0;
+        nmn = fmax(nmn, -(ab.ymin + d));
+      }
       const double s1 = sm[0], s2 = sm[1], c = sm[2];
       const double f = kB == 2 ? s2 : s1;
       if (!(f > 1.0) || !(c > 0.0)) break;  // at the root (to rounding)
@@ -338,6 +868,28 @@ __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx
   return lo;
 }
 
+// tau and z = F(tau) over a source by the whole block; ab as in newton_tau
+// (m0 > 0 only for alpha = 1.5, 2).
+template <typename Src>
+__device__ void solve_block(const Src &src, const Above &ab, double lo0, double hi, const DecodeParams &dp,
+                            double *dred, double &tau, double &z) {
+  double zk = 0.0;
+  if (dp.ibeta == 2) tau = newton_tau<2, Src, BlockRed>(src, ab, lo0, hi, dp, dred, &zk);
+  else if (dp.ibeta == 1) tau = newton_tau<1, Src, BlockRed>(src, ab, lo0, hi, dp, dred, &zk);
+  else tau = newton_tau<0, Src, BlockRed>(src, ab, lo0, hi, dp, dred, &zk);
+  if (zk > 0.0) {
+    z = zk;
+    return;
+  }
+  double zz = 0.0;
+  src.each([&](double x) { const double y = x - tau; if (y > 0.0) zz += pw_rt(y, dp); });
+  if (ab.m0 > 0.0 && threadIdx.x == 0) {  // the moment entries: sum (y + d)^beta in closed form
+    const double d = ab.e - tau;
+    zz += dp.ibeta == 2 ? ab.m2 + (2.0 * d) * ab.m1 + (d * d) * ab.m0 : ab.m1 + d * ab.m0;
+  }
+  z = block_sum(zz, dred);
+}
+
 // sparsemax closed form (Martins & Astudillo 2016) by a bitonic sort in LDS:
 // sort z descending; k* = max{k : 1 + k z_(k) > sum_{j<=k} z_(j)};
 // tau = (sum_{j<=k*} z_(j) - 1) / k*.  The condition holds exactly for k <= k*.
@@ -394,488 +946,60 @@ __device__ double sparsemax_tau_sort(const double *cx, int n, double *buf, doubl
   return (part - 1.0) / (double)ks;
 }
 
-// Threshold tau and normalizer z = sum p of a row from its candidates, which
-// sit in LDS (tier 0), in registers (tier 1, not for generic alpha) or in the
-// workspace (tier 2).
-template <int kB>
-__device__ __forceinline__ void solve_row(int tier, const DecodeParams &dp, double mx, double lo0, int total, const double *cx,
-                                          double *sortbuf, const double (&rx)[kRegPer], const GlobSeg<1> &gs,
-                                          double *dred, int *s_kstar, double *s_tau, double &tau, double &z) {
-  const int tid = threadIdx.x;
-  const GlobSeg<16> gs8{gs.x, gs.soff, gs.sbase, gs.nseg, gs.n};  // 16 scores per thread in flight per step
-  double zk = 0.0;  // F at tau when the solver found it from its sums (else 0)
-  if (tier == 0 && kB == 1 && dp.tau_method == 1) {
-    tau = sparsemax_tau_sort(cx, total, sortbuf, dred, s_kstar);
-  } else if (tier == 0) {
-    if (tid < kWave) {
-      const double t = newton_tau<kB, LdsVals, WaveRed>(LdsVals{cx, total, tid, kWave}, (double)total, mx, lo0, dp,
-                                                         dred, &zk);
-      if (tid == 0) { s_tau[0] = t; s_tau[1] = zk; }
-    }
-    __syncthreads();
-    tau = s_tau[0];
-    zk = s_tau[1];
-  } else if (kB != 0 && tier == 1) {
-    tau = newton_tau<kB, RegVals, BlockRed>(RegVals{rx, total}, (double)total, mx, lo0, dp, dred, &zk);
-  } else if (kB != 0) {
-    tau = newton_tau<kB, GlobSeg<16>, BlockRed>(gs8, (double)total, mx, lo0, dp, dred, &zk);
-  } else {
-    tau = newton_tau<kB, GlobSeg<1>, BlockRed>(gs, (double)total, mx, lo0, dp, dred, &zk);
-  }
-  if (zk > 0.0) {
-    z = zk;
-    return;
-  }
-  double zz = 0.0;
-  auto zsum = [&](double x) { const double y = x - tau; if (y > 0.0) zz += pw<kB>(y, dp); };
-  if (tier == 0) LdsVals{cx, total, tid, kDThreads}.each(zsum);
-  else if (kB != 0 && tier == 1) RegVals{rx, total}.each(zsum);
-  else if (kB != 0) gs8.each(zsum);
-  else gs.each(zsum);
-  z = block_sum(zz, dred);
-}
+// ------------------------------------------------------------- support gather
+// Support entries are placed in LDS by block scans (in the order they are
+// offered); a flush turns each token id into its V row (the item's physical
+// page) and accumulates p_t v_t: kEpp entries per pass with kTpe threads each
+// (8 coordinates per 16-byte load), fp32 in a fixed order.
+constexpr int kSupCap = 2048;  // support entries held in LDS between flushes
+template <typename T, int DIM>
+struct GatherLds {
+  static constexpr int kTpe = DIM / 8;           // threads per support entry
+  static constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
+  uint32_t tok[kSupCap];  // token id, then V row
+  float w[kSupCap];
+  float accs[kEpp][DIM + 1];
+};
 
-// ---------------------------------------------------------------- kernel 1: scores
-template <typename T, int DIM, int P>
-__global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
-    Dims D, DecodeParams dp, const T *__restrict__ q, const T *__restrict__ k_pool,
-    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt,
-    float *__restrict__ weights_out, DecodeWs ws) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kParts = kDThreads / P;  // threads per token
-  constexpr int kPer = DIM / kParts;     // coordinates per thread
-  __shared__ double dred[2 * kDThreads / kWave];
-  __shared__ int scan_scratch[kDThreads / kWave];
-  const int rows = D.B * D.Hq;
-  int *prefix = reinterpret_cast<int *>(smem);
-  const int tid = threadIdx.x;
-  // kernel 2's arrival counters start at zero
-  for (int r = blockIdx.x * kDThreads + tid; r < rows; r += gridDim.x * kDThreads) ws.ctr[r] = 0u;
-  const int total = build_item_map(D, seq_lens, sel_cnt, prefix, rows, scan_scratch);
-  const int MP = D.max_pages;
-  const size_t wrow = (size_t)MP * P;
-  const int tok = tid / kParts, part = tid % kParts;
-#pragma unroll 1
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int r = find_row(prefix, rows, item);
-    const int i = item - prefix[r];
-    const int cnt = prefix[r + 1] - prefix[r];
-    const int b = r / D.Hq, g = (r % D.Hq) / D.G;
-    // independent loads first: sequence length, page ids, the query slice
-    const int L = seq_len_clamped(seq_lens, b, D);
-    const int p = sel_idx[(size_t)r * MP + i];
-    const int prev = i > 0 ? sel_idx[(size_t)r * MP + i - 1] : -1;
-    float qv[kPer];
-    load_vec<kPer>(q + (size_t)r * DIM + part * kPer, qv);
-    const int np = n_pages_of(L, P);
-    const int pc = min(max(p, 0), MP - 1);
-    const int phys = page_table[(size_t)b * MP + pc];
-    const bool bad_item = p < 0 || p >= np || prev >= p || phys < 0 || phys >= D.num_phys;
-    const int physc = min(max(phys, 0), D.num_phys - 1);
-    const int n = min(P, L - pc * P);
-    float kv[kPer];
-    load_vec<kPer>(k_pool + (((size_t)physc * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
-    double acc = 0.0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[e], acc);
-#pragma unroll
-    for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    const double x = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
-    if (part == 0) ws.xs[(size_t)r * wrow + (size_t)i * P + tok] = x;
-    const double pm = block_max(x, dred);
-    if (tid == 0) {
-      ws.pmax[(size_t)r * MP + i] = bad_item ? NAN : pm;
-      ws.iphys[(size_t)r * MP + i] = (uint32_t)physc;
-    }
-    // weights_out: zero every slot of the pages this item covers, (prev, p]
-    // (the last item also covers the pages after p); kernel 2 writes the
-    // support weights.
-    if (weights_out && !bad_item) {
-      const size_t lo_s = (size_t)(prev + 1) * P;
-      const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
-      for (size_t s = lo_s + tid; s < hi_s; s += kDThreads) weights_out[(size_t)r * wrow + s] = 0.0f;
-    }
-  }
-}
-
-// ------------------------------------------------ kernel 2: threshold and output
-template <typename T, int DIM, int P>
-__global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
-    Dims D, DecodeParams dp, const T *__restrict__ v_pool, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt, float *__restrict__ out,
-    double *__restrict__ tau_out, float *__restrict__ weights_out, DecodeWs ws) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kTpe = DIM / 8;           // threads per support entry in the V gather
-  constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
-  __shared__ double dred[3 * kDThreads / kWave];  // up to three block sums at once
-  __shared__ int scan_scratch[kDThreads / kWave];
-  __shared__ int s_last, s_kstar;
-  __shared__ double s_tau[2];
-  __shared__ int soff[kSplitMax + 1], sbase[kSplitMax];
-  __shared__ double sL[kSplitMax];
-  __shared__ int s_cnt[kDThreads / kWave][kNThr];
-  __shared__ uint32_t sup_v[kSupChunk];
-  __shared__ int sup_i[kSupChunk];
-  __shared__ float sup_w[kSupChunk];
-  __shared__ float accs[kEpp][DIM + 1];
-  __shared__ uint32_t s_ipr[kIprLds];
-  double *cx = reinterpret_cast<double *>(smem);              // [kCand] candidate X
-  int *ci = reinterpret_cast<int *>(cx + kCand);              // [kCand] token index
-  uint32_t *cv = reinterpret_cast<uint32_t *>(ci + kCand);    // [kCand] V row index
-  double *sortbuf = reinterpret_cast<double *>(cv + kCand);   // [kCand] (sort form only)
-  const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  EKV_MARK(1, 0);
-  const int MP = D.max_pages;
-  const size_t wrow = (size_t)MP * P;
-  const int g = (r % D.Hq) / D.G;
-  bool bad;
-  const int cnt = row_items(D, seq_lens, sel_cnt, r, &bad);
-  if (cnt == 0) {
-    if (c == 0) {
-      if (tid == 0 && tau_out) tau_out[r] = NAN;
-      for (int i = tid; i < DIM; i += kDThreads) out[(size_t)r * DIM + i] = bad ? NAN : 0.0f;
-      if (weights_out)
-        for (size_t i = tid; i < wrow; i += kDThreads) weights_out[(size_t)r * wrow + i] = 0.0f;
-    }
-    return;
-  }
-  const int nX = cnt * P;
-  const int nsplit = min((int)gridDim.y, (nX + kChunkTok - 1) / kChunkTok);
-  if (c >= nsplit) return;
-  const double *pmr = ws.pmax + (size_t)r * MP;
-  const uint32_t *ipr = ws.iphys + (size_t)r * MP;
-  double *xrow = ws.xs + (size_t)r * wrow;
-  uint32_t *xir = ws.xi + (size_t)r * wrow;
-
-  // 1. row maximum from the page maxima; a NaN maximum marks a malformed item
-  double mx = -INFINITY;
-  int nan = 0;
-#pragma unroll 1
-  for (int base = 0; base < cnt; base += 8 * kDThreads) {
-    double v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = pmr[min(base + u * kDThreads + tid, cnt - 1)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) { mx = fmax(mx, v[u]); nan |= v[u] != v[u]; }
-  }
-  mx = block_max(mx, dred);
-  nan = __syncthreads_or(nan);
-  if (bad || nan) {
-    if (c == 0) {
-      if (tid == 0 && tau_out) tau_out[r] = NAN;
-      for (int i = tid; i < DIM; i += kDThreads) out[(size_t)r * DIM + i] = NAN;
-    }
-    return;
-  }
-  const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
-
-  EKV_MARK(1, 1);
-  // 2. this chunk's candidates.  Pass 1 counts the chunk's scores above
-  //    mx - 2^-i (i < 8); C tokens above mx - d give F(mx - d - C^-(alpha-1))
-  //    >= C * (C^-(alpha-1))^(1/(alpha-1)) = 1, so each count certifies a
-  //    lower bound on tau, valid for the whole row.  A lone block also keeps
-  //    its candidates X > mx - 1 in LDS.  Each thread takes 8 consecutive
-  //    tokens of one page (P is a multiple of 8), so one block scan per 2048
-  //    tokens keeps the index order.
-  const int tlo = (int)((long long)c * cnt / nsplit) * P, thi = (int)((long long)(c + 1) * cnt / nsplit) * P;
-  const bool alone = nsplit == 1;
-  double th[kNThr];
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) th[i] = mx - ldexp(1.0, -i);
-  int cnt8[kNThr];
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) cnt8[i] = 0;
-  int nlds = 0;
-  // thread tid takes tokens base + 8 tid .. + 7 of each 2048-token step; the
-  // first kKeepIt steps stay in registers for pass 2 (a chunk of up to 6144
-  // tokens -- every chunk until a row keeps more than kSplitMax of them -- is
-  // read once)
-  double keep[kKeepIt][8];
-  uint32_t keep_ph[kKeepIt];
-  auto load8 = [&](int base, double (&v)[8], uint32_t &ph) __attribute__((always_inline)) {
-    const int tc = min(base + 8 * tid, thi - 8);
-    const double2 *src = reinterpret_cast<const double2 *>(xrow + tc);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) { const double2 d2 = src[h]; v[2 * h] = d2.x; v[2 * h + 1] = d2.y; }
-    ph = ipr[tc / P];
-  };
-  auto count8 = [&](int base, const double (&v)[8], uint32_t ph) __attribute__((always_inline)) {
-    const int t0 = base + 8 * tid;
-    const bool valid = t0 < thi;  // all 8 tokens or none (thi - t0 is a multiple of 8)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-#pragma unroll
-      for (int i = 0; i < kNThr; ++i) cnt8[i] += (valid && v[u] > th[i]) ? 1 : 0;
-    }
-    if (alone) {
-      int take = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) take += (valid && v[u] > thr) ? 1 : 0;
-      int tot;
-      int at = nlds + block_excl_scan(take, scan_scratch, &tot);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (valid && v[u] > thr) {
-          if (at < kCand) {
-            const int t = t0 + u;
-            cx[at] = v[u];
-            ci[at] = t;
-            cv[at] = (ph * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
-          }
-          ++at;
-        }
-      }
-      nlds += tot;
-    }
-  };
-#pragma unroll
-  for (int it = 0; it < kKeepIt; ++it) {
-    const int base = tlo + it * 8 * kDThreads;
-    if (base < thi) {  // uniform
-      load8(base, keep[it], keep_ph[it]);
-      count8(base, keep[it], keep_ph[it]);
-    }
-  }
-#pragma unroll 1
-  for (int base = tlo + kKeepIt * 8 * kDThreads; base < thi; base += 8 * kDThreads) {
-    double v[8];
-    uint32_t ph;
-    load8(base, v, ph);
-    count8(base, v, ph);
-  }
-  // block totals of the counts, then the tightest certified bound
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) cnt8[i] = wave_sum(cnt8[i]);
-  __syncthreads();
-  if ((tid & (kWave - 1)) == 0)
-    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = cnt8[i];
-  __syncthreads();
-  // lane i (mod kNThr) evaluates threshold i's bound and a wave max combines
-  // them: one reciprocal power per lane instead of kNThr in sequence (a chain
-  // of dependent fp64 operations that dominates this phase otherwise)
-  double Lc;
-  {
-    static_assert((kNThr & (kNThr - 1)) == 0, "kNThr is a power of two");
-    const int i = tid & (kNThr - 1);
-    int ci_ = 0;
-    for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
-    const double cand =
-        ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
-    Lc = fmax(thr, wave_max(cand));
-  }
-  if (!alone && tid < kNThr) {  // the chunk's counts, summed over the row by the last block
-    int ct = 0;
-    for (int w = 0; w < kDThreads / kWave; ++w) ct += s_cnt[w][tid];
-    st_agent(&ws.segn[((size_t)r * kSplitMax + c) * kNThr + tid], ct);
-  }
-  const bool lds_all = alone && nlds <= kCand;  // every candidate X > mx - 1 is in LDS
-  int total = nlds;                              // entries in the workspace segments (tiers 1, 2)
-  double L = Lc;
-  if (!lds_all) {
-    // pass 2: compact X > Lc in place to the chunk's start (and into LDS when
-    // alone); writes trail the reads, so no unread score is overwritten
-    nlds = 0;
-    int ncand = 0;
-    auto compact8 = [&](int base, const double (&v)[8], uint32_t ph) __attribute__((always_inline)) {
-      const int t0 = base + 8 * tid;
-      const bool valid = t0 < thi;
-      int take = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) take += (valid && v[u] > Lc) ? 1 : 0;
-      int tot;
-      int at = ncand + block_excl_scan(take, scan_scratch, &tot);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (valid && v[u] > Lc) {
-          const int t = t0 + u;
-          st_agent(&xrow[tlo + at], v[u]);
-          st_agent(&xir[tlo + at], (uint32_t)t);
-          if (alone && at < kCand) {
-            cx[at] = v[u];
-            ci[at] = t;
-            cv[at] = (ph * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)(t % P);
-          }
-          ++at;
-        }
-      }
-      ncand += tot;
-    };
-#pragma unroll
-    for (int it = 0; it < kKeepIt; ++it) {
-      const int base = tlo + it * 8 * kDThreads;
-      if (base < thi) compact8(base, keep[it], keep_ph[it]);
-    }
-#pragma unroll 1
-    for (int base = tlo + kKeepIt * 8 * kDThreads; base < thi; base += 8 * kDThreads) {
-      double v[8];
-      uint32_t ph;
-      load8(base, v, ph);
-      compact8(base, v, ph);
-    }
-    total = ncand;
-    nlds = alone ? ncand : 0;
-  }
-  EKV_MARK(1, 2);
-  if (!alone) {
-    if (tid == 0) {
-      st_agent(&ws.segcnt[(size_t)r * kSplitMax + c], total);
-      st_agent(&ws.segL[(size_t)r * kSplitMax + c], Lc);
-    }
-    if (!arrive_last(&ws.ctr[r], (unsigned)nsplit, &s_last)) return;
-    EKV_MARK(1, 3);
-    // the row's last block: segment offsets, the row's bound, then the
-    // candidates above it into LDS
-    if (tid < nsplit) {
-      soff[tid + 1] = ld_agent(&ws.segcnt[(size_t)r * kSplitMax + tid]);
-      sL[tid] = ld_agent(&ws.segL[(size_t)r * kSplitMax + tid]);
-      sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
-    }
-    // the row's counts above mx - 2^-i are the chunks' counts summed: a bound
-    // as certified as each chunk's and tighter (about sqrt(chunks) for alpha 1.5)
-    if (tid < kNThr) {
-      int ct = 0;
-      for (int s2 = 0; s2 < nsplit; ++s2) ct += ld_agent(&ws.segn[((size_t)r * kSplitMax + s2) * kNThr + tid]);
-      s_cnt[0][tid] = ct;
-    }
-    const bool ipr_lds = cnt <= kIprLds;  // the merge below looks pages up in LDS
-    if (ipr_lds)
-      for (int k = tid; k < cnt; k += kDThreads) s_ipr[k] = ipr[k];
-    __syncthreads();
-    if (tid == 0) {  // segment offsets (the first step's entry addresses need them)
-      soff[0] = 0;
-      for (int s2 = 0; s2 < nsplit; ++s2) soff[s2 + 1] += soff[s2];
-    }
-    __syncthreads();
-    total = soff[nsplit];
-    const GlobSeg<1> gs0{xrow, soff, sbase, nsplit, total};
-    // each thread takes 8 consecutive entries, so one block scan per 2048
-    // entries keeps the candidates in index order; each step's scores and
-    // token ids are requested one step ahead, so their round trip overlaps the
-    // previous step's scan (the first step's, the row bound below)
-    nlds = 0;
-    auto ld8 = [&](int base, double (&v)[8], uint32_t (&t)[8]) __attribute__((always_inline)) {
-      int a[8];
-      gs0.addr_run<8>(base + 8 * tid, a);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        v[u] = ld_agent(&xrow[a[u]]);
-        t[u] = ld_agent(&xir[a[u]]);
-      }
-    };
-    double vn[8];
-    uint32_t tn[8];
-    if (total > 0) ld8(0, vn, tn);
-    if (tid < kWave) {  // lane i (mod kNThr): threshold i's bound from the summed count
-      const int i = tid & (kNThr - 1);
-      const int ct = s_cnt[0][i];
-      const double cand =
-          ct > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ct, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
-      const double cmax = wave_max(cand);
-      if (tid == 0) {
-        double lm = fmax(thr, cmax);
-        for (int s2 = 0; s2 < nsplit; ++s2) lm = fmax(lm, sL[s2]);
-        s_tau[0] = lm;
-      }
-    }
-    lds_barrier();  // s_tau; the first step's loads stay in flight
-    L = s_tau[0];
-#pragma unroll 1
-    for (int base = 0; base < total; base += 8 * kDThreads) {
-      const int k0 = base + 8 * tid;
-      double v[8];
-      uint32_t t[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) { v[u] = vn[u]; t[u] = tn[u]; }
-      if (base + 8 * kDThreads < total) ld8(base + 8 * kDThreads, vn, tn);
-      uint32_t ph[8];
-      if (ipr_lds) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ph[u] = s_ipr[min(t[u] / P, (uint32_t)(cnt - 1))];
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ph[u] = ipr[t[u] / P];
-      }
-      int mine = 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) mine += (k0 + u < total && v[u] > L) ? 1 : 0;
-      int tot;
-      int at = nlds + block_excl_scan<true>(mine, scan_scratch, &tot);  // the next step's loads stay in flight
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (k0 + u < total && v[u] > L) {
-          if (at < kCand) {
-            cx[at] = v[u];
-            ci[at] = (int)t[u];
-            cv[at] = (ph[u] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t[u] % P;
-          }
-          ++at;
-        }
-      }
-      nlds += tot;
-      if (nlds > kCand) break;  // the LDS set is only used when it holds them all (uniform)
-    }
-  } else if (tid == 0) {
-    soff[0] = 0;
-    soff[1] = total;
-    sbase[0] = 0;
-  }
-  __syncthreads();
-  EKV_MARK(1, 4);
-  // candidate tiers: LDS (one wave solves), registers (block), workspace passes
-  const int tier = nlds <= kCand ? 0 : ((total <= kRegPer * kDThreads && dp.ibeta != 0) ? 1 : 2);
-  const int nsol = tier == 0 ? nlds : total;  // values the solver sees
-  const int nseg = alone ? 1 : nsplit;
-  const GlobSeg<1> gs{xrow, soff, sbase, nseg, total};
-  double rx[kRegPer];
-  uint32_t ri[kRegPer];
-  if (tier == 1) {
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j) {
-      const int a = gs.addr(min(tid * kRegPer + j, total - 1));
-      rx[j] = ld_agent(&xrow[a]);
-      ri[j] = ld_agent(&xir[a]);
-    }
-  }
-
-  EKV_MARK(1, 5);
-  // 3. threshold and normalizer
+template <typename T, int DIM>
+struct Gather {
+  static constexpr int kTpe = GatherLds<T, DIM>::kTpe;
+  static constexpr int kEpp = GatherLds<T, DIM>::kEpp;
+  GatherLds<T, DIM> *sh;
+  int *scan_scratch;
+  const T *v_pool;
+  const DecodeWs *ws;
+  long long rbase;
+  const uint32_t *ipr;  // LDS copy of the row's item -> physical page table (nullptr: read ws->iphys)
+  int P, Hkv, g;
+  float *wrow;          // weights_out row (nullable)
   double tau, z;
-  if (dp.ibeta == 2) solve_row<2>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
-  else if (dp.ibeta == 1) solve_row<1>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
-  else solve_row<0>(tier, dp, mx, L, nsol, cx, sortbuf, rx, gs, dred, &s_kstar, s_tau, tau, z);
-  EKV_MARK(1, 6);
-  if (tid == 0 && tau_out) tau_out[r] = tau / dp.a;
-
-  // 4. support gather, chunk by chunk in index order: compact (token, weight;
-  //    V row when known), then kEpp entries at a time, kTpe threads per
-  //    entry, each thread 8 coordinates with one 16-byte load; fixed-order
-  //    final sum.
-  const int ge = tid / kTpe, gc = tid % kTpe;
+  DecodeParams dp;
+  int nsup;
   float acc8[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) acc8[u] = 0.0f;
-  int nsup = 0;
-  const bool resolve = tier != 0;  // V rows looked up per flush from the item's physical page
-  auto flush = [&]() __attribute__((always_inline)) {
+
+  __device__ __forceinline__ void flush() {
     __syncthreads();
-    if (resolve) {
-      for (int k = tid; k < nsup; k += kDThreads) {
-        const uint32_t t = (uint32_t)sup_i[k];
-        sup_v[k] = (ipr[t / P] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + t % P;
-      }
-      __syncthreads();
+    const int tid = threadIdx.x;
+    for (int k = tid; k < nsup; k += kDThreads) {
+      const uint32_t t = sh->tok[k];
+      const uint32_t item = t / (uint32_t)P, slot = t % (uint32_t)P;
+      const uint32_t ph = ipr ? ipr[item] : ws->iphys[(size_t)rbase + item];
+      if (wrow) wrow[(size_t)ws->ipage[(size_t)rbase + item] * P + slot] = sh->w[k];
+      sh->tok[k] = (ph * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + slot;
     }
+    __syncthreads();
+    const int ge = tid / kTpe, gc = tid % kTpe;
     int e = ge;
     // four entries per thread in flight, then two, then one
 #pragma unroll 1
     for (; e + 3 * kEpp < nsup; e += 4 * kEpp) {
       float v0[8], v1[8], v2[8], v3[8];
-      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
-      load_vec<8>(v_pool + (size_t)sup_v[e + kEpp] * DIM + gc * 8, v1);
-      load_vec<8>(v_pool + (size_t)sup_v[e + 2 * kEpp] * DIM + gc * 8, v2);
-      load_vec<8>(v_pool + (size_t)sup_v[e + 3 * kEpp] * DIM + gc * 8, v3);
-      const float w0 = sup_w[e], w1 = sup_w[e + kEpp], w2 = sup_w[e + 2 * kEpp], w3 = sup_w[e + 3 * kEpp];
+      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sh->tok[e + kEpp] * DIM + gc * 8, v1);
+      load_vec<8>(v_pool + (size_t)sh->tok[e + 2 * kEpp] * DIM + gc * 8, v2);
+      load_vec<8>(v_pool + (size_t)sh->tok[e + 3 * kEpp] * DIM + gc * 8, v3);
+      const float w0 = sh->w[e], w1 = sh->w[e + kEpp], w2 = sh->w[e + 2 * kEpp], w3 = sh->w[e + 3 * kEpp];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
 #pragma unroll
@@ -887,9 +1011,9 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     }
     if (e + kEpp < nsup) {
       float v0[8], v1[8];
-      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
-      load_vec<8>(v_pool + (size_t)sup_v[e + kEpp] * DIM + gc * 8, v1);
-      const float w0 = sup_w[e], w1 = sup_w[e + kEpp];
+      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sh->tok[e + kEpp] * DIM + gc * 8, v1);
+      const float w0 = sh->w[e], w1 = sh->w[e + kEpp];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
 #pragma unroll
@@ -898,497 +1022,835 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     }
     if (e < nsup) {
       float v0[8];
-      load_vec<8>(v_pool + (size_t)sup_v[e] * DIM + gc * 8, v0);
-      const float w0 = sup_w[e];
+      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
+      const float w0 = sh->w[e];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
     }
-    if (weights_out) {
-      for (int k = tid; k < nsup; k += kDThreads) {
-        const int pg = sel_idx[(size_t)r * MP + sup_i[k] / P];
-        weights_out[(size_t)r * wrow + (size_t)pg * P + sup_i[k] % P] = sup_w[k];
+    __syncthreads();
+    nsup = 0;
+  }
+  // up to R entries of this thread (x, token id), consecutive in index order
+  // (R * 256 <= kSupCap); one block scan places the block's support entries
+  template <int R>
+  __device__ __forceinline__ void offer(const double (&x)[R], const uint32_t (&tk)[R]) {
+    static_assert(R * kDThreads <= kSupCap, "one offer fits the chunk");
+    int take = 0;
+#pragma unroll
+    for (int u = 0; u < R; ++u) take += x[u] - tau > 0.0 ? 1 : 0;
+    int tot;
+    int at = block_excl_scan<true>(take, scan_scratch, &tot);  // loads issued before stay in flight
+    if (nsup + tot > kSupCap) {  // uniform
+      flush();
+    }
+    at += nsup;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const double y = x[u] - tau;
+      if (y > 0.0) {
+        sh->tok[at] = tk[u];
+        sh->w[at] = (float)(pw_rt(y, dp) / z);
+        ++at;
+      }
+    }
+    nsup += tot;
+  }
+  // the block's sum of p_t v_t into dst[0 .. DIM) (fixed order)
+  __device__ __forceinline__ void finish(float *dst, bool agent) {
+    flush();
+    const int tid = threadIdx.x, ge = tid / kTpe, gc = tid % kTpe;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sh->accs[ge][gc * 8 + u] = acc8[u];
+    __syncthreads();
+    for (int cc = tid; cc < DIM; cc += kDThreads) {
+      float s = sh->accs[0][cc];
+      for (int e = 1; e < kEpp; ++e) s += sh->accs[e][cc];
+      if (agent) st_agent(&dst[cc], s);
+      else dst[cc] = s;
+    }
+  }
+};
+
+// Waits until the row's step is at least `need` (kStDone counts); returns the
+// step seen, or 0 after the time limit.
+__device__ unsigned wait_step(const unsigned *state, unsigned need, unsigned *s_flag) {
+  if (threadIdx.x == 0) {
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned v;
+    for (;;) {
+      v = ld_agent(state);
+      if (v >= need) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+        v = 0u;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *s_flag = v;
+  }
+  __syncthreads();
+  return *s_flag;
+}
+
+__device__ __forceinline__ void publish_step(unsigned *state, unsigned v) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) st_agent(state, v);
+}
+
+template <int DIM>
+__device__ void row_nan(const RowsArgs &ra, int r) {
+  for (int i = threadIdx.x; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = NAN;
+  if (threadIdx.x == 0 && ra.tau) ra.tau[r] = NAN;
+}
+
+// LDS of the rows kernel (one layout per role, overlaid)
+template <typename T, int DIM>
+struct RowsLds {
+  int off[kMaxSlices + 1];
+  uint32_t start[kMaxSlices];
+  int dense[kMaxSlices];
+  union {
+    struct {
+      double cx[kCand];
+      uint32_t ci[kCand];
+      uint32_t ipr[kIprLds];
+      union {
+        GatherLds<T, DIM> ga;
+        double sortbuf[kCand];
+      };
+    } lead;
+    unsigned hist[kBins];
+    double win[kWin];
+    GatherLds<T, DIM> ga;
+  };
+};
+
+template <typename T, int DIM>
+__device__ __forceinline__ Gather<T, DIM> make_gather(GatherLds<T, DIM> *sh, int *scan_scratch, const Dims &D,
+                                                      const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws,
+                                                      int r, long long rbase, const uint32_t *ipr, double tau,
+                                                      double z) {
+  Gather<T, DIM> ga;
+  ga.sh = sh;
+  ga.scan_scratch = scan_scratch;
+  ga.v_pool = (const T *)ra.v_pool;
+  ga.ws = &ws;
+  ga.rbase = rbase;
+  ga.ipr = ipr;
+  ga.P = D.P;
+  ga.Hkv = D.Hkv;
+  ga.g = (r % D.Hq) / D.G;
+  ga.wrow = ra.weights_out ? ra.weights_out + (size_t)r * D.max_pages * D.P : nullptr;
+  ga.tau = tau;
+  ga.z = z;
+  ga.dp = dp;
+  ga.nsup = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ga.acc8[u] = 0.0f;
+  return ga;
+}
+
+// Support gather over the entries of sg (eight per thread per step, the next
+// eight in flight); the block's partial output goes to dst.
+template <typename T, int DIM>
+__device__ __forceinline__ void gather_entries(Gather<T, DIM> &ga, const Segs &sg, const DecodeWs &ws, float *dst,
+                                               bool agent) {
+  Batch8 cur, nxt;
+  load_batch8(sg, ws, 8 * (int)threadIdx.x, true, cur);
+#pragma unroll 1
+  for (int base = 0; base < sg.total; base += 8 * kDThreads) {
+    if (base + 8 * kDThreads < sg.total) load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, nxt);
+    ga.template offer<8>(cur.v, cur.t);
+    cur = nxt;
+  }
+  ga.finish(dst, agent);
+}
+
+// Every entry of row r in the workspace: tau by passes over them (generic
+// exponent, or a window too wide for the slots) and, when `gather`, the
+// support gather with the output written here.
+template <typename T, int DIM>
+__device__ void row_slow(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                         RowsLds<T, DIM> &sm, const Segs &sg, double lo0, double hi, long long rbase, double *dred,
+                         int *scan_scratch, bool gather, double *tau_o, double *z_o) {
+  const GlobVals src{&ws, &sg};
+  const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
+  double tau, z;
+  solve_block(src, none, lo0, hi, dp, dred, tau, z);
+  *tau_o = tau;
+  *z_o = z;
+  if (!gather) return;
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, tau, z);
+  gather_entries<T, DIM>(ga, sg, ws, ra.out + (size_t)r * DIM, false);
+}
+
+// ---------------------------------------------------------------- leader
+// Values in a global array, strided over the block (fixed order), 8 in flight
+struct ArrVals {
+  const double *v;
+  int n;
+  template <typename Fn>
+  __device__ __forceinline__ void each(Fn &&fn) const {
+#pragma unroll 1
+    for (int base = 0; base < n; base += 8 * kDThreads) {
+      double x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kDThreads + (int)threadIdx.x;
+        x[u] = i < n ? ld_agent(&v[i]) : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) fn(x[u]);
+    }
+  }
+};
+
+// Opens the helper steps of a large row: histogram range [lo, mx] and a
+// cleared histogram, then the step flag.
+template <typename T, int DIM>
+__device__ void open_large(const DecodeWs &ws, int r, double mx, double mn) {
+  const double thr = mx - 1.0;
+  double lo = fmax(thr, mn);
+  double w = (mx - lo) / (double)kBins;
+  if (!(w > 0.0) || !(w < INFINITY)) {
+    lo = thr;
+    w = 1.0 / (double)kBins;
+  }
+  for (int i = threadIdx.x; i < kBins; i += kDThreads) st_agent(&ws.hist[(size_t)r * kBins + i], 0u);
+  if (threadIdx.x == 0) {
+    st_agent(&ws.rpar[(size_t)r * 8 + 0], mx);
+    st_agent(&ws.rpar[(size_t)r * 8 + 1], lo);
+    st_agent(&ws.rpar[(size_t)r * 8 + 2], w);
+  }
+  publish_step(&ws.state[r], kStHist);
+}
+
+// A row with at most kLeadMax entries: two passes over the entries (batches
+// of 2048, the next in flight; one batch stays in registers): the counts
+// above mx - 2^-i give the certified bound Lb, then the candidates X > Lb in
+// index order go to LDS (up to kCand) and to the row's window buffer (up to
+// kWbuf).  A row with more candidates goes to the helpers.  Every decision
+// and every sum depends on the entries alone, not on timing.
+template <typename T, int DIM>
+__device__ void row_leader(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                           RowsLds<T, DIM> &sm) {
+  __shared__ double dred[3 * kDThreads / kWave];
+  __shared__ int scan_scratch[kDThreads / kWave];
+  __shared__ unsigned long long scan64[kDThreads / kWave];
+  __shared__ int s_cnt[kDThreads / kWave][kNThr];
+  __shared__ double s_tau[2];
+  __shared__ int s_kstar;
+  const int tid = threadIdx.x;
+  const int ns = ra.ns;
+  EKV_MARK(1, 0);
+  // 1. slice summaries: entry total, row maximum and minimum, malformed marks
+  const long long rbase = ws.rbase[r];
+  const int rcnt = ws.rcnt[r];
+  double mm[2];
+  int nan, nseg;
+  const int N = load_segs(ws, r, ns, 0, ns, sm.off, sm.start, sm.dense, scan64, &nseg, mm, &nan);
+  const double mx = block_max(mm[0], dred);
+  const double mn = block_min_d(mm[1], dred);
+  nan = __syncthreads_or(nan);
+  const Segs sg{sm.off, sm.start, sm.dense, nseg, N, (unsigned long long)rbase * (unsigned long long)D.P};
+  if (nan) {
+    row_nan<DIM>(ra, r);
+    publish_step(&ws.state[r], kStDone);
+    return;
+  }
+  if (N == 0) {
+    for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
+    if (tid == 0 && ra.tau) ra.tau[r] = NAN;
+    publish_step(&ws.state[r], kStDone);
+    return;
+  }
+  const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
+  if (N > kLeadMax) {
+    if (dp.ibeta == 0) {  // generic exponent: passes over the workspace by this block
+      publish_step(&ws.state[r], kStDone);  // no helper steps for this row
+      double tau, z;
+      row_slow<T, DIM>(D, dp, ra, ws, r, sm, sg, thr, mx, rbase, dred, scan_scratch, true, &tau, &z);
+      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+      return;
+    }
+    open_large<T, DIM>(ws, r, mx, mn);
+    return;
+  }
+  EKV_MARK(1, 1);
+  // 2. pass 1: counts above mx - 2^-i (lane i mod kNThr evaluates threshold i
+  //    later); the row's item -> physical page table into LDS meanwhile
+  const int nb = (N + 8 * kDThreads - 1) / (8 * kDThreads);
+  const bool ipr_lds = rcnt <= kIprLds;
+  Batch8 cur, nxt;
+  load_batch8(sg, ws, 8 * tid, true, cur);
+  {
+    uint32_t ip[kIprLds / kDThreads];
+#pragma unroll
+    for (int u = 0; u < kIprLds / kDThreads; ++u) {
+      const int i = u * kDThreads + tid;
+      ip[u] = (ipr_lds && i < rcnt) ? ws.iphys[(size_t)rbase + i] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kIprLds / kDThreads; ++u) {
+      const int i = u * kDThreads + tid;
+      if (ipr_lds && i < rcnt) sm.lead.ipr[i] = ip[u];
+    }
+  }
+  int c8[kNThr];
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) c8[i] = 0;
+  auto count8 = [&](const Batch8 &bt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (bt.v[u] > thr)
+#pragma unroll
+        for (int i = 0; i < kNThr; ++i) c8[i] += bt.v[u] > mx - ldexp(1.0, -i) ? 1 : 0;
+  };
+  if (nb > 1) load_batch8(sg, ws, 8 * kDThreads + 8 * tid, false, nxt);
+  count8(cur);
+#pragma unroll 1
+  for (int bi = 1; bi < nb; ++bi) {
+    Batch8 nn;
+    if (bi + 1 < nb) load_batch8(sg, ws, (bi + 1) * 8 * kDThreads + 8 * tid, false, nn);
+    count8(nxt);
+    nxt = nn;
+  }
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) c8[i] = wave_sum(c8[i]);
+  if ((tid & (kWave - 1)) == 0)
+    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = c8[i];
+  __syncthreads();
+  // certified bound: C entries above mx - d give F(mx - d - C^-(alpha-1)) >= 1
+  double Lb;
+  {
+    const int i = tid & (kNThr - 1);
+    int ci_ = 0;
+    for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
+    const double cand =
+        ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+    const double wm = wave_max(cand);
+    if (tid == 0) s_tau[0] = fmax(thr, wm);
+    __syncthreads();
+    Lb = s_tau[0];
+  }
+  // 3. pass 2: candidates X > Lb in index order into LDS and the window buffer
+  double *wrow = ws.wbuf + (size_t)r * kHelpers * kSlot;
+  uint32_t *wtok = ws.wtok + (size_t)r * kHelpers * kSlot;
+  int nC = 0;
+  auto compact8 = [&](const Batch8 &bt) __attribute__((always_inline)) {
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mine += bt.v[u] > Lb ? 1 : 0;
+    int tot;
+    int at = nC + block_excl_scan<true>(mine, scan_scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (bt.v[u] > Lb) {
+        if (at < kCand) {
+          sm.lead.cx[at] = bt.v[u];
+          sm.lead.ci[at] = bt.t[u];
+        }
+        if (at < kWbuf) {  // coherent stores: helpers may rewrite these bytes in this launch
+          st_agent(&wrow[at], bt.v[u]);
+          st_agent(&wtok[at], bt.t[u]);
+        }
+        ++at;
+      }
+    nC += tot;
+  };
+  if (nb == 1) {
+    compact8(cur);
+  } else {
+    load_batch8(sg, ws, 8 * tid, true, cur);
+#pragma unroll 1
+    for (int bi = 0; bi < nb; ++bi) {
+      if (bi + 1 < nb) load_batch8(sg, ws, (bi + 1) * 8 * kDThreads + 8 * tid, true, nxt);
+      compact8(cur);
+      cur = nxt;
+    }
+  }
+  __syncthreads();
+  EKV_MARK(1, 2);
+  if (nC > kWbuf) {  // more candidates than the leader holds
+    if (dp.ibeta == 0) {  // generic exponent: passes over the workspace by this block
+      publish_step(&ws.state[r], kStDone);
+      double tau, z;
+      row_slow<T, DIM>(D, dp, ra, ws, r, sm, sg, Lb, mx, rbase, dred, scan_scratch, true, &tau, &z);
+      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+      return;
+    }
+    open_large<T, DIM>(ws, r, mx, mn);  // the helpers take the row
+    return;
+  }
+  publish_step(&ws.state[r], kStDone);  // the helpers are not needed
+  // 4. tau and z: one wave over the LDS candidates, the sort form, or the
+  //    block over the window buffer
+  double tau, z;
+  const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
+  const double hi = mx - pow((double)max(nC, 1), -dp.a);  // F(hi) <= 1: at most nC entries above it
+  const bool lds = nC <= kCand;
+  if (lds && dp.ibeta == 1 && dp.tau_method == 1) {
+    tau = sparsemax_tau_sort(sm.lead.cx, nC, sm.lead.sortbuf, dred, &s_kstar);
+    double zz = 0.0;
+    for (int i = tid; i < nC; i += kDThreads) {
+      const double y = sm.lead.cx[i] - tau;
+      if (y > 0.0) zz += y;
+    }
+    z = block_sum(zz, dred);
+  } else if (lds) {
+    if (tid < kWave) {
+      double t, zk = 0.0;
+      const LdsVals src{sm.lead.cx, nC, tid, kWave};
+      if (dp.ibeta == 2) t = newton_tau<2, LdsVals, WaveRed>(src, none, Lb, hi, dp, dred, &zk);
+      else if (dp.ibeta == 1) t = newton_tau<1, LdsVals, WaveRed>(src, none, Lb, hi, dp, dred, &zk);
+      else t = newton_tau<0, LdsVals, WaveRed>(src, none, Lb, hi, dp, dred, &zk);
+      if (zk == 0.0) {  // F at t from the candidates
+        double zz = 0.0;
+        src.each([&](double x) { const double y = x - t; if (y > 0.0) zz += pw_rt(y, dp); });
+        zk = wave_sum(zz);
+      }
+      if (tid == 0) {
+        s_tau[0] = t;
+        s_tau[1] = zk;
       }
     }
     __syncthreads();
-    nsup = 0;
-  };
-  // one compaction step over 256 entries (x, token, V row) in index order
-  auto step = [&](double xk, int ik, uint32_t vk) __attribute__((always_inline)) {
-    const double y = xk - tau;
-    const int take = y > 0.0 ? 1 : 0;
-    int tot;
-    const int pos = block_excl_scan(take, scan_scratch, &tot);
-    if (nsup + tot > kSupChunk) flush();
-    if (take) {
-      sup_v[nsup + pos] = vk;
-      sup_i[nsup + pos] = ik;
-      sup_w[nsup + pos] = (float)(pw_rt(y, dp) / z);
-    }
-    nsup += tot;
-  };
-  if (tier == 0) {
-#pragma unroll 1
-    for (int k0 = 0; k0 < nsol; k0 += kDThreads) {
-      const int k = k0 + tid;
-      step(k < nsol ? cx[k] : -INFINITY, k < nsol ? ci[k] : 0, k < nsol ? cv[k] : 0u);
-    }
-  } else if (tier == 1) {
-    // each thread's support entries are consecutive in index order: one scan
-    // places them all when they fit one gather pass
-    int mine = 0;
-#pragma unroll
-    for (int j = 0; j < kRegPer; ++j) mine += (tid * kRegPer + j < total && rx[j] - tau > 0.0) ? 1 : 0;
-    int stot;
-    int at = block_excl_scan(mine, scan_scratch, &stot);
-    if (stot <= kSupChunk) {
-#pragma unroll
-      for (int j = 0; j < kRegPer; ++j) {
-        const double y = rx[j] - tau;
-        if (tid * kRegPer + j < total && y > 0.0) {
-          sup_i[at] = (int)ri[j];
-          sup_w[at] = (float)(pw_rt(y, dp) / z);
-          ++at;
-        }
-      }
-      nsup = stot;
-    } else {
-      // registers rotate down one slot per step, so every access has a fixed index
-#pragma unroll 1
-      for (int j = 0; j < kRegPer; ++j) {
-        step(tid * kRegPer + j < total ? rx[0] : -INFINITY, (int)ri[0], 0u);
-#pragma unroll
-        for (int u = 0; u + 1 < kRegPer; ++u) { rx[u] = rx[u + 1]; ri[u] = ri[u + 1]; }
-      }
-    }
+    tau = s_tau[0];
+    z = s_tau[1];
   } else {
+    solve_block(ArrVals{wrow, nC}, none, Lb, hi, dp, dred, tau, z);
+  }
+  EKV_MARK(1, 3);
+  if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+  // 5. support gather over the candidates in index order
+  Gather<T, DIM> ga =
+      make_gather<T, DIM>(&sm.lead.ga, scan_scratch, D, dp, ra, ws, r, rbase, ipr_lds ? sm.lead.ipr : nullptr, tau, z);
 #pragma unroll 1
-    for (int k0 = 0; k0 < total; k0 += kDThreads) {
-      const int k = k0 + tid;
-      const int a = gs.addr(min(k, total - 1));
-      const double xv = ld_agent(&xrow[a]);
-      const uint32_t t = ld_agent(&xir[a]);
-      step(k < total ? xv : -INFINITY, (int)t, 0u);
-    }
-  }
-  flush();
-  EKV_MARK(1, 7);
+  for (int k0 = 0; k0 < nC; k0 += 4 * kDThreads) {
+    double x4[4];
+    uint32_t t4[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) accs[ge][gc * 8 + u] = acc8[u];
-  __syncthreads();
-  for (int cc = tid; cc < DIM; cc += kDThreads) {
-    float s = accs[0][cc];
-    for (int e = 1; e < kEpp; ++e) s += accs[e][cc];
-    out[(size_t)r * DIM + cc] = s;
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 4 * tid + u;
+      x4[u] = k < nC ? (lds ? sm.lead.cx[k] : ld_agent(&wrow[k])) : -INFINITY;
+      t4[u] = k < nC ? (lds ? sm.lead.ci[k] : ld_agent(&wtok[k])) : 0u;
+    }
+    ga.template offer<4>(x4, t4);
   }
+  ga.finish(ra.out + (size_t)r * DIM, false);
+  EKV_MARK(1, 4);
 }
 
-static DecodeWs carve_decode(const Dims &D, void *base, size_t *bytes) {
+// ---------------------------------------------------------------- helpers
+// Helper j of row r takes slices [j ns / nh, (j + 1) ns / nh).
+template <typename T, int DIM>
+__device__ void row_helper(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int step,
+                           int r, int j, RowsLds<T, DIM> &sm) {
+  __shared__ double dred[3 * kDThreads / kWave];
+  __shared__ int scan_scratch[kDThreads / kWave];
+  __shared__ unsigned s_flag;
+  __shared__ int s_last;
+  __shared__ unsigned long long red64[kDThreads / kWave];
+  __shared__ double s_par[8];
+  __shared__ double s_hp[kHelpers][5];
+  __shared__ int s_woff[kHelpers + 1];
+  __shared__ int s_ovf;
+  __shared__ double s_amin;
+  const int tid = threadIdx.x;
+  const int ns = ra.ns, nh = ra.nh;
+  const unsigned need = step == 0 ? kStHist : (step == 1 ? kStMom : kStGath);
+  const unsigned st = wait_step(&ws.state[r], need, &s_flag);
+  if (st == kStDone) return;
+  if (st == 0u) {  // time limit: the row is marked failed
+    row_nan<DIM>(ra, r);
+    return;
+  }
+  EKV_MARK(2, 0);
+  if (tid < 8) s_par[tid] = ld_agent(&ws.rpar[(size_t)r * 8 + tid]);
+  const long long rbase = ws.rbase[r];
+  const int s0 = (int)((long long)j * ns / nh), s1 = (int)((long long)(j + 1) * ns / nh);
+  int nseg;
+  const int M = load_segs(ws, r, ns, s0, s1, sm.off, sm.start, sm.dense, red64, &nseg);
+  const Segs sg{sm.off, sm.start, sm.dense, nseg, M, (unsigned long long)rbase * (unsigned long long)D.P};
+  const double mx = s_par[0];
+  if (step == 0) {
+    // ---- histogram of the entries above mx - 1 over [lo, mx] in kBins bins
+    const double lo = s_par[1], w = s_par[2], thr = mx - 1.0;
+    for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    Batch8 cur, nxt;
+    load_batch8(sg, ws, 8 * tid, false, cur);
+#pragma unroll 1
+    for (int base = 0; base < M; base += 8 * kDThreads) {
+      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (cur.v[u] > thr) {
+          const double f = floor((cur.v[u] - lo) / w);
+          const int bin = !(f >= 0.0) ? 0 : (f >= (double)kBins ? kBins - 1 : (int)f);
+          atomicAdd(&sm.hist[bin], 1u);
+        }
+      cur = nxt;
+    }
+    __syncthreads();
+    for (int i = tid; i < kBins; i += kDThreads)
+      if (sm.hist[i]) atomicAdd(&ws.hist[(size_t)r * kBins + i], sm.hist[i]);
+    if (!arrive_last(&ws.ctr[3 * r], (unsigned)nh, &s_last)) return;
+    // ---- the row's last helper: certified window.  Bin b's entries lie in
+    // [e_{b-1}, e_{b+2}] (one bin of slack for the rounding of the binning), so
+    //   LB(k) = sum_{b >= k+2} n_b ((b-1-k) w)^beta <= F(e_k)
+    //   UB(k) = sum_{b >= k-1} n_b ((b+2-k) w)^beta >= F(e_k),
+    // written with suffix sums of n_b, n_b b, n_b b^2 in integers.  tau lies in
+    // [e_klo, e_khi]: klo the largest edge with LB >= 1, khi the smallest with
+    // UB <= 1 (1 -/+ 1e-9 for the final rounding).
+    for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = ld_agent(&ws.hist[(size_t)r * kBins + i]);
+    __syncthreads();
+    constexpr int kPer = kBins / kDThreads;
+    long long l0 = 0, l1 = 0, l2 = 0;
+    for (int u = 0; u < kPer; ++u) {
+      const long long bb = (long long)tid * kPer + u, n = sm.hist[bb];
+      l0 += n;
+      l1 += n * bb;
+      l2 += n * bb * bb;
+    }
+    // suffix sums from this thread's first bin: totals minus the exclusive prefix
+    unsigned long long t0_, t1_, t2_;
+    const long long q0 = (long long)block_excl_scan64((unsigned long long)l0, red64, &t0_);
+    const long long q1 = (long long)block_excl_scan64((unsigned long long)l1, red64, &t1_);
+    const long long q2 = (long long)block_excl_scan64((unsigned long long)l2, red64, &t2_);
+    long long S0 = (long long)t0_ - q0, S1 = (long long)t1_ - q1, S2 = (long long)t2_ - q2;
+    const double wb = dp.ibeta == 2 ? w * w : w;
+    int klo = -1, khi = 0x7fffffff;
+    auto nb = [&](long long bb) -> long long { return (bb >= 0 && bb < kBins) ? (long long)sm.hist[bb] : 0ll; };
+    const int kend = tid == kDThreads - 1 ? kPer + 1 : kPer;  // the last thread also takes edge kBins
+    for (int u = 0; u < kend; ++u) {
+      const long long k = (long long)tid * kPer + u;
+      const long long a0 = nb(k), a1 = nb(k + 1);
+      // suffix at k + 2 and at max(k - 1, 0)
+      const long long T0 = S0 - a0 - a1, T1 = S1 - a0 * k - a1 * (k + 1);
+      const long long T2 = S2 - a0 * k * k - a1 * (k + 1) * (k + 1);
+      const long long m = k > 0 ? k - 1 : 0, am = k > 0 ? nb(k - 1) : 0;
+      const long long U0 = S0 + am, U1 = S1 + am * m, U2 = S2 + am * m * m;
+      double lb, ub;
+      if (dp.ibeta == 2) {
+        lb = (double)(T2 - 2 * (k + 1) * T1 + (k + 1) * (k + 1) * T0) * wb;
+        ub = (double)(U2 + 2 * (2 - k) * U1 + (2 - k) * (2 - k) * U0) * wb;
+      } else {
+        lb = (double)(T1 - (k + 1) * T0) * wb;
+        ub = (double)(U1 + (2 - k) * U0) * wb;
+      }
+      if (lb >= 1.0 + 1e-9) klo = max(klo, (int)k);
+      if (ub <= 1.0 - 1e-9) khi = min(khi, (int)k);
+      S0 -= a0;
+      S1 -= a0 * k;
+      S2 -= a0 * k * k;
+    }
+    klo = (int)block_max((double)klo, dred);
+    khi = (int)block_min_d((double)khi, dred);
+    if (tid == 0) {
+      const double e_lo = klo >= 0 ? lo + (double)klo * w : thr;
+      const double e_hi = khi <= kBins ? lo + (double)khi * w : mx;
+      st_agent(&ws.rpar[(size_t)r * 8 + 3], e_lo);
+      st_agent(&ws.rpar[(size_t)r * 8 + 4], fmax(e_hi, e_lo));
+    }
+    EKV_MARK(2, 1);
+    publish_step(&ws.state[r], kStMom);
+    return;
+  }
+  if (step == 1) {
+    // ---- moments above e_hi, window entries (e_lo, e_hi] into this helper's slot
+    const double e_lo = s_par[3], e_hi = s_par[4];
+    double m1 = 0.0, m2 = 0.0, ymin = INFINITY;
+    int m0 = 0, wc = 0;
+    double *slot = ws.wbuf + ((size_t)r * kHelpers + j) * kSlot;
+    Batch8 cur, nxt;
+    load_batch8(sg, ws, 8 * tid, false, cur);
+#pragma unroll 1
+    for (int base = 0; base < M; base += 8 * kDThreads) {
+      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
+      int take = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const double v = cur.v[u];
+        if (v > e_hi) {
+          const double y = v - e_hi;
+          ++m0;
+          m1 += y;
+          m2 += y * y;
+          ymin = fmin(ymin, y);
+        } else if (v > e_lo) {
+          ++take;
+        }
+      }
+      int tot;
+      int at = wc + block_excl_scan<true>(take, scan_scratch, &tot);  // the next batch's loads stay in flight
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (!(cur.v[u] > e_hi) && cur.v[u] > e_lo) {
+          if (at < kSlot) st_agent(&slot[at], cur.v[u]);
+          ++at;
+        }
+      wc += tot;
+      cur = nxt;
+    }
+    double sums[3] = {(double)m0, m1, m2};
+    block_sum_n<3>(sums, dred);
+    ymin = block_min_d(ymin, dred);
+    if (tid == 0) {
+      double *hp = ws.hpart + ((size_t)r * kHelpers + j) * 8;
+      st_agent(&hp[0], sums[0]);
+      st_agent(&hp[1], sums[1]);
+      st_agent(&hp[2], sums[2]);
+      st_agent(&hp[3], ymin);
+      st_agent(&hp[4], (double)wc);
+    }
+    if (!arrive_last(&ws.ctr[3 * r + 1], (unsigned)nh, &s_last)) return;
+    // ---- the row's last helper: tau from the moments and the window entries
+    if (tid < nh)
+      for (int c = 0; c < 5; ++c) s_hp[tid][c] = ld_agent(&ws.hpart[((size_t)r * kHelpers + tid) * 8 + c]);
+    __syncthreads();
+    if (tid == 0) {
+      double a0 = 0.0, a1 = 0.0, a2 = 0.0, amin = INFINITY;
+      int off = 0, ovf = 0;
+      for (int h = 0; h < nh; ++h) {
+        a0 += s_hp[h][0];
+        a1 += s_hp[h][1];
+        a2 += s_hp[h][2];
+        amin = fmin(amin, s_hp[h][3]);
+        s_woff[h] = off;
+        const int c = (int)s_hp[h][4];
+        ovf |= c > kSlot ? 1 : 0;
+        off += c;
+      }
+      s_woff[nh] = off;
+      s_ovf = ovf | (off > kWin ? 1 : 0);
+      s_par[5] = a0;
+      s_par[6] = a1;
+      s_par[7] = a2;
+      s_amin = amin;
+    }
+    __syncthreads();
+    const Above ab{s_par[5], s_par[6], s_par[7], s_amin, e_hi};
+    const int W = s_woff[nh];
+    const bool ovf = s_ovf != 0;
+    __syncthreads();
+    double tau, z;
+    if (!ovf) {
+      for (int h = 0; h < nh; ++h) {
+        const int n = s_woff[h + 1] - s_woff[h];
+        for (int i = tid; i < n; i += kDThreads)
+          sm.win[s_woff[h] + i] = ld_agent(&ws.wbuf[((size_t)r * kHelpers + h) * kSlot + i]);
+      }
+      __syncthreads();
+      solve_block(LdsVals{sm.win, W, tid, kDThreads}, ab, e_lo, e_hi, dp, dred, tau, z);
+    } else {
+      // window too wide for the slots: passes over every entry of the row
+      const int N = load_segs(ws, r, ns, 0, ns, sm.off, sm.start, sm.dense, red64, &nseg);
+      const Segs whole{sm.off, sm.start, sm.dense, nseg, N, (unsigned long long)rbase * (unsigned long long)D.P};
+      row_slow<T, DIM>(D, dp, ra, ws, r, sm, whole, e_lo, e_hi, rbase, dred, scan_scratch, false, &tau, &z);
+    }
+    if (tid == 0) {
+      st_agent(&ws.rpar[(size_t)r * 8 + 5], tau);
+      st_agent(&ws.rpar[(size_t)r * 8 + 6], z);
+      if (ra.tau) ra.tau[r] = tau / dp.a;
+    }
+    EKV_MARK(2, 2);
+    publish_step(&ws.state[r], kStGath);
+    return;
+  }
+  // ---- step 2: the support gather of this helper's entries; the last helper
+  // sums the partial outputs in helper order
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, s_par[5], s_par[6]);
+  gather_entries<T, DIM>(ga, sg, ws, ws.opart + ((size_t)r * kHelpers + j) * DIM, true);
+  if (!arrive_last(&ws.ctr[3 * r + 2], (unsigned)nh, &s_last)) return;
+  for (int c = tid; c < DIM; c += kDThreads) {
+    float s = ld_agent(&ws.opart[((size_t)r * kHelpers) * DIM + c]);
+    for (int h = 1; h < nh; ++h) s += ld_agent(&ws.opart[((size_t)r * kHelpers + h) * DIM + c]);
+    ra.out[(size_t)r * DIM + c] = s;
+  }
+  EKV_MARK(2, 3);
+  publish_step(&ws.state[r], kStDone);
+}
+
+// Block index: [0, rows) leaders; then the helpers of step 0, 1, 2, each
+// rows x nh blocks ordered by (row, helper).
+template <typename T, int DIM>
+__global__ __launch_bounds__(kDThreads) void rows_kernel(Dims D, DecodeParams dp, RowsArgs ra, DecodeWs ws) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  RowsLds<T, DIM> &sm = *reinterpret_cast<RowsLds<T, DIM> *>(smem_raw);
+  const int rows = D.B * D.Hq;
+  const int bid = blockIdx.x;
+  if (bid < rows) {
+    row_leader<T, DIM>(D, dp, ra, ws, bid, sm);
+    return;
+  }
+  const int k = bid - rows;
+  const int per = rows * ra.nh;
+  const int step = k / per, rem = k % per;
+  row_helper<T, DIM>(D, dp, ra, ws, step, rem / ra.nh, rem % ra.nh, sm);
+}
+
+// =================================================================== launchers
+static int decode_slices(const Dims &D) {
+  const long long groups = (long long)D.B * D.Hkv;
+  long long ns = (1024 + groups - 1) / groups;  // about 1024 score blocks (4 per CU)
+  ns = std::max(ns, (long long)((D.max_pages + kMaxR - 1) / kMaxR));
+  ns = std::min(ns, (long long)std::max(1, D.max_pages));
+  ns = std::min(ns, (long long)kMaxSlices);
+  return (int)std::max(1ll, ns);
+}
+
+static DecodeWs carve_decode(const Dims &D, int ns, long long item_cap, void *base, size_t *bytes) {
   Carve cv(base);
-  const size_t rows = (size_t)D.B * D.Hq;
+  const size_t rows = (size_t)D.B * D.Hq, cap_tok = (size_t)item_cap * D.P;
   DecodeWs w;
-  w.xs = cv.take<double>(rows * D.max_pages * D.P);
-  w.xi = cv.take<uint32_t>(rows * D.max_pages * D.P);
-  w.pmax = cv.take<double>(rows * D.max_pages);
-  w.iphys = cv.take<uint32_t>(rows * D.max_pages);
-  w.segcnt = cv.take<int>(rows * kSplitMax);
-  w.segL = cv.take<double>(rows * kSplitMax);
-  w.segn = cv.take<int>(rows * kSplitMax * kNThr);
-  w.ctr = cv.take<unsigned int>(rows);
+  w.cx = cv.take<double>(cap_tok);
+  w.ct = cv.take<uint32_t>(cap_tok);
+  w.iphys = cv.take<uint32_t>((size_t)item_cap);
+  w.ipage = cv.take<uint32_t>((size_t)item_cap);
+  w.s_cnt = cv.take<int>(rows * ns);
+  w.s_max = cv.take<double>(rows * ns);
+  w.s_min = cv.take<double>(rows * ns);
+  w.s_start = cv.take<uint32_t>(rows * ns);
+  w.s_dense = cv.take<int>(rows * ns);
+  w.rbase = cv.take<long long>(rows);
+  w.rcnt = cv.take<int>(rows);
+  w.state = cv.take<unsigned>(rows);
+  w.ctr = cv.take<unsigned>(rows * 3);
+  w.rpar = cv.take<double>(rows * 8);
+  w.hist = cv.take<unsigned>(rows * kBins);
+  w.hpart = cv.take<double>(rows * kHelpers * 8);
+  w.wbuf = cv.take<double>(rows * kHelpers * kSlot);
+  w.wtok = cv.take<uint32_t>(rows * kHelpers * kSlot);
+  w.opart = cv.take<float>(rows * kHelpers * D.d);
   if (bytes) *bytes = cv.bytes();
   return w;
 }
 
-size_t decode_ws_bytes(const Dims &D, bool) {
-  size_t b = 0;
-  carve_decode(D, nullptr, &b);
-  return b;
+// item capacity limit: every row's full set, and tokens addressable in 32 bits
+static long long cap_limit(const Dims &D) {
+  const long long dense = (long long)D.B * D.Hq * D.max_pages;
+  return std::min(dense, (long long)(0xFFFFFFFFll / D.P));
 }
 
-template <typename T, int DIM, int P>
-static hipError_t launch_finish_t(const Dims &D, const DecodeParams &dp, const void *v_pool, const int32_t *seq_lens,
-                                  const int32_t *sel_idx, const int32_t *sel_cnt, float *out, double *tau,
-                                  float *weights_out, const DecodeWs &w, hipStream_t s) {
-  const int rows = D.B * D.Hq;
-  const size_t cand_bytes = (size_t)kCand * (8 + 4 + 4) + (dp.tau_method == 1 ? (size_t)kCand * 8 : 0);
+size_t decode_ws_bytes_items(const Dims &D, long long items) {
+  size_t b = 0;
+  carve_decode(D, decode_slices(D), std::min(std::max(items, 1ll), cap_limit(D)), nullptr, &b);
+  return b;
+}
+size_t decode_ws_bytes(const Dims &D, bool) { return decode_ws_bytes_items(D, cap_limit(D)); }
+size_t full_ws_bytes(const Dims &D) { return decode_ws_bytes(D, true); }
+size_t decode_group_ws_bytes(const Dims &D) { return decode_ws_bytes(D, false); }
+size_t decode_ws_min_bytes(const Dims &D) { return decode_ws_bytes_items(D, 1); }
+
+// items a workspace of ws_bytes holds
+static long long item_cap_of(const Dims &D, int ns, size_t ws_bytes) {
+  size_t fixed = 0;
+  carve_decode(D, ns, 0, nullptr, &fixed);
+  if (ws_bytes <= fixed) return 0;
+  // an upper estimate (the four item regions without their alignment), then
+  // down to the largest capacity that fits: a few steps at most
+  long long cap = (long long)((ws_bytes - fixed) / ((size_t)D.P * 12 + 8));
+  cap = std::min(cap, cap_limit(D));
+  size_t b = 0;
+  carve_decode(D, ns, cap, nullptr, &b);
+  while (cap > 0 && b > ws_bytes) {
+    --cap;
+    carve_decode(D, ns, cap, nullptr, &b);
+  }
+  return cap;
+}
+
+template <typename T, int DIM, int P, int G>
+static hipError_t launch_dec_t(const Dims &D, const DecodeParams &dp, const KsArgs &ka, const void *v_pool, float *out,
+                               double *tau, const DecodeWs &w, hipStream_t s) {
+  const int groups = D.B * D.Hkv, rows = D.B * D.Hq;
+  hipLaunchKernelGGL((scores_kernel<T, DIM, P, G>), dim3(groups * ka.ns), dim3(kDThreads), 0, s, D, dp, ka, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   static bool attr_set = false;
+  const size_t lds = sizeof(RowsLds<T, DIM>);
   if (!attr_set) {
-    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)((size_t)kCand * (8 + 4 + 4 + 8)));
+    (void)hipFuncSetAttribute((const void *)rows_kernel<T, DIM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  const long long chunks = ((long long)D.max_pages * D.P + kChunkTok - 1) / kChunkTok;
-  const int split = (int)(chunks < kSplitMax ? chunks : kSplitMax);
-  hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P>), dim3(rows, split), dim3(kDThreads), cand_bytes, s, D, dp,
-                     (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
+  // helpers per row and step: about 1024 blocks per step in all
+  const int nh = std::max(1, std::min(std::min(kHelpers, ka.ns), (1024 + rows - 1) / rows));
+  RowsArgs ra{v_pool, out, tau, ka.weights_out, ka.ns, nh};
+  const long long grid = (long long)rows * (1 + 3 * ra.nh);
+  hipLaunchKernelGGL((rows_kernel<T, DIM>), dim3((unsigned)grid), dim3(kDThreads), lds, s, D, dp, ra, w);
   return hipGetLastError();
 }
 
 template <typename T, int DIM, int P>
-static hipError_t launch_decode_t(const Dims &D, const DecodeParams &dp, const void *q,
-                                  const void *k_pool, const void *v_pool, const int32_t *page_table,
-                                  const int32_t *seq_lens, const int32_t *sel_idx,
-                                  const int32_t *sel_cnt, float *out, double *tau,
-                                  float *weights_out, void *ws, hipStream_t s) {
-  const DecodeWs w = carve_decode(D, ws, nullptr);
-  const int rows = D.B * D.Hq;
-  const size_t map_bytes = (size_t)(rows + 1) * 4;
-  hipLaunchKernelGGL((decode_scores_kernel<T, DIM, P>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
-                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w, s);
+static hipError_t launch_dec_g(const Dims &D, const DecodeParams &dp, const KsArgs &ka, const void *v, float *out,
+                               double *tau, const DecodeWs &w, hipStream_t s) {
+  switch (D.G) {
+    case 1: return launch_dec_t<T, DIM, P, 1>(D, dp, ka, v, out, tau, w, s);
+    case 2: return launch_dec_t<T, DIM, P, 2>(D, dp, ka, v, out, tau, w, s);
+    case 4: return launch_dec_t<T, DIM, P, 4>(D, dp, ka, v, out, tau, w, s);
+    case 8: return launch_dec_t<T, DIM, P, 8>(D, dp, ka, v, out, tau, w, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int DIM>
-static hipError_t launch_decode_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
-                                  const void *v_pool, const int32_t *pt, const int32_t *sl, const int32_t *si,
-                                  const int32_t *sc, float *out, double *tau, float *wo, void *ws, hipStream_t s) {
-  if (D.P == 16) return launch_decode_t<T, DIM, 16>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
-  if (D.P == 32) return launch_decode_t<T, DIM, 32>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
-  return launch_decode_t<T, DIM, 64>(D, dp, q, k_pool, v_pool, pt, sl, si, sc, out, tau, wo, ws, s);
+static hipError_t launch_dec_p(const Dims &D, const DecodeParams &dp, const KsArgs &ka, const void *v, float *out,
+                               double *tau, const DecodeWs &w, hipStream_t s) {
+  if (D.P == 16) return launch_dec_g<T, DIM, 16>(D, dp, ka, v, out, tau, w, s);
+  if (D.P == 32) return launch_dec_g<T, DIM, 32>(D, dp, ka, v, out, tau, w, s);
+  return launch_dec_g<T, DIM, 64>(D, dp, ka, v, out, tau, w, s);
 }
 
-hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const void *k_pool,
-                                const void *v_pool, const int32_t *page_table,
-                                const int32_t *seq_lens, const int32_t *sel_idx,
-                                const int32_t *sel_cnt, double alpha, int tau_method, float *out,
-                                double *tau, float *weights_out, void *ws, hipStream_t s) {
+// mode: 0 a set per query head, 1 a set per KV head, 2 every page
+static hipError_t launch_decode_mode(const Dims &D, int dtype, int mode, const void *q, const void *k_pool,
+                                     const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                     const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
+                                     float *out, double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                                     hipStream_t s) {
   DecodeParams dp;
   dp.a = alpha - 1.0;
   dp.beta = 1.0 / dp.a;
   dp.c = D.scale;
   dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
   dp.tau_method = tau_method;
+  const int ns = decode_slices(D);
+  if ((D.max_pages + ns - 1) / ns > kMaxR) return hipErrorInvalidValue;
+  const long long cap = item_cap_of(D, ns, ws_bytes);
+  const DecodeWs w = carve_decode(D, ns, cap, ws, nullptr);
+  const KsArgs ka{q, k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, mode, ns, cap};
   if (dtype == ENTMAXKV_BF16) {
-    if (D.d == 64) return launch_decode_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-    return launch_decode_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+    if (D.d == 64) return launch_dec_p<uint16_t, 64>(D, dp, ka, v_pool, out, tau, w, s);
+    return launch_dec_p<uint16_t, 128>(D, dp, ka, v_pool, out, tau, w, s);
   }
-  if (D.d == 64) return launch_decode_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-  return launch_decode_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
+  if (D.d == 64) return launch_dec_p<float, 64>(D, dp, ka, v_pool, out, tau, w, s);
+  return launch_dec_p<float, 128>(D, dp, ka, v_pool, out, tau, w, s);
 }
 
-// ------------------------------------- group-shared selection: one set per KV head
-// Items (group row (b, g), i): the i-th page of the KV head's set.  The page's
-// K slice is read once and scored for the G query heads of the group; each
-// head's row receives the item in kernel 2's layout (exact X per token, page
-// maximum -- NaN for a malformed item --, physical page) and the expanded
-// selection (every head of the group lists the group's pages), so kernel 2 runs
-// unchanged.  Group counts are copied to the heads as given, so a count outside
-// [0, N_b] marks all G rows as malformed in kernel 2.
-template <typename T, int DIM, int P, int G>
-__global__ __launch_bounds__(kDThreads) void group_scores_kernel(
-    Dims D, DecodeParams dp, const T *__restrict__ q, const T *__restrict__ k_pool,
-    const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens,
-    const int32_t *__restrict__ gsel_idx, const int32_t *__restrict__ gsel_cnt, int32_t *__restrict__ hsel_idx,
-    int32_t *__restrict__ hsel_cnt, float *__restrict__ weights_out, DecodeWs ws) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kParts = kDThreads / P;  // threads per token
-  constexpr int kPer = DIM / kParts;     // coordinates per thread
-  __shared__ double smax[kDThreads / kWave][G];
-  __shared__ int scan_scratch[kDThreads / kWave];
-  Dims Dg = D;  // rows = KV heads
-  Dg.Hq = D.Hkv;
-  Dg.G = 1;
-  const int grows = D.B * D.Hkv, rows = D.B * D.Hq;
-  int *prefix = reinterpret_cast<int *>(smem);
-  const int tid = threadIdx.x;
-  for (int r = blockIdx.x * kDThreads + tid; r < rows; r += gridDim.x * kDThreads) {
-    ws.ctr[r] = 0u;  // kernel 2's arrival counters start at zero
-    hsel_cnt[r] = gsel_cnt[(size_t)(r / D.Hq) * D.Hkv + (r % D.Hq) / G];
-  }
-  const int total = build_item_map(Dg, seq_lens, gsel_cnt, prefix, grows, scan_scratch);
-  const int MP = D.max_pages;
-  const size_t wrow = (size_t)MP * P;
-  const int tok = tid / kParts, part = tid % kParts;
-#pragma unroll 1
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const int gr = find_row(prefix, grows, item);
-    const int i = item - prefix[gr];
-    const int cnt = prefix[gr + 1] - prefix[gr];
-    const int b = gr / D.Hkv, g = gr % D.Hkv;
-    const int r0 = b * D.Hq + g * G;
-    const int L = seq_len_clamped(seq_lens, b, D);
-    const int p = gsel_idx[(size_t)gr * MP + i];
-    const int prev = i > 0 ? gsel_idx[(size_t)gr * MP + i - 1] : -1;
-    float qv[G][kPer];
-#pragma unroll
-    for (int h = 0; h < G; ++h) load_vec<kPer>(q + (size_t)(r0 + h) * DIM + part * kPer, qv[h]);
-    const int np = n_pages_of(L, P);
-    const int pc = min(max(p, 0), MP - 1);
-    const int phys = page_table[(size_t)b * MP + pc];
-    const bool bad_item = p < 0 || p >= np || prev >= p || phys < 0 || phys >= D.num_phys;
-    const int physc = min(max(phys, 0), D.num_phys - 1);
-    const int n = min(P, L - pc * P);
-    float kv[kPer];
-    load_vec<kPer>(k_pool + (((size_t)physc * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
-    double x[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[h][e], acc);  // exact products
-#pragma unroll
-      for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-      x[h] = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
-      if (part == 0) ws.xs[(size_t)(r0 + h) * wrow + (size_t)i * P + tok] = x[h];
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) x[h] = wave_max(x[h]);
-    if ((tid & (kWave - 1)) == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h) smax[tid / kWave][h] = x[h];
-    __syncthreads();
-    if (tid < G) {
-      double m = smax[0][tid];
-      for (int w = 1; w < kDThreads / kWave; ++w) m = fmax(m, smax[w][tid]);
-      const size_t o = (size_t)(r0 + tid) * MP + i;
-      ws.pmax[o] = bad_item ? NAN : m;
-      ws.iphys[o] = (uint32_t)physc;
-      hsel_idx[o] = p;
-    }
-    __syncthreads();
-    // weights_out: zero every slot of the pages this item covers, (prev, p]
-    // (the last item also covers the pages after p); kernel 2 writes the
-    // support weights
-    if (weights_out && !bad_item) {
-      const size_t lo_s = (size_t)(prev + 1) * P;
-      const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
-      for (int h = 0; h < G; ++h)
-        for (size_t s = lo_s + tid; s < hi_s; s += kDThreads) weights_out[(size_t)(r0 + h) * wrow + s] = 0.0f;
-    }
-  }
-}
-
-size_t decode_group_ws_bytes(const Dims &D) {
-  Carve cv(nullptr);
-  size_t b = 0;
-  carve_decode(D, nullptr, &b);
-  cv.take<char>(b);
-  cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
-  cv.take<int32_t>((size_t)D.B * D.Hq);
-  return cv.bytes();
-}
-
-template <typename T, int DIM, int P, int G>
-static hipError_t launch_group_t(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
-                                 const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
-                                 const int32_t *gsel_idx, const int32_t *gsel_cnt, float *out, double *tau,
-                                 float *weights_out, void *ws, hipStream_t s) {
-  size_t dec_bytes = 0;
-  carve_decode(D, nullptr, &dec_bytes);
-  Carve cv(ws);
-  char *dec = cv.take<char>(dec_bytes);
-  int32_t *hsel_idx = cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
-  int32_t *hsel_cnt = cv.take<int32_t>((size_t)D.B * D.Hq);
-  const DecodeWs w = carve_decode(D, dec, nullptr);
-  const size_t map_bytes = (size_t)(D.B * D.Hkv + 1) * 4;
-  hipLaunchKernelGGL((group_scores_kernel<T, DIM, P, G>), dim3(kDGrid), dim3(kDThreads), map_bytes, s, D, dp,
-                     (const T *)q, (const T *)k_pool, page_table, seq_lens, gsel_idx, gsel_cnt, hsel_idx, hsel_cnt,
-                     weights_out, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, hsel_idx, hsel_cnt, out, tau, weights_out, w, s);
-}
-
-template <typename T, int DIM, int P>
-static hipError_t launch_group_g(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
-                                 const int32_t *pt, const int32_t *sl, const int32_t *si, const int32_t *sc,
-                                 float *out, double *tau, float *wo, void *ws, hipStream_t s) {
-  switch (D.G) {
-    case 1: return launch_group_t<T, DIM, P, 1>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-    case 2: return launch_group_t<T, DIM, P, 2>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-    case 4: return launch_group_t<T, DIM, P, 4>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-    case 8: return launch_group_t<T, DIM, P, 8>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename T, int DIM>
-static hipError_t launch_group_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
-                                 const int32_t *pt, const int32_t *sl, const int32_t *si, const int32_t *sc,
-                                 float *out, double *tau, float *wo, void *ws, hipStream_t s) {
-  if (D.P == 16) return launch_group_g<T, DIM, 16>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-  if (D.P == 32) return launch_group_g<T, DIM, 32>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
-  return launch_group_g<T, DIM, 64>(D, dp, q, k, v, pt, sl, si, sc, out, tau, wo, ws, s);
+hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
+                                const int32_t *page_table, const int32_t *seq_lens, const int32_t *sel_idx,
+                                const int32_t *sel_cnt, double alpha, int tau_method, float *out, double *tau,
+                                float *weights_out, void *ws, size_t ws_bytes, hipStream_t s) {
+  return launch_decode_mode(D, dtype, 0, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, alpha,
+                            tau_method, out, tau, weights_out, ws, ws_bytes, s);
 }
 
 hipError_t launch_entmax_decode_group(const Dims &D, int dtype, const void *q, const void *k_pool,
                                       const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
                                       const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
-                                      float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
-  DecodeParams dp;
-  dp.a = alpha - 1.0;
-  dp.beta = 1.0 / dp.a;
-  dp.c = D.scale;
-  dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
-  dp.tau_method = tau_method;
-  if (dtype == ENTMAXKV_BF16) {
-    if (D.d == 64) return launch_group_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-    return launch_group_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-  }
-  if (D.d == 64) return launch_group_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-  return launch_group_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, ws, s);
-}
-
-// ------------------------------------------- full cache: every page selected
-// One block per (range of pps pages, KV head g, sequence b); 256 threads, one
-// page per iteration (kDThreads / P threads per token), the next page's K slice
-// loaded while the current one is scored.  For each of the G query heads of the
-// group: exact X of every token (-inf past the sequence end) in kernel 2's
-// item-major layout, the page maximum (NaN for a bad page id), the physical
-// page, the identity selection sel_idx[i] = i and its count N_b.
-template <typename T, int DIM, int P, int G>
-__global__ __launch_bounds__(kDThreads) void full_scores_kernel(Dims D, DecodeParams dp, int pps,
-                                                                const T *__restrict__ q,
-                                                                const T *__restrict__ k_pool,
-                                                                const int32_t *__restrict__ page_table,
-                                                                const int32_t *__restrict__ seq_lens,
-                                                                int32_t *__restrict__ sel_idx,
-                                                                int32_t *__restrict__ sel_cnt,
-                                                                float *__restrict__ weights_out, DecodeWs ws) {
-  constexpr int kParts = kDThreads / P;  // threads per token
-  constexpr int kPer = DIM / kParts;     // coordinates per thread
-  __shared__ double smax[kDThreads / kWave][G];
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, tok = tid / kParts, part = tid % kParts;
-  const int MP = D.max_pages;
-  const size_t wrow = (size_t)MP * P;
-  const int L = seq_len_clamped(seq_lens, b, D);
-  const int np = n_pages_of(L, P);
-  const int p0 = s * pps, p1 = min(np, p0 + pps);
-  const int r0 = b * D.Hq + g * G;
-  if (s == 0 && tid < G) {
-    ws.ctr[r0 + tid] = 0u;  // kernel 2's arrival counters start at zero
-    sel_cnt[r0 + tid] = np;
-  }
-  // weights_out: kernel 2 writes the support; every other slot is zeroed here
-  // (the range holding the last page also zeroes the tail of the row)
-  const int last_s = np > 0 ? (np - 1) / pps : 0;
-  if (weights_out && s <= last_s) {
-    const size_t lo = (size_t)p0 * P, hi = s == last_s ? wrow : (size_t)p1 * P;
-    for (int h = 0; h < G; ++h)
-      for (size_t i = lo + tid; i < hi; i += kDThreads) weights_out[(size_t)(r0 + h) * wrow + i] = 0.0f;
-  }
-  if (p0 >= p1) return;
-
-  float qv[G][kPer];
-#pragma unroll
-  for (int h = 0; h < G; ++h) load_vec<kPer>(q + (size_t)(r0 + h) * DIM + part * kPer, qv[h]);
-  auto phys_of = [&](int p) { return page_table[(size_t)b * MP + p]; };
-  int ph = phys_of(p0);
-  float kv[kPer];
-  load_vec<kPer>(k_pool + (((size_t)min(max(ph, 0), D.num_phys - 1) * D.Hkv + g) * P + tok) * DIM + part * kPer, kv);
-#pragma unroll 1
-  for (int p = p0; p < p1; ++p) {
-    // next page's K slice first
-    const int pn = min(p + 1, p1 - 1);
-    const int phn = phys_of(pn);
-    float kn[kPer];
-    load_vec<kPer>(k_pool + (((size_t)min(max(phn, 0), D.num_phys - 1) * D.Hkv + g) * P + tok) * DIM + part * kPer, kn);
-    const bool bad = ph < 0 || ph >= D.num_phys;
-    const int n = min(P, L - p * P);
-    double x[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double acc = 0.0;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) acc = __builtin_fma((double)kv[e], (double)qv[h][e], acc);  // exact products
-#pragma unroll
-      for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-      x[h] = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
-      if (part == 0) ws.xs[(size_t)(r0 + h) * wrow + (size_t)p * P + tok] = x[h];
-    }
-    // page maxima of the G heads
-#pragma unroll
-    for (int h = 0; h < G; ++h) x[h] = wave_max(x[h]);
-    if ((tid & (kWave - 1)) == 0)
-#pragma unroll
-      for (int h = 0; h < G; ++h) smax[tid / kWave][h] = x[h];
-    __syncthreads();
-    if (tid < G) {
-      double m = smax[0][tid];
-      for (int w = 1; w < kDThreads / kWave; ++w) m = fmax(m, smax[w][tid]);
-      const size_t o = (size_t)(r0 + tid) * MP + p;
-      ws.pmax[o] = bad ? NAN : m;
-      ws.iphys[o] = (uint32_t)min(max(ph, 0), D.num_phys - 1);
-      sel_idx[o] = p;
-    }
-    __syncthreads();
-    ph = phn;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) kv[e] = kn[e];
-  }
-}
-
-size_t full_ws_bytes(const Dims &D) {
-  Carve cv(nullptr);
-  size_t b = 0;
-  carve_decode(D, nullptr, &b);
-  cv.take<char>(b);
-  cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
-  cv.take<int32_t>((size_t)D.B * D.Hq);
-  return cv.bytes();
-}
-
-template <typename T, int DIM, int P, int G>
-static hipError_t launch_full_t(const Dims &D, const DecodeParams &dp, const void *q, const void *k_pool,
-                                const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
-                                float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
-  size_t dec_bytes = 0;
-  carve_decode(D, nullptr, &dec_bytes);
-  Carve cv(ws);
-  char *dec = cv.take<char>(dec_bytes);
-  int32_t *sel_idx = cv.take<int32_t>((size_t)D.B * D.Hq * D.max_pages);
-  int32_t *sel_cnt = cv.take<int32_t>((size_t)D.B * D.Hq);
-  const DecodeWs w = carve_decode(D, dec, nullptr);
-  // about 2048 blocks over the (b, g, page) space
-  const long long items = (long long)D.B * D.Hkv * D.max_pages;
-  const int pps = (int)std::max<long long>(1, (items + 2047) / 2048);
-  const int S = (D.max_pages + pps - 1) / pps;
-  hipLaunchKernelGGL((full_scores_kernel<T, DIM, P, G>), dim3(S, D.Hkv, D.B), dim3(kDThreads), 0, s, D, dp, pps,
-                     (const T *)q, (const T *)k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, w);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_finish_t<T, DIM, P>(D, dp, v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w, s);
-}
-
-template <typename T, int DIM, int P>
-static hipError_t launch_full_g(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
-                                const int32_t *pt, const int32_t *sl, float *out, double *tau, float *wo, void *ws,
-                                hipStream_t s) {
-  switch (D.G) {
-    case 1: return launch_full_t<T, DIM, P, 1>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-    case 2: return launch_full_t<T, DIM, P, 2>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-    case 4: return launch_full_t<T, DIM, P, 4>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-    case 8: return launch_full_t<T, DIM, P, 8>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename T, int DIM>
-static hipError_t launch_full_p(const Dims &D, const DecodeParams &dp, const void *q, const void *k, const void *v,
-                                const int32_t *pt, const int32_t *sl, float *out, double *tau, float *wo, void *ws,
-                                hipStream_t s) {
-  if (D.P == 16) return launch_full_g<T, DIM, 16>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-  if (D.P == 32) return launch_full_g<T, DIM, 32>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
-  return launch_full_g<T, DIM, 64>(D, dp, q, k, v, pt, sl, out, tau, wo, ws, s);
+                                      float *out, double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                                      hipStream_t s) {
+  return launch_decode_mode(D, dtype, 1, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, alpha,
+                            tau_method, out, tau, weights_out, ws, ws_bytes, s);
 }
 
 hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *page_table, const int32_t *seq_lens, double alpha, int tau_method,
-                              float *out, double *tau, float *weights_out, void *ws, hipStream_t s) {
-  DecodeParams dp;
-  dp.a = alpha - 1.0;
-  dp.beta = 1.0 / dp.a;
-  dp.c = D.scale;
-  dp.ibeta = alpha == 1.5 ? 2 : (alpha == 2.0 ? 1 : 0);
-  dp.tau_method = tau_method;
-  if (dtype == ENTMAXKV_BF16) {
-    if (D.d == 64) return launch_full_p<uint16_t, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
-    return launch_full_p<uint16_t, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
-  }
-  if (D.d == 64) return launch_full_p<float, 64>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
-  return launch_full_p<float, 128>(D, dp, q, k_pool, v_pool, page_table, seq_lens, out, tau, weights_out, ws, s);
+                              float *out, double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                              hipStream_t s) {
+  return launch_decode_mode(D, dtype, 2, q, k_pool, v_pool, page_table, seq_lens, nullptr, nullptr, alpha,
+                            tau_method, out, tau, weights_out, ws, ws_bytes, s);
 }
 
 EKV_TRACE_DUMP(ekv_trace_dump_decode)

@@ -64,18 +64,25 @@ hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const 
                         const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
                         double *tau_hat, void *ws, hipStream_t s);
 
+// Decode workspaces: the item capacity (kept pages over all query-head rows)
+// follows from the bytes given; decode_ws_bytes is the size for every row's
+// full set, decode_ws_bytes_items the size for `items` kept pages and
+// decode_ws_min_bytes the size for one.
 size_t decode_ws_bytes(const Dims &D, bool full);
+size_t decode_ws_bytes_items(const Dims &D, long long items);
+size_t decode_ws_min_bytes(const Dims &D);
 hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const void *k_pool,
                                 const void *v_pool, const int32_t *page_table,
                                 const int32_t *seq_lens, const int32_t *sel_idx,
                                 const int32_t *sel_cnt, double alpha, int tau_method, float *out,
-                                double *tau, float *weights_out, void *ws, hipStream_t s);
+                                double *tau, float *weights_out, void *ws, size_t ws_bytes, hipStream_t s);
 
 size_t decode_group_ws_bytes(const Dims &D);
 hipError_t launch_entmax_decode_group(const Dims &D, int dtype, const void *q, const void *k_pool,
                                       const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
                                       const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
-                                      float *out, double *tau, float *weights_out, void *ws, hipStream_t s);
+                                      float *out, double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                                      hipStream_t s);
 
 size_t topk_group_ws_bytes(const Dims &D);
 hipError_t launch_topk_group(const Dims &D, const float *box, const int32_t *seq_lens, int k,
@@ -90,7 +97,8 @@ hipError_t launch_gauss_group(const Dims &D, const float *box, const float *mu, 
 size_t full_ws_bytes(const Dims &D);
 hipError_t launch_entmax_full(const Dims &D, int dtype, const void *q, const void *k_pool, const void *v_pool,
                               const int32_t *page_table, const int32_t *seq_lens, double alpha, int tau_method,
-                              float *out, double *tau, float *weights_out, void *ws, hipStream_t s);
+                              float *out, double *tau, float *weights_out, void *ws, size_t ws_bytes,
+                              hipStream_t s);
 
 size_t softmax_ws_bytes(const Dims &D);
 size_t softmax_sparse_ws_bytes(const Dims &D);

@@ -1,14 +1,16 @@
 """GPU parity of the entmax decodes on long selections.
 
-Rows here keep more than one chunk of tokens (the sparse decode then splits a
-row over several blocks and merges their candidates), and with a small score
-scale more candidates than fit in LDS (the threshold is then solved over the
-candidates in the workspace).  Same bars as the small cases: thresholds to
-1e-12, bit-exact supports, weights to 1e-5, outputs to the KV-dtype tolerance.
+Rows here keep many slices of tokens, and with a small score scale more than
+4096 entries: the row then goes to the helper blocks (histogram window,
+moments and window solve, split gather), or for a generic alpha to the
+leader's passes over the workspace.  Same bars as the small cases: thresholds
+to 1e-12, bit-exact supports, weights to 1e-5, outputs to the KV-dtype
+tolerance; a repeated call gives the same bits.
 """
 import numpy as np
 import pytest
 
+import sparse_decode_attention_page_amd as E
 from gpu_util import Dev, decode_check
 from sparse_decode_attention_page_amd import synth
 
@@ -51,17 +53,36 @@ def _selections(inp, seed=5):
     return sel, cnt
 
 
-@pytest.mark.parametrize("alpha,method", [(1.5, 0), (2.0, 0), (2.0, 1)])
+@pytest.mark.parametrize("alpha,method", [(1.5, 0), (2.0, 0), (2.0, 1), (1.25, 0)])
 def test_entmax_decode_sparse_long_rows(large, alpha, method):
     inp, D = large
     sel, cnt = _selections(inp)
     decode_check(inp, D, alpha, sel, cnt, tau_method=method)
 
 
-@pytest.mark.parametrize("alpha", [1.5, 2.0])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
 def test_entmax_decode_full_long_rows(large, alpha):
     inp, D = large
     decode_check(inp, D, alpha, None, None, full=True)
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_entmax_decode_long_rows_repeat_bitwise(large, alpha):
+    """Two calls on the same inputs give identical out, tau and weights (the
+    helper steps merge integer counts and fixed-order partials)."""
+    import torch
+    inp, D = large
+    sel, cnt = _selections(inp)
+    si, ci = torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda()
+    res = []
+    for _ in range(2):
+        out = torch.full((inp.B, inp.Hq, inp.d), np.nan, device="cuda")
+        tau = torch.full((inp.B, inp.Hq), np.nan, dtype=torch.float64, device="cuda")
+        w = torch.full((inp.B, inp.Hq, inp.max_pages * inp.P), np.nan, device="cuda")
+        E.entmax_decode_sparse(D.shape, D.q, D.k, D.v, D.pt, D.sl, si, ci, alpha, out, tau=tau, weights_out=w)
+        res.append((out.cpu().numpy(), tau.cpu().numpy(), w.cpu().numpy()))
+    for a, b in zip(res[0], res[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
 @pytest.mark.parametrize("scale", [0.0, 0.002], ids=["scale_default", "scale0.002"])
