@@ -61,6 +61,8 @@ constexpr int kWbuf = kHelpers * kSlot;  // candidates a leader keeps in its win
 constexpr int kIprLds = 2048;     // a row's item -> physical page table staged in LDS up to this size
 constexpr unsigned kStHist = 2, kStMom = 3, kStGath = 4, kStDone = 0xFFu;  // row steps (0: scores written)
 constexpr unsigned long long kSpinTicks = 20000000ull;                     // 0.2 s of the 100 MHz clock
+constexpr int kLargeN = 32768;  // rows with more entries take the histogram route
+constexpr int kStStride = 32;  // row step flags 128 bytes apart, so waiting blocks of different rows poll different lines
 
 struct DecodeWs {
   double *cx;         // [cap_tok]  entry X
@@ -74,9 +76,10 @@ struct DecodeWs {
   int *s_dense;       // [rows][ns] 1: the entries are every kept token, in place
   long long *rbase;   // [rows] first item of the row
   int *rcnt;          // [rows] items of the row
-  unsigned *state;    // [rows] step of a large row
-  unsigned *ctr;      // [rows][3] arrival counters of the helper steps
+  unsigned *state;    // [rows][kStStride] step of a large row (one 128-byte line per row)
+  unsigned *ctr;      // [rows][4] arrival counters of the helper steps and of the chunks
   double *rpar;       // [rows][8] published parameters (mx, lo, w, e_lo, e_hi, tau, z)
+  double *crec;       // [rows][kHelpers][16] chunk records (entries kept, bound, counts, start, compacted)
   unsigned *hist;     // [rows][kBins]
   double *hpart;      // [rows][kHelpers][8] moment partials
   double *wbuf;       // [rows][kHelpers][kSlot] window entries (a leader's candidates: kWbuf)
@@ -398,11 +401,16 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
     const int r = r0 + tid;
     ws.rbase[r] = s_base[tid];
     ws.rcnt[r] = s_items[tid];
-    ws.state[r] = 0u;
-    ws.ctr[3 * r] = 0u;
-    ws.ctr[3 * r + 1] = 0u;
-    ws.ctr[3 * r + 2] = 0u;
+    ws.state[(size_t)r * kStStride] = 0u;
+    ws.ctr[4 * r] = 0u;
+    ws.ctr[4 * r + 1] = 0u;
+    ws.ctr[4 * r + 2] = 0u;
+    ws.ctr[4 * r + 3] = 0u;
   }
+  // the histogram of a row that may take the histogram route starts at zero
+  for (int h = 0; h < G; ++h)
+    if (s == 0 && (long long)s_items[h] * P > kLargeN)
+      for (int i = tid; i < kBins; i += kDThreads) ws.hist[(size_t)(r0 + h) * kBins + i] = 0u;
   EKV_MARK(0, 1);
 
   // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
@@ -572,7 +580,7 @@ struct RowsArgs {
   float *out;
   double *tau;
   float *weights_out;
-  int ns, nh;
+  int ns, nh;  // slices per row; blocks (chunks at most) per row
 };
 
 // The entries of a run of slices, concatenated in index order; the slice
@@ -723,6 +731,14 @@ struct LdsVals {
     for (int i = t0; i < n; i += stride) fn(v[i]);
   }
 };
+struct RegVals16 {  // 16 values per thread (-inf for unused slots)
+  const double (&v)[16];
+  template <typename Fn>
+  __device__ __forceinline__ void each(Fn &&fn) const {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) fn(v[j]);
+  }
+};
 struct GlobVals {  // every entry of a run of slices, 8 per thread in flight
   const DecodeWs *ws;
   const Segs *sg;
@@ -871,7 +887,7 @@ __device__ __forceinline__ double newton_tau(const Src &src, const Above &ab, do
 // tau and z = F(tau) over a source by the whole block; ab as in newton_tau
 // (m0 > 0 only for alpha = 1.5, 2).
 template <typename Src>
-__device__ void solve_block(const Src &src, const Above &ab, double lo0, double hi, const DecodeParams &dp,
+__device__ __forceinline__ void solve_block(const Src &src, const Above &ab, double lo0, double hi, const DecodeParams &dp,
                             double *dred, double &tau, double &z) {
   double zk = 0.0;
   if (dp.ibeta == 2) tau = newton_tau<2, Src, BlockRed>(src, ab, lo0, hi, dp, dred, &zk);
@@ -894,7 +910,7 @@ __device__ void solve_block(const Src &src, const Above &ab, double lo0, double 
 // sort z descending; k* = max{k : 1 + k z_(k) > sum_{j<=k} z_(j)};
 // tau = (sum_{j<=k*} z_(j) - 1) / k*.  The condition holds exactly for k <= k*.
 // Only the candidates are sorted: every score outside them is below tau.
-__device__ double sparsemax_tau_sort(const double *cx, int n, double *buf, double *dred, int *s_kstar) {
+__device__ __forceinline__ double sparsemax_tau_sort(const double *cx, int n, double *buf, double *dred, int *s_kstar) {
   int m = 1;
   while (m < n) m <<= 1;
   for (int i = threadIdx.x; i < m; i += kDThreads) buf[i] = i < n ? cx[i] : -INFINITY;
@@ -991,9 +1007,21 @@ struct Gather {
     __syncthreads();
     const int ge = tid / kTpe, gc = tid % kTpe;
     int e = ge;
-    // four entries per thread in flight, then two, then one
+    // eight entries per thread in flight, then four, two, one (the sum runs
+    // over e, e + kEpp, e + 2 kEpp, ... in that order either way)
 #pragma unroll 1
-    for (; e + 3 * kEpp < nsup; e += 4 * kEpp) {
+    for (; e + 7 * kEpp < nsup; e += 8 * kEpp) {
+      float v[8][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) load_vec<8>(v_pool + (size_t)sh->tok[e + i * kEpp] * DIM + gc * 8, v[i]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wi = sh->w[e + i * kEpp];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc8[u] += wi * v[i][u];
+      }
+    }
+    if (e + 3 * kEpp < nsup) {
       float v0[8], v1[8], v2[8], v3[8];
       load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
       load_vec<8>(v_pool + (size_t)sh->tok[e + kEpp] * DIM + gc * 8, v1);
@@ -1008,6 +1036,7 @@ struct Gather {
       for (int u = 0; u < 8; ++u) acc8[u] += w2 * v2[u];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w3 * v3[u];
+      e += 4 * kEpp;
     }
     if (e + kEpp < nsup) {
       float v0[8], v1[8];
@@ -1073,7 +1102,7 @@ struct Gather {
 
 // Waits until the row's step is at least `need` (kStDone counts); returns the
 // step seen, or 0 after the time limit.
-__device__ unsigned wait_step(const unsigned *state, unsigned need, unsigned *s_flag) {
+__device__ __forceinline__ unsigned wait_step(const unsigned *state, unsigned need, unsigned *s_flag) {
   if (threadIdx.x == 0) {
     const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
     unsigned v;
@@ -1084,7 +1113,7 @@ __device__ unsigned wait_step(const unsigned *state, unsigned need, unsigned *s_
         v = 0u;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(32);  // about 1 us between polls
     }
     *s_flag = v;
   }
@@ -1099,7 +1128,7 @@ __device__ __forceinline__ void publish_step(unsigned *state, unsigned v) {
 }
 
 template <int DIM>
-__device__ void row_nan(const RowsArgs &ra, int r) {
+__device__ __forceinline__ void row_nan(const RowsArgs &ra, int r) {
   for (int i = threadIdx.x; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = NAN;
   if (threadIdx.x == 0 && ra.tau) ra.tau[r] = NAN;
 }
@@ -1167,25 +1196,7 @@ __device__ __forceinline__ void gather_entries(Gather<T, DIM> &ga, const Segs &s
   ga.finish(dst, agent);
 }
 
-// Every entry of row r in the workspace: tau by passes over them (generic
-// exponent, or a window too wide for the slots) and, when `gather`, the
-// support gather with the output written here.
-template <typename T, int DIM>
-__device__ void row_slow(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
-                         RowsLds<T, DIM> &sm, const Segs &sg, double lo0, double hi, long long rbase, double *dred,
-                         int *scan_scratch, bool gather, double *tau_o, double *z_o) {
-  const GlobVals src{&ws, &sg};
-  const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
-  double tau, z;
-  solve_block(src, none, lo0, hi, dp, dred, tau, z);
-  *tau_o = tau;
-  *z_o = z;
-  if (!gather) return;
-  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, tau, z);
-  gather_entries<T, DIM>(ga, sg, ws, ra.out + (size_t)r * DIM, false);
-}
-
-// ---------------------------------------------------------------- leader
+// ------------------------------------------------------------ chunk blocks
 // Values in a global array, strided over the block (fixed order), 8 in flight
 struct ArrVals {
   const double *v;
@@ -1206,192 +1217,136 @@ struct ArrVals {
   }
 };
 
-// Opens the helper steps of a large row: histogram range [lo, mx] and a
-// cleared histogram, then the step flag.
-template <typename T, int DIM>
-__device__ void open_large(const DecodeWs &ws, int r, double mx, double mn) {
-  const double thr = mx - 1.0;
-  double lo = fmax(thr, mn);
-  double w = (mx - lo) / (double)kBins;
-  if (!(w > 0.0) || !(w < INFINITY)) {
-    lo = thr;
-    w = 1.0 / (double)kBins;
+// After the chunk step, chunk c's record says whether its entries were
+// compacted (one run of m entries at `start`, token ids explicit) or left in
+// the layout of its slices [s0, s1).  Builds the Segs of chunk c in LDS
+// (every thread calls it).
+__device__ __forceinline__ Segs chunk_segs(const DecodeWs &ws, int r, int ns, int c, long long rbase, int P,
+                                           int *off, uint32_t *start, int *dense, unsigned long long *scan64) {
+  const double *rec = ws.crec + ((size_t)r * kHelpers + c) * 16;
+  const int m = (int)ld_agent(&rec[0]);
+  const bool compacted = ld_agent(&rec[11]) != 0.0;
+  const uint32_t st = (uint32_t)ld_agent(&rec[10]);
+  const int s0 = (int)ld_agent(&rec[13]), s1 = (int)ld_agent(&rec[14]);
+  const unsigned long long tok0 = (unsigned long long)rbase * (unsigned long long)P;
+  if (compacted) {
+    __syncthreads();  // the tables may still be in use
+    if (threadIdx.x == 0) {
+      off[0] = 0;
+      off[1] = m;
+      start[0] = st;
+      dense[0] = 0;
+    }
+    __syncthreads();
+    return Segs{off, start, dense, 1, m, tok0};
   }
-  for (int i = threadIdx.x; i < kBins; i += kDThreads) st_agent(&ws.hist[(size_t)r * kBins + i], 0u);
-  if (threadIdx.x == 0) {
-    st_agent(&ws.rpar[(size_t)r * 8 + 0], mx);
-    st_agent(&ws.rpar[(size_t)r * 8 + 1], lo);
-    st_agent(&ws.rpar[(size_t)r * 8 + 2], w);
-  }
-  publish_step(&ws.state[r], kStHist);
+  int nseg;
+  __syncthreads();
+  const int M = load_segs(ws, r, ns, s0, s1, off, start, dense, scan64, &nseg);
+  return Segs{off, start, dense, nseg, M, tok0};
 }
 
-// A row with at most kLeadMax entries: two passes over the entries (batches
-// of 2048, the next in flight; one batch stays in registers): the counts
-// above mx - 2^-i give the certified bound Lb, then the candidates X > Lb in
-// index order go to LDS (up to kCand) and to the row's window buffer (up to
-// kWbuf).  A row with more candidates goes to the helpers.  Every decision
-// and every sum depends on the entries alone, not on timing.
+// Every entry of row r, chunk by chunk (tables rebuilt per chunk and pass)
+struct RowVals {
+  const DecodeWs *ws;
+  int r, ns, nc, P;
+  long long rbase;
+  int *off;
+  uint32_t *start;
+  int *dense;
+  unsigned long long *scan64;
+  template <typename Fn>
+  __device__ __forceinline__ void each(Fn &&fn) const {
+#pragma unroll 1
+    for (int c = 0; c < nc; ++c) {
+      const Segs sg = chunk_segs(*ws, r, ns, c, rbase, P, off, start, dense, scan64);
+      const GlobVals gv{ws, &sg};
+      gv.each(fn);
+    }
+  }
+};
+
+// Row tau and output from every entry by passes over the workspace (generic
+// exponent with many candidates, or a window too wide for the slots); with
+// `gather` the support gather and the output too.
 template <typename T, int DIM>
-__device__ void row_leader(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
-                           RowsLds<T, DIM> &sm) {
-  __shared__ double dred[3 * kDThreads / kWave];
-  __shared__ int scan_scratch[kDThreads / kWave];
-  __shared__ unsigned long long scan64[kDThreads / kWave];
-  __shared__ int s_cnt[kDThreads / kWave][kNThr];
-  __shared__ double s_tau[2];
-  __shared__ int s_kstar;
-  const int tid = threadIdx.x;
-  const int ns = ra.ns;
-  EKV_MARK(1, 0);
-  // 1. slice summaries: entry total, row maximum and minimum, malformed marks
-  const long long rbase = ws.rbase[r];
-  const int rcnt = ws.rcnt[r];
-  double mm[2];
-  int nan, nseg;
-  const int N = load_segs(ws, r, ns, 0, ns, sm.off, sm.start, sm.dense, scan64, &nseg, mm, &nan);
-  const double mx = block_max(mm[0], dred);
-  const double mn = block_min_d(mm[1], dred);
-  nan = __syncthreads_or(nan);
-  const Segs sg{sm.off, sm.start, sm.dense, nseg, N, (unsigned long long)rbase * (unsigned long long)D.P};
-  if (nan) {
-    row_nan<DIM>(ra, r);
-    publish_step(&ws.state[r], kStDone);
-    return;
-  }
-  if (N == 0) {
-    for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
-    if (tid == 0 && ra.tau) ra.tau[r] = NAN;
-    publish_step(&ws.state[r], kStDone);
-    return;
-  }
-  const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
-  if (N > kLeadMax) {
-    if (dp.ibeta == 0) {  // generic exponent: passes over the workspace by this block
-      publish_step(&ws.state[r], kStDone);  // no helper steps for this row
-      double tau, z;
-      row_slow<T, DIM>(D, dp, ra, ws, r, sm, sg, thr, mx, rbase, dred, scan_scratch, true, &tau, &z);
-      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
-      return;
-    }
-    open_large<T, DIM>(ws, r, mx, mn);
-    return;
-  }
-  EKV_MARK(1, 1);
-  // 2. pass 1: counts above mx - 2^-i (lane i mod kNThr evaluates threshold i
-  //    later); the row's item -> physical page table into LDS meanwhile
-  const int nb = (N + 8 * kDThreads - 1) / (8 * kDThreads);
-  const bool ipr_lds = rcnt <= kIprLds;
-  Batch8 cur, nxt;
-  load_batch8(sg, ws, 8 * tid, true, cur);
-  {
-    uint32_t ip[kIprLds / kDThreads];
-#pragma unroll
-    for (int u = 0; u < kIprLds / kDThreads; ++u) {
-      const int i = u * kDThreads + tid;
-      ip[u] = (ipr_lds && i < rcnt) ? ws.iphys[(size_t)rbase + i] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kIprLds / kDThreads; ++u) {
-      const int i = u * kDThreads + tid;
-      if (ipr_lds && i < rcnt) sm.lead.ipr[i] = ip[u];
-    }
-  }
-  int c8[kNThr];
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) c8[i] = 0;
-  auto count8 = [&](const Batch8 &bt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (bt.v[u] > thr)
-#pragma unroll
-        for (int i = 0; i < kNThr; ++i) c8[i] += bt.v[u] > mx - ldexp(1.0, -i) ? 1 : 0;
-  };
-  if (nb > 1) load_batch8(sg, ws, 8 * kDThreads + 8 * tid, false, nxt);
-  count8(cur);
+__device__ __forceinline__ void row_slow(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                         RowsLds<T, DIM> &sm, double lo0, double hi, long long rbase, double *dred, int *scan_scratch,
+                         unsigned long long *scan64, int nc, bool gather, double *tau_o, double *z_o) {
+  const RowVals src{&ws, r, ra.ns, nc, D.P, rbase, sm.off, sm.start, sm.dense, scan64};
+  const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
+  double tau, z;
+  solve_block(src, none, lo0, hi, dp, dred, tau, z);
+  *tau_o = tau;
+  *z_o = z;
+  if (!gather) return;
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, tau, z);
 #pragma unroll 1
-  for (int bi = 1; bi < nb; ++bi) {
-    Batch8 nn;
-    if (bi + 1 < nb) load_batch8(sg, ws, (bi + 1) * 8 * kDThreads + 8 * tid, false, nn);
-    count8(nxt);
-    nxt = nn;
-  }
-#pragma unroll
-  for (int i = 0; i < kNThr; ++i) c8[i] = wave_sum(c8[i]);
-  if ((tid & (kWave - 1)) == 0)
-    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = c8[i];
-  __syncthreads();
-  // certified bound: C entries above mx - d give F(mx - d - C^-(alpha-1)) >= 1
-  double Lb;
-  {
-    const int i = tid & (kNThr - 1);
-    int ci_ = 0;
-    for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
-    const double cand =
-        ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
-    const double wm = wave_max(cand);
-    if (tid == 0) s_tau[0] = fmax(thr, wm);
-    __syncthreads();
-    Lb = s_tau[0];
-  }
-  // 3. pass 2: candidates X > Lb in index order into LDS and the window buffer
-  double *wrow = ws.wbuf + (size_t)r * kHelpers * kSlot;
-  uint32_t *wtok = ws.wtok + (size_t)r * kHelpers * kSlot;
-  int nC = 0;
-  auto compact8 = [&](const Batch8 &bt) __attribute__((always_inline)) {
-    int mine = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) mine += bt.v[u] > Lb ? 1 : 0;
-    int tot;
-    int at = nC + block_excl_scan<true>(mine, scan_scratch, &tot);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (bt.v[u] > Lb) {
-        if (at < kCand) {
-          sm.lead.cx[at] = bt.v[u];
-          sm.lead.ci[at] = bt.t[u];
-        }
-        if (at < kWbuf) {  // coherent stores: helpers may rewrite these bytes in this launch
-          st_agent(&wrow[at], bt.v[u]);
-          st_agent(&wtok[at], bt.t[u]);
-        }
-        ++at;
-      }
-    nC += tot;
-  };
-  if (nb == 1) {
-    compact8(cur);
-  } else {
-    load_batch8(sg, ws, 8 * tid, true, cur);
+  for (int c = 0; c < nc; ++c) {
+    const Segs sg = chunk_segs(ws, r, ra.ns, c, rbase, D.P, sm.off, sm.start, sm.dense, scan64);
+    Batch8 cur, nxt;
+    load_batch8(sg, ws, 8 * (int)threadIdx.x, true, cur);
 #pragma unroll 1
-    for (int bi = 0; bi < nb; ++bi) {
-      if (bi + 1 < nb) load_batch8(sg, ws, (bi + 1) * 8 * kDThreads + 8 * tid, true, nxt);
-      compact8(cur);
+    for (int base = 0; base < sg.total; base += 8 * kDThreads) {
+      if (base + 8 * kDThreads < sg.total)
+        load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, nxt);
+      ga.template offer<8>(cur.v, cur.t);
       cur = nxt;
     }
   }
-  __syncthreads();
-  EKV_MARK(1, 2);
-  if (nC > kWbuf) {  // more candidates than the leader holds
-    if (dp.ibeta == 0) {  // generic exponent: passes over the workspace by this block
-      publish_step(&ws.state[r], kStDone);
-      double tau, z;
-      row_slow<T, DIM>(D, dp, ra, ws, r, sm, sg, Lb, mx, rbase, dred, scan_scratch, true, &tau, &z);
-      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
-      return;
-    }
-    open_large<T, DIM>(ws, r, mx, mn);  // the helpers take the row
-    return;
+  ga.finish(ra.out + (size_t)r * DIM, false);
+}
+
+// The end of a row whose entries (at most 16 per thread, -inf for unused or
+// dropped slots) are in registers: the candidates X > Lb in index order into
+// LDS, tau and z (one wave over LDS, the sort form, or the block over the
+// registers), then the support gather and the output.
+template <typename T, int DIM>
+__device__ __forceinline__ void row_finish(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                       RowsLds<T, DIM> &sm, double (&xv)[16], uint32_t (&tv)[16], double mx, double Lb,
+                       long long rbase, double *dred, int *scan_scratch, double *s_tau, int *s_kstar) {
+  const int tid = threadIdx.x;
+  // the row's item -> physical page table into LDS (loads issued first)
+  const int rcnt = ws.rcnt[r];
+  const bool ipr_lds = rcnt <= kIprLds;
+  uint32_t ip[kIprLds / kDThreads];
+#pragma unroll
+  for (int u = 0; u < kIprLds / kDThreads; ++u) {
+    const int i = u * kDThreads + tid;
+    ip[u] = (ipr_lds && i < rcnt) ? ws.iphys[(size_t)rbase + i] : 0u;
   }
-  publish_step(&ws.state[r], kStDone);  // the helpers are not needed
-  // 4. tau and z: one wave over the LDS candidates, the sort form, or the
-  //    block over the window buffer
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (!(xv[u] > Lb)) xv[u] = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kIprLds / kDThreads; ++u) {
+    const int i = u * kDThreads + tid;
+    if (ipr_lds && i < rcnt) sm.lead.ipr[i] = ip[u];
+  }
+  int nC;
+  {
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mine += xv[u] > Lb ? 1 : 0;
+    int at = block_excl_scan(mine, scan_scratch, &nC);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (xv[u] > Lb) {
+        if (at < kCand) {
+          sm.lead.cx[at] = xv[u];
+          sm.lead.ci[at] = tv[u];
+        }
+        ++at;
+      }
+    __syncthreads();
+  }
+  EKV_MARK(1, 3);
   double tau, z;
   const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
   const double hi = mx - pow((double)max(nC, 1), -dp.a);  // F(hi) <= 1: at most nC entries above it
   const bool lds = nC <= kCand;
   if (lds && dp.ibeta == 1 && dp.tau_method == 1) {
-    tau = sparsemax_tau_sort(sm.lead.cx, nC, sm.lead.sortbuf, dred, &s_kstar);
+    tau = sparsemax_tau_sort(sm.lead.cx, nC, sm.lead.sortbuf, dred, s_kstar);
     double zz = 0.0;
     for (int i = tid; i < nC; i += kDThreads) {
       const double y = sm.lead.cx[i] - tau;
@@ -1419,151 +1374,455 @@ __device__ void row_leader(const Dims &D, const DecodeParams &dp, const RowsArgs
     tau = s_tau[0];
     z = s_tau[1];
   } else {
-    solve_block(ArrVals{wrow, nC}, none, Lb, hi, dp, dred, tau, z);
+    solve_block(RegVals16{xv}, none, Lb, hi, dp, dred, tau, z);
   }
-  EKV_MARK(1, 3);
+  EKV_MARK(1, 4);
   if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
-  // 5. support gather over the candidates in index order
-  Gather<T, DIM> ga =
-      make_gather<T, DIM>(&sm.lead.ga, scan_scratch, D, dp, ra, ws, r, rbase, ipr_lds ? sm.lead.ipr : nullptr, tau, z);
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.lead.ga, scan_scratch, D, dp, ra, ws, r, rbase,
+                                          ipr_lds ? sm.lead.ipr : nullptr, tau, z);
+  if (lds) {
 #pragma unroll 1
-  for (int k0 = 0; k0 < nC; k0 += 4 * kDThreads) {
-    double x4[4];
-    uint32_t t4[4];
+    for (int k0 = 0; k0 < nC; k0 += 4 * kDThreads) {
+      double x4[4];
+      uint32_t t4[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + 4 * tid + u;
-      x4[u] = k < nC ? (lds ? sm.lead.cx[k] : ld_agent(&wrow[k])) : -INFINITY;
-      t4[u] = k < nC ? (lds ? sm.lead.ci[k] : ld_agent(&wtok[k])) : 0u;
+      for (int u = 0; u < 4; ++u) {
+        const int k = k0 + 4 * tid + u;
+        x4[u] = k < nC ? sm.lead.cx[k] : -INFINITY;
+        t4[u] = k < nC ? sm.lead.ci[k] : 0u;
+      }
+      ga.template offer<4>(x4, t4);
     }
-    ga.template offer<4>(x4, t4);
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      double x8[8];
+      uint32_t t8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x8[u] = xv[8 * half + u];
+        t8[u] = tv[8 * half + u];
+      }
+      ga.template offer<8>(x8, t8);
+    }
   }
   ga.finish(ra.out + (size_t)r * DIM, false);
-  EKV_MARK(1, 4);
+  EKV_MARK(1, 5);
 }
 
-// ---------------------------------------------------------------- helpers
-// Helper j of row r takes slices [j ns / nh, (j + 1) ns / nh).
+// The blocks of a row.  Every block reads every slice's summary (entry
+// counts, max and min) and derives the same chunking: nc = ceil(N / kChunkEnt)
+// chunks (at most nh), slices assigned to chunks by their entry prefix, so
+// chunks hold about N / nc entries each; a block whose chunk index is nc or
+// more leaves.  Each chunk counts its entries above mx - 2^-i (a certified
+// bound Lc for the row: C entries above mx - d give F(mx - d - C^-(alpha-1))
+// >= 1) and, in a row of at most kLargeN entries, compacts its entries above
+// max(mx - 1, Lc) in place; in a larger row it adds its entries to the row's
+// integer histogram instead.  The row's last chunk to arrive merges: the row
+// bound Lb from every chunk's bound and the summed counts; a smaller row is
+// solved and gathered there (one wave over LDS candidates, or the block).  In
+// a large row the last chunk certifies a window [e_lo, e_hi] for tau from the
+// histogram (bounds of F at the bin edges) and every chunk then (a) sums the
+// moments of its entries above e_hi and hands over those in the window (the
+// last to arrive solves for tau exactly) and (b) gathers its support (the
+// last sums the partial outputs in chunk order).  Between (a) and (b) the
+// chunks of the row wait for its last block; a row has at most nh <= 32
+// chunks, fewer than an XCD holds at once, and blocks are dispatched in
+// index order, so every waited-for block is running.  Every decision and
+// every sum depends on the entries alone, not on timing.
+constexpr int kChunkPer = 16;                     // entries per thread a chunk block holds
+constexpr int kChunkCap = kChunkPer * kDThreads;  // entries a chunk compacts
+constexpr int kChunkEnt = 4096;                   // entries per chunk a row aims at
+constexpr int kLastCap = 4096;                    // entries the last block solves over
+constexpr int kSumPer = kMaxSlices / kDThreads;   // slice summaries per thread
+
 template <typename T, int DIM>
-__device__ void row_helper(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int step,
-                           int r, int j, RowsLds<T, DIM> &sm) {
+__device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                          int c, RowsLds<T, DIM> &sm) {
   __shared__ double dred[3 * kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
+  __shared__ unsigned long long scan64[kDThreads / kWave];
+  __shared__ int s_cnt[kDThreads / kWave][kNThr];
+  __shared__ double s_tau[2];
+  __shared__ int s_kstar, s_last, s_ovf;
   __shared__ unsigned s_flag;
-  __shared__ int s_last;
-  __shared__ unsigned long long red64[kDThreads / kWave];
+  __shared__ double s_rec[kHelpers][15];
   __shared__ double s_par[8];
   __shared__ double s_hp[kHelpers][5];
   __shared__ int s_woff[kHelpers + 1];
-  __shared__ int s_ovf;
   __shared__ double s_amin;
   const int tid = threadIdx.x;
-  const int ns = ra.ns, nh = ra.nh;
-  const unsigned need = step == 0 ? kStHist : (step == 1 ? kStMom : kStGath);
-  const unsigned st = wait_step(&ws.state[r], need, &s_flag);
-  if (st == kStDone) return;
-  if (st == 0u) {  // time limit: the row is marked failed
-    row_nan<DIM>(ra, r);
+  const int ns = ra.ns;
+  EKV_MARK(1, 0);
+  // 1. every slice's summary in registers: N, mx, mn, malformed marks
+  const long long rbase = ws.rbase[r];
+  const unsigned long long tok0 = (unsigned long long)rbase * (unsigned long long)D.P;
+  const int per = (ns + kDThreads - 1) / kDThreads;
+  const int i0 = tid * per;
+  int scn[kSumPer];
+  uint32_t sst[kSumPer];
+  int sdn[kSumPer];
+  double mx = -INFINITY, mn = INFINITY;
+  int nan = 0, myN = 0;
+#pragma unroll
+  for (int u = 0; u < kSumPer; ++u) {
+    scn[u] = 0;
+    const int i = i0 + u;
+    if (u < per && i < ns) {
+      const size_t o = (size_t)r * ns + i;
+      scn[u] = ws.s_cnt[o];
+      sst[u] = ws.s_start[o];
+      sdn[u] = ws.s_dense[o];
+      const double v = ws.s_max[o];
+      nan |= v != v;
+      mx = fmax(mx, v);
+      mn = fmin(mn, ws.s_min[o]);
+      myN += scn[u];
+    }
+  }
+  int N;
+  const int nbefore = block_excl_scan(myN, scan_scratch, &N);
+  mx = block_max(mx, dred);
+  mn = block_min_d(mn, dred);
+  nan = __syncthreads_or(nan);
+  const int nc = N > 0 ? min(ra.nh, (N + kChunkEnt - 1) / kChunkEnt) : 1;
+  if (c >= nc) return;
+  const bool large = N > kLargeN && dp.ibeta != 0;
+  const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
+  // this chunk's slices: chunk of a slice = floor(entries before it * nc / N)
+  int myc[kSumPer];
+  {
+    int before = nbefore;
+#pragma unroll
+    for (int u = 0; u < kSumPer; ++u) {
+      myc[u] = N > 0 ? (int)(((long long)before * nc) / N) : 0;
+      if (myc[u] > nc - 1) myc[u] = nc - 1;
+      before += scn[u];
+    }
+  }
+  // the non-empty slices of this chunk as one LDS table (packed 64-bit scan:
+  // table position in the high half, entry offset in the low half); the
+  // chunk's slice range goes to its record
+  int M, nseg, cs0 = ns, cs1 = 0;
+  {
+    unsigned long long mine = 0;
+#pragma unroll
+    for (int u = 0; u < kSumPer; ++u) {
+      const int i = i0 + u;
+      if (u < per && i < ns && myc[u] == c) {
+        cs0 = min(cs0, i);
+        cs1 = max(cs1, i + 1);
+        if (scn[u] > 0) mine += (1ull << 32) + (unsigned)scn[u];
+      }
+    }
+    unsigned long long tot;
+    unsigned long long run = block_excl_scan64(mine, scan64, &tot);
+#pragma unroll
+    for (int u = 0; u < kSumPer; ++u) {
+      const int i = i0 + u;
+      if (u < per && i < ns && myc[u] == c && scn[u] > 0) {
+        const int at = (int)(run >> 32);
+        sm.off[at] = (int)(run & 0xFFFFFFFFull);
+        sm.start[at] = sst[u];
+        sm.dense[at] = sdn[u];
+        run += (1ull << 32) + (unsigned)scn[u];
+      }
+    }
+    const int ntab = (int)(tot >> 32);
+    M = (int)(tot & 0xFFFFFFFFull);
+    if (tid == 0) {
+      sm.off[ntab] = M;
+      if (ntab == 0) {
+        sm.off[0] = 0;
+        sm.off[1] = 0;
+        sm.start[0] = 0u;
+        sm.dense[0] = 1;
+      }
+    }
+    nseg = ntab > 0 ? ntab : 1;
+    cs0 = -(int)block_max((double)-cs0, dred);
+    cs1 = (int)block_max((double)cs1, dred);
+  }
+  const Segs sg{sm.off, sm.start, sm.dense, nseg, M, tok0};
+  EKV_MARK(1, 6);
+  // histogram range of a large row: every entry above lo is binned
+  double hlo = fmax(thr, mn);
+  double hw = (mx - hlo) / (double)kBins;
+  if (!(hw > 0.0) || !(hw < INFINITY)) hw = 1.0 / (double)kBins;
+  // 2. counts above mx - 2^-i; compaction (smaller rows) or histogram (large)
+  int c8[kNThr];
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) c8[i] = 0;
+  auto count1 = [&](double x) __attribute__((always_inline)) {
+    if (x > thr)
+#pragma unroll
+      for (int i = 0; i < kNThr; ++i) c8[i] += x > mx - ldexp(1.0, -i) ? 1 : 0;
+  };
+  const bool small = !large && M <= kChunkCap;
+  double xv[kChunkPer];
+  uint32_t tv[kChunkPer];
+  if (large)
+    for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = 0u;
+  __syncthreads();
+  if (!nan && M > 0) {
+    if (small) {
+      const int k0 = kChunkPer * tid;
+      size_t ad[kChunkPer];
+      bool dn[kChunkPer];
+      sg.addr_run<kChunkPer>(k0, ad, dn);
+#pragma unroll
+      for (int u = 0; u < kChunkPer; ++u) {
+        xv[u] = ws.cx[ad[u]];
+        tv[u] = sg.tok_of(ws, ad[u], dn[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kChunkPer; ++u) {
+        if (k0 + u >= M) xv[u] = -INFINITY;
+        count1(xv[u]);
+      }
+    } else {
+      Batch8 cur, nxt;
+      load_batch8(sg, ws, 8 * tid, false, cur);
+#pragma unroll 1
+      for (int base = 0; base < M; base += 8 * kDThreads) {
+        if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double x = cur.v[u];
+          count1(x);
+          if (large && x > hlo) {
+            const double f = floor((x - hlo) / hw);
+            const int bin = !(f >= 0.0) ? 0 : (f >= (double)kBins ? kBins - 1 : (int)f);
+            atomicAdd(&sm.hist[bin], 1u);
+          }
+        }
+        cur = nxt;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kNThr; ++i) c8[i] = wave_sum(c8[i]);
+  if ((tid & (kWave - 1)) == 0)
+    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = c8[i];
+  __syncthreads();
+  if (large)
+    for (int i = tid; i < kBins; i += kDThreads)
+      if (sm.hist[i]) atomicAdd(&ws.hist[(size_t)r * kBins + i], sm.hist[i]);
+  double Lc;
+  {
+    const int i = tid & (kNThr - 1);
+    int ci_ = 0;
+    for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
+    const double cand =
+        ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+    const double wm = wave_max(cand);
+    if (tid == 0) s_tau[0] = fmax(thr, wm);
+    __syncthreads();
+    Lc = s_tau[0];
+  }
+  EKV_MARK(1, 7);
+  if (nc == 1 && small) {
+    // a lone chunk holds the whole row in registers: the candidates above Lb
+    // (= Lc, the row's own counts) go to LDS directly
+    if (nan || N == 0) {
+      if (nan) {
+        row_nan<DIM>(ra, r);
+      } else {
+        for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
+        if (tid == 0 && ra.tau) ra.tau[r] = NAN;
+      }
+      return;
+    }
+    row_finish<T, DIM>(D, dp, ra, ws, r, sm, xv, tv, mx, Lc, rbase, dred, scan_scratch, s_tau, &s_kstar);
+    return;
+  }
+  const uint32_t cstart = sm.start[0] - (uint32_t)sm.off[0];  // the chunk's first entry position
+  int m = M;
+  if (small && !nan && M > 0) {
+    // in place: entry k of the chunk sits at or after position cstart + k
+    // (each slice's entries are a prefix of its item range), so every write
+    // lands on an entry read before the scan's barrier
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < kChunkPer; ++u) mine += xv[u] > Lc ? 1 : 0;
+    int at = block_excl_scan(mine, scan_scratch, &m);
+#pragma unroll
+    for (int u = 0; u < kChunkPer; ++u)
+      if (xv[u] > Lc) {
+        st_agent(&ws.cx[cstart + at], xv[u]);
+        st_agent(&ws.ct[cstart + at], tv[u]);
+        ++at;
+      }
+  }
+  if (tid == 0) {
+    double *rec = ws.crec + ((size_t)r * kHelpers + c) * 16;
+    st_agent(&rec[0], (double)m);
+    st_agent(&rec[1], Lc);
+    for (int i = 0; i < kNThr; ++i) st_agent(&rec[2 + i], (double)(s_cnt[0][i] + s_cnt[1][i] + s_cnt[2][i] + s_cnt[3][i]));
+    st_agent(&rec[10], (double)cstart);
+    st_agent(&rec[11], small ? 1.0 : 0.0);
+    st_agent(&rec[12], (double)M);
+    st_agent(&rec[13], (double)cs0);
+    st_agent(&rec[14], (double)cs1);
+  }
+  EKV_MARK(1, 1);
+  if (nc > 1 && !arrive_last(&ws.ctr[4 * r + 3], (unsigned)nc, &s_last)) {
+    if (!large) return;
+  } else {
+    // ---- 3. the row's last chunk: merge (a lone chunk first completes its
+    // own record and histogram stores)
+    EKV_MARK(1, 2);
+    if (nc == 1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (tid < nc)
+      for (int f = 0; f < 15; ++f) s_rec[tid][f] = ld_agent(&ws.crec[((size_t)r * kHelpers + tid) * 16 + f]);
+    __syncthreads();
+    if (nan || N == 0) {
+      if (nan) {
+        row_nan<DIM>(ra, r);
+      } else {
+        for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
+        if (tid == 0 && ra.tau) ra.tau[r] = NAN;
+      }
+      if (large) publish_step(&ws.state[(size_t)r * kStStride], kStDone);
+      return;
+    }
+    int mtot = 0;
+    bool all_small = true;
+    for (int cc = 0; cc < nc; ++cc) {
+      mtot += (int)s_rec[cc][0];
+      all_small &= s_rec[cc][11] != 0.0;
+    }
+    double Lb;
+    {
+      // lane i (mod kNThr): threshold i's bound from the summed counts
+      const int i = tid & (kNThr - 1);
+      int ct = 0;
+      for (int cc = 0; cc < nc; ++cc) ct += (int)s_rec[cc][2 + i];
+      const double cand =
+          ct > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ct, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+      double bnd = wave_max(cand);
+      for (int cc = 0; cc < nc; ++cc) bnd = fmax(bnd, s_rec[cc][1]);
+      if (tid == 0) s_tau[0] = fmax(thr, bnd);
+      __syncthreads();
+      Lb = s_tau[0];
+    }
+    if (large) {
+      // ---- certified window from the row's histogram.  Bin b's entries lie
+      // in [e_{b-1}, e_{b+2}] (one bin of slack for the rounding of the
+      // binning), so
+      //   LB(k) = sum_{b >= k+2} n_b ((b-1-k) w)^beta <= F(e_k)
+      //   UB(k) = sum_{b >= k-1} n_b ((b+2-k) w)^beta >= F(e_k)
+      // (entries at or below lo add nothing at an edge e_k >= lo), written
+      // with suffix sums of n_b, n_b b, n_b b^2 in integers.  tau lies in
+      // [e_klo, e_khi]: klo the largest edge with LB >= 1 (else Lb), khi the
+      // smallest with UB <= 1 (1 -/+ 1e-9 for the final rounding).
+      for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = ld_agent(&ws.hist[(size_t)r * kBins + i]);
+      __syncthreads();
+      constexpr int kPer = kBins / kDThreads;
+      long long l0 = 0, l1 = 0, l2 = 0;
+      for (int u = 0; u < kPer; ++u) {
+        const long long bb = (long long)tid * kPer + u, n = sm.hist[bb];
+        l0 += n;
+        l1 += n * bb;
+        l2 += n * bb * bb;
+      }
+      unsigned long long t0_, t1_, t2_;
+      const long long q0 = (long long)block_excl_scan64((unsigned long long)l0, scan64, &t0_);
+      const long long q1 = (long long)block_excl_scan64((unsigned long long)l1, scan64, &t1_);
+      const long long q2 = (long long)block_excl_scan64((unsigned long long)l2, scan64, &t2_);
+      long long S0 = (long long)t0_ - q0, S1 = (long long)t1_ - q1, S2 = (long long)t2_ - q2;
+      const double wb = dp.ibeta == 2 ? hw * hw : hw;
+      int klo = -1, khi = 0x7fffffff;
+      auto nb = [&](long long bb) -> long long { return (bb >= 0 && bb < kBins) ? (long long)sm.hist[bb] : 0ll; };
+      const int kend = tid == kDThreads - 1 ? kPer + 1 : kPer;  // the last thread also takes edge kBins
+      for (int u = 0; u < kend; ++u) {
+        const long long k = (long long)tid * kPer + u;
+        const long long a0 = nb(k), a1 = nb(k + 1);
+        const long long T0 = S0 - a0 - a1, T1 = S1 - a0 * k - a1 * (k + 1);
+        const long long T2 = S2 - a0 * k * k - a1 * (k + 1) * (k + 1);
+        const long long mm = k > 0 ? k - 1 : 0, am = k > 0 ? nb(k - 1) : 0;
+        const long long U0 = S0 + am, U1 = S1 + am * mm, U2 = S2 + am * mm * mm;
+        double lb, ub;
+        if (dp.ibeta == 2) {
+          lb = (double)(T2 - 2 * (k + 1) * T1 + (k + 1) * (k + 1) * T0) * wb;
+          ub = (double)(U2 + 2 * (2 - k) * U1 + (2 - k) * (2 - k) * U0) * wb;
+        } else {
+          lb = (double)(T1 - (k + 1) * T0) * wb;
+          ub = (double)(U1 + (2 - k) * U0) * wb;
+        }
+        if (lb >= 1.0 + 1e-9) klo = max(klo, (int)k);
+        if (ub <= 1.0 - 1e-9) khi = min(khi, (int)k);
+        S0 -= a0;
+        S1 -= a0 * k;
+        S2 -= a0 * k * k;
+      }
+      klo = (int)block_max((double)klo, dred);
+      khi = (int)block_min_d((double)khi, dred);
+      if (tid == 0) {
+        const double e_lo = fmax(klo >= 0 ? hlo + (double)klo * hw : Lb, Lb);
+        const double e_hi = khi <= kBins ? hlo + (double)khi * hw : mx;
+        st_agent(&ws.rpar[(size_t)r * 8 + 3], e_lo);
+        st_agent(&ws.rpar[(size_t)r * 8 + 4], fmax(e_hi, e_lo));
+      }
+      EKV_MARK(1, 3);
+      publish_step(&ws.state[(size_t)r * kStStride], kStMom);
+    } else if (!all_small || mtot > kLastCap) {
+      // many candidates: passes over the row's entries by this block
+      double tau, z;
+      row_slow<T, DIM>(D, dp, ra, ws, r, sm, Lb, mx, rbase, dred, scan_scratch, scan64, nc, true, &tau, &z);
+      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+      return;
+    } else {
+      // ---- the compacted entries (16 consecutive per thread), those above
+      // Lb into LDS in index order, then tau and the gather
+      if (tid < nc) {
+        sm.start[tid] = (uint32_t)s_rec[tid][10];
+        sm.dense[tid] = 0;
+      }
+      if (tid == 0) {
+        int o = 0;
+        for (int cc = 0; cc < nc; ++cc) {
+          sm.off[cc] = o;
+          o += (int)s_rec[cc][0];
+        }
+        sm.off[nc] = o;
+      }
+      __syncthreads();
+      const Segs cs{sm.off, sm.start, sm.dense, nc, mtot, tok0};
+      {
+        const int k0 = kChunkPer * tid;
+        size_t ad[kChunkPer];
+        bool dn[kChunkPer];
+        cs.addr_run<kChunkPer>(k0, ad, dn);
+#pragma unroll
+        for (int u = 0; u < kChunkPer; ++u) {
+          xv[u] = nc > 1 ? ld_agent(&ws.cx[ad[u]]) : ws.cx[ad[u]];
+          tv[u] = nc > 1 ? ld_agent(&ws.ct[ad[u]]) : ws.ct[ad[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < kChunkPer; ++u)
+          if (k0 + u >= mtot || !(xv[u] > Lb)) xv[u] = -INFINITY;
+      }
+      row_finish<T, DIM>(D, dp, ra, ws, r, sm, xv, tv, mx, Lb, rbase, dred, scan_scratch, s_tau, &s_kstar);
+      return;
+    }
+  }
+  // ---- large row, every chunk: (a) moments above e_hi and the window entries
+  if (wait_step(&ws.state[(size_t)r * kStStride], kStMom, &s_flag) != kStMom) {
+    if (s_flag == 0u) row_nan<DIM>(ra, r);  // time limit
     return;
   }
   EKV_MARK(2, 0);
   if (tid < 8) s_par[tid] = ld_agent(&ws.rpar[(size_t)r * 8 + tid]);
-  const long long rbase = ws.rbase[r];
-  const int s0 = (int)((long long)j * ns / nh), s1 = (int)((long long)(j + 1) * ns / nh);
-  int nseg;
-  const int M = load_segs(ws, r, ns, s0, s1, sm.off, sm.start, sm.dense, red64, &nseg);
-  const Segs sg{sm.off, sm.start, sm.dense, nseg, M, (unsigned long long)rbase * (unsigned long long)D.P};
-  const double mx = s_par[0];
-  if (step == 0) {
-    // ---- histogram of the entries above mx - 1 over [lo, mx] in kBins bins
-    const double lo = s_par[1], w = s_par[2], thr = mx - 1.0;
-    for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = 0u;
-    __syncthreads();
-    Batch8 cur, nxt;
-    load_batch8(sg, ws, 8 * tid, false, cur);
-#pragma unroll 1
-    for (int base = 0; base < M; base += 8 * kDThreads) {
-      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (cur.v[u] > thr) {
-          const double f = floor((cur.v[u] - lo) / w);
-          const int bin = !(f >= 0.0) ? 0 : (f >= (double)kBins ? kBins - 1 : (int)f);
-          atomicAdd(&sm.hist[bin], 1u);
-        }
-      cur = nxt;
-    }
-    __syncthreads();
-    for (int i = tid; i < kBins; i += kDThreads)
-      if (sm.hist[i]) atomicAdd(&ws.hist[(size_t)r * kBins + i], sm.hist[i]);
-    if (!arrive_last(&ws.ctr[3 * r], (unsigned)nh, &s_last)) return;
-    // ---- the row's last helper: certified window.  Bin b's entries lie in
-    // [e_{b-1}, e_{b+2}] (one bin of slack for the rounding of the binning), so
-    //   LB(k) = sum_{b >= k+2} n_b ((b-1-k) w)^beta <= F(e_k)
-    //   UB(k) = sum_{b >= k-1} n_b ((b+2-k) w)^beta >= F(e_k),
-    // written with suffix sums of n_b, n_b b, n_b b^2 in integers.  tau lies in
-    // [e_klo, e_khi]: klo the largest edge with LB >= 1, khi the smallest with
-    // UB <= 1 (1 -/+ 1e-9 for the final rounding).
-    for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = ld_agent(&ws.hist[(size_t)r * kBins + i]);
-    __syncthreads();
-    constexpr int kPer = kBins / kDThreads;
-    long long l0 = 0, l1 = 0, l2 = 0;
-    for (int u = 0; u < kPer; ++u) {
-      const long long bb = (long long)tid * kPer + u, n = sm.hist[bb];
-      l0 += n;
-      l1 += n * bb;
-      l2 += n * bb * bb;
-    }
-    // suffix sums from this thread's first bin: totals minus the exclusive prefix
-    unsigned long long t0_, t1_, t2_;
-    const long long q0 = (long long)block_excl_scan64((unsigned long long)l0, red64, &t0_);
-    const long long q1 = (long long)block_excl_scan64((unsigned long long)l1, red64, &t1_);
-    const long long q2 = (long long)block_excl_scan64((unsigned long long)l2, red64, &t2_);
-    long long S0 = (long long)t0_ - q0, S1 = (long long)t1_ - q1, S2 = (long long)t2_ - q2;
-    const double wb = dp.ibeta == 2 ? w * w : w;
-    int klo = -1, khi = 0x7fffffff;
-    auto nb = [&](long long bb) -> long long { return (bb >= 0 && bb < kBins) ? (long long)sm.hist[bb] : 0ll; };
-    const int kend = tid == kDThreads - 1 ? kPer + 1 : kPer;  // the last thread also takes edge kBins
-    for (int u = 0; u < kend; ++u) {
-      const long long k = (long long)tid * kPer + u;
-      const long long a0 = nb(k), a1 = nb(k + 1);
-      // suffix at k + 2 and at max(k - 1, 0)
-      const long long T0 = S0 - a0 - a1, T1 = S1 - a0 * k - a1 * (k + 1);
-      const long long T2 = S2 - a0 * k * k - a1 * (k + 1) * (k + 1);
-      const long long m = k > 0 ? k - 1 : 0, am = k > 0 ? nb(k - 1) : 0;
-      const long long U0 = S0 + am, U1 = S1 + am * m, U2 = S2 + am * m * m;
-      double lb, ub;
-      if (dp.ibeta == 2) {
-        lb = (double)(T2 - 2 * (k + 1) * T1 + (k + 1) * (k + 1) * T0) * wb;
-        ub = (double)(U2 + 2 * (2 - k) * U1 + (2 - k) * (2 - k) * U0) * wb;
-      } else {
-        lb = (double)(T1 - (k + 1) * T0) * wb;
-        ub = (double)(U1 + (2 - k) * U0) * wb;
-      }
-      if (lb >= 1.0 + 1e-9) klo = max(klo, (int)k);
-      if (ub <= 1.0 - 1e-9) khi = min(khi, (int)k);
-      S0 -= a0;
-      S1 -= a0 * k;
-      S2 -= a0 * k * k;
-    }
-    klo = (int)block_max((double)klo, dred);
-    khi = (int)block_min_d((double)khi, dred);
-    if (tid == 0) {
-      const double e_lo = klo >= 0 ? lo + (double)klo * w : thr;
-      const double e_hi = khi <= kBins ? lo + (double)khi * w : mx;
-      st_agent(&ws.rpar[(size_t)r * 8 + 3], e_lo);
-      st_agent(&ws.rpar[(size_t)r * 8 + 4], fmax(e_hi, e_lo));
-    }
-    EKV_MARK(2, 1);
-    publish_step(&ws.state[r], kStMom);
-    return;
-  }
-  if (step == 1) {
-    // ---- moments above e_hi, window entries (e_lo, e_hi] into this helper's slot
-    const double e_lo = s_par[3], e_hi = s_par[4];
+  __syncthreads();
+  const double e_lo = s_par[3], e_hi = s_par[4];
+  {
     double m1 = 0.0, m2 = 0.0, ymin = INFINITY;
     int m0 = 0, wc = 0;
-    double *slot = ws.wbuf + ((size_t)r * kHelpers + j) * kSlot;
+    double *slot = ws.wbuf + ((size_t)r * kHelpers + c) * kSlot;
     Batch8 cur, nxt;
     load_batch8(sg, ws, 8 * tid, false, cur);
 #pragma unroll 1
@@ -1598,32 +1857,33 @@ __device__ void row_helper(const Dims &D, const DecodeParams &dp, const RowsArgs
     block_sum_n<3>(sums, dred);
     ymin = block_min_d(ymin, dred);
     if (tid == 0) {
-      double *hp = ws.hpart + ((size_t)r * kHelpers + j) * 8;
+      double *hp = ws.hpart + ((size_t)r * kHelpers + c) * 8;
       st_agent(&hp[0], sums[0]);
       st_agent(&hp[1], sums[1]);
       st_agent(&hp[2], sums[2]);
       st_agent(&hp[3], ymin);
       st_agent(&hp[4], (double)wc);
     }
-    if (!arrive_last(&ws.ctr[3 * r + 1], (unsigned)nh, &s_last)) return;
-    // ---- the row's last helper: tau from the moments and the window entries
-    if (tid < nh)
-      for (int c = 0; c < 5; ++c) s_hp[tid][c] = ld_agent(&ws.hpart[((size_t)r * kHelpers + tid) * 8 + c]);
+  }
+  if (arrive_last(&ws.ctr[4 * r + 1], (unsigned)nc, &s_last)) {
+    // the row's last: tau from the moments and the window entries
+    if (tid < nc)
+      for (int f = 0; f < 5; ++f) s_hp[tid][f] = ld_agent(&ws.hpart[((size_t)r * kHelpers + tid) * 8 + f]);
     __syncthreads();
     if (tid == 0) {
       double a0 = 0.0, a1 = 0.0, a2 = 0.0, amin = INFINITY;
       int off = 0, ovf = 0;
-      for (int h = 0; h < nh; ++h) {
+      for (int h = 0; h < nc; ++h) {
         a0 += s_hp[h][0];
         a1 += s_hp[h][1];
         a2 += s_hp[h][2];
         amin = fmin(amin, s_hp[h][3]);
         s_woff[h] = off;
-        const int c = (int)s_hp[h][4];
-        ovf |= c > kSlot ? 1 : 0;
-        off += c;
+        const int cnt_h = (int)s_hp[h][4];
+        ovf |= cnt_h > kSlot ? 1 : 0;
+        off += cnt_h;
       }
-      s_woff[nh] = off;
+      s_woff[nc] = off;
       s_ovf = ovf | (off > kWin ? 1 : 0);
       s_par[5] = a0;
       s_par[6] = a1;
@@ -1632,12 +1892,11 @@ __device__ void row_helper(const Dims &D, const DecodeParams &dp, const RowsArgs
     }
     __syncthreads();
     const Above ab{s_par[5], s_par[6], s_par[7], s_amin, e_hi};
-    const int W = s_woff[nh];
+    const int W = s_woff[nc];
     const bool ovf = s_ovf != 0;
-    __syncthreads();
     double tau, z;
     if (!ovf) {
-      for (int h = 0; h < nh; ++h) {
+      for (int h = 0; h < nc; ++h) {
         const int n = s_woff[h + 1] - s_woff[h];
         for (int i = tid; i < n; i += kDThreads)
           sm.win[s_woff[h] + i] = ld_agent(&ws.wbuf[((size_t)r * kHelpers + h) * kSlot + i]);
@@ -1646,55 +1905,52 @@ __device__ void row_helper(const Dims &D, const DecodeParams &dp, const RowsArgs
       solve_block(LdsVals{sm.win, W, tid, kDThreads}, ab, e_lo, e_hi, dp, dred, tau, z);
     } else {
       // window too wide for the slots: passes over every entry of the row
-      const int N = load_segs(ws, r, ns, 0, ns, sm.off, sm.start, sm.dense, red64, &nseg);
-      const Segs whole{sm.off, sm.start, sm.dense, nseg, N, (unsigned long long)rbase * (unsigned long long)D.P};
-      row_slow<T, DIM>(D, dp, ra, ws, r, sm, whole, e_lo, e_hi, rbase, dred, scan_scratch, false, &tau, &z);
+      // (this block's table is rebuilt by the pass and restored below)
+      row_slow<T, DIM>(D, dp, ra, ws, r, sm, e_lo, e_hi, rbase, dred, scan_scratch, scan64, nc, false, &tau, &z);
+      const Segs again = chunk_segs(ws, r, ns, c, rbase, D.P, sm.off, sm.start, sm.dense, scan64);
+      (void)again;
     }
     if (tid == 0) {
       st_agent(&ws.rpar[(size_t)r * 8 + 5], tau);
       st_agent(&ws.rpar[(size_t)r * 8 + 6], z);
       if (ra.tau) ra.tau[r] = tau / dp.a;
     }
-    EKV_MARK(2, 2);
-    publish_step(&ws.state[r], kStGath);
+    EKV_MARK(2, 1);
+    publish_step(&ws.state[(size_t)r * kStStride], kStGath);
+  }
+  // ---- (b) the support gather of this chunk; the last sums the partial
+  // outputs in chunk order
+  if (wait_step(&ws.state[(size_t)r * kStStride], kStGath, &s_flag) != kStGath) {
+    if (s_flag == 0u) row_nan<DIM>(ra, r);
     return;
   }
-  // ---- step 2: the support gather of this helper's entries; the last helper
-  // sums the partial outputs in helper order
+  if (tid < 8) s_par[tid] = ld_agent(&ws.rpar[(size_t)r * 8 + tid]);
+  __syncthreads();
   Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, s_par[5], s_par[6]);
-  gather_entries<T, DIM>(ga, sg, ws, ws.opart + ((size_t)r * kHelpers + j) * DIM, true);
-  if (!arrive_last(&ws.ctr[3 * r + 2], (unsigned)nh, &s_last)) return;
-  for (int c = tid; c < DIM; c += kDThreads) {
-    float s = ld_agent(&ws.opart[((size_t)r * kHelpers) * DIM + c]);
-    for (int h = 1; h < nh; ++h) s += ld_agent(&ws.opart[((size_t)r * kHelpers + h) * DIM + c]);
-    ra.out[(size_t)r * DIM + c] = s;
+  gather_entries<T, DIM>(ga, sg, ws, ws.opart + ((size_t)r * kHelpers + c) * DIM, true);
+  if (!arrive_last(&ws.ctr[4 * r + 2], (unsigned)nc, &s_last)) return;
+  for (int cc = tid; cc < DIM; cc += kDThreads) {
+    float sum = ld_agent(&ws.opart[((size_t)r * kHelpers) * DIM + cc]);
+    for (int h = 1; h < nc; ++h) sum += ld_agent(&ws.opart[((size_t)r * kHelpers + h) * DIM + cc]);
+    ra.out[(size_t)r * DIM + cc] = sum;
   }
-  EKV_MARK(2, 3);
-  publish_step(&ws.state[r], kStDone);
+  EKV_MARK(2, 2);
+  publish_step(&ws.state[(size_t)r * kStStride], kStDone);
 }
 
-// Block index: [0, rows) leaders; then the helpers of step 0, 1, 2, each
-// rows x nh blocks ordered by (row, helper).
+// Block index: row r's blocks are r * nh .. r * nh + nh - 1.
 template <typename T, int DIM>
 __global__ __launch_bounds__(kDThreads) void rows_kernel(Dims D, DecodeParams dp, RowsArgs ra, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RowsLds<T, DIM> &sm = *reinterpret_cast<RowsLds<T, DIM> *>(smem_raw);
   const int rows = D.B * D.Hq;
   const int bid = blockIdx.x;
-  if (bid < rows) {
-    row_leader<T, DIM>(D, dp, ra, ws, bid, sm);
-    return;
-  }
-  const int k = bid - rows;
-  const int per = rows * ra.nh;
-  const int step = k / per, rem = k % per;
-  row_helper<T, DIM>(D, dp, ra, ws, step, rem / ra.nh, rem % ra.nh, sm);
+  if (bid < rows * ra.nh) row_block<T, DIM>(D, dp, ra, ws, bid / ra.nh, bid % ra.nh, sm);
 }
 
 // =================================================================== launchers
 static int decode_slices(const Dims &D) {
-  const long long groups = (long long)D.B * D.Hkv;
-  long long ns = (1024 + groups - 1) / groups;  // about 1024 score blocks (4 per CU)
+  long long ns = (D.max_pages + 127) / 128;  // about 128 pages per slice
   ns = std::max(ns, (long long)((D.max_pages + kMaxR - 1) / kMaxR));
   ns = std::min(ns, (long long)std::max(1, D.max_pages));
   ns = std::min(ns, (long long)kMaxSlices);
@@ -1716,9 +1972,10 @@ static DecodeWs carve_decode(const Dims &D, int ns, long long item_cap, void *ba
   w.s_dense = cv.take<int>(rows * ns);
   w.rbase = cv.take<long long>(rows);
   w.rcnt = cv.take<int>(rows);
-  w.state = cv.take<unsigned>(rows);
-  w.ctr = cv.take<unsigned>(rows * 3);
+  w.state = cv.take<unsigned>(rows * kStStride);
+  w.ctr = cv.take<unsigned>(rows * 4);
   w.rpar = cv.take<double>(rows * 8);
+  w.crec = cv.take<double>(rows * kHelpers * 16);
   w.hist = cv.take<unsigned>(rows * kBins);
   w.hpart = cv.take<double>(rows * kHelpers * 8);
   w.wbuf = cv.take<double>(rows * kHelpers * kSlot);
@@ -1775,10 +2032,11 @@ static hipError_t launch_dec_t(const Dims &D, const DecodeParams &dp, const KsAr
     (void)hipFuncSetAttribute((const void *)rows_kernel<T, DIM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  // helpers per row and step: about 1024 blocks per step in all
-  const int nh = std::max(1, std::min(std::min(kHelpers, ka.ns), (1024 + rows - 1) / rows));
+  // blocks per row (chunks at most): about 512 blocks in all, one per slot
+  // of the GPU at this kernel's occupancy
+  const int nh = std::max(1, std::min(std::min(kHelpers, ka.ns), 512 / std::max(1, rows)));
   RowsArgs ra{v_pool, out, tau, ka.weights_out, ka.ns, nh};
-  const long long grid = (long long)rows * (1 + 3 * ra.nh);
+  const long long grid = (long long)rows * nh;
   hipLaunchKernelGGL((rows_kernel<T, DIM>), dim3((unsigned)grid), dim3(kDThreads), lds, s, D, dp, ra, w);
   return hipGetLastError();
 }
