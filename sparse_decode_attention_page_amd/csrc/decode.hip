@@ -50,7 +50,6 @@ namespace ekv {
 constexpr int kDThreads = 256;
 constexpr int kMaxSlices = 1024;  // slices per (b, g) at most
 constexpr int kMaxR = 512;        // pages per slice at most (the page map of scores_kernel)
-constexpr int kLeadMax = 16384;   // entries a leader streams over (more: the helpers)
 constexpr int kCand = 1024;       // candidates in LDS for the one-wave solve and the sort form
 constexpr int kNThr = 8;          // count thresholds mx - 2^-i behind the certified bound on tau
 constexpr int kHelpers = 32;      // helper blocks per row and step, at most
@@ -58,7 +57,6 @@ constexpr int kBins = 4096;       // histogram bins of a large row
 constexpr int kSlot = 128;        // window entries a helper hands over
 constexpr int kWin = 4096;        // window entries the solving helper keeps in LDS
 constexpr int kWbuf = kHelpers * kSlot;  // candidates a leader keeps in its window buffer
-constexpr int kIprLds = 2048;     // a row's item -> physical page table staged in LDS up to this size
 constexpr unsigned kStHist = 2, kStMom = 3, kStGath = 4, kStDone = 0xFFu;  // row steps (0: scores written)
 constexpr unsigned long long kSpinTicks = 20000000ull;                     // 0.2 s of the 100 MHz clock
 constexpr int kLargeN = 32768;  // rows with more entries take the histogram route
@@ -66,16 +64,13 @@ constexpr int kStStride = 32;  // row step flags 128 bytes apart, so waiting blo
 
 struct DecodeWs {
   double *cx;         // [cap_tok]  entry X
-  uint32_t *ct;       // [cap_tok]  token id (item * P + slot) of a compact entry
-  uint32_t *iphys;    // [item_cap] physical page of an item
-  uint32_t *ipage;    // [item_cap] logical page of an item
+  uint32_t *ct;       // [cap_tok]  the entry's V row: (physical page * Hkv + g) * P + slot
+  uint32_t *cl;       // [cap_tok]  its logical position page * P + slot (written for weights_out only)
   int *s_cnt;         // [rows][ns] entries stored for the slice
   double *s_max;      // [rows][ns] max X over the slice's kept tokens (-inf: none; NaN: malformed)
   double *s_min;      // [rows][ns] min X over the slice's kept tokens (+inf: none)
   uint32_t *s_start;  // [rows][ns] index in cx of the slice's first entry
-  int *s_dense;       // [rows][ns] 1: the entries are every kept token, in place
-  long long *rbase;   // [rows] first item of the row
-  int *rcnt;          // [rows] items of the row
+  int *rcnt;          // [rows] items of the row (entries at most rcnt * P)
   unsigned *state;    // [rows][kStStride] step of a large row (one 128-byte line per row)
   unsigned *ctr;      // [rows][4] arrival counters of the helper steps and of the chunks
   double *rpar;       // [rows][8] published parameters (mx, lo, w, e_lo, e_hi, tau, z)
@@ -124,6 +119,7 @@ __device__ __forceinline__ double wave_min_d(double v) { return -wave_max(-v); }
 __device__ __forceinline__ double block_min_d(double v, double *scratch) { return -block_max(-v, scratch); }
 
 // Exclusive prefix sum over a block of a 64-bit value (fixed order).
+template <bool kLdsOnly = false>
 __device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long long v, unsigned long long *scratch,
                                                                 unsigned long long *total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
@@ -133,9 +129,9 @@ __device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long lo
     const unsigned long long y = __shfl_up(x, o, kWave);
     if (lane >= o) x += y;
   }
-  __syncthreads();
+  block_sync<kLdsOnly>();
   if (lane == kWave - 1) scratch[w] = x;
-  __syncthreads();
+  block_sync<kLdsOnly>();
   unsigned long long base = 0, tot = 0;
   for (int i = 0; i < nw; ++i) {
     if (i < w) base += scratch[i];
@@ -185,7 +181,7 @@ __device__ __forceinline__ void wave_bounds(const int32_t *list, int n, int key1
 }
 
 // =========================================================== 1. scores kernel
-constexpr int kXl = 4096;  // X values a scores block stages in LDS (a slice whose union fits is compacted)
+constexpr int kXl = 2048;  // X values a scores block stages in LDS (a batch of union pages)
 
 // 16 consecutive K coordinates as loaded (two or four 16-byte loads), unpacked
 // to floats where they are used
@@ -243,7 +239,8 @@ __device__ __forceinline__ int ks_row_items(const Dims &D, const KsArgs &a, int 
 }
 
 template <typename T, int DIM, int P, int G>
-__global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
+__global__ __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   constexpr int kParts = DIM / 16;                            // threads per token, 16 coordinates each
   constexpr int kUpp = P * kParts;                            // (token, part) units per page
   constexpr int kTpp = kUpp < kDThreads ? kUpp : kDThreads;   // threads per page
@@ -252,9 +249,9 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
   constexpr int kLdsPages = kXl / (P * G);                   // union pages whose X fits the LDS stage
   static_assert(kTpp % kWave == 0, "a page's threads form whole waves");
   __shared__ unsigned umask[kMaxR];
-  __shared__ int upos[G][kMaxR];
   __shared__ int ulist[kMaxR];
   __shared__ uint32_t uphys[kMaxR];
+  __shared__ int ptab[kMaxR];  // the slice's page-table entries
   __shared__ int s_lo[G], s_hi[G];
   __shared__ long long s_base[G];
   __shared__ int s_items[G];
@@ -266,7 +263,6 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
   __shared__ unsigned long long scan64[kDThreads / kWave];
   __shared__ __align__(16) float qs[G][DIM];
   __shared__ double xl[kXl];
-  __shared__ double s_thr[G];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int ns = a.ns;
   const int gi = blockIdx.x / ns, s = blockIdx.x % ns;
@@ -280,6 +276,13 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
   const T *q = (const T *)a.q;
   const T *k_pool = (const T *)a.k_pool;
   EKV_MARK(0, 0);
+  // the slice's page-table entries, loaded beside the selection counts below
+  int ptv[kMaxR / kDThreads];
+#pragma unroll
+  for (int i = 0; i < kMaxR / kDThreads; ++i) {
+    const int o = tid + i * kDThreads;
+    ptv[i] = (o < R && p0 + o < np) ? a.page_table[(size_t)b * MP + p0 + o] : -1;
+  }
 
   // ---- the group's rows: first item (items of every earlier row), counts
   long long part = 0;
@@ -326,13 +329,15 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
     }
   }
   for (int o = tid; o < R; o += kDThreads) umask[o] = 0u;
+#pragma unroll
+  for (int i = 0; i < kMaxR / kDThreads; ++i) {
+    const int o = tid + i * kDThreads;
+    if (o < R) ptab[o] = ptv[i];
+  }
   __syncthreads();
   if (a.mode == 2) {
     for (int o = tid; o < R; o += kDThreads)
-      if (p0 + o < np) {
-        umask[o] = all;
-        upos[0][o] = p0 + o;
-      }
+      if (p0 + o < np) umask[o] = all;
   } else {
     for (int li = wv; li < nl; li += kDThreads / kWave) {
       const int32_t *list = a.sel_idx + (size_t)(a.mode == 0 ? r0 + li : gi) * MP;
@@ -347,7 +352,6 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
           continue;
         }
         atomicOr(&umask[o], a.mode == 0 ? (1u << li) : all);
-        upos[li][o] = i;
       }
       if (__any(bad) && lane == 0) atomicOr(&s_bad, a.mode == 0 ? (1u << li) : all);
     }
@@ -368,25 +372,13 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
   const int nU = (int)s_nu;
   for (int k = tid; k < nU; k += kDThreads) {
     const int o = ulist[k];
-    const int ph = a.page_table[(size_t)b * MP + p0 + o];
+    const int ph = ptab[o];
     const bool ok = ph >= 0 && ph < D.num_phys;
     uphys[k] = ok ? (uint32_t)ph : 0u;
     if (!ok) atomicOr(&s_bad, umask[o]);
   }
   __syncthreads();
   const unsigned live = all & ~s_bad;
-  // per-item physical and logical pages of the rows' items in this slice
-  for (int k = tid; k < nU; k += kDThreads) {
-    const int o = ulist[k];
-    const unsigned m = umask[o] & live;
-    for (int h = 0; h < G; ++h)
-      if (m & (1u << h)) {
-        const int item = upos[a.mode == 0 ? h : 0][o];
-        const size_t idx = (size_t)(s_base[h] + item);
-        ws.iphys[idx] = uphys[k];
-        ws.ipage[idx] = (uint32_t)(p0 + o);
-      }
-  }
   // weights_out: every slot of the slice's pages (the last slice to the end of
   // the row) is zeroed here; rows_kernel writes the support
   if (a.weights_out) {
@@ -399,8 +391,7 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
   // row bookkeeping of the rows_kernel (once per row)
   if (s == 0 && tid < G) {
     const int r = r0 + tid;
-    ws.rbase[r] = s_base[tid];
-    ws.rcnt[r] = s_items[tid];
+    ws.rcnt[r] = (s_bad >> tid) & 1u ? 0 : s_items[tid];
     ws.state[(size_t)r * kStStride] = 0u;
     ws.ctr[4 * r] = 0u;
     ws.ctr[4 * r + 1] = 0u;
@@ -413,7 +404,7 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
       for (int i = tid; i < kBins; i += kDThreads) ws.hist[(size_t)(r0 + h) * kBins + i] = 0u;
   EKV_MARK(0, 1);
 
-  // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
+  // ---- q of the group's heads in LDS
   const int j = tid / kTpp, u0 = tid % kTpp, e = u0 % kParts;
   for (int i = tid; i < G * DIM; i += kDThreads) qs[i / DIM][i % DIM] = load_f(q, (size_t)r0 * DIM + i);
   __syncthreads();
@@ -424,9 +415,13 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
     lmax[h] = -INFINITY;
     lmin[h] = INFINITY;
   }
-  // compact when the union's X fits the LDS stage, else the dense layout
-  const bool dense = nU > kLdsPages;
-  auto item_of = [&](int h, int o) __attribute__((always_inline)) { return upos[a.mode == 0 ? h : 0][o]; };
+  // union pages in batches of kLdsPages, whose X fits the LDS stage; after a
+  // batch, each head's running max takes in the batch and the batch's entries
+  // above (running max) - 1 are appended to the head's entries (token ids
+  // explicit).  The running max never exceeds the slice max, so the stored
+  // entries hold every entry above (slice max) - 1, in index order.
+  static_assert(kLdsPages % kPpi == 0, "a batch is whole passes");
+  constexpr int kPpb = kLdsPages / kPpi;  // passes per batch
   auto lo_of = [&](int h) __attribute__((always_inline)) { return s_lo[a.mode == 0 ? h : 0]; };
   auto load_pass = [&](int pass, KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
     const int k = pass * kPpi + j;
@@ -440,10 +435,11 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
     }
   };
   // X of one pass (-inf for heads that did not keep the page and for slots
-  // past the sequence end) into the LDS stage or the dense layout
+  // past the sequence end) into the LDS stage at the batch's page position
   auto score_pass = [&](int pass, const KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
     const int k = pass * kPpi + j;
     const bool act = k < nU;
+    const int kl = k % kLdsPages;
     const int o = act ? ulist[k] : 0;
     const unsigned m = act ? (umask[o] & live) : 0u;
     const int ntok = min(P, L - (p0 + o) * P);
@@ -472,13 +468,76 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
         }
         lmax[h] = fmax(lmax[h], x);
         if (x > -INFINITY) lmin[h] = fmin(lmin[h], x);
-        if (act && e == 0) {
-          if (!dense) xl[(k * P + t) * G + h] = x;
-          else if (m & (1u << h)) ws.cx[(size_t)(s_base[h] + item_of(h, o)) * P + t] = x;
-        }
+        if (act && e == 0) xl[(kl * P + t) * G + h] = x;
       }
     }
   };
+  // a finished batch: running max, then the batch's entries above it - 1
+  int ncnt[G];
+  double rmax[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ncnt[h] = 0;
+    rmax[h] = -INFINITY;
+  }
+  // the batch of union pages from kb0: each thread takes kTpt consecutive
+  // tokens of the stage, every head; one packed scan per four heads places
+  // the entries
+  constexpr int kTpt = kXl / G / kDThreads;  // stage tokens per thread
+  static_assert(kTpt * G * kDThreads == kXl, "the stage splits evenly");
+  auto compact_batch = [&](int kb0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const double wm = wave_max(lmax[h]);
+      if (lane == 0) s_red[wv][h] = wm;
+    }
+    lds_barrier();  // also orders the batch's LDS stage writes before the reads below
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      double mm = s_red[0][h];
+      for (int w = 1; w < kDThreads / kWave; ++w) mm = fmax(mm, s_red[w][h]);
+      rmax[h] = mm;  // lmax is each thread's max so far
+    }
+    const int tk0 = tid * kTpt;
+    auto xat = [&](int i, int h) __attribute__((always_inline)) {
+      return kb0 + (tk0 + i) / P < nU ? xl[(tk0 + i) * G + h] : -INFINITY;
+    };
+    unsigned long long pk[(G + 3) / 4];
+#pragma unroll
+    for (int q = 0; q < (G + 3) / 4; ++q) pk[q] = 0ull;
+#pragma unroll
+    for (int i = 0; i < kTpt; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (xat(i, h) > rmax[h] - 1.0) pk[h / 4] += 1ull << (16 * (h % 4));
+#pragma unroll
+    for (int q = 0; q < (G + 3) / 4; ++q) {
+      unsigned long long tot;
+      const unsigned long long pre = block_excl_scan64<true>(pk[q], scan64, &tot);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const int h = 4 * q + hh;
+        if (h < G) {
+          size_t at = (size_t)(s_base[h] + lo_of(h)) * P + ncnt[h] + (int)((pre >> (16 * hh)) & 0xFFFFull);
+#pragma unroll
+          for (int i = 0; i < kTpt; ++i) {
+            const double x = xat(i, h);
+            if (x > rmax[h] - 1.0) {
+              const int k = kb0 + (tk0 + i) / P, t = (tk0 + i) % P;
+              ws.cx[at] = x;
+              ws.ct[at] = (uphys[k] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)t;
+              if (a.weights_out) ws.cl[at] = (uint32_t)((p0 + ulist[k]) * P + t);
+              ++at;
+            }
+          }
+          ncnt[h] += (int)((tot >> (16 * hh)) & 0xFFFFull);
+        }
+      }
+    }
+    lds_barrier();  // the stage is read before the next batch overwrites it
+  };
+
+  // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
   KRaw<T> ka0[kUpt], ka1[kUpt], ka2[kUpt];
   if (npass > 0) load_pass(0, ka0);
   if (npass > 1) load_pass(1, ka1);
@@ -491,6 +550,7 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
       ka0[u] = ka1[u];
       ka1[u] = ka2[u];
     }
+    if ((pass + 1) % kPpb == 0 || pass + 1 == npass) compact_batch((pass - pass % kPpb) * kPpi);
   }
   // slice max / min per head
 #pragma unroll
@@ -513,63 +573,17 @@ __global__ __launch_bounds__(kDThreads) void scores_kernel(Dims D, DecodeParams 
     }
     s_mx[tid] = m;
     s_mn[tid] = n;
-    s_thr[tid] = m - 1.0;  // every candidate of the row (X > row max - 1) is above it
   }
   __syncthreads();
-  int ncnt[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) ncnt[h] = 0;
-  if (!dense) {
-    // compaction: the entries X > (slice max) - 1 of each head in index
-    // order, four heads per packed 64-bit scan (16-bit counts)
-#pragma unroll 1
-    for (int pass = 0; pass < npass; ++pass) {
-      const int k = pass * kPpi + j;
-      const bool act = k < nU;
-      const int o = act ? ulist[k] : 0;
-#pragma unroll
-      for (int u = 0; u < kUpt; ++u) {
-        const int t = (u0 + u * kTpp) / kParts;
-#pragma unroll
-        for (int h0 = 0; h0 < G; h0 += 4) {
-          double xo[4];
-          unsigned long long mine = 0;
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            xo[hh] = (h0 + hh < G && act && e == 0) ? xl[(k * P + t) * G + h0 + hh] : -INFINITY;
-            if (h0 + hh < G && xo[hh] > s_thr[h0 + hh]) mine |= 1ull << (16 * hh);
-          }
-          unsigned long long tot;
-          const unsigned long long pre = block_excl_scan64(mine, scan64, &tot);
-#pragma unroll
-          for (int hh = 0; hh < 4; ++hh) {
-            const int h = h0 + hh;
-            if (h < G) {
-              if ((mine >> (16 * hh)) & 1ull) {
-                const size_t at = (size_t)(s_base[h] + lo_of(h)) * P + ncnt[h] + (int)((pre >> (16 * hh)) & 0xFFFFull);
-                ws.cx[at] = xo[hh];
-                ws.ct[at] = (uint32_t)(item_of(h, o) * P + t);
-              }
-              ncnt[h] += (int)((tot >> (16 * hh)) & 0xFFFFull);
-            }
-          }
-        }
-      }
-    }
-  }
   // ---- per (row, slice) summary
   if (tid < G) {
     const int h = tid, r = r0 + h;
     const bool bad = (s_bad >> h) & 1u;
-    const int lo = lo_of(h), hi = s_hi[a.mode == 0 ? h : 0];
     const size_t o = (size_t)r * ns + s;
-    int c = 0;
-    if (!bad) c = dense ? (hi - lo) * P : ncnt[h];
-    ws.s_cnt[o] = c;
+    ws.s_cnt[o] = bad ? 0 : ncnt[h];
     ws.s_max[o] = bad ? NAN : s_mx[h];
     ws.s_min[o] = s_mn[h];
-    ws.s_start[o] = bad ? 0u : (uint32_t)((s_base[h] + lo) * P);
-    ws.s_dense[o] = dense ? 1 : 0;
+    ws.s_start[o] = bad ? 0u : (uint32_t)((s_base[h] + lo_of(h)) * P);
   }
   EKV_MARK(0, 2);
 }
@@ -583,130 +597,94 @@ struct RowsArgs {
   int ns, nh;  // slices per row; blocks (chunks at most) per row
 };
 
-// The entries of a run of slices, concatenated in index order; the slice
-// tables sit in LDS.  Entry k of slice i is cx[start[i] + k - off[i]]; its
-// token id is ct[...] for a compact slice and the offset from the row's first
-// token for a dense one.
+// The entries of a run of slices, concatenated in index order, by a window
+// [off, off + n] of an LDS table of entry offsets (ascending; off[0] may be
+// nonzero) and first positions: entry k of the run is slice i's entry
+// k + off[0] - off[i], at cx[start[i] + k + off[0] - off[i]] (its V row at ct,
+// its position at cl, same index).
 struct Segs {
-  const int *off;           // [n + 1]
-  const uint32_t *start;    // [n]
-  const int *dense;         // [n]
-  int n, total;
-  unsigned long long tok0;  // rbase * P
+  const int *off;         // [n + 1]
+  const uint32_t *start;  // [n]
+  int n, total, e0;
   __device__ __forceinline__ int seg_of(int k) const {
     int lo = 0, hi = n - 1;  // last slice starting at or before k
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= k) lo = mid; else hi = mid - 1;
+      if (off[mid] - e0 <= k) lo = mid; else hi = mid - 1;
     }
     return lo;
   }
-  // addresses of entries min(k0 + u, total - 1), u < R: one search, then the
-  // slice advances with k (empty slices are stepped over)
+  // addresses of entries min(k0 + u, total - 1), u < R (total > 0): one
+  // search, then the slice advances with k (empty slices are stepped over)
   template <int R>
-  __device__ __forceinline__ void addr_run(int k0, size_t (&ad)[R], bool (&dn)[R]) const {
+  __device__ __forceinline__ void addr_run(int k0, size_t (&ad)[R]) const {
     int lo = seg_of(min(k0, total - 1));
-    int next = lo + 1 < n ? off[lo + 1] : 0x7fffffff;
+    int next = lo + 1 < n ? off[lo + 1] - e0 : 0x7fffffff;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int k = min(k0 + u, total - 1);
       while (k >= next) {
         ++lo;
-        next = lo + 1 < n ? off[lo + 1] : 0x7fffffff;
+        next = lo + 1 < n ? off[lo + 1] - e0 : 0x7fffffff;
       }
-      ad[u] = (size_t)start[lo] + (size_t)(k - off[lo]);
-      dn[u] = dense[lo] != 0;
+      ad[u] = (size_t)start[lo] + (size_t)(k + e0 - off[lo]);
     }
-  }
-  __device__ __forceinline__ uint32_t tok_of(const DecodeWs &ws, size_t ad, bool dn) const {
-    return dn ? (uint32_t)(ad - tok0) : ws.ct[ad];
   }
 };
+// entries k0 + u * kDThreads, u < R (those past the end: the last entry),
+// each found by its own fixed-step search of the table, all R side by side
+template <int R>
+__device__ __forceinline__ void addr_strided(const Segs &sg, int k0, size_t (&ad)[R]) {
+  int lo[R], kk[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    lo[u] = 0;
+    kk[u] = min(k0 + u * kDThreads, sg.total - 1) + sg.e0;
+  }
+  int step = 1;
+  while (2 * step < sg.n) step <<= 1;
+#pragma unroll 1
+  for (; step > 0; step >>= 1) {
+    int v[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) v[u] = sg.off[min(lo[u] + step, sg.n - 1)];  // every read issued first
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const bool go = (lo[u] + step < sg.n) & (v[u] <= kk[u]);  // no short circuit: the reads stay unconditional
+      lo[u] += go ? step : 0;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < R; ++u) ad[u] = (size_t)sg.start[lo[u]] + (size_t)(kk[u] - sg.off[lo[u]]);
+}
 
-// Slice tables of the non-empty slices among [s0, s1) of row r into LDS (one
-// packed 64-bit scan gives both the entry offsets and the table positions);
-// returns the entry total, *nseg the number of tables.  With mxmn, also the
-// max and min of the slices' X over this thread's slices and a NaN mark.
-__device__ __forceinline__ int load_segs(const DecodeWs &ws, int r, int ns, int s0, int s1, int *off, uint32_t *start,
-                                         int *dense, unsigned long long *scan64, int *nseg, double *mxmn = nullptr,
-                                         int *nan = nullptr) {
-  const int n = s1 - s0;
-  constexpr int kMaxPer = (kMaxSlices + kDThreads - 1) / kDThreads;
-  const int per = (n + kDThreads - 1) / kDThreads;
-  const int i0 = threadIdx.x * per;
-  int c[kMaxPer];
-  uint32_t st[kMaxPer];
-  int dn[kMaxPer];
-  double mx = -INFINITY, mn = INFINITY;
-  int bad = 0;
-#pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    const int i = i0 + u;
-    c[u] = 0;
-    if (u < per && i < n) {
-      const size_t o = (size_t)r * ns + s0 + i;
-      c[u] = ws.s_cnt[o];
-      st[u] = ws.s_start[o];
-      dn[u] = ws.s_dense[o];
-      if (mxmn) {
-        const double v = ws.s_max[o];
-        bad |= v != v;
-        mx = fmax(mx, v);
-        mn = fmin(mn, ws.s_min[o]);
-      }
-    }
-  }
-  if (mxmn) {
-    mxmn[0] = mx;
-    mxmn[1] = mn;
-    *nan = bad;
-  }
-  unsigned long long mine = 0;
-#pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) mine += ((unsigned long long)(c[u] > 0 ? 1 : 0) << 32) + (unsigned)c[u];
-  unsigned long long tot;
-  unsigned long long run = block_excl_scan64(mine, scan64, &tot);
-#pragma unroll
-  for (int u = 0; u < kMaxPer; ++u) {
-    if (c[u] > 0) {
-      const int at = (int)(run >> 32);
-      off[at] = (int)(run & 0xFFFFFFFFull);
-      start[at] = st[u];
-      dense[at] = dn[u];
-      run += (1ull << 32) + (unsigned)c[u];
-    }
-  }
-  const int ntab = (int)(tot >> 32), total = (int)(tot & 0xFFFFFFFFull);
-  if (threadIdx.x == 0) {
-    off[ntab] = total;
-    if (ntab == 0) {  // an empty run: one empty table keeps the lookups in range
-      off[0] = 0;
-      off[1] = 0;
-      start[0] = 0u;
-      dense[0] = 1;
-    }
-  }
-  __syncthreads();
-  *nseg = ntab > 0 ? ntab : 1;
-  return total;
+// the run of table entries [t0, t1) (the table visible to every thread)
+__device__ __forceinline__ Segs segs_window(const int *off, const uint32_t *start, int t0, int t1) {
+  Segs sg;
+  sg.off = off + t0;
+  sg.start = start + t0;
+  sg.n = t1 - t0;
+  sg.e0 = off[t0];
+  sg.total = off[t1] - sg.e0;
+  return sg;
 }
 
 // Eight consecutive entries per thread (X, and token ids when asked);
 // entries past the end read -inf.
 struct Batch8 {
   double v[8];
-  uint32_t t[8];
+  uint32_t t[8];  // V rows
 };
-__device__ __forceinline__ void load_batch8(const Segs &sg, const DecodeWs &ws, int k0, bool toks, Batch8 &bt) {
+__device__ __forceinline__ void load_batch8(const Segs &sg, const DecodeWs &ws, int k0, bool toks, bool agent,
+                                            Batch8 &bt) {
   if (k0 < sg.total) {
     size_t ad[8];
-    bool dn[8];
-    sg.addr_run<8>(k0, ad, dn);
+    sg.addr_run<8>(k0, ad);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) bt.v[u] = ws.cx[ad[u]];
+    for (int u = 0; u < 8; ++u) bt.v[u] = agent ? ld_agent(&ws.cx[ad[u]]) : ws.cx[ad[u]];
     if (toks)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) bt.t[u] = sg.tok_of(ws, ad[u], dn[u]);
+      for (int u = 0; u < 8; ++u) bt.t[u] = agent ? ld_agent(&ws.ct[ad[u]]) : ws.ct[ad[u]];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (k0 + u >= sg.total) bt.v[u] = -INFINITY;
@@ -742,17 +720,18 @@ struct RegVals16 {  // 16 values per thread (-inf for unused slots)
 struct GlobVals {  // every entry of a run of slices, 8 per thread in flight
   const DecodeWs *ws;
   const Segs *sg;
+  bool agent;       // entries another block of the launch may have rewritten
   template <typename Fn>
   __device__ __forceinline__ void each(Fn &&fn) const {
 #pragma unroll 1
     for (int base = 0; base < sg->total; base += 8 * kDThreads) {
       const int k0 = base + 8 * (int)threadIdx.x;
+      if (k0 >= sg->total) continue;
       size_t ad[8];
-      bool dn[8];
-      sg->addr_run<8>(k0, ad, dn);
+      sg->addr_run<8>(k0, ad);
       double v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ws->cx[ad[u]];
+      for (int u = 0; u < 8; ++u) v[u] = agent ? ld_agent(&ws->cx[ad[u]]) : ws->cx[ad[u]];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (k0 + u < sg->total) fn(v[u]);
@@ -964,15 +943,14 @@ __device__ __forceinline__ double sparsemax_tau_sort(const double *cx, int n, do
 
 // ------------------------------------------------------------- support gather
 // Support entries are placed in LDS by block scans (in the order they are
-// offered); a flush turns each token id into its V row (the item's physical
-// page) and accumulates p_t v_t: kEpp entries per pass with kTpe threads each
-// (8 coordinates per 16-byte load), fp32 in a fixed order.
+// offered); a flush accumulates p_t v_t over them: kEpp entries per pass with
+// kTpe threads each (8 coordinates per 16-byte load), fp32 in a fixed order.
 constexpr int kSupCap = 2048;  // support entries held in LDS between flushes
 template <typename T, int DIM>
 struct GatherLds {
   static constexpr int kTpe = DIM / 8;           // threads per support entry
   static constexpr int kEpp = kDThreads / kTpe;  // support entries per gather pass
-  uint32_t tok[kSupCap];  // token id, then V row
+  uint32_t vrow[kSupCap];
   float w[kSupCap];
   float accs[kEpp][DIM + 1];
 };
@@ -984,28 +962,14 @@ struct Gather {
   GatherLds<T, DIM> *sh;
   int *scan_scratch;
   const T *v_pool;
-  const DecodeWs *ws;
-  long long rbase;
-  const uint32_t *ipr;  // LDS copy of the row's item -> physical page table (nullptr: read ws->iphys)
-  int P, Hkv, g;
-  float *wrow;          // weights_out row (nullable)
   double tau, z;
   DecodeParams dp;
   int nsup;
   float acc8[8];
 
   __device__ __forceinline__ void flush() {
-    __syncthreads();
-    const int tid = threadIdx.x;
-    for (int k = tid; k < nsup; k += kDThreads) {
-      const uint32_t t = sh->tok[k];
-      const uint32_t item = t / (uint32_t)P, slot = t % (uint32_t)P;
-      const uint32_t ph = ipr ? ipr[item] : ws->iphys[(size_t)rbase + item];
-      if (wrow) wrow[(size_t)ws->ipage[(size_t)rbase + item] * P + slot] = sh->w[k];
-      sh->tok[k] = (ph * (uint32_t)Hkv + (uint32_t)g) * (uint32_t)P + slot;
-    }
-    __syncthreads();
-    const int ge = tid / kTpe, gc = tid % kTpe;
+    lds_barrier();
+    const int tid = threadIdx.x, ge = tid / kTpe, gc = tid % kTpe;
     int e = ge;
     // eight entries per thread in flight, then four, two, one (the sum runs
     // over e, e + kEpp, e + 2 kEpp, ... in that order either way)
@@ -1013,7 +977,7 @@ struct Gather {
     for (; e + 7 * kEpp < nsup; e += 8 * kEpp) {
       float v[8][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) load_vec<8>(v_pool + (size_t)sh->tok[e + i * kEpp] * DIM + gc * 8, v[i]);
+      for (int i = 0; i < 8; ++i) load_vec<8>(v_pool + (size_t)sh->vrow[e + i * kEpp] * DIM + gc * 8, v[i]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float wi = sh->w[e + i * kEpp];
@@ -1023,10 +987,10 @@ struct Gather {
     }
     if (e + 3 * kEpp < nsup) {
       float v0[8], v1[8], v2[8], v3[8];
-      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
-      load_vec<8>(v_pool + (size_t)sh->tok[e + kEpp] * DIM + gc * 8, v1);
-      load_vec<8>(v_pool + (size_t)sh->tok[e + 2 * kEpp] * DIM + gc * 8, v2);
-      load_vec<8>(v_pool + (size_t)sh->tok[e + 3 * kEpp] * DIM + gc * 8, v3);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e + kEpp] * DIM + gc * 8, v1);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e + 2 * kEpp] * DIM + gc * 8, v2);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e + 3 * kEpp] * DIM + gc * 8, v3);
       const float w0 = sh->w[e], w1 = sh->w[e + kEpp], w2 = sh->w[e + 2 * kEpp], w3 = sh->w[e + 3 * kEpp];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
@@ -1040,8 +1004,8 @@ struct Gather {
     }
     if (e + kEpp < nsup) {
       float v0[8], v1[8];
-      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
-      load_vec<8>(v_pool + (size_t)sh->tok[e + kEpp] * DIM + gc * 8, v1);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e + kEpp] * DIM + gc * 8, v1);
       const float w0 = sh->w[e], w1 = sh->w[e + kEpp];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
@@ -1051,33 +1015,31 @@ struct Gather {
     }
     if (e < nsup) {
       float v0[8];
-      load_vec<8>(v_pool + (size_t)sh->tok[e] * DIM + gc * 8, v0);
+      load_vec<8>(v_pool + (size_t)sh->vrow[e] * DIM + gc * 8, v0);
       const float w0 = sh->w[e];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc8[u] += w0 * v0[u];
     }
-    __syncthreads();
+    lds_barrier();
     nsup = 0;
   }
-  // up to R entries of this thread (x, token id), consecutive in index order
+  // up to R entries of this thread (X, V row), consecutive in index order
   // (R * 256 <= kSupCap); one block scan places the block's support entries
   template <int R>
-  __device__ __forceinline__ void offer(const double (&x)[R], const uint32_t (&tk)[R]) {
-    static_assert(R * kDThreads <= kSupCap, "one offer fits the chunk");
+  __device__ __forceinline__ void offer(const double (&x)[R], const uint32_t (&vr)[R]) {
+    static_assert(R * kDThreads <= kSupCap, "one offer fits the buffer");
     int take = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) take += x[u] - tau > 0.0 ? 1 : 0;
     int tot;
     int at = block_excl_scan<true>(take, scan_scratch, &tot);  // loads issued before stay in flight
-    if (nsup + tot > kSupCap) {  // uniform
-      flush();
-    }
+    if (nsup + tot > kSupCap) flush();                          // uniform
     at += nsup;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const double y = x[u] - tau;
       if (y > 0.0) {
-        sh->tok[at] = tk[u];
+        sh->vrow[at] = vr[u];
         sh->w[at] = (float)(pw_rt(y, dp) / z);
         ++at;
       }
@@ -1099,6 +1061,49 @@ struct Gather {
     }
   }
 };
+
+template <typename T, int DIM>
+__device__ __forceinline__ Gather<T, DIM> make_gather(GatherLds<T, DIM> *sh, int *scan_scratch, const DecodeParams &dp,
+                                                      const RowsArgs &ra, double tau, double z) {
+  Gather<T, DIM> ga;
+  ga.sh = sh;
+  ga.scan_scratch = scan_scratch;
+  ga.v_pool = (const T *)ra.v_pool;
+  ga.tau = tau;
+  ga.z = z;
+  ga.dp = dp;
+  ga.nsup = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) ga.acc8[u] = 0.0f;
+  return ga;
+}
+
+// Support gather over the entries of sg (eight per thread per step, the next
+// eight in flight); the block's partial output goes to dst.
+template <typename T, int DIM>
+__device__ __forceinline__ void gather_entries(Gather<T, DIM> &ga, const Segs &sg, const DecodeWs &ws, bool agent) {
+  Batch8 cur, nxt;
+  load_batch8(sg, ws, 8 * (int)threadIdx.x, true, agent, cur);
+#pragma unroll 1
+  for (int base = 0; base < sg.total; base += 8 * kDThreads) {
+    if (base + 8 * kDThreads < sg.total)
+      load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, agent, nxt);
+    ga.template offer<8>(cur.v, cur.t);
+    cur = nxt;
+  }
+}
+
+// weights_out: p_t of every entry of sg above tau, at its position
+__device__ __forceinline__ void write_weights(const Segs &sg, const DecodeWs &ws, float *wrow, double tau, double z,
+                                              const DecodeParams &dp, bool agent) {
+#pragma unroll 1
+  for (int k = threadIdx.x; k < sg.total; k += kDThreads) {
+    size_t ad[1];
+    sg.addr_run<1>(k, ad);
+    const double y = (agent ? ld_agent(&ws.cx[ad[0]]) : ws.cx[ad[0]]) - tau;
+    if (y > 0.0) wrow[agent ? ld_agent(&ws.cl[ad[0]]) : ws.cl[ad[0]]] = (float)(pw_rt(y, dp) / z);
+  }
+}
 
 // Waits until the row's step is at least `need` (kStDone counts); returns the
 // step seen, or 0 after the time limit.
@@ -1133,17 +1138,24 @@ __device__ __forceinline__ void row_nan(const RowsArgs &ra, int r) {
   if (threadIdx.x == 0 && ra.tau) ra.tau[r] = NAN;
 }
 
+// an empty row: zero output, tau NaN
+template <int DIM>
+__device__ __forceinline__ void row_empty(const RowsArgs &ra, int r) {
+  for (int i = threadIdx.x; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
+  if (threadIdx.x == 0 && ra.tau) ra.tau[r] = NAN;
+}
+
 // LDS of the rows kernel (one layout per role, overlaid)
 template <typename T, int DIM>
 struct RowsLds {
-  int off[kMaxSlices + 1];
-  uint32_t start[kMaxSlices];
-  int dense[kMaxSlices];
+  int off[kMaxSlices + 1];      // the row's non-empty slices: entry offsets (ascending), then N
+  uint32_t start[kMaxSlices];   // and their first positions in cx
+  int moff[kHelpers + 1];       // compacted chunk runs: entry offsets (a chunk left in place adds 0)
+  uint32_t mst[kHelpers];       // and first positions
   union {
     struct {
       double cx[kCand];
-      uint32_t ci[kCand];
-      uint32_t ipr[kIprLds];
+      uint32_t cv[kCand];
       union {
         GatherLds<T, DIM> ga;
         double sortbuf[kCand];
@@ -1155,197 +1167,87 @@ struct RowsLds {
   };
 };
 
-template <typename T, int DIM>
-__device__ __forceinline__ Gather<T, DIM> make_gather(GatherLds<T, DIM> *sh, int *scan_scratch, const Dims &D,
-                                                      const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws,
-                                                      int r, long long rbase, const uint32_t *ipr, double tau,
-                                                      double z) {
-  Gather<T, DIM> ga;
-  ga.sh = sh;
-  ga.scan_scratch = scan_scratch;
-  ga.v_pool = (const T *)ra.v_pool;
-  ga.ws = &ws;
-  ga.rbase = rbase;
-  ga.ipr = ipr;
-  ga.P = D.P;
-  ga.Hkv = D.Hkv;
-  ga.g = (r % D.Hq) / D.G;
-  ga.wrow = ra.weights_out ? ra.weights_out + (size_t)r * D.max_pages * D.P : nullptr;
-  ga.tau = tau;
-  ga.z = z;
-  ga.dp = dp;
-  ga.nsup = 0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) ga.acc8[u] = 0.0f;
-  return ga;
-}
-
-// Support gather over the entries of sg (eight per thread per step, the next
-// eight in flight); the block's partial output goes to dst.
-template <typename T, int DIM>
-__device__ __forceinline__ void gather_entries(Gather<T, DIM> &ga, const Segs &sg, const DecodeWs &ws, float *dst,
-                                               bool agent) {
-  Batch8 cur, nxt;
-  load_batch8(sg, ws, 8 * (int)threadIdx.x, true, cur);
-#pragma unroll 1
-  for (int base = 0; base < sg.total; base += 8 * kDThreads) {
-    if (base + 8 * kDThreads < sg.total) load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, nxt);
-    ga.template offer<8>(cur.v, cur.t);
-    cur = nxt;
-  }
-  ga.finish(dst, agent);
-}
-
 // ------------------------------------------------------------ chunk blocks
-// Values in a global array, strided over the block (fixed order), 8 in flight
-struct ArrVals {
-  const double *v;
-  int n;
-  template <typename Fn>
-  __device__ __forceinline__ void each(Fn &&fn) const {
-#pragma unroll 1
-    for (int base = 0; base < n; base += 8 * kDThreads) {
-      double x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kDThreads + (int)threadIdx.x;
-        x[u] = i < n ? ld_agent(&v[i]) : -INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) fn(x[u]);
+// Chunk c of nc holds the table entries t whose entries-before count off[t]
+// maps to c (floor(off[t] nc / N)); [t0, t1) by two searches of the table.
+__device__ __forceinline__ void chunk_window(const int *off, int ntab, int N, int nc, int c, int *t0, int *t1) {
+  auto first_ge = [&](int cc) __attribute__((always_inline)) {
+    int lo = 0, hi = ntab;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((long long)off[mid] * nc / N >= cc) hi = mid; else lo = mid + 1;
     }
-  }
-};
-
-// After the chunk step, chunk c's record says whether its entries were
-// compacted (one run of m entries at `start`, token ids explicit) or left in
-// the layout of its slices [s0, s1).  Builds the Segs of chunk c in LDS
-// (every thread calls it).
-__device__ __forceinline__ Segs chunk_segs(const DecodeWs &ws, int r, int ns, int c, long long rbase, int P,
-                                           int *off, uint32_t *start, int *dense, unsigned long long *scan64) {
-  const double *rec = ws.crec + ((size_t)r * kHelpers + c) * 16;
-  const int m = (int)ld_agent(&rec[0]);
-  const bool compacted = ld_agent(&rec[11]) != 0.0;
-  const uint32_t st = (uint32_t)ld_agent(&rec[10]);
-  const int s0 = (int)ld_agent(&rec[13]), s1 = (int)ld_agent(&rec[14]);
-  const unsigned long long tok0 = (unsigned long long)rbase * (unsigned long long)P;
-  if (compacted) {
-    __syncthreads();  // the tables may still be in use
-    if (threadIdx.x == 0) {
-      off[0] = 0;
-      off[1] = m;
-      start[0] = st;
-      dense[0] = 0;
-    }
-    __syncthreads();
-    return Segs{off, start, dense, 1, m, tok0};
-  }
-  int nseg;
-  __syncthreads();
-  const int M = load_segs(ws, r, ns, s0, s1, off, start, dense, scan64, &nseg);
-  return Segs{off, start, dense, nseg, M, tok0};
+    return lo;
+  };
+  *t0 = (c == 0 || N == 0) ? 0 : first_ge(c);
+  *t1 = (c == nc - 1 || N == 0) ? ntab : first_ge(c + 1);
 }
 
-// Every entry of row r, chunk by chunk (tables rebuilt per chunk and pass)
+// After the chunk step: chunk c's entries, compacted (one run at mst[c], its
+// entries read back through agent-scope loads) or in place (its window of the
+// row's table).  s_rec holds the chunks' records.
+__device__ __forceinline__ Segs chunk_segs(const int *off, const uint32_t *start, const int *moff,
+                                           const uint32_t *mst, const double (*s_rec)[13], int ntab, int N, int nc,
+                                           int c) {
+  if (s_rec[c][11] != 0.0) return segs_window(moff, mst, c, c + 1);
+  int t0, t1;
+  chunk_window(off, ntab, N, nc, c, &t0, &t1);
+  return segs_window(off, start, t0, t1);
+}
+
+// Every entry of row r, chunk by chunk (agent-scope loads: compacted runs
+// were written by other blocks of the launch)
 struct RowVals {
   const DecodeWs *ws;
-  int r, ns, nc, P;
-  long long rbase;
-  int *off;
-  uint32_t *start;
-  int *dense;
-  unsigned long long *scan64;
+  const int *off, *moff;
+  const uint32_t *start, *mst;
+  const double (*s_rec)[13];
+  int ntab, N, nc;
   template <typename Fn>
   __device__ __forceinline__ void each(Fn &&fn) const {
 #pragma unroll 1
     for (int c = 0; c < nc; ++c) {
-      const Segs sg = chunk_segs(*ws, r, ns, c, rbase, P, off, start, dense, scan64);
-      const GlobVals gv{ws, &sg};
+      const Segs sg = chunk_segs(off, start, moff, mst, s_rec, ntab, N, nc, c);
+      const GlobVals gv{ws, &sg, true};
       gv.each(fn);
     }
   }
 };
 
-// Row tau and output from every entry by passes over the workspace (generic
+// Row tau and z from every entry by passes over the workspace (generic
 // exponent with many candidates, or a window too wide for the slots); with
-// `gather` the support gather and the output too.
+// `gather` the support gather, the output and weights_out too.
 template <typename T, int DIM>
-__device__ __forceinline__ void row_slow(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
-                         RowsLds<T, DIM> &sm, double lo0, double hi, long long rbase, double *dred, int *scan_scratch,
-                         unsigned long long *scan64, int nc, bool gather, double *tau_o, double *z_o) {
-  const RowVals src{&ws, r, ra.ns, nc, D.P, rbase, sm.off, sm.start, sm.dense, scan64};
+__device__ __forceinline__ void row_slow(const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
+                                         RowsLds<T, DIM> &sm, const RowVals &src, double lo0, double hi, double *dred,
+                                         int *scan_scratch, float *wrow, bool gather, double *tau_o, double *z_o) {
   const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
   double tau, z;
   solve_block(src, none, lo0, hi, dp, dred, tau, z);
   *tau_o = tau;
   *z_o = z;
   if (!gather) return;
-  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, tau, z);
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, dp, ra, tau, z);
 #pragma unroll 1
-  for (int c = 0; c < nc; ++c) {
-    const Segs sg = chunk_segs(ws, r, ra.ns, c, rbase, D.P, sm.off, sm.start, sm.dense, scan64);
-    Batch8 cur, nxt;
-    load_batch8(sg, ws, 8 * (int)threadIdx.x, true, cur);
-#pragma unroll 1
-    for (int base = 0; base < sg.total; base += 8 * kDThreads) {
-      if (base + 8 * kDThreads < sg.total)
-        load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, nxt);
-      ga.template offer<8>(cur.v, cur.t);
-      cur = nxt;
-    }
+  for (int c = 0; c < src.nc; ++c) {
+    const Segs sg = chunk_segs(src.off, src.start, src.moff, src.mst, src.s_rec, src.ntab, src.N, src.nc, c);
+    gather_entries<T, DIM>(ga, sg, ws, true);
+    if (wrow) write_weights(sg, ws, wrow, tau, z, dp, true);
   }
   ga.finish(ra.out + (size_t)r * DIM, false);
 }
 
-// The end of a row whose entries (at most 16 per thread, -inf for unused or
-// dropped slots) are in registers: the candidates X > Lb in index order into
-// LDS, tau and z (one wave over LDS, the sort form, or the block over the
-// registers), then the support gather and the output.
+// tau and z over the nC <= kCand candidates in LDS (one wave, or the sparsemax
+// sort form), then their support gather and the row's output
 template <typename T, int DIM>
-__device__ __forceinline__ void row_finish(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
-                       RowsLds<T, DIM> &sm, double (&xv)[16], uint32_t (&tv)[16], double mx, double Lb,
-                       long long rbase, double *dred, int *scan_scratch, double *s_tau, int *s_kstar) {
+__device__ __forceinline__ void finish_lds(const DecodeParams &dp, const RowsArgs &ra, int r, RowsLds<T, DIM> &sm,
+                                           int nC, double mx, double Lb, double *dred, int *scan_scratch,
+                                           double *s_tau, int *s_kstar, double *tau_o, double *z_o) {
   const int tid = threadIdx.x;
-  // the row's item -> physical page table into LDS (loads issued first)
-  const int rcnt = ws.rcnt[r];
-  const bool ipr_lds = rcnt <= kIprLds;
-  uint32_t ip[kIprLds / kDThreads];
-#pragma unroll
-  for (int u = 0; u < kIprLds / kDThreads; ++u) {
-    const int i = u * kDThreads + tid;
-    ip[u] = (ipr_lds && i < rcnt) ? ws.iphys[(size_t)rbase + i] : 0u;
-  }
-#pragma unroll
-  for (int u = 0; u < 16; ++u)
-    if (!(xv[u] > Lb)) xv[u] = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < kIprLds / kDThreads; ++u) {
-    const int i = u * kDThreads + tid;
-    if (ipr_lds && i < rcnt) sm.lead.ipr[i] = ip[u];
-  }
-  int nC;
-  {
-    int mine = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) mine += xv[u] > Lb ? 1 : 0;
-    int at = block_excl_scan(mine, scan_scratch, &nC);
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (xv[u] > Lb) {
-        if (at < kCand) {
-          sm.lead.cx[at] = xv[u];
-          sm.lead.ci[at] = tv[u];
-        }
-        ++at;
-      }
-    __syncthreads();
-  }
-  EKV_MARK(1, 3);
   double tau, z;
   const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
   const double hi = mx - pow((double)max(nC, 1), -dp.a);  // F(hi) <= 1: at most nC entries above it
-  const bool lds = nC <= kCand;
-  if (lds && dp.ibeta == 1 && dp.tau_method == 1) {
+  if (dp.ibeta == 1 && dp.tau_method == 1) {
     tau = sparsemax_tau_sort(sm.lead.cx, nC, sm.lead.sortbuf, dred, s_kstar);
     double zz = 0.0;
     for (int i = tid; i < nC; i += kDThreads) {
@@ -1353,7 +1255,7 @@ __device__ __forceinline__ void row_finish(const Dims &D, const DecodeParams &dp
       if (y > 0.0) zz += y;
     }
     z = block_sum(zz, dred);
-  } else if (lds) {
+  } else {
     if (tid < kWave) {
       double t, zk = 0.0;
       const LdsVals src{sm.lead.cx, nC, tid, kWave};
@@ -1373,27 +1275,68 @@ __device__ __forceinline__ void row_finish(const Dims &D, const DecodeParams &dp
     __syncthreads();
     tau = s_tau[0];
     z = s_tau[1];
-  } else {
-    solve_block(RegVals16{xv}, none, Lb, hi, dp, dred, tau, z);
   }
   EKV_MARK(1, 4);
   if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
-  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.lead.ga, scan_scratch, D, dp, ra, ws, r, rbase,
-                                          ipr_lds ? sm.lead.ipr : nullptr, tau, z);
-  if (lds) {
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.lead.ga, scan_scratch, dp, ra, tau, z);
 #pragma unroll 1
-    for (int k0 = 0; k0 < nC; k0 += 4 * kDThreads) {
-      double x4[4];
-      uint32_t t4[4];
+  for (int k0 = 0; k0 < nC; k0 += 4 * kDThreads) {
+    double x4[4];
+    uint32_t t4[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = k0 + 4 * tid + u;
-        x4[u] = k < nC ? sm.lead.cx[k] : -INFINITY;
-        t4[u] = k < nC ? sm.lead.ci[k] : 0u;
-      }
-      ga.template offer<4>(x4, t4);
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 4 * tid + u;
+      x4[u] = k < nC ? sm.lead.cx[k] : -INFINITY;
+      t4[u] = k < nC ? sm.lead.cv[k] : 0u;
     }
+    ga.template offer<4>(x4, t4);
+  }
+  ga.finish(ra.out + (size_t)r * DIM, false);
+  *tau_o = tau;
+  *z_o = z;
+}
+
+// The end of a row whose entries (at most 16 per thread, -inf for unused or
+// dropped slots) are in registers: the candidates X > Lb in index order into
+// LDS, tau and z (over LDS, or the block over the registers), then the
+// support gather, the output and weights_out.
+template <typename T, int DIM>
+__device__ __forceinline__ void row_finish(const DecodeParams &dp, const RowsArgs &ra, int r, RowsLds<T, DIM> &sm,
+                                           double (&xv)[16], const uint32_t (&tv)[16], const uint32_t (&lv)[16],
+                                           double mx, double Lb, float *wrow, double *dred, int *scan_scratch,
+                                           double *s_tau, int *s_kstar) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if (!(xv[u] > Lb)) xv[u] = -INFINITY;
+  int nC;
+  {
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mine += xv[u] > Lb ? 1 : 0;
+    int at = block_excl_scan(mine, scan_scratch, &nC);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (xv[u] > Lb) {
+        if (at < kCand) {
+          sm.lead.cx[at] = xv[u];
+          sm.lead.cv[at] = tv[u];
+        }
+        ++at;
+      }
+    __syncthreads();
+  }
+  EKV_MARK(1, 3);
+  double tau, z;
+  if (nC <= kCand) {
+    finish_lds<T, DIM>(dp, ra, r, sm, nC, mx, Lb, dred, scan_scratch, s_tau, s_kstar, &tau, &z);
   } else {
+    const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
+    const double hi = mx - pow((double)nC, -dp.a);
+    solve_block(RegVals16{xv}, none, Lb, hi, dp, dred, tau, z);
+    EKV_MARK(1, 4);
+    if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+    Gather<T, DIM> ga = make_gather<T, DIM>(&sm.lead.ga, scan_scratch, dp, ra, tau, z);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       double x8[8];
@@ -1405,150 +1348,233 @@ __device__ __forceinline__ void row_finish(const Dims &D, const DecodeParams &dp
       }
       ga.template offer<8>(x8, t8);
     }
+    ga.finish(ra.out + (size_t)r * DIM, false);
   }
-  ga.finish(ra.out + (size_t)r * DIM, false);
+  if (wrow)
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const double y = xv[u] - tau;
+      if (y > 0.0) wrow[lv[u]] = (float)(pw_rt(y, dp) / z);
+    }
   EKV_MARK(1, 5);
 }
 
 // The blocks of a row.  Every block reads every slice's summary (entry
-// counts, max and min) and derives the same chunking: nc = ceil(N / kChunkEnt)
-// chunks (at most nh), slices assigned to chunks by their entry prefix, so
-// chunks hold about N / nc entries each; a block whose chunk index is nc or
-// more leaves.  Each chunk counts its entries above mx - 2^-i (a certified
-// bound Lc for the row: C entries above mx - d give F(mx - d - C^-(alpha-1))
-// >= 1) and, in a row of at most kLargeN entries, compacts its entries above
-// max(mx - 1, Lc) in place; in a larger row it adds its entries to the row's
-// integer histogram instead.  The row's last chunk to arrive merges: the row
-// bound Lb from every chunk's bound and the summed counts; a smaller row is
-// solved and gathered there (one wave over LDS candidates, or the block).  In
-// a large row the last chunk certifies a window [e_lo, e_hi] for tau from the
-// histogram (bounds of F at the bin edges) and every chunk then (a) sums the
-// moments of its entries above e_hi and hands over those in the window (the
-// last to arrive solves for tau exactly) and (b) gathers its support (the
-// last sums the partial outputs in chunk order).  Between (a) and (b) the
-// chunks of the row wait for its last block; a row has at most nh <= 32
-// chunks, fewer than an XCD holds at once, and blocks are dispatched in
-// index order, so every waited-for block is running.  Every decision and
-// every sum depends on the entries alone, not on timing.
+// counts, max and min) and builds the row's table of non-empty slices; the
+// row has nc chunks (one when N <= kChunkCap, else about N / kChunkEnt, at
+// most nh), a slice going to chunk floor(entries before it * nc / N); a block
+// whose chunk index is nc or more leaves.  Each chunk counts its entries
+// above mx - 2^-i (a certified bound Lc for the row: C entries above mx - d
+// give F(mx - d - C^-(alpha-1)) >= 1).  A lone chunk holding the whole row
+// in registers finishes it at once.  Otherwise a chunk of a row of at most
+// kLargeN entries compacts its entries above Lc in place, and in a larger row
+// adds its entries to the row's integer histogram instead.  The row's last
+// chunk to arrive merges: the row bound Lb from every chunk's bound and the
+// summed counts; a smaller row is solved and gathered there (one wave over
+// LDS candidates, or the block).  In a large row the last chunk certifies a
+// window [e_lo, e_hi] for tau from the histogram (bounds of F at the bin
+// edges) and every chunk then (a) sums the moments of its entries above e_hi
+// and hands over those in the window (the last to arrive solves for tau
+// exactly) and (b) gathers its support (the last sums the partial outputs in
+// chunk order).  Between (a) and (b) the chunks of a row wait for its last
+// block; a row has at most nh <= 32 chunks, fewer than an XCD holds at once,
+// and blocks are dispatched in index order, so every waited-for block is
+// running.  Every decision and every sum depends on the entries alone, not on
+// timing.
 constexpr int kChunkPer = 16;                     // entries per thread a chunk block holds
 constexpr int kChunkCap = kChunkPer * kDThreads;  // entries a chunk compacts
-constexpr int kChunkEnt = 4096;                   // entries per chunk a row aims at
+constexpr int kChunkEnt = 3072;                   // entries per chunk a split row aims at (slack for slice sizes)
+constexpr int kMidCap = 16384;                    // entries a lone block streams over (two passes)
 constexpr int kLastCap = 4096;                    // entries the last block solves over
 constexpr int kSumPer = kMaxSlices / kDThreads;   // slice summaries per thread
 
 template <typename T, int DIM>
-__device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws, int r,
-                          int c, RowsLds<T, DIM> &sm) {
+__device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp, const RowsArgs &ra, const DecodeWs &ws,
+                                          int r, int c, RowsLds<T, DIM> &sm) {
   __shared__ double dred[3 * kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
   __shared__ unsigned long long scan64[kDThreads / kWave];
   __shared__ int s_cnt[kDThreads / kWave][kNThr];
+  __shared__ int s_nan[kDThreads / kWave];
   __shared__ double s_tau[2];
   __shared__ int s_kstar, s_last, s_ovf;
   __shared__ unsigned s_flag;
-  __shared__ double s_rec[kHelpers][15];
+  __shared__ double s_rec[kHelpers][13];
   __shared__ double s_par[8];
   __shared__ double s_hp[kHelpers][5];
   __shared__ int s_woff[kHelpers + 1];
   __shared__ double s_amin;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int ns = ra.ns;
+  float *wrow = ra.weights_out ? ra.weights_out + (size_t)r * D.max_pages * D.P : nullptr;
   EKV_MARK(1, 0);
-  // 1. every slice's summary in registers: N, mx, mn, malformed marks
-  const long long rbase = ws.rbase[r];
-  const unsigned long long tok0 = (unsigned long long)rbase * (unsigned long long)D.P;
+  if (c > 0) {  // a chunk index past the row's bound on chunks (from its items) leaves at once
+    const long long ub = (long long)ws.rcnt[r] * D.P;
+    if (ub <= kMidCap || c >= (int)((ub + kChunkEnt - 1) / kChunkEnt)) return;
+  }
+  // 1. the slices' summaries: the row's max, min and malformed mark (one
+  // barrier), then the table of the slices holding entries above mx - 1 (one
+  // packed scan: table position high, entry offset low).  A slice whose max
+  // is at most mx - 1 holds no entry that can carry weight (tau >= mx - 1).
   const int per = (ns + kDThreads - 1) / kDThreads;
   const int i0 = tid * per;
   int scn[kSumPer];
   uint32_t sst[kSumPer];
-  int sdn[kSumPer];
+  double smx[kSumPer];
   double mx = -INFINITY, mn = INFINITY;
-  int nan = 0, myN = 0;
+  int nan = 0;
 #pragma unroll
   for (int u = 0; u < kSumPer; ++u) {
     scn[u] = 0;
+    smx[u] = -INFINITY;
     const int i = i0 + u;
     if (u < per && i < ns) {
       const size_t o = (size_t)r * ns + i;
       scn[u] = ws.s_cnt[o];
       sst[u] = ws.s_start[o];
-      sdn[u] = ws.s_dense[o];
-      const double v = ws.s_max[o];
-      nan |= v != v;
-      mx = fmax(mx, v);
+      smx[u] = ws.s_max[o];
+      nan |= smx[u] != smx[u];
+      mx = fmax(mx, smx[u]);
       mn = fmin(mn, ws.s_min[o]);
-      myN += scn[u];
     }
   }
-  int N;
-  const int nbefore = block_excl_scan(myN, scan_scratch, &N);
-  mx = block_max(mx, dred);
-  mn = block_min_d(mn, dred);
-  nan = __syncthreads_or(nan);
-  const int nc = N > 0 ? min(ra.nh, (N + kChunkEnt - 1) / kChunkEnt) : 1;
-  if (c >= nc) return;
-  const bool large = N > kLargeN && dp.ibeta != 0;
+  {
+    const double wmx = wave_max(mx), wmn = wave_min_d(mn);
+    const int wnan = __any(nan) ? 1 : 0;
+    if (lane == 0) {
+      dred[wv] = wmx;
+      dred[kDThreads / kWave + wv] = wmn;
+      s_nan[wv] = wnan;
+    }
+    __syncthreads();
+    mx = dred[0];
+    mn = dred[kDThreads / kWave];
+    nan = s_nan[0];
+    for (int i = 1; i < kDThreads / kWave; ++i) {
+      mx = fmax(mx, dred[i]);
+      mn = fmin(mn, dred[kDThreads / kWave + i]);
+      nan |= s_nan[i];
+    }
+  }
   const double thr = mx - 1.0;  // tau >= thr: F(mx - 1) >= 1
-  // this chunk's slices: chunk of a slice = floor(entries before it * nc / N)
-  int myc[kSumPer];
-  {
-    int before = nbefore;
+  unsigned long long mine = 0;
 #pragma unroll
-    for (int u = 0; u < kSumPer; ++u) {
-      myc[u] = N > 0 ? (int)(((long long)before * nc) / N) : 0;
-      if (myc[u] > nc - 1) myc[u] = nc - 1;
-      before += scn[u];
-    }
+  for (int u = 0; u < kSumPer; ++u) {
+    if (!(smx[u] > thr)) scn[u] = 0;
+    if (scn[u] > 0) mine += (1ull << 32) + (unsigned)scn[u];
   }
-  // the non-empty slices of this chunk as one LDS table (packed 64-bit scan:
-  // table position in the high half, entry offset in the low half); the
-  // chunk's slice range goes to its record
-  int M, nseg, cs0 = ns, cs1 = 0;
   {
-    unsigned long long mine = 0;
-#pragma unroll
-    for (int u = 0; u < kSumPer; ++u) {
-      const int i = i0 + u;
-      if (u < per && i < ns && myc[u] == c) {
-        cs0 = min(cs0, i);
-        cs1 = max(cs1, i + 1);
-        if (scn[u] > 0) mine += (1ull << 32) + (unsigned)scn[u];
-      }
-    }
     unsigned long long tot;
     unsigned long long run = block_excl_scan64(mine, scan64, &tot);
 #pragma unroll
     for (int u = 0; u < kSumPer; ++u) {
       const int i = i0 + u;
-      if (u < per && i < ns && myc[u] == c && scn[u] > 0) {
+      if (u < per && i < ns && scn[u] > 0) {
         const int at = (int)(run >> 32);
         sm.off[at] = (int)(run & 0xFFFFFFFFull);
         sm.start[at] = sst[u];
-        sm.dense[at] = sdn[u];
         run += (1ull << 32) + (unsigned)scn[u];
       }
     }
-    const int ntab = (int)(tot >> 32);
-    M = (int)(tot & 0xFFFFFFFFull);
-    if (tid == 0) {
-      sm.off[ntab] = M;
-      if (ntab == 0) {
-        sm.off[0] = 0;
-        sm.off[1] = 0;
-        sm.start[0] = 0u;
-        sm.dense[0] = 1;
-      }
-    }
-    nseg = ntab > 0 ? ntab : 1;
-    cs0 = -(int)block_max((double)-cs0, dred);
-    cs1 = (int)block_max((double)cs1, dred);
+    mine = tot;
   }
-  const Segs sg{sm.off, sm.start, sm.dense, nseg, M, tok0};
+  const int ntab = (int)(mine >> 32), N = (int)(mine & 0xFFFFFFFFull);
+  if (tid == 0) sm.off[ntab] = N;
+  __syncthreads();
+  const int nc = N > kMidCap ? min(ra.nh, (N + kChunkEnt - 1) / kChunkEnt) : 1;
+  if (c >= nc) return;
+  const bool large = N > kLargeN && dp.ibeta != 0;
+  int t0, t1;
+  chunk_window(sm.off, ntab, N, nc, c, &t0, &t1);
+  const Segs sg = segs_window(sm.off, sm.start, t0, t1);
+  const int M = sg.total;
   EKV_MARK(1, 6);
   // histogram range of a large row: every entry above lo is binned
   double hlo = fmax(thr, mn);
   double hw = (mx - hlo) / (double)kBins;
   if (!(hw > 0.0) || !(hw < INFINITY)) hw = 1.0 / (double)kBins;
+  if (nc == 1 && !large && M > kChunkCap) {
+    // a lone block over more entries than its registers hold: rounds of
+    // kChunkCap entries (16 per thread).  The counts of the rounds so far
+    // already certify a bound (a part of the row's entries gives a weaker
+    // one), so each round puts its entries above the bound reached into the
+    // LDS candidates (a fixed order) and the entries are read once.
+    if (nan) {
+      row_nan<DIM>(ra, r);
+      return;
+    }
+    int q8[kNThr];
+#pragma unroll
+    for (int i = 0; i < kNThr; ++i) q8[i] = 0;
+    double Lq = thr;
+    int nC = 0;
+    const int rounds = (M + kChunkCap - 1) / kChunkCap;
+#pragma unroll 1
+    for (int qr = 0; qr < rounds; ++qr) {
+      double xq[kChunkPer];
+      uint32_t tq[kChunkPer];
+      {
+        size_t ad[kChunkPer];
+        addr_strided<kChunkPer>(sg, qr * kChunkCap + tid, ad);
+#pragma unroll
+        for (int u = 0; u < kChunkPer; ++u) {
+          xq[u] = ws.cx[ad[u]];
+          tq[u] = ws.ct[ad[u]];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kChunkPer; ++u) {
+        if (qr * kChunkCap + tid + u * kDThreads >= M) xq[u] = -INFINITY;
+        if (xq[u] > thr)
+#pragma unroll
+          for (int i = 0; i < kNThr; ++i) q8[i] += xq[u] > mx - ldexp(1.0, -i) ? 1 : 0;
+      }
+      {
+        int w8[kNThr];
+#pragma unroll
+        for (int i = 0; i < kNThr; ++i) w8[i] = wave_sum(q8[i]);
+        if (lane == 0)
+          for (int i = 0; i < kNThr; ++i) s_cnt[wv][i] = w8[i];
+        __syncthreads();
+        const int i = tid & (kNThr - 1);
+        int ci_ = 0;
+        for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
+        const double cand =
+            ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
+        Lq = fmax(Lq, wave_max(cand));
+      }
+      int take = 0;
+#pragma unroll
+      for (int u = 0; u < kChunkPer; ++u) take += xq[u] > Lq ? 1 : 0;
+      int tot;
+      int at = nC + block_excl_scan(take, scan_scratch, &tot);
+#pragma unroll
+      for (int u = 0; u < kChunkPer; ++u)
+        if (xq[u] > Lq) {
+          if (at < kCand) {
+            sm.lead.cx[at] = xq[u];
+            sm.lead.cv[at] = tq[u];
+          }
+          ++at;
+        }
+      nC += tot;
+    }
+    __syncthreads();
+    EKV_MARK(1, 3);
+    double tau, z;
+    if (nC <= kCand) {
+      finish_lds<T, DIM>(dp, ra, r, sm, nC, mx, Lq, dred, scan_scratch, s_tau, &s_kstar, &tau, &z);
+    } else {  // many candidates: passes over the row's entries
+      if (tid == 0) s_rec[0][11] = 0.0;
+      __syncthreads();
+      const RowVals rv{&ws, sm.off, sm.moff, sm.start, sm.mst, s_rec, ntab, N, 1};
+      row_slow<T, DIM>(dp, ra, ws, r, sm, rv, Lq, mx, dred, scan_scratch, nullptr, true, &tau, &z);
+      if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
+    }
+    if (wrow) write_weights(sg, ws, wrow, tau, z, dp, false);
+    EKV_MARK(1, 5);
+    return;
+  }
   // 2. counts above mx - 2^-i; compaction (smaller rows) or histogram (large)
   int c8[kNThr];
 #pragma unroll
@@ -1560,32 +1586,34 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
   };
   const bool small = !large && M <= kChunkCap;
   double xv[kChunkPer];
-  uint32_t tv[kChunkPer];
+  uint32_t tv[kChunkPer], lv[kChunkPer];
   if (large)
     for (int i = tid; i < kBins; i += kDThreads) sm.hist[i] = 0u;
-  __syncthreads();
+  if (large) __syncthreads();
   if (!nan && M > 0) {
     if (small) {
-      const int k0 = kChunkPer * tid;
+      // entries tid + u * kDThreads (a fixed order of the chunk's entries)
       size_t ad[kChunkPer];
-      bool dn[kChunkPer];
-      sg.addr_run<kChunkPer>(k0, ad, dn);
+      addr_strided<kChunkPer>(sg, tid, ad);
+      EKV_MARK(3, 0);
 #pragma unroll
       for (int u = 0; u < kChunkPer; ++u) {
         xv[u] = ws.cx[ad[u]];
-        tv[u] = sg.tok_of(ws, ad[u], dn[u]);
+        tv[u] = ws.ct[ad[u]];
+        lv[u] = wrow ? ws.cl[ad[u]] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < kChunkPer; ++u) {
-        if (k0 + u >= M) xv[u] = -INFINITY;
+        if (tid + u * kDThreads >= M) xv[u] = -INFINITY;
         count1(xv[u]);
       }
+      EKV_MARK(3, 1);
     } else {
       Batch8 cur, nxt;
-      load_batch8(sg, ws, 8 * tid, false, cur);
+      load_batch8(sg, ws, 8 * tid, false, false, cur);
 #pragma unroll 1
       for (int base = 0; base < M; base += 8 * kDThreads) {
-        if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
+        if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, false, nxt);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const double x = cur.v[u];
@@ -1599,12 +1627,20 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
         cur = nxt;
       }
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kChunkPer; ++u) {
+      xv[u] = -INFINITY;
+      tv[u] = 0u;
+      lv[u] = 0u;
+    }
   }
 #pragma unroll
   for (int i = 0; i < kNThr; ++i) c8[i] = wave_sum(c8[i]);
-  if ((tid & (kWave - 1)) == 0)
-    for (int i = 0; i < kNThr; ++i) s_cnt[tid / kWave][i] = c8[i];
+  if (lane == 0)
+    for (int i = 0; i < kNThr; ++i) s_cnt[wv][i] = c8[i];
   __syncthreads();
+  EKV_MARK(3, 2);
   if (large)
     for (int i = tid; i < kBins; i += kDThreads)
       if (sm.hist[i]) atomicAdd(&ws.hist[(size_t)r * kBins + i], sm.hist[i]);
@@ -1615,42 +1651,34 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     for (int w = 0; w < kDThreads / kWave; ++w) ci_ += s_cnt[w][i];
     const double cand =
         ci_ > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ci_, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
-    const double wm = wave_max(cand);
-    if (tid == 0) s_tau[0] = fmax(thr, wm);
-    __syncthreads();
-    Lc = s_tau[0];
+    Lc = fmax(thr, wave_max(cand));  // every wave holds the same counts
   }
   EKV_MARK(1, 7);
   if (nc == 1 && small) {
     // a lone chunk holds the whole row in registers: the candidates above Lb
     // (= Lc, the row's own counts) go to LDS directly
-    if (nan || N == 0) {
-      if (nan) {
-        row_nan<DIM>(ra, r);
-      } else {
-        for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
-        if (tid == 0 && ra.tau) ra.tau[r] = NAN;
-      }
-      return;
-    }
-    row_finish<T, DIM>(D, dp, ra, ws, r, sm, xv, tv, mx, Lc, rbase, dred, scan_scratch, s_tau, &s_kstar);
+    if (nan) row_nan<DIM>(ra, r);
+    else if (N == 0) row_empty<DIM>(ra, r);
+    else row_finish<T, DIM>(dp, ra, r, sm, xv, tv, lv, mx, Lc, wrow, dred, scan_scratch, s_tau, &s_kstar);
     return;
   }
-  const uint32_t cstart = sm.start[0] - (uint32_t)sm.off[0];  // the chunk's first entry position
+  const uint32_t cstart = t1 > t0 ? sm.start[t0] : 0u;  // the chunk's first entry position
   int m = M;
   if (small && !nan && M > 0) {
-    // in place: entry k of the chunk sits at or after position cstart + k
-    // (each slice's entries are a prefix of its item range), so every write
-    // lands on an entry read before the scan's barrier
-    int mine = 0;
+    // in place: every entry of the chunk is in registers before the scan's
+    // barrier, and the m kept ones go to [cstart, cstart + m), inside the
+    // chunk's own slice regions (which follow each other from cstart and
+    // hold at least its M entries)
+    int mineC = 0;
 #pragma unroll
-    for (int u = 0; u < kChunkPer; ++u) mine += xv[u] > Lc ? 1 : 0;
-    int at = block_excl_scan(mine, scan_scratch, &m);
+    for (int u = 0; u < kChunkPer; ++u) mineC += xv[u] > Lc ? 1 : 0;
+    int at = block_excl_scan(mineC, scan_scratch, &m);
 #pragma unroll
     for (int u = 0; u < kChunkPer; ++u)
       if (xv[u] > Lc) {
         st_agent(&ws.cx[cstart + at], xv[u]);
         st_agent(&ws.ct[cstart + at], tv[u]);
+        if (wrow) st_agent(&ws.cl[cstart + at], lv[u]);
         ++at;
       }
   }
@@ -1658,12 +1686,11 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     double *rec = ws.crec + ((size_t)r * kHelpers + c) * 16;
     st_agent(&rec[0], (double)m);
     st_agent(&rec[1], Lc);
-    for (int i = 0; i < kNThr; ++i) st_agent(&rec[2 + i], (double)(s_cnt[0][i] + s_cnt[1][i] + s_cnt[2][i] + s_cnt[3][i]));
+    for (int i = 0; i < kNThr; ++i)
+      st_agent(&rec[2 + i], (double)(s_cnt[0][i] + s_cnt[1][i] + s_cnt[2][i] + s_cnt[3][i]));
     st_agent(&rec[10], (double)cstart);
     st_agent(&rec[11], small ? 1.0 : 0.0);
     st_agent(&rec[12], (double)M);
-    st_agent(&rec[13], (double)cs0);
-    st_agent(&rec[14], (double)cs1);
   }
   EKV_MARK(1, 1);
   if (nc > 1 && !arrive_last(&ws.ctr[4 * r + 3], (unsigned)nc, &s_last)) {
@@ -1677,15 +1704,11 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
       __syncthreads();
     }
     if (tid < nc)
-      for (int f = 0; f < 15; ++f) s_rec[tid][f] = ld_agent(&ws.crec[((size_t)r * kHelpers + tid) * 16 + f]);
+      for (int f = 0; f < 13; ++f) s_rec[tid][f] = ld_agent(&ws.crec[((size_t)r * kHelpers + tid) * 16 + f]);
     __syncthreads();
     if (nan || N == 0) {
-      if (nan) {
-        row_nan<DIM>(ra, r);
-      } else {
-        for (int i = tid; i < DIM; i += kDThreads) ra.out[(size_t)r * DIM + i] = 0.0f;
-        if (tid == 0 && ra.tau) ra.tau[r] = NAN;
-      }
+      if (nan) row_nan<DIM>(ra, r);
+      else row_empty<DIM>(ra, r);
       if (large) publish_step(&ws.state[(size_t)r * kStStride], kStDone);
       return;
     }
@@ -1694,6 +1717,15 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     for (int cc = 0; cc < nc; ++cc) {
       mtot += (int)s_rec[cc][0];
       all_small &= s_rec[cc][11] != 0.0;
+    }
+    if (tid == 0) {  // the compacted runs
+      int o = 0;
+      for (int cc = 0; cc < nc; ++cc) {
+        sm.moff[cc] = o;
+        sm.mst[cc] = (uint32_t)s_rec[cc][10];
+        if (s_rec[cc][11] != 0.0) o += (int)s_rec[cc][0];
+      }
+      sm.moff[nc] = o;
     }
     double Lb;
     {
@@ -1705,10 +1737,10 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
           ct > 0 ? (mx - ldexp(1.0, -i)) - pow_neg_a((double)ct, dp) - 1e-12 * fmax(1.0, fabs(mx)) : -INFINITY;
       double bnd = wave_max(cand);
       for (int cc = 0; cc < nc; ++cc) bnd = fmax(bnd, s_rec[cc][1]);
-      if (tid == 0) s_tau[0] = fmax(thr, bnd);
-      __syncthreads();
-      Lb = s_tau[0];
+      Lb = fmax(thr, bnd);
     }
+    __syncthreads();  // the runs table
+    const RowVals rv{&ws, sm.off, sm.moff, sm.start, sm.mst, s_rec, ntab, N, nc};
     if (large) {
       // ---- certified window from the row's histogram.  Bin b's entries lie
       // in [e_{b-1}, e_{b+2}] (one bin of slack for the rounding of the
@@ -1772,41 +1804,25 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     } else if (!all_small || mtot > kLastCap) {
       // many candidates: passes over the row's entries by this block
       double tau, z;
-      row_slow<T, DIM>(D, dp, ra, ws, r, sm, Lb, mx, rbase, dred, scan_scratch, scan64, nc, true, &tau, &z);
+      row_slow<T, DIM>(dp, ra, ws, r, sm, rv, Lb, mx, dred, scan_scratch, wrow, true, &tau, &z);
       if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;
       return;
     } else {
       // ---- the compacted entries (16 consecutive per thread), those above
       // Lb into LDS in index order, then tau and the gather
-      if (tid < nc) {
-        sm.start[tid] = (uint32_t)s_rec[tid][10];
-        sm.dense[tid] = 0;
-      }
-      if (tid == 0) {
-        int o = 0;
-        for (int cc = 0; cc < nc; ++cc) {
-          sm.off[cc] = o;
-          o += (int)s_rec[cc][0];
-        }
-        sm.off[nc] = o;
-      }
-      __syncthreads();
-      const Segs cs{sm.off, sm.start, sm.dense, nc, mtot, tok0};
+      const Segs cs = segs_window(sm.moff, sm.mst, 0, nc);
       {
-        const int k0 = kChunkPer * tid;
         size_t ad[kChunkPer];
-        bool dn[kChunkPer];
-        cs.addr_run<kChunkPer>(k0, ad, dn);
+        if (mtot > 0) addr_strided<kChunkPer>(cs, tid, ad);
 #pragma unroll
         for (int u = 0; u < kChunkPer; ++u) {
-          xv[u] = nc > 1 ? ld_agent(&ws.cx[ad[u]]) : ws.cx[ad[u]];
-          tv[u] = nc > 1 ? ld_agent(&ws.ct[ad[u]]) : ws.ct[ad[u]];
+          const bool in = tid + u * kDThreads < mtot;
+          xv[u] = in ? ld_agent(&ws.cx[ad[u]]) : -INFINITY;
+          tv[u] = in ? ld_agent(&ws.ct[ad[u]]) : 0u;
+          lv[u] = (in && wrow) ? ld_agent(&ws.cl[ad[u]]) : 0u;
         }
-#pragma unroll
-        for (int u = 0; u < kChunkPer; ++u)
-          if (k0 + u >= mtot || !(xv[u] > Lb)) xv[u] = -INFINITY;
       }
-      row_finish<T, DIM>(D, dp, ra, ws, r, sm, xv, tv, mx, Lb, rbase, dred, scan_scratch, s_tau, &s_kstar);
+      row_finish<T, DIM>(dp, ra, r, sm, xv, tv, lv, mx, Lb, wrow, dred, scan_scratch, s_tau, &s_kstar);
       return;
     }
   }
@@ -1824,10 +1840,10 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     int m0 = 0, wc = 0;
     double *slot = ws.wbuf + ((size_t)r * kHelpers + c) * kSlot;
     Batch8 cur, nxt;
-    load_batch8(sg, ws, 8 * tid, false, cur);
+    load_batch8(sg, ws, 8 * tid, false, false, cur);
 #pragma unroll 1
     for (int base = 0; base < M; base += 8 * kDThreads) {
-      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, nxt);
+      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, false, nxt);
       int take = 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -1905,10 +1921,13 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
       solve_block(LdsVals{sm.win, W, tid, kDThreads}, ab, e_lo, e_hi, dp, dred, tau, z);
     } else {
       // window too wide for the slots: passes over every entry of the row
-      // (this block's table is rebuilt by the pass and restored below)
-      row_slow<T, DIM>(D, dp, ra, ws, r, sm, e_lo, e_hi, rbase, dred, scan_scratch, scan64, nc, false, &tau, &z);
-      const Segs again = chunk_segs(ws, r, ns, c, rbase, D.P, sm.off, sm.start, sm.dense, scan64);
-      (void)again;
+      // (every chunk of a large row is in place: the row's table)
+      if (tid == 0) {
+        for (int cc = 0; cc < nc; ++cc) s_rec[cc][11] = 0.0;
+      }
+      __syncthreads();
+      const RowVals rv{&ws, sm.off, sm.moff, sm.start, sm.mst, s_rec, ntab, N, nc};
+      row_slow<T, DIM>(dp, ra, ws, r, sm, rv, e_lo, e_hi, dred, scan_scratch, nullptr, false, &tau, &z);
     }
     if (tid == 0) {
       st_agent(&ws.rpar[(size_t)r * 8 + 5], tau);
@@ -1926,8 +1945,10 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
   }
   if (tid < 8) s_par[tid] = ld_agent(&ws.rpar[(size_t)r * 8 + tid]);
   __syncthreads();
-  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, D, dp, ra, ws, r, rbase, nullptr, s_par[5], s_par[6]);
-  gather_entries<T, DIM>(ga, sg, ws, ws.opart + ((size_t)r * kHelpers + c) * DIM, true);
+  Gather<T, DIM> ga = make_gather<T, DIM>(&sm.ga, scan_scratch, dp, ra, s_par[5], s_par[6]);
+  gather_entries<T, DIM>(ga, sg, ws, false);
+  ga.finish(ws.opart + ((size_t)r * kHelpers + c) * DIM, true);
+  if (wrow) write_weights(sg, ws, wrow, s_par[5], s_par[6], dp, false);
   if (!arrive_last(&ws.ctr[4 * r + 2], (unsigned)nc, &s_last)) return;
   for (int cc = tid; cc < DIM; cc += kDThreads) {
     float sum = ld_agent(&ws.opart[((size_t)r * kHelpers) * DIM + cc]);
@@ -1949,6 +1970,12 @@ __global__ __launch_bounds__(kDThreads) void rows_kernel(Dims D, DecodeParams dp
 }
 
 // =================================================================== launchers
+// Query-head rows up to which a set per query head goes to the per-item
+// decode: there a step is a few dependent memory round trips per kernel, and
+// one page per block in flight beats the slices' union step; above it the
+// slices share each K page among the heads of a group and split large rows.
+constexpr long long kItemRows = 64;
+
 static int decode_slices(const Dims &D) {
   long long ns = (D.max_pages + 127) / 128;  // about 128 pages per slice
   ns = std::max(ns, (long long)((D.max_pages + kMaxR - 1) / kMaxR));
@@ -1963,14 +1990,11 @@ static DecodeWs carve_decode(const Dims &D, int ns, long long item_cap, void *ba
   DecodeWs w;
   w.cx = cv.take<double>(cap_tok);
   w.ct = cv.take<uint32_t>(cap_tok);
-  w.iphys = cv.take<uint32_t>((size_t)item_cap);
-  w.ipage = cv.take<uint32_t>((size_t)item_cap);
+  w.cl = cv.take<uint32_t>(cap_tok);
   w.s_cnt = cv.take<int>(rows * ns);
   w.s_max = cv.take<double>(rows * ns);
   w.s_min = cv.take<double>(rows * ns);
   w.s_start = cv.take<uint32_t>(rows * ns);
-  w.s_dense = cv.take<int>(rows * ns);
-  w.rbase = cv.take<long long>(rows);
   w.rcnt = cv.take<int>(rows);
   w.state = cv.take<unsigned>(rows * kStStride);
   w.ctr = cv.take<unsigned>(rows * 4);
@@ -2006,9 +2030,9 @@ static long long item_cap_of(const Dims &D, int ns, size_t ws_bytes) {
   size_t fixed = 0;
   carve_decode(D, ns, 0, nullptr, &fixed);
   if (ws_bytes <= fixed) return 0;
-  // an upper estimate (the four item regions without their alignment), then
+  // an upper estimate (the three token regions without their alignment), then
   // down to the largest capacity that fits: a few steps at most
-  long long cap = (long long)((ws_bytes - fixed) / ((size_t)D.P * 12 + 8));
+  long long cap = (long long)((ws_bytes - fixed) / ((size_t)D.P * 16));
   cap = std::min(cap, cap_limit(D));
   size_t b = 0;
   carve_decode(D, ns, cap, nullptr, &b);
@@ -2032,9 +2056,10 @@ static hipError_t launch_dec_t(const Dims &D, const DecodeParams &dp, const KsAr
     (void)hipFuncSetAttribute((const void *)rows_kernel<T, DIM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  // blocks per row (chunks at most): about 512 blocks in all, one per slot
-  // of the GPU at this kernel's occupancy
-  const int nh = std::max(1, std::min(std::min(kHelpers, ka.ns), 512 / std::max(1, rows)));
+  // blocks per row (chunks at most); those past a row's bound on chunks leave
+  // at once.  An odd count spreads the rows' first blocks over the XCDs
+  // (blocks go to the XCDs in turn).
+  const int nh = std::max(1, std::min(kHelpers - 1, ka.ns));
   RowsArgs ra{v_pool, out, tau, ka.weights_out, ka.ns, nh};
   const long long grid = (long long)rows * nh;
   hipLaunchKernelGGL((rows_kernel<T, DIM>), dim3((unsigned)grid), dim3(kDThreads), lds, s, D, dp, ra, w);
@@ -2075,7 +2100,15 @@ static hipError_t launch_decode_mode(const Dims &D, int dtype, int mode, const v
   dp.tau_method = tau_method;
   const int ns = decode_slices(D);
   if ((D.max_pages + ns - 1) / ns > kMaxR) return hipErrorInvalidValue;
+  // an entry's V row (physical page * Hkv + g) * P + slot is held in 32 bits
+  if ((unsigned long long)D.num_phys * (unsigned long long)D.Hkv * (unsigned long long)D.P > 0xFFFFFFFFull)
+    return hipErrorInvalidValue;
   const long long cap = item_cap_of(D, ns, ws_bytes);
+  // a set per query head over a few rows: the per-item decode (decode_items.hip),
+  // same item capacity (its layout needs fewer bytes per item)
+  if (mode == 0 && (long long)D.B * D.Hq <= kItemRows && decode_items_ws_bytes(D, cap) <= ws_bytes)
+    return launch_entmax_decode_items(D, dtype, q, k_pool, v_pool, page_table, seq_lens, sel_idx, sel_cnt, alpha,
+                                      tau_method, out, tau, weights_out, ws, cap, s);
   const DecodeWs w = carve_decode(D, ns, cap, ws, nullptr);
   const KsArgs ka{q, k_pool, page_table, seq_lens, sel_idx, sel_cnt, weights_out, mode, ns, cap};
   if (dtype == ENTMAXKV_BF16) {

@@ -77,6 +77,14 @@ hipError_t launch_entmax_decode(const Dims &D, int dtype, const void *q, const v
                                 const int32_t *sel_cnt, double alpha, int tau_method, float *out,
                                 double *tau, float *weights_out, void *ws, size_t ws_bytes, hipStream_t s);
 
+// per-item decode (a set per query head, few rows) into a workspace of `cap` items
+size_t decode_items_ws_bytes(const Dims &D, long long cap);
+hipError_t launch_entmax_decode_items(const Dims &D, int dtype, const void *q, const void *k_pool,
+                                      const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,
+                                      const int32_t *sel_idx, const int32_t *sel_cnt, double alpha, int tau_method,
+                                      float *out, double *tau, float *weights_out, void *ws, long long cap,
+                                      hipStream_t s);
+
 size_t decode_group_ws_bytes(const Dims &D);
 hipError_t launch_entmax_decode_group(const Dims &D, int dtype, const void *q, const void *k_pool,
                                       const void *v_pool, const int32_t *page_table, const int32_t *seq_lens,

@@ -1,9 +1,12 @@
 """GPU parity of the entmax decodes on long selections.
 
-Rows here keep many slices of tokens, and with a small score scale more than
-4096 entries: the row then goes to the helper blocks (histogram window,
-moments and window solve, split gather), or for a generic alpha to the
-leader's passes over the workspace.  Same bars as the small cases: thresholds
+Rows here keep many tokens, and with a small score scale many candidates.
+Two batch shapes: 8 query-head rows (a set per query head goes to the
+per-item decode: chunk blocks, merge, register or workspace solve) and 68
+rows (the slice decode: lone blocks over rounds of entries, chunked rows
+merged by their last block, and above 32768 entries the helper steps --
+histogram window, moments and window solve, split gather -- or for a generic
+alpha passes over the workspace).  Same bars as the small cases: thresholds
 to 1e-12, bit-exact supports, weights to 1e-5, outputs to the KV-dtype
 tolerance; a repeated call gives the same bits.
 """
@@ -23,11 +26,17 @@ pytestmark = pytest.mark.gpu
 SCALES = [0.0, 0.08, 0.02, 0.01, 0.002]
 
 
-@pytest.fixture(scope="module", params=SCALES, ids=lambda s: f"scale{s}")
+# (batch, contexts): 8 rows, and 68 rows (past the per-item decode's row limit)
+SHAPES = [(2, (20000, 9001)), (17, (20000, 9001) * 8 + (4000,))]
+
+
+@pytest.fixture(scope="module", params=[(s, b) for b in range(len(SHAPES)) for s in SCALES],
+                ids=lambda p: f"rows{SHAPES[p[1]][0] * 4}_scale{p[0]}")
 def large(request):
-    inp = synth.random_small(11, B=2, Hq=4, Hkv=2, d=64, P=16, dtype="bf16", ctx=(20000, 9001),
-                             planted_per_kv=5)
-    return inp, Dev(inp, scale=request.param)
+    scale, bi = request.param
+    B, ctx = SHAPES[bi]
+    inp = synth.random_small(11, B=B, Hq=4, Hkv=2, d=64, P=16, dtype="bf16", ctx=ctx, planted_per_kv=5)
+    return inp, Dev(inp, scale=scale)
 
 
 def _selections(inp, seed=5):

@@ -22,6 +22,9 @@ SMALL = [
     (2, 3, 2, 1, 64, 64, "f32", (4096, 65, 1)),
     (3, 2, 8, 1, 64, 32, "bf16", (3000, 2017)),
     (4, 1, 1, 1, 64, 16, "f32", (4096,)),
+    # more than 64 query-head rows: a set per query head goes to the slice decode
+    (5, 5, 16, 4, 64, 16, "bf16", (1000, 333, 2048, 1, 4000)),
+    (6, 3, 32, 4, 128, 32, "f32", (3000, 700, 1)),
 ]
 
 
