@@ -68,7 +68,7 @@ struct DecodeWs {
   uint32_t *cl;       // [cap_tok]  its logical position page * P + slot (written for weights_out only)
   int *s_cnt;         // [rows][ns] entries stored for the slice
   double *s_max;      // [rows][ns] max X over the slice's kept tokens (-inf: none; NaN: malformed)
-  double *s_min;      // [rows][ns] min X over the slice's kept tokens (+inf: none)
+  double *s_min;      // [rows][ns] min X over the slice's stored entries (+inf: none)
   uint32_t *s_start;  // [rows][ns] index in cx of the slice's first entry
   int *rcnt;          // [rows] items of the row (entries at most rcnt * P)
   unsigned *state;    // [rows][kStStride] step of a large row (one 128-byte line per row)
@@ -239,7 +239,7 @@ __device__ __forceinline__ int ks_row_items(const Dims &D, const KsArgs &a, int 
 }
 
 template <typename T, int DIM, int P, int G>
-__global__ __launch_bounds__(kDThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kDThreads)
 void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   constexpr int kParts = DIM / 16;                            // threads per token, 16 coordinates each
   constexpr int kUpp = P * kParts;                            // (token, part) units per page
@@ -258,6 +258,7 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   __shared__ unsigned s_bad, s_nu;
   __shared__ double s_red[kDThreads / kWave][2 * G];
   __shared__ double s_mx[G], s_mn[G];
+  __shared__ double s_mnw[kDThreads / kWave][G];  // per wave: min of the entries it stored
   __shared__ long long red64[kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
   __shared__ unsigned long long scan64[kDThreads / kWave];
@@ -409,12 +410,10 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   for (int i = tid; i < G * DIM; i += kDThreads) qs[i / DIM][i % DIM] = load_f(q, (size_t)r0 * DIM + i);
   __syncthreads();
   const int npass = (nU + kPpi - 1) / kPpi;
-  double lmax[G], lmin[G];
+  double lmax[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lmax[h] = -INFINITY;
-    lmin[h] = INFINITY;
-  }
+  for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
+  if (tid < (kDThreads / kWave) * G) s_mnw[tid / G][tid % G] = INFINITY;
   // union pages in batches of kLdsPages, whose X fits the LDS stage; after a
   // batch, each head's running max takes in the batch and the batch's entries
   // above (running max) - 1 are appended to the head's entries (token ids
@@ -423,15 +422,16 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   static_assert(kLdsPages % kPpi == 0, "a batch is whole passes");
   constexpr int kPpb = kLdsPages / kPpi;  // passes per batch
   auto lo_of = [&](int h) __attribute__((always_inline)) { return s_lo[a.mode == 0 ? h : 0]; };
+  // every call issues its loads (past the last union page: that page again,
+  // unused), so the count of loads in flight after a buffer's is fixed and its
+  // wait leaves the later buffers' loads in flight
   auto load_pass = [&](int pass, KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
-    const int k = pass * kPpi + j;
-    if (k < nU) {  // uniform per wave
-      const size_t ph = uphys[k];
+    const int k = min(pass * kPpi + j, nU - 1);
+    const size_t ph = uphys[k];
 #pragma unroll
-      for (int u = 0; u < kUpt; ++u) {
-        const int t = (u0 + u * kTpp) / kParts;
-        kv[u].load(k_pool + ((ph * D.Hkv + g) * P + t) * DIM + e * 16);
-      }
+    for (int u = 0; u < kUpt; ++u) {
+      const int t = (u0 + u * kTpp) / kParts;
+      kv[u].load(k_pool + ((ph * D.Hkv + g) * P + t) * DIM + e * 16);
     }
   };
   // X of one pass (-inf for heads that did not keep the page and for slots
@@ -467,19 +467,14 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
           if (t < ntok) x = dp.a * (dp.c * acc);
         }
         lmax[h] = fmax(lmax[h], x);
-        if (x > -INFINITY) lmin[h] = fmin(lmin[h], x);
         if (act && e == 0) xl[(kl * P + t) * G + h] = x;
       }
     }
   };
   // a finished batch: running max, then the batch's entries above it - 1
   int ncnt[G];
-  double rmax[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    ncnt[h] = 0;
-    rmax[h] = -INFINITY;
-  }
+  for (int h = 0; h < G; ++h) ncnt[h] = 0;
   // the batch of union pages from kb0: each thread takes kTpt consecutive
   // tokens of the stage, every head; one packed scan per four heads places
   // the entries
@@ -492,6 +487,7 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
       if (lane == 0) s_red[wv][h] = wm;
     }
     lds_barrier();  // also orders the batch's LDS stage writes before the reads below
+    double rmax[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       double mm = s_red[0][h];
@@ -514,11 +510,15 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
     for (int q = 0; q < (G + 3) / 4; ++q) {
       unsigned long long tot;
       const unsigned long long pre = block_excl_scan64<true>(pk[q], scan64, &tot);
+      // the totals are the block's: keep them (and the counts) in scalar registers
+      tot = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(tot >> 32)) << 32) |
+            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)tot);
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
         const int h = 4 * q + hh;
         if (h < G) {
           size_t at = (size_t)(s_base[h] + lo_of(h)) * P + ncnt[h] + (int)((pre >> (16 * hh)) & 0xFFFFull);
+          double mn = INFINITY;
 #pragma unroll
           for (int i = 0; i < kTpt; ++i) {
             const double x = xat(i, h);
@@ -527,9 +527,12 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
               ws.cx[at] = x;
               ws.ct[at] = (uphys[k] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)t;
               if (a.weights_out) ws.cl[at] = (uint32_t)((p0 + ulist[k]) * P + t);
+              mn = fmin(mn, x);
               ++at;
             }
           }
+          mn = wave_min_d(mn);
+          if (lane == 0) s_mnw[wv][h] = fmin(s_mnw[wv][h], mn);
           ncnt[h] += (int)((tot >> (16 * hh)) & 0xFFFFull);
         }
       }
@@ -538,38 +541,36 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   };
 
   // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
-  KRaw<T> ka0[kUpt], ka1[kUpt], ka2[kUpt];
-  if (npass > 0) load_pass(0, ka0);
-  if (npass > 1) load_pass(1, ka1);
-#pragma unroll 1
-  for (int pass = 0; pass < npass; ++pass) {
-    if (pass + 2 < npass) load_pass(pass + 2, ka2);
-    score_pass(pass, ka0);
-#pragma unroll
-    for (int u = 0; u < kUpt; ++u) {
-      ka0[u] = ka1[u];
-      ka1[u] = ka2[u];
-    }
+  // three K buffers used in turn by the unrolled loop (no register copies,
+  // which would wait for loads still in flight)
+  KRaw<T> kA[kUpt], kB[kUpt], kC[kUpt];
+  auto step = [&](int pass, const KRaw<T> (&cur)[kUpt], KRaw<T> (&ahead)[kUpt]) __attribute__((always_inline)) {
+    load_pass(pass + 2, ahead);
+    score_pass(pass, cur);
     if ((pass + 1) % kPpb == 0 || pass + 1 == npass) compact_batch((pass - pass % kPpb) * kPpi);
+  };
+  if (npass > 0) {
+    load_pass(0, kA);
+    load_pass(1, kB);
+#pragma unroll 1
+    for (int pass = 0; pass < npass; pass += 3) {
+      step(pass, kA, kC);
+      if (pass + 1 < npass) step(pass + 1, kB, kA);
+      if (pass + 2 < npass) step(pass + 2, kC, kB);
+    }
   }
-  // slice max / min per head
+  // slice max per head, and the min of the stored entries
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lmax[h] = wave_max(lmax[h]);
-    lmin[h] = wave_min_d(lmin[h]);
-  }
+  for (int h = 0; h < G; ++h) lmax[h] = wave_max(lmax[h]);
   if (lane == 0)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_red[wv][h] = lmax[h];
-      s_red[wv][G + h] = lmin[h];
-    }
+    for (int h = 0; h < G; ++h) s_red[wv][h] = lmax[h];
   __syncthreads();
   if (tid < G) {
-    double m = s_red[0][tid], n = s_red[0][G + tid];
+    double m = s_red[0][tid], n = s_mnw[0][tid];
     for (int w = 1; w < kDThreads / kWave; ++w) {
       m = fmax(m, s_red[w][tid]);
-      n = fmin(n, s_red[w][G + tid]);
+      n = fmin(n, s_mnw[w][tid]);
     }
     s_mx[tid] = m;
     s_mn[tid] = n;
@@ -694,6 +695,26 @@ __device__ __forceinline__ void load_batch8(const Segs &sg, const DecodeWs &ws, 
       bt.v[u] = -INFINITY;
       bt.t[u] = 0u;
     }
+  }
+}
+
+// fn over every batch of sg's entries (eight per thread, 2048 per batch) in
+// order, the next batch's loads issued before fn runs on the current one; two
+// buffers used in turn (copying a buffer would wait for its loads).  fn may
+// hold block barriers: every thread makes the same calls.
+template <typename Fn>
+__device__ __forceinline__ void stream_batches(const Segs &sg, const DecodeWs &ws, bool toks, bool agent, Fn &&fn) {
+  constexpr int kStep = 8 * kDThreads;
+  const int M = sg.total, t8 = 8 * (int)threadIdx.x;
+  Batch8 b0, b1;
+  load_batch8(sg, ws, t8, toks, agent, b0);
+#pragma unroll 1
+  for (int base = 0; base < M; base += 2 * kStep) {
+    if (base + kStep < M) load_batch8(sg, ws, base + kStep + t8, toks, agent, b1);
+    fn(b0);
+    if (base + kStep >= M) break;
+    if (base + 2 * kStep < M) load_batch8(sg, ws, base + 2 * kStep + t8, toks, agent, b0);
+    fn(b1);
   }
 }
 
@@ -1082,15 +1103,9 @@ __device__ __forceinline__ Gather<T, DIM> make_gather(GatherLds<T, DIM> *sh, int
 // eight in flight); the block's partial output goes to dst.
 template <typename T, int DIM>
 __device__ __forceinline__ void gather_entries(Gather<T, DIM> &ga, const Segs &sg, const DecodeWs &ws, bool agent) {
-  Batch8 cur, nxt;
-  load_batch8(sg, ws, 8 * (int)threadIdx.x, true, agent, cur);
-#pragma unroll 1
-  for (int base = 0; base < sg.total; base += 8 * kDThreads) {
-    if (base + 8 * kDThreads < sg.total)
-      load_batch8(sg, ws, base + 8 * kDThreads + 8 * (int)threadIdx.x, true, agent, nxt);
-    ga.template offer<8>(cur.v, cur.t);
-    cur = nxt;
-  }
+  stream_batches(sg, ws, true, agent, [&](const Batch8 &bt) __attribute__((always_inline)) {
+    ga.template offer<8>(bt.v, bt.t);
+  });
 }
 
 // weights_out: p_t of every entry of sg above tau, at its position
@@ -1609,14 +1624,10 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
       }
       EKV_MARK(3, 1);
     } else {
-      Batch8 cur, nxt;
-      load_batch8(sg, ws, 8 * tid, false, false, cur);
-#pragma unroll 1
-      for (int base = 0; base < M; base += 8 * kDThreads) {
-        if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, false, nxt);
+      stream_batches(sg, ws, false, false, [&](const Batch8 &bt) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const double x = cur.v[u];
+          const double x = bt.v[u];
           count1(x);
           if (large && x > hlo) {
             const double f = floor((x - hlo) / hw);
@@ -1624,8 +1635,7 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
             atomicAdd(&sm.hist[bin], 1u);
           }
         }
-        cur = nxt;
-      }
+      });
     }
   } else {
 #pragma unroll
@@ -1839,15 +1849,11 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
     double m1 = 0.0, m2 = 0.0, ymin = INFINITY;
     int m0 = 0, wc = 0;
     double *slot = ws.wbuf + ((size_t)r * kHelpers + c) * kSlot;
-    Batch8 cur, nxt;
-    load_batch8(sg, ws, 8 * tid, false, false, cur);
-#pragma unroll 1
-    for (int base = 0; base < M; base += 8 * kDThreads) {
-      if (base + 8 * kDThreads < M) load_batch8(sg, ws, base + 8 * kDThreads + 8 * tid, false, false, nxt);
+    stream_batches(sg, ws, false, false, [&](const Batch8 &bt) __attribute__((always_inline)) {
       int take = 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const double v = cur.v[u];
+        const double v = bt.v[u];
         if (v > e_hi) {
           const double y = v - e_hi;
           ++m0;
@@ -1862,13 +1868,12 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
       int at = wc + block_excl_scan<true>(take, scan_scratch, &tot);  // the next batch's loads stay in flight
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (!(cur.v[u] > e_hi) && cur.v[u] > e_lo) {
-          if (at < kSlot) st_agent(&slot[at], cur.v[u]);
+        if (!(bt.v[u] > e_hi) && bt.v[u] > e_lo) {
+          if (at < kSlot) st_agent(&slot[at], bt.v[u]);
           ++at;
         }
       wc += tot;
-      cur = nxt;
-    }
+    });
     double sums[3] = {(double)m0, m1, m2};
     block_sum_n<3>(sums, dred);
     ymin = block_min_d(ymin, dred);
