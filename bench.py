@@ -60,9 +60,10 @@ def parse():
     ap.add_argument("--oracle-1t", action="store_true",
                     help="time the oracle's step on the tiny and 32k workloads (CPU only; run with "
                          "OMP_NUM_THREADS=1 by the CPU-baseline leg), print one JSON line, then exit")
-    ap.add_argument("--only", default="", choices=["", "score", "step", "copy"],
-                    help="profiling aid: run only score_pages, only the step, or a plain 1 GiB device copy "
-                         "(the calibration of the HBM byte counters), then exit")
+    ap.add_argument("--only", default="", choices=["", "score", "step", "full", "copy"],
+                    help="profiling aid: run only score_pages, only the step, only the full-cache entmax and "
+                         "softmax decodes, or a plain 1 GiB device copy (the calibration of the HBM byte "
+                         "counters), then exit")
     return ap.parse_args()
 
 
@@ -191,6 +192,15 @@ def main():
     if args.only == "step":
         for i in range(args.steps):
             step(i % R)
+        torch.cuda.synchronize()
+        return
+    if args.only == "full":
+        ws_sm = E.workspace(shape, E.CALL_SOFTMAX)
+        ws_f = E.workspace(shape, E.CALL_DECODE_FULL)
+        for i in range(args.steps):
+            q, k, v, meta = reps[i % R]
+            E.entmax_decode_full(shape, q, k, v, pt, sl, alpha, out, ws=ws_f)
+            E.softmax_decode_full(shape, q, k, v, pt, sl, out, ws=ws_sm)
         torch.cuda.synchronize()
         return
 

@@ -22,17 +22,29 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
+_OVERRIDE = os.environ.get("ENTMAXKV_ORACLE_LIB")  # another build of oracle.c (the sanitizer run)
 _lib = None
+_FLAGS = ["-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared"]
 
 
 def build() -> str:
     """Compile oracle.c into liboracle.so with gcc (fp64, no FMA contraction)."""
     src = os.path.join(_HERE, "oracle.c")
-    cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off", "-fno-fast-math",
-           "-fopenmp", "-fPIC", "-shared", "-o", _SO + ".tmp", src, "-lm"]
+    cmd = ["gcc", "-O2", *_FLAGS, "-o", _SO + ".tmp", src, "-lm"]
     subprocess.check_call(cmd)
     os.replace(_SO + ".tmp", _SO)
     return _SO
+
+
+def build_sanitized(out: str) -> str:
+    """Compile oracle.c under AddressSanitizer and UndefinedBehaviorSanitizer
+    (any report aborts) into `out`; load it with ENTMAXKV_ORACLE_LIB=out in a
+    process started with gcc's libasan preloaded."""
+    src = os.path.join(_HERE, "oracle.c")
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", *_FLAGS, "-o", out, src, "-lm"]
+    subprocess.check_call(cmd)
+    return out
 
 
 def _load():
@@ -40,9 +52,13 @@ def _load():
     if _lib is not None:
         return _lib
     src = os.path.join(_HERE, "oracle.c")
-    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
-        build()
-    lib = ctypes.CDLL(_SO)
+    if _OVERRIDE:
+        so = _OVERRIDE
+    else:
+        so = _SO
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+            build()
+    lib = ctypes.CDLL(so)
     _lib = lib
     vp = ctypes.c_void_p
     lib.orc_round_bf16.restype = ctypes.c_double

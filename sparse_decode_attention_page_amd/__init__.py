@@ -16,7 +16,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libentmaxkv.so")
+# another build of the library (the host-side sanitizer run) may be named by ENTMAXKV_LIB
+LIB_PATH = os.environ.get("ENTMAXKV_LIB") or os.path.join(_HERE, "libentmaxkv.so")
 _lib = None
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = range(6)

@@ -35,6 +35,37 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_host_sanitized(out: str, jobs: int | None = None) -> str:
+    """The library with its host code (argument validation, workspace sizing,
+    launch set-up) under AddressSanitizer and UndefinedBehaviorSanitizer (the
+    GPU code is built as usual, without them) into `out`: for CPU runs of the
+    checks that fail before any launch, in a process started with clang's ASan
+    runtime preloaded.  Skipped when `out` is newer than every source."""
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(ROOT, "include", "entmaxkv.h")]
+    if os.path.exists(out) and os.path.getmtime(out) > max(os.path.getmtime(f) for f in srcs):
+        return out
+    tmp = out + ".objs"
+    os.makedirs(tmp, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def comp(src: str) -> str:
+        obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+        cmd = ["hipcc", *FLAGS, "-Xarch_host", "-g", *san, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(jobs or min(len(SOURCES), os.cpu_count() or 4, 8)) as ex:
+        objs = list(ex.map(comp, SOURCES))
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-o", out, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return out
+
+
 def build(jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 8)
