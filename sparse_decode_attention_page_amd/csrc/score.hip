@@ -88,8 +88,14 @@ struct ScoreCfg {
   static constexpr int kRowChunks = DIM / kE;          // chunks per (box) metadata row
   static constexpr int kF8Chunks = DIM / 16;           // chunks per E4M3 row
   static constexpr int kRecBytes = F8 ? 6 * DIM : 4 * DIM * (int)sizeof(T);
-  static constexpr int kTileBytes = kTilePages * kRecBytes;
-  static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;  // 16-byte loads per thread per tile
+  // a tile is staged in parts of the coordinates (every row's same range), 512
+  // bytes of each record per part, so a part's tile is 32 KB and four blocks fit
+  // a CU at every (d, dtype); the compact records stay whole
+  static constexpr int kParts = F8 ? 1 : (kRecBytes > 512 ? kRecBytes / 512 : 1);
+  static constexpr int kPartRec = kRecBytes / kParts;                  // bytes of a record per part
+  static constexpr int kRowPartChunks = kRowChunks / kParts;           // chunks of a row per part
+  static constexpr int kTileBytes = kTilePages * kPartRec;             // LDS stage: one part of a tile
+  static constexpr int kLoads = kTileBytes / 16 / kScoreThreads;       // 16-byte loads per thread per part
   static constexpr int kLds = kTileBytes + kScoreTiles * (kTilePages + 1) * 4;
   static constexpr int kBlocksPerCu = (160 * 1024) / (kLds + 1024) >= 4 ? 4 : (160 * 1024) / (kLds + 1024);
   // coefficient table, doubles per (b, g) row: [box wave][i][j][q-, q+] (head
@@ -100,30 +106,35 @@ struct ScoreCfg {
   static constexpr int kWarmLines = DIM * G * 8 / 64;    // 64-byte lines of one wave's region (G > 1)
 };
 
-// Tile loads: thread t fetches 16-byte chunks u*256 + t of the tile (a wave
-// instruction covers 1 KB of consecutive records); missing pages read record 0
-// and are masked later.
+// Tile loads, part `part` of the coordinates: thread t fetches 16-byte chunks
+// u*256 + t of the part's tile (chunk pos of a record's part is chunk c of row
+// pos / kRowPartChunks, c = part * kRowPartChunks + pos % kRowPartChunks; a
+// wave instruction covers runs of consecutive bytes); missing pages read
+// record 0 and are masked later.
 template <typename T, int DIM, int G, bool F8, int L>
 __device__ __forceinline__ void score_load_tile(u32x4 (&r)[L], const char *mbase, const int *phys, int g, int hkv,
-                                                int tid) {
+                                                int tid, int part) {
   using C = ScoreCfg<T, DIM, G, F8>;
 #pragma unroll
   for (int u = 0; u < L; ++u) {
     const int off = (u * kScoreThreads + tid) * 16;
-    const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
+    const int rec = off / C::kPartRec, pos = (off % C::kPartRec) / 16;
+    const int gpos = C::kParts == 1 ? pos
+                                    : (pos / C::kRowPartChunks) * C::kRowChunks + part * C::kRowPartChunks +
+                                          pos % C::kRowPartChunks;
     const int ph = max(phys[rec], 0);
-    r[u] = *reinterpret_cast<const u32x4 *>(mbase + ((size_t)ph * hkv + g) * C::kRecBytes + pos * 16);
+    r[u] = *reinterpret_cast<const u32x4 *>(mbase + ((size_t)ph * hkv + g) * C::kRecBytes + gpos * 16);
   }
 }
-// ... and into LDS, chunk pos of record rec at slot pos ^ (rec & 7)
+// ... and into LDS, chunk pos of record rec's part at slot pos ^ (rec & 7)
 template <typename T, int DIM, int G, bool F8, int L>
 __device__ __forceinline__ void score_stash_tile(const u32x4 (&r)[L], unsigned char *buf, int tid) {
   using C = ScoreCfg<T, DIM, G, F8>;
 #pragma unroll
   for (int u = 0; u < L; ++u) {
     const int off = (u * kScoreThreads + tid) * 16;
-    const int rec = off / C::kRecBytes, pos = (off % C::kRecBytes) / 16;
-    *reinterpret_cast<u32x4 *>(buf + rec * C::kRecBytes + ((pos ^ (rec & 7)) * 16)) = r[u];
+    const int rec = off / C::kPartRec, pos = (off % C::kPartRec) / 16;
+    *reinterpret_cast<u32x4 *>(buf + rec * C::kPartRec + ((pos ^ (rec & 7)) * 16)) = r[u];
   }
 }
 
@@ -226,18 +237,20 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
       for (int i = 0; i < C::kWarmLines; ++i) warm ^= cl[(C::kWarmLines + i) * 16];
     }
   }
-  // two register buffers: tile lt + 1 is requested once tile lt is in LDS (with
-  // more in flight from the start the per-tile latency grows with the deeper
-  // memory queue and the first tile arrives later, measured on cold HBM)
+  // two register buffers: step st + 1 (a part of a tile) is requested once step
+  // st is in LDS (with more in flight from the start the per-tile latency grows
+  // with the deeper memory queue and the first tile arrives later, measured on
+  // cold HBM)
+  constexpr int NP = C::kParts;
   u32x4 ring[2][C::kLoads];
   // tile loads are issued at raised wave priority (measured: 0.1-0.6 us per launch
   // faster; the whole prologue at raised priority was slower)
   __builtin_amdgcn_s_setprio(3);
-  score_load_tile<T, DIM, G, F8>(ring[0], mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid);
+  score_load_tile<T, DIM, G, F8>(ring[0], mbase, s_phys[0], row0 % D.Hkv, D.Hkv, tid, 0);
   __builtin_amdgcn_s_setprio(0);
 
   const double c = D.scale, c2 = D.scale * D.scale;
-  const unsigned char *rec = tile + lane * C::kRecBytes;
+  const unsigned char *rec = tile + lane * C::kPartRec;
   const int sw = lane & 7;
   float outv[kScoreTiles][G];
 #pragma unroll
@@ -248,61 +261,60 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
 #pragma unroll
   for (int lt = 0; lt < kScoreTiles; ++lt) {
     if (lt < nt) {
-      if (lt > 0) lds_barrier();  // the previous tile is fully read
-      score_stash_tile<T, DIM, G, F8>(ring[lt & 1], tile, tid);
-      asm volatile("" ::: "memory");
-      if (lt + 1 < nt) {
-        __builtin_amdgcn_s_setprio(3);  // the loads issue ahead of other waves' FMA stream
-        score_load_tile<T, DIM, G, F8>(ring[(lt + 1) & 1], mbase, s_phys[lt + 1],
-                                       ((t_begin + lt + 1) / tiles_per_row) % D.Hkv, D.Hkv, tid);
-        __builtin_amdgcn_s_setprio(0);
-      }
-      lds_barrier();
-      if (lt == 0) asm volatile("" ::"s"(warm));
-      if (lt == 0) EKV_MARK(0, 2);
-
       // ---- lane = page.  Box waves: acc[j] = sum_i (q-_i kmin_i + q+_i kmax_i)
       // for head h0 + j, coordinate by coordinate; mean / variance waves:
       // acc[h] = sum_i coef[i][h] * row_i (q for the mean row, q^2 for the variance row).
+      // The parts come in coordinate order, so the sums run over i in index order.
       const int row = (t_begin + lt) / tiles_per_row;
       const double *cf = cf0 + (size_t)(row - row0) * C::kCoefRow;
       const bool ok = s_phys[lt][lane] >= 0;
-      if (wave < 2) {
-        if (G > 1 || wave == 0) {  // wave-uniform
-          double acc[kGH];
+      double acc[G];
 #pragma unroll
-          for (int j = 0; j < kGH; ++j) acc[j] = 0.0;
+      for (int h = 0; h < G; ++h) acc[h] = 0.0;
+#pragma unroll
+      for (int part = 0; part < NP; ++part) {
+        const int st = lt * NP + part;
+        if (st > 0) lds_barrier();  // the previous step is fully read
+        score_stash_tile<T, DIM, G, F8>(ring[st & 1], tile, tid);
+        asm volatile("" ::: "memory");
+        if (st + 1 < nt * NP) {
+          const int nl = (st + 1) / NP, np_ = (st + 1) % NP;
+          __builtin_amdgcn_s_setprio(3);  // the loads issue ahead of other waves' FMA stream
+          score_load_tile<T, DIM, G, F8>(ring[(st + 1) & 1], mbase, s_phys[nl],
+                                         ((t_begin + nl) / tiles_per_row) % D.Hkv, D.Hkv, tid, np_);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        lds_barrier();
+        if (st == 0) asm volatile("" ::"s"(warm));
+        if (st == 0) EKV_MARK(0, 2);
+        const int i0 = part * C::kRowPartChunks * kE;  // first coordinate of the part
+        if (wave < 2) {
+          if (G > 1 || wave == 0) {  // wave-uniform
 #pragma unroll 2
-          for (int ch = 0; ch < C::kRowChunks; ++ch) {
-            double xn[kE], xp[kE];
-            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (ch ^ sw) * 16), xn);
-            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((C::kRowChunks + ch) ^ sw) * 16), xp);
+            for (int ch = 0; ch < C::kRowPartChunks; ++ch) {
+              double xn[kE], xp[kE];
+              Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + (ch ^ sw) * 16), xn);
+              Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((C::kRowPartChunks + ch) ^ sw) * 16), xp);
 #pragma unroll
-            for (int e = 0; e < kE; ++e) {
-              const double *ci = cf + (size_t)(ch * kE + e) * kGH * 2;
+              for (int e = 0; e < kE; ++e) {
+                const double *ci = cf + (size_t)(i0 + ch * kE + e) * kGH * 2;
 #pragma unroll
-              for (int j = 0; j < kGH; ++j) {
-                // exact products (bf16 x bf16 in 16 bits, f32 x f32 in 48): fused == separate
-                acc[j] = __builtin_fma(ci[2 * j], xn[e], acc[j]);
-                acc[j] = __builtin_fma(ci[2 * j + 1], xp[e], acc[j]);
+                for (int j = 0; j < kGH; ++j) {
+                  // exact products (bf16 x bf16 in 16 bits, f32 x f32 in 48): fused == separate
+                  acc[j] = __builtin_fma(ci[2 * j], xn[e], acc[j]);
+                  acc[j] = __builtin_fma(ci[2 * j + 1], xp[e], acc[j]);
+                }
               }
             }
           }
-#pragma unroll
-          for (int j = 0; j < kGH; ++j) outv[lt][j] = ok ? __double2float_ru(c * acc[j]) : NAN;
-        }
-      } else {
-        double acc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = 0.0;
-        if (!F8) {
+        } else if (!F8) {
 #pragma unroll 2
-          for (int ch = 0; ch < C::kRowChunks; ++ch) {
+          for (int ch = 0; ch < C::kRowPartChunks; ++ch) {
             double x[kE];
-            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowChunks + ch) ^ sw) * 16), x);
+            Chunk<T>::unpack(*reinterpret_cast<const uint4 *>(rec + ((wave * C::kRowPartChunks + ch) ^ sw) * 16), x);
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-              const double *ci = cf + (size_t)(ch * kE + e) * G;
+              const double *ci = cf + (size_t)(i0 + ch * kE + e) * G;
 #pragma unroll
               for (int h = 0; h < G; ++h) {
                 if constexpr (sizeof(T) == 2)
@@ -329,6 +341,13 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
             }
           }
         }
+      }
+      if (wave < 2) {
+        if (G > 1 || wave == 0) {
+#pragma unroll
+          for (int j = 0; j < kGH; ++j) outv[lt][j] = ok ? __double2float_ru(c * acc[j]) : NAN;
+        }
+      } else {
         const double sc = wave == 2 ? c : c2;
 #pragma unroll
         for (int h = 0; h < G; ++h) outv[lt][h] = ok ? (float)(sc * acc[h]) : NAN;
