@@ -2061,10 +2061,14 @@ static hipError_t launch_dec_t(const Dims &D, const DecodeParams &dp, const KsAr
     (void)hipFuncSetAttribute((const void *)rows_kernel<T, DIM>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  // blocks per row (chunks at most); those past a row's bound on chunks leave
-  // at once.  An odd count spreads the rows' first blocks over the XCDs
-  // (blocks go to the XCDs in turn).
-  const int nh = std::max(1, std::min(kHelpers - 1, ka.ns));
+  // blocks per row (chunks at most).  A chunk of a large row holds its slot
+  // while it waits for its row's last block, so more chunks per row leave fewer
+  // rows in flight; measured on gfx950 (slice decode): 512 rows of 10^5 entries
+  // 7 chunks 2.20 ms (1 chunk 3.12, 3 2.84, 15 2.30, 31 2.75), 32 rows of ~10^6
+  // tokens (full cache) 15 chunks 504 us (7 541, 31 ~600).  Blocks past a row's
+  // bound on chunks leave at once.  An odd count spreads the rows' first blocks
+  // over the XCDs (blocks go to the XCDs in turn).
+  const int nh = std::max(1, std::min(std::min(kHelpers - 1, ka.ns), rows >= 256 ? 7 : 15));
   RowsArgs ra{v_pool, out, tau, ka.weights_out, ka.ns, nh};
   const long long grid = (long long)rows * nh;
   hipLaunchKernelGGL((rows_kernel<T, DIM>), dim3((unsigned)grid), dim3(kDThreads), lds, s, D, dp, ra, w);
