@@ -67,15 +67,6 @@ const GaussConsts &gauss_consts() {
   return gc;
 }
 
-unsigned long long next_epoch() {
-  static std::atomic<unsigned long long> ctr{
-      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull};
-  const unsigned long long mask = (1ull << 40) - 1;
-  unsigned long long e;
-  do { e = ctr.fetch_add(1) & mask; } while (e == 0);
-  return e;
-}
-
 static thread_local char g_err[256] = "";
 
 static int32_t hip_status(hipError_t e) {

@@ -338,29 +338,5 @@ __device__ __forceinline__ bool arrive_last(unsigned int *counter, unsigned int 
   return *flag_smem != 0;
 }
 
-// Same handshake for a counter that may hold garbage (a fresh workspace): the
-// counter packs (epoch << 24 | arrivals); an arrival that finds another epoch
-// restarts the count.  `epoch` (1 .. 2^40-1) comes from the host per launch;
-// the last block resets the counter to 0, which no epoch matches.
-__device__ __forceinline__ bool arrive_last_ep(unsigned long long *ctr, unsigned long long epoch,
-                                               unsigned int expected, int *flag_smem) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long old = atomicAdd(ctr, 0ull);
-    unsigned long long nv;
-    for (;;) {
-      nv = ((old >> 24) == epoch) ? old + 1ull : ((epoch << 24) | 1ull);
-      const unsigned long long prev = atomicCAS(ctr, old, nv);
-      if (prev == old) break;
-      old = prev;
-    }
-    const bool last = (nv & 0xFFFFFFull) == (unsigned long long)expected;
-    if (last) atomicExch(ctr, 0ull);
-    *flag_smem = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *flag_smem != 0;
-}
 
 }  // namespace ekv

@@ -9,30 +9,35 @@
 // alpha-entmax (Peters, Niculae & Martins 2019): with X_t = (alpha-1) s_t,
 // p_t = [X_t - tau]_+^(1/(alpha-1)), tau the root of F(tau) = sum_t p_t = 1.
 //
-// Two launches.
+// The decode for many query-head rows, for sets per KV head and for the full
+// cache (a set per query head over a few rows goes to decode_items.hip).  Two
+// launches.
 //  1. scores_kernel.  A block takes one KV head (b, g) and one slice of the
 //     sequence's pages.  It finds each query head's kept pages inside the slice
 //     (a 64-way search of the ascending set), merges them into the group's
 //     union, reads each union page's K slice once and scores it for every head
 //     of the group that kept it (bf16 products are exact in fp64; fp64 sums).
-//     Per (row, slice) it stores the entries the threshold step reads: when the
-//     slice's scores fit in registers, only the candidates X > (slice max) - 1
-//     with their token ids (compact); otherwise every kept token's X in place
-//     (dense, token id implicit).  F(max X - 1) >= 1, so tau >= max X - 1 and
-//     no other token of the row can carry weight.
-//  2. rows_kernel.  A leader block per row reads the slices' summaries.  A row
-//     with at most 4096 entries is finished by its leader: a certified lower
-//     bound on tau from counts above max - 2^-i, the candidates above it into
-//     LDS, tau by Newton from the left with an exact last piece (or the
-//     sparsemax sort form), then the V rows of the support.  A larger row goes
-//     to helper blocks in three steps, each started by the previous one: an
-//     integer histogram of the entries, from which bounds of F at the bin edges
-//     certify a window [e_lo, e_hi] holding tau; the moments of the entries
-//     above e_hi and the entries inside the window (the step's last block
-//     solves for tau exactly); the weighted V gather, merged in helper order.
-//     A block waits only for blocks of lower index, which the hardware
-//     dispatches first, and every wait ends after a time limit (the row then
-//     reads NaN).  Every sum has a fixed order, so results repeat bit for bit.
+//     Scores pass through an LDS stage in batches; after each batch a head's
+//     entries above (running max) - 1 are appended to its entries with their
+//     V row.  F(max X - 1) >= 1, so tau >= max X - 1: no other token of the
+//     row can carry weight, and the running max never exceeds the row's.
+//     Per (row, slice) a summary: entry count, max, min, first position.
+//  2. rows_kernel.  Up to nh blocks per row read the summaries and keep the
+//     slices whose max exceeds the row's max - 1.  A row of at most 4096
+//     entries is finished by one block from registers: a certified lower bound
+//     on tau from counts above max - 2^-i, the candidates above it into LDS,
+//     tau by Newton from the left with an exact last piece (or the sparsemax
+//     sort form), then the V rows of the support; up to 16384 entries one
+//     block takes them in rounds, each round tightening the bound.  Larger rows
+//     are split into chunks that compact their candidates in place for the
+//     row's last block, or, above 32768 entries, go through three steps, each
+//     started by the previous one: an integer histogram of the entries, from
+//     which bounds of F at the bin edges certify a window [e_lo, e_hi] holding
+//     tau; the moments of the entries above e_hi and the entries inside the
+//     window (the step's last block solves for tau exactly); the weighted V
+//     gather, merged in chunk order.  A chunk waits only for its own row's last
+//     block, every wait ends after a time limit (the row then reads NaN), and
+//     every sum has a fixed order, so results repeat bit for bit.
 //
 // Full cache (the decode that reads every cached token, one of the baselines of
 // the summary's efficiency results, section 4): the same two launches with the
@@ -56,8 +61,7 @@ constexpr int kHelpers = 32;      // helper blocks per row and step, at most
 constexpr int kBins = 4096;       // histogram bins of a large row
 constexpr int kSlot = 128;        // window entries a helper hands over
 constexpr int kWin = 4096;        // window entries the solving helper keeps in LDS
-constexpr int kWbuf = kHelpers * kSlot;  // candidates a leader keeps in its window buffer
-constexpr unsigned kStHist = 2, kStMom = 3, kStGath = 4, kStDone = 0xFFu;  // row steps (0: scores written)
+constexpr unsigned kStMom = 3, kStGath = 4, kStDone = 0xFFu;  // steps of a large row (0: scores written)
 constexpr unsigned long long kSpinTicks = 20000000ull;                     // 0.2 s of the 100 MHz clock
 constexpr int kLargeN = 32768;  // rows with more entries take the histogram route
 constexpr int kStStride = 32;  // row step flags 128 bytes apart, so waiting blocks of different rows poll different lines
@@ -77,8 +81,7 @@ struct DecodeWs {
   double *crec;       // [rows][kHelpers][16] chunk records (entries kept, bound, counts, start, compacted)
   unsigned *hist;     // [rows][kBins]
   double *hpart;      // [rows][kHelpers][8] moment partials
-  double *wbuf;       // [rows][kHelpers][kSlot] window entries (a leader's candidates: kWbuf)
-  uint32_t *wtok;     // [rows][kHelpers][kSlot] token ids of a leader's candidates
+  double *wbuf;       // [rows][kHelpers][kSlot] window entries handed over by each chunk
   float *opart;       // [rows][kHelpers][d] partial outputs
 };
 
@@ -1508,6 +1511,10 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
   double hlo = fmax(thr, mn);
   double hw = (mx - hlo) / (double)kBins;
   if (!(hw > 0.0) || !(hw < INFINITY)) hw = 1.0 / (double)kBins;
+  // bins by a product with 1/w: its rounding moves an entry by at most one
+  // bin, which the window's bounds allow for (a bin's entries are taken to lie
+  // anywhere in the bins beside it)
+  const double inv_hw = 1.0 / hw;
   if (nc == 1 && !large && M > kChunkCap) {
     // a lone block over more entries than its registers hold: rounds of
     // kChunkCap entries (16 per thread).  The counts of the rounds so far
@@ -1630,7 +1637,7 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
           const double x = bt.v[u];
           count1(x);
           if (large && x > hlo) {
-            const double f = floor((x - hlo) / hw);
+            const double f = floor((x - hlo) * inv_hw);
             const int bin = !(f >= 0.0) ? 0 : (f >= (double)kBins ? kBins - 1 : (int)f);
             atomicAdd(&sm.hist[bin], 1u);
           }
@@ -2008,7 +2015,6 @@ static DecodeWs carve_decode(const Dims &D, int ns, long long item_cap, void *ba
   w.hist = cv.take<unsigned>(rows * kBins);
   w.hpart = cv.take<double>(rows * kHelpers * 8);
   w.wbuf = cv.take<double>(rows * kHelpers * kSlot);
-  w.wtok = cv.take<uint32_t>(rows * kHelpers * kSlot);
   w.opart = cv.take<float>(rows * kHelpers * D.d);
   if (bytes) *bytes = cv.bytes();
   return w;

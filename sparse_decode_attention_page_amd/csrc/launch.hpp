@@ -31,9 +31,6 @@ struct GaussConsts {
 };
 const GaussConsts &gauss_consts();
 
-// per-launch epoch for arrival counters that may hold garbage (1 .. 2^40-1)
-unsigned long long next_epoch();
-
 hipError_t launch_build_meta(const Dims &D, int dtype, bool f8, const void *k_pool, const int32_t *page_table,
                              const int32_t *seq_lens, const int32_t *from_token, void *meta,
                              hipStream_t s);
