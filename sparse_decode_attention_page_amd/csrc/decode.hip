@@ -186,43 +186,117 @@ __device__ __forceinline__ void wave_bounds(const int32_t *list, int n, int key1
 // =========================================================== 1. scores kernel
 constexpr int kXl = 2048;  // X values a scores block stages in LDS (a batch of union pages)
 
-// 16 consecutive K coordinates as loaded (two or four 16-byte loads), unpacked
-// to floats where they are used
-template <typename T>
-struct KRaw;
-template <>
-struct KRaw<uint16_t> {
-  uint4 v[2];
+// C consecutive K coordinates of one token as loaded (bf16: C/2 words, fp32: C
+// words), converted to fp64 where they are used
+template <typename T, int C>
+struct KVec;
+template <int C>
+struct KVec<uint16_t, C> {
+  uint32_t w[C / 2];
   __device__ __forceinline__ void load(const uint16_t *p) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    v[0] = q[0];
-    v[1] = q[1];
-  }
-  __device__ __forceinline__ void unpack(float (&f)[16]) const {
+    if constexpr (C % 8 == 0) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f[8 * c + 0] = bf16lo(v[c].x); f[8 * c + 1] = bf16hi(v[c].x);
-      f[8 * c + 2] = bf16lo(v[c].y); f[8 * c + 3] = bf16hi(v[c].y);
-      f[8 * c + 4] = bf16lo(v[c].z); f[8 * c + 5] = bf16hi(v[c].z);
-      f[8 * c + 6] = bf16lo(v[c].w); f[8 * c + 7] = bf16hi(v[c].w);
+      for (int c = 0; c < C / 8; ++c) {
+        const uint4 u = reinterpret_cast<const uint4 *>(p)[c];
+        w[4 * c + 0] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
+      }
+    } else {
+      static_assert(C == 4, "bf16 coordinates come in fours or eights");
+      const uint2 u = *reinterpret_cast<const uint2 *>(p);
+      w[0] = u.x; w[1] = u.y;
     }
   }
+  __device__ __forceinline__ double at(int i) const {
+    return (double)((i & 1) ? bf16hi(w[i / 2]) : bf16lo(w[i / 2]));
+  }
 };
-template <>
-struct KRaw<float> {
-  float4 v[4];
+template <int C>
+struct KVec<float, C> {
+  float w[C];
   __device__ __forceinline__ void load(const float *p) {
-    const float4 *q = reinterpret_cast<const float4 *>(p);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = q[c];
-  }
-  __device__ __forceinline__ void unpack(float (&f)[16]) const {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      f[4 * c + 0] = v[c].x; f[4 * c + 1] = v[c].y; f[4 * c + 2] = v[c].z; f[4 * c + 3] = v[c].w;
+    for (int c = 0; c < C / 4; ++c) {
+      const float4 u = reinterpret_cast<const float4 *>(p)[c];
+      w[4 * c + 0] = u.x; w[4 * c + 1] = u.y; w[4 * c + 2] = u.z; w[4 * c + 3] = u.w;
     }
   }
+  __device__ __forceinline__ double at(int i) const { return (double)w[i]; }
 };
+
+// Lane pairings inside the lanes of one token: level J pairs lane e with
+// e ^ m_J, m_J = 1, 2, 7, 15, 16 for J = 0..4 (two quad permutes, the mirrors
+// inside 8 and 16 lanes, a swizzle across rows).  Each m_J has J as its top
+// bit, so the pairings of J = L-1 .. 0 taken in turn join all 2^L lanes.
+constexpr int pair_mask(int j) { return j == 0 ? 1 : j == 1 ? 2 : j == 2 ? 7 : j == 3 ? 15 : 16; }
+template <int kCtrl>
+__device__ __forceinline__ double mov_dpp_f64(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, kCtrl, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), kCtrl, 0xF, 0xF, true);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+template <int kJ>
+__device__ __forceinline__ double pair_f64(double v) {
+  if constexpr (kJ == 0) return mov_dpp_f64<0xB1>(v);        // quad_perm [1,0,3,2]
+  else if constexpr (kJ == 1) return mov_dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  else if constexpr (kJ == 2) return mov_dpp_f64<0x141>(v);  // row_half_mirror
+  else if constexpr (kJ == 3) return mov_dpp_f64<0x140>(v);  // row_mirror
+  else return __shfl_xor(v, 16, kWave);
+}
+
+// The per-head partials of a token's 2^L lanes are summed in L levels (level
+// l pairs by m_J, J = L-1-l).  In the first lg G levels a lane keeps the lower
+// half of its slots and adds its partner's upper half (a reduce-scatter); in
+// the rest partners add their one slot.  Lane e holds head f(e) ^ i in slot i,
+// with f linear over GF(2) and chosen so that partners line up:
+// f(e ^ m_J) = f(e) ^ (slots handed over at that level), i.e. column J of f is
+// that count xor the columns of m_J's lower bits.  Lane e ends with the full
+// sum of head f(e); partners' sums take the same operands, so lanes of one
+// head agree bit for bit.
+constexpr int head_map_col(int L, int lg_g, int j) {
+  const int l = L - 1 - j;
+  int x = l < lg_g ? (1 << lg_g) >> (l + 1) : 0;
+  for (int b = 0; b < j; ++b)
+    if ((pair_mask(j) >> b) & 1) x ^= head_map_col(L, lg_g, b);
+  return x;
+}
+template <int L, int kLgG>
+__device__ __forceinline__ int head_map(int e) {
+  int r = 0;
+#pragma unroll
+  for (int j = 0; j < L; ++j)
+    if ((e >> j) & 1) r ^= head_map_col(L, kLgG, j);
+  return r;
+}
+template <int kJ, int kV, int G>
+__device__ __forceinline__ double head_sum_levels(double (&acc)[G]) {
+  if constexpr (kJ < 0) {
+    return acc[0];
+  } else if constexpr (kV > 1) {
+    constexpr int kH = kV / 2;
+#pragma unroll
+    for (int i = 0; i < kH; ++i) acc[i] += pair_f64<kJ>(acc[i + kH]);
+    return head_sum_levels<kJ - 1, kH, G>(acc);
+  } else {
+    acc[0] += pair_f64<kJ>(acc[0]);
+    return head_sum_levels<kJ - 1, 1, G>(acc);
+  }
+}
+
+// max over the kSg lanes of the thread's team inside its wave (kSg = 32: the
+// wave's halves, 64: the wave); uniform over the team.  All 64 lanes active.
+template <int kSg>
+__device__ __forceinline__ double team_max_w(double v) {
+  v = fmax(v, dpp_f64<kDppXor1>(v));
+  v = fmax(v, dpp_f64<kDppXor2>(v));
+  v = fmax(v, dpp_f64<kDppRor4>(v));
+  v = fmax(v, dpp_f64<kDppRor8>(v));
+  const double m0 = fmax(readlane_f64(v, 0), readlane_f64(v, 16));
+  const double m1 = fmax(readlane_f64(v, 32), readlane_f64(v, 48));
+  if constexpr (kSg == 64) return fmax(m0, m1);
+  else return (threadIdx.x & 32) ? m1 : m0;
+}
+
 struct KsArgs {
   const void *q, *k_pool;
   const int32_t *page_table, *seq_lens, *sel_idx, *sel_cnt;
@@ -244,29 +318,42 @@ __device__ __forceinline__ int ks_row_items(const Dims &D, const KsArgs &a, int 
 template <typename T, int DIM, int P, int G>
 __global__ __launch_bounds__(kDThreads)
 void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
-  constexpr int kParts = DIM / 16;                            // threads per token, 16 coordinates each
-  constexpr int kUpp = P * kParts;                            // (token, part) units per page
-  constexpr int kTpp = kUpp < kDThreads ? kUpp : kDThreads;   // threads per page
-  constexpr int kPpi = kDThreads / kTpp;                      // pages per pass
-  constexpr int kUpt = kUpp / kTpp;                           // units per thread and page
-  constexpr int kLdsPages = kXl / (P * G);                   // union pages whose X fits the LDS stage
-  static_assert(kTpp % kWave == 0, "a page's threads form whole waves");
+  // scoring: kL lanes per token, kC coordinates each, q of the lane's
+  // coordinates for every head in registers (fp64)
+  constexpr int kC = 32 / G < 16 ? 32 / G : 16;
+  constexpr int kLpt = DIM / kC;
+  constexpr int kL = kLpt == 2 ? 1 : kLpt == 4 ? 2 : kLpt == 8 ? 3 : kLpt == 16 ? 4 : 5;
+  constexpr int kLgG = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  constexpr int kTpp = kDThreads / kLpt;  // tokens per pass
+  constexpr int kLdsTok = kXl / G;        // tokens per head in the LDS stage (a batch)
+  constexpr int kXs = kLdsTok + 8;        // a head's stage row (padded: the heads' rows start in other banks)
+  constexpr int kPpb = kLdsTok / kTpp;    // passes per batch
+  constexpr int kKw = kC * (int)sizeof(T) / 4;
+  constexpr int kRing = 32 / kKw >= 4 ? 4 : 2;  // K buffers in turn (kRing - 1 passes ahead)
+  static_assert((1 << kL) == kLpt && kLpt >= G && kLpt <= 32, "a token's lanes split its heads");
+  static_assert(kPpb % kRing == 0 && kLdsTok % P == 0, "a batch is whole passes and whole pages");
+  static_assert(P % (kWave / kLpt) == 0, "a wave's tokens lie in one page");
+  // compaction: a team of kS threads per head, kSg of them in one wave
+  constexpr int kS = kDThreads / G;
+  constexpr int kSg = kS < kWave ? kS : kWave;
+  constexpr int kWpt = kS / kSg;          // waves per team
+  constexpr int kTw = kLdsTok / kWpt;     // stage tokens per team wave
+  constexpr int kGr = kTw / kSg;          // groups of kSg consecutive tokens
+  static_assert(kSg == 32 || kSg == 64, "a team fills a wave or its halves");
   __shared__ unsigned umask[kMaxR];
   __shared__ int ulist[kMaxR];
-  __shared__ uint32_t uphys[kMaxR];
+  __shared__ uint32_t urow[kMaxR];   // union page: V row of its slot 0, (physical page * Hkv + g) * P
+  __shared__ uint32_t uinfo[kMaxR];  // union page: heads that kept it | tokens << 8
   __shared__ int ptab[kMaxR];  // the slice's page-table entries
   __shared__ int s_lo[G], s_hi[G];
   __shared__ long long s_base[G];
   __shared__ int s_items[G];
   __shared__ unsigned s_bad, s_nu;
-  __shared__ double s_red[kDThreads / kWave][2 * G];
-  __shared__ double s_mx[G], s_mn[G];
-  __shared__ double s_mnw[kDThreads / kWave][G];  // per wave: min of the entries it stored
+  __shared__ double s_tm[G][kWpt];  // per team wave: max (then min)
+  __shared__ int s_tc[G][kWpt];     // per team wave: entries of the batch
   __shared__ long long red64[kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
-  __shared__ unsigned long long scan64[kDThreads / kWave];
-  __shared__ __align__(16) float qs[G][DIM];
-  __shared__ double xl[kXl];
+  __shared__ double xl[G * kXs];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int ns = a.ns;
   const int gi = blockIdx.x / ns, s = blockIdx.x % ns;
@@ -286,6 +373,18 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
   for (int i = 0; i < kMaxR / kDThreads; ++i) {
     const int o = tid + i * kDThreads;
     ptv[i] = (o < R && p0 + o < np) ? a.page_table[(size_t)b * MP + p0 + o] : -1;
+  }
+  // the lane's q coordinates, every head, slot i holding head hl ^ i
+  const int e = tid % kLpt;
+  const unsigned zt = (unsigned)(tid / kLpt);
+  const int hl = head_map<kL, kLgG>(e);
+  double qd[G][kC];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float qf[kC];
+    load_vec<kC>(q + (size_t)(r0 + (hl ^ i)) * DIM + e * kC, qf);
+#pragma unroll
+    for (int c = 0; c < kC; ++c) qd[i][c] = (double)qf[c];
   }
 
   // ---- the group's rows: first item (items of every earlier row), counts
@@ -378,7 +477,8 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
     const int o = ulist[k];
     const int ph = ptab[o];
     const bool ok = ph >= 0 && ph < D.num_phys;
-    uphys[k] = ok ? (uint32_t)ph : 0u;
+    urow[k] = ok ? ((uint32_t)ph * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P : 0u;
+    uinfo[k] = umask[o] | (uint32_t)min(P, L - (p0 + o) * P) << 8;
     if (!ok) atomicOr(&s_bad, umask[o]);
   }
   __syncthreads();
@@ -408,186 +508,142 @@ void scores_kernel(Dims D, DecodeParams dp, KsArgs a, DecodeWs ws) {
       for (int i = tid; i < kBins; i += kDThreads) ws.hist[(size_t)(r0 + h) * kBins + i] = 0u;
   EKV_MARK(0, 1);
 
-  // ---- q of the group's heads in LDS
-  const int j = tid / kTpp, u0 = tid % kTpp, e = u0 % kParts;
-  for (int i = tid; i < G * DIM; i += kDThreads) qs[i / DIM][i % DIM] = load_f(q, (size_t)r0 * DIM + i);
-  __syncthreads();
-  const int npass = (nU + kPpi - 1) / kPpi;
-  double lmax[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lmax[h] = -INFINITY;
-  if (tid < (kDThreads / kWave) * G) s_mnw[tid / G][tid % G] = INFINITY;
-  // union pages in batches of kLdsPages, whose X fits the LDS stage; after a
-  // batch, each head's running max takes in the batch and the batch's entries
-  // above (running max) - 1 are appended to the head's entries (token ids
-  // explicit).  The running max never exceeds the slice max, so the stored
-  // entries hold every entry above (slice max) - 1, in index order.
-  static_assert(kLdsPages % kPpi == 0, "a batch is whole passes");
-  constexpr int kPpb = kLdsPages / kPpi;  // passes per batch
-  auto lo_of = [&](int h) __attribute__((always_inline)) { return s_lo[a.mode == 0 ? h : 0]; };
+  // ---- scores of the union pages' tokens, kTpp tokens per pass.  Union token
+  // z (page z / P of the union, slot z % P) goes to the lane group zt of pass
+  // z / kTpp; the lanes' per-head partials are summed by head_sum_levels, and
+  // one lane per head and token puts its X into the LDS stage (-inf for heads
+  // that did not keep the page and for slots past the sequence end; positions
+  // past the union's last page are written but never read).
+  const bool wr = (e & ((1 << (kL - kLgG)) - 1)) == 0;
+  const int npass = (nU * P + kTpp - 1) / kTpp;
+  const int nbatch = (npass + kPpb - 1) / kPpb;
+  const unsigned ulast = (unsigned)max(nU - 1, 0);
   // every call issues its loads (past the last union page: that page again,
   // unused), so the count of loads in flight after a buffer's is fixed and its
   // wait leaves the later buffers' loads in flight
-  auto load_pass = [&](int pass, KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
-    const int k = min(pass * kPpi + j, nU - 1);
-    const size_t ph = uphys[k];
-#pragma unroll
-    for (int u = 0; u < kUpt; ++u) {
-      const int t = (u0 + u * kTpp) / kParts;
-      kv[u].load(k_pool + ((ph * D.Hkv + g) * P + t) * DIM + e * 16);
-    }
+  auto load_pass = [&](int pass, KVec<T, kC> &kv) __attribute__((always_inline)) {
+    const unsigned z = (unsigned)pass * kTpp + zt;
+    const unsigned k = min(z / P, ulast);
+    kv.load(k_pool + (size_t)(urow[k] + z % P) * DIM + e * kC);
   };
-  // X of one pass (-inf for heads that did not keep the page and for slots
-  // past the sequence end) into the LDS stage at the batch's page position
-  auto score_pass = [&](int pass, const KRaw<T> (&kv)[kUpt]) __attribute__((always_inline)) {
-    const int k = pass * kPpi + j;
-    const bool act = k < nU;
-    const int kl = k % kLdsPages;
-    const int o = act ? ulist[k] : 0;
-    const unsigned m = act ? (umask[o] & live) : 0u;
-    const int ntok = min(P, L - (p0 + o) * P);
+  auto score_pass = [&](int pass, const KVec<T, kC> &kv) __attribute__((always_inline)) {
+    const unsigned z = (unsigned)pass * kTpp + zt;
+    const unsigned k = z / P, t = z % P;
+    const unsigned info = uinfo[min(k, ulast)];
+    const unsigned m = k < (unsigned)nU ? (info & live) : 0u;
+    double acc[G];
 #pragma unroll
-    for (int u = 0; u < kUpt; ++u) {
-      const int t = (u0 + u * kTpp) / kParts;
-      float kf[16];
-      kv[u].unpack(kf);
+    for (int i = 0; i < G; ++i) {
+      acc[i] = kv.at(0) * qd[i][0];  // exact products
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        double x = -INFINITY;
-        if (m & (1u << h)) {  // uniform per wave
-          const float4 *qp = reinterpret_cast<const float4 *>(&qs[h][e * 16]);
-          double acc = 0.0;
+      for (int c = 1; c < kC; ++c) acc[i] = __builtin_fma(kv.at(c), qd[i][c], acc[i]);
+    }
+    const double sum = head_sum_levels<kL - 1, G, G>(acc);
+    const double x = ((m >> hl) & 1u) && t < (info >> 8) ? dp.a * (dp.c * sum) : -INFINITY;
+    if (wr) xl[hl * kXs + z % kLdsTok] = x;
+  };
+
+  // ---- a finished batch: head th's team reads the head's stage row, takes
+  // its max into the running max and appends the entries above (running max)
+  // - 1 to the head's entries, in index order (ballots inside each group of kSg
+  // consecutive tokens; the team's waves take consecutive shares).  The running
+  // max never exceeds the slice max, so the stored entries hold every entry
+  // above (slice max) - 1.
+  const int th = tid / kS, tw = (tid % kS) / kSg, tl = lane % kSg;
+  const unsigned long long tmask = kSg == kWave ? ~0ull : (((1ull << kSg) - 1ull) << (lane & kSg));
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const size_t hbase = (size_t)(s_base[th] + s_lo[a.mode == 0 ? th : 0]) * P;
+  double rmax = -INFINITY, mn = INFINITY;
+  int ncnt = 0;
+  auto compact_batch = [&](int bt) __attribute__((always_inline)) {
+    lds_barrier();  // the batch's stage writes before the reads below
+    const int kb0 = bt * (kLdsTok / P);
+    double v[kGr];
+    double bm = -INFINITY;
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 qv = qp[c4];
-            acc = __builtin_fma((double)kf[4 * c4 + 0], (double)qv.x, acc);  // exact products
-            acc = __builtin_fma((double)kf[4 * c4 + 1], (double)qv.y, acc);
-            acc = __builtin_fma((double)kf[4 * c4 + 2], (double)qv.z, acc);
-            acc = __builtin_fma((double)kf[4 * c4 + 3], (double)qv.w, acc);
-          }
+    for (int i = 0; i < kGr; ++i) {
+      const int zl = tw * kTw + i * kSg + tl;
+      v[i] = kb0 + zl / P < nU ? xl[th * kXs + zl] : -INFINITY;
+      bm = fmax(bm, v[i]);
+    }
+    bm = team_max_w<kSg>(bm);
+    if constexpr (kWpt > 1) {
+      if (tl == 0) s_tm[th][tw] = bm;
+      lds_barrier();
 #pragma unroll
-          for (int sh = kParts / 2; sh > 0; sh >>= 1) acc += __shfl_xor(acc, sh, kWave);
-          if (t < ntok) x = dp.a * (dp.c * acc);
-        }
-        lmax[h] = fmax(lmax[h], x);
-        if (act && e == 0) xl[(kl * P + t) * G + h] = x;
+      for (int w = 0; w < kWpt; ++w) bm = fmax(bm, s_tm[th][w]);
+    }
+    rmax = fmax(rmax, bm);
+    const double thr = rmax - 1.0;
+    int pre = 0, tot = 0;  // entries of the team's earlier waves, of the whole team
+    if constexpr (kWpt > 1) {
+      int cw = 0;
+#pragma unroll
+      for (int i = 0; i < kGr; ++i) cw += __popcll(__ballot(v[i] > thr) & tmask);
+      if (tl == 0) s_tc[th][tw] = cw;
+      lds_barrier();
+#pragma unroll
+      for (int w = 0; w < kWpt; ++w) {
+        const int c = s_tc[th][w];
+        pre += w < tw ? c : 0;
+        tot += c;
       }
     }
-  };
-  // a finished batch: running max, then the batch's entries above it - 1
-  int ncnt[G];
+    size_t at = hbase + ncnt + pre;
 #pragma unroll
-  for (int h = 0; h < G; ++h) ncnt[h] = 0;
-  // the batch of union pages from kb0: each thread takes kTpt consecutive
-  // tokens of the stage, every head; one packed scan per four heads places
-  // the entries
-  constexpr int kTpt = kXl / G / kDThreads;  // stage tokens per thread
-  static_assert(kTpt * G * kDThreads == kXl, "the stage splits evenly");
-  auto compact_batch = [&](int kb0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const double wm = wave_max(lmax[h]);
-      if (lane == 0) s_red[wv][h] = wm;
-    }
-    lds_barrier();  // also orders the batch's LDS stage writes before the reads below
-    double rmax[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double mm = s_red[0][h];
-      for (int w = 1; w < kDThreads / kWave; ++w) mm = fmax(mm, s_red[w][h]);
-      rmax[h] = mm;  // lmax is each thread's max so far
-    }
-    const int tk0 = tid * kTpt;
-    auto xat = [&](int i, int h) __attribute__((always_inline)) {
-      return kb0 + (tk0 + i) / P < nU ? xl[(tk0 + i) * G + h] : -INFINITY;
-    };
-    unsigned long long pk[(G + 3) / 4];
-#pragma unroll
-    for (int q = 0; q < (G + 3) / 4; ++q) pk[q] = 0ull;
-#pragma unroll
-    for (int i = 0; i < kTpt; ++i)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (xat(i, h) > rmax[h] - 1.0) pk[h / 4] += 1ull << (16 * (h % 4));
-#pragma unroll
-    for (int q = 0; q < (G + 3) / 4; ++q) {
-      unsigned long long tot;
-      const unsigned long long pre = block_excl_scan64<true>(pk[q], scan64, &tot);
-      // the totals are the block's: keep them (and the counts) in scalar registers
-      tot = ((unsigned long long)__builtin_amdgcn_readfirstlane((unsigned)(tot >> 32)) << 32) |
-            (unsigned)__builtin_amdgcn_readfirstlane((unsigned)tot);
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const int h = 4 * q + hh;
-        if (h < G) {
-          size_t at = (size_t)(s_base[h] + lo_of(h)) * P + ncnt[h] + (int)((pre >> (16 * hh)) & 0xFFFFull);
-          double mn = INFINITY;
-#pragma unroll
-          for (int i = 0; i < kTpt; ++i) {
-            const double x = xat(i, h);
-            if (x > rmax[h] - 1.0) {
-              const int k = kb0 + (tk0 + i) / P, t = (tk0 + i) % P;
-              ws.cx[at] = x;
-              ws.ct[at] = (uphys[k] * (uint32_t)D.Hkv + (uint32_t)g) * (uint32_t)P + (uint32_t)t;
-              if (a.weights_out) ws.cl[at] = (uint32_t)((p0 + ulist[k]) * P + t);
-              mn = fmin(mn, x);
-              ++at;
-            }
-          }
-          mn = wave_min_d(mn);
-          if (lane == 0) s_mnw[wv][h] = fmin(s_mnw[wv][h], mn);
-          ncnt[h] += (int)((tot >> (16 * hh)) & 0xFFFFull);
-        }
+    for (int i = 0; i < kGr; ++i) {
+      const bool keep = v[i] > thr;
+      const unsigned long long bal = __ballot(keep) & tmask;
+      if (keep) {
+        const int zl = tw * kTw + i * kSg + tl;
+        const int k = kb0 + zl / P, t = zl % P;
+        const size_t w = at + __popcll(bal & below);
+        ws.cx[w] = v[i];
+        ws.ct[w] = urow[k] + (uint32_t)t;
+        if (a.weights_out) ws.cl[w] = (uint32_t)((p0 + ulist[k]) * P + t);
+        mn = fmin(mn, v[i]);
       }
+      at += __popcll(bal);
     }
+    ncnt += kWpt > 1 ? tot : (int)(at - hbase - ncnt);
     lds_barrier();  // the stage is read before the next batch overwrites it
   };
 
-  // ---- scores of the union pages, kPpi pages per pass, K two passes ahead
-  // three K buffers used in turn by the unrolled loop (no register copies,
-  // which would wait for loads still in flight)
-  KRaw<T> kA[kUpt], kB[kUpt], kC[kUpt];
-  auto step = [&](int pass, const KRaw<T> (&cur)[kUpt], KRaw<T> (&ahead)[kUpt]) __attribute__((always_inline)) {
-    load_pass(pass + 2, ahead);
-    score_pass(pass, cur);
-    if ((pass + 1) % kPpb == 0 || pass + 1 == npass) compact_batch((pass - pass % kPpb) * kPpi);
-  };
+  // ---- the passes, kRing K buffers used in turn (no register copies, which
+  // would wait for loads still in flight), kRing - 1 passes ahead
+  KVec<T, kC> kb[kRing];
   if (npass > 0) {
-    load_pass(0, kA);
-    load_pass(1, kB);
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i) load_pass(i, kb[i]);
+    for (int bt = 0; bt < nbatch; ++bt) {
+      const int pe = min(npass, (bt + 1) * kPpb);
 #pragma unroll 1
-    for (int pass = 0; pass < npass; pass += 3) {
-      step(pass, kA, kC);
-      if (pass + 1 < npass) step(pass + 1, kB, kA);
-      if (pass + 2 < npass) step(pass + 2, kC, kB);
+      for (int p = bt * kPpb; p < pe; p += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) {
+          load_pass(p + i + kRing - 1, kb[(i + kRing - 1) % kRing]);
+          score_pass(p + i, kb[i]);
+        }
+      }
+      compact_batch(bt);
     }
   }
-  // slice max per head, and the min of the stored entries
+  // ---- per (row, slice) summary: entry count, max, min of the stored entries
+  mn = -team_max_w<kSg>(-mn);
+  if constexpr (kWpt > 1) {
+    if (tl == 0) s_tm[th][tw] = mn;
+    lds_barrier();
 #pragma unroll
-  for (int h = 0; h < G; ++h) lmax[h] = wave_max(lmax[h]);
-  if (lane == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_red[wv][h] = lmax[h];
-  __syncthreads();
-  if (tid < G) {
-    double m = s_red[0][tid], n = s_mnw[0][tid];
-    for (int w = 1; w < kDThreads / kWave; ++w) {
-      m = fmax(m, s_red[w][tid]);
-      n = fmin(n, s_mnw[w][tid]);
-    }
-    s_mx[tid] = m;
-    s_mn[tid] = n;
+    for (int w = 0; w < kWpt; ++w) mn = fmin(mn, s_tm[th][w]);
   }
-  __syncthreads();
-  // ---- per (row, slice) summary
-  if (tid < G) {
-    const int h = tid, r = r0 + h;
+  if (tid % kS == 0) {
+    const int h = th, r = r0 + h;
     const bool bad = (s_bad >> h) & 1u;
     const size_t o = (size_t)r * ns + s;
-    ws.s_cnt[o] = bad ? 0 : ncnt[h];
-    ws.s_max[o] = bad ? NAN : s_mx[h];
-    ws.s_min[o] = s_mn[h];
-    ws.s_start[o] = bad ? 0u : (uint32_t)((s_base[h] + lo_of(h)) * P);
+    ws.s_cnt[o] = bad ? 0 : ncnt;
+    ws.s_max[o] = bad ? NAN : rmax;
+    ws.s_min[o] = mn;
+    ws.s_start[o] = bad ? 0u : (uint32_t)hbase;
   }
   EKV_MARK(0, 2);
 }
