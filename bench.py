@@ -149,9 +149,21 @@ def main():
         q, k, v, meta = reps[r]
         E.entmax_decode_sparse(shape, q, k, v, pt, sl, sel, cnt, alpha, out, ws=ws_d)
 
+    ws_sg = E.workspace(shape, E.CALL_SCORE_GAUSS)
+
+    def score_select(r):
+        """score + selection: one call for the Gaussian policy (the selector's
+        bracket comes from the scoring launch), score_pages + select_pages_topk
+        otherwise."""
+        if args.policy == "gauss":
+            q, k, v, meta = reps[r]
+            E.score_select_pages_gauss(shape, q, meta, pt, sl, box, mu, var, alpha, wl.delta, sel, cnt, ws=ws_sg)
+        else:
+            score(r)
+            select()
+
     def step(r):
-        score(r)
-        select()
+        score_select(r)
         decode(r)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -327,10 +339,11 @@ def main():
             def stream_step():
                 seq2.add_(1)
                 E.append_token(shape, knew, vnew, k2, v2, pt, seq2, meta2)
-                E.score_pages(shape, reps[0][0], meta2, pt, seq2, box, mu, var, ws=ws_s)
                 if args.policy == "gauss":
-                    E.select_pages_gauss(shape, box, mu, var, seq2, alpha, wl.delta, sel3, cnt3, ws=ws_g)
+                    E.score_select_pages_gauss(shape, reps[0][0], meta2, pt, seq2, box, mu, var, alpha, wl.delta,
+                                               sel3, cnt3, ws=ws_sg)
                 else:
+                    E.score_pages(shape, reps[0][0], meta2, pt, seq2, box, mu, var, ws=ws_s)
                     E.select_pages_topk(shape, box, seq2, wl.topk or 64, sel3, cnt3, ws=ws_t)
                 E.entmax_decode_sparse(shape, reps[0][0], k2, v2, pt, seq2, sel3, cnt3, alpha, out3, ws=ws_d)
 
@@ -356,8 +369,10 @@ def main():
             L_end = int(seq2.max().item())
             stream_res = {"us_per_step": round(st_us, 3), "steps": n_st,
                           "context_end": L_end, "context_start": L_end - n_st,
-                          "step": "append_token (K/V row + page metadata) + score_pages + "
-                                  "select_pages_" + args.policy + " + entmax_decode_sparse, one HIP graph per step"}
+                          "step": "append_token (K/V row + page metadata) + " +
+                                  ("score_select_pages_gauss" if args.policy == "gauss"
+                                   else "score_pages + select_pages_topk") +
+                                  " + entmax_decode_sparse, one HIP graph per step"}
             # append_token's own launch duration: a graph of 20 launches (the
             # same token rewritten, so every launch does the same work)
             gap = torch.cuda.CUDAGraph()
@@ -440,8 +455,8 @@ def main():
                 return a.elapsed_time(b) * 1e3 / n_rep
 
             variants = {}
-            for name, f8, grp in (("compact_meta", True, False), ("group_sets", False, True),
-                                  ("compact_meta_group_sets", True, True)):
+            for name, f8, grp in (("separate_calls", False, False), ("compact_meta", True, False),
+                                  ("group_sets", False, True), ("compact_meta_group_sets", True, True)):
                 us = graph_us(lambda r, f8=f8, grp=grp: v_step(r, f8, grp), args.steps)
                 v_step(0, f8, grp)  # replica 0's selection, for the quality figures below
                 torch.cuda.synchronize()
@@ -522,7 +537,8 @@ def main():
                          f"{int(seq.max())} tokens in pages of {P}; alpha={alpha}, "
                          + (f"Gaussian selection Delta={wl.delta}" if args.policy == "gauss"
                             else f"top-k {wl.topk or 64}")),
-            "step": "score_pages + select_pages_" + args.policy + " + entmax_decode_sparse",
+            "step": ("score_select_pages_gauss (score_pages + select_pages_gauss in one call)"
+                     if args.policy == "gauss" else "score_pages + select_pages_topk") + " + entmax_decode_sparse",
             "replicas": R,
             "launch": "hip graph replay" if graphs else "eager",
             "kv_dtype": wl.dtype,
@@ -694,12 +710,11 @@ def passage_leg(args, name):
     cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
     out = torch.empty((B, Hq, d), device="cuda")
     sl, pt = inp.seq_lens, inp.page_table
-    ws_s, ws_g = E.workspace(shape, E.CALL_SCORE), E.workspace(shape, E.CALL_GAUSS)
+    ws_sg = E.workspace(shape, E.CALL_SCORE_GAUSS)
 
     def select(r):
         q, k, v, m = reps[r]
-        E.score_pages(shape, q, m, pt, sl, box, mu, var, ws=ws_s)
-        E.select_pages_gauss(shape, box, mu, var, sl, alpha, wl.delta, sel, cnt, ws=ws_g)
+        E.score_select_pages_gauss(shape, q, m, pt, sl, box, mu, var, alpha, wl.delta, sel, cnt, ws=ws_sg)
 
     select(0)
     torch.cuda.synchronize()

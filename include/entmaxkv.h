@@ -96,7 +96,8 @@ enum entmaxkv_call {
   ENTMAXKV_CALL_SOFTMAX_SPARSE = 7,
   ENTMAXKV_CALL_TOPK_GROUP = 8,
   ENTMAXKV_CALL_GAUSS_GROUP = 9,
-  ENTMAXKV_CALL_DECODE_GROUP = 10
+  ENTMAXKV_CALL_DECODE_GROUP = 10,
+  ENTMAXKV_CALL_SCORE_GAUSS = 11
 };
 
 /* Bytes of workspace a call needs for this shape (0 if none).  Returns 0 for
@@ -246,6 +247,23 @@ int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const 
                            double n_sigma, const uint8_t *seq_mask, int32_t *sel_idx,
                            int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
                            hipStream_t stream);
+
+/*
+ * score_select_pages_gauss -- score_pages followed by select_pages_gauss in one
+ * call ([EntmaxKV s.2.A] then [s.2.B, policy 2]): the same box/mu/var,
+ * sel_idx/sel_cnt and tau_hat bits as the two calls made in turn (same
+ * arguments, same meaning, same errors), with the selector's bracket (the
+ * largest lone-page bound and the largest top quadrature point of each row)
+ * taken from maxima the scoring launch writes as it stores mu and var, so the
+ * selector's own pass over the statistics for it is not run.  bf16 or fp32
+ * records (not the compact format).  Both steps are asynchronous on `stream`.
+ * ws: entmaxkv_workspace_bytes(shape, ENTMAXKV_CALL_SCORE_GAUSS).
+ */
+int32_t score_select_pages_gauss(const entmaxkv_shape *shape, const void *q, const void *meta,
+                                 const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                 float *var, double alpha, double delta, double n_sigma, const uint8_t *seq_mask,
+                                 int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /*
  * entmax_decode_sparse -- [EntmaxKV s.2.C]: alpha-entmax attention of each

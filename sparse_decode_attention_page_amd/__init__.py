@@ -23,7 +23,7 @@ _lib = None
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = range(6)
 F32, BF16 = 0, 1
 (CALL_SCORE, CALL_TOPK, CALL_GAUSS, CALL_DECODE_SPARSE, CALL_DECODE_FULL, CALL_SOFTMAX, CALL_SOFTMAX_SPARSE,
- CALL_TOPK_GROUP, CALL_GAUSS_GROUP, CALL_DECODE_GROUP) = range(1, 11)
+ CALL_TOPK_GROUP, CALL_GAUSS_GROUP, CALL_DECODE_GROUP, CALL_SCORE_GAUSS) = range(1, 12)
 
 EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_f8", "append_token",
            "select_pages_topk", "select_pages_gauss", "select_pages_topk_group", "select_pages_gauss_group",
@@ -31,7 +31,7 @@ EXPORTS = ("build_page_meta", "score_pages", "build_page_meta_f8", "score_pages_
            "entmax_decode_sparse", "entmax_decode_full", "softmax_decode_full", "softmax_decode_sparse",
            "entmaxkv_workspace_bytes", "entmaxkv_status_string", "entmaxkv_gauss_hermite16",
            "entmaxkv_stream_read", "score_pages_noalloc", "entmaxkv_score_scratch_bytes",
-           "entmaxkv_decode_workspace_bytes")
+           "entmaxkv_decode_workspace_bytes", "score_select_pages_gauss")
 
 
 class EntmaxKVError(RuntimeError):
@@ -93,6 +93,9 @@ def load(path: str | None = None):
     lib.select_pages_topk.argtypes = [sh, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.select_pages_gauss.restype = i32
     lib.select_pages_gauss.argtypes = [sh, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp, vp, vp, sz, vp]
+    lib.score_select_pages_gauss.restype = i32
+    lib.score_select_pages_gauss.argtypes = [sh, vp, vp, vp, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp, vp, vp, sz,
+                                             vp]
     lib.select_pages_topk_group.restype = i32
     lib.select_pages_topk_group.argtypes = [sh, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.select_pages_gauss_group.restype = i32
@@ -367,6 +370,21 @@ def select_pages_gauss(shape: Shape, box, mu, var, seq_lens, alpha, delta, sel_i
             *_sel_args(shape, sel_idx, sel_cnt), _ptr(tau_hat, _torch().float64, "tau_hat", _N(shape).rows))
     _call("select_pages_gauss", shape, CALL_GAUSS, ws, args, stream)
     return sel_idx, sel_cnt
+
+
+def score_select_pages_gauss(shape: Shape, q, meta, page_table, seq_lens, box, mu, var, alpha, delta,
+                             sel_idx, sel_cnt, n_sigma=3.0, seq_mask=None, tau_hat=None, ws=None, stream=None):
+    """score_pages then select_pages_gauss in one call (the selector's bracket
+    comes from the scoring launch); the same outputs as the two calls in turn."""
+    torch = _torch()
+    n = _N(shape)
+    qp, pt, sl, bp, mp, vp = _score_args(shape, q, page_table, seq_lens, box, mu, var)
+    mt = _ptr(meta, _kv_dtype(shape), "meta", n.meta)
+    args = (qp, mt, pt, sl, bp, mp, vp, float(alpha), float(delta), float(n_sigma),
+            _ptr(seq_mask, torch.uint8, "seq_mask", n.batch), *_sel_args(shape, sel_idx, sel_cnt),
+            _ptr(tau_hat, torch.float64, "tau_hat", n.rows))
+    _call("score_select_pages_gauss", shape, CALL_SCORE_GAUSS, ws, args, stream)
+    return box, mu, var, sel_idx, sel_cnt
 
 
 def select_pages_topk_group(shape: Shape, box, seq_lens, k, sel_idx, sel_cnt, seq_mask=None, ws=None,

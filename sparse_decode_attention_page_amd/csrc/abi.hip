@@ -145,6 +145,15 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const probe_u32x4 *__r
 }
 }  // namespace
 
+// score_select_pages_gauss: the scorer's table, the bracket summary, the selector's workspace
+static size_t score_gauss_ws_bytes(const Dims &D) {
+  Carve cv(nullptr);
+  cv.take<char>(score_ws_bytes(D));
+  cv.take<double>(score_summary_doubles(D));
+  cv.take<char>(gauss_ws_bytes(D));
+  return cv.bytes();
+}
+
 extern "C" {
 
 size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call) {
@@ -161,6 +170,7 @@ size_t entmaxkv_workspace_bytes(const entmaxkv_shape *shape, int32_t which_call)
     case ENTMAXKV_CALL_TOPK_GROUP: return topk_group_ws_bytes(D);
     case ENTMAXKV_CALL_GAUSS_GROUP: return gauss_group_ws_bytes(D);
     case ENTMAXKV_CALL_DECODE_GROUP: return decode_group_ws_bytes(D);
+    case ENTMAXKV_CALL_SCORE_GAUSS: return score_gauss_ws_bytes(D);
   }
   return 0;
 }
@@ -280,6 +290,36 @@ int32_t select_pages_topk(const entmaxkv_shape *shape, const float *box, const i
   if (!box || !seq_lens || !sel_idx || !sel_cnt || k <= 0) return ENTMAXKV_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(topk_ws_bytes(D), ws, ws_bytes))) return st;
   return hip_status(launch_topk(D, box, seq_lens, k, seq_mask, sel_idx, sel_cnt, ws, stream));
+}
+
+int32_t score_select_pages_gauss(const entmaxkv_shape *shape, const void *q, const void *meta,
+                                 const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                 float *var, double alpha, double delta, double n_sigma, const uint8_t *seq_mask,
+                                 int32_t *sel_idx, int32_t *sel_cnt, double *tau_hat, void *ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  Dims D;
+  int32_t st = check_shape(shape, &D);
+  if (st) return st;
+  if (!q || !meta || !page_table || !seq_lens || !box || !mu || !var || !sel_idx || !sel_cnt)
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (misaligned16(q, meta)) return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if (!(alpha > 1.0) || !std::isfinite(alpha) || !(delta >= 0.0) || !std::isfinite(delta) ||
+      !(n_sigma >= 0.0) || !std::isfinite(n_sigma))
+    return ENTMAXKV_ERR_INVALID_ARGUMENT;
+  if ((st = check_ws(score_gauss_ws_bytes(D), ws, ws_bytes))) return st;
+  Carve cv(ws);
+  void *ws_score = cv.take<char>(score_ws_bytes(D));
+  double *summ = cv.take<double>(score_summary_doubles(D));
+  void *ws_gauss = cv.take<char>(gauss_ws_bytes(D));
+  ScoreSummary sm;
+  sm.summ = summ;
+  sm.x_top = gauss_consts().x[15];
+  sm.nzero = gauss_zero_words(D, ws_gauss, &sm.zero);
+  hipError_t e = launch_score_summary(D, shape->dtype, q, meta, page_table, seq_lens, box, mu, var, ws_score, sm,
+                                      stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_gauss_from_summary(D, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, sel_idx,
+                                              sel_cnt, tau_hat, summ, ws_gauss, stream));
 }
 
 int32_t select_pages_gauss(const entmaxkv_shape *shape, const float *box, const float *mu,

@@ -70,11 +70,14 @@ struct GaussParams {
   int ibeta;         // 1, 2 or 0 (generic)
   int rows;
   int vec;           // box/mu/var 16-byte aligned and max_pages % 4 == 0
+  int sum_tiles;     // 0: the bracket launch's chunk partials; else the scorer's summary, entries per row
 };
 
 struct GaussWs {
-  double *part;      // [rows][nchunk][2]  chunk max of the lone-page bound, chunk's largest point
   unsigned *cnt;     // [rows][kNodes][kNB] sum of n_p over the points of node j in bin b
+  unsigned *ctr;     // [rows][2]          arrival counters of K2 and K3 (zeroed by K1)
+  double *part;      // [rows][nchunk][2]  chunk max of the lone-page bound, chunk's largest point
+  const double *summ;  // [rows][sum_tiles][2] the scorer's bracket terms (when sum_tiles > 0)
   int *win;          // [rows][2]          window bins k_lo, k_hi
   double *mom;       // [rows][nchunk][3]  moments above e_hi about e_hi
   int *wcnt;         // [rows][nchunk]     window points per chunk
@@ -82,7 +85,6 @@ struct GaussWs {
   int *list;         // [rows][max_pages]  kept / undecided pages (undecided: bit 31), chunk segments
   int *lcnt;         // [rows][nchunk]
   double *amax;      // [rows][nchunk][2]  chunk's largest estimate and its page
-  unsigned *ctr;     // [rows][2]          arrival counters of K2 and K3 (zeroed by K1)
 };
 
 __device__ __forceinline__ bool page_valid(float bx, float m, float v) {
@@ -169,16 +171,29 @@ struct Pages4 {
   }
 };
 
-// Row bracket from the chunk partials: every thread loads its share (all in
-// flight at once), then a block max (max does not depend on the order).  Called
-// by every thread of the block; red holds 2 kGThreads / kWave doubles.
-__device__ __forceinline__ void row_bracket(const GaussParams &gp, const GaussWs &ws, const RowCtx &rc, double &lo,
-                                            double &hi, double *red) {
+// Row bracket from the chunk partials (or from the scorer's summary: the
+// largest mean over full pages and the largest top point, per 64-page tile;
+// the last page, when partial, adds its own lone-page bound): every thread
+// loads its share (all in flight at once), then a block max (max does not
+// depend on the order).  Called by every thread of the block; red holds
+// 2 kGThreads / kWave doubles.
+__device__ __forceinline__ void row_bracket(const Dims &D, const GaussParams &gp, const GaussWs &ws,
+                                            const RowCtx &rc, const float *box, const float *mu,
+                                            const float *var, double &lo, double &hi, double *red) {
   double l = -INFINITY, h = -INFINITY;
-  for (int c = threadIdx.x; c < rc.nch; c += kGThreads) {
-    const double2 v = *reinterpret_cast<const double2 *>(ws.part + ((size_t)rc.row * gp.nchunk + c) * 2);
-    l = fmax(l, v.x);
-    h = fmax(h, v.y);
+  if (gp.sum_tiles) {
+    const int nt = (rc.np + 63) / 64;
+    for (int c = threadIdx.x; c < nt; c += kGThreads) {
+      const double2 v = *reinterpret_cast<const double2 *>(ws.summ + ((size_t)rc.row * gp.sum_tiles + c) * 2);
+      l = fmax(l, v.x);
+      h = fmax(h, v.y);
+    }
+  } else {
+    for (int c = threadIdx.x; c < rc.nch; c += kGThreads) {
+      const double2 v = *reinterpret_cast<const double2 *>(ws.part + ((size_t)rc.row * gp.nchunk + c) * 2);
+      l = fmax(l, v.x);
+      h = fmax(h, v.y);
+    }
   }
   l = wave_max(l);
   h = wave_max(h);
@@ -194,6 +209,16 @@ __device__ __forceinline__ void row_bracket(const GaussParams &gp, const GaussWs
   for (int i = 1; i < nw; ++i) {
     lo = fmax(lo, red[i]);
     hi = fmax(hi, red[nw + i]);
+  }
+  if (gp.sum_tiles) {
+    lo = gp.a * lo - gp.lone_full;
+    hi = gp.a * hi;
+    const int nlast = rc.L - (rc.np - 1) * D.P;
+    if (rc.np > 0 && nlast < D.P) {
+      const size_t i = (size_t)rc.row * D.max_pages + rc.np - 1;
+      const float bx = box[i], m = mu[i], v2 = var[i];
+      if (page_valid(bx, m, v2)) lo = fmax(lo, gp.a * (double)m - lone_gap(nlast, gp));
+    }
   }
 }
 // Bin edges: e_b = lo + b w for b < kNB, e_kNB = hi.
@@ -301,7 +326,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_count_kernel(Dims D, GaussPar
   pg0.load(box, mu, var, base, p_begin + 4 * tid, D, gp);
   if (tid < kNodes) s_gx[tid] = gc.x[tid];  // read in the node loop below (ordered by row_bracket's barrier)
   double lo, hi;
-  row_bracket(gp, ws, rc, lo, hi, s_red);
+  row_bracket(D, gp, ws, rc, box, mu, var, lo, hi, s_red);
   if (!(hi > -INFINITY)) return;  // no valid page: K3 writes the empty result
   const double w = (hi - lo) / kNB, iw = 1.0 / w;
   {
@@ -542,7 +567,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_solve_kernel(
   }
   const int klo = ws.win[rc.row * 2 + 0], khi = ws.win[rc.row * 2 + 1];
   double lo, hi;
-  row_bracket(gp, ws, rc, lo, hi, s_red);
+  row_bracket(D, gp, ws, rc, box, mu, var, lo, hi, s_red);
   if (!(hi > -INFINITY)) {  // no pages, or none valid: empty selection
     if (chunk == 0 && tid == 0) {
       sel_cnt[rc.row] = 0;
@@ -982,6 +1007,7 @@ static GaussParams make_params(const Dims &D, double alpha, double delta, double
   gp.lone_full = gp.ibeta == 2 ? std::sqrt(2.5 / (double)D.P) : 2.5 / (double)D.P;
   gp.rows = D.B * D.Hq;
   gp.vec = 0;
+  gp.sum_tiles = 0;
   // about EKV_GAUSS_BLOCKS blocks over the (row, chunk) space; chunks are
   // multiples of 256 pages (4 per thread of one 1024-page group), at most
   // kMaxChunks per row
@@ -1001,8 +1027,10 @@ static GaussWs carve_gauss(const Dims &D, const GaussParams &gp, void *base, siz
   Carve cv(base);
   const size_t rows = (size_t)D.B * D.Hq;
   GaussWs w;
+  w.cnt = cv.take<unsigned>(rows * kNodes * kNB);  // counts and counters first: one zeroed range
+  w.ctr = cv.take<unsigned int>(rows * 2);
   w.part = cv.take<double>(rows * gp.nchunk * 2);
-  w.cnt = cv.take<unsigned>(rows * kNodes * kNB);
+  w.summ = nullptr;
   w.win = cv.take<int>(rows * 2);
   w.mom = cv.take<double>(rows * gp.nchunk * 3);
   w.wcnt = cv.take<int>(rows * gp.nchunk);
@@ -1010,7 +1038,6 @@ static GaussWs carve_gauss(const Dims &D, const GaussParams &gp, void *base, siz
   w.list = cv.take<int>(rows * (size_t)D.max_pages);
   w.lcnt = cv.take<int>(rows * gp.nchunk);
   w.amax = cv.take<double>(rows * gp.nchunk * 2);
-  w.ctr = cv.take<unsigned int>(rows * 2);
   if (bytes) *bytes = cv.bytes();
   return w;
 }
@@ -1022,10 +1049,10 @@ size_t gauss_ws_bytes(const Dims &D) {
   return bytes;
 }
 
-hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const float *var,
-                        const int32_t *seq_lens, double alpha, double delta, double n_sigma,
-                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
-                        double *tau_hat, void *ws, hipStream_t s) {
+static hipError_t launch_gauss_impl(const Dims &D, const float *box, const float *mu, const float *var,
+                                    const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                                    const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                                    double *tau_hat, const double *summ, void *ws, hipStream_t s) {
   GaussParams gp = make_params(D, alpha, delta, n_sigma);
   const GaussConsts &gc = gauss_consts();
   const int rows = D.B * D.Hq;
@@ -1039,13 +1066,39 @@ hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const 
   gp.vec = (al % 16 == 0 && D.max_pages % 4 == 0) ? 1 : 0;
   GaussWs w = carve_gauss(D, gp, ws, nullptr);
   const dim3 grid(grid_of(gp));
-  hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var, seq_lens,
-                     seq_mask, w);
+  if (summ) {  // bracket from the scorer's summary; counts and counters zeroed by the scorer
+    gp.sum_tiles = (D.max_pages + 63) / 64;
+    w.summ = summ;
+  } else {
+    hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var, seq_lens,
+                       seq_mask, w);
+  }
   hipLaunchKernelGGL(gauss_count_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var, seq_lens,
                      seq_mask, w);
   hipLaunchKernelGGL(gauss_solve_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var, seq_lens,
                      seq_mask, sel_idx, sel_cnt, tau_hat, w);
   return hipGetLastError();
+}
+
+hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const float *var,
+                        const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                        const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                        double *tau_hat, void *ws, hipStream_t s) {
+  return launch_gauss_impl(D, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, sel_idx, sel_cnt, tau_hat,
+                           nullptr, ws, s);
+}
+
+hipError_t launch_gauss_from_summary(const Dims &D, const float *box, const float *mu, const float *var,
+                                     const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                                     const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                                     double *tau_hat, const double *summ, void *ws, hipStream_t s) {
+  return launch_gauss_impl(D, box, mu, var, seq_lens, alpha, delta, n_sigma, seq_mask, sel_idx, sel_cnt, tau_hat,
+                           summ, ws, s);
+}
+
+long long gauss_zero_words(const Dims &D, void *ws, unsigned **zero) {
+  *zero = static_cast<unsigned *>(ws);
+  return (long long)D.B * D.Hq * (kNodes * kNB + 2);
 }
 
 EKV_TRACE_DUMP(ekv_trace_dump_gauss)

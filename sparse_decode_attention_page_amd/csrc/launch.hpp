@@ -44,6 +44,21 @@ hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const 
                         const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
                         float *var, void *ws, hipStream_t s);
 
+// score_pages that also writes the Gaussian selector's bracket terms (two
+// doubles per (query row, 64-page tile): the largest mean over the tile's valid
+// full pages, the largest mu + sqrt2 sigma x_top over its valid pages) to summ,
+// and zeroes the nzero words at zero (the selector's counts and counters).
+struct ScoreSummary {
+  double *summ = nullptr;
+  double x_top = 0.0;
+  unsigned *zero = nullptr;
+  long long nzero = 0;
+};
+size_t score_summary_doubles(const Dims &D);
+hipError_t launch_score_summary(const Dims &D, int dtype, const void *q, const void *meta,
+                                const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                float *var, void *ws, const ScoreSummary &sm, hipStream_t s);
+
 // score_pages with the coefficient table in the library's static device scratch
 size_t score_scratch_bytes();
 hipError_t launch_score_noalloc(const Dims &D, int dtype, const void *q, const void *meta,
@@ -60,6 +75,17 @@ hipError_t launch_gauss(const Dims &D, const float *box, const float *mu, const 
                         const int32_t *seq_lens, double alpha, double delta, double n_sigma,
                         const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
                         double *tau_hat, void *ws, hipStream_t s);
+// The selector's words that must be zero before its counting launch (counts
+// and arrival counters, contiguous at the start of its workspace region
+// returned in *zero), for a caller whose own launch zeroes them; then
+// launch_gauss_from_summary runs the selector with the bracket read from the
+// scorer's summary (summ, tiles_per_row entries per row) instead of its own
+// bracket launch.
+long long gauss_zero_words(const Dims &D, void *ws, unsigned **zero);
+hipError_t launch_gauss_from_summary(const Dims &D, const float *box, const float *mu, const float *var,
+                                     const int32_t *seq_lens, double alpha, double delta, double n_sigma,
+                                     const uint8_t *seq_mask, int32_t *sel_idx, int32_t *sel_cnt,
+                                     double *tau_hat, const double *summ, void *ws, hipStream_t s);
 
 // Decode workspaces: the item capacity (kept pages over all query-head rows)
 // follows from the bytes given; decode_ws_bytes is the size for every row's

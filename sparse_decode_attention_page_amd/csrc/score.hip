@@ -138,12 +138,22 @@ __device__ __forceinline__ void score_stash_tile(const u32x4 (&r)[L], unsigned c
   }
 }
 
-template <typename T, int DIM, int G, bool F8>
+// Zeroes block bi's share of the n words at z (SUM variant: the Gaussian
+// selector's counts and arrival counters, read by its next launches).
+__device__ __forceinline__ void zero_share(const ScoreSummary &sm, int bi, int nb, int tid) {
+  const long long per = (sm.nzero + nb - 1) / nb, z0 = (long long)bi * per;
+  const long long z1 = z0 + per < sm.nzero ? z0 + per : sm.nzero;
+  for (long long i = z0 + tid; i < z1; i += kScoreThreads) sm.zero[i] = 0u;
+}
+
+// SUM: also writes, per (query row, tile), the two maxima the Gaussian
+// selector's bracket is made of (see the epilogue).
+template <typename T, int DIM, int G, bool F8, bool SUM>
 __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPerCu)) void score_pages_kernel(
     Dims D, int tiles_per_row, int n_cu, const T *__restrict__ q, const T *__restrict__ meta,
     const int32_t *__restrict__ page_table, const int32_t *__restrict__ seq_lens, double *__restrict__ coef_w,
     const double *__restrict__ coef_r, float *__restrict__ box, float *__restrict__ mu,
-    float *__restrict__ var) {
+    float *__restrict__ var, ScoreSummary sm) {
   using C = ScoreCfg<T, DIM, G, F8>;
   constexpr int kE = C::kE;
   constexpr int kGH = C::kGH;  // box heads of each of waves 0 and 1 (G = 1: wave 0 only)
@@ -160,7 +170,10 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   const int lb = (n_cu > 0 && nb % n_cu == 0) ? (bi % n_cu) * (nb / n_cu) + bi / n_cu : bi;
   const int t_begin = lb * kScoreTiles;
   const int t_end = min(n_tiles, t_begin + kScoreTiles);
-  if (t_begin >= t_end) return;
+  if (t_begin >= t_end) {
+    if constexpr (SUM) zero_share(sm, bi, nb, tid);
+    return;
+  }
   const int nt = t_end - t_begin;
   const char *mbase = reinterpret_cast<const char *>(meta);
   const int row0 = t_begin / tiles_per_row, nrows = (t_end - 1) / tiles_per_row - row0 + 1;
@@ -356,6 +369,56 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
   }
   EKV_MARK(0, 3);
 
+  if constexpr (SUM) {
+    // The Gaussian selector's bracket from the values as stored (fp32), per
+    // (query row, tile): the largest mean over the tile's valid full pages and
+    // the largest top quadrature point mu + sqrt2 sigma x_16 over its valid
+    // pages (valid: box, mu and var finite).  Scaling by alpha - 1 > 0 and
+    // subtracting a constant are monotone in fp64, so the selector's bracket
+    // from these maxima has the bits of its own per-page maxima.
+    // Every wave hands its values to LDS; then wave w takes heads w, w + 4, ...
+    __shared__ float s_sb[kScoreTiles][G][kTilePages], s_sm[kScoreTiles][G][kTilePages],
+        s_sv[kScoreTiles][G][kTilePages];
+#pragma unroll
+    for (int lt = 0; lt < kScoreTiles; ++lt) {
+      if (wave < 2) {
+        if (G > 1 || wave == 0) {
+#pragma unroll
+          for (int j = 0; j < kGH; ++j) s_sb[lt][G == 1 ? 0 : wave * kGH + j][lane] = outv[lt][j];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) (wave == 2 ? s_sm : s_sv)[lt][h][lane] = outv[lt][h];
+      }
+    }
+    lds_barrier();
+#pragma unroll 1
+    for (int h = wave; h < G; h += 4) {
+#pragma unroll
+      for (int lt = 0; lt < kScoreTiles; ++lt) {
+        if (lt < nt) {
+          const int t = t_begin + lt;
+          const int row = t / tiles_per_row;
+          const int b = row / D.Hkv, g = row - b * D.Hkv, tin = t - row * tiles_per_row;
+          const int p = tin * kTilePages + lane;
+          const long long L = seq_len_clamped(seq_lens, b, D);
+          const float m = s_sm[lt][h][lane], v2 = s_sv[lt][h][lane], bx = s_sb[lt][h][lane];
+          const bool valid = p < s_np[lt] && isfinite(bx) && isfinite(m) && isfinite(v2);
+          const double md = (double)m;
+          double m1 = valid && (long long)(p + 1) * D.P <= L ? md : -INFINITY;
+          double tp = valid ? md + 1.4142135623730951 * sqrt(v2 > 0.0f ? (double)v2 : 0.0) * sm.x_top : -INFINITY;
+          m1 = wave_max(m1);
+          tp = wave_max(tp);
+          if (lane == 0) {
+            double *o = sm.summ + (((size_t)b * D.Hq + g * G + h) * tiles_per_row + tin) * 2;
+            o[0] = m1;
+            o[1] = tp;
+          }
+        }
+      }
+    }
+  }
+
   // ---- outputs: lane = page, 64 consecutive floats per (kind, head) and tile
 #pragma unroll
   for (int lt = 0; lt < kScoreTiles; ++lt) {
@@ -381,6 +444,7 @@ __global__ __launch_bounds__(kScoreThreads, (ScoreCfg<T, DIM, G, F8>::kBlocksPer
       }
     }
   }
+  if constexpr (SUM) zero_share(sm, bi, nb, tid);
   EKV_MARK(0, 4);
 }
 
@@ -402,10 +466,10 @@ static int device_cu_count() {
   return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-template <typename T, int DIM, int G, bool F8>
+template <typename T, int DIM, int G, bool F8, bool SUM>
 static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
                                  const int32_t *page_table, const int32_t *seq_lens, float *box,
-                                 float *mu, float *var, void *ws, hipStream_t s) {
+                                 float *mu, float *var, void *ws, const ScoreSummary &sm, hipStream_t s) {
   Carve cv(ws);
   double *coef = cv.take<double>((size_t)D.B * D.Hkv * 4 * D.d * D.G);
   const int tiles_per_row = (D.max_pages + kTilePages - 1) / kTilePages;
@@ -413,21 +477,21 @@ static hipError_t launch_score_t(const Dims &D, const void *q, const void *meta,
   const long long grid = (n_tiles + kScoreTiles - 1) / kScoreTiles;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G, F8>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s, D,
+  hipLaunchKernelGGL((score_pages_kernel<T, DIM, G, F8, SUM>), dim3((unsigned)grid), dim3(kScoreThreads), 0, s, D,
                      tiles_per_row, device_cu_count(), (const T *)q, (const T *)meta, page_table, seq_lens, coef,
-                     (const double *)coef, box, mu, var);
+                     (const double *)coef, box, mu, var, sm);
   return hipGetLastError();
 }
 
-template <typename T, int DIM, bool F8>
+template <typename T, int DIM, bool F8, bool SUM = false>
 static hipError_t launch_score_d(const Dims &D, const void *q, const void *meta,
                                  const int32_t *pt, const int32_t *sl, float *box, float *mu,
-                                 float *var, void *ws, hipStream_t s) {
+                                 float *var, void *ws, hipStream_t s, const ScoreSummary &sm = ScoreSummary{}) {
   switch (D.G) {
-    case 1: return launch_score_t<T, DIM, 1, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 2: return launch_score_t<T, DIM, 2, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 4: return launch_score_t<T, DIM, 4, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
-    case 8: return launch_score_t<T, DIM, 8, F8>(D, q, meta, pt, sl, box, mu, var, ws, s);
+    case 1: return launch_score_t<T, DIM, 1, F8, SUM>(D, q, meta, pt, sl, box, mu, var, ws, sm, s);
+    case 2: return launch_score_t<T, DIM, 2, F8, SUM>(D, q, meta, pt, sl, box, mu, var, ws, sm, s);
+    case 4: return launch_score_t<T, DIM, 4, F8, SUM>(D, q, meta, pt, sl, box, mu, var, ws, sm, s);
+    case 8: return launch_score_t<T, DIM, 8, F8, SUM>(D, q, meta, pt, sl, box, mu, var, ws, sm, s);
   }
   return hipErrorInvalidValue;
 }
@@ -446,6 +510,22 @@ hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const 
   }
   if (D.d == 64) return launch_score_d<float, 64, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
   return launch_score_d<float, 128, false>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s);
+}
+
+hipError_t launch_score_summary(const Dims &D, int dtype, const void *q, const void *meta,
+                                const int32_t *page_table, const int32_t *seq_lens, float *box, float *mu,
+                                float *var, void *ws, const ScoreSummary &sm, hipStream_t s) {
+  if (dtype == ENTMAXKV_BF16) {
+    if (D.d == 64)
+      return launch_score_d<uint16_t, 64, false, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s, sm);
+    return launch_score_d<uint16_t, 128, false, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s, sm);
+  }
+  if (D.d == 64) return launch_score_d<float, 64, false, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s, sm);
+  return launch_score_d<float, 128, false, true>(D, q, meta, page_table, seq_lens, box, mu, var, ws, s, sm);
+}
+
+size_t score_summary_doubles(const Dims &D) {
+  return (size_t)D.B * D.Hq * ((D.max_pages + kTilePages - 1) / kTilePages) * 2;
 }
 
 // ---------------------------------------------------- allocation-free variant

@@ -83,6 +83,11 @@ def test_bad_arguments():
                                   None) == E.ERR_INVALID_ARGUMENT
     assert lib.entmax_decode_full(s, FAKE, FAKE, FAKE, FAKE, FAKE, 2.0, 7, FAKE, None, None, FAKE, big,
                                   None) == E.ERR_INVALID_ARGUMENT
+    # the fused score + Gaussian selection checks both steps' arguments
+    assert lib.score_select_pages_gauss(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 0.5, 3.0, None, FAKE, FAKE,
+                                        None, FAKE, big, None) == E.ERR_INVALID_ARGUMENT
+    assert lib.score_select_pages_gauss(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.5, 0.5, 3.0, None, None, FAKE,
+                                        None, FAKE, big, None) == E.ERR_INVALID_ARGUMENT
     # sparse decode needs a selection
     assert lib.entmax_decode_sparse(s, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1.5, 0, FAKE, None, None,
                                     FAKE, big, None) == E.ERR_INVALID_ARGUMENT
@@ -113,6 +118,10 @@ def test_workspace_too_small_or_misaligned():
                                   need, None) == E.ERR_WORKSPACE
     assert lib.select_pages_gauss(s, FAKE, FAKE, FAKE, FAKE, 1.5, 0.5, 3.0, None, FAKE, FAKE, None,
                                   ctypes.c_void_p(264), need, None) == E.ERR_INVALID_ARGUMENT
+    fused = E.workspace_bytes(sh, E.CALL_SCORE_GAUSS)
+    assert fused >= need + E.workspace_bytes(sh, E.CALL_SCORE)
+    assert lib.score_select_pages_gauss(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.5, 0.5, 3.0, None, FAKE, FAKE,
+                                        None, FAKE, fused - 1, None) == E.ERR_WORKSPACE
     for call in (E.CALL_SCORE, E.CALL_DECODE_SPARSE, E.CALL_DECODE_FULL, E.CALL_SOFTMAX):
         assert E.workspace_bytes(sh, call) > 0
     assert E.workspace_bytes(sh, 99) == 0

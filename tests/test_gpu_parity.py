@@ -176,6 +176,45 @@ def test_select_gauss(case, alpha, delta):
     assert np.allclose(tg, to, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("alpha,delta", [(1.5, 0.5), (2.0, 0.5), (1.5, 0.0), (1.25, 0.5)])
+def test_score_select_gauss_fused(case, alpha, delta):
+    """score_select_pages_gauss: box/mu/var, sets and tau_hat are the bits of
+    score_pages then select_pages_gauss, and match the oracle (sets exactly,
+    tau_hat to 1e-12); a masked sequence's rows are left untouched."""
+    inp, D, meta_o, (box_o, mu_o, var_o) = case
+    t = torch()
+    meta = D.zeros_meta()
+    E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta)
+    mask = np.ones(inp.B, np.uint8)
+    if inp.B > 1:
+        mask[1] = 0
+    mk = t.from_numpy(mask).cuda()
+    box, mu, var = D.per_page(), D.per_page(), D.per_page()
+    sel, cnt = D.sel_buffers()
+    tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    for _ in range(2):  # the second call reuses the workspace (its counters were left at zero)
+        ws = E.workspace(D.shape, E.CALL_SCORE_GAUSS) if _ == 0 else ws
+        E.score_select_pages_gauss(D.shape, D.q, meta, D.pt, D.sl, box, mu, var, alpha, delta, sel, cnt,
+                                   seq_mask=mk, tau_hat=tau, ws=ws)
+    box2, mu2, var2 = D.per_page(), D.per_page(), D.per_page()
+    E.score_pages(D.shape, D.q, meta, D.pt, D.sl, box2, mu2, var2)
+    sel2, cnt2 = D.sel_buffers()
+    tau2 = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+    E.select_pages_gauss(D.shape, box2, mu2, var2, D.sl, alpha, delta, sel2, cnt2, seq_mask=mk, tau_hat=tau2)
+    for a, b in ((box, box2), (mu, mu2), (var, var2)):
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+    assert np.array_equal(cnt.cpu().numpy(), cnt2.cpu().numpy())
+    assert np.array_equal(sel.cpu().numpy(), sel2.cpu().numpy())
+    tg = tau.cpu().numpy()
+    assert np.array_equal(tg.view(np.uint64), tau2.cpu().numpy().view(np.uint64))
+    so, co, to = oracle.select_gauss(D.oshape, box_o, mu_o, var_o, inp.seq_lens, alpha, delta, seq_mask=mask)
+    keep = mask.astype(bool)
+    sg, cg = sel.cpu().numpy(), cnt.cpu().numpy()
+    assert sets_equal(sg[keep], cg[keep], so[keep], co[keep]) == []
+    assert np.allclose(tg[keep], to[keep], rtol=1e-12, atol=1e-12)
+    assert np.all(cg[~keep] == -1) and np.all(np.isnan(tg[~keep]))
+
+
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
 def test_entmax_decode_sparse_topk(case, alpha):
     inp, D, _, (box_o, _, _) = case
