@@ -1320,7 +1320,7 @@ __device__ __forceinline__ void finish_lds(const DecodeParams &dp, const RowsArg
   const int tid = threadIdx.x;
   double tau, z;
   const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
-  const double hi = mx - pow((double)max(nC, 1), -dp.a);  // F(hi) <= 1: at most nC entries above it
+  const double hi = mx - pow_neg_a((double)max(nC, 1), dp);  // F(hi) <= 1: at most nC entries above it
   if (dp.ibeta == 1 && dp.tau_method == 1) {
     tau = sparsemax_tau_sort(sm.lead.cx, nC, sm.lead.sortbuf, dred, s_kstar);
     double zz = 0.0;
@@ -1406,7 +1406,7 @@ __device__ __forceinline__ void row_finish(const DecodeParams &dp, const RowsArg
     finish_lds<T, DIM>(dp, ra, r, sm, nC, mx, Lb, dred, scan_scratch, s_tau, s_kstar, &tau, &z);
   } else {
     const Above none{0.0, 0.0, 0.0, 0.0, 0.0};
-    const double hi = mx - pow((double)nC, -dp.a);
+    const double hi = mx - pow_neg_a((double)nC, dp);
     solve_block(RegVals16{xv}, none, Lb, hi, dp, dred, tau, z);
     EKV_MARK(1, 4);
     if (tid == 0 && ra.tau) ra.tau[r] = tau / dp.a;

@@ -263,7 +263,7 @@ __device__ __forceinline__ double newton_tau(const Src &src, double n, double mx
                                              const DecodeParams &dp, double *dred, double *z_out) {
   const Red red;
   double lo = lo0;
-  double hi = mx - pow(n, -dp.a);
+  double hi = mx - pow_neg_a(n, dp);
   *z_out = 0.0;
   if (!(hi > lo)) return lo;
   if (kB == 1 || kB == 2) {
@@ -746,21 +746,32 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     EKV_MARK(1, 3);
     // the row's last block: segment offsets, the row's bound, then the
     // candidates above it into LDS
+    // every chunk's hand-off is requested at once (one round trip): thread t
+    // < nsplit kNThr takes count (chunk t / kNThr, threshold t % kNThr),
+    // threads below nsplit also their chunk's candidate count and bound
+    static_assert(kSplitMax * kNThr <= kDThreads, "one count per thread");
+    const bool has_n = tid < nsplit * kNThr;
+    int n_t = 0, c_t = 0;
+    double l_t = 0.0;
+    if (has_n) n_t = ld_agent(&ws.segn[((size_t)r * kSplitMax + tid / kNThr) * kNThr + tid % kNThr]);
     if (tid < nsplit) {
-      soff[tid + 1] = ld_agent(&ws.segcnt[(size_t)r * kSplitMax + tid]);
-      sL[tid] = ld_agent(&ws.segL[(size_t)r * kSplitMax + tid]);
-      sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
-    }
-    // the row's counts above mx - 2^-i are the chunks' counts summed: a bound
-    // as certified as each chunk's and tighter (about sqrt(chunks) for alpha 1.5)
-    if (tid < kNThr) {
-      int ct = 0;
-      for (int s2 = 0; s2 < nsplit; ++s2) ct += ld_agent(&ws.segn[((size_t)r * kSplitMax + s2) * kNThr + tid]);
-      s_cnt[0][tid] = ct;
+      c_t = ld_agent(&ws.segcnt[(size_t)r * kSplitMax + tid]);
+      l_t = ld_agent(&ws.segL[(size_t)r * kSplitMax + tid]);
     }
     const bool ipr_lds = cnt <= kIprLds;  // the merge below looks pages up in LDS
     if (ipr_lds)
       for (int k = tid; k < cnt; k += kDThreads) s_ipr[k] = ipr[k];
+    if (tid < kNThr) s_cnt[0][tid] = 0;
+    __syncthreads();
+    // the row's counts above mx - 2^-i are the chunks' counts summed (integer
+    // adds, in any order): a bound as certified as each chunk's and tighter
+    // (about sqrt(chunks) for alpha 1.5)
+    if (has_n) atomicAdd(&s_cnt[0][tid % kNThr], n_t);
+    if (tid < nsplit) {
+      soff[tid + 1] = c_t;
+      sL[tid] = l_t;
+      sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
+    }
     __syncthreads();
     if (tid == 0) {  // segment offsets (the first step's entry addresses need them)
       soff[0] = 0;
