@@ -1192,7 +1192,7 @@ __device__ __forceinline__ unsigned wait_step(const unsigned *state, unsigned ne
         v = 0u;
         break;
       }
-      __builtin_amdgcn_s_sleep(32);  // about 1 us between polls
+      __builtin_amdgcn_s_sleep(8);  // about 0.2 us between polls
     }
     *s_flag = v;
   }
@@ -1776,8 +1776,13 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if (tid < nc)
-      for (int f = 0; f < 13; ++f) s_rec[tid][f] = ld_agent(&ws.crec[((size_t)r * kHelpers + tid) * 16 + f]);
+    if (tid < nc) {  // all of a record's fields requested at once (one round trip)
+      double v[13];
+#pragma unroll
+      for (int f = 0; f < 13; ++f) v[f] = ld_agent(&ws.crec[((size_t)r * kHelpers + tid) * 16 + f]);
+#pragma unroll
+      for (int f = 0; f < 13; ++f) s_rec[tid][f] = v[f];
+    }
     __syncthreads();
     if (nan || N == 0) {
       if (nan) row_nan<DIM>(ra, r);
@@ -1951,8 +1956,13 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
   }
   if (arrive_last(&ws.ctr[4 * r + 1], (unsigned)nc, &s_last)) {
     // the row's last: tau from the moments and the window entries
-    if (tid < nc)
-      for (int f = 0; f < 5; ++f) s_hp[tid][f] = ld_agent(&ws.hpart[((size_t)r * kHelpers + tid) * 8 + f]);
+    if (tid < nc) {
+      double v[5];
+#pragma unroll
+      for (int f = 0; f < 5; ++f) v[f] = ld_agent(&ws.hpart[((size_t)r * kHelpers + tid) * 8 + f]);
+#pragma unroll
+      for (int f = 0; f < 5; ++f) s_hp[tid][f] = v[f];
+    }
     __syncthreads();
     if (tid == 0) {
       double a0 = 0.0, a1 = 0.0, a2 = 0.0, amin = INFINITY;
@@ -2019,8 +2029,15 @@ __device__ __forceinline__ void row_block(const Dims &D, const DecodeParams &dp,
   if (wrow) write_weights(sg, ws, wrow, s_par[5], s_par[6], dp, false);
   if (!arrive_last(&ws.ctr[4 * r + 2], (unsigned)nc, &s_last)) return;
   for (int cc = tid; cc < DIM; cc += kDThreads) {
-    float sum = ld_agent(&ws.opart[((size_t)r * kHelpers) * DIM + cc]);
-    for (int h = 1; h < nc; ++h) sum += ld_agent(&ws.opart[((size_t)r * kHelpers + h) * DIM + cc]);
+    // every chunk's partial requested at once, then added in chunk order
+    float part[kHelpers];
+#pragma unroll
+    for (int h = 0; h < kHelpers; ++h)
+      part[h] = h < nc ? ld_agent(&ws.opart[((size_t)r * kHelpers + h) * DIM + cc]) : 0.0f;
+    float sum = part[0];
+#pragma unroll
+    for (int h = 1; h < kHelpers; ++h)
+      if (h < nc) sum += part[h];
     ra.out[(size_t)r * DIM + cc] = sum;
   }
   EKV_MARK(2, 2);
