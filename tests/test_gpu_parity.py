@@ -215,6 +215,37 @@ def test_score_select_gauss_fused(case, alpha, delta):
     assert np.all(cg[~keep] == -1) and np.all(np.isnan(tg[~keep]))
 
 
+def test_score_select_gauss_fused_invalid_pages(case):
+    """Pages whose record holds a NaN (box, mu and var then non-finite) are
+    skipped by the fused call's bracket exactly as by the selector's own: the
+    same sets and tau_hat bits as the two calls in turn."""
+    inp, D, _, _ = case
+    t = torch()
+    meta = D.zeros_meta()
+    E.build_page_meta(D.shape, D.k, D.pt, D.sl, meta)
+    pt = inp.page_table
+    for b in range(inp.B):  # the first and the last page of every sequence, KV head 0
+        npg = (int(inp.seq_lens[b]) + inp.P - 1) // inp.P
+        for p_ in {0, npg - 1}:
+            meta[int(pt[b, p_]), 0, 0, 0] = float("nan")
+    out = []
+    for fused in (True, False):
+        box, mu, var = D.per_page(), D.per_page(), D.per_page()
+        sel, cnt = D.sel_buffers()
+        tau = t.full((inp.B, inp.Hq), np.nan, dtype=t.float64, device="cuda")
+        if fused:
+            E.score_select_pages_gauss(D.shape, D.q, meta, D.pt, D.sl, box, mu, var, 1.5, 0.5, sel, cnt,
+                                       tau_hat=tau)
+        else:
+            E.score_pages(D.shape, D.q, meta, D.pt, D.sl, box, mu, var)
+            E.select_pages_gauss(D.shape, box, mu, var, D.sl, 1.5, 0.5, sel, cnt, tau_hat=tau)
+        out.append((sel.cpu().numpy(), cnt.cpu().numpy(), tau.cpu().numpy(), box.cpu().numpy()))
+    (s1, c1, t1, b1), (s2, c2, t2, b2) = out
+    assert np.isnan(b1[:, 0]).any()  # the planted NaN reached the scores
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert np.array_equal(t1.view(np.uint64), t2.view(np.uint64))
+
+
 @pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
 def test_entmax_decode_sparse_topk(case, alpha):
     inp, D, _, (box_o, _, _) = case
