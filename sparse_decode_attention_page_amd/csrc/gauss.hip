@@ -31,7 +31,7 @@
 //       [e_lo, e_hi) between the last edge certified F >= 1 and the first
 //       certified F < 1, usually two or three bins.
 //   K3  solve: every block adds the moments of its points above e_hi about e_hi
-//       (sequential per thread, then a fixed-order block sum), lists its points
+//       (per page of a thread, pages combined in order, then a fixed-order block sum), lists its points
 //       inside the window in page order, and classifies its pages as kept /
 //       dropped / undecided for any threshold in the window.  The row's last
 //       block adds the chunks' moments in chunk order, solves F = 1 on the
@@ -586,6 +586,7 @@ __global__ __launch_bounds__(kGThreads) void gauss_solve_kernel(
   // the thread's 4 pages): moments of the points above ehi about ehi, the
   // window points, the page codes and the largest estimate
   double S[3] = {0.0, 0.0, 0.0};
+  double Su[4][3] = {{0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}};
   int listed = 0, wlisted = 0;
   double best = -INFINITY;
   int bestp = 0x7FFFFFFF;
@@ -616,24 +617,23 @@ __global__ __launch_bounds__(kGThreads) void gauss_solve_kernel(
         if (est > best || (est == best && p < bestp)) { best = est; bestp = p; }
       }
     }
+    // branch-free: a point at or below e_hi adds zeros; each of the 4 pages
+    // keeps its own moment sums (independent chains), combined in page order
+    // after the loop
     bool any = true;
 #pragma unroll 1
     for (int j = kNodes - 1; j >= 0 && any; --j) {
       const double xj = s_gx[j], wj = s_gw[j];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (!act[u]) continue;
         const double y = gh_point(gp.a, mm[u], sg[u], xj);
-        if (y > ehi) {
-          const double c = nn[u] * wj, d = y - ehi;
-          S[0] += c;
-          S[1] += c * d;
-          if (gp.ibeta == 2) S[2] += c * d * d;
-        } else if (y > elo) {
-          wm[u] |= 1u << j;
-        } else {
-          act[u] = false;
-        }
+        const bool up = act[u] && y > ehi;
+        const double c = up ? nn[u] * wj : 0.0, d = up ? y - ehi : 0.0;
+        Su[u][0] += c;
+        Su[u][1] += c * d;
+        if (gp.ibeta == 2) Su[u][2] += c * d * d;
+        wm[u] |= (act[u] && !up && y > elo) ? 1u << j : 0u;
+        act[u] = act[u] && y > elo;
       }
       any = __any(act[0] || act[1] || act[2] || act[3]);
     }
@@ -661,6 +661,8 @@ __global__ __launch_bounds__(kGThreads) void gauss_solve_kernel(
     listed += tot & 0xFFFF;
   }
   EKV_MARK(2, 2);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) S[k] = ((Su[0][k] + Su[1][k]) + Su[2][k]) + Su[3][k];
   block_sum_n<3>(S, dred);
   {
     const double bm = block_max(best, dred);
