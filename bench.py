@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--selector-sweep", action="store_true",
                     help="time select_pages_topk (k=64) and select_pages_gauss over contexts 32k..1M "
                          "(one JSON line with the table), then exit")
+    ap.add_argument("--config-sweep", action="store_true",
+                    help="step time (HIP-graph replay; Gaussian selection through score_select_pages_gauss and "
+                         "Top-k) and the full-cache softmax / entmax times on each smaller workload (4k, 32k, "
+                         "128k tokens); one JSON line with the table, then exit")
     ap.add_argument("--quality", action="store_true",
                     help="approximation quality vs KV budget on every synthetic workload (recall of the "
                          "full-cache entmax support, discarded mass and relative output error of entmax and "
@@ -97,6 +101,9 @@ def main():
         return
     if args.quality:
         quality_sweep(args)
+        return
+    if args.config_sweep:
+        config_sweep(args)
         return
     wl = synth.WORKLOADS[args.workload]
     alpha = wl.alphas[0]
@@ -795,6 +802,109 @@ def passage_leg(args, name):
     log(f"[bench] quality-matched leg ({name}): step {step_us:.2f} us, full softmax {sm_us:.1f} us, full entmax "
         f"{ef_us:.1f} us; delta entmax {res['delta_entmax_mean']:.3e}, rel err {res['rel_err_entmax_mean']:.3e}")
     return res
+
+
+def config_sweep(args):
+    """The step on each smaller workload: score + selection + sparse entmax decode
+    as HIP-graph replays over two replicas, once with the Gaussian selection
+    (score_select_pages_gauss) and once with Top-k (score_pages +
+    select_pages_topk), for every alpha the workload lists; beside them the
+    full-cache softmax and entmax decodes (eager, events around each call)."""
+    import numpy as np
+    import torch
+
+    import sparse_decode_attention_page_amd as E
+    from sparse_decode_attention_page_amd import synth
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rows = []
+    for name in ("tiny_4k", "gqa_32k", "gqa_128k"):
+        wl = synth.WORKLOADS[name]
+        inp = synth.make_device(wl, args.seed)
+        shape = E.make_shape(inp.q, inp.k_pool, inp.page_table)
+        B, Hq, Hkv, d, P, MP = inp.B, inp.Hq, inp.Hkv, inp.d, inp.P, inp.max_pages
+        meta = torch.zeros((inp.num_phys, Hkv, 4, d), dtype=inp.k_pool.dtype, device="cuda")
+        E.build_page_meta(shape, inp.k_pool, inp.page_table, inp.seq_lens, meta)
+        reps = [(inp.q, inp.k_pool, inp.v_pool, meta),
+                (inp.q.clone(), inp.k_pool.clone(), inp.v_pool.clone(), meta.clone())]
+        sl, pt = inp.seq_lens, inp.page_table
+        box = torch.empty((B, Hq, MP), device="cuda")
+        mu, var = torch.empty_like(box), torch.empty_like(box)
+        sel = torch.empty((B, Hq, MP), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((B, Hq), dtype=torch.int32, device="cuda")
+        out = torch.empty((B, Hq, d), device="cuda")
+        ws_s, ws_t = E.workspace(shape, E.CALL_SCORE), E.workspace(shape, E.CALL_TOPK)
+        ws_sg = E.workspace(shape, E.CALL_SCORE_GAUSS)
+        ws_d = E.workspace(shape, E.CALL_DECODE_SPARSE)
+        k_top = wl.topk or 64
+
+        def graph_us(fn):
+            fn(0), fn(1)
+            torch.cuda.synchronize()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            gs = []
+            with torch.cuda.stream(s):
+                for r in range(2):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        fn(r)
+                    gs.append(g)
+            torch.cuda.current_stream().wait_stream(s)
+            for i in range(max(args.warmup, 2)):
+                gs[i % 2].replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for i in range(args.steps):
+                gs[i % 2].replay()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / args.steps
+
+        def eager_us(fn, n=10):
+            fn()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        q0, k0, v0, m0 = reps[0]
+        ws_sm, ws_f = E.workspace(shape, E.CALL_SOFTMAX), E.workspace(shape, E.CALL_DECODE_FULL)
+        sm_us = eager_us(lambda: E.softmax_decode_full(shape, q0, k0, v0, pt, sl, out, ws=ws_sm))
+        for alpha in wl.alphas:
+            def gauss_step(r, alpha=alpha):
+                q, k, v, m = reps[r]
+                E.score_select_pages_gauss(shape, q, m, pt, sl, box, mu, var, alpha, wl.delta, sel, cnt, ws=ws_sg)
+                E.entmax_decode_sparse(shape, q, k, v, pt, sl, sel, cnt, alpha, out, ws=ws_d)
+
+            def topk_step(r, alpha=alpha):
+                q, k, v, m = reps[r]
+                E.score_pages(shape, q, m, pt, sl, box, mu, var, ws=ws_s)
+                E.select_pages_topk(shape, box, sl, k_top, sel, cnt, ws=ws_t)
+                E.entmax_decode_sparse(shape, q, k, v, pt, sl, sel, cnt, alpha, out, ws=ws_d)
+
+            g_us = graph_us(gauss_step)
+            gauss_step(0)
+            torch.cuda.synchronize()
+            g_kept = float(cnt.double().mean())
+            t_us = graph_us(topk_step)
+            ef_us = eager_us(lambda: E.entmax_decode_full(shape, q0, k0, v0, pt, sl, alpha, out, ws=ws_f))
+            row = {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "P": P, "kv_dtype": wl.dtype,
+                   "context": int(sl.max()), "alpha": alpha, "delta": wl.delta, "topk": k_top,
+                   "step_gauss_us": round(g_us, 2), "gauss_kept_pages_per_head_mean": round(g_kept, 2),
+                   "step_topk_us": round(t_us, 2), "pages_per_seq": MP,
+                   "softmax_decode_full_us": round(sm_us, 2), "entmax_decode_full_us": round(ef_us, 2)}
+            log(f"[configs] {row}")
+            rows.append(row)
+        del inp, reps, meta
+        torch.cuda.empty_cache()
+    print(json.dumps({"config_sweep": rows, "unit": "us per step (graph replay) / per call (full-cache, eager)"}),
+          flush=True)
 
 
 def selector_sweep(args):
