@@ -446,8 +446,15 @@ __global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
     const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt,
     float *__restrict__ weights_out, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int kParts = kDThreads / P;  // threads per token
+  // A block scores kIPB items (pages) at once, a group of kGT threads each, 4
+  // threads per token: one page of 64 tokens per pass, two of 32, four of 16
+  // (small pages would otherwise leave most of the block's loads tiny).
+  constexpr int kIPB = P >= 64 ? 1 : 64 / P;
+  constexpr int kGT = kDThreads / kIPB;  // threads per item
+  constexpr int kParts = kGT / P;        // threads per token
   constexpr int kPer = DIM / kParts;     // coordinates per thread
+  constexpr int kGW = kGT / kWave;       // waves per item
+  static_assert(kParts >= 1 && kGT % kWave == 0 && DIM % kParts == 0, "item groups of whole waves");
   __shared__ double dred[2 * kDThreads / kWave];
   __shared__ int scan_scratch[kDThreads / kWave];
   const int rows = D.B * D.Hq;
@@ -462,13 +469,20 @@ __global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
   EKV_MARK(0, 1);
   const int MP = D.max_pages;
   const size_t wrow = (size_t)MP * P;
-  const int tok = tid / kParts, part = tid % kParts;
+  const int grp = tid / kGT, gtid = tid % kGT;
+  const int tok = gtid / kParts, part = gtid % kParts;
+  const int wv = tid / kWave, lane = tid & (kWave - 1);
 #pragma unroll 1
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  for (int item0 = blockIdx.x * kIPB; item0 < total; item0 += gridDim.x * kIPB) {
+    // every thread runs the pass (the group maximum below needs whole waves);
+    // a group past the last item, or on a row past the workspace's capacity,
+    // computes on clamped indices and stores nothing
+    const int item = min(item0 + grp, total - 1);
+    const bool live = item0 + grp < total;
     const int r = find_row(prefix, rows, item);
     const int i = item - prefix[r];
     const int cnt = prefix[r + 1] - prefix[r];
-    if ((long long)prefix[r + 1] > ws.cap) continue;  // the row is past the workspace's capacity (uniform)
+    const bool fits = (long long)prefix[r + 1] <= ws.cap;  // the row is within the workspace's capacity
     const size_t it = (size_t)prefix[r] + i;
     const int b = r / D.Hq, g = (r % D.Hq) / D.G;
     // independent loads first: sequence length, page ids, the query slice
@@ -491,19 +505,29 @@ __global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
 #pragma unroll
     for (int o = kParts / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, kWave);
     const double x = tok < n ? dp.a * (dp.c * acc) : -INFINITY;
-    if (part == 0) ws.xs[it * P + tok] = x;
-    const double pm = block_max(x, dred);
-    if (tid == 0) {
+    const bool store = live && fits;
+    if (store && part == 0) ws.xs[it * P + tok] = x;
+    // the page maximum: the group's waves, combined through LDS when a page spans several
+    double pm = wave_max(x);
+    if constexpr (kGW > 1) {
+      __syncthreads();
+      if (lane == 0) dred[wv] = pm;
+      __syncthreads();
+      pm = dred[grp * kGW];
+#pragma unroll
+      for (int k = 1; k < kGW; ++k) pm = fmax(pm, dred[grp * kGW + k]);
+    }
+    if (store && gtid == 0) {
       ws.pmax[it] = bad_item ? NAN : pm;
       ws.iphys[it] = (uint32_t)physc;
     }
     // weights_out: zero every slot of the pages this item covers, (prev, p]
     // (the last item also covers the pages after p); kernel 2 writes the
     // support weights.
-    if (weights_out && !bad_item) {
+    if (weights_out && store && !bad_item) {
       const size_t lo_s = (size_t)(prev + 1) * P;
       const size_t hi_s = (i == cnt - 1) ? wrow : (size_t)(p + 1) * P;
-      for (size_t s = lo_s + tid; s < hi_s; s += kDThreads) weights_out[(size_t)r * wrow + s] = 0.0f;
+      for (size_t s = lo_s + gtid; s < hi_s; s += kGT) weights_out[(size_t)r * wrow + s] = 0.0f;
     }
   }
   EKV_MARK(0, 2);
