@@ -44,7 +44,7 @@ namespace ekv {
 namespace items {
 
 constexpr int kDThreads = 256;
-constexpr int kDGrid = 1024;      // kernel 1: items are strided over this many blocks
+constexpr int kDGrid = 2048;      // kernel 1: items are strided over this many blocks
 constexpr int kChunkTok = 2048;   // kernel 2: tokens per chunk block (long_1m decode: 2048 26.6 us, 1024 30.3, 4096 27.2, 8192 30.9)
 constexpr int kSplitMax = 32;     // kernel 2: chunk blocks per row at most
 constexpr int kCand = 1024;       // candidates a last block keeps in LDS (one wave solves for tau)
