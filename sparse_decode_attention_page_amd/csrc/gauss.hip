@@ -182,7 +182,7 @@ __device__ __forceinline__ void row_bracket(const Dims &D, const GaussParams &gp
                                             const float *var, double &lo, double &hi, double *red) {
   double l = -INFINITY, h = -INFINITY;
   if (gp.sum_tiles) {
-    const int nt = (rc.np + 63) / 64;
+    const int nt = (rc.np + kSummaryTile - 1) / kSummaryTile;
     for (int c = threadIdx.x; c < nt; c += kGThreads) {
       const double2 v = *reinterpret_cast<const double2 *>(ws.summ + ((size_t)rc.row * gp.sum_tiles + c) * 2);
       l = fmax(l, v.x);
@@ -1069,7 +1069,7 @@ static hipError_t launch_gauss_impl(const Dims &D, const float *box, const float
   GaussWs w = carve_gauss(D, gp, ws, nullptr);
   const dim3 grid(grid_of(gp));
   if (summ) {  // bracket from the scorer's summary; counts and counters zeroed by the scorer
-    gp.sum_tiles = (D.max_pages + 63) / 64;
+    gp.sum_tiles = (D.max_pages + kSummaryTile - 1) / kSummaryTile;
     w.summ = summ;
   } else {
     hipLaunchKernelGGL(gauss_bracket_kernel, grid, dim3(kGThreads), 0, s, D, gp, gc, box, mu, var, seq_lens,

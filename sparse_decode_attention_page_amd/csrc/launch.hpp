@@ -48,6 +48,7 @@ hipError_t launch_score(const Dims &D, int dtype, bool f8, const void *q, const 
 // doubles per (query row, 64-page tile): the largest mean over the tile's valid
 // full pages, the largest mu + sqrt2 sigma x_top over its valid pages) to summ,
 // and zeroes the nzero words at zero (the selector's counts and counters).
+constexpr int kSummaryTile = 64;  // pages per summary entry (the scorer's tile)
 struct ScoreSummary {
   double *summ = nullptr;
   double x_top = 0.0;

@@ -45,6 +45,7 @@
 namespace ekv {
 
 constexpr int kTilePages = 64;      // one page per lane
+static_assert(kTilePages == kSummaryTile, "one bracket summary entry per tile");
 constexpr int kScoreThreads = 256;  // four waves: box (two), mean, variance
 constexpr int kScoreTiles = 2;      // tiles per block
 static_assert(kScoreTiles * kTilePages <= kScoreThreads, "one page id per thread in the prologue");
