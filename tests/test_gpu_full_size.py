@@ -158,6 +158,27 @@ def test_full_gauss_selection_is_deterministic(full):
     assert t.equal(t1.view(t.int64), t2.view(t.int64)), "tau_hat bits differ between two runs"
 
 
+def test_full_fused_score_select_gauss(full):
+    """score_select_pages_gauss at the full size (the benchmark's step): box,
+    mu and var, the sets and the tau_hat bits equal score_pages followed by
+    select_pages_gauss, on every row."""
+    t = torch()
+    inp, wl = full["inp"], full["wl"]
+    B, Hq, MP = inp.B, inp.Hq, inp.max_pages
+    box, mu, var = (t.full((B, Hq, MP), np.nan, device="cuda") for _ in range(3))
+    sel = t.full((B, Hq, MP), -1, dtype=t.int32, device="cuda")
+    cnt = t.full((B, Hq), -1, dtype=t.int32, device="cuda")
+    tau = t.full((B, Hq), np.nan, dtype=t.float64, device="cuda")
+    E.score_select_pages_gauss(full["shape"], inp.q, full["meta"], inp.page_table, inp.seq_lens, box, mu, var,
+                               wl.alphas[0], wl.delta, sel, cnt, tau_hat=tau)
+    s2, c2, t2 = _select(full, "gauss")
+    for a, b in ((box, full["box"]), (mu, full["mu"]), (var, full["var"])):
+        assert t.equal(a.view(t.int32), b.view(t.int32))
+    assert t.equal(cnt, c2)
+    assert t.equal(sel, s2)
+    assert t.equal(tau.view(t.int64), t2.view(t.int64))
+
+
 @pytest.mark.parametrize("kind", ["sparse_gauss", "sparse_topk", "full"])
 def test_full_entmax_sampled_rows(full, kind):
     t = torch()
