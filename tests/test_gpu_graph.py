@@ -5,7 +5,8 @@ Two graphs on a 8,192-token, 32/8-head, bf16 slice with pages of 16:
 
 * the decode step (score_pages -> select_pages_gauss / select_pages_topk ->
   entmax_decode_sparse, the group-shared forms with one set per KV head, the
-  compact-record scorer, softmax over the kept pages) captured once; before each
+  compact-record scorer, softmax over the kept pages, score and Gaussian
+  selection as one call) captured once; before each
   of four replays the query
   is overwritten eagerly, and the replay's page sets, counts and outputs are
   compared with an eager run on the same query;
@@ -64,9 +65,16 @@ class _Step:
         self.ws_tg = E.workspace(shape, E.CALL_TOPK_GROUP)
         self.ws_dg = E.workspace(shape, E.CALL_DECODE_GROUP)
         self.ws_sm = E.workspace(shape, E.CALL_SOFTMAX_SPARSE)
+        self.ws_sg = E.workspace(shape, E.CALL_SCORE_GAUSS)
         self.meta8 = None
 
     def __call__(self, q, k_pool, v_pool, meta, pt, sl):
+        if self.policy == "gauss_fused":  # score and Gaussian selection in one call
+            E.score_select_pages_gauss(self.shape, q, meta, pt, sl, self.box, self.mu, self.var, self.alpha,
+                                       self.delta, self.sel, self.cnt, ws=self.ws_sg)
+            E.entmax_decode_sparse(self.shape, q, k_pool, v_pool, pt, sl, self.sel, self.cnt, self.alpha,
+                                   self.out, ws=self.ws_d)
+            return
         if self.policy == "gauss_f8":  # compact records, built once from the same keys
             if self.meta8 is None:
                 self.meta8 = E.meta_f8_empty(self.shape)
@@ -124,7 +132,8 @@ def _close(x, y, tag):
         f"{tag}: outputs differ (max abs {float((x - y).abs().max()):.3e})")
 
 
-@pytest.mark.parametrize("policy", ["gauss", "topk", "gauss_group", "topk_group", "gauss_f8", "gauss_softmax"])
+@pytest.mark.parametrize("policy", ["gauss", "topk", "gauss_group", "topk_group", "gauss_f8", "gauss_softmax",
+                                    "gauss_fused"])
 def test_graph_replays_match_eager_step(policy):
     import torch
     wl, inp, shape, meta = _inputs(11)
