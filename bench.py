@@ -933,9 +933,15 @@ def selector_sweep(args):
         E.score_pages(shape, inp.q, meta, inp.page_table, inp.seq_lens, box, mu, var,
                       ws=E.workspace(shape, E.CALL_SCORE))
         ws_t, ws_g = E.workspace(shape, E.CALL_TOPK), E.workspace(shape, E.CALL_GAUSS)
+        ws_s, ws_sg = E.workspace(shape, E.CALL_SCORE), E.workspace(shape, E.CALL_SCORE_GAUSS)
         calls = {"topk64": lambda: E.select_pages_topk(shape, box, inp.seq_lens, 64, sel, cnt, ws=ws_t),
                  "gauss": lambda: E.select_pages_gauss(shape, box, mu, var, inp.seq_lens, alpha, wl.delta,
-                                                       sel, cnt, ws=ws_g)}
+                                                       sel, cnt, ws=ws_g),
+                 "score": lambda: E.score_pages(shape, inp.q, meta, inp.page_table, inp.seq_lens, box, mu, var,
+                                                ws=ws_s),
+                 "score_select_gauss": lambda: E.score_select_pages_gauss(shape, inp.q, meta, inp.page_table,
+                                                                          inp.seq_lens, box, mu, var, alpha,
+                                                                          wl.delta, sel, cnt, ws=ws_sg)}
         row = {"context": ctx, "pages": MP}
         for name, fn in calls.items():
             for _ in range(3):
