@@ -791,15 +791,22 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
     // adds, in any order): a bound as certified as each chunk's and tighter
     // (about sqrt(chunks) for alpha 1.5)
     if (has_n) atomicAdd(&s_cnt[0][tid % kNThr], n_t);
-    if (tid < nsplit) {
-      soff[tid + 1] = c_t;
-      sL[tid] = l_t;
-      sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
-    }
-    __syncthreads();
-    if (tid == 0) {  // segment offsets (the first step's entry addresses need them)
-      soff[0] = 0;
-      for (int s2 = 0; s2 < nsplit; ++s2) soff[s2 + 1] += soff[s2];
+    // segment offsets (the first step's entry addresses need them): an
+    // inclusive scan of the chunks' candidate counts across wave 0's lanes
+    static_assert(kSplitMax <= kWave, "one chunk per lane of wave 0");
+    if (tid < kWave) {
+      int incl = tid < nsplit ? c_t : 0;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (tid >= o) incl += v;
+      }
+      if (tid < nsplit) {
+        soff[tid + 1] = incl;
+        sL[tid] = l_t;
+        sbase[tid] = (int)((long long)tid * cnt / nsplit) * P;
+      }
+      if (tid == 0) soff[0] = 0;
     }
     __syncthreads();
     total = soff[nsplit];
