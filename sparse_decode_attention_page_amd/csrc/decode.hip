@@ -260,13 +260,16 @@ constexpr int head_map_col(int L, int lg_g, int j) {
     if ((pair_mask(j) >> b) & 1) x ^= head_map_col(L, lg_g, b);
   return x;
 }
-template <int L, int kLgG>
+// The columns are constants of the template (folded here: the recursive helper
+// called at run time would make the kernel a non-leaf function).
+template <int L, int kLgG, int J = 0>
 __device__ __forceinline__ int head_map(int e) {
-  int r = 0;
-#pragma unroll
-  for (int j = 0; j < L; ++j)
-    if ((e >> j) & 1) r ^= head_map_col(L, kLgG, j);
-  return r;
+  if constexpr (J == L) {
+    return 0;
+  } else {
+    constexpr int col = head_map_col(L, kLgG, J);
+    return (((e >> J) & 1) ? col : 0) ^ head_map<L, kLgG, J + 1>(e);
+  }
 }
 template <int kJ, int kV, int G>
 __device__ __forceinline__ double head_sum_levels(double (&acc)[G]) {
