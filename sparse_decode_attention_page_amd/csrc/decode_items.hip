@@ -534,9 +534,13 @@ __global__ __launch_bounds__(kDThreads) void decode_scores_kernel(
 }
 
 // ------------------------------------------------ kernel 2: threshold and output
-template <typename T, int DIM, int P>
+// kB fixes the power's exponent code (2: alpha = 1.5, 1: alpha = 2) at compile
+// time: those kernels hold no call of the generic pow, whose calling
+// convention costs the kernel SGPR spills and instructions on every phase
+// (0.6 us of ~21 at 1M tokens); kB = 0 takes the code from dp.
+template <typename T, int DIM, int P, int kB>
 __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
-    Dims D, DecodeParams dp, const T *__restrict__ v_pool, const int32_t *__restrict__ seq_lens,
+    Dims D, DecodeParams dp_in, const T *__restrict__ v_pool, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ sel_idx, const int32_t *__restrict__ sel_cnt, float *__restrict__ out,
     double *__restrict__ tau_out, float *__restrict__ weights_out, DecodeWs ws) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -558,6 +562,8 @@ __global__ __launch_bounds__(kDThreads) void decode_finish_kernel(
   int *ci = reinterpret_cast<int *>(cx + kCand);              // [kCand] token index
   uint32_t *cv = reinterpret_cast<uint32_t *>(ci + kCand);    // [kCand] V row index
   double *sortbuf = reinterpret_cast<double *>(cv + kCand);   // [kCand] (sort form only)
+  DecodeParams dp = dp_in;
+  if constexpr (kB != 0) dp.ibeta = kB;
   const int r = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   EKV_MARK(1, 0);
   const int MP = D.max_pages;
@@ -1070,14 +1076,27 @@ static hipError_t launch_finish_t(const Dims &D, const DecodeParams &dp, const v
   const size_t cand_bytes = (size_t)kCand * (8 + 4 + 4) + (dp.tau_method == 1 ? (size_t)kCand * 8 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)((size_t)kCand * (8 + 4 + 4 + 8)));
+    const int most = (int)((size_t)kCand * (8 + 4 + 4 + 8));
+    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P, 2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        most);
+    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        most);
+    hipFuncSetAttribute((const void *)decode_finish_kernel<T, DIM, P, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        most);
     attr_set = true;
   }
   const long long chunks = ((long long)D.max_pages * D.P + kChunkTok - 1) / kChunkTok;
   const int split = (int)(chunks < kSplitMax ? chunks : kSplitMax);
-  hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P>), dim3(rows, split), dim3(kDThreads), cand_bytes, s, D, dp,
-                     (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
+  const dim3 grid(rows, split);
+  if (dp.ibeta == 2)
+    hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P, 2>), grid, dim3(kDThreads), cand_bytes, s, D, dp,
+                       (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
+  else if (dp.ibeta == 1)
+    hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P, 1>), grid, dim3(kDThreads), cand_bytes, s, D, dp,
+                       (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
+  else
+    hipLaunchKernelGGL((decode_finish_kernel<T, DIM, P, 0>), grid, dim3(kDThreads), cand_bytes, s, D, dp,
+                       (const T *)v_pool, seq_lens, sel_idx, sel_cnt, out, tau, weights_out, w);
   return hipGetLastError();
 }
 
